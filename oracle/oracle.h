@@ -1,0 +1,83 @@
+/* CPU oracle for the tile-based differentiable Gaussian-splatting rasterizer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The HIP product path
+ * neither includes this header nor links this code, and this code includes
+ * nothing from the product path.
+ *
+ * Sources (titles of the pages the method comes from):
+ *   [3DGS-CUDA]  "What the 3DGS Literature Left on the Table" (rasterizer
+ *                optimisation blog: Steps 1-6, Figures 3-10)
+ *   [LOAD-IMB]   "Mitigating SM-Level Load Imbalance in 3D Gaussian
+ *                Splatting on GPUs" (section 2.1 Eq. 1-3, section 4 Eq. 4-6)
+ *
+ * Arithmetic modes
+ *   mirror : IEEE fp32, round-to-nearest-even, no contraction (built with
+ *            -ffp-contract=off); fmaf only where written. Every DECISION
+ *            (tile emission, alpha cutoff, transmittance stop) is taken here.
+ *   truth  : fp64 values with the mirror's decisions frozen; used for
+ *            projection values and for the analytic backward.
+ *
+ * Splat record (12 floats): mx, my, a, b, c, o, r, g, b, tau, depth, 0.
+ * Culled Gaussians carry tau = -1 and zeros elsewhere.
+ * Gradient record (9 values): d mx, d my, d a, d b, d c, d o, d r, d g, d b.
+ */
+#ifndef GS_ORACLE_H
+#define GS_ORACLE_H
+#include <stdint.h>
+
+typedef struct {
+  int32_t width, height;
+  double fx, fy, cx, cy;
+  double w2c[12];  /* row-major [R | t] */
+  double znear, lowpass;
+} or_camera;
+
+/* Real orthonormal SH basis (degree <= 3) at unit direction d; Y has (deg+1)^2 entries. */
+void or_sh_basis(int degree, const double *d, double *Y);
+
+/* Projection (EWA, Eq. 1 of [LOAD-IMB]) in fp64; writes fp32 records and,
+   if splats64 != NULL, the unrounded fp64 records. */
+void or_project(int n, const float *means, const float *log_scales, const float *quats,
+                const float *opac, const float *sh, int degree, const or_camera *cam,
+                float *splats, double *splats64);
+
+/* Opacity-aware exact conic-tile binning ([3DGS-CUDA] Step 1 (b), Figure 3). */
+void or_bin_count(int n, const float *splats, int width, int height, int32_t *counts);
+void or_bin_emit(int n, const float *splats, int width, int height, const int64_t *offsets,
+                 uint64_t *keys, int32_t *ids);
+
+/* Order pairs by (key, id) and cut the tile ranges. */
+void or_sort_pairs(int64_t npairs, const uint64_t *keys, const int32_t *ids,
+                   uint64_t *sorted_keys, int32_t *sorted_ids);
+void or_tile_ranges(int64_t npairs, const uint64_t *sorted_keys, int ntiles, int32_t *ranges);
+
+/* Forward blend, mirror mode (Eq. 2-3 of [LOAD-IMB]). last[p] = number of list
+   entries consumed by the pixel (stop index + 1, or the full tile length).
+   tile_mask (nullable) restricts the work to tiles with a nonzero byte; other
+   pixels are left untouched. stats (nullable) += {hits, evaluations}. */
+void or_render_fwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
+                   int width, int height, const uint8_t *tile_mask, float *rgb, float *T_final,
+                   int32_t *last, uint8_t *knife, int64_t *stats);
+
+/* Untiled brute force: every pixel walks every visible splat in (depth, id) order. */
+void or_render_fwd_untiled(int n, const float *splats, int width, int height,
+                           float *rgb, float *T_final);
+
+/* Forward values in fp64 with frozen decisions: hits from the fp32 records
+   splats_dec, stop from last; values from splats_val (fp64 records). */
+void or_render_fwd_values(const float *splats_dec, const double *splats_val,
+                          const int32_t *sorted_ids, const int32_t *ranges, int width, int height,
+                          const int32_t *last, double *rgb, double *T_final);
+
+/* Analytic backward, truth mode: grads[n][9] (overwritten) of L = sum_p g_p . C_p. */
+void or_render_bwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
+                   int width, int height, const int32_t *last, const float *dL_drgb,
+                   int n, double *grads);
+
+/* Per-frame chunking policy (Eq. 6 of [LOAD-IMB]). counts_desc: tile counts in
+   descending order. Writes h (tiles to chunk) and k (chunks per tile; 1 when off). */
+void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, double lambda_,
+                     double beta, double eps, int32_t *h_out, int32_t *k_out);
+
+#endif
