@@ -1,0 +1,246 @@
+"""MI355X-native tile-based differentiable Gaussian-splatting rasterizer.
+
+The work runs in hand-written HIP kernels behind the C ABI declared in
+``include/gs.h`` (``libgs.so`` in this package directory). This module is the
+thin Python binding: it marshals torch tensors (device memory) and the current
+HIP stream into those calls and raises ``GsError`` on a bad status. It does no
+arithmetic of its own, and it fails loudly when the library has not been built.
+
+Low-level calls keep the C names (``gs_project``, ``gs_bin_tiles``,
+``gs_sort_keys``, ``gs_render_fwd``, ``gs_render_bwd``); ``Rasterizer`` owns the
+scratch buffers and chains them into a frame.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgs.so")
+
+GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY = 0, -1, -2
+GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED = -3, -4, -5
+SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
+
+EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_bin_tiles",
+           "gs_sort_keys", "gs_render_fwd", "gs_render_bwd")
+
+
+class GsError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+
+
+class GsCamera(C.Structure):
+    _fields_ = [("width", C.c_int32), ("height", C.c_int32), ("fx", C.c_float), ("fy", C.c_float),
+                ("cx", C.c_float), ("cy", C.c_float), ("world_to_cam", C.c_float * 12),
+                ("znear", C.c_float), ("lowpass", C.c_float)]
+
+
+class GsSched(C.Structure):
+    _fields_ = [("chunk_mode", C.c_int32), ("force_k", C.c_int32), ("force_h", C.c_int32),
+                ("lambda_", C.c_float), ("beta", C.c_float), ("eps", C.c_float)]
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = C.CDLL(LIB_PATH)
+    P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    cam_p = C.POINTER(GsCamera)
+    L.gs_strerror.argtypes, L.gs_strerror.restype = [i32], C.c_char_p
+    L.gs_workspace_size.argtypes, L.gs_workspace_size.restype = [i32, i32, i32, i64], sz
+    L.gs_fwd_state_size.argtypes, L.gs_fwd_state_size.restype = [i32, i32], sz
+    L.gs_project.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P]
+    L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, sz, P]
+    L.gs_sort_keys.argtypes = [i32, P, P, P, P, i64, cam_p, P, P, P, P, sz, P]
+    L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
+    L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
+    for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd"):
+        getattr(L, name).restype = i32
+    _lib_handle = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().gs_strerror(int(status)).decode()
+
+
+def make_camera(cam) -> GsCamera:
+    """GsCamera from any object with width, height, fx, fy, cx, cy, world_to_cam, znear, lowpass."""
+    c = GsCamera()
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    for i, v in enumerate(list(cam.world_to_cam)):
+        c.world_to_cam[i] = float(v)
+    c.znear, c.lowpass = float(cam.znear), float(cam.lowpass)
+    return c
+
+
+def make_sched(chunk_mode: int = 1, force_k: int = 0, force_h: int = 0, lambda_: float = 0.0,
+               beta: float = 0.0, eps: float = 0.10) -> GsSched:
+    return GsSched(int(chunk_mode), int(force_k), int(force_h), float(lambda_), float(beta),
+                   float(eps))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(status, what):
+    if status != GS_OK:
+        raise GsError(status, what)
+
+
+def workspace_size(n, width, height, capacity) -> int:
+    return int(lib().gs_workspace_size(int(n), int(width), int(height), int(capacity)))
+
+
+def fwd_state_size(width, height) -> int:
+    return int(lib().gs_fwd_state_size(int(width), int(height)))
+
+
+# ------------------------------------------------------------------ C-named calls
+
+def gs_project(n, means, log_scales, quats, opacities, sh, sh_degree, cam, splats, stream=None):
+    _check(lib().gs_project(int(n), _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacities),
+                            _ptr(sh), int(sh_degree), C.byref(cam), _ptr(splats), _stream(stream)),
+           "gs_project")
+
+
+def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace, stream=None):
+    _check(lib().gs_bin_tiles(int(n), _ptr(splats), C.byref(cam), int(capacity), _ptr(offsets),
+                              _ptr(keys), _ptr(ids), _ptr(status), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gs_bin_tiles")
+
+
+def gs_sort_keys(n, splats, offsets, keys, ids, capacity, cam, sorted_keys, sorted_ids, ranges,
+                 workspace, stream=None):
+    _check(lib().gs_sort_keys(int(n), _ptr(splats), _ptr(offsets), _ptr(keys), _ptr(ids),
+                              int(capacity), C.byref(cam), _ptr(sorted_keys), _ptr(sorted_ids),
+                              _ptr(ranges), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gs_sort_keys")
+
+
+def gs_render_fwd(n, splats, sorted_ids, ranges, cam, sched, rgb, T_final, last, fwd_state,
+                  stats, workspace, stream=None):
+    _check(lib().gs_render_fwd(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges), C.byref(cam),
+                               C.byref(sched) if sched is not None else None, _ptr(rgb),
+                               _ptr(T_final), _ptr(last), _ptr(fwd_state),
+                               fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)),
+           "gs_render_fwd")
+
+
+def gs_render_bwd(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, dL_drgb,
+                  dL_dsplat, workspace, stream=None):
+    _check(lib().gs_render_bwd(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges), C.byref(cam),
+                               _ptr(T_final), _ptr(last), _ptr(fwd_state),
+                               fwd_state.numel() * fwd_state.element_size(), _ptr(dL_drgb),
+                               _ptr(dL_dsplat), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gs_render_bwd")
+
+
+# ------------------------------------------------------------------ frame driver
+
+class Rasterizer:
+    """Owns the per-frame buffers for one image size and chains the five calls.
+
+    Buffers grow when needed (more Gaussians, more pairs); a pair overflow
+    reported by gs_bin_tiles is handled by growing and running the frame again.
+    """
+
+    def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None):
+        self.cam = make_camera(camera)
+        self.W, self.H = int(camera.width), int(camera.height)
+        self.tiles = ((self.W + 15) // 16) * ((self.H + 15) // 16)
+        self.device = torch.device(device)
+        self.sched = sched if sched is not None else make_sched()
+        self.capacity = int(capacity)
+        self.n = -1
+        dev = self.device
+        self.rgb = torch.empty((3, self.H, self.W), dtype=torch.float32, device=dev)
+        self.T = torch.empty((self.H, self.W), dtype=torch.float32, device=dev)
+        self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev)
+        self.fwd_state = torch.empty(fwd_state_size(self.W, self.H), dtype=torch.uint8, device=dev)
+        self.ranges = torch.empty((self.tiles, 2), dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.stats = torch.zeros(4, dtype=torch.int64, device=dev)
+
+    def _ensure(self, n, capacity):
+        dev = self.device
+        if n != self.n:
+            self.splats = torch.empty((max(n, 1), SPLAT_FLOATS), dtype=torch.float32, device=dev)
+            self.offsets = torch.empty(n + 1, dtype=torch.int32, device=dev)
+            self.grads = torch.empty((max(n, 1), GRAD_FLOATS), dtype=torch.float32, device=dev)
+            self.n = n
+            self.workspace = None
+        if capacity != self.capacity or not hasattr(self, "keys"):
+            self.capacity = capacity
+            self.keys = torch.empty(max(capacity, 1), dtype=torch.int64, device=dev)
+            self.ids = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+            self.sorted_keys = torch.empty(max(capacity, 1), dtype=torch.int64, device=dev)
+            self.sorted_ids = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+            self.workspace = None
+        if self.workspace is None:
+            ws = workspace_size(n, self.W, self.H, self.capacity)
+            self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+    def project(self, means, log_scales, quats, opacities, sh, sh_degree):
+        n = int(means.shape[0])
+        self._ensure(n, self.capacity)
+        gs_project(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, self.splats)
+        return self.splats[:n]
+
+    def bin_and_sort(self, n, want_keys=False):
+        """Bin and sort the current splats; grows the pair buffers on overflow."""
+        for _ in range(3):
+            gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets, self.keys, self.ids,
+                         self.status, self.workspace)
+            gs_sort_keys(n, self.splats, self.offsets, self.keys, self.ids, self.capacity, self.cam,
+                         self.sorted_keys if want_keys else None, self.sorted_ids, self.ranges,
+                         self.workspace)
+            if int(self.status.item()) == GS_OK:
+                return int(self.offsets[n].item())
+            need = int(self.offsets[n].item())
+            self._ensure(n, max(need + need // 8, 1024))
+        raise GsError(GS_ERR_CAPACITY, "bin_and_sort")
+
+    def render_fwd(self, n, stats=False):
+        if stats:
+            self.stats.zero_()
+        gs_render_fwd(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched, self.rgb,
+                      self.T, self.last, self.fwd_state, self.stats if stats else None,
+                      self.workspace)
+        return self.rgb, self.T, self.last
+
+    def render_bwd(self, n, dL_drgb):
+        gs_render_bwd(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.T, self.last,
+                      self.fwd_state, dL_drgb, self.grads, self.workspace)
+        return self.grads[:n]

@@ -1,0 +1,178 @@
+// C-ABI entry points: argument validation, camera preparation, workspace and
+// forward-state layout, and the kernel launches of each stage. The functions
+// are declared (with their contracts) in include/gs.h.
+#include <math.h>
+#include <string.h>
+
+#include "gs_common.h"
+
+hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
+                             const float *opac, const float *sh, int degree, const CamK &cam,
+                             float *splats, hipStream_t st);
+hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
+                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status,
+                         int32_t *scan_buf, hipStream_t st);
+size_t gs_sort_ws_bytes(int n, int64_t cap);
+int gs_scan_buf_elems(int n_max);
+hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, const uint64_t *keys,
+                          int64_t cap, const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
+                          int32_t *ranges, void *ws, hipStream_t st);
+hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
+                                const int32_t *ranges, const CamK &cam, float *rgb, float *T,
+                                int32_t *last, int32_t *sub_last, int64_t *stats, hipStream_t st);
+hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
+                                const int32_t *ranges, const CamK &cam, const float *T,
+                                const int32_t *last, const int32_t *sub_last, const float *dL,
+                                float *grads, int n, hipStream_t st);
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool finite_pos(float v) { return isfinite(v) && v > 0.0f; }
+
+// Fills the kernel-side camera; false on invalid values.
+bool prep_camera(const gs_camera *c, CamK *k) {
+  if (!c || c->width <= 0 || c->height <= 0) return false;
+  if (!finite_pos(c->fx) || !finite_pos(c->fy) || !isfinite(c->cx) || !isfinite(c->cy)) return false;
+  if (!isfinite(c->znear) || !isfinite(c->lowpass) || c->lowpass < 0.0f) return false;
+  for (int i = 0; i < 12; i++)
+    if (!isfinite(c->world_to_cam[i])) return false;
+  k->width = c->width;
+  k->height = c->height;
+  k->tiles_x = (c->width + 15) / 16;
+  k->tiles_y = (c->height + 15) / 16;
+  k->fx = c->fx; k->fy = c->fy; k->cx = c->cx; k->cy = c->cy;
+  const float *M = c->world_to_cam;
+  for (int r = 0; r < 3; r++) {
+    for (int j = 0; j < 3; j++) k->R[3 * r + j] = M[4 * r + j];
+    k->t[r] = M[4 * r + 3];
+  }
+  for (int j = 0; j < 3; j++)
+    k->centre[j] = -(k->R[j] * k->t[0] + k->R[3 + j] * k->t[1] + k->R[6 + j] * k->t[2]);
+  k->znear = c->znear;
+  k->lowpass = c->lowpass;
+  return true;
+}
+
+int64_t num_tiles(int32_t w, int32_t h) { return (int64_t)((w + 15) / 16) * ((h + 15) / 16); }
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gs_strerror(int32_t s) {
+  switch (s) {
+    case GS_OK: return "ok";
+    case GS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GS_ERR_CAPACITY: return "pair buffer capacity exceeded";
+    case GS_ERR_WORKSPACE: return "workspace or forward state too small";
+    case GS_ERR_HIP: return "HIP runtime error";
+    case GS_ERR_UNSUPPORTED: return "unsupported size";
+    default: return "unknown status";
+  }
+}
+
+size_t gs_fwd_state_size(int32_t width, int32_t height) {
+  if (width <= 0 || height <= 0) return 0;
+  return round256((size_t)num_tiles(width, height) * 4 * sizeof(int32_t));
+}
+
+size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity) {
+  if (n < 0 || width <= 0 || height <= 0 || pair_capacity < 0) return 0;
+  const size_t bin = round256((size_t)gs_scan_buf_elems(n) * sizeof(int32_t));
+  const size_t sort = gs_sort_ws_bytes(n, pair_capacity);
+  return bin > sort ? bin : sort;
+}
+
+int32_t gs_project(int32_t n, const float *means, const float *log_scales, const float *quats,
+                   const float *opacities, const float *sh, int32_t sh_degree, const gs_camera *cam,
+                   float *splats, void *stream) {
+  CamK k;
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GS_OK;
+  if (!means || !log_scales || !quats || !opacities || !sh || !splats) return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(quats, 16) || !aligned(splats, 16) || !aligned(sh, 4)) return GS_ERR_INVALID_ARGUMENT;
+  return hip_status(gs_launch_project(n, means, log_scales, quats, opacities, sh, sh_degree, k,
+                                      splats, (hipStream_t)stream));
+}
+
+int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
+                     int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  CamK k;
+  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX || !prep_camera(cam, &k))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!offsets || !device_status || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
+  if (pair_capacity > 0 && (!keys || !ids)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8))) return GS_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
+    return GS_ERR_WORKSPACE;
+  return hip_status(gs_launch_bin(n, splats, k, pair_capacity, offsets, keys, ids, device_status,
+                                  reinterpret_cast<int32_t *>(workspace), (hipStream_t)stream));
+}
+
+int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, const uint64_t *keys,
+                     const int32_t *ids, int64_t pair_capacity, const gs_camera *cam,
+                     uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  CamK k;
+  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX || !prep_camera(cam, &k))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!offsets || !tile_ranges || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
+  if (pair_capacity > 0 && (!keys || !ids || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8)) ||
+      (sorted_keys && !aligned(sorted_keys, 8)) || !aligned(tile_ranges, 8))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
+    return GS_ERR_WORKSPACE;
+  (void)ids;  // ids are implied by offsets: pair j of splat i has id i
+  return hip_status(gs_launch_sort(n, splats, offsets, keys, pair_capacity, k, sorted_keys,
+                                   sorted_ids, tile_ranges, workspace, (hipStream_t)stream));
+}
+
+int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
+                      const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
+                      float *rgb, float *T_final, int32_t *last, void *fwd_state,
+                      size_t fwd_state_bytes, int64_t *stats, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  CamK k;
+  if (n < 0 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!tile_ranges || !rgb || !T_final || !last || !fwd_state) return GS_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (!splats || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8)) return GS_ERR_INVALID_ARGUMENT;
+  if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
+  (void)sched; (void)workspace; (void)workspace_bytes;
+  return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, rgb, T_final, last,
+                                         reinterpret_cast<int32_t *>(fwd_state), stats,
+                                         (hipStream_t)stream));
+}
+
+int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
+                      const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
+                      const int32_t *last, const void *fwd_state, size_t fwd_state_bytes,
+                      const float *dL_drgb, float *dL_dsplat, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  CamK k;
+  if (n < 0 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!tile_ranges || !T_final || !last || !fwd_state || !dL_drgb) return GS_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (!splats || !sorted_ids || !dL_dsplat)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8) ||
+      (dL_dsplat && !aligned(dL_dsplat, 16)))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
+  (void)workspace; (void)workspace_bytes;
+  return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
+                                         reinterpret_cast<const int32_t *>(fwd_state), dL_drgb,
+                                         dL_dsplat, n, (hipStream_t)stream));
+}
+
+}  // extern "C"

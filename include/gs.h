@@ -1,0 +1,170 @@
+/* gs.h - C ABI of the MI355X (gfx950) tile-based differentiable Gaussian-splatting
+ * rasterizer.
+ *
+ * The method (sources by page title):
+ *   "Mitigating SM-Level Load Imbalance in 3D Gaussian Splatting on GPUs"
+ *      section 2.1 Eq. 1 (projection), Eq. 2-3 (alpha and front-to-back
+ *      blending with the 1e-4 transmittance stop), section 4 (persistent
+ *      longest-first tile scheduling, depth-wise chunking with saturation
+ *      signalling, Eq. 4-5 composition, Eq. 6 per-frame chunking policy).
+ *   "What the 3DGS Literature Left on the Table" Step 1 (a)-(e): the 9
+ *      screen-space gradients, exact opacity-aware conic-tile binning, the
+ *      (tile, depth) key sort, 16x16 tiles, the scalar backward accumulator.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
+ *     The library allocates nothing and keeps no global mutable state.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Each call only
+ *     enqueues kernels on it and returns; it never synchronises.
+ *   - Synchronous errors (argument validation, HIP launch errors) return a
+ *     negative gs_status; after an error nothing more is enqueued by that call,
+ *     and outputs are undefined only if a launch error occurred mid-call.
+ *   - All floating-point arithmetic is fp32. Keys, ids, counts and ranges are
+ *     integers.
+ *
+ * Data layouts
+ *   splat record (GS_SPLAT_FLOATS = 12 floats, 48 B, 16-B aligned):
+ *       mx, my, a, b, c, o, r, g, b, tau, depth, 0
+ *     (mx, my) centre in pixels; (a, b, c) the conic Sigma'^-1 = [[a,b],[b,c]];
+ *     o opacity; (r, g, b) colour; tau = 2 ln(255 o), the alpha >= 1/255
+ *     cutoff as a bound on q; depth = camera-space z. Culled: tau = -1, rest 0.
+ *   pixel (px, py) is sampled at (px + 0.5, py + 0.5);
+ *     q = a dx^2 + 2 b dx dy + c dy^2, evaluated in the canonical fp32 form
+ *     fma(c*dy, dy, fma((2b)*dx, dy, (a*dx)*dx)); a pixel is hit iff q <= tau.
+ *   tiles are 16x16 pixels; tiles_x = ceil(W/16), tiles_y = ceil(H/16),
+ *     tile id = ty * tiles_x + tx.
+ *   images are planar: rgb / dL_drgb [3][H][W]; T_final, last [H][W].
+ *   gradient record (GS_GRAD_FLOATS = 9): d/d (mx, my, a, b, c, o, r, g, b).
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARGUMENT = -1, /* bad size, NULL pointer, degree outside 0..3 */
+  GS_ERR_CAPACITY = -2,         /* pair buffer too small (reported on the device) */
+  GS_ERR_WORKSPACE = -3,        /* workspace or fwd_state smaller than required */
+  GS_ERR_HIP = -4,              /* a HIP runtime call or kernel launch failed */
+  GS_ERR_UNSUPPORTED = -5       /* image too large for this build (> 65535 tiles) */
+} gs_status;
+
+#define GS_TILE 16
+#define GS_SPLAT_FLOATS 12
+#define GS_GRAD_FLOATS 9
+
+/* Pinhole camera, passed by HOST pointer. world_to_cam is row-major [R | t]
+ * (camera: +x right, +y down, +z forward). Gaussians with t_z <= znear are
+ * culled. lowpass (px^2) is added to both diagonal entries of Sigma'. */
+typedef struct {
+  int32_t width, height;
+  float fx, fy, cx, cy;
+  float world_to_cam[12];
+  float znear;
+  float lowpass;
+} gs_camera;
+
+/* Tile scheduling knobs, passed by HOST pointer (NULL = defaults:
+ * chunk_mode 1, lambda/beta calibrated for this build, eps 0.10).
+ *   chunk_mode 0: no depth chunking (persistent longest-first queue only)
+ *              1: automatic (Eq. 6 policy, evaluated on the device per frame)
+ *              2: force chunking of the force_h heaviest tiles into force_k chunks
+ *                 (force_h <= 0 means every tile), force_k in {2,4,8,16}. */
+typedef struct {
+  int32_t chunk_mode;
+  int32_t force_k;
+  int32_t force_h;
+  float lambda_;
+  float beta;
+  float eps;
+} gs_sched;
+
+/* Human-readable name of a status (host). */
+const char *gs_strerror(int32_t status);
+
+/* Bytes of scratch the calls below need for n Gaussians, a W x H image and a
+ * pair buffer of pair_capacity entries (host). One workspace may serve all
+ * calls of a frame on one stream; it must not be shared by concurrent calls. */
+size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity);
+
+/* Bytes of the opaque per-frame state that gs_render_fwd writes and
+ * gs_render_bwd reads (per-subtile bounds, chunk plan and chunk partials). */
+size_t gs_fwd_state_size(int32_t width, int32_t height);
+
+/* Projection (Eq. 1 of the load-imbalance page) and SH colour.
+ *   means [n][3], log_scales [n][3], quats [n][4] (w,x,y,z; need not be unit),
+ *   opacities [n] (activated, in (0,1)), sh [n][(deg+1)^2][3] (sh_degree 0..3)
+ *   -> splats [n][12] (record above; every row written).
+ * Colour = sum_k Y_k(d) sh[k] with d the unit direction from the camera centre
+ * to the mean and Y_k the real orthonormal SH basis (no offset, no clamp). */
+int32_t gs_project(int32_t n, const float *means, const float *log_scales, const float *quats,
+                   const float *opacities, const float *sh, int32_t sh_degree,
+                   const gs_camera *cam, float *splats, void *stream);
+
+/* Exact opacity-aware conic-tile binning (Step 1 (b) of the literature page).
+ * A tile is emitted for splat i when the ellipse q <= tau (1 + 2^-10) meets the
+ * tile's pixel-sample hull widened by 2^-8 px; spans are solved per tile row
+ * in closed form with the canonical fp32 operation sequence (bit-exact).
+ *   offsets [n+1] <- exclusive prefix sum of per-splat pair counts;
+ *                    offsets[n] = I, the number of pairs (always written).
+ *   keys [pair_capacity] <- (tile << 32) | float_bits(depth), ids <- splat id,
+ *     in splat-id order, tiles of one splat ascending.
+ *   device_status [1] <- GS_OK, or GS_ERR_CAPACITY when I > pair_capacity; in
+ *     that case keys/ids are not written and the later calls of the frame do
+ *     nothing. The caller reads it after the frame, grows the buffers to
+ *     offsets[n] and runs the frame again. */
+int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
+                     int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Order the pairs by (tile, depth, splat id) and cut the per-tile ranges
+ * (Step 1 (d): depth sort of the visible splats, then a stable sort by tile).
+ *   sorted_ids [pair_capacity] <- splat ids in that order
+ *   sorted_keys [pair_capacity] or NULL <- the keys in that order
+ *   tile_ranges [T][2] <- [start, end) of every tile (empty tiles: start = end
+ *     = number of pairs of lower tiles). */
+int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, const uint64_t *keys,
+                     const int32_t *ids, int64_t pair_capacity, const gs_camera *cam,
+                     uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward blend (Eq. 2-3): per pixel, front to back over its tile's list;
+ * alpha = min(0.99, o exp(-q/2)) on hits (q <= tau); C += alpha T c;
+ * T *= (1 - alpha); the pixel stops after the splat that takes T below 1e-4.
+ * Tiles are served by a persistent longest-first queue; heavy tiles may be
+ * split into depth chunks (Eq. 4-5) with saturation signalling, exactly:
+ * results do not depend on the schedule beyond fp32 rounding.
+ *   rgb [3][H][W], T_final [H][W] <- colour and final transmittance
+ *   last [H][W] <- list entries the pixel consumed (stop index + 1, or the
+ *                  tile's full length when it never stopped)
+ *   fwd_state <- opaque, gs_fwd_state_size bytes, read by gs_render_bwd
+ *   stats [4] or NULL <- += {hits, lane evaluations, wave-splat steps, chunked tiles} */
+int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
+                      const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
+                      float *rgb, float *T_final, int32_t *last, void *fwd_state,
+                      size_t fwd_state_bytes, int64_t *stats, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Backward of the forward blend with respect to the 9 screen-space splat
+ * parameters (Step 1 (a), (e) of the literature page), given dL/dC per pixel.
+ * Each pixel walks its list back from `last`, recovers T by division by
+ * (1 - alpha), keeps the scalar accumulator accum = c_behind . dL/dC, and
+ * forms dL/dalpha = T (c . dL/dC - accum). Per-wave sums go to the output
+ * with float atomics, so low-order bits depend on the atomic order.
+ *   dL_dsplat [n][9] <- fully overwritten (rows of culled splats are 0). */
+int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
+                      const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
+                      const int32_t *last, const void *fwd_state, size_t fwd_state_bytes,
+                      const float *dL_drgb, float *dL_dsplat, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GS_H */
