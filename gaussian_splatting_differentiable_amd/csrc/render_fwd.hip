@@ -67,11 +67,17 @@ __global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
   int wlast = 0;
   unsigned long long nhits = 0, nsteps = 0;
 
+  // prefetch the first batch; each batch's loads are issued one batch ahead
+  int pid = -1;
+  Splat pre;
+  if (start + lane < end) {
+    pid = sorted_ids[start + lane];
+    pre = splats[pid];
+  }
   for (int b = start; b < end && live; b += GS_WAVE) {
-    const int k = b + lane;
     bool cand = false;
-    if (k < end) {
-      Splat s = splats[sorted_ids[k]];
+    if (pid >= 0) {
+      Splat s = pre;
       cand = rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y, st.hx0, st.hx1, st.hy0,
                           st.hy1);
       s.p0.w = 2.0f * s.p0.w;          // 2b, exact
@@ -79,6 +85,12 @@ __global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
       sbuf[lane] = s;
     }
     uint64_t work = __ballot(cand);
+    const int nb = b + GS_WAVE;
+    pid = -1;
+    if (nb + lane < end) {
+      pid = sorted_ids[nb + lane];
+      pre = splats[pid];
+    }
     __syncthreads();
     while (work) {
       const int j = __builtin_ctzll(work);
@@ -89,20 +101,22 @@ __global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
       const bool hit = alive && (q <= s.p2.y);
       const uint64_t hm = __ballot(hit);
       nsteps++;
-      if (hm) {
-        nhits += __popcll(hm);
-        wlast = b + j - start + 1;
-        if (hit) {
-          const float al = fminf(0.99f, __builtin_amdgcn_exp2f(fmaf(q, NEG_HALF_LOG2E, s.p2.w)));
-          const float w = al * T;
-          C0 = fmaf(w, s.p1.z, C0);
-          C1 = fmaf(w, s.p1.w, C1);
-          C2 = fmaf(w, s.p2.x, C2);
-          T = T - w;
-          if (T < 1e-4f) {
-            alive = false;
-            lastv = b + j - start + 1;
-          }
+      if (hm == 0) continue;
+      nhits += __popcll(hm);
+      wlast = b + j - start + 1;
+      // branchless: a missed pixel blends with alpha = 0
+      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+      const float al = hit ? fminf(0.99f, ex) : 0.0f;
+      const float w = al * T;
+      C0 = __builtin_fmaf(w, s.p1.z, C0);
+      C1 = __builtin_fmaf(w, s.p1.w, C1);
+      C2 = __builtin_fmaf(w, s.p2.x, C2);
+      T = T - w;
+      const bool stop = hit && (T < 1e-4f);
+      if (__ballot(stop)) {
+        if (stop) {
+          alive = false;
+          lastv = b + j - start + 1;
         }
         live = __ballot(alive);
         if (!live) break;

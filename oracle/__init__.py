@@ -79,6 +79,7 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = None
+    lib.or_num_threads.argtypes, lib.or_num_threads.restype = [], C.c_int
     _lib = lib
     return lib
 
@@ -89,6 +90,10 @@ def _p(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().or_num_threads())
 
 
 def sh_basis(degree: int, d) -> np.ndarray:

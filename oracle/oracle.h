@@ -80,4 +80,7 @@ void or_render_bwd(const float *splats, const int32_t *sorted_ids, const int32_t
 void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, double lambda_,
                      double beta, double eps, int32_t *h_out, int32_t *k_out);
 
+/* OpenMP threads used by the parallel loops (for reporting). */
+int or_num_threads(void);
+
 #endif

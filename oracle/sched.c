@@ -15,6 +15,9 @@
  */
 #include <math.h>
 #include "oracle.h"
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, double lambda_,
                      double beta, double eps, int32_t *h_out, int32_t *k_out) {
@@ -44,4 +47,13 @@ void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, dou
     *h_out = bh;
     *k_out = bk;
   }
+}
+
+/* Number of OpenMP threads the oracle's parallel loops use (1 without OpenMP). */
+int or_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

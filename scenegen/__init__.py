@@ -104,7 +104,9 @@ def _sh(rng_dc, rng_rest, n, degree):
     sh = np.empty((n, k, 3), np.float32)
     sh[:, 0, :] = rng_dc.uniform(-0.5, 0.5, (n, 3))
     if k > 1:
-        sh[:, 1:, :] = rng_rest.normal(0.0, 0.05, (n, k - 1, 3))
+        rest = rng_rest.standard_normal((n, k - 1, 3), dtype=np.float32)
+        rest *= np.float32(0.05)
+        sh[:, 1:, :] = rest
     return sh
 
 
@@ -149,7 +151,7 @@ def _finish(name, seed_streams, means, log_scale_mu, log_scale_sd, op_mu, op_sd,
     quats = _unit_quats(r_quats, n)
     opac = _sigmoid(r_op.normal(op_mu, op_sd, n))
     sh = _sh(r_dc, r_rest, n, degree)
-    grad = r_grad.standard_normal((3, cam.height, cam.width))
+    grad = r_grad.standard_normal((3, cam.height, cam.width), dtype=np.float32)
     return Scene(name, means.astype(np.float32), ls.astype(np.float32),
                  quats.astype(np.float32), opac.astype(np.float32), sh, degree,
                  cam, grad.astype(np.float32))

@@ -206,3 +206,22 @@ def test_end_to_end_chain_small():
     assert np.quantile(d, 0.999) < 1e-4
     rel = np.linalg.norm(g - ref["grads"], axis=0) / np.linalg.norm(ref["grads"], axis=0)
     assert np.all(rel < 1e-2), rel
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_size_configs(cfg):
+    """Full-size scenes: every stage against the oracle over the whole frame."""
+    gsr = _gsr()
+    sc, ref = reference(cfg)
+    r = gsr.Rasterizer(sc.camera, capacity=16)
+    sp = r.project(dev(sc.means), dev(sc.log_scales), dev(sc.quats), dev(sc.opacities), dev(sc.sh),
+                   sc.sh_degree)
+    check_projection(sc, ref["splats"], host(sp))
+    del r
+    out = run_stages(gsr, sc, ref)
+    check_binning(ref, out)
+    check_sort(ref, out)
+    check_forward(ref, out)
+    check_backward(ref, out)
+    print(f"config {cfg}: pairs {out['I']}, hits {int(out['stats'][0])}, "
+          f"knife-edge pixels {int(ref['fwd']['knife'].sum())}", flush=True)
