@@ -95,11 +95,11 @@ def main():
         gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats)
         if ev is not None:
             ev[1].record(stream)
-        gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, r.keys, r.ids, r.status, r.workspace)
+        gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status, r.workspace)
         if ev is not None:
             ev[2].record(stream)
-        gsr.gs_sort_keys(n, r.splats, r.offsets, r.keys, r.ids, cap, r.cam, None, r.sorted_ids,
-                         r.ranges, r.workspace)
+        gsr.gs_sort_keys(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids, r.ranges,
+                         r.workspace)
         if ev is not None:
             ev[3].record(stream)
         gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T, r.last,

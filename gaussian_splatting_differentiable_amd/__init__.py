@@ -64,7 +64,7 @@ def lib():
     L.gs_fwd_state_size.argtypes, L.gs_fwd_state_size.restype = [i32, i32], sz
     L.gs_project.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P]
     L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, sz, P]
-    L.gs_sort_keys.argtypes = [i32, P, P, P, P, i64, cam_p, P, P, P, P, sz, P]
+    L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, sz, P]
     L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
     for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd"):
@@ -137,10 +137,10 @@ def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace
            "gs_bin_tiles")
 
 
-def gs_sort_keys(n, splats, offsets, keys, ids, capacity, cam, sorted_keys, sorted_ids, ranges,
-                 workspace, stream=None):
-    _check(lib().gs_sort_keys(int(n), _ptr(splats), _ptr(offsets), _ptr(keys), _ptr(ids),
-                              int(capacity), C.byref(cam), _ptr(sorted_keys), _ptr(sorted_ids),
+def gs_sort_keys(n, splats, offsets, capacity, cam, sorted_keys, sorted_ids, ranges, workspace,
+                 stream=None):
+    _check(lib().gs_sort_keys(int(n), _ptr(splats), _ptr(offsets), int(capacity), C.byref(cam),
+                              _ptr(sorted_keys), _ptr(sorted_ids),
                               _ptr(ranges), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_sort_keys")
@@ -218,12 +218,16 @@ class Rasterizer:
         gs_project(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, self.splats)
         return self.splats[:n]
 
-    def bin_and_sort(self, n, want_keys=False):
-        """Bin and sort the current splats; grows the pair buffers on overflow."""
+    def bin_and_sort(self, n, want_keys=False, want_emission=False):
+        """Bin and sort the current splats; grows the pair buffers on overflow.
+
+        want_emission also writes the id-order (keys, ids) list of gs_bin_tiles;
+        want_keys writes the sorted keys."""
         for _ in range(3):
-            gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets, self.keys, self.ids,
+            gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets,
+                         self.keys if want_emission else None, self.ids if want_emission else None,
                          self.status, self.workspace)
-            gs_sort_keys(n, self.splats, self.offsets, self.keys, self.ids, self.capacity, self.cam,
+            gs_sort_keys(n, self.splats, self.offsets, self.capacity, self.cam,
                          self.sorted_keys if want_keys else None, self.sorted_ids, self.ranges,
                          self.workspace)
             if int(self.status.item()) == GS_OK:

@@ -12,10 +12,10 @@ hipError_t gs_launch_project(int n, const float *means, const float *log_scales,
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
                          int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status,
                          int32_t *scan_buf, hipStream_t st);
-size_t gs_sort_ws_bytes(int n, int64_t cap);
+size_t gs_sort_ws_bytes(int n, int64_t cap, int ntiles);
 int gs_scan_buf_elems(int n_max);
-hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, const uint64_t *keys,
-                          int64_t cap, const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
+hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
+                          const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
                           int32_t *ranges, void *ws, hipStream_t st);
 hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, float *rgb, float *T,
@@ -85,7 +85,7 @@ size_t gs_fwd_state_size(int32_t width, int32_t height) {
 size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity) {
   if (n < 0 || width <= 0 || height <= 0 || pair_capacity < 0) return 0;
   const size_t bin = round256((size_t)gs_scan_buf_elems(n) * sizeof(int32_t));
-  const size_t sort = gs_sort_ws_bytes(n, pair_capacity);
+  const size_t sort = gs_sort_ws_bytes(n, pair_capacity, (int)num_tiles(width, height));
   return bin > sort ? bin : sort;
 }
 
@@ -109,7 +109,7 @@ int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64
     return GS_ERR_INVALID_ARGUMENT;
   if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
   if (!offsets || !device_status || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
-  if (pair_capacity > 0 && (!keys || !ids)) return GS_ERR_INVALID_ARGUMENT;
+  if ((keys == nullptr) != (ids == nullptr)) return GS_ERR_INVALID_ARGUMENT;
   if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8))) return GS_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
     return GS_ERR_WORKSPACE;
@@ -117,24 +117,22 @@ int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64
                                   reinterpret_cast<int32_t *>(workspace), (hipStream_t)stream));
 }
 
-int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, const uint64_t *keys,
-                     const int32_t *ids, int64_t pair_capacity, const gs_camera *cam,
-                     uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
-                     void *workspace, size_t workspace_bytes, void *stream) {
+int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
+                     const gs_camera *cam, uint64_t *sorted_keys, int32_t *sorted_ids,
+                     int32_t *tile_ranges, void *workspace, size_t workspace_bytes, void *stream) {
   CamK k;
   if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX || !prep_camera(cam, &k))
     return GS_ERR_INVALID_ARGUMENT;
   if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
   if (!offsets || !tile_ranges || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
-  if (pair_capacity > 0 && (!keys || !ids || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8)) ||
-      (sorted_keys && !aligned(sorted_keys, 8)) || !aligned(tile_ranges, 8))
+  if (pair_capacity > 0 && !sorted_ids) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (sorted_keys && !aligned(sorted_keys, 8)) ||
+      !aligned(tile_ranges, 8))
     return GS_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
     return GS_ERR_WORKSPACE;
-  (void)ids;  // ids are implied by offsets: pair j of splat i has id i
-  return hip_status(gs_launch_sort(n, splats, offsets, keys, pair_capacity, k, sorted_keys,
-                                   sorted_ids, tile_ranges, workspace, (hipStream_t)stream));
+  return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
+                                   tile_ranges, workspace, (hipStream_t)stream));
 }
 
 int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,

@@ -113,26 +113,30 @@ int32_t gs_project(int32_t n, const float *means, const float *log_scales, const
  * in closed form with the canonical fp32 operation sequence (bit-exact).
  *   offsets [n+1] <- exclusive prefix sum of per-splat pair counts;
  *                    offsets[n] = I, the number of pairs (always written).
- *   keys [pair_capacity] <- (tile << 32) | float_bits(depth), ids <- splat id,
- *     in splat-id order, tiles of one splat ascending.
+ *   keys, ids [pair_capacity] or both NULL <- (tile << 32) | float_bits(depth)
+ *     and the splat id of every pair, in splat-id order, tiles of one splat
+ *     ascending. The frame does not need them (gs_sort_keys emits the pairs
+ *     again, directly in depth order); they expose the emission for checking.
  *   device_status [1] <- GS_OK, or GS_ERR_CAPACITY when I > pair_capacity; in
- *     that case keys/ids are not written and the later calls of the frame do
- *     nothing. The caller reads it after the frame, grows the buffers to
+ *     that case nothing is emitted and the later calls of the frame do nothing.
+ *     The caller reads it after the frame, grows its pair buffers to at least
  *     offsets[n] and runs the frame again. */
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
                      int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Order the pairs by (tile, depth, splat id) and cut the per-tile ranges
- * (Step 1 (d): depth sort of the visible splats, then a stable sort by tile).
+ * (Step 1 (d), Figure 5 of the literature page): stable radix sort of the
+ * visible splats (those with offsets[i+1] > offsets[i]) by fp32 depth bits,
+ * emission of their tile keys in that order (the same canonical spans as
+ * gs_bin_tiles), then a stable radix sort by tile id.
  *   sorted_ids [pair_capacity] <- splat ids in that order
- *   sorted_keys [pair_capacity] or NULL <- the keys in that order
+ *   sorted_keys [pair_capacity] or NULL <- (tile << 32) | float_bits(depth)
  *   tile_ranges [T][2] <- [start, end) of every tile (empty tiles: start = end
  *     = number of pairs of lower tiles). */
-int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, const uint64_t *keys,
-                     const int32_t *ids, int64_t pair_capacity, const gs_camera *cam,
-                     uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
-                     void *workspace, size_t workspace_bytes, void *stream);
+int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
+                     const gs_camera *cam, uint64_t *sorted_keys, int32_t *sorted_ids,
+                     int32_t *tile_ranges, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Forward blend (Eq. 2-3): per pixel, front to back over its tile's list;
  * alpha = min(0.99, o exp(-q/2)) on hits (q <= tau); C += alpha T c;

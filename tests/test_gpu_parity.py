@@ -78,7 +78,7 @@ def run_stages(gsr, sc, ref, capacity=None, sched=None):
     r = gsr.Rasterizer(cam, capacity=cap, sched=sched)
     r._ensure(n, cap)
     r.splats[:n].copy_(dev(ref["splats"]))
-    I = r.bin_and_sort(n, want_keys=True)
+    I = r.bin_and_sort(n, want_keys=True, want_emission=True)
     out = dict(I=I, offsets=host(r.offsets), keys=host(r.keys)[:I].view(np.uint64),
                ids=host(r.ids)[:I], sorted_keys=host(r.sorted_keys)[:I].view(np.uint64),
                sorted_ids=host(r.sorted_ids)[:I], ranges=host(r.ranges))
@@ -168,8 +168,8 @@ def test_capacity_overflow_reports_and_recovers():
     r._ensure(sc.n, 16)
     r.splats[:sc.n].copy_(dev(ref["splats"]))
     gsr.gs_bin_tiles(sc.n, r.splats, r.cam, 16, r.offsets, r.keys, r.ids, r.status, r.workspace)
-    gsr.gs_sort_keys(sc.n, r.splats, r.offsets, r.keys, r.ids, 16, r.cam, None, r.sorted_ids,
-                     r.ranges, r.workspace)
+    gsr.gs_sort_keys(sc.n, r.splats, r.offsets, 16, r.cam, None, r.sorted_ids, r.ranges,
+                     r.workspace)
     assert int(host(r.status)[0]) == gsr.GS_ERR_CAPACITY
     assert int(host(r.offsets)[sc.n]) == npairs
     assert np.all(host(r.ranges) == 0)          # later calls do nothing for the frame
