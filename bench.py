@@ -82,8 +82,10 @@ def main():
     torch.cuda.synchronize()
     stats = r.stats.cpu().numpy()
     hits = int(stats[0])
-    print(f"[bench] pairs {npairs}, hits {hits}, lane evaluations {int(stats[1])}",
-          file=sys.stderr, flush=True)
+    plan = r.fwd_state[:8].cpu().numpy().view(np.int32)  # (chunked tiles h, chunks k)
+    chunked, chunks = int(plan[0]), int(plan[1])
+    print(f"[bench] pairs {npairs}, hits {hits}, lane evaluations {int(stats[1])}, "
+          f"chunked tiles {chunked} x {chunks}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     cap = r.capacity
@@ -164,7 +166,8 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{sc.name}: {n} Gaussians, SH degree {sc.sh_degree}, "
                                f"{cam.width}x{cam.height} image, {cam.num_tiles} tiles",
-                   "pairs": npairs, "hits": hits},
+                   "pairs": npairs, "hits": hits, "chunk_mode": args.chunk_mode,
+                   "chunked_tiles": chunked, "chunks_per_tile": chunks},
         "ms": {k: round(v, 4) for k, v in ms.items()},
         "ms_min": {k: round(v, 4) for k, v in ms_min.items()},
         "ms_raster_fwd_bwd": round(ms_raster, 4),

@@ -88,8 +88,15 @@ def make_camera(cam) -> GsCamera:
     return c
 
 
-def make_sched(chunk_mode: int = 1, force_k: int = 0, force_h: int = 0, lambda_: float = 0.0,
-               beta: float = 0.0, eps: float = 0.10) -> GsSched:
+# Defaults of the per-frame chunking policy (Eq. 6 constants; the page does not
+# print lambda and beta, these are calibrated for this build).
+DEFAULT_LAMBDA, DEFAULT_BETA, DEFAULT_EPS = 512.0, 0.25, 0.10
+HK_MAX = 4096  # cap on h*k, the chunks of chunked tiles per frame
+
+
+def make_sched(chunk_mode: int = 1, force_k: int = 0, force_h: int = 0,
+               lambda_: float = DEFAULT_LAMBDA, beta: float = DEFAULT_BETA,
+               eps: float = DEFAULT_EPS) -> GsSched:
     return GsSched(int(chunk_mode), int(force_k), int(force_h), float(lambda_), float(beta),
                    float(eps))
 

@@ -4,7 +4,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "gs_common.h"
+#include "render_common.h"
 
 hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
                              const float *opac, const float *sh, int degree, const CamK &cam,
@@ -18,12 +18,13 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
                           int32_t *ranges, void *ws, hipStream_t st);
 hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
-                                const int32_t *ranges, const CamK &cam, float *rgb, float *T,
-                                int32_t *last, int32_t *sub_last, int64_t *stats, hipStream_t st);
+                                const int32_t *ranges, const CamK &cam, const gs_sched &sched,
+                                float *rgb, float *T, int32_t *last, void *fwd_state,
+                                int64_t *stats, int workers_waves, hipStream_t st);
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
-                                const int32_t *last, const int32_t *sub_last, const float *dL,
-                                float *grads, int n, hipStream_t st);
+                                const int32_t *last, const void *fwd_state, const float *dL,
+                                float *grads, int n, int workers_waves, hipStream_t st);
 
 namespace {
 
@@ -61,6 +62,27 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
 
+// Persistent workers to launch: one wavefront per wave slot of the current
+// device (32 per CU), 0 on error.
+int worker_waves() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus > 0 ? cus * 32 : 0;
+}
+
+gs_sched default_sched() {
+  gs_sched s;
+  s.chunk_mode = 1;
+  s.force_k = 0;
+  s.force_h = 0;
+  s.lambda_ = 512.0f;
+  s.beta = 0.25f;
+  s.eps = 0.10f;
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,8 +100,8 @@ const char *gs_strerror(int32_t s) {
 }
 
 size_t gs_fwd_state_size(int32_t width, int32_t height) {
-  if (width <= 0 || height <= 0) return 0;
-  return round256((size_t)num_tiles(width, height) * 4 * sizeof(int32_t));
+  if (width <= 0 || height <= 0 || num_tiles(width, height) > GS_MAX_TILES) return 0;
+  return fwd_layout((int)num_tiles(width, height)).total;
 }
 
 size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity) {
@@ -147,10 +169,16 @@ int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
   if (n > 0 && (!splats || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
   if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8)) return GS_ERR_INVALID_ARGUMENT;
   if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
-  (void)sched; (void)workspace; (void)workspace_bytes;
-  return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, rgb, T_final, last,
-                                         reinterpret_cast<int32_t *>(fwd_state), stats,
-                                         (hipStream_t)stream));
+  if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
+  const gs_sched sc = sched ? *sched : default_sched();
+  if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
+      !(sc.beta >= 0.0f))
+    return GS_ERR_INVALID_ARGUMENT;
+  const int workers = worker_waves();
+  if (workers <= 0) return GS_ERR_HIP;
+  (void)workspace; (void)workspace_bytes;
+  return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
+                                         last, fwd_state, stats, workers, (hipStream_t)stream));
 }
 
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -167,10 +195,13 @@ int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
       (dL_dsplat && !aligned(dL_dsplat, 16)))
     return GS_ERR_INVALID_ARGUMENT;
   if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
+  if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
+  const int workers = worker_waves();
+  if (workers <= 0) return GS_ERR_HIP;
   (void)workspace; (void)workspace_bytes;
   return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
-                                         reinterpret_cast<const int32_t *>(fwd_state), dL_drgb,
-                                         dL_dsplat, n, (hipStream_t)stream));
+                                         fwd_state, dL_drgb, dL_dsplat, n, workers,
+                                         (hipStream_t)stream));
 }
 
 }  // extern "C"

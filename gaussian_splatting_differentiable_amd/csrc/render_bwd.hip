@@ -9,131 +9,140 @@
 // for missed pixels and one canonical q shared with the forward pass; Step 6.3
 // the per-splat term alpha T (c . dL/dC - accum), with log2(o) folded into the
 // exponent and o divided back out once after the sum.
+// "Mitigating SM-Level Load Imbalance in 3D Gaussian Splatting on GPUs",
+// section 4: the same persistent longest-first queue as the forward pass; a
+// chunk of a heavy tile is differentiated on its own from the forward pass's
+// chunk state: it starts from the transmittance after its last processed
+// splat, T_end, with accum = (sum over later chunks of C_chunk . dL/dC) / T_end.
 //
-// gfx950 mapping: one wavefront per 8x8 sub-tile, LDS-staged batches of 64
-// splats walked back to front; the next batch's records are fetched while the
-// current one is processed; the per-wave cull ballot skips splats that miss the
-// sub-tile and a second ballot skips splats no live pixel hits.
-#include "gs_common.h"
+// gfx950 mapping: one wavefront per item (an 8x8 quarter), LDS-staged batches
+// of 64 splats walked back to front with the next batch fetched ahead; the
+// per-wave cull ballot skips splats that miss the quarter and a second ballot
+// skips splats no live pixel hits.
+#include "render_common.h"
 #include "wave_reduce.h"
 
 namespace {
 
 constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 
-__global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n) {
+// Zero the gradient output and rewind the backward queues of this frame.
+__global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n,
+                                              int32_t *__restrict__ bwd_heads) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i <= GS_GROUPS) bwd_heads[i * GS_HEAD_STRIDE] = 0;
   const int64_t n4 = n / 4;
   if (i < n4) reinterpret_cast<float4 *>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (i < n - 4 * n4) p[4 * n4 + i] = 0.0f;
 }
 
-__global__ void __launch_bounds__(GS_WAVE) k_render_bwd(
-    const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
-    const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
-    const int32_t *__restrict__ last, const int32_t *__restrict__ sub_last,
-    const float *__restrict__ dL, float *__restrict__ grads) {
-  __shared__ Splat sbuf[GS_WAVE];
-  __shared__ int sid[GS_WAVE];
-  const int item = blockIdx.x;
-  const int tile = item >> 2, quad = item & 3;
-  const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
-  const int x0 = tx * 16 + (quad & 1) * 8, y0 = ty * 16 + (quad >> 1) * 8;
-  if (x0 >= cam.width || y0 >= cam.height) return;
-  const float hx0 = (float)x0 + 0.5f, hx1 = (float)min(x0 + 7, cam.width - 1) + 0.5f;
-  const float hy0 = (float)y0 + 0.5f, hy1 = (float)min(y0 + 7, cam.height - 1) + 0.5f;
-  const int lane = threadIdx.x;
-  const int px = x0 + (lane & 7), py = y0 + (lane >> 3);
-  const bool inside = px < cam.width && py < cam.height;
-  const int start = ranges[tile].x;
-  const int64_t P = (int64_t)cam.width * cam.height;
-  const int64_t p = (int64_t)py * cam.width + px;
-  float T = 1.0f, g0 = 0.f, g1 = 0.f, g2 = 0.f;
-  int lastp = 0;
-  if (inside) {
-    T = Tfin[p];
-    lastp = last[p];
-    g0 = dL[p];
-    g1 = dL[P + p];
-    g2 = dL[2 * P + p];
-  }
-  // walk back only from the last splat any lane of this sub-tile blended
-  int kmax = lastp;
+__device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) kmax = max(kmax, __shfl_xor(kmax, d, GS_WAVE));
-  kmax = min(kmax, sub_last[item]);
-  const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
-  const int comp = comp_of_lane(lane);
-  float accum = 0.0f;
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, GS_WAVE));
+  return v;
+}
 
-  // prefetch the first (highest) batch
-  int hiE = start + kmax;
-  int lo = max(start, hiE - GS_WAVE);
-  int pid = -1;
-  Splat pre;
-  if (lo + lane < hiE) {
-    pid = sorted_ids[lo + lane];
-    pre = splats[pid];
+constexpr int RB = 2;                // 64-splat rounds per batch
+constexpr int BATCH = RB * GS_WAVE;  // splats per staged batch
+
+// Two-stage load pipeline for the back-to-front walk: the ids of the batch
+// after next and the records of the next batch are in flight while a batch is
+// processed. Slots outside the range carry id -1 (and read record 0).
+__device__ __forceinline__ void load_ids(const int32_t *__restrict__ sids, int lo, int hi,
+                                         int (&id)[RB]) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int r = 0; r < RB; r++) {
+    const int e = lo + r * GS_WAVE + lane;
+    id[r] = e < hi ? sids[e] : -1;
   }
-  while (hiE > start) {
-    // stage the prefetched batch [lo, hiE)
-    const Splat s_in = pre;
-    const int id_in = pid;
-    bool cand = false;
-    if (id_in >= 0) {
-      cand = rect_may_hit(s_in.p0.x, s_in.p0.y, s_in.p0.z, s_in.p0.w, s_in.p1.x, s_in.p2.y, hx0,
-                          hx1, hy0, hy1);
-      Splat s = s_in;
+}
+
+__device__ __forceinline__ void load_recs(const Splat *__restrict__ splats, const int (&id)[RB],
+                                          Splat (&rec)[RB]) {
+#pragma unroll
+  for (int r = 0; r < RB; r++) rec[r] = splats[id[r] >= 0 ? id[r] : 0];
+}
+
+// Walk positions [cs, cs + kmax) back to front for one quarter. Lane state:
+// T (transmittance after the lane's last consumed entry), accum, and lastp,
+// the number of entries the lane consumed from cs.
+__device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
+                                          const int32_t *__restrict__ sids, int cs, int kmax,
+                                          const SubTile &st, float fx, float fy, int lastp,
+                                          float T, float accum, float g0, float g1, float g2,
+                                          Splat *sbuf, int *sid, float *__restrict__ grads) {
+  const int lane = __lane_id();
+  const int comp = comp_of_lane(lane);
+  int hiE = cs + kmax;
+  int lo = max(cs, hiE - BATCH);
+  int idc[RB], idn[RB];
+  Splat rec[RB];
+  if (hiE > cs) {
+    load_ids(sids, lo, hiE, idc);
+    load_recs(splats, idc, rec);
+    load_ids(sids, max(cs, lo - BATCH), lo, idn);
+  }
+  while (hiE > cs) {
+    uint64_t work[RB];
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+      Splat s = rec[r];
+      const bool cand = idc[r] >= 0 && rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x,
+                                                    s.p2.y, st.hx0, st.hx1, st.hy0, st.hy1);
       s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
-      sbuf[lane] = s;
-      sid[lane] = id_in;
+      sbuf[r * GS_WAVE + lane] = s;
+      sid[r * GS_WAVE + lane] = idc[r];
+      work[r] = __ballot(cand);
     }
-    uint64_t work = __ballot(cand);
-    // issue the loads of the next (lower) batch
-    const int nhi = lo, nlo = max(start, lo - GS_WAVE);
-    pid = -1;
-    if (nlo + lane < nhi) {
-      pid = sorted_ids[nlo + lane];
-      pre = splats[pid];
-    }
+    const int nhi = lo, nlo = max(cs, lo - BATCH);
+    // records of [nlo, nhi), ids of the batch below it
+#pragma unroll
+    for (int r = 0; r < RB; r++) idc[r] = idn[r];
+    load_recs(splats, idc, rec);
+    load_ids(sids, max(cs, nlo - BATCH), nlo, idn);
     __syncthreads();
-    while (work) {
-      const int j = 63 - __builtin_clzll(work);  // back to front
-      work &= ~(1ull << j);
-      const Splat s = sbuf[j];
-      const int rel = lo + j - start;
-      const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
-      const float dx = fx - s.p0.x, dy = fy - s.p0.y;
-      const float adx = a * dx, cdy = c * dy;
-      const float q = __builtin_fmaf(cdy, dy, __builtin_fmaf((2.0f * b) * dx, dy, adx * dx));
-      const bool hit = inside && rel < lastp && (q <= s.p2.y);
-      if (__ballot(hit) == 0) continue;
-      // branchless: a missed pixel takes alpha = 0, which leaves T and accum
-      // unchanged and contributes zero to every sum
-      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-      const float oG = hit ? ex : 0.0f;                 // o G
-      const float al = fminf(0.99f, oG);
-      T = T * __builtin_amdgcn_rcpf(1.0f - al);        // T before this splat
-      const float cg = __builtin_fmaf(s.p1.z, g0, __builtin_fmaf(s.p1.w, g1, s.p2.x * g2));
-      const float diff = cg - accum;
-      const float dal = T * diff;                       // dL/dalpha
-      accum = __builtin_fmaf(al, diff, accum);
-      const float w = al * T;
-      const bool live_g = oG < 0.99f;                   // clamped alpha passes no gradient
-      const float m = live_g ? al * dal : 0.0f;         // -2 dL/dq
-      float gr[9];
-      gr[0] = m * __builtin_fmaf(b, dy, adx);           // dq/dmx = -2 (a dx + b dy)
-      gr[1] = m * __builtin_fmaf(b, dx, cdy);
-      gr[2] = (-0.5f * m) * (dx * dx);
-      gr[3] = -(m * (dx * dy));
-      gr[4] = (-0.5f * m) * (dy * dy);
-      gr[5] = live_g ? oG * dal : 0.0f;                 // o G dL/dalpha
-      gr[6] = w * g0;
-      gr[7] = w * g1;
-      gr[8] = w * g2;
-      float out = reduce_scatter9(gr);
-      if (comp == 5) out *= __builtin_amdgcn_rcpf(s.p1.y);
-      if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[j] + comp], out);
+#pragma unroll
+    for (int rr = RB - 1; rr >= 0; rr--) {
+      while (work[rr]) {
+        const int j = 63 - __builtin_clzll(work[rr]);  // back to front
+        work[rr] &= ~(1ull << j);
+        const int slot = rr * GS_WAVE + j;
+        const Splat s = sbuf[slot];
+        const int rel = lo + slot - cs;
+        const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
+        const float dx = fx - s.p0.x, dy = fy - s.p0.y;
+        const float adx = a * dx, cdy = c * dy;
+        const float q = __builtin_fmaf(cdy, dy, __builtin_fmaf((2.0f * b) * dx, dy, adx * dx));
+        const bool hit = rel < lastp && (q <= s.p2.y);
+        if (__ballot(hit) == 0) continue;
+        // branchless: a missed pixel takes alpha = 0, which leaves T and accum
+        // unchanged and contributes zero to every sum
+        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+        const float oG = hit ? ex : 0.0f;  // o G
+        const float al = fminf(0.99f, oG);
+        T = T * __builtin_amdgcn_rcpf(1.0f - al);  // T before this splat
+        const float cg = __builtin_fmaf(s.p1.z, g0, __builtin_fmaf(s.p1.w, g1, s.p2.x * g2));
+        const float diff = cg - accum;
+        const float dal = T * diff;  // dL/dalpha
+        accum = __builtin_fmaf(al, diff, accum);
+        const float w = al * T;
+        const bool live_g = oG < 0.99f;  // a clamped alpha passes no gradient
+        const float m = live_g ? al * dal : 0.0f;  // -2 dL/dq
+        float gr[9];
+        gr[0] = m * __builtin_fmaf(b, dy, adx);  // dq/dmx = -2 (a dx + b dy)
+        gr[1] = m * __builtin_fmaf(b, dx, cdy);
+        gr[2] = (-0.5f * m) * (dx * dx);
+        gr[3] = -(m * (dx * dy));
+        gr[4] = (-0.5f * m) * (dy * dy);
+        gr[5] = live_g ? oG * dal : 0.0f;  // o G dL/dalpha
+        gr[6] = w * g0;
+        gr[7] = w * g1;
+        gr[8] = w * g2;
+        float out = reduce_scatter9(gr);
+        if (comp == 5) out *= __builtin_amdgcn_rcpf(s.p1.y);
+        if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[slot] + comp], out);
+      }
     }
     __syncthreads();
     hiE = nhi;
@@ -141,18 +150,93 @@ __global__ void __launch_bounds__(GS_WAVE) k_render_bwd(
   }
 }
 
+__global__ void __launch_bounds__(GS_WAVE) __attribute__((amdgpu_waves_per_eu(1, 4))) k_render_bwd(
+    const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
+    const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
+    const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
+    const float *__restrict__ dL, float *__restrict__ grads) {
+  __shared__ Splat sbuf[BATCH];
+  __shared__ int sid[BATCH];
+  FwdState fs = fwd_state_at(state, ntiles);
+  const int k = fs.hdr->k, nA = fs.hdr->nA;
+  const int64_t P = (int64_t)cam.width * cam.height;
+  const int lane = __lane_id();
+  int g = blockIdx.x % GS_GROUPS, tried = 0;
+  bool chunks_done = nA == 0;
+  for (;;) {
+    // the pass-B chunk items (items[nA, 2nA)), then the group queues
+    const int t = next_item(fs, 1, nA, g, tried, chunks_done);
+    if (t < 0) break;
+    const int it = fs.items[nA + t];
+    const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
+    const int idx = item_index(it);
+    const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
+    const SubTile st = subtile_of(tile, quad, cam);
+    if (st.empty) continue;
+    const int px = st.x0 + (lane & 7), py = st.y0 + (lane >> 3);
+    const bool inside = px < cam.width && py < cam.height;
+    const int64_t pix = (int64_t)py * cam.width + px;
+    const int2 rg = ranges[tile];
+    float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+    if (inside) {
+      g0 = dL[pix];
+      g1 = dL[P + pix];
+      g2 = dL[2 * P + pix];
+    }
+    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
+    if (kind == ITEM_PLAIN) {
+      float T = 1.0f;
+      int lastp = 0;
+      if (inside) {
+        T = Tfin[pix];
+        lastp = last[pix];
+      }
+      const int kmax = min(wave_max(lastp), fs.sub_last[tile * 4 + quad]);
+      walk_back(splats, sorted_ids, rg.x, kmax, st, fx, fy, lastp, T, 0.0f, g0, g1, g2, sbuf,
+                sid, grads);
+      continue;
+    }
+    // a chunk of a heavy tile
+    int cs, ce;
+    chunk_range(rg.x, rg.y, p, k, cs, ce);
+    const int ci = chunk_index(idx, p, quad, k);
+    const int64_t cp = (int64_t)ci * 64 + lane;
+    int lb = inside ? fs.LB[cp] : -1;
+    float T = 1.0f, accum = 0.0f;
+    if (lb > 0) {
+      T = fs.TB[cp];
+      float behind = 0.0f;  // sum over later chunks of C . dL/dC
+      for (int q = p + 1; q < k; q++) {
+        const int64_t c2 = (int64_t)chunk_index(idx, q, quad, k) * 64 + lane;
+        if (fs.LB[c2] < 0) break;
+        behind = __builtin_fmaf(fs.CB[3 * c2], g0,
+                                __builtin_fmaf(fs.CB[3 * c2 + 1], g1,
+                                               __builtin_fmaf(fs.CB[3 * c2 + 2], g2, behind)));
+      }
+      accum = behind / T;
+    } else {
+      lb = 0;
+    }
+    const int kmax = min(wave_max(lb), fs.chunk_last[ci]);
+    walk_back(splats, sorted_ids, cs, kmax, st, fx, fy, lb, T, accum, g0, g1, g2, sbuf, sid,
+              grads);
+  }
+}
+
 }  // namespace
 
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
-                                const int32_t *last, const int32_t *sub_last, const float *dL,
-                                float *grads, int n, hipStream_t st) {
+                                const int32_t *last, const void *fwd_state, const float *dL,
+                                float *grads, int n, int workers_waves, hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
-  if (ng > 0)
-    hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng);
-  const int items = cam.tiles_x * cam.tiles_y * 4;
-  hipLaunchKernelGGL(k_render_bwd, dim3(items), dim3(GS_WAVE), 0, st,
+  const int ntiles = cam.tiles_x * cam.tiles_y;
+  const FwdState fs = fwd_state_at(const_cast<void *>(fwd_state), ntiles);
+  hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng,
+                     queue_head(fs, 1, 0));
+  hipLaunchKernelGGL(k_render_bwd, dim3(workers_waves), dim3(GS_WAVE), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
-                     reinterpret_cast<const int2 *>(ranges), cam, T, last, sub_last, dL, grads);
+                     reinterpret_cast<const int2 *>(ranges), cam, T, last,
+                     reinterpret_cast<char *>(const_cast<void *>(fwd_state)), ntiles, dL, grads);
   return hipGetLastError();
 }

@@ -2,156 +2,401 @@
 //
 // "Mitigating SM-Level Load Imbalance in 3D Gaussian Splatting on GPUs",
 // section 2.1, Eq. 2-3: alpha = o exp(-q/2); C = sum c alpha T; a pixel stops
-// blending once T falls below 1e-4.
+// blending once T falls below 1e-4. Section 4: a persistent kernel takes work
+// from a longest-first queue; the heaviest tiles are split into contiguous
+// depth chunks (Eq. 4-5) with saturation signalling.
 // "What the 3DGS Literature Left on the Table": Step 1 (b) the alpha >= 1/255
 // cutoff as q <= tau; Step 1 (c) sub-tile culling of staged splat batches with a
-// vote (ballot) and a find-first-set worklist; Step 1 (e) base-2 exponential;
-// Step 5 branch-light blending with one canonical q for forward and backward;
-// Step 6.3 log2(o) folded into the exponent.
+// ballot and a find-first-set worklist; Step 1 (e) base-2 exponential; Step 5
+// branchless blending with one canonical q shared with the backward; Step 6.3
+// log2(o) folded into the exponent.
 //
-// gfx950 mapping: one wavefront owns one 8x8 sub-tile (64 lanes = 64 pixels) and
-// walks its tile's list in batches of 64 splats that the lanes stage into LDS
-// (one record per lane, three 16-byte loads). Each lane tests its staged splat
-// against the sub-tile's sample rectangle; the ballot of those tests is the
-// worklist, walked on the scalar unit. No barrier is needed: each wave is a
-// workgroup.
-#include "gs_common.h"
+// gfx950 mapping: every workgroup is one wavefront, a persistent worker that
+// pops items (an 8x8 quarter of a tile or of a chunk) until the queues are
+// empty. A worker walks its list in batches of 128 splats staged in LDS (two
+// records per lane, three 16-byte loads each, the next batch in flight while
+// the current one is blended); each lane tests its staged splats against the
+// quarter's sample rectangle and the ballots of those tests are the worklist,
+// walked on the scalar unit.
+//
+// Exact chunking (a reading of section 4.2: chunks that start at T = 1 can stop
+// later than the sequential renderer, so the composition is made exact):
+//   pass A, chunk p: per pixel the product P_p of (1 - alpha) over the chunk,
+//     stopping once P_p < 1e-4; if every pixel of the quarter stops, the chunk
+//     lowers sat[] with atomicMin and later chunks give up (checked per batch).
+//   pass B, chunk p: waits for pass A of chunks 0..p-1 (queued earlier, so
+//     already taken by running workers), starts from T_in = prod_{q<p} P_q and
+//     blends with the exact stop rule, writing (C, T, consumed) of the chunk.
+//   the last pass-B worker of a quarter sums the chunk colours (Eq. 5 with the
+//     transmittance already applied) and writes the pixel outputs.
+#include "render_common.h"
 
 namespace {
 
 constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
+constexpr float T_STOP = 1e-4f;
+constexpr int RB = 2;                 // 64-splat rounds per batch
+constexpr int BATCH = RB * GS_WAVE;   // splats per staged batch
 
-struct SubTile {
-  int tile, quad, x0, y0;
-  float hx0, hx1, hy0, hy1;  // sample hull of the sub-tile
-  bool empty;
+struct Px {
+  float fx, fy;
+  bool inside;
+  int64_t p;  // pixel index
 };
 
-__device__ __forceinline__ SubTile subtile_of(int item, const CamK &cam) {
-  SubTile st;
-  st.tile = item >> 2;
-  st.quad = item & 3;
-  const int tx = st.tile % cam.tiles_x, ty = st.tile / cam.tiles_x;
-  st.x0 = tx * 16 + (st.quad & 1) * 8;
-  st.y0 = ty * 16 + (st.quad >> 1) * 8;
-  st.empty = st.x0 >= cam.width || st.y0 >= cam.height;
-  st.hx0 = (float)st.x0 + 0.5f;
-  st.hx1 = (float)min(st.x0 + 7, cam.width - 1) + 0.5f;
-  st.hy0 = (float)st.y0 + 0.5f;
-  st.hy1 = (float)min(st.y0 + 7, cam.height - 1) + 0.5f;
-  return st;
+__device__ __forceinline__ Px pixel_of(const SubTile &st, const CamK &cam) {
+  Px x;
+  const int lane = __lane_id();
+  const int px = st.x0 + (lane & 7), py = st.y0 + (lane >> 3);
+  x.inside = px < cam.width && py < cam.height;
+  x.fx = (float)px + 0.5f;
+  x.fy = (float)py + 0.5f;
+  x.p = (int64_t)py * cam.width + px;
+  return x;
+}
+
+// Stage one splat record for the worklist: 2b and log2(o) replace b and pad.
+__device__ __forceinline__ bool stage(Splat s, const SubTile &st, Splat *slot) {
+  const bool cand = rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y, st.hx0, st.hx1,
+                                 st.hy0, st.hy1);
+  s.p0.w = 2.0f * s.p0.w;
+  s.p2.w = __log2f(s.p1.y);
+  *slot = s;
+  return cand;
+}
+
+// Two-stage load pipeline over a splat list: ids two batches ahead, records one
+// batch ahead, so neither the id load nor the dependent record load stalls the
+// batch being blended. Slots past the end carry id -1 (and read record 0).
+struct Pipe {
+  int idc[RB];    // ids of the batch whose records are in rec
+  int idn[RB];    // ids of the batch after it
+  Splat rec[RB];
+};
+
+__device__ __forceinline__ void load_ids(const int32_t *__restrict__ sids, int b, int ce,
+                                         int (&id)[RB]) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int r = 0; r < RB; r++) {
+    const int e = b + r * GS_WAVE + lane;
+    id[r] = e < ce ? sids[e] : -1;
+  }
+}
+
+__device__ __forceinline__ void load_recs(const Splat *__restrict__ splats, const int (&id)[RB],
+                                          Splat (&rec)[RB]) {
+#pragma unroll
+  for (int r = 0; r < RB; r++) rec[r] = splats[id[r] >= 0 ? id[r] : 0];
+}
+
+__device__ __forceinline__ void pipe_start(Pipe &pp, const Splat *__restrict__ splats,
+                                           const int32_t *__restrict__ sids, int cs, int ce) {
+  load_ids(sids, cs, ce, pp.idc);
+  load_recs(splats, pp.idc, pp.rec);
+  load_ids(sids, cs + BATCH, ce, pp.idn);
+}
+
+// After the batch at b is staged: start the records of b + BATCH and the ids of
+// b + 2 BATCH.
+__device__ __forceinline__ void pipe_advance(Pipe &pp, const Splat *__restrict__ splats,
+                                             const int32_t *__restrict__ sids, int b, int ce) {
+#pragma unroll
+  for (int r = 0; r < RB; r++) pp.idc[r] = pp.idn[r];
+  load_recs(splats, pp.idc, pp.rec);
+  load_ids(sids, b + 2 * BATCH, ce, pp.idn);
+}
+
+struct Blend {
+  float C0, C1, C2, T;
+  int consumed;  // list entries consumed (relative to the range start)
+  int wlast;     // 1 + last position any lane hit (relative), 0 if none
+};
+
+// Blend [cs, ce) into pixels that start with transmittance T0 (alive when
+// T0 >= 1e-4).
+__device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
+                                             const int32_t *__restrict__ sids, int cs, int ce,
+                                             const SubTile &st, const Px &x, float T0,
+                                             Splat *sbuf, unsigned long long &nhits,
+                                             unsigned long long &nsteps) {
+  Blend r;
+  r.C0 = r.C1 = r.C2 = 0.0f;
+  r.T = T0;
+  r.consumed = ce - cs;
+  r.wlast = 0;
+  bool alive = x.inside && T0 >= T_STOP;
+  if (!alive) r.consumed = 0;
+  uint64_t live = __ballot(alive);
+  const int lane = __lane_id();
+  Pipe pp;
+  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce);
+  for (int b = cs; b < ce && live; b += BATCH) {
+    uint64_t work[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; rr++) {
+      const bool cand = stage(pp.rec[rr], st, &sbuf[rr * GS_WAVE + lane]) && pp.idc[rr] >= 0;
+      work[rr] = __ballot(cand);
+    }
+    pipe_advance(pp, splats, sids, b, ce);
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < RB; rr++) {
+      while (work[rr] && live) {
+        const int j = __builtin_ctzll(work[rr]);
+        work[rr] &= work[rr] - 1;
+        const Splat s = sbuf[rr * GS_WAVE + j];
+        const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
+        const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
+        const bool hit = alive && (q <= s.p2.y);
+        const uint64_t hm = __ballot(hit);
+        nsteps++;
+        if (hm == 0) continue;
+        const int pos = b + rr * GS_WAVE + j - cs;
+        nhits += __popcll(hm);
+        r.wlast = pos + 1;
+        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+        const float al = hit ? fminf(0.99f, ex) : 0.0f;
+        const float w = al * r.T;
+        r.C0 = __builtin_fmaf(w, s.p1.z, r.C0);
+        r.C1 = __builtin_fmaf(w, s.p1.w, r.C1);
+        r.C2 = __builtin_fmaf(w, s.p2.x, r.C2);
+        r.T = r.T - w;
+        const bool stop = hit && (r.T < T_STOP);
+        if (__ballot(stop)) {
+          if (stop) {
+            alive = false;
+            r.consumed = pos + 1;
+          }
+          live = __ballot(alive);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  (void)lane;
+  return r;
+}
+
+// Pass A: transmittance product over the chunk; gives up when sat < chunk.
+__device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
+                                               const int32_t *__restrict__ sids, int cs, int ce,
+                                               const SubTile &st, const Px &x, Splat *sbuf,
+                                               const int32_t *sat, int chunk, bool &gave_up,
+                                               unsigned long long &nsteps) {
+  float P = 1.0f;
+  bool alive = x.inside;
+  uint64_t live = __ballot(alive);
+  gave_up = false;
+  const int lane = __lane_id();
+  Pipe pp;
+  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce);
+  for (int b = cs; b < ce && live; b += BATCH) {
+    if (__hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < chunk) {
+      gave_up = true;
+      break;
+    }
+    uint64_t work[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; rr++) {
+      const bool cand = stage(pp.rec[rr], st, &sbuf[rr * GS_WAVE + lane]) && pp.idc[rr] >= 0;
+      work[rr] = __ballot(cand);
+    }
+    pipe_advance(pp, splats, sids, b, ce);
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < RB; rr++) {
+      while (work[rr] && live) {
+        const int j = __builtin_ctzll(work[rr]);
+        work[rr] &= work[rr] - 1;
+        const Splat s = sbuf[rr * GS_WAVE + j];
+        const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
+        const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
+        const bool hit = alive && (q <= s.p2.y);
+        nsteps++;
+        if (__ballot(hit) == 0) continue;
+        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+        const float al = hit ? fminf(0.99f, ex) : 0.0f;
+        P = P - al * P;
+        const bool stop = hit && (P < T_STOP);
+        if (__ballot(stop)) {
+          if (stop) alive = false;
+          live = __ballot(alive);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  (void)lane;
+  return P;
+}
+
+// Every lane's earlier stores become visible device-wide before lane 0 publishes.
+__device__ __forceinline__ void wave_release() {
+  __threadfence();
+  __syncthreads();
+}
+
+__device__ __forceinline__ float ld_f(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_i(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
-    int32_t *__restrict__ last, int32_t *__restrict__ sub_last,
+    int32_t *__restrict__ last, char *__restrict__ state, int T,
     unsigned long long *__restrict__ stats) {
-  __shared__ Splat sbuf[GS_WAVE];
-  const int item = blockIdx.x;
-  const SubTile st = subtile_of(item, cam);
-  if (st.empty) {
-    if (threadIdx.x == 0) sub_last[item] = 0;
-    return;
-  }
-  const int lane = threadIdx.x;
-  const int px = st.x0 + (lane & 7), py = st.y0 + (lane >> 3);
-  const bool inside = px < cam.width && py < cam.height;
-  const int2 rg = ranges[st.tile];
-  const int start = rg.x, end = rg.y;
-  const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
-  float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-  int lastv = end - start;
-  bool alive = inside;
-  uint64_t live = __ballot(alive);
-  int wlast = 0;
+  __shared__ Splat sbuf[BATCH];
+  FwdState fs = fwd_state_at(state, T);
+  const int k = fs.hdr->k, nA = fs.hdr->nA;
+  const int64_t P = (int64_t)cam.width * cam.height;
+  const int lane = __lane_id();
   unsigned long long nhits = 0, nsteps = 0;
-
-  // prefetch the first batch; each batch's loads are issued one batch ahead
-  int pid = -1;
-  Splat pre;
-  if (start + lane < end) {
-    pid = sorted_ids[start + lane];
-    pre = splats[pid];
-  }
-  for (int b = start; b < end && live; b += GS_WAVE) {
-    bool cand = false;
-    if (pid >= 0) {
-      Splat s = pre;
-      cand = rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y, st.hx0, st.hx1, st.hy0,
-                          st.hy1);
-      s.p0.w = 2.0f * s.p0.w;          // 2b, exact
-      s.p2.w = __log2f(s.p1.y);        // log2(o) for the folded exponent
-      sbuf[lane] = s;
+  int g = blockIdx.x % GS_GROUPS, tried = 0;
+  bool chunks_done = nA == 0;
+  for (;;) {
+    const int t = next_item(fs, 0, 2 * nA, g, tried, chunks_done);
+    if (t < 0) break;
+    const int it = fs.items[t];
+    const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
+    const int idx = item_index(it);
+    const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
+    const SubTile st = subtile_of(tile, quad, cam);
+    const int2 rg = ranges[tile];
+    const Px x = pixel_of(st, cam);
+    if (kind == ITEM_PLAIN) {
+      if (st.empty) {
+        if (lane == 0) fs.sub_last[tile * 4 + quad] = 0;
+        continue;
+      }
+      const Blend r = blend_range(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits, nsteps);
+      if (x.inside) {
+        rgb[x.p] = r.C0;
+        rgb[P + x.p] = r.C1;
+        rgb[2 * P + x.p] = r.C2;
+        Tout[x.p] = r.T;
+        last[x.p] = r.consumed;
+      }
+      if (lane == 0) fs.sub_last[tile * 4 + quad] = r.wlast;
+      continue;
     }
-    uint64_t work = __ballot(cand);
-    const int nb = b + GS_WAVE;
-    pid = -1;
-    if (nb + lane < end) {
-      pid = sorted_ids[nb + lane];
-      pre = splats[pid];
+    int cs, ce;
+    chunk_range(rg.x, rg.y, p, k, cs, ce);
+    const int ci = chunk_index(idx, p, quad, k);
+    int32_t *sat = &fs.sat[idx * 4 + quad];
+    if (kind == ITEM_PASS_A) {
+      float Pp = 0.0f;
+      if (!st.empty) {
+        bool gave_up = false;
+        Pp = product_range(splats, sorted_ids, cs, ce, st, x, sbuf, sat, p, gave_up, nsteps);
+        if (gave_up) Pp = 0.0f;  // an earlier chunk already took every pixel below 1e-4
+        // every pixel of the quarter below the threshold: later chunks may give up
+        if (!gave_up && __ballot(x.inside && Pp >= T_STOP) == 0 && lane == 0) atomicMin(sat, p);
+      }
+      fs.PA[(int64_t)ci * 64 + lane] = Pp;
+      wave_release();
+      if (lane == 0) st_flag(&fs.doneA[ci], 1);
+      continue;
     }
-    __syncthreads();
-    while (work) {
-      const int j = __builtin_ctzll(work);
-      work &= work - 1;
-      const Splat s = sbuf[j];
-      const float dx = fx - s.p0.x, dy = fy - s.p0.y;
-      const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
-      const bool hit = alive && (q <= s.p2.y);
-      const uint64_t hm = __ballot(hit);
-      nsteps++;
-      if (hm == 0) continue;
-      nhits += __popcll(hm);
-      wlast = b + j - start + 1;
-      // branchless: a missed pixel blends with alpha = 0
-      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-      const float al = hit ? fminf(0.99f, ex) : 0.0f;
-      const float w = al * T;
-      C0 = __builtin_fmaf(w, s.p1.z, C0);
-      C1 = __builtin_fmaf(w, s.p1.w, C1);
-      C2 = __builtin_fmaf(w, s.p2.x, C2);
-      T = T - w;
-      const bool stop = hit && (T < 1e-4f);
-      if (__ballot(stop)) {
-        if (stop) {
-          alive = false;
-          lastv = b + j - start + 1;
+    // pass B: wait for pass A of the earlier chunks of this quarter
+    float Tin = 1.0f;
+    int ok = 1;
+    if (lane == 0) {
+      for (int q = 0; q < p && ok; q++) {
+        int spins = 0;
+        while (ld_flag(&fs.doneA[chunk_index(idx, q, quad, k)]) == 0) {
+          if (++spins > GS_SPIN_LIMIT) {
+            atomicOr(&fs.hdr->err, 1);
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
         }
-        live = __ballot(alive);
-        if (!live) break;
       }
     }
-    __syncthreads();
-  }
-  if (inside) {
-    const int64_t P = (int64_t)cam.width * cam.height;
-    const int64_t p = (int64_t)py * cam.width + px;
-    rgb[p] = C0;
-    rgb[P + p] = C1;
-    rgb[2 * P + p] = C2;
-    Tout[p] = T;
-    last[p] = lastv;
-  }
-  if (lane == 0) {
-    sub_last[item] = wlast;
-    if (stats) {
-      atomicAdd(&stats[0], nhits);
-      atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
-      atomicAdd(&stats[2], nsteps);
+    ok = __shfl(ok, 0, GS_WAVE);
+    __threadfence();  // acquire: the producers' PA stores are visible from here
+    for (int q = 0; q < p; q++)
+      Tin = ok ? Tin * ld_f(&fs.PA[(int64_t)chunk_index(idx, q, quad, k) * 64 + lane]) : 0.0f;
+    Blend r;
+    r.C0 = r.C1 = r.C2 = 0.0f;
+    r.T = Tin;
+    r.consumed = -1;
+    r.wlast = 0;
+    const bool skip = st.empty || ld_i(sat) < p;
+    if (!skip) {
+      r = blend_range(splats, sorted_ids, cs, ce, st, x, Tin, sbuf, nhits, nsteps);
+      if (!(x.inside && Tin >= T_STOP)) r.consumed = -1;  // stopped before this chunk
     }
+    const int64_t cp = (int64_t)ci * 64 + lane;
+    fs.CB[3 * cp] = r.C0;
+    fs.CB[3 * cp + 1] = r.C1;
+    fs.CB[3 * cp + 2] = r.C2;
+    fs.TB[cp] = r.T;
+    fs.LB[cp] = r.consumed;
+    if (lane == 0) fs.chunk_last[ci] = r.wlast;
+    wave_release();
+    int prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&fs.doneB[idx * 4 + quad], 1, __ATOMIC_ACQ_REL,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0, GS_WAVE);
+    if (prev != k - 1 || st.empty) continue;
+    // the last finisher of this quarter composes the chunks in depth order
+    __threadfence();
+    float C0 = 0.f, C1 = 0.f, C2 = 0.f, Tf = 1.0f;
+    int lastv = 0;
+    for (int q = 0; q < k; q++) {
+      const int64_t c2 = (int64_t)chunk_index(idx, q, quad, k) * 64 + lane;
+      const int lb = ld_i(&fs.LB[c2]);
+      if (lb < 0) break;
+      C0 += ld_f(&fs.CB[3 * c2]);
+      C1 += ld_f(&fs.CB[3 * c2 + 1]);
+      C2 += ld_f(&fs.CB[3 * c2 + 2]);
+      Tf = ld_f(&fs.TB[c2]);
+      int qs, qe;
+      chunk_range(rg.x, rg.y, q, k, qs, qe);
+      lastv = qs - rg.x + lb;
+      if (Tf < T_STOP) break;
+    }
+    if (x.inside) {
+      rgb[x.p] = C0;
+      rgb[P + x.p] = C1;
+      rgb[2 * P + x.p] = C2;
+      Tout[x.p] = Tf;
+      last[x.p] = lastv;
+    }
+  }
+  if (stats && lane == 0) {
+    atomicAdd(&stats[0], nhits);
+    atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
+    atomicAdd(&stats[2], nsteps);
   }
 }
 
 }  // namespace
 
+hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
+                              int force_h, double lambda_, double beta, double eps, double workers,
+                              void *fwd_state, int64_t *stats, hipStream_t st);
+
 hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
-                                const int32_t *ranges, const CamK &cam, float *rgb, float *T,
-                                int32_t *last, int32_t *sub_last, int64_t *stats, hipStream_t st) {
-  const int items = cam.tiles_x * cam.tiles_y * 4;
-  hipLaunchKernelGGL(k_render_fwd, dim3(items), dim3(GS_WAVE), 0, st,
+                                const int32_t *ranges, const CamK &cam, const gs_sched &sched,
+                                float *rgb, float *T, int32_t *last, void *fwd_state,
+                                int64_t *stats, int workers_waves, hipStream_t st) {
+  const int ntiles = cam.tiles_x * cam.tiles_y;
+  hipError_t e = gs_launch_schedule(ranges, cam, sched.chunk_mode, sched.force_k, sched.force_h,
+                                    sched.lambda_, sched.beta, sched.eps,
+                                    (double)workers_waves / 4.0, fwd_state, stats, st);
+  if (e != hipSuccess) return e;
+  // one worker per wave slot; workers that find the queues empty exit at once
+  hipLaunchKernelGGL(k_render_fwd, dim3(workers_waves), dim3(GS_WAVE), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
-                     reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last, sub_last,
+                     reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
+                     reinterpret_cast<char *>(fwd_state), ntiles,
                      reinterpret_cast<unsigned long long *>(stats));
   return hipGetLastError();
 }

@@ -73,7 +73,7 @@ def _load():
         "or_render_fwd_untiled": [i32, P, i32, i32, P, P],
         "or_render_fwd_values": [P, P, P, P, i32, i32, P, P, P],
         "or_render_bwd": [P, P, P, i32, i32, P, P, i32, P],
-        "or_chunk_policy": [i32, P, dbl, dbl, dbl, dbl, P, P],
+        "or_chunk_policy": [i32, P, dbl, dbl, dbl, dbl, i32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -203,12 +203,12 @@ def render_bwd(splats, sorted_ids, ranges, width, height, last, dL_drgb) -> np.n
     return grads
 
 
-def chunk_policy(counts_desc, workers, lambda_, beta, eps=0.10):
+def chunk_policy(counts_desc, workers, lambda_, beta, eps=0.10, max_items=1 << 30):
     counts_desc = _c(counts_desc, np.int32)
     h = np.zeros(1, np.int32)
     k = np.zeros(1, np.int32)
     _load().or_chunk_policy(counts_desc.shape[0], _p(counts_desc), float(workers),
-                            float(lambda_), float(beta), float(eps), _p(h), _p(k))
+                            float(lambda_), float(beta), float(eps), int(max_items), _p(h), _p(k))
     return int(h[0]), int(k[0])
 
 

@@ -76,9 +76,10 @@ void or_render_bwd(const float *splats, const int32_t *sorted_ids, const int32_t
                    int n, double *grads);
 
 /* Per-frame chunking policy (Eq. 6 of [LOAD-IMB]). counts_desc: tile counts in
-   descending order. Writes h (tiles to chunk) and k (chunks per tile; 1 when off). */
+   descending order. Writes h (tiles to chunk) and k (chunks per tile; 1 when off);
+   only candidates with h k <= max_items are considered. */
 void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, double lambda_,
-                     double beta, double eps, int32_t *h_out, int32_t *k_out);
+                     double beta, double eps, int max_items, int32_t *h_out, int32_t *k_out);
 
 /* OpenMP threads used by the parallel loops (for reporting). */
 int or_num_threads(void);

@@ -9,6 +9,8 @@
  * The policy searches k in {2, 4, 8, 16} and h = 1..T, keeps the first strict
  * minimum (k ascending, then h ascending), and chunks only if that minimum is at
  * least eps (10%) below the no-chunking estimate T(0) = max(N_total / K, N_1) + beta N_1.
+ * Candidates are limited to h k <= max_items (the number of chunk partials a frame
+ * can hold).
  * All arithmetic is fp64 in this exact order, so a device copy can match it bit
  * for bit. lambda and beta are not printed on the page: parity for their values
  * is unpinned.
@@ -20,7 +22,7 @@
 #endif
 
 void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, double lambda_,
-                     double beta, double eps, int32_t *h_out, int32_t *k_out) {
+                     double beta, double eps, int max_items, int32_t *h_out, int32_t *k_out) {
   *h_out = 0;
   *k_out = 1;
   if (ntiles <= 0) return;
@@ -31,7 +33,7 @@ void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, dou
   double best = T0;
   int bh = 0, bk = 1;
   for (int k = 2; k <= 16; k *= 2) {
-    for (int h = 1; h <= ntiles; h++) {
+    for (int h = 1; h <= ntiles && h * k <= max_items; h++) {
       const double next = h < ntiles ? (double)counts_desc[h] : 0.0;
       const double l = fmax(N1 / (double)k, next);
       const double avg = (Nt + (lambda_ * (double)h) * (double)k) / workers;

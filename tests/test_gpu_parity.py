@@ -225,3 +225,113 @@ def test_full_size_configs(cfg):
     check_backward(ref, out)
     print(f"config {cfg}: pairs {out['I']}, hits {int(out['stats'][0])}, "
           f"knife-edge pixels {int(ref['fwd']['knife'].sum())}", flush=True)
+
+
+# ---------------------------------------------------------------- scheduling and chunking
+
+def _plan_layout(T):
+    """Offsets into the opaque forward state, read here for checking only:
+    header (h, k, nA, nplain, err, ntiles, group offsets), queue heads,
+    per-quarter bounds, LPT order, sorted counts."""
+    rnd = lambda b: (b + 255) // 256 * 256
+    hdr = 0
+    heads = rnd(4 * 15)
+    sub_last = heads + rnd(4 * 2 * 9 * 16)
+    order = sub_last + rnd(16 * T)
+    counts = order + rnd(4 * T)
+    return dict(hdr=hdr, order=order, counts=counts)
+
+
+def read_plan(r):
+    T = r.tiles
+    L = _plan_layout(T)
+    raw = host(r.fwd_state)
+    hdr = raw[L["hdr"]:L["hdr"] + 60].view(np.int32)
+    order = raw[L["order"]:L["order"] + 4 * T].view(np.int32)
+    counts = raw[L["counts"]:L["counts"] + 4 * T].view(np.int32)
+    assert int(hdr[5]) == T
+    return dict(h=int(hdr[0]), k=int(hdr[1]), nA=int(hdr[2]), err=int(hdr[4]), order=order,
+                counts=counts, qoff=hdr[6:15].copy())
+
+
+def _workers():
+    return torch.cuda.get_device_properties(0).multi_processor_count * 32 / 4.0
+
+
+@pytest.mark.parametrize("k", [2, 4, 8, 16])
+def test_forced_chunking_matches_oracle(k):
+    """Every tile split into k depth chunks: exact composition, so the results
+    still match the unchunked oracle to the same bars."""
+    gsr = _gsr()
+    sc, ref = reference(2)
+    sched = gsr.make_sched(chunk_mode=2, force_k=k, force_h=0)
+    out = run_stages(gsr, sc, ref, sched=sched)
+    check_forward(ref, out)
+    check_backward(ref, out)
+    assert int(out["stats"][3]) == min(sc.camera.num_tiles, gsr.HK_MAX // k)
+
+
+@pytest.mark.parametrize("k,h", [(2, 3), (16, 40)])
+def test_forced_chunking_ragged(k, h):
+    gsr = _gsr()
+    sc = scenegen.random_scene(104, 6000, 150, 70, 120.0, degree=1, log_scale=(-2.2, 0.7),
+                               opacity=(1.0, 2.0))
+    ref = oracle.frame(sc)
+    out = run_stages(gsr, sc, ref, sched=gsr.make_sched(chunk_mode=2, force_k=k, force_h=h))
+    check_forward(ref, out)
+    check_backward(ref, out)
+
+
+def _policy_frame(gsr, counts, W, H):
+    """Run the device schedule on given tile counts (a dummy list of culled splats)."""
+    cam = scenegen.pinhole(W, H, float(W))
+    T = cam.num_tiles
+    assert len(counts) == T
+    ranges = np.zeros((T, 2), np.int32)
+    ranges[:, 1] = np.cumsum(counts)
+    ranges[1:, 0] = ranges[:-1, 1]
+    I = int(ranges[-1, 1])
+    r = gsr.Rasterizer(cam, capacity=max(I, 1))
+    r._ensure(1, max(I, 1))
+    r.splats.zero_()
+    r.splats[:, 9] = -1.0
+    r.sorted_ids.zero_()
+    r.ranges.copy_(dev(ranges))
+    r.render_fwd(1)
+    return read_plan(r)
+
+
+@pytest.mark.parametrize("case", ["pareto", "one_outlier", "flat", "two_level"])
+def test_device_policy_equals_host_policy(case):
+    gsr = _gsr()
+    rng = np.random.default_rng(abs(hash(case)) % 1000)
+    W, H = 1920, 1080
+    T = ((W + 15) // 16) * ((H + 15) // 16)
+    if case == "pareto":
+        counts = (rng.pareto(1.2, T) * 300).astype(np.int64)
+    elif case == "one_outlier":
+        counts = rng.integers(50, 400, T)
+        counts[1234] = 250_000
+    elif case == "flat":
+        counts = np.full(T, 700)
+    else:
+        counts = np.where(rng.random(T) < 0.02, 40_000, 900)
+    counts = np.minimum(counts, 2_000_000).astype(np.int32)
+    plan = _policy_frame(gsr, counts, W, H)
+    assert plan["err"] == 0
+    # exact LPT order: count descending, ties by tile id
+    ref_order = np.lexsort((np.arange(T), -counts.astype(np.int64)))
+    assert np.array_equal(plan["order"], ref_order)
+    assert np.array_equal(plan["counts"], counts[ref_order])
+    f32 = lambda v: float(np.float32(v))  # the knobs travel as fp32 in gs_sched
+    h, k = oracle.chunk_policy(counts[ref_order], _workers(), f32(gsr.DEFAULT_LAMBDA),
+                               f32(gsr.DEFAULT_BETA), f32(gsr.DEFAULT_EPS), gsr.HK_MAX)
+    assert (plan["h"], plan["k"] if plan["h"] else 1) == (h, k), (plan["h"], plan["k"], h, k)
+    assert plan["nA"] == 4 * h * (k if h else 0)
+    # the group queues partition the quarters of the unchunked tiles
+    assert plan["qoff"][0] == 0 and plan["qoff"][-1] == 4 * (T - h)
+    assert np.all(np.diff(plan["qoff"]) >= 0)
+    if case == "one_outlier":
+        assert h >= 1
+    if case == "flat":
+        assert h == 0
