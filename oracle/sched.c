@@ -1,19 +1,25 @@
 /* Oracle: per-frame chunking policy. TEST INFRASTRUCTURE ONLY.
  *
- * [LOAD-IMB] section 4.4, Eq. 6 (garbled in extraction; reading below).
- * With tile counts N_1 >= N_2 >= ... and N_total = sum_t N_t, chunking the h
- * heaviest tiles into k chunks each costs an average-workload term
- * (N_total + lambda h k) / K over K concurrent workers; the longest remaining
- * unit is l(h, k) = max(N_1 / k, N_{h+1}); the estimate is
- *   T(h, k) = max((N_total + lambda h k) / K, l) + beta l.
+ * [LOAD-IMB] section 4.4, Eq. 6 (garbled in extraction; reading below), with
+ * the cost of exact chunk composition folded in.
+ * With tile counts N_1 >= N_2 >= ... and N_total = sum_t N_t, the page's model
+ * charges the average workload over K concurrent workers plus a fixed cost
+ * lambda per chunk, and the longest remaining unit:
+ *   T(h, k) = max(avg, l) + beta l.
+ * Chunks here are composed exactly (a transmittance pass over every chunk,
+ * then a blending pass from the exact incoming transmittance), so a split tile
+ * is walked twice and a chunk's blending waits for the transmittance of the
+ * chunks in front of it. The model therefore charges
+ *   avg = ((N_total + S_h) + lambda h k) / K,  S_h = N_1 + ... + N_h,
+ *   l   = max(2 N_1 / k, N_{h+1}).
  * The policy searches k in {2, 4, 8, 16} and h = 1..T, keeps the first strict
  * minimum (k ascending, then h ascending), and chunks only if that minimum is at
  * least eps (10%) below the no-chunking estimate T(0) = max(N_total / K, N_1) + beta N_1.
  * Candidates are limited to h k <= max_items (the number of chunk partials a frame
  * can hold).
- * All arithmetic is fp64 in this exact order, so a device copy can match it bit
- * for bit. lambda and beta are not printed on the page: parity for their values
- * is unpinned.
+ * All arithmetic is fp64 in this exact order (S_h summed exactly in int64), so a
+ * device copy can match it bit for bit. lambda and beta are not printed on the
+ * page: parity for their values is unpinned.
  */
 #include <math.h>
 #include "oracle.h"
@@ -33,10 +39,12 @@ void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, dou
   double best = T0;
   int bh = 0, bk = 1;
   for (int k = 2; k <= 16; k *= 2) {
+    int64_t Sh = 0;
     for (int h = 1; h <= ntiles && h * k <= max_items; h++) {
+      Sh += counts_desc[h - 1];
       const double next = h < ntiles ? (double)counts_desc[h] : 0.0;
-      const double l = fmax(N1 / (double)k, next);
-      const double avg = (Nt + (lambda_ * (double)h) * (double)k) / workers;
+      const double l = fmax((2.0 * N1) / (double)k, next);
+      const double avg = ((Nt + (double)Sh) + (lambda_ * (double)h) * (double)k) / workers;
       const double est = fmax(avg, l) + beta * l;
       if (est < best) {
         best = est;
