@@ -90,7 +90,7 @@ def make_camera(cam) -> GsCamera:
 
 # Defaults of the per-frame chunking policy (Eq. 6 constants; the page does not
 # print lambda and beta, these are calibrated for this build).
-DEFAULT_LAMBDA, DEFAULT_BETA, DEFAULT_EPS = 512.0, 0.25, 0.10
+DEFAULT_LAMBDA, DEFAULT_BETA, DEFAULT_EPS = 131072.0, 0.25, 0.10
 HK_MAX = 4096  # cap on h*k, the chunks of chunked tiles per frame
 
 

@@ -77,7 +77,7 @@ gs_sched default_sched() {
   s.chunk_mode = 1;
   s.force_k = 0;
   s.force_h = 0;
-  s.lambda_ = 512.0f;
+  s.lambda_ = 131072.0f;  // measured on MI355X (see gs_sched in gs.h)
   s.beta = 0.25f;
   s.eps = 0.10f;
   return s;

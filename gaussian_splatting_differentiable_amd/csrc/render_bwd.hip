@@ -28,9 +28,10 @@ constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 
 // Zero the gradient output and rewind the backward queues of this frame.
 __global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n,
+                                              const PlanHdr *__restrict__ hdr,
                                               int32_t *__restrict__ bwd_heads) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i <= GS_GROUPS) bwd_heads[i * GS_HEAD_STRIDE] = 0;
+  if (i < GS_GROUPS) bwd_heads[i * GS_HEAD_STRIDE] = hdr->init_b[i];
   const int64_t n4 = n / 4;
   if (i < n4) reinterpret_cast<float4 *>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (i < n - 4 * n4) p[4 * n4 + i] = 0.0f;
@@ -42,7 +43,7 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
-constexpr int RB = 2;                // 64-splat rounds per batch
+constexpr int RB = 1;                // 64-splat rounds per batch
 constexpr int BATCH = RB * GS_WAVE;  // splats per staged batch
 
 // Two-stage load pipeline for the back-to-front walk: the ids of the batch
@@ -101,7 +102,7 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
     for (int r = 0; r < RB; r++) idc[r] = idn[r];
     load_recs(splats, idc, rec);
     load_ids(sids, max(cs, nlo - BATCH), nlo, idn);
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int rr = RB - 1; rr >= 0; rr--) {
       while (work[rr]) {
@@ -144,30 +145,32 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
         if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[slot] + comp], out);
       }
     }
-    __syncthreads();
+    wave_sync();
     hiE = nhi;
     lo = nlo;
   }
 }
 
-__global__ void __launch_bounds__(GS_WAVE) __attribute__((amdgpu_waves_per_eu(1, 4))) k_render_bwd(
+__global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
+__attribute__((amdgpu_waves_per_eu(8))) k_render_bwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
     const float *__restrict__ dL, float *__restrict__ grads) {
-  __shared__ Splat sbuf[BATCH];
-  __shared__ int sid[BATCH];
+  __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
+  __shared__ int sid_all[GS_WAVES_PER_BLOCK][BATCH];
+  Splat *sbuf = sbuf_all[wave_in_block()];
+  int *sid = sid_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
-  const int k = fs.hdr->k, nA = fs.hdr->nA;
+  const int k = fs.hdr->k;
   const int64_t P = (int64_t)cam.width * cam.height;
   const int lane = __lane_id();
-  int g = blockIdx.x % GS_GROUPS, tried = 0;
-  bool chunks_done = nA == 0;
+  Worker wk = make_worker();
   for (;;) {
-    // the pass-B chunk items (items[nA, 2nA)), then the group queues
-    const int t = next_item(fs, 1, nA, g, tried, chunks_done);
+    const int t = next_item(fs, 1, wk);
     if (t < 0) break;
-    const int it = fs.items[nA + t];
+    set_round_priority(wk.round++);
+    const int it = fs.items[t];
     const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
     const int idx = item_index(it);
     const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
@@ -233,8 +236,9 @@ hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const FwdState fs = fwd_state_at(const_cast<void *>(fwd_state), ntiles);
   hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng,
-                     queue_head(fs, 1, 0));
-  hipLaunchKernelGGL(k_render_bwd, dim3(workers_waves), dim3(GS_WAVE), 0, st,
+                     fs.hdr, queue_head(fs, 1, 0));
+  hipLaunchKernelGGL(k_render_bwd, dim3(workers_waves / GS_WAVES_PER_BLOCK),
+                     dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
                      reinterpret_cast<char *>(const_cast<void *>(fwd_state)), ntiles, dL, grads);

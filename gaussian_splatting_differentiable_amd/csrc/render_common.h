@@ -13,18 +13,20 @@
 
 #define GS_HK_MAX 4096        // maximum h*k (chunks of chunked tiles per frame)
 #define GS_SLOTS_MAX 2048     // maximum h (k >= 2)
-#define GS_SPIN_LIMIT (1 << 24)
+#define GS_SPIN_LIMIT (1 << 20)  // probes of a bounded wait (seconds at the longest back-off)
 
 // Item: kind (2 bits) | quad (2 bits) | chunk p (4 bits) | index (24 bits).
 enum ItemKind { ITEM_PLAIN = 0, ITEM_PASS_A = 1, ITEM_PASS_B = 2 };
 
-// Queues: one global queue for the chunk items (all pass A, then all pass B),
-// then one queue per XCD group for the other quarters. Tiles are grouped into
-// GS_GROUPS vertical strips of the image, so neighbouring tiles (which share
-// splats) and the four quarters of one tile are served by the workers of one
-// XCD and its L2; workers that empty their group's queue take from the others.
+// Queues: one per XCD group. Tiles are grouped into GS_GROUPS vertical strips of
+// the image, so neighbouring tiles (which share splats) and the four quarters of
+// one tile are served by the workers of one XCD and its L2. Group g's queue
+// holds, in order, the pass-A items of its chunked tiles, their pass-B items,
+// then the quarters of its other tiles (longest first); workers that empty
+// their group's queue take from the others.
 #define GS_GROUPS 8
 #define GS_HEAD_STRIDE 16  // ints between two queue heads (one 64-byte line)
+#define GS_WAVES_PER_BLOCK 4
 
 __host__ __device__ __forceinline__ int make_item(int kind, int quad, int p, int idx) {
   return (kind << 30) | (quad << 28) | (p << 24) | idx;
@@ -40,7 +42,12 @@ struct PlanHdr {
   int32_t nplain;               // quarters of the other tiles = 4 (T - h)
   int32_t err;                  // a bounded wait gave up (never expected)
   int32_t ntiles;
-  int32_t qoff[GS_GROUPS + 1];  // group queues within the plain items
+  int32_t qoff[GS_GROUPS + 1];  // group g's items are items[qoff[g], qoff[g+1])
+  int32_t qa[GS_GROUPS];        // pass-A items at the front of group g (as many pass-B follow)
+  // Items handed out without a queue pop: a worker's first item is the one at
+  // its index within its group (in the forward only in groups without chunk
+  // items, since a pass-B item waits on items in front of it).
+  int32_t init_f[GS_GROUPS], init_b[GS_GROUPS];
 };
 
 // Byte layout of fwd_state for T tiles.
@@ -59,7 +66,7 @@ __host__ __device__ inline FwdLayout fwd_layout(int T) {
   };
   const size_t cq = (size_t)GS_HK_MAX * 4;  // chunk items (per quad)
   L.hdr = take(sizeof(PlanHdr));
-  L.heads = take(4 * (size_t)2 * (GS_GROUPS + 1) * GS_HEAD_STRIDE);
+  L.heads = take(4 * (size_t)2 * GS_GROUPS * GS_HEAD_STRIDE);
   L.sub_last = take(4 * (size_t)T * 4);
   L.order = take(4 * (size_t)T);
   L.counts = take(4 * (size_t)T);
@@ -78,7 +85,7 @@ __host__ __device__ inline FwdLayout fwd_layout(int T) {
 
 struct FwdState {
   PlanHdr *hdr;
-  int32_t *heads;  // [pass 0 fwd / 1 bwd][queue 0 chunks, 1.. groups] * GS_HEAD_STRIDE
+  int32_t *heads;  // [pass 0 fwd / 1 bwd][group] * GS_HEAD_STRIDE
   int32_t *sub_last, *order, *counts, *items, *sat, *doneA, *doneB, *chunk_last;
   float *PA, *CB, *TB;
   int32_t *LB;
@@ -105,8 +112,14 @@ __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
   return s;
 }
 
-__host__ __device__ __forceinline__ int32_t *queue_head(const FwdState &fs, int pass, int q) {
-  return fs.heads + (pass * (GS_GROUPS + 1) + q) * GS_HEAD_STRIDE;
+__host__ __device__ __forceinline__ int32_t *queue_head(const FwdState &fs, int pass, int g) {
+  return fs.heads + (pass * GS_GROUPS + g) * GS_HEAD_STRIDE;
+}
+
+// Workers of group g when `nblocks` workgroups are launched (workgroup b runs on
+// XCD b mod GS_GROUPS).
+__host__ __device__ __forceinline__ int group_workers(int g, int nblocks) {
+  return GS_WAVES_PER_BLOCK * ((nblocks - g + GS_GROUPS - 1) / GS_GROUPS);
 }
 
 // Group (XCD strip) of a tile: vertical strips of the tile grid.
@@ -146,6 +159,36 @@ __device__ __forceinline__ SubTile subtile_of(int tile, int quad, const CamK &ca
   return st;
 }
 
+// A workgroup holds GS_WAVES_PER_BLOCK independent wave workers, each with its
+// own slice of LDS.
+
+__device__ __forceinline__ int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / GS_WAVE);
+}
+
+// Orders this wave's LDS stores before its later LDS loads (and the reverse):
+// the workers of a workgroup never share LDS, so no workgroup barrier is needed.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Issue priority of a worker on its `round`-th item (0 = first). A SIMD issues
+// from the highest-priority ready wave and breaks ties by wave age, so a worker
+// wave dispatched late would otherwise be starved by older workers for as long
+// as they find work, and its item would finish last. Lowering the priority
+// with every item a worker takes approximates first-come-first-served across
+// items instead.
+__device__ __forceinline__ void set_round_priority(int round) {
+  switch (round) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // Wave-uniform queue pop: one lane advances the head, every lane gets the ticket.
 __device__ __forceinline__ int queue_pop(int32_t *head) {
   int t = 0;
@@ -153,34 +196,56 @@ __device__ __forceinline__ int queue_pop(int32_t *head) {
   return __shfl(t, 0, GS_WAVE);
 }
 
-// Next item of a persistent worker: the chunk queue [0, nchunk) first, then its
-// own group's queue, then the other groups'. Returns the index into items[]
-// (relative to `base`), or -1 when everything is taken. `g` is the group
-// currently being drained (starts at the worker's XCD).
-__device__ __forceinline__ int next_item(const FwdState &fs, int pass, int nchunk, int &g,
-                                         int &tried, bool &chunks_done) {
-  if (!chunks_done) {
-    const int t = queue_pop(queue_head(fs, pass, 0));
-    if (t < nchunk) return t;
-    chunks_done = true;
-  }
-  while (tried < GS_GROUPS) {
-    const int q0 = fs.hdr->qoff[g], q1 = fs.hdr->qoff[g + 1];
-    if (q1 > q0) {
-      const int t = queue_pop(queue_head(fs, pass, 1 + g));
-      if (q0 + t < q1) return nchunk + q0 + t;
-    }
-    g = (g + 1) % GS_GROUPS;
-    tried++;
-  }
-  return -1;
-}
-
 // Spin on a flag with relaxed loads (no cache invalidation per probe); the
 // caller issues one acquire fence after it succeeds.
 __device__ __forceinline__ int ld_flag(const int32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// A persistent worker: its group (the XCD it runs on), its index within the
+// group, and its progress through the queues.
+struct Worker {
+  int g, wg, tried, round;
+};
+
+__device__ __forceinline__ Worker make_worker() {
+  Worker w;
+  w.g = blockIdx.x % GS_GROUPS;
+  // wave v of the group's j-th workgroup: consecutive items (the quarters of a
+  // tile) go to different workgroups, as they would from a shared queue
+  const int blocks = (gridDim.x - w.g + GS_GROUPS - 1) / GS_GROUPS;
+  w.wg = wave_in_block() * blocks + (int)(blockIdx.x / GS_GROUPS);
+  w.tried = 0;
+  w.round = 0;
+  return w;
+}
+
+// Next item (an index into items[]) of a worker, or -1 when every queue is
+// empty. pass 0 (forward) serves every item of a group; pass 1 (backward)
+// skips the pass-A items. The first item comes without a pop: the queue heads
+// start past the items handed out that way, so a frame's first wave of work
+// does not serialise on the heads. After that: the worker's own group, then
+// the others. (An atomic load to skip drained queues costs more than the pop:
+// it waits on the worker's outstanding stores.)
+__device__ __forceinline__ int next_item(const FwdState &fs, int pass, Worker &w) {
+  const PlanHdr *hd = fs.hdr;
+  if (w.round == 0) {
+    const int init = pass ? hd->init_b[w.g] : hd->init_f[w.g];
+    if (w.wg < init) return hd->qoff[w.g] + (pass ? hd->qa[w.g] : 0) + w.wg;
+  }
+  while (w.tried < GS_GROUPS) {
+    const int lo = hd->qoff[w.g] + (pass ? hd->qa[w.g] : 0), hi = hd->qoff[w.g + 1];
+    int32_t *head = queue_head(fs, pass, w.g);
+    if (lo < hi) {
+      const int t = queue_pop(head);
+      if (lo + t < hi) return lo + t;
+    }
+    w.g = (w.g + 1) % GS_GROUPS;
+    w.tried++;
+  }
+  return -1;
+}
+
 __device__ __forceinline__ void st_flag(int32_t *p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -35,13 +35,13 @@ namespace {
 
 constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 constexpr float T_STOP = 1e-4f;
-constexpr int RB = 2;                 // 64-splat rounds per batch
+constexpr int RB = 1;                 // 64-splat rounds per batch
 constexpr int BATCH = RB * GS_WAVE;   // splats per staged batch
 
 struct Px {
   float fx, fy;
   bool inside;
-  int64_t p;  // pixel index
+  int p;  // pixel index (fewer than 2^31 / 3 pixels: at most 65535 tiles)
 };
 
 __device__ __forceinline__ Px pixel_of(const SubTile &st, const CamK &cam) {
@@ -51,7 +51,7 @@ __device__ __forceinline__ Px pixel_of(const SubTile &st, const CamK &cam) {
   x.inside = px < cam.width && py < cam.height;
   x.fx = (float)px + 0.5f;
   x.fy = (float)py + 0.5f;
-  x.p = (int64_t)py * cam.width + px;
+  x.p = py * cam.width + px;
   return x;
 }
 
@@ -118,8 +118,8 @@ struct Blend {
 __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int cs, int ce,
                                              const SubTile &st, const Px &x, float T0,
-                                             Splat *sbuf, unsigned long long &nhits,
-                                             unsigned long long &nsteps) {
+                                             Splat *sbuf, uint32_t &nhits,
+                                             uint32_t &nsteps) {
   Blend r;
   r.C0 = r.C1 = r.C2 = 0.0f;
   r.T = T0;
@@ -139,7 +139,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
       work[rr] = __ballot(cand);
     }
     pipe_advance(pp, splats, sids, b, ce);
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int rr = 0; rr < RB; rr++) {
       while (work[rr] && live) {
@@ -172,7 +172,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
         }
       }
     }
-    __syncthreads();
+    wave_sync();
   }
   (void)lane;
   return r;
@@ -183,7 +183,7 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
                                                const int32_t *__restrict__ sids, int cs, int ce,
                                                const SubTile &st, const Px &x, Splat *sbuf,
                                                const int32_t *sat, int chunk, bool &gave_up,
-                                               unsigned long long &nsteps) {
+                                               uint32_t &nsteps) {
   float P = 1.0f;
   bool alive = x.inside;
   uint64_t live = __ballot(alive);
@@ -191,8 +191,11 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
   const int lane = __lane_id();
   Pipe pp;
   if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce);
+  // sat is read one batch late: the load goes out with the batch prefetch, so
+  // waiting for it costs nothing beyond the wait for the prefetch itself
+  int satv = chunk;
   for (int b = cs; b < ce && live; b += BATCH) {
-    if (__hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < chunk) {
+    if (satv < chunk) {
       gave_up = true;
       break;
     }
@@ -203,7 +206,8 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
       work[rr] = __ballot(cand);
     }
     pipe_advance(pp, splats, sids, b, ce);
-    __syncthreads();
+    const int satn = __hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wave_sync();
 #pragma unroll
     for (int rr = 0; rr < RB; rr++) {
       while (work[rr] && live) {
@@ -225,7 +229,8 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
         }
       }
     }
-    __syncthreads();
+    satv = satn;
+    wave_sync();
   }
   (void)lane;
   return P;
@@ -234,7 +239,7 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
 // Every lane's earlier stores become visible device-wide before lane 0 publishes.
 __device__ __forceinline__ void wave_release() {
   __threadfence();
-  __syncthreads();
+  wave_sync();
 }
 
 __device__ __forceinline__ float ld_f(const float *p) {
@@ -244,22 +249,24 @@ __device__ __forceinline__ int ld_i(const int32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
+__global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
+__attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
     int32_t *__restrict__ last, char *__restrict__ state, int T,
     unsigned long long *__restrict__ stats) {
-  __shared__ Splat sbuf[BATCH];
+  __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
+  Splat *sbuf = sbuf_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, T);
-  const int k = fs.hdr->k, nA = fs.hdr->nA;
-  const int64_t P = (int64_t)cam.width * cam.height;
+  const int k = fs.hdr->k;
+  const int P = cam.width * cam.height;
   const int lane = __lane_id();
-  unsigned long long nhits = 0, nsteps = 0;
-  int g = blockIdx.x % GS_GROUPS, tried = 0;
-  bool chunks_done = nA == 0;
+  uint32_t nhits = 0, nsteps = 0;  // per worker; far below 2^32
+  Worker wk = make_worker();
   for (;;) {
-    const int t = next_item(fs, 0, 2 * nA, g, tried, chunks_done);
+    const int t = next_item(fs, 0, wk);
     if (t < 0) break;
+    set_round_priority(wk.round++);
     const int it = fs.items[t];
     const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
     const int idx = item_index(it);
@@ -313,7 +320,12 @@ __global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
             ok = 0;
             break;
           }
-          __builtin_amdgcn_s_sleep(4);
+          // back off: a few quick probes, then about 8k cycles between probes,
+          // so thousands of waiting waves do not load the L2 with probes
+          if (spins < 64)
+            __builtin_amdgcn_s_sleep(4);
+          else
+            __builtin_amdgcn_s_sleep(127);
         }
       }
     }
@@ -371,16 +383,16 @@ __global__ void __launch_bounds__(GS_WAVE) k_render_fwd(
     }
   }
   if (stats && lane == 0) {
-    atomicAdd(&stats[0], nhits);
+    atomicAdd(&stats[0], (unsigned long long)nhits);
     atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
-    atomicAdd(&stats[2], nsteps);
+    atomicAdd(&stats[2], (unsigned long long)nsteps);
   }
 }
 
 }  // namespace
 
 hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
-                              int force_h, double lambda_, double beta, double eps, double workers,
+                              int force_h, double lambda_, double beta, double eps, int nblocks,
                               void *fwd_state, int64_t *stats, hipStream_t st);
 
 hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
@@ -388,12 +400,14 @@ hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
                                 int64_t *stats, int workers_waves, hipStream_t st) {
   const int ntiles = cam.tiles_x * cam.tiles_y;
+  const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   hipError_t e = gs_launch_schedule(ranges, cam, sched.chunk_mode, sched.force_k, sched.force_h,
-                                    sched.lambda_, sched.beta, sched.eps,
-                                    (double)workers_waves / 4.0, fwd_state, stats, st);
+                                    sched.lambda_, sched.beta, sched.eps, nblocks, fwd_state,
+                                    stats, st);
   if (e != hipSuccess) return e;
-  // one worker per wave slot; workers that find the queues empty exit at once
-  hipLaunchKernelGGL(k_render_fwd, dim3(workers_waves), dim3(GS_WAVE), 0, st,
+  // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
+  // queues empty exit at once
+  hipLaunchKernelGGL(k_render_fwd, dim3(nblocks), dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,

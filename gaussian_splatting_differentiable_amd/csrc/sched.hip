@@ -1,16 +1,21 @@
 // Per-frame tile schedule: longest-processing-time order, the chunking policy
-// and the persistent work queue.
+// and the work queues of the persistent raster kernels.
 //
 // "Mitigating SM-Level Load Imbalance in 3D Gaussian Splatting on GPUs":
 // section 4.1 orders the tiles by descending pair count N_t (a radix sort of the
 // tile indices that leaves the Gaussian data in place); section 4.3 chunks the
 // heaviest tiles and schedules the rest in that order; section 4.4, Eq. 6 picks
-// the number of chunked tiles h and chunks per tile k per frame:
-//   l(h,k) = max(N_1/k, N_{h+1});  T(h,k) = max((N_total + lambda h k)/K, l) + beta l,
+// the number of chunked tiles h and chunks per tile k per frame. Chunks are
+// composed exactly here (a transmittance pass, then a blending pass from the
+// exact incoming transmittance), so a split tile is walked twice and the model
+// charges that:
+//   avg = ((N_total + S_h) + lambda h k) / K,  S_h = N_1 + ... + N_h,
+//   l = max(2 N_1 / k, N_{h+1}),  T(h,k) = max(avg, l) + beta l,
 // k in {2,4,8,16}, first strict minimum over (k, h), enabled only when at least
-// eps below the no-chunking estimate. Here h k is also capped at GS_HK_MAX.
-// The policy arithmetic is fp64 in one fixed order and this TU is compiled with
-// -ffp-contract=off, so a host copy of the policy returns the same (h, k).
+// eps below the no-chunking estimate max(N_total / K, N_1) + beta N_1. Here h k
+// is also capped at GS_HK_MAX. The policy arithmetic is fp64 in one fixed order
+// and this TU is compiled with -ffp-contract=off, so a host copy of the policy
+// returns the same (h, k).
 //
 // One workgroup of 1024 threads does everything; T <= 65535 tiles.
 #include "render_common.h"
@@ -33,6 +38,32 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v) {
   return t;
 }
 
+// Block-wide exclusive prefix sum of one value per thread; `total` gets the sum.
+template <typename V>
+__device__ __forceinline__ V block_excl_scan(V v, V &total) {
+  __shared__ V ws[NW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  V inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const V t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  __syncthreads();
+  if (lane == 63) ws[w] = inc;
+  __syncthreads();
+  V before = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < NW; q++) {
+    const V x = ws[q];
+    before += q < w ? x : V(0);
+    tot += x;
+  }
+  total = tot;
+  __syncthreads();
+  return before + inc - v;
+}
+
 // One stable LSD pass (8-bit digit at `shift`) of (key, val) over n elements in
 // global memory, by one workgroup. Wave w owns the contiguous chunk
 // [w*chunk, (w+1)*chunk); a first sweep counts digits per wave, a second sweep
@@ -47,29 +78,20 @@ __device__ void block_radix_pass(const uint32_t *kin, const int32_t *vin, uint32
   const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
   for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&cnt[w][(kin[e] >> shift) & 255], 1);
   __syncthreads();
-  // exclusive offsets in (digit, wave) order
-  __shared__ int dtot[256];
+  // offsets in (digit, wave) order: within a digit over the waves, then the
+  // digit totals scanned by the whole block
+  int dtot = 0;
   if (threadIdx.x < 256) {
-    int tot = 0;
     for (int q = 0; q < NW; q++) {
       const int c = cnt[q][threadIdx.x];
-      cnt[q][threadIdx.x] = tot;
-      tot += c;
-    }
-    dtot[threadIdx.x] = tot;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int d = 0; d < 256; d++) {
-      const int t = dtot[d];
-      dtot[d] = run;
-      run += t;
+      cnt[q][threadIdx.x] = dtot;
+      dtot += c;
     }
   }
-  __syncthreads();
+  int all;
+  const int dbase = block_excl_scan<int>(dtot, all);
   if (threadIdx.x < 256)
-    for (int q = 0; q < NW; q++) cnt[q][threadIdx.x] += dtot[threadIdx.x];
+    for (int q = 0; q < NW; q++) cnt[q][threadIdx.x] += dbase;
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int base = c0; base < c1; base += 64) {
@@ -95,12 +117,19 @@ __device__ void block_radix_pass(const uint32_t *kin, const int32_t *vin, uint32
   __syncthreads();
 }
 
+constexpr int NCLS = 2 * GS_GROUPS;  // (group, chunked?) classes of the LPT positions
+
+__device__ __forceinline__ uint32_t class_of(int e, int h, const int32_t *order, int tiles_x) {
+  return 2u * (uint32_t)tile_group(order[e], tiles_x) + (e >= h ? 1u : 0u);
+}
+
 __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges, int T, int tiles_x,
                                                  int chunk_mode, int force_k, int force_h,
                                                  double lambda_, double beta, double eps,
-                                                 double workers, char *__restrict__ fwd_state,
+                                                 int nblocks, char *__restrict__ fwd_state,
                                                  unsigned long long *__restrict__ stats) {
   FwdState fs = fwd_state_at(fwd_state, T);
+  const double workers = (double)(nblocks * GS_WAVES_PER_BLOCK) / 4.0;  // four waves per tile
   uint32_t *tmp_k = reinterpret_cast<uint32_t *>(fs.items);
   int32_t *tmp_v = fs.items + T;
   uint32_t *key = reinterpret_cast<uint32_t *>(fs.counts);
@@ -144,17 +173,25 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     h = force_h <= 0 ? T : min(force_h, T);
     h = min(h, GS_HK_MAX / k);
   } else if (chunk_mode == 1 && T > 0) {
+    constexpr int HMAX = GS_HK_MAX / 2;  // the largest h of any candidate
+    __shared__ long long sS[HMAX + 1];   // sS[h] = N_1 + ... + N_h (exact)
     __shared__ double s_best[NT];
     __shared__ int s_idx[NT];
     long long total_ll = 0;
     for (int t = threadIdx.x; t < T; t += NT) total_ll += fs.counts[t];
-    __shared__ long long s_tot[NW];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) total_ll += __shfl_xor(total_ll, d, 64);
-    if ((threadIdx.x & 63) == 0) s_tot[threadIdx.x >> 6] = total_ll;
+    long long tot;
+    (void)block_excl_scan<long long>(total_ll, tot);
+    {
+      static_assert(HMAX == 2 * NT, "two prefix entries per thread");
+      const int i0 = 2 * threadIdx.x;
+      const long long a = i0 < T ? fs.counts[i0] : 0, b = i0 + 1 < T ? fs.counts[i0 + 1] : 0;
+      long long all;
+      const long long before = block_excl_scan<long long>(a + b, all);
+      sS[i0 + 1] = before + a;
+      sS[i0 + 2] = before + a + b;
+      if (threadIdx.x == 0) sS[0] = 0;
+    }
     __syncthreads();
-    long long tot = 0;
-    for (int w = 0; w < NW; w++) tot += s_tot[w];
     const double Nt = (double)tot, N1 = (double)fs.counts[0];
     const double T0 = fmax(Nt / workers, N1) + beta * N1;
     // candidates in (k ascending, h ascending) order
@@ -171,8 +208,8 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
       const int kk = 2 << q;
       const int hh = i - off[q] + 1;
       const double next = hh < T ? (double)fs.counts[hh] : 0.0;
-      const double l = fmax(N1 / (double)kk, next);
-      const double avg = (Nt + (lambda_ * (double)hh) * (double)kk) / workers;
+      const double l = fmax((2.0 * N1) / (double)kk, next);
+      const double avg = ((Nt + (double)sS[hh]) + (lambda_ * (double)hh) * (double)kk) / workers;
       const double est = fmax(avg, l) + beta * l;
       if (est < best || (est == best && i < bidx)) {
         best = est;
@@ -203,56 +240,82 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   }
   if (h == 0) k = 1;
 
-  // 4. queues: pass-A chunk items, pass-B chunk items, then the quarters of the
-  //    other tiles grouped by image strip (a stable partition of the LPT order)
-  const int nA = 4 * h * k;
-  for (int i = threadIdx.x; i < nA; i += NT) {
-    const int s = i / (4 * k), rem = i % (4 * k);
-    const int p = rem >> 2, q = rem & 3;
-    fs.items[i] = make_item(ITEM_PASS_A, q, p, s);
-    fs.items[nA + i] = make_item(ITEM_PASS_B, q, p, s);
-    fs.doneA[i] = 0;
-  }
-  __shared__ int gcnt[GS_GROUPS][NT];
-  __shared__ int goff[GS_GROUPS + 1];
-  const int rest = T - h;
-  const int seg = (rest + NT - 1) / NT;
-  const int e0 = h + min(rest, (int)threadIdx.x * seg), e1 = h + min(rest, ((int)threadIdx.x + 1) * seg);
-  for (int g = 0; g < GS_GROUPS; g++) gcnt[g][threadIdx.x] = 0;
-  for (int e = e0; e < e1; e++) gcnt[tile_group(fs.order[e], tiles_x)][threadIdx.x]++;
+  // 4. queues. The LPT positions e in [0, T) fall into classes (group of the
+  //    tile, chunked iff e < h); a stable partition by class keeps the LPT order
+  //    inside every class. The per-quarter bounds array (written by the forward
+  //    pass later) holds the partition's temporaries.
+  uint32_t *ck = reinterpret_cast<uint32_t *>(fs.sub_last);
+  int32_t *cv = fs.sub_last + T;
+  uint32_t *ck2 = reinterpret_cast<uint32_t *>(fs.sub_last + 2 * T);
+  int32_t *perm = fs.sub_last + 3 * T;
+  __shared__ int ccount[NCLS], cstart[NCLS], qoff[GS_GROUPS + 1];
+  if (threadIdx.x < NCLS) ccount[threadIdx.x] = 0;
   __syncthreads();
-  if (threadIdx.x < GS_GROUPS) {
-    int run = 0;
-    for (int t = 0; t < NT; t++) {
-      const int c = gcnt[threadIdx.x][t];
-      gcnt[threadIdx.x][t] = run;
-      run += c;
-    }
-    goff[threadIdx.x + 1] = run;
+  for (int e = threadIdx.x; e < T; e += NT) {
+    const uint32_t c = class_of(e, h, fs.order, tiles_x);
+    ck[e] = c;
+    cv[e] = e;
+    atomicAdd(&ccount[c], 1);
   }
   __syncthreads();
+  block_radix_pass(ck, cv, ck2, perm, T, 0);
   if (threadIdx.x == 0) {
-    goff[0] = 0;
-    for (int g = 0; g < GS_GROUPS; g++) goff[g + 1] += goff[g];
+    int run = 0, q = 0;
+    for (int c = 0; c < NCLS; c++) {
+      cstart[c] = run;
+      run += ccount[c];
+    }
+    for (int g = 0; g < GS_GROUPS; g++) {
+      qoff[g] = q;
+      q += 8 * k * ccount[2 * g] + 4 * ccount[2 * g + 1];
+    }
+    qoff[GS_GROUPS] = q;
   }
   __syncthreads();
-  for (int e = e0; e < e1; e++) {
-    const int tile = fs.order[e];
-    const int g = tile_group(tile, tiles_x);
-    const int pos = 2 * nA + 4 * (goff[g] + gcnt[g][threadIdx.x]++);
-    for (int q = 0; q < 4; q++) fs.items[pos + q] = make_item(ITEM_PLAIN, q, 0, tile);
+  for (int i = threadIdx.x; i < T; i += NT) {
+    const int e = perm[i];
+    const int c = (int)ck2[i];
+    const int g = c >> 1, r = i - cstart[c];
+    if ((c & 1) == 0) {  // chunked: LPT slot e
+      const int a0 = qoff[g] + 4 * k * r, b0 = a0 + 4 * k * ccount[c];
+      for (int p = 0; p < k; p++)
+        for (int q = 0; q < 4; q++) {
+          fs.items[a0 + 4 * p + q] = make_item(ITEM_PASS_A, q, p, e);
+          fs.items[b0 + 4 * p + q] = make_item(ITEM_PASS_B, q, p, e);
+        }
+    } else {
+      const int p0 = qoff[g] + 8 * k * ccount[c - 1] + 4 * r;
+      const int tile = fs.order[e];
+      for (int q = 0; q < 4; q++) fs.items[p0 + q] = make_item(ITEM_PLAIN, q, 0, tile);
+    }
   }
+  const int nA = 4 * h * k;
+  for (int i = threadIdx.x; i < nA; i += NT) fs.doneA[i] = 0;
   for (int i = threadIdx.x; i < 4 * h; i += NT) {
     fs.sat[i] = k;
     fs.doneB[i] = 0;
   }
-  for (int i = threadIdx.x; i < 2 * (GS_GROUPS + 1); i += NT) fs.heads[i * GS_HEAD_STRIDE] = 0;
-  if (threadIdx.x <= GS_GROUPS) fs.hdr->qoff[threadIdx.x] = 4 * goff[threadIdx.x];
+  if (threadIdx.x < GS_GROUPS) {
+    const int g = threadIdx.x;
+    const int len = qoff[g + 1] - qoff[g], qa = 4 * k * ccount[2 * g];
+    const int W = group_workers(g, nblocks);
+    // A pass-B item waits on pass-A items, so every item in front of it must be
+    // held by a running worker: a group with chunk items hands out nothing
+    // without a pop in the forward pass. The backward never waits.
+    const int init_f = qa > 0 ? 0 : min(len, W);
+    const int init_b = min(len - qa, W);
+    fs.hdr->qa[g] = qa;
+    fs.hdr->init_f[g] = init_f;
+    fs.hdr->init_b[g] = init_b;
+    queue_head(fs, 0, g)[0] = init_f;
+    queue_head(fs, 1, g)[0] = init_b;
+  }
+  if (threadIdx.x <= GS_GROUPS) fs.hdr->qoff[threadIdx.x] = qoff[threadIdx.x];
   if (threadIdx.x == 0) {
     fs.hdr->h = h;
     fs.hdr->k = k;
     fs.hdr->nA = nA;
-    fs.hdr->nplain = 4 * rest;
+    fs.hdr->nplain = 4 * (T - h);
     fs.hdr->err = 0;
     fs.hdr->ntiles = T;
     if (stats) atomicAdd(&stats[3], (unsigned long long)h);
@@ -262,11 +325,11 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
 }  // namespace
 
 hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
-                              int force_h, double lambda_, double beta, double eps, double workers,
+                              int force_h, double lambda_, double beta, double eps, int nblocks,
                               void *fwd_state, int64_t *stats, hipStream_t st) {
   const int T = cam.tiles_x * cam.tiles_y;
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(NT), 0, st, reinterpret_cast<const int2 *>(ranges), T,
-                     cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, workers,
+                     cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, nblocks,
                      reinterpret_cast<char *>(fwd_state),
                      reinterpret_cast<unsigned long long *>(stats));
   return hipGetLastError();

@@ -71,7 +71,11 @@ typedef struct {
 } gs_camera;
 
 /* Tile scheduling knobs, passed by HOST pointer (NULL = defaults:
- * chunk_mode 1, lambda/beta calibrated for this build, eps 0.10).
+ * chunk_mode 1, lambda 131072, beta 0.25, eps 0.10). The page prints neither
+ * lambda (fixed cost of one chunk, in pair units) nor beta; these values come
+ * from timing forced (h, k) plans on MI355X: with them the policy leaves
+ * scenes whose tiles saturate early unchunked and splits the outliers of
+ * scenes with long unsaturated lists.
  *   chunk_mode 0: no depth chunking (persistent longest-first queue only)
  *              1: automatic (Eq. 6 policy, evaluated on the device per frame)
  *              2: force chunking of the force_h heaviest tiles into force_k chunks

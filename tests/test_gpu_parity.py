@@ -88,7 +88,7 @@ def run_stages(gsr, sc, ref, capacity=None, sched=None):
     r.render_fwd(n, stats=True)
     grads = r.render_bwd(n, dev(sc.dL_drgb))
     out.update(rgb=host(r.rgb), T=host(r.T), last=host(r.last), grads=host(grads),
-               stats=host(r.stats))
+               stats=host(r.stats), plan=read_plan(r))
     return out
 
 
@@ -231,27 +231,65 @@ def test_full_size_configs(cfg):
 
 def _plan_layout(T):
     """Offsets into the opaque forward state, read here for checking only:
-    header (h, k, nA, nplain, err, ntiles, group offsets), queue heads,
-    per-quarter bounds, LPT order, sorted counts."""
+    header (h, k, nA, nplain, err, ntiles, group offsets, pass-A counts, static
+    hand-out counts), queue heads, per-quarter bounds, LPT order, sorted counts,
+    the queue items."""
     rnd = lambda b: (b + 255) // 256 * 256
     hdr = 0
-    heads = rnd(4 * 15)
-    sub_last = heads + rnd(4 * 2 * 9 * 16)
+    heads = rnd(4 * 39)
+    sub_last = heads + rnd(4 * 2 * 8 * 16)
     order = sub_last + rnd(16 * T)
     counts = order + rnd(4 * T)
-    return dict(hdr=hdr, order=order, counts=counts)
+    items = counts + rnd(4 * T)
+    return dict(hdr=hdr, heads=heads, order=order, counts=counts, items=items)
 
 
 def read_plan(r):
     T = r.tiles
     L = _plan_layout(T)
     raw = host(r.fwd_state)
-    hdr = raw[L["hdr"]:L["hdr"] + 60].view(np.int32)
+    hdr = raw[L["hdr"]:L["hdr"] + 156].view(np.int32)
     order = raw[L["order"]:L["order"] + 4 * T].view(np.int32)
     counts = raw[L["counts"]:L["counts"] + 4 * T].view(np.int32)
+    qoff = hdr[6:15].copy()
+    items = raw[L["items"]:L["items"] + 4 * int(qoff[-1])].view(np.int32)
     assert int(hdr[5]) == T
     return dict(h=int(hdr[0]), k=int(hdr[1]), nA=int(hdr[2]), err=int(hdr[4]), order=order,
-                counts=counts, qoff=hdr[6:15].copy())
+                counts=counts, qoff=qoff, qa=hdr[15:23].copy(), items=items.copy())
+
+
+def check_queues(plan, tiles_x):
+    """Group g's queue: the pass-A items of its chunked tiles, as many pass-B
+    items, then the quarters of its other tiles in longest-first order; every
+    item exactly once, every tile in the group of its image strip."""
+    h, k, order, items, qoff = plan["h"], plan["k"], plan["order"], plan["items"], plan["qoff"]
+    T = len(order)
+    group = lambda tile: (tile % tiles_x) * 8 // tiles_x
+    kind, quad, p, idx = (items >> 30) & 3, (items >> 28) & 3, (items >> 24) & 15, items & 0xFFFFFF
+    rank = np.empty(T, np.int64)
+    rank[order] = np.arange(T)
+    seen_a, seen_b, seen_p = set(), set(), set()
+    for g in range(8):
+        lo, hi, qa = int(qoff[g]), int(qoff[g + 1]), int(plan["qa"][g])
+        assert np.all(kind[lo:lo + qa] == 1) and np.all(kind[lo + qa:lo + 2 * qa] == 2)
+        assert np.all(kind[lo + 2 * qa:hi] == 0)
+        for a, b in ((lo, lo + qa), (lo + qa, lo + 2 * qa)):
+            slots = idx[a:b]
+            assert np.all(slots < h) and all(group(order[s]) == g for s in slots)
+            assert np.all(np.diff(slots) >= 0)  # chunked tiles in LPT order
+        for i in range(lo, lo + qa):
+            seen_a.add((int(idx[i]), int(p[i]), int(quad[i])))
+        for i in range(lo + qa, lo + 2 * qa):
+            seen_b.add((int(idx[i]), int(p[i]), int(quad[i])))
+        tiles = idx[lo + 2 * qa:hi]
+        assert all(group(t) == g for t in tiles)
+        assert np.all(np.diff(rank[tiles]) >= 0)  # longest first, quarters of a tile together
+        assert np.all(rank[tiles] >= h)
+        for i in range(lo + 2 * qa, hi):
+            seen_p.add((int(idx[i]), int(quad[i])))
+    assert len(seen_a) == len(seen_b) == 4 * h * (k if h else 0)
+    assert seen_a == seen_b and all(pp < k for _, pp, _ in seen_a)
+    assert len(seen_p) == 4 * (T - h) and int(qoff[-1]) == 8 * h * k + 4 * (T - h)
 
 
 def _workers():
@@ -269,6 +307,7 @@ def test_forced_chunking_matches_oracle(k):
     check_forward(ref, out)
     check_backward(ref, out)
     assert int(out["stats"][3]) == min(sc.camera.num_tiles, gsr.HK_MAX // k)
+    check_queues(out["plan"], (sc.camera.width + 15) // 16)
 
 
 @pytest.mark.parametrize("k,h", [(2, 3), (16, 40)])
@@ -280,6 +319,8 @@ def test_forced_chunking_ragged(k, h):
     out = run_stages(gsr, sc, ref, sched=gsr.make_sched(chunk_mode=2, force_k=k, force_h=h))
     check_forward(ref, out)
     check_backward(ref, out)
+    assert out["plan"]["h"] == h and out["plan"]["k"] == k
+    check_queues(out["plan"], (sc.camera.width + 15) // 16)
 
 
 def _policy_frame(gsr, counts, W, H):
@@ -328,9 +369,8 @@ def test_device_policy_equals_host_policy(case):
                                f32(gsr.DEFAULT_BETA), f32(gsr.DEFAULT_EPS), gsr.HK_MAX)
     assert (plan["h"], plan["k"] if plan["h"] else 1) == (h, k), (plan["h"], plan["k"], h, k)
     assert plan["nA"] == 4 * h * (k if h else 0)
-    # the group queues partition the quarters of the unchunked tiles
-    assert plan["qoff"][0] == 0 and plan["qoff"][-1] == 4 * (T - h)
-    assert np.all(np.diff(plan["qoff"]) >= 0)
+    assert plan["qoff"][0] == 0 and np.all(np.diff(plan["qoff"]) >= 0)
+    check_queues(plan, (W + 15) // 16)
     if case == "one_outlier":
         assert h >= 1
     if case == "flat":
