@@ -1,18 +1,21 @@
-"""Benchmark: one step = the whole rasterizer path on one synthetic frame.
+"""Benchmark: one step = the rasterizer hot path on one synthetic frame.
 
 Workload: the garden-shaped scene, 1,535,033 Gaussians, SH degree 3,
 1297x840 image (82 x 53 = 4346 tiles), seeded synthetic data already resident
-in HBM. One step runs gs_project, gs_bin_tiles, gs_sort_keys, gs_render_fwd and
-gs_render_bwd on one HIP stream. The headline value is tile-Gaussian pairs per
-second over the whole step; ms per stage and a roofline fraction for the
-dominant call come with it, and the CPU oracle is timed on the host beside it
-(a baseline only).
+in HBM. A step runs gs_bin_tiles, gs_sort_keys, gs_render_fwd (tile schedule
+included) and gs_render_bwd on one HIP stream over the projected splats;
+gs_project (the feeder) is timed in its own loop and reported beside it. The
+headline value is tile-Gaussian pairs per second over the step. The roofline
+object covers the longest raster kernel, with algorithmic work per unit as
+defined below, and the CPU oracle is timed on the host beside it (a baseline
+only).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,13 +26,54 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd raster ms/frame and tile-pairs/sec at 1.5M Gaussians 1297×840; % roofline"
 
-# Algorithmic work per (pixel, splat) hit, op-counted from the method's
-# definition (FMA = 2 flops): forward 21 flops + 1 exp; backward 54 flops
+# Algorithmic work per unit, op-counted from the method's definition (FMA = 2
+# flops). Per (pixel, splat) hit: forward 21 flops + 1 exp; backward 54 flops
 # (including the 9 pixel-to-splat accumulations) + exp + reciprocal.
 FWD_FLOPS_PER_HIT = 21
 BWD_FLOPS_PER_HIT = 54
+# Bytes: every (tile, splat) pair reads its 48-byte record and 4-byte id; the
+# forward writes 20 bytes per pixel (rgb, T, last); the backward reads them
+# (dL/drgb, T, last) and adds 36 bytes of gradient per (8x8 sub-tile, splat)
+# pair with at least one hit.
+PAIR_BYTES = 52
+PIXEL_BYTES = 20
+ATOMIC_BYTES = 36
 PEAK_FP32_TFLOPS = 157.3     # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0        # MI355X published HBM3E bandwidth
+
+CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_amd", "csrc")
+KERNEL_SOURCES = {
+    "k_render_fwd": ["render_fwd.hip", "render_common.h", "gs_common.h"],
+    "k_render_bwd": ["render_bwd.hip", "render_common.h", "gs_common.h", "wave_reduce.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if there
+    is none for this kernel and workload or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash(kernel):
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -41,6 +85,31 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--chunk-mode", type=int, default=1)
     return p.parse_args()
+
+
+def cpu_baseline(sc, npairs_gpu):
+    """The oracle's bin, sort, forward and backward on the same scene, repeated
+    for about 10 s of host time (projection once, outside the clock)."""
+    import oracle
+    cam = sc.camera
+    W, H = cam.width, cam.height
+    splats = oracle.project_scene(sc)
+    frames, pairs, t_total = 0, 0, 0.0
+    while t_total < 10.0 and frames < 20:
+        t0 = time.perf_counter()
+        offsets, keys, ids = oracle.bin_tiles(splats, W, H)
+        skeys, sids = oracle.sort_pairs(keys, ids)
+        ranges = oracle.tile_ranges(skeys, cam.num_tiles)
+        f = oracle.render_fwd(splats, sids, ranges, W, H)
+        oracle.render_bwd(splats, sids, ranges, W, H, f["last"], sc.dL_drgb)
+        t_total += time.perf_counter() - t0
+        frames += 1
+        pairs += len(sids)
+    return {"value": round(pairs / t_total, 1), "unit": "tile-pairs/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{frames} whole frames of the same scene through the oracle's bin, sort, "
+                      f"forward and backward ({t_total:.1f} s; {pairs // frames} pairs per frame, "
+                      f"GPU {npairs_gpu})"}
 
 
 def main():
@@ -81,41 +150,38 @@ def main():
     r.render_fwd(n, stats=True)
     torch.cuda.synchronize()
     stats = r.stats.cpu().numpy()
-    hits = int(stats[0])
+    hits, lane_evals, sub_hits = int(stats[0]), int(stats[1]), int(stats[2])
     plan = r.fwd_state[:8].cpu().numpy().view(np.int32)  # (chunked tiles h, chunks k)
     chunked, chunks = int(plan[0]), int(plan[1])
-    print(f"[bench] pairs {npairs}, hits {hits}, lane evaluations {int(stats[1])}, "
-          f"chunked tiles {chunked} x {chunks}", file=sys.stderr, flush=True)
+    print(f"[bench] pairs {npairs}, hits {hits}, lane evaluations {lane_evals}, sub-tile hits "
+          f"{sub_hits}, chunked tiles {chunked} x {chunks}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     cap = r.capacity
-    stages = ["project", "bin", "sort", "fwd", "bwd"]
+    stages = ["bin", "sort", "fwd", "bwd"]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats)
-        if ev is not None:
-            ev[1].record(stream)
         gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status, r.workspace)
         if ev is not None:
-            ev[2].record(stream)
+            ev[1].record(stream)
         gsr.gs_sort_keys(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids, r.ranges,
                          r.workspace)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
         gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T, r.last,
                           r.fwd_state, None, r.workspace)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
         gsr.gs_render_bwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last, r.fwd_state,
                           dL, r.grads, r.workspace)
         if ev is not None:
-            ev[5].record(stream)
+            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -130,31 +196,49 @@ def main():
     for ev in events:
         for i, s in enumerate(stages):
             per[s].append(ev[i].elapsed_time(ev[i + 1]))
-    ms = {s: float(np.mean(v)) for s, v in per.items()}
+    ms = {s: float(np.median(v)) for s, v in per.items()}
     ms_min = {s: float(np.min(v)) for s, v in per.items()}
     ms_step = t_wall * 1e3 / args.steps
-    ms_raster = ms["fwd"] + ms["bwd"]
 
-    # roofline of the dominant call
+    # the feeder, in its own loop
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for k in range(args.steps):
+        pe[2 * k].record(stream)
+        gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats)
+        pe[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_project = float(np.median([pe[2 * k].elapsed_time(pe[2 * k + 1]) for k in range(args.steps)]))
+
+    # roofline of the longest raster kernel: algorithmic bytes and flops per launch
+    P = cam.width * cam.height
+    work = {
+        "fwd": dict(flops=FWD_FLOPS_PER_HIT * hits, bytes=PAIR_BYTES * npairs + PIXEL_BYTES * P),
+        "bwd": dict(flops=BWD_FLOPS_PER_HIT * hits,
+                    bytes=PAIR_BYTES * npairs + PIXEL_BYTES * P + ATOMIC_BYTES * sub_hits),
+    }
+    t_roof = {s: max(w["flops"] / (PEAK_FP32_TFLOPS * 1e12), w["bytes"] / (PEAK_HBM_GBS * 1e9))
+              for s, w in work.items()}
     dom = max(("fwd", "bwd"), key=lambda s: ms[s])
-    flops = (BWD_FLOPS_PER_HIT if dom == "bwd" else FWD_FLOPS_PER_HIT) * hits
-    achieved = flops / (ms[dom] * 1e-3) / 1e12
-    roofline = {"bound": "alu", "kernel": f"gs_render_{dom}", "achieved": round(achieved, 3),
-                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None}
-    raster_flops = (FWD_FLOPS_PER_HIT + BWD_FLOPS_PER_HIT) * hits
-    raster_frac = raster_flops / (ms_raster * 1e-3) / 1e12 / PEAK_FP32_TFLOPS
+    kname = f"k_render_{dom}"
+    w = work[dom]
+    hbm_binds = w["bytes"] / (PEAK_HBM_GBS * 1e9) >= w["flops"] / (PEAK_FP32_TFLOPS * 1e12)
+    t_s = ms[dom] * 1e-3
+    traffic = measured_traffic(kname, sc.name)
+    if hbm_binds:
+        achieved = w["bytes"] / t_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        achieved = w["flops"] / t_s / 1e12
+        roofline = {"bound": "alu", "achieved": round(achieved, 3),
+                    "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic}
+    roofline.update(kernel=kname, algorithmic_bytes=w["bytes"], algorithmic_flops=w["flops"],
+                    fp32_frac=round(w["flops"] / t_s / 1e12 / PEAK_FP32_TFLOPS, 4))
+    ms_raster = ms["fwd"] + ms["bwd"]
+    raster_frac = (t_roof["fwd"] + t_roof["bwd"]) / (ms_raster * 1e-3)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        tc = time.perf_counter()
-        o = oracle.frame(sc)
-        t_cpu = time.perf_counter() - tc
-        cpu = {"value": round(len(o["sorted_ids"]) / t_cpu, 1), "unit": "tile-pairs/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"one whole frame of the same scene (project, bin, sort, forward, "
-                         f"backward; {t_cpu:.2f} s)"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(sc, npairs)
 
     line = {
         "metric": METRIC,
@@ -166,13 +250,15 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{sc.name}: {n} Gaussians, SH degree {sc.sh_degree}, "
                                f"{cam.width}x{cam.height} image, {cam.num_tiles} tiles",
-                   "pairs": npairs, "hits": hits, "chunk_mode": args.chunk_mode,
+                   "pairs": npairs, "hits": hits, "lane_evaluations": lane_evals,
+                   "subtile_hits": sub_hits, "chunk_mode": args.chunk_mode,
                    "chunked_tiles": chunked, "chunks_per_tile": chunks},
         "ms": {k: round(v, 4) for k, v in ms.items()},
         "ms_min": {k: round(v, 4) for k, v in ms_min.items()},
+        "ms_project": round(ms_project, 4),
         "ms_raster_fwd_bwd": round(ms_raster, 4),
         "raster_pairs_per_s": round(npairs / (ms_raster * 1e-3), 1),
-        "raster_frac_fp32_peak": round(raster_frac, 4),
+        "raster_roofline_frac": round(raster_frac, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -119,7 +119,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int cs, int ce,
                                              const SubTile &st, const Px &x, float T0,
                                              Splat *sbuf, uint32_t &nhits,
-                                             uint32_t &nsteps) {
+                                             uint32_t &nsteps, uint32_t &nhsteps) {
   Blend r;
   r.C0 = r.C1 = r.C2 = 0.0f;
   r.T = T0;
@@ -154,6 +154,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
         if (hm == 0) continue;
         const int pos = b + rr * GS_WAVE + j - cs;
         nhits += __popcll(hm);
+        nhsteps++;
         r.wlast = pos + 1;
         const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
         const float al = hit ? fminf(0.99f, ex) : 0.0f;
@@ -261,7 +262,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
   const int k = fs.hdr->k;
   const int P = cam.width * cam.height;
   const int lane = __lane_id();
-  uint32_t nhits = 0, nsteps = 0;  // per worker; far below 2^32
+  uint32_t nhits = 0, nsteps = 0, nhsteps = 0;  // per worker; far below 2^32
   Worker wk = make_worker();
   for (;;) {
     const int t = next_item(fs, 0, wk);
@@ -279,7 +280,8 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
         if (lane == 0) fs.sub_last[tile * 4 + quad] = 0;
         continue;
       }
-      const Blend r = blend_range(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits, nsteps);
+      const Blend r = blend_range(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits, nsteps,
+                                    nhsteps);
       if (x.inside) {
         rgb[x.p] = r.C0;
         rgb[P + x.p] = r.C1;
@@ -340,7 +342,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
     r.wlast = 0;
     const bool skip = st.empty || ld_i(sat) < p;
     if (!skip) {
-      r = blend_range(splats, sorted_ids, cs, ce, st, x, Tin, sbuf, nhits, nsteps);
+      r = blend_range(splats, sorted_ids, cs, ce, st, x, Tin, sbuf, nhits, nsteps, nhsteps);
       if (!(x.inside && Tin >= T_STOP)) r.consumed = -1;  // stopped before this chunk
     }
     const int64_t cp = (int64_t)ci * 64 + lane;
@@ -385,7 +387,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
   if (stats && lane == 0) {
     atomicAdd(&stats[0], (unsigned long long)nhits);
     atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
-    atomicAdd(&stats[2], (unsigned long long)nsteps);
+    atomicAdd(&stats[2], (unsigned long long)nhsteps);
   }
 }
 

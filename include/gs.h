@@ -152,7 +152,11 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
  *   last [H][W] <- list entries the pixel consumed (stop index + 1, or the
  *                  tile's full length when it never stopped)
  *   fwd_state <- opaque, gs_fwd_state_size bytes, read by gs_render_bwd
- *   stats [4] or NULL <- += {hits, lane evaluations, wave-splat steps, chunked tiles} */
+ *   stats [4] or NULL <- += {hits: (pixel, splat) pairs blended; lane evaluations:
+ *                          64 x (8x8 sub-tile, splat) pairs tested; sub-tile hits:
+ *                          (8x8 sub-tile, splat) pairs with at least one hit, which
+ *                          is the number of gradient atomics the backward issues;
+ *                          chunked tiles h} */
 int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
                       float *rgb, float *T_final, int32_t *last, void *fwd_state,
