@@ -169,7 +169,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_bwd(
   for (;;) {
     const int t = next_item(fs, 1, wk);
     if (t < 0) break;
-    set_round_priority(wk.round++);
+    wk.round++;
     const int it = fs.items[t];
     const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
     const int idx = item_index(it);

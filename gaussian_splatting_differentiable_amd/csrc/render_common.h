@@ -174,21 +174,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Issue priority of a worker on its `round`-th item (0 = first). A SIMD issues
-// from the highest-priority ready wave and breaks ties by wave age, so a worker
-// wave dispatched late would otherwise be starved by older workers for as long
-// as they find work, and its item would finish last. Lowering the priority
-// with every item a worker takes approximates first-come-first-served across
-// items instead.
-__device__ __forceinline__ void set_round_priority(int round) {
-  switch (round) {
-    case 0: __builtin_amdgcn_s_setprio(3); break;
-    case 1: __builtin_amdgcn_s_setprio(2); break;
-    case 2: __builtin_amdgcn_s_setprio(1); break;
-    default: __builtin_amdgcn_s_setprio(0); break;
-  }
-}
-
 // Wave-uniform queue pop: one lane advances the head, every lane gets the ticket.
 __device__ __forceinline__ int queue_pop(int32_t *head) {
   int t = 0;

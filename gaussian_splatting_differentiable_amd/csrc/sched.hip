@@ -64,19 +64,35 @@ __device__ __forceinline__ V block_excl_scan(V v, V &total) {
   return before + inc - v;
 }
 
+// Per-lane register batch of the single-workgroup passes below: a wave loads
+// RB_ROUNDS rounds of 64 elements before it uses any of them, so each batch
+// costs one global-memory round trip instead of one per round.
+constexpr int RB_ROUNDS = 8;
+
 // One stable LSD pass (8-bit digit at `shift`) of (key, val) over n elements in
 // global memory, by one workgroup. Wave w owns the contiguous chunk
 // [w*chunk, (w+1)*chunk); a first sweep counts digits per wave, a second sweep
 // ranks each round of 64 with a ballot match and scatters.
-__device__ void block_radix_pass(const uint32_t *kin, const int32_t *vin, uint32_t *kout,
-                                 int32_t *vout, int n, int shift) {
+__device__ void block_radix_pass(const uint32_t *__restrict__ kin, const int32_t *__restrict__ vin,
+                                 uint32_t *__restrict__ kout, int32_t *__restrict__ vout, int n,
+                                 int shift) {
   __shared__ int cnt[NW][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < NW * 256; i += NT) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const int chunk = (n + NW - 1) / NW;
   const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
-  for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&cnt[w][(kin[e] >> shift) & 255], 1);
+  for (int base = c0; base < c1; base += 64 * RB_ROUNDS) {
+    uint32_t kk[RB_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const int e = base + 64 * r + lane;
+      kk[r] = e < c1 ? kin[e] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++)
+      if (base + 64 * r + lane < c1) atomicAdd(&cnt[w][(kk[r] >> shift) & 255], 1);
+  }
   __syncthreads();
   // offsets in (digit, wave) order: within a digit over the waves, then the
   // digit totals scanned by the whole block
@@ -94,34 +110,38 @@ __device__ void block_radix_pass(const uint32_t *kin, const int32_t *vin, uint32
     for (int q = 0; q < NW; q++) cnt[q][threadIdx.x] += dbase;
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int base = c0; base < c1; base += 64) {
-    const int e = base + lane;
-    const bool valid = e < c1;
-    const uint32_t k = valid ? kin[e] : 0u;
-    const int32_t v = valid ? vin[e] : 0;
-    const uint32_t d = (k >> shift) & 255u;
-    uint64_t peers = __ballot(valid);
+  for (int base = c0; base < c1; base += 64 * RB_ROUNDS) {
+    uint32_t kk[RB_ROUNDS];
+    int32_t vv[RB_ROUNDS];
 #pragma unroll
-    for (int b = 0; b < 8; b++) {
-      const uint64_t bal = __ballot((d >> b) & 1u);
-      peers &= ((d >> b) & 1u) ? bal : ~bal;
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const int e = base + 64 * r + lane;
+      kk[r] = e < c1 ? kin[e] : 0u;
+      vv[r] = e < c1 ? vin[e] : 0;
     }
-    if (valid) {
-      const int below = __popcll(peers & lt);
-      const int pos = cnt[w][d] + below;
-      kout[pos] = k;
-      vout[pos] = v;
-      if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const bool valid = base + 64 * r + lane < c1;
+      const uint32_t d = (kk[r] >> shift) & 255u;
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; b++) {
+        const uint64_t bal = __ballot((d >> b) & 1u);
+        peers &= ((d >> b) & 1u) ? bal : ~bal;
+      }
+      if (valid) {
+        const int below = __popcll(peers & lt);
+        const int pos = cnt[w][d] + below;
+        kout[pos] = kk[r];
+        vout[pos] = vv[r];
+        if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+      }
     }
   }
   __syncthreads();
 }
 
 constexpr int NCLS = 2 * GS_GROUPS;  // (group, chunked?) classes of the LPT positions
-
-__device__ __forceinline__ uint32_t class_of(int e, int h, const int32_t *order, int tiles_x) {
-  return 2u * (uint32_t)tile_group(order[e], tiles_x) + (e >= h ? 1u : 0u);
-}
 
 __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges, int T, int tiles_x,
                                                  int chunk_mode, int force_k, int force_h,
@@ -135,12 +155,23 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   uint32_t *key = reinterpret_cast<uint32_t *>(fs.counts);
   // 1. counts and the (bit-limited) descending key
   uint32_t mx = 0;
-  for (int t = threadIdx.x; t < T; t += NT) {
-    const int2 r = ranges[t];
-    const uint32_t c = (uint32_t)max(0, r.y - r.x);
-    key[t] = c;
-    fs.order[t] = t;
-    mx = max(mx, c);
+  for (int t0 = threadIdx.x; t0 < T; t0 += NT * RB_ROUNDS) {
+    int2 rr[RB_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const int t = t0 + r * NT;
+      rr[r] = t < T ? ranges[t] : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const int t = t0 + r * NT;
+      if (t < T) {
+        const uint32_t c = (uint32_t)max(0, rr[r].y - rr[r].x);
+        key[t] = c;
+        fs.order[t] = t;
+        mx = max(mx, c);
+      }
+    }
   }
   mx = block_max(mx);
   int bits = 0;
@@ -163,7 +194,14 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     }
     __syncthreads();
   }
-  for (int t = threadIdx.x; t < T; t += NT) fs.counts[t] = (int32_t)(full - key[t]);
+  for (int t0 = threadIdx.x; t0 < T; t0 += NT * RB_ROUNDS) {
+    uint32_t kk[RB_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) kk[r] = t0 + r * NT < T ? key[t0 + r * NT] : 0u;
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++)
+      if (t0 + r * NT < T) fs.counts[t0 + r * NT] = (int32_t)(full - kk[r]);
+  }
   __syncthreads();
 
   // 3. chunking policy
@@ -175,6 +213,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   } else if (chunk_mode == 1 && T > 0) {
     constexpr int HMAX = GS_HK_MAX / 2;  // the largest h of any candidate
     __shared__ long long sS[HMAX + 1];   // sS[h] = N_1 + ... + N_h (exact)
+    __shared__ int sN[HMAX + 1];         // sN[h] = N_{h+1} (0 past the last tile)
     __shared__ double s_best[NT];
     __shared__ int s_idx[NT];
     long long total_ll = 0;
@@ -189,7 +228,12 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
       const long long before = block_excl_scan<long long>(a + b, all);
       sS[i0 + 1] = before + a;
       sS[i0 + 2] = before + a + b;
-      if (threadIdx.x == 0) sS[0] = 0;
+      sN[i0] = (int)a;
+      sN[i0 + 1] = (int)b;
+      if (threadIdx.x == 0) {
+        sS[0] = 0;
+        sN[HMAX] = HMAX < T ? fs.counts[HMAX] : 0;
+      }
     }
     __syncthreads();
     const double Nt = (double)tot, N1 = (double)fs.counts[0];
@@ -207,7 +251,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
       const int q = i < off[1] ? 0 : (i < off[2] ? 1 : (i < off[3] ? 2 : 3));
       const int kk = 2 << q;
       const int hh = i - off[q] + 1;
-      const double next = hh < T ? (double)fs.counts[hh] : 0.0;
+      const double next = hh < T ? (double)sN[hh] : 0.0;
       const double l = fmax((2.0 * N1) / (double)kk, next);
       const double avg = ((Nt + (double)sS[hh]) + (lambda_ * (double)hh) * (double)kk) / workers;
       const double est = fmax(avg, l) + beta * l;
@@ -251,11 +295,23 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   __shared__ int ccount[NCLS], cstart[NCLS], qoff[GS_GROUPS + 1];
   if (threadIdx.x < NCLS) ccount[threadIdx.x] = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < T; e += NT) {
-    const uint32_t c = class_of(e, h, fs.order, tiles_x);
-    ck[e] = c;
-    cv[e] = e;
-    atomicAdd(&ccount[c], 1);
+  for (int e0 = threadIdx.x; e0 < T; e0 += NT * RB_ROUNDS) {
+    int tl[RB_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const int e = e0 + r * NT;
+      tl[r] = e < T ? fs.order[e] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < RB_ROUNDS; r++) {
+      const int e = e0 + r * NT;
+      if (e < T) {
+        const uint32_t c = 2u * (uint32_t)tile_group(tl[r], tiles_x) + (e >= h ? 1u : 0u);
+        ck[e] = c;
+        cv[e] = e;
+        atomicAdd(&ccount[c], 1);
+      }
+    }
   }
   __syncthreads();
   block_radix_pass(ck, cv, ck2, perm, T, 0);
@@ -272,9 +328,22 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     qoff[GS_GROUPS] = q;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < T; i += NT) {
-    const int e = perm[i];
-    const int c = (int)ck2[i];
+  for (int i0 = threadIdx.x; i0 < T; i0 += NT * RB_ROUNDS) {
+    int ee[RB_ROUNDS], cc[RB_ROUNDS], tl[RB_ROUNDS];
+#pragma unroll
+    for (int u = 0; u < RB_ROUNDS; u++) {
+      const int i = i0 + u * NT;
+      ee[u] = i < T ? perm[i] : 0;
+      cc[u] = i < T ? (int)ck2[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < RB_ROUNDS; u++) tl[u] = fs.order[ee[u]];
+#pragma unroll
+    for (int u = 0; u < RB_ROUNDS; u++) {
+    const int i = i0 + u * NT;
+    if (i >= T) continue;
+    const int e = ee[u];
+    const int c = cc[u];
     const int g = c >> 1, r = i - cstart[c];
     if ((c & 1) == 0) {  // chunked: LPT slot e
       const int a0 = qoff[g] + 4 * k * r, b0 = a0 + 4 * k * ccount[c];
@@ -285,8 +354,9 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
         }
     } else {
       const int p0 = qoff[g] + 8 * k * ccount[c - 1] + 4 * r;
-      const int tile = fs.order[e];
+      const int tile = tl[u];
       for (int q = 0; q < 4; q++) fs.items[p0 + q] = make_item(ITEM_PLAIN, q, 0, tile);
+    }
     }
   }
   const int nA = 4 * h * k;
