@@ -10,10 +10,9 @@ hipError_t gs_launch_project(int n, const float *means, const float *log_scales,
                              const float *opac, const float *sh, int degree, const CamK &cam,
                              float *splats, hipStream_t st);
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
-                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status,
-                         int32_t *scan_buf, hipStream_t st);
-size_t gs_sort_ws_bytes(int n, int64_t cap, int ntiles);
-int gs_scan_buf_elems(int n_max);
+                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
+                         hipStream_t st);
+size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y);
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
                           int32_t *ranges, void *ws, hipStream_t st);
@@ -106,9 +105,7 @@ size_t gs_fwd_state_size(int32_t width, int32_t height) {
 
 size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity) {
   if (n < 0 || width <= 0 || height <= 0 || pair_capacity < 0) return 0;
-  const size_t bin = round256((size_t)gs_scan_buf_elems(n) * sizeof(int32_t));
-  const size_t sort = gs_sort_ws_bytes(n, pair_capacity, (int)num_tiles(width, height));
-  return bin > sort ? bin : sort;
+  return gs_sort_ws_bytes(n, pair_capacity, (width + 15) / 16, (height + 15) / 16);
 }
 
 int32_t gs_project(int32_t n, const float *means, const float *log_scales, const float *quats,
@@ -136,7 +133,7 @@ int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64
   if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
     return GS_ERR_WORKSPACE;
   return hip_status(gs_launch_bin(n, splats, k, pair_capacity, offsets, keys, ids, device_status,
-                                  reinterpret_cast<int32_t *>(workspace), (hipStream_t)stream));
+                                  workspace, (hipStream_t)stream));
 }
 
 int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,

@@ -12,30 +12,14 @@
 // -ffp-contract=off: every operation below rounds on its own and fmaf appears
 // only where written, so the emitted pairs are reproducible bit for bit.
 //
-// Kernels: k_bin_count (per-splat pair count into offsets[]), a device-wide
+// Kernels: the counting pass (sort.hip: per-splat pair counts into offsets[],
+// plus what the sort needs from the same pass over the records), a device-wide
 // exclusive scan (scan.hip), then k_bin_emit (status; keys/ids at the offsets
 // in splat-id order when the caller asks for them). The sort stage re-emits the
 // pairs directly in depth order, so the frame does not need the id-order list.
 #include "bin_spans.h"
 
 namespace {
-
-__global__ void __launch_bounds__(256) k_bin_count(int n, const Splat *__restrict__ splats, int W,
-                                                   int H, int tiles_x, int tiles_y,
-                                                   int32_t *__restrict__ counts) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const RowSpans r = spans_setup(splats[i], tiles_y);
-  int cnt = 0;
-  if (r.ok) {
-    for (int ty = r.ty_a; ty < r.ty_b; ty++) {
-      int a, b;
-      row_span(r, ty, W, H, tiles_x, a, b);
-      cnt += b > a ? b - a : 0;
-    }
-  }
-  counts[i] = cnt;
-}
 
 __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict__ splats, int W,
                                                   int H, int tiles_x, int tiles_y,
@@ -71,17 +55,19 @@ __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict
 
 hipError_t gs_launch_scan_i32(const int32_t *in, int32_t *out, int n, int32_t *block_buf,
                               hipStream_t st);
+hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int64_t cap,
+                               int32_t *counts, void *ws, int32_t **scan_buf, hipStream_t st);
 
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
-                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status,
-                         int32_t *scan_buf, hipStream_t st) {
+                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
+                         hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   dim3 block(256), grid(gs_div_up(n > 0 ? n : 1, 256));
-  if (n > 0)
-    hipLaunchKernelGGL(k_bin_count, grid, block, 0, st, n, sp, cam.width, cam.height, cam.tiles_x,
-                       cam.tiles_y, offsets);
+  int32_t *scan_buf = nullptr;
+  hipError_t e = gs_launch_bin_count(n, splats, cam, capacity, offsets, ws, &scan_buf, st);
+  if (e != hipSuccess) return e;
   // exclusive scan of the n counts, total in offsets[n]
-  hipError_t e = gs_launch_scan_i32(offsets, offsets, n, scan_buf, st);
+  e = gs_launch_scan_i32(offsets, offsets, n, scan_buf, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bin_emit, grid, block, 0, st, n, sp, cam.width, cam.height, cam.tiles_x,
                      cam.tiles_y, offsets, capacity, keys, ids, status);

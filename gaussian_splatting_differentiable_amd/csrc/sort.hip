@@ -1,4 +1,5 @@
-// gs_sort_keys: order the (tile, depth) pairs and cut the tile ranges.
+// Pair ordering for the tile rasterizer: the counting half of gs_bin_tiles and
+// all of gs_sort_keys.
 //
 // "What the 3DGS Literature Left on the Table", Step 1 (d), Figure 5: filter the
 // visible splats, sort them once front to back by their 32-bit depth, emit the
@@ -6,14 +7,29 @@
 // The result is ordered by (tile, depth, splat id): the depth sort is stable over
 // an id-ordered input and the tile sort is stable.
 //
-// Radix passes are onesweep-style LSD passes, one kernel per digit. A block takes
-// a partition by atomic ticket, ranks its 4096 keys stably (per-wave ballot match
-// on the digit bits), publishes its digit counts and looks back over earlier
-// partitions for its global offsets (decoupled look-back: a partition only waits
-// for partitions with a lower ticket, which are already running, and the wait is
-// bounded). Keys are reordered in LDS so that global writes are contiguous runs
-// per digit. Per-tile counts come from an LDS histogram in the emission kernel;
-// the tile ranges are their exclusive prefix sum.
+// gs_bin_tiles counts every splat's pairs with the canonical row spans and, in
+// the same pass over the splat records, leaves in the workspace what the sort
+// needs: each splat's 32-bit depth key (or "no pairs"), the four depth-digit
+// histograms and the per-tile pair counts (LDS histograms per workgroup). It
+// also clears the look-back words of every radix pass of the frame.
+//
+// gs_sort_keys then runs:
+//   - four onesweep LSD passes over the visible splats' depth keys (4096-key
+//     partitions), the last of which also writes each splat's pair count in
+//     depth order;
+//   - an exclusive scan of those counts: the pair offsets in depth order, and
+//     for every 16384-pair partition the splat its first pair belongs to;
+//   - the first tile pass (low 8 bits of the tile id) with the emission fused
+//     in: a partition generates its own pairs into LDS from the splats that
+//     cover it, so the depth-ordered pair list is never written to memory;
+//   - the second tile pass (the high bits), writing the sorted ids.
+//
+// A onesweep pass: a workgroup takes a partition by atomic ticket, ranks its
+// keys stably (per-wave ballot match on the digit bits), publishes its digit
+// counts and looks back over earlier partitions for its global offsets
+// (decoupled look-back: a partition only waits for partitions with a lower
+// ticket, which are already running, and the wait is bounded). Keys are
+// reordered in LDS so that global writes are contiguous runs per digit.
 //
 // This TU includes the canonical binning code: compile with -ffp-contract=off.
 #include <stddef.h>
@@ -22,20 +38,23 @@
 
 namespace {
 
-constexpr int OS_THREADS = 1024;
-constexpr int OS_WAVES = OS_THREADS / 64;
-constexpr int OS_ITEMS = 16;
-constexpr int OS_PART = OS_THREADS * OS_ITEMS;  // keys per partition
 constexpr uint32_t ST_AGG = 1u << 30, ST_INC = 2u << 30, ST_CNT = (1u << 30) - 1;
 constexpr int SPIN_LIMIT = 1 << 22;
 constexpr int HIST_TILES_LDS = 16384;  // tile histogram kept in LDS up to this many tiles
 constexpr int SCAN_T = 256, SCAN_I = 8, SCAN_TILE = SCAN_T * SCAN_I;
+constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pairs (a NaN pattern)
+constexpr int BIN_T = 256, BIN_BLOCKS_MAX = 512;
 
-// Per-call control block at the start of the sort workspace.
+// partitions: depth passes and tile passes
+constexpr int DS_THREADS = 256, DS_ITEMS = 16, DS_PART = DS_THREADS * DS_ITEMS;
+constexpr int TS_THREADS = 512, TS_ITEMS = 16, TS_PART = TS_THREADS * TS_ITEMS;
+
+// Per-frame control block at the start of the workspace.
 struct SortCtl {
   int32_t m;               // visible splats (with at least one pair)
   int32_t npairs;          // pairs of this frame (0 after an overflow)
   int32_t err;             // a look-back wait hit its bound (never expected)
+  int32_t overflow;        // the frame's pairs exceed the capacity
   int32_t tickets[8];      // partition tickets, one per radix pass
   uint32_t dhist[4][256];  // depth digit histograms
   uint32_t dbase[4][256];  // depth digit exclusive offsets
@@ -51,9 +70,11 @@ __device__ __forceinline__ void st_status(uint32_t *p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Inclusive scan over a 256-thread block; total of the block in `total`.
-__device__ __forceinline__ int block_scan256(int v, int &total) {
-  __shared__ int wsum[4];
+// Inclusive scan over a block of NT threads; total of the block in `total`.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int &total) {
+  constexpr int NWV = NT / 64;
+  __shared__ int wsum[NWV];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -64,7 +85,7 @@ __device__ __forceinline__ int block_scan256(int v, int &total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; w++) {
+  for (int w = 0; w < NWV; w++) {
     base += (w < wid) ? wsum[w] : 0;
     tot += wsum[w];
   }
@@ -73,124 +94,280 @@ __device__ __forceinline__ int block_scan256(int v, int &total) {
   return v + base;
 }
 
-__device__ __forceinline__ bool splat_visible(const int32_t *offsets, int i, bool overflow) {
-  return !overflow && offsets[i + 1] > offsets[i];
+// ---------------------------------------------------------------- workspace layout
+
+__host__ __device__ inline int64_t parts_of(int64_t n, int part) { return (n + part - 1) / part; }
+
+struct SortWs {
+  SortCtl *ctl;
+  int32_t *tile_counts;     // T
+  int32_t *tile_diff;       // tiles_y x (tiles_x + 1): per-row difference array of pair counts
+  uint32_t *dkey;           // n: depth key per splat (NO_DEPTH without pairs)
+  uint32_t *dk[2], *dv[2];  // n each: depth passes
+  int32_t *dcnt;            // n: pair counts in depth order
+  int32_t *doff;            // n + 1: pair offsets in depth order
+  int32_t *part_first;      // tile partitions: the splat (depth rank) of the first pair
+  int32_t *bsum;            // block sums of the depth-order scan
+  uint32_t *tk[2], *tv[2];  // capacity each: tile passes
+  uint32_t *status;         // look-back words: 4 depth passes, then 2 tile passes
+  int32_t *scan_buf;        // the binning scan's block buffer
+  int64_t pd, pt;           // status words per depth pass / per tile pass
+  int64_t nstatus;
+  size_t bytes;
+};
+
+SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y, int scan_elems) {
+  const int ntiles = tiles_x * tiles_y;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    char *r = base + off;
+    off += (size_t)((bytes + 255) / 256) * 256;
+    return r;
+  };
+  SortWs w;
+  const int64_t n2 = (int64_t)n + 2;
+  w.ctl = (SortCtl *)take(sizeof(SortCtl));
+  w.tile_counts = (int32_t *)take(4 * (int64_t)(ntiles + 1));
+  w.tile_diff = (int32_t *)take(4 * (int64_t)tiles_y * (tiles_x + 1));
+  w.dkey = (uint32_t *)take(4 * n2);
+  for (int i = 0; i < 2; i++) w.dk[i] = (uint32_t *)take(4 * n2);
+  for (int i = 0; i < 2; i++) w.dv[i] = (uint32_t *)take(4 * n2);
+  w.dcnt = (int32_t *)take(4 * n2);
+  w.doff = (int32_t *)take(4 * n2);
+  w.part_first = (int32_t *)take(4 * (parts_of(cap, TS_PART) + 2));
+  w.bsum = (int32_t *)take(4 * ((int64_t)n / SCAN_TILE + 4));
+  for (int i = 0; i < 2; i++) w.tk[i] = (uint32_t *)take(4 * (cap + 2));
+  for (int i = 0; i < 2; i++) w.tv[i] = (uint32_t *)take(4 * (cap + 2));
+  w.pd = (parts_of(n, DS_PART) + 1) * 256;
+  w.pt = (parts_of(cap, TS_PART) + 1) * 256;
+  w.nstatus = 4 * w.pd + 2 * w.pt;
+  w.status = (uint32_t *)take(4 * w.nstatus);
+  w.scan_buf = (int32_t *)take(4 * (int64_t)scan_elems);
+  w.bytes = off;
+  return w;
 }
 
-// Inclusive scan over a block of OS_THREADS threads; total in `total`.
-__device__ __forceinline__ int block_scan_os(int v, int &total) {
-  __shared__ int wsum[OS_WAVES];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  if (lane == 63) wsum[wid] = v;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < OS_WAVES; w++) {
-    base += (w < wid) ? wsum[w] : 0;
-    tot += wsum[w];
-  }
-  __syncthreads();
-  total = tot;
-  return v + base;
-}
+// ---------------------------------------------------------------- binning side
 
-// ---------------------------------------------------------------- setup
-
-__global__ void __launch_bounds__(1024) k_sort_init(SortCtl *__restrict__ ctl,
-                                                    int32_t *__restrict__ tile_counts, int ntiles) {
+__global__ void __launch_bounds__(1024) k_bin_init(SortCtl *__restrict__ ctl,
+                                                   int32_t *__restrict__ tile_diff, int ndiff) {
   int32_t *w = reinterpret_cast<int32_t *>(ctl);
   const int nw = (int)(sizeof(SortCtl) / 4);
   for (int i = threadIdx.x; i < nw; i += blockDim.x) w[i] = 0;
-  for (int i = threadIdx.x; i < ntiles; i += blockDim.x) tile_counts[i] = 0;
+  for (int i = threadIdx.x; i < ndiff; i += blockDim.x) tile_diff[i] = 0;
 }
 
-// Depth digit histograms of the visible splats (all four passes at once); also
-// clears the look-back status words of every pass.
-__global__ void __launch_bounds__(256) k_depth_hist(int n, const Splat *__restrict__ splats,
-                                                   const int32_t *__restrict__ offsets,
-                                                   int64_t cap, SortCtl *__restrict__ ctl,
-                                                   uint32_t *__restrict__ status, int64_t nstatus) {
-  __shared__ uint32_t h[4][256];
-  for (int i = threadIdx.x; i < 1024; i += 256) (&h[0][0])[i] = 0;
-  __syncthreads();
-  const bool overflow = (int64_t)offsets[n] > cap;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nstatus;
-       i += (int64_t)gridDim.x * 256)
+// Per-splat pair counts (exact spans), plus the depth keys, the depth-digit
+// histograms and the per-row difference array of the tile counts (+1 where a
+// row span starts, -1 where it ends: two updates per row, however long the
+// span) for the sort; clears the sort's look-back words.
+__global__ void __launch_bounds__(BIN_T) k_bin_count(
+    int n, const Splat *__restrict__ splats, int W, int H, int tiles_x, int tiles_y,
+    int32_t *__restrict__ counts, uint32_t *__restrict__ dkey, SortCtl *__restrict__ ctl,
+    int32_t *__restrict__ tile_diff, uint32_t *__restrict__ status, int64_t nstatus) {
+  __shared__ uint32_t dh[4][256];
+  extern __shared__ int th[];  // the difference array, when it fits (sized at launch)
+  const int stride = tiles_x + 1;
+  const int ndiff = tiles_y * stride;
+  const bool lds_hist = ndiff <= HIST_TILES_LDS;
+  for (int i = threadIdx.x; i < 1024; i += BIN_T) (&dh[0][0])[i] = 0;
+  if (lds_hist)
+    for (int i = threadIdx.x; i < ndiff; i += BIN_T) th[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * BIN_T + threadIdx.x; i < nstatus;
+       i += (int64_t)gridDim.x * BIN_T)
     status[i] = 0;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-    if (!splat_visible(offsets, i, overflow)) continue;
-    const uint32_t k = __float_as_uint(splats[i].p2.z);
+  __syncthreads();
+  for (int i = blockIdx.x * BIN_T + threadIdx.x; i < n; i += gridDim.x * BIN_T) {
+    const Splat s = splats[i];
+    const RowSpans r = spans_setup(s, tiles_y);
+    int cnt = 0;
+    if (r.ok) {
+      for (int ty = r.ty_a; ty < r.ty_b; ty++) {
+        int a, b;
+        row_span(r, ty, W, H, tiles_x, a, b);
+        if (b > a) {
+          int32_t *h = lds_hist ? th : tile_diff;
+          atomicAdd(&h[ty * stride + a], 1);
+          atomicAdd(&h[ty * stride + b], -1);
+          cnt += b - a;
+        }
+      }
+    }
+    counts[i] = cnt;
+    uint32_t k = NO_DEPTH;
+    if (cnt > 0) {
+      k = __float_as_uint(s.p2.z);
 #pragma unroll
-    for (int p = 0; p < 4; p++) atomicAdd(&h[p][(k >> (8 * p)) & 255], 1u);
+      for (int p = 0; p < 3; p++) atomicAdd(&dh[p][(k >> (8 * p)) & 255], 1u);
+    }
+    dkey[i] = k;
+    // the top digit (sign and high exponent bits) takes a handful of values in
+    // a frame: count it once per distinct value in the wave, not per lane
+    uint64_t todo = __ballot(cnt > 0);
+    const uint32_t d3 = k >> 24;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const uint32_t dl = (uint32_t)__shfl((int)d3, leader, 64);
+      const uint64_t same = __ballot(cnt > 0 && d3 == dl) & todo;
+      if (__lane_id() == leader) atomicAdd(&dh[3][dl], (uint32_t)__popcll(same));
+      todo &= ~same;
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 1024; i += 256) {
-    const uint32_t v = (&h[0][0])[i];
+  for (int i = threadIdx.x; i < 1024; i += BIN_T) {
+    const uint32_t v = (&dh[0][0])[i];
     if (v) atomicAdd(&ctl->dhist[0][0] + i, v);
   }
+  if (lds_hist)
+    for (int i = threadIdx.x; i < ndiff; i += BIN_T)
+      if (th[i]) atomicAdd(&tile_diff[i], th[i]);
 }
 
-__global__ void __launch_bounds__(256) k_depth_bases(SortCtl *__restrict__ ctl) {
+// ---------------------------------------------------------------- sort setup
+
+// Depth digit offsets and the number of visible splats; an overflowing frame
+// sorts nothing.
+__global__ void __launch_bounds__(256) k_depth_bases(SortCtl *__restrict__ ctl,
+                                                     const int32_t *__restrict__ offsets, int n,
+                                                     int64_t cap) {
+  const bool overflow = (int64_t)offsets[n] > cap;
+  if (threadIdx.x < 8) ctl->tickets[threadIdx.x] = 0;
+  if (threadIdx.x == 0) ctl->err = 0;
   for (int p = 0; p < 4; p++) {
     int tot;
-    const int v = (int)ctl->dhist[p][threadIdx.x];
-    const int incl = block_scan256(v, tot);
+    const int v = overflow ? 0 : (int)ctl->dhist[p][threadIdx.x];
+    const int incl = block_scan<256>(v, tot);
     ctl->dbase[p][threadIdx.x] = (uint32_t)(incl - v);
-    if (p == 0 && threadIdx.x == 0) ctl->m = tot;
+    if (p == 0 && threadIdx.x == 0) {
+      ctl->m = tot;
+      ctl->overflow = overflow ? 1 : 0;
+    }
   }
 }
 
 // ---------------------------------------------------------------- onesweep pass
 
-// FIRST: the keys are the depths of the visible splats read in id order (the
-// compaction is fused into the first pass); otherwise keys/values come from kin/vin.
-template <int BITS, bool FIRST>
-__global__ void __launch_bounds__(OS_THREADS) k_onesweep(
+enum Src { SRC_KEYS = 0, SRC_DEPTH0 = 1, SRC_EMIT = 2 };
+
+// Inputs of one pass beyond the (key, value) arrays.
+struct PassIn {
+  const SortCtl *ctl;
+  const uint32_t *dkey;        // SRC_DEPTH0
+  const int32_t *offsets;      // last depth pass: pair counts
+  int32_t *cout;               // last depth pass: pair counts in depth order (or null)
+  const uint32_t *dval;        // SRC_EMIT: splat ids in depth order
+  const int32_t *doff;         // SRC_EMIT: pair offsets in depth order
+  const int32_t *part_first;   // SRC_EMIT
+  const Splat *splats;         // SRC_EMIT
+  int W, H, tiles_x, tiles_y;  // SRC_EMIT
+};
+
+template <int NT, int ITEMS, int BITS, int SRC>
+__global__ void __launch_bounds__(NT) k_onesweep(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
-    uint32_t *__restrict__ vout, const int32_t *__restrict__ n_dev, int n_max,
-    const Splat *__restrict__ splats, const int32_t *__restrict__ offsets, int64_t cap, int shift,
+    uint32_t *__restrict__ vout, const int32_t *__restrict__ n_dev, int n_max, int shift,
     const uint32_t *__restrict__ digit_base, uint32_t *__restrict__ status,
-    int32_t *__restrict__ ticket, int32_t *__restrict__ err) {
+    int32_t *__restrict__ ticket, int32_t *__restrict__ err, PassIn in) {
   constexpr int B = 1 << BITS;
-  __shared__ uint32_t s_key[OS_PART];
-  __shared__ uint32_t s_val[OS_PART];
-  __shared__ int s_wcnt[OS_WAVES][B];
+  constexpr int NWV = NT / 64;
+  constexpr int PART = NT * ITEMS;
+  __shared__ uint32_t s_key[PART];
+  __shared__ uint32_t s_val[PART];
+  __shared__ int s_wcnt[NWV][B];
   __shared__ int s_lbase[B];
   __shared__ uint32_t s_gbase[B];
   __shared__ int s_part, s_nvalid;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) s_part = atomicAdd(ticket, 1);
-  for (int i = tid; i < OS_WAVES * B; i += OS_THREADS) (&s_wcnt[0][0])[i] = 0;
+  for (int i = tid; i < NWV * B; i += NT) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
   const int part = s_part;
-  const int n = FIRST ? n_max : clamp_n(*n_dev, n_max);
-  const bool overflow = FIRST ? ((int64_t)offsets[n_max] > cap) : false;
-  const int64_t base = (int64_t)part * OS_PART + (int64_t)w * (OS_ITEMS * 64);
-  const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t key[OS_ITEMS], val[OS_ITEMS];
-  int rnk[OS_ITEMS];
+  const int n = SRC == SRC_DEPTH0 ? n_max : clamp_n(*n_dev, n_max);
+  const int64_t p0 = (int64_t)part * PART;
+  if constexpr (SRC == SRC_DEPTH0) {
+    if (p0 >= n) return;  // past the last splat
+  } else {
+    if (p0 >= n) return;  // past the last key: no later partition waits on it
+  }
+  if constexpr (SRC == SRC_EMIT) {
+    // generate this partition's pairs into LDS, in depth order; each thread
+    // takes GEN splats at a time with all their loads in flight together
+    constexpr int GEN = 4;
+    const int nv = (int)min((int64_t)PART, n - p0);
+    const int m = in.ctl->m;
+    const int nparts = (int)parts_of(n, PART);
+    const int r0 = in.part_first[part];
+    const int r1 = part + 1 < nparts ? in.part_first[part + 1] : m - 1;
+    for (int rb = r0; rb <= r1; rb += NT * GEN) {
+      int gg[GEN];
+      int64_t qq[GEN];
+      Splat sp[GEN];
 #pragma unroll
-  for (int r = 0; r < OS_ITEMS; r++) {
-    const int64_t e = base + r * 64 + lane;
-    bool valid = e < n;
-    uint32_t k = 0, v = 0;
-    if (valid) {
-      if constexpr (FIRST) {
-        valid = splat_visible(offsets, (int)e, overflow);
-        if (valid) {
-          k = __float_as_uint(splats[e].p2.z);
-          v = (uint32_t)e;
+      for (int u = 0; u < GEN; u++) {
+        const int r = rb + u * NT + tid;
+        gg[u] = r <= r1 ? (int)in.dval[r] : -1;
+        qq[u] = r <= r1 ? in.doff[r] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < GEN; u++) sp[u] = in.splats[gg[u] >= 0 ? gg[u] : 0];
+#pragma unroll
+      for (int u = 0; u < GEN; u++) {
+        if (gg[u] < 0) continue;
+        const int g = gg[u];
+        int64_t q = qq[u];
+        const RowSpans rs = spans_setup(sp[u], in.tiles_y);
+        if (!rs.ok) continue;
+        for (int ty = rs.ty_a; ty < rs.ty_b && q < p0 + nv; ty++) {
+          int a, b;
+          row_span(rs, ty, in.W, in.H, in.tiles_x, a, b);
+          if (b <= a) continue;
+          if (q + (b - a) <= p0) {
+            q += b - a;
+            continue;
+          }
+          for (int tx = a; tx < b; tx++, q++) {
+            if (q >= p0 && q < p0 + nv) {
+              s_key[q - p0] = (uint32_t)(ty * in.tiles_x + tx);
+              s_val[q - p0] = (uint32_t)g;
+            }
+          }
         }
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t base = p0 + (int64_t)w * (ITEMS * 64);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t key[ITEMS], val[ITEMS];
+  int rnk[ITEMS];
+  bool overflow = false;
+  if constexpr (SRC == SRC_DEPTH0) overflow = in.ctl->overflow != 0;
+  // all of this thread's keys are loaded before any is ranked
+#pragma unroll
+  for (int r = 0; r < ITEMS; r++) {
+    const int64_t e = base + r * 64 + lane;
+    uint32_t k = NO_DEPTH, v = 0;
+    if (e < n) {
+      if constexpr (SRC == SRC_DEPTH0) {
+        k = in.dkey[e];
+        v = (uint32_t)e;
+      } else if constexpr (SRC == SRC_EMIT) {
+        k = s_key[e - p0];
+        v = s_val[e - p0];
       } else {
         k = kin[e];
         v = vin[e];
       }
     }
+    key[r] = k;
+    val[r] = v;
+  }
+#pragma unroll
+  for (int r = 0; r < ITEMS; r++) {
+    const int64_t e = base + r * 64 + lane;
+    bool valid = e < n;
+    if constexpr (SRC == SRC_DEPTH0) valid = valid && key[r] != NO_DEPTH && !overflow;
+    const uint32_t k = valid ? key[r] : 0u;
     const uint32_t d = (k >> shift) & (B - 1);
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -205,22 +382,21 @@ __global__ void __launch_bounds__(OS_THREADS) k_onesweep(
       if (below == __popcll(peers) - 1) s_wcnt[w][d] = wr + 1;
     }
     key[r] = k;
-    val[r] = v;
     rnk[r] = wr;
   }
   __syncthreads();
-  // per digit: exclusive prefix over the 4 waves and the block total
+  // per digit: exclusive prefix over the waves and the block total
   int total = 0;
   if (tid < B) {
 #pragma unroll
-    for (int q = 0; q < OS_WAVES; q++) {
+    for (int q = 0; q < NWV; q++) {
       const int c = s_wcnt[q][tid];
       s_wcnt[q][tid] = total;
       total += c;
     }
   }
   int ntot;
-  const int incl = block_scan_os(tid < B ? total : 0, ntot);
+  const int incl = block_scan<NT>(tid < B ? total : 0, ntot);
   if (tid < B) {
     s_lbase[tid] = incl - total;
     // publish this partition's count, then look back for the exclusive prefix
@@ -230,22 +406,36 @@ __global__ void __launch_bounds__(OS_THREADS) k_onesweep(
       st_status(&status[me], ST_INC | (uint32_t)total);
     } else {
       st_status(&status[me], ST_AGG | (uint32_t)total);
+      // walk back LBW predecessors per round trip: sum aggregates up to the
+      // first inclusive prefix; wait where a predecessor has not published
+      constexpr int LBW = 16;
       int p = part - 1;
       int spins = 0;
       while (p >= 0) {
-        const uint32_t s = ld_status(&status[(int64_t)p * B + tid]);
-        const uint32_t f = s & ~ST_CNT;
-        if (f == 0) {
+        uint32_t sw[LBW];
+#pragma unroll
+        for (int j = 0; j < LBW; j++)
+          sw[j] = p - j >= 0 ? ld_status(&status[(int64_t)(p - j) * B + tid]) : ST_INC;
+        bool done = false;
+        int used = 0;
+#pragma unroll
+        for (int j = 0; j < LBW; j++) {
+          if (done || used < j) continue;
+          const uint32_t f = sw[j] & ~ST_CNT;
+          if (f == 0) continue;
+          excl += sw[j] & ST_CNT;
+          used = j + 1;
+          if (f == ST_INC) done = true;
+        }
+        if (done) break;
+        p -= used;
+        if (used < LBW) {  // stopped at an unpublished predecessor
           if (++spins > SPIN_LIMIT) {
             atomicOr(err, 1);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
-          continue;
         }
-        excl += s & ST_CNT;
-        if (f == ST_INC) break;
-        p--;
       }
       st_status(&status[me], ST_INC | (excl + (uint32_t)total));
     }
@@ -255,7 +445,7 @@ __global__ void __launch_bounds__(OS_THREADS) k_onesweep(
   __syncthreads();
   // reorder in LDS by digit (stable)
 #pragma unroll
-  for (int r = 0; r < OS_ITEMS; r++) {
+  for (int r = 0; r < ITEMS; r++) {
     if (rnk[r] >= 0) {
       const uint32_t d = (key[r] >> shift) & (B - 1);
       const int pos = s_lbase[d] + s_wcnt[w][d] + rnk[r];
@@ -265,57 +455,57 @@ __global__ void __launch_bounds__(OS_THREADS) k_onesweep(
   }
   __syncthreads();
   const int nv = s_nvalid;
-  for (int i = tid; i < nv; i += OS_THREADS) {
+  const int bound = SRC == SRC_DEPTH0 ? in.ctl->m : n;
+  for (int i = tid; i < nv; i += NT) {
     const uint32_t k = s_key[i];
     const uint32_t d = (k >> shift) & (B - 1);
     const uint32_t dst = s_gbase[d] + (uint32_t)(i - s_lbase[d]);
-    if (dst >= (uint32_t)n) continue;  // only after a look-back bound was hit (err is set)
+    if (dst >= (uint32_t)bound) continue;  // only after a look-back bound was hit (err is set)
     if (kout) kout[dst] = k;
-    vout[dst] = s_val[i];
+    const uint32_t v = s_val[i];
+    vout[dst] = v;
+    if (in.cout) in.cout[dst] = in.offsets[v + 1] - in.offsets[v];
   }
 }
 
 // ---------------------------------------------------------------- depth-ordered pair offsets
 
-__global__ void __launch_bounds__(SCAN_T) k_dcount_reduce(const SortCtl *__restrict__ ctl,
-                                                          int n_max,
-                                                          const uint32_t *__restrict__ dval,
-                                                          const int32_t *__restrict__ offsets,
-                                                          int32_t *__restrict__ bsum) {
+__global__ void __launch_bounds__(SCAN_T) k_dscan_reduce(const SortCtl *__restrict__ ctl,
+                                                         int n_max,
+                                                         const int32_t *__restrict__ dcnt,
+                                                         int32_t *__restrict__ bsum) {
   const int m = clamp_n(ctl->m, n_max);
   const int base = blockIdx.x * SCAN_TILE;
   int v = 0;
+#pragma unroll
   for (int j = 0; j < SCAN_I; j++) {
     const int r = base + j * SCAN_T + threadIdx.x;
-    if (r < m) {
-      const int g = (int)dval[r];
-      v += offsets[g + 1] - offsets[g];
-    }
+    v += r < m ? dcnt[r] : 0;
   }
   int tot;
-  block_scan256(v, tot);
+  block_scan<SCAN_T>(v, tot);
   if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
 }
 
-// doff[r] = pairs of the splats ranked before r. Each block sums the (few) block
-// sums before it itself, so the scan needs no third kernel; the block after the
-// last writes the grand total.
-__global__ void __launch_bounds__(SCAN_T) k_dcount_apply(SortCtl *__restrict__ ctl, int n_max,
-                                                         const uint32_t *__restrict__ dval,
-                                                         const int32_t *__restrict__ offsets,
-                                                         const int32_t *__restrict__ bsum,
-                                                         int32_t *__restrict__ doff) {
+// doff[r] = pairs of the splats ranked before r; for every tile partition k the
+// splat whose pairs contain pair k * TS_PART. Each block sums the (few) block
+// sums before it itself; the block after the last writes the total.
+__global__ void __launch_bounds__(SCAN_T) k_dscan_apply(SortCtl *__restrict__ ctl, int n_max,
+                                                        const int32_t *__restrict__ dcnt,
+                                                        const int32_t *__restrict__ bsum,
+                                                        int32_t *__restrict__ doff,
+                                                        int32_t *__restrict__ part_first) {
   const int m = clamp_n(ctl->m, n_max);
   const int nb = (m + SCAN_TILE - 1) / SCAN_TILE;
   if ((int)blockIdx.x > nb) return;
   int pre = 0;
   for (int b = threadIdx.x; b < (int)blockIdx.x; b += SCAN_T) pre += bsum[b];
   int block_base;
-  block_scan256(pre, block_base);
+  block_scan<SCAN_T>(pre, block_base);
   if ((int)blockIdx.x == nb) {
     if (threadIdx.x == 0) {
       doff[m] = block_base;
-      ctl->npairs = block_base;
+      ctl->npairs = ctl->overflow ? 0 : block_base;
     }
     return;
   }
@@ -325,82 +515,77 @@ __global__ void __launch_bounds__(SCAN_T) k_dcount_apply(SortCtl *__restrict__ c
 #pragma unroll
   for (int j = 0; j < SCAN_I; j++) {
     const int r = base + threadIdx.x * SCAN_I + j;
-    x[j] = 0;
-    if (r < m) {
-      const int g = (int)dval[r];
-      x[j] = offsets[g + 1] - offsets[g];
-    }
+    x[j] = r < m ? dcnt[r] : 0;
     v += x[j];
   }
   int t2;
-  const int incl = block_scan256(v, t2);
+  const int incl = block_scan<SCAN_T>(v, t2);
   int run = block_base + incl - v;
 #pragma unroll
   for (int j = 0; j < SCAN_I; j++) {
     const int r = base + threadIdx.x * SCAN_I + j;
-    if (r < m) doff[r] = run;
+    if (r < m) {
+      doff[r] = run;
+      // tile partitions whose first pair lies in [run, run + x[j])
+      for (int64_t k = ((int64_t)run + TS_PART - 1) / TS_PART; k * TS_PART < (int64_t)run + x[j]; k++)
+        part_first[k] = r;
+    }
     run += x[j];
   }
 }
 
-// ---------------------------------------------------------------- emission in depth order
-
-__global__ void __launch_bounds__(256) k_emit_depth_order(
-    const SortCtl *__restrict__ ctl, int n_max, const uint32_t *__restrict__ dval,
-    const int32_t *__restrict__ doff, const Splat *__restrict__ splats, int W, int H, int tiles_x,
-    int tiles_y, uint32_t *__restrict__ tile_out, uint32_t *__restrict__ id_out,
-    int32_t *__restrict__ tile_counts) {
-  __shared__ int hist[HIST_TILES_LDS];
-  const int ntiles = tiles_x * tiles_y;
-  const bool lds_hist = ntiles <= HIST_TILES_LDS;
-  if (lds_hist)
-    for (int i = threadIdx.x; i < ntiles; i += 256) hist[i] = 0;
-  __syncthreads();
-  const int m = clamp_n(ctl->m, n_max);
-  for (int r = blockIdx.x * 256 + threadIdx.x; r < m; r += gridDim.x * 256) {
-    const int g = (int)dval[r];
-    const RowSpans rs = spans_setup(splats[g], tiles_y);
-    if (!rs.ok) continue;
-    int pos = doff[r];
-    for (int ty = rs.ty_a; ty < rs.ty_b; ty++) {
-      int a, b;
-      row_span(rs, ty, W, H, tiles_x, a, b);
-      for (int tx = a; tx < b; tx++) {
-        const int t = ty * tiles_x + tx;
-        tile_out[pos] = (uint32_t)t;
-        id_out[pos] = (uint32_t)g;
-        pos++;
-        if (lds_hist)
-          atomicAdd(&hist[t], 1);
-        else
-          atomicAdd(&tile_counts[t], 1);
-      }
-    }
-  }
-  __syncthreads();
-  if (lds_hist)
-    for (int i = threadIdx.x; i < ntiles; i += 256)
-      if (hist[i]) atomicAdd(&tile_counts[i], hist[i]);
-}
-
 // Tile ranges (exclusive prefix of the per-tile counts) and the digit offsets of
 // the two tile passes: the low digit groups tiles by t mod 2^b0, the high digit
-// by t >> b0, whose offset is the start of tile d << b0.
+// by t >> b0, whose offset is the start of tile d << b0. An overflowing frame
+// gets empty ranges.
 __global__ void __launch_bounds__(1024) k_tile_bases(SortCtl *__restrict__ ctl,
-                                                     const int32_t *__restrict__ tile_counts,
-                                                     int ntiles, int b0,
+                                                     const int32_t *__restrict__ tile_diff,
+                                                     int32_t *__restrict__ tile_counts, int tiles_x,
+                                                     int tiles_y, int b0,
                                                      int32_t *__restrict__ ranges) {
   __shared__ int wsum[16];
   __shared__ int carry;
   __shared__ uint32_t lo_hist[256];
+  const int ntiles = tiles_x * tiles_y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const bool overflow = ctl->overflow != 0;
+  // per-tile counts: every row of the difference array sums to zero (each span
+  // adds +1 and -1 in its own row), so the inclusive prefix of the whole array,
+  // taken row-major, is the count of each tile
+  const int stride = tiles_x + 1, ndiff = tiles_y * stride;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < ndiff; c0 += 1024) {
+    const int i = c0 + threadIdx.x;
+    const int x = i < ndiff ? tile_diff[i] : 0;
+    int v = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(v, d, 64);
+      if (lane >= d) v += o;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    int base = carry, tot = 0;
+    for (int q = 0; q < 16; q++) {
+      base += (q < wid) ? wsum[q] : 0;
+      tot += wsum[q];
+    }
+    if (i < ndiff) {
+      const int ty = i / stride, tx = i - ty * stride;
+      if (tx < tiles_x) tile_counts[ty * tiles_x + tx] = base + v;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
   if (threadIdx.x == 0) carry = 0;
   if (threadIdx.x < 256) lo_hist[threadIdx.x] = 0;
   __syncthreads();
   const uint32_t mask0 = (1u << b0) - 1u;
   for (int c0 = 0; c0 < ntiles; c0 += 1024) {
     const int t = c0 + threadIdx.x;
-    const int x = t < ntiles ? tile_counts[t] : 0;
+    const int x = (t < ntiles && !overflow) ? tile_counts[t] : 0;
     if (x) atomicAdd(&lo_hist[t & mask0], (uint32_t)x);
     int v = x;
 #pragma unroll
@@ -424,13 +609,11 @@ __global__ void __launch_bounds__(1024) k_tile_bases(SortCtl *__restrict__ ctl,
     if (threadIdx.x == 0) carry += tot;
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (uint32_t d = 0; d <= mask0; d++) {
-      ctl->tbase[0][d] = run;
-      run += lo_hist[d];
-    }
-  }
+  // low-digit offsets: every thread takes part in the scan
+  const int v = threadIdx.x <= (int)mask0 ? (int)lo_hist[threadIdx.x] : 0;
+  int tot;
+  const int incl = block_scan<1024>(v, tot);
+  if (threadIdx.x <= (int)mask0) ctl->tbase[0][threadIdx.x] = (uint32_t)(incl - v);
 }
 
 __global__ void __launch_bounds__(256) k_sorted_keys(const SortCtl *__restrict__ ctl, int cap,
@@ -443,49 +626,29 @@ __global__ void __launch_bounds__(256) k_sorted_keys(const SortCtl *__restrict__
   out[k] = ((uint64_t)tiles[k] << 32) | (uint64_t)__float_as_uint(splats[ids[k]].p2.z);
 }
 
-// ---------------------------------------------------------------- workspace layout
-
-int64_t parts_of(int64_t n) { return (n + OS_PART - 1) / OS_PART; }
-
-struct SortWs {
-  SortCtl *ctl;
-  int32_t *tile_counts;
-  uint32_t *dk[2], *dv[2];  // n each
-  int32_t *doff;            // n + 1
-  int32_t *bsum;            // block sums of the depth-order scan
-  uint32_t *tk[2], *tv[2];  // capacity each
-  uint32_t *status;         // look-back words: 4 depth passes, then 2 tile passes
-  int64_t pd, pt;           // status words per depth pass / per tile pass
-  size_t bytes;
-};
-
-SortWs carve(char *base, int n, int64_t cap, int ntiles) {
-  size_t off = 0;
-  auto take = [&](int64_t bytes) {
-    char *r = base + off;
-    off += (size_t)((bytes + 255) / 256) * 256;
-    return r;
-  };
-  SortWs w;
-  w.ctl = (SortCtl *)take(sizeof(SortCtl));
-  w.tile_counts = (int32_t *)take(4 * (int64_t)(ntiles + 1));
-  for (int i = 0; i < 2; i++) w.dk[i] = (uint32_t *)take(4 * ((int64_t)n + 2));
-  for (int i = 0; i < 2; i++) w.dv[i] = (uint32_t *)take(4 * ((int64_t)n + 2));
-  w.doff = (int32_t *)take(4 * ((int64_t)n + 2));
-  w.bsum = (int32_t *)take(4 * ((int64_t)n / SCAN_TILE + 4));
-  for (int i = 0; i < 2; i++) w.tk[i] = (uint32_t *)take(4 * (cap + 2));
-  for (int i = 0; i < 2; i++) w.tv[i] = (uint32_t *)take(4 * (cap + 2));
-  w.pd = (parts_of(n) + 1) * 256;
-  w.pt = (parts_of(cap) + 1) * 256;
-  w.status = (uint32_t *)take(4 * (4 * w.pd + 2 * w.pt));
-  w.bytes = off;
-  return w;
-}
-
 }  // namespace
 
-size_t gs_sort_ws_bytes(int n, int64_t cap, int ntiles) {
-  return carve(nullptr, n, cap, ntiles).bytes + 256;
+int gs_scan_buf_elems(int n_max);
+
+size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y) {
+  return carve(nullptr, n, cap, tiles_x, tiles_y, gs_scan_buf_elems(n)).bytes + 256;
+}
+
+// gs_bin_tiles' counting kernels; the per-splat counts go to counts[0, n).
+hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int64_t cap,
+                               int32_t *counts, void *ws, int32_t **scan_buf, hipStream_t st) {
+  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y,
+                   gs_scan_buf_elems(n));
+  *scan_buf = w.scan_buf;
+  hipLaunchKernelGGL(k_bin_init, dim3(1), dim3(1024), 0, st, w.ctl, w.tile_diff,
+                     cam.tiles_y * (cam.tiles_x + 1));
+  const int blocks = max(1, min(BIN_BLOCKS_MAX, gs_div_up(n > 0 ? n : 1, BIN_T)));
+  const int ndiff = cam.tiles_y * (cam.tiles_x + 1);
+  const size_t lds = ndiff <= HIST_TILES_LDS ? 4 * (size_t)ndiff : 0;
+  hipLaunchKernelGGL(k_bin_count, dim3(blocks), dim3(BIN_T), lds, st, n,
+                     reinterpret_cast<const Splat *>(splats), cam.width, cam.height, cam.tiles_x,
+                     cam.tiles_y, counts, w.dkey, w.ctl, w.tile_diff, w.status, w.nstatus);
+  return hipGetLastError();
 }
 
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
@@ -493,7 +656,8 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
                           int32_t *ranges, void *ws, hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   const int ntiles = cam.tiles_x * cam.tiles_y;
-  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, ntiles);
+  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y,
+                   gs_scan_buf_elems(n));
   SortCtl *ctl = w.ctl;
   char *cb = reinterpret_cast<char *>(ctl);
   auto dbase = [&](int p) { return reinterpret_cast<uint32_t *>(cb + offsetof(SortCtl, dbase)) + 256 * p; };
@@ -503,58 +667,72 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   const int32_t *m_dev = reinterpret_cast<const int32_t *>(cb + offsetof(SortCtl, m));
   const int32_t *i_dev = reinterpret_cast<const int32_t *>(cb + offsetof(SortCtl, npairs));
   const int capi = (int)cap;
-  const int64_t nstatus = 4 * w.pd + 2 * w.pt;
+  PassIn in{};
+  in.ctl = ctl;
 
-  hipLaunchKernelGGL(k_sort_init, dim3(1), dim3(1024), 0, st, ctl, w.tile_counts, ntiles);
-  const int hist_blocks = max(1, min(1024, gs_div_up(n > 0 ? n : 1, 256)));
-  hipLaunchKernelGGL(k_depth_hist, dim3(hist_blocks), dim3(256), 0, st, n, sp, offsets, cap, ctl,
-                     w.status, nstatus);
-  hipLaunchKernelGGL(k_depth_bases, dim3(1), dim3(256), 0, st, ctl);
-  // depth sort of the visible splats: 4 passes of 8 bits
-  const int npd = (int)(parts_of(n) > 1 ? parts_of(n) : 1);
-  hipLaunchKernelGGL((k_onesweep<8, true>), dim3(npd), dim3(OS_THREADS), 0, st, nullptr, nullptr,
-                     w.dk[1], w.dv[1], nullptr, n, sp, offsets, cap, 0, dbase(0), w.status,
-                     ticket(0), err);
+  hipLaunchKernelGGL(k_depth_bases, dim3(1), dim3(256), 0, st, ctl, offsets, n, cap);
+  // depth sort of the visible splats: 4 passes of 8 bits; the last also writes
+  // each splat's pair count in depth order
+  const int npd = (int)(parts_of(n, DS_PART) > 1 ? parts_of(n, DS_PART) : 1);
+  {
+    PassIn a = in;
+    a.dkey = w.dkey;
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_DEPTH0>), dim3(npd),
+                       dim3(DS_THREADS), 0, st, nullptr, nullptr, w.dk[1], w.dv[1], nullptr, n, 0,
+                       dbase(0), w.status, ticket(0), err, a);
+  }
   int cur = 1;
   for (int pass = 1; pass < 4; pass++) {
-    hipLaunchKernelGGL((k_onesweep<8, false>), dim3(npd), dim3(OS_THREADS), 0, st, w.dk[cur],
-                       w.dv[cur], w.dk[cur ^ 1], w.dv[cur ^ 1], m_dev, n, nullptr, nullptr, cap,
-                       8 * pass, dbase(pass), w.status + pass * w.pd, ticket(pass), err);
+    PassIn a = in;
+    if (pass == 3) {
+      a.offsets = offsets;
+      a.cout = w.dcnt;
+    }
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_KEYS>), dim3(npd), dim3(DS_THREADS),
+                       0, st, w.dk[cur], w.dv[cur], pass == 3 ? nullptr : w.dk[cur ^ 1],
+                       w.dv[cur ^ 1], m_dev, n, 8 * pass, dbase(pass), w.status + pass * w.pd,
+                       ticket(pass), err, a);
     cur ^= 1;
   }
   const uint32_t *dval = w.dv[cur];
-  // pair offsets in depth order
+  // pair offsets in depth order and the first splat of every tile partition
   const int nb = gs_div_up(n > 0 ? n : 1, SCAN_TILE);
-  hipLaunchKernelGGL(k_dcount_reduce, dim3(nb), dim3(SCAN_T), 0, st, ctl, n, dval, offsets, w.bsum);
-  hipLaunchKernelGGL(k_dcount_apply, dim3(nb + 1), dim3(SCAN_T), 0, st, ctl, n, dval, offsets,
-                     w.bsum, w.doff);
-  // emit the pairs in depth order, with the per-tile histogram
-  const int eblocks = max(1, min(2048, gs_div_up(n > 0 ? n : 1, 256)));
-  hipLaunchKernelGGL(k_emit_depth_order, dim3(eblocks), dim3(256), 0, st, ctl, n, dval, w.doff, sp,
-                     cam.width, cam.height, cam.tiles_x, cam.tiles_y, w.tk[0], w.tv[0],
-                     w.tile_counts);
-  // stable sort by tile id: the low 8 bits, then (for more than 256 tiles) the rest
+  hipLaunchKernelGGL(k_dscan_reduce, dim3(nb), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum);
+  hipLaunchKernelGGL(k_dscan_apply, dim3(nb + 1), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum,
+                     w.doff, w.part_first);
+  // tile ranges and the tile digit offsets (counts from the binning pass)
   int tbits = 1;
   while ((1 << tbits) < ntiles) tbits++;
   const int b0 = 8;
-  hipLaunchKernelGGL(k_tile_bases, dim3(1), dim3(1024), 0, st, ctl, w.tile_counts, ntiles, b0,
-                     ranges);
-  const int npt = (int)(parts_of(cap) > 1 ? parts_of(cap) : 1);
+  hipLaunchKernelGGL(k_tile_bases, dim3(1), dim3(1024), 0, st, ctl, w.tile_diff, w.tile_counts,
+                     cam.tiles_x, cam.tiles_y, b0, ranges);
+  // tile passes: the first generates its partition's pairs itself
+  const int npt = (int)(parts_of(cap, TS_PART) > 1 ? parts_of(cap, TS_PART) : 1);
   uint32_t *status_t0 = w.status + 4 * w.pd, *status_t1 = status_t0 + w.pt;
-  uint32_t *final_tiles = sorted_keys ? w.tk[0] : nullptr;
   uint32_t *ids_out = reinterpret_cast<uint32_t *>(sorted_ids);
+  PassIn e = in;
+  e.dval = dval;
+  e.doff = w.doff;
+  e.part_first = w.part_first;
+  e.splats = sp;
+  e.W = cam.width;
+  e.H = cam.height;
+  e.tiles_x = cam.tiles_x;
+  e.tiles_y = cam.tiles_y;
+  uint32_t *final_tiles = nullptr;
   if (tbits <= 8) {
-    hipLaunchKernelGGL((k_onesweep<8, false>), dim3(npt), dim3(OS_THREADS), 0, st, w.tk[0],
-                       w.tv[0], final_tiles ? w.tk[1] : nullptr, ids_out, i_dev, capi, nullptr,
-                       nullptr, cap, 0, tbase(0), status_t0, ticket(4), err);
-    final_tiles = w.tk[1];
+    final_tiles = sorted_keys ? w.tk[1] : nullptr;
+    hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 8, SRC_EMIT>), dim3(npt), dim3(TS_THREADS),
+                       0, st, nullptr, nullptr, final_tiles, ids_out, i_dev, capi, 0, tbase(0),
+                       status_t0, ticket(4), err, e);
   } else {
-    hipLaunchKernelGGL((k_onesweep<8, false>), dim3(npt), dim3(OS_THREADS), 0, st, w.tk[0],
-                       w.tv[0], w.tk[1], w.tv[1], i_dev, capi, nullptr, nullptr, cap, 0, tbase(0),
-                       status_t0, ticket(4), err);
-    hipLaunchKernelGGL((k_onesweep<8, false>), dim3(npt), dim3(OS_THREADS), 0, st, w.tk[1],
-                       w.tv[1], final_tiles, ids_out, i_dev, capi, nullptr, nullptr, cap, b0,
-                       tbase(1), status_t1, ticket(5), err);
+    hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 8, SRC_EMIT>), dim3(npt), dim3(TS_THREADS),
+                       0, st, nullptr, nullptr, w.tk[0], w.tv[0], i_dev, capi, 0, tbase(0),
+                       status_t0, ticket(4), err, e);
+    final_tiles = sorted_keys ? w.tk[1] : nullptr;
+    hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 8, SRC_KEYS>), dim3(npt), dim3(TS_THREADS),
+                       0, st, w.tk[0], w.tv[0], final_tiles, ids_out, i_dev, capi, b0, tbase(1),
+                       status_t1, ticket(5), err, in);
   }
   if (sorted_keys)
     hipLaunchKernelGGL(k_sorted_keys, dim3(gs_div_up(cap > 0 ? cap : 1, 256)), dim3(256), 0, st,

@@ -124,7 +124,11 @@ int32_t gs_project(int32_t n, const float *means, const float *log_scales, const
  *   device_status [1] <- GS_OK, or GS_ERR_CAPACITY when I > pair_capacity; in
  *     that case nothing is emitted and the later calls of the frame do nothing.
  *     The caller reads it after the frame, grows its pair buffers to at least
- *     offsets[n] and runs the frame again. */
+ *     offsets[n] and runs the frame again.
+ *   workspace <- also receives, from the same pass over the splat records, what
+ *     gs_sort_keys needs: each splat's depth key, the depth-digit and per-tile
+ *     pair histograms, and cleared radix look-back words. Pass the same
+ *     workspace, untouched, to the gs_sort_keys call of the same frame. */
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
                      int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
                      void *workspace, size_t workspace_bytes, void *stream);
@@ -134,6 +138,9 @@ int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64
  * visible splats (those with offsets[i+1] > offsets[i]) by fp32 depth bits,
  * emission of their tile keys in that order (the same canonical spans as
  * gs_bin_tiles), then a stable radix sort by tile id.
+ * Reads the state gs_bin_tiles of the same frame left in `workspace`: call it
+ * once after every gs_bin_tiles, with the same workspace, splats, offsets,
+ * camera and pair_capacity.
  *   sorted_ids [pair_capacity] <- splat ids in that order
  *   sorted_keys [pair_capacity] or NULL <- (tile << 32) | float_bits(depth)
  *   tile_ranges [T][2] <- [start, end) of every tile (empty tiles: start = end
