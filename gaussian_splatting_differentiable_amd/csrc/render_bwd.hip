@@ -37,6 +37,81 @@ __global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n,
   if (i < n - 4 * n4) p[4 * n4 + i] = 0.0f;
 }
 
+// Backward queue order. The forward pass leaves every item's walk length (the
+// quarter's or chunk's last hit), so the backward can serve its items longest
+// first exactly ([LOAD-IMB] section 4.1 orders by N_t, which overstates the work
+// of tiles whose pixels saturate early). One workgroup per group sorts the
+// group's backward items stably by a quarter-octave bucket of that length.
+constexpr int BO_T = 1024, BO_W = BO_T / 64, BO_BITS = 6, BO_BINS = 1 << BO_BITS;
+
+__device__ __forceinline__ uint32_t order_bin(const FwdState &fs, int it, int k) {
+  const int quad = item_quad(it), idx = item_index(it);
+  const int len = item_kind(it) == ITEM_PLAIN
+                      ? fs.sub_last[idx * 4 + quad]
+                      : fs.chunk_last[chunk_index(idx, item_chunk(it), quad, k)];
+  const int b = (int)(4.0f * __log2f((float)max(len, 0) + 1.0f));
+  return (uint32_t)(BO_BINS - 1 - min(b, BO_BINS - 1));  // ascending bin = longest first
+}
+
+__global__ void __launch_bounds__(BO_T) k_bwd_order(char *__restrict__ state, int ntiles,
+                                                   int nblocks) {
+  __shared__ int cnt[BO_W][BO_BINS];
+  FwdState fs = fwd_state_at(state, ntiles);
+  const int g = blockIdx.x, k = fs.hdr->k;
+  const int lo = fs.hdr->qoff[g] + fs.hdr->qa[g], hi = fs.hdr->qoff[g + 1];
+  const int n = hi - lo;
+  // the backward's own hand-out: the first items go to its workers without a pop
+  if (threadIdx.x == 0) {
+    const int init = min(n, group_workers(g, nblocks));
+    fs.hdr->init_b[g] = init;
+    queue_head(fs, 1, g)[0] = init;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < BO_W * BO_BINS; i += BO_T) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int chunk = (n + BO_W - 1) / BO_W;
+  const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
+  for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&cnt[w][order_bin(fs, fs.items[lo + e], k)], 1);
+  __syncthreads();
+  __shared__ int btot[BO_BINS];
+  if (threadIdx.x < BO_BINS) {
+    int t = 0;
+    for (int q = 0; q < BO_W; q++) t += cnt[q][threadIdx.x];
+    btot[threadIdx.x] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < BO_BINS) {
+    // exclusive offsets in (bin, wave) order
+    int run = 0;
+    for (int d = 0; d < (int)threadIdx.x; d++) run += btot[d];
+    for (int q = 0; q < BO_W; q++) {
+      const int c = cnt[q][threadIdx.x];
+      cnt[q][threadIdx.x] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int base = c0; base < c1; base += 64) {
+    const int e = base + lane;
+    const bool valid = e < c1;
+    const int it = valid ? fs.items[lo + e] : 0;
+    const uint32_t d = valid ? order_bin(fs, it, k) : 0u;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < BO_BITS; b++) {
+      const uint64_t bal = __ballot((d >> b) & 1u);
+      peers &= ((d >> b) & 1u) ? bal : ~bal;
+    }
+    if (valid) {
+      const int below = __popcll(peers & lt);
+      const int pos = cnt[w][d] + below;
+      fs.bitems[lo + pos] = it;
+      if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+    }
+  }
+}
+
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, GS_WAVE));
@@ -170,7 +245,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_bwd(
     const int t = next_item(fs, 1, wk);
     if (t < 0) break;
     wk.round++;
-    const int it = fs.items[t];
+    const int it = fs.bitems[t];
     const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
     const int idx = item_index(it);
     const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
@@ -230,17 +305,20 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_bwd(
 
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
-                                const int32_t *last, const void *fwd_state, const float *dL,
+                                const int32_t *last, void *fwd_state, const float *dL,
                                 float *grads, int n, int workers_waves, hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
   const int ntiles = cam.tiles_x * cam.tiles_y;
-  const FwdState fs = fwd_state_at(const_cast<void *>(fwd_state), ntiles);
+  const FwdState fs = fwd_state_at(fwd_state, ntiles);
+  const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
+  hipLaunchKernelGGL(k_bwd_order, dim3(GS_GROUPS), dim3(BO_T), 0, st,
+                     reinterpret_cast<char *>(fwd_state), ntiles, nblocks);
   hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng,
                      fs.hdr, queue_head(fs, 1, 0));
-  hipLaunchKernelGGL(k_render_bwd, dim3(workers_waves / GS_WAVES_PER_BLOCK),
+  hipLaunchKernelGGL(k_render_bwd, dim3(nblocks),
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
-                     reinterpret_cast<char *>(const_cast<void *>(fwd_state)), ntiles, dL, grads);
+                     reinterpret_cast<char *>(fwd_state), ntiles, dL, grads);
   return hipGetLastError();
 }

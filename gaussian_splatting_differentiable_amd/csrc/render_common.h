@@ -53,7 +53,7 @@ struct PlanHdr {
 // Byte layout of fwd_state for T tiles.
 struct FwdLayout {
   size_t hdr, heads, sub_last, order, counts, items, sat, doneA, doneB, chunk_last, PA, CB, TB,
-      LB, total;
+      LB, bitems, total;
 };
 
 __host__ __device__ inline FwdLayout fwd_layout(int T) {
@@ -79,6 +79,7 @@ __host__ __device__ inline FwdLayout fwd_layout(int T) {
   L.CB = take(4 * cq * 64 * 3);
   L.TB = take(4 * cq * 64);
   L.LB = take(4 * cq * 64);
+  L.bitems = take(4 * ((size_t)T * 4 + 2 * cq));
   L.total = off;
   return L;
 }
@@ -89,6 +90,7 @@ struct FwdState {
   int32_t *sub_last, *order, *counts, *items, *sat, *doneA, *doneB, *chunk_last;
   float *PA, *CB, *TB;
   int32_t *LB;
+  int32_t *bitems;  // the backward's queue items, longest walk first within each group
 };
 
 __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
@@ -109,6 +111,7 @@ __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
   s.CB = reinterpret_cast<float *>(b + L.CB);
   s.TB = reinterpret_cast<float *>(b + L.TB);
   s.LB = reinterpret_cast<int32_t *>(b + L.LB);
+  s.bitems = reinterpret_cast<int32_t *>(b + L.bitems);
   return s;
 }
 

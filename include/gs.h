@@ -158,7 +158,7 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
  *   rgb [3][H][W], T_final [H][W] <- colour and final transmittance
  *   last [H][W] <- list entries the pixel consumed (stop index + 1, or the
  *                  tile's full length when it never stopped)
- *   fwd_state <- opaque, gs_fwd_state_size bytes, read by gs_render_bwd
+ *   fwd_state <- opaque, gs_fwd_state_size bytes, consumed by gs_render_bwd
  *   stats [4] or NULL <- += {hits: (pixel, splat) pairs blended; lane evaluations:
  *                          64 x (8x8 sub-tile, splat) pairs tested; sub-tile hits:
  *                          (8x8 sub-tile, splat) pairs with at least one hit, which
@@ -176,10 +176,13 @@ int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
  * (1 - alpha), keeps the scalar accumulator accum = c_behind . dL/dC, and
  * forms dL/dalpha = T (c . dL/dC - accum). Per-wave sums go to the output
  * with float atomics, so low-order bits depend on the atomic order.
+ *   fwd_state: the state gs_render_fwd left for this frame; the backward also
+ *     keeps its own work queue in it (so it is not const), and may run again
+ *     on the same state.
  *   dL_dsplat [n][9] <- fully overwritten (rows of culled splats are 0). */
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
-                      const int32_t *last, const void *fwd_state, size_t fwd_state_bytes,
+                      const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
                       const float *dL_drgb, float *dL_dsplat, void *workspace,
                       size_t workspace_bytes, void *stream);
 

@@ -293,7 +293,8 @@ def check_queues(plan, tiles_x):
 
 
 def _workers():
-    return torch.cuda.get_device_properties(0).multi_processor_count * 32 / 4.0
+    """K of the policy: the library's persistent worker waves (16 per CU), four per tile."""
+    return torch.cuda.get_device_properties(0).multi_processor_count * 16 / 4.0
 
 
 @pytest.mark.parametrize("k", [2, 4, 8, 16])
