@@ -67,9 +67,9 @@ int worker_waves() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  // 16 persistent worker waves per CU (4 per SIMD): fewer co-resident waves let
-  // each item finish sooner, which shortens the tail of the launch more than
-  // the extra latency hiding of 8 waves per SIMD would gain (measured)
+  // one workgroup of 16 persistent worker waves per CU (4 per SIMD): fewer
+  // co-resident waves let each item finish sooner, which shortens the tail of
+  // the launch more than the latency hiding of 8 waves per SIMD gains (measured)
   return cus > 0 ? cus * 16 : 0;
 }
 

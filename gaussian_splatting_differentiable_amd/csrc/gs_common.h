@@ -27,6 +27,13 @@ struct CamK {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Lanes of the wave where p holds, as a scalar mask (the bool goes straight to
+// the ballot, with no round trip through a 0/1 vector register).
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Value of v in the first active lane, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_first(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Canonical fp32 quadratic form of the conic at offset (dx, dy). Forward,
 // backward and the sub-tile cull must all take the hit decision from exactly
 // this expression (Step 5 of the literature page: fwd and bwd agree bit-for-bit).

@@ -97,10 +97,10 @@ __global__ void __launch_bounds__(BO_T) k_bwd_order(char *__restrict__ state, in
     const bool valid = e < c1;
     const int it = valid ? fs.items[lo + e] : 0;
     const uint32_t d = valid ? order_bin(fs, it, k) : 0u;
-    uint64_t peers = __ballot(valid);
+    uint64_t peers = wave_ballot(valid);
 #pragma unroll
     for (int b = 0; b < BO_BITS; b++) {
-      const uint64_t bal = __ballot((d >> b) & 1u);
+      const uint64_t bal = wave_ballot((d >> b) & 1u);
       peers &= ((d >> b) & 1u) ? bal : ~bal;
     }
     if (valid) {
@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(BO_T) k_bwd_order(char *__restrict__ state, in
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, GS_WAVE));
-  return v;
+  return wave_first(v);
 }
 
 constexpr int RB = 1;                // 64-splat rounds per batch
@@ -169,7 +169,7 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
       s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
       sbuf[r * GS_WAVE + lane] = s;
       sid[r * GS_WAVE + lane] = idc[r];
-      work[r] = __ballot(cand);
+      work[r] = wave_ballot(cand);
     }
     const int nhi = lo, nlo = max(cs, lo - BATCH);
     // records of [nlo, nhi), ids of the batch below it
@@ -191,7 +191,7 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
         const float adx = a * dx, cdy = c * dy;
         const float q = __builtin_fmaf(cdy, dy, __builtin_fmaf((2.0f * b) * dx, dy, adx * dx));
         const bool hit = rel < lastp && (q <= s.p2.y);
-        if (__ballot(hit) == 0) continue;
+        if (wave_ballot(hit) == 0) continue;
         // branchless: a missed pixel takes alpha = 0, which leaves T and accum
         // unchanged and contributes zero to every sum
         const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
@@ -227,7 +227,7 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
 }
 
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
-__attribute__((amdgpu_waves_per_eu(8))) k_render_bwd(
+__attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
@@ -240,7 +240,8 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_bwd(
   const int k = fs.hdr->k;
   const int64_t P = (int64_t)cam.width * cam.height;
   const int lane = __lane_id();
-  Worker wk = make_worker();
+  __shared__ uint32_t drained;
+  Worker wk = make_worker(&drained);
   for (;;) {
     const int t = next_item(fs, 1, wk);
     if (t < 0) break;

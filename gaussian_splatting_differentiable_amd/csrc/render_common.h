@@ -26,7 +26,9 @@ enum ItemKind { ITEM_PLAIN = 0, ITEM_PASS_A = 1, ITEM_PASS_B = 2 };
 // their group's queue take from the others.
 #define GS_GROUPS 8
 #define GS_HEAD_STRIDE 16  // ints between two queue heads (one 64-byte line)
-#define GS_WAVES_PER_BLOCK 4
+// One workgroup of 16 wave workers per CU (4 per SIMD): the waves of a CU share
+// one LDS mask of drained queues.
+#define GS_WAVES_PER_BLOCK 16
 
 __host__ __device__ __forceinline__ int make_item(int kind, int quad, int p, int idx) {
   return (kind << 30) | (quad << 28) | (p << 24) | idx;
@@ -119,6 +121,7 @@ __host__ __device__ __forceinline__ int32_t *queue_head(const FwdState &fs, int 
   return fs.heads + (pass * GS_GROUPS + g) * GS_HEAD_STRIDE;
 }
 
+
 // Workers of group g when `nblocks` workgroups are launched (workgroup b runs on
 // XCD b mod GS_GROUPS).
 __host__ __device__ __forceinline__ int group_workers(int g, int nblocks) {
@@ -181,7 +184,7 @@ __device__ __forceinline__ void wave_sync() {
 __device__ __forceinline__ int queue_pop(int32_t *head) {
   int t = 0;
   if (__lane_id() == 0) t = atomicAdd(head, 1);
-  return __shfl(t, 0, GS_WAVE);
+  return wave_first(t);
 }
 
 // Spin on a flag with relaxed loads (no cache invalidation per probe); the
@@ -190,46 +193,76 @@ __device__ __forceinline__ int ld_flag(const int32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A persistent worker: its group (the XCD it runs on), its index within the
-// group, and its progress through the queues.
+// A persistent worker: its home group (the XCD it runs on), its index within
+// that group, its round, and what it knows of drained queues: its own
+// findings and the LDS mask of its workgroup.
 struct Worker {
-  int g, wg, tried, round;
+  int home, wg, round;
+  uint32_t known;     // groups this wave found empty
+  uint32_t *drained;  // the workgroup's LDS mask of groups found empty
 };
 
-__device__ __forceinline__ Worker make_worker() {
+// Call from every thread of the workgroup, before any of its waves pops.
+__device__ __forceinline__ Worker make_worker(uint32_t *drained) {
+  if (threadIdx.x == 0) *drained = 0u;
+  __syncthreads();
   Worker w;
-  w.g = blockIdx.x % GS_GROUPS;
+  w.home = blockIdx.x % GS_GROUPS;
   // wave v of the group's j-th workgroup: consecutive items (the quarters of a
   // tile) go to different workgroups, as they would from a shared queue
-  const int blocks = (gridDim.x - w.g + GS_GROUPS - 1) / GS_GROUPS;
+  const int blocks = (gridDim.x - w.home + GS_GROUPS - 1) / GS_GROUPS;
   w.wg = wave_in_block() * blocks + (int)(blockIdx.x / GS_GROUPS);
-  w.tried = 0;
   w.round = 0;
+  w.known = 0u;
+  w.drained = drained;
   return w;
+}
+
+// One pop on group g's queue: the item index, or -1 if the queue is empty (then
+// g is recorded as drained in the wave and in the workgroup's LDS mask).
+__device__ __forceinline__ int pop_group(const FwdState &fs, int pass, Worker &w, int g) {
+  const PlanHdr *hd = fs.hdr;
+  const int lo = hd->qoff[g] + (pass ? hd->qa[g] : 0), hi = hd->qoff[g + 1];
+  if (lo < hi) {
+    const int t = queue_pop(queue_head(fs, pass, g));
+    if (lo + t < hi) return lo + t;
+  }
+  w.known |= 1u << g;
+  if (__lane_id() == 0)
+    __hip_atomic_fetch_or(w.drained, 1u << g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return -1;
 }
 
 // Next item (an index into items[]) of a worker, or -1 when every queue is
 // empty. pass 0 (forward) serves every item of a group; pass 1 (backward)
 // skips the pass-A items. The first item comes without a pop: the queue heads
 // start past the items handed out that way, so a frame's first wave of work
-// does not serialise on the heads. After that: the worker's own group, then
-// the others. (An atomic load to skip drained queues costs more than the pop:
-// it waits on the worker's outstanding stores.)
+// does not serialise on the heads. After that the worker pops its home group,
+// then the others nearest first (+1, -1, +2, ...), neighbouring strips sharing
+// more splats.
+//
+// A pop on a drained head is a same-address atomic, and at the end of a frame
+// every worker would make one per group: thousands of them, serialised on
+// eight addresses, behind the pops of the workers still busy. So a pop that
+// comes back empty is recorded in the workgroup's LDS mask and the other waves
+// of the CU skip that queue; every bit records a pop that came back empty, so
+// each round either returns an item or learns one more empty group.
 __device__ __forceinline__ int next_item(const FwdState &fs, int pass, Worker &w) {
   const PlanHdr *hd = fs.hdr;
   if (w.round == 0) {
-    const int init = pass ? hd->init_b[w.g] : hd->init_f[w.g];
-    if (w.wg < init) return hd->qoff[w.g] + (pass ? hd->qa[w.g] : 0) + w.wg;
+    const int init = pass ? hd->init_b[w.home] : hd->init_f[w.home];
+    if (w.wg < init) return hd->qoff[w.home] + (pass ? hd->qa[w.home] : 0) + w.wg;
   }
-  while (w.tried < GS_GROUPS) {
-    const int lo = hd->qoff[w.g] + (pass ? hd->qa[w.g] : 0), hi = hd->qoff[w.g + 1];
-    int32_t *head = queue_head(fs, pass, w.g);
-    if (lo < hi) {
-      const int t = queue_pop(head);
-      if (lo + t < hi) return lo + t;
+  for (int c = 0; c < GS_GROUPS; c++) {
+    const int g = (w.home + (c + 1) / 2 * ((c & 1) ? 1 : -1) + GS_GROUPS) % GS_GROUPS;
+    if (w.known & (1u << g)) continue;
+    const uint32_t dm = __hip_atomic_load(w.drained, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (wave_first((int)dm) & (1 << g)) {
+      w.known |= 1u << g;
+      continue;
     }
-    w.g = (w.g + 1) % GS_GROUPS;
-    w.tried++;
+    const int t = pop_group(fs, pass, w, g);
+    if (t >= 0) return t;
   }
   return -1;
 }

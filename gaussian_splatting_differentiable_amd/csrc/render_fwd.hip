@@ -11,13 +11,13 @@
 // branchless blending with one canonical q shared with the backward; Step 6.3
 // log2(o) folded into the exponent.
 //
-// gfx950 mapping: every workgroup is one wavefront, a persistent worker that
-// pops items (an 8x8 quarter of a tile or of a chunk) until the queues are
-// empty. A worker walks its list in batches of 128 splats staged in LDS (two
-// records per lane, three 16-byte loads each, the next batch in flight while
-// the current one is blended); each lane tests its staged splats against the
-// quarter's sample rectangle and the ballots of those tests are the worklist,
-// walked on the scalar unit.
+// gfx950 mapping: one workgroup of 16 wavefronts per CU, each a persistent worker
+// that pops items (an 8x8 quarter of a tile or of a chunk) until the queues are
+// empty. A worker walks its list in batches of 64 splats staged in LDS (one
+// record per lane, three 16-byte loads, the next batch in flight while the
+// current one is blended); each lane tests its staged splat against the
+// quarter's sample rectangle and the ballot of those tests is the worklist,
+// walked on the scalar unit with the next entry's record read ahead.
 //
 // Exact chunking (a reading of section 4.2: chunks that start at T = 1 can stop
 // later than the sequential renderer, so the composition is made exact):
@@ -35,8 +35,7 @@ namespace {
 
 constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 constexpr float T_STOP = 1e-4f;
-constexpr int RB = 1;                 // 64-splat rounds per batch
-constexpr int BATCH = RB * GS_WAVE;   // splats per staged batch
+constexpr int BATCH = GS_WAVE;  // splats per staged batch
 
 struct Px {
   float fx, fy;
@@ -69,42 +68,54 @@ __device__ __forceinline__ bool stage(Splat s, const SubTile &st, Splat *slot) {
 // batch ahead, so neither the id load nor the dependent record load stalls the
 // batch being blended. Slots past the end carry id -1 (and read record 0).
 struct Pipe {
-  int idc[RB];    // ids of the batch whose records are in rec
-  int idn[RB];    // ids of the batch after it
-  Splat rec[RB];
+  int idc;     // id of this lane's slot in the batch whose records are in rec
+  int idn;     // id of its slot in the batch after it
+  Splat rec;
 };
 
-__device__ __forceinline__ void load_ids(const int32_t *__restrict__ sids, int b, int ce,
-                                         int (&id)[RB]) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int r = 0; r < RB; r++) {
-    const int e = b + r * GS_WAVE + lane;
-    id[r] = e < ce ? sids[e] : -1;
-  }
-}
-
-__device__ __forceinline__ void load_recs(const Splat *__restrict__ splats, const int (&id)[RB],
-                                          Splat (&rec)[RB]) {
-#pragma unroll
-  for (int r = 0; r < RB; r++) rec[r] = splats[id[r] >= 0 ? id[r] : 0];
+__device__ __forceinline__ int load_id(const int32_t *__restrict__ sids, int b, int ce) {
+  const int e = b + __lane_id();
+  return e < ce ? sids[e] : -1;
 }
 
 __device__ __forceinline__ void pipe_start(Pipe &pp, const Splat *__restrict__ splats,
                                            const int32_t *__restrict__ sids, int cs, int ce) {
-  load_ids(sids, cs, ce, pp.idc);
-  load_recs(splats, pp.idc, pp.rec);
-  load_ids(sids, cs + BATCH, ce, pp.idn);
+  pp.idc = load_id(sids, cs, ce);
+  pp.rec = splats[pp.idc >= 0 ? pp.idc : 0];
+  pp.idn = load_id(sids, cs + BATCH, ce);
 }
 
 // After the batch at b is staged: start the records of b + BATCH and the ids of
 // b + 2 BATCH.
 __device__ __forceinline__ void pipe_advance(Pipe &pp, const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int b, int ce) {
-#pragma unroll
-  for (int r = 0; r < RB; r++) pp.idc[r] = pp.idn[r];
-  load_recs(splats, pp.idc, pp.rec);
-  load_ids(sids, b + 2 * BATCH, ce, pp.idn);
+  pp.idc = pp.idn;
+  pp.rec = splats[pp.idc >= 0 ? pp.idc : 0];
+  pp.idn = load_id(sids, b + 2 * BATCH, ce);
+}
+
+// Walk the staged worklist (set bits of work, lowest slot first), calling
+// f(record, slot) on each until f returns false. The LDS read of the next
+// entry's record is issued before f runs on the current one, so its latency
+// overlaps the blending; two record buffers alternate, so no copies are made.
+template <class F>
+__device__ __forceinline__ void walk_worklist(uint64_t w, const Splat *sbuf, F &&f) {
+  if (!w) return;
+  int j0 = __builtin_ctzll(w);
+  w &= w - 1;
+  Splat s0 = sbuf[j0];
+  for (;;) {
+    const bool more1 = w != 0;
+    const int j1 = more1 ? __builtin_ctzll(w) : j0;
+    w &= w - 1;
+    const Splat s1 = sbuf[j1];
+    if (!f(s0, j0) || !more1) return;
+    const bool more0 = w != 0;
+    j0 = more0 ? __builtin_ctzll(w) : j1;
+    w &= w - 1;
+    s0 = sbuf[j0];
+    if (!f(s1, j1) || !more0) return;
+  }
 }
 
 struct Blend {
@@ -113,8 +124,11 @@ struct Blend {
   int wlast;     // 1 + last position any lane hit (relative), 0 if none
 };
 
-// Blend [cs, ce) into pixels that start with transmittance T0 (alive when
-// T0 >= 1e-4).
+// Blend [cs, ce) into pixels that start with transmittance T0. Branchless per
+// entry: a lane that misses (or has stopped) takes alpha = 0, which leaves its
+// colour and T unchanged bit for bit. A lane is alive exactly while its T is at
+// least 1e-4 (lanes outside the image start at T = 0), so the hit mask is the
+// AND of two compare ballots and needs no per-lane flag.
 __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int cs, int ce,
                                              const SubTile &st, const Px &x, float T0,
@@ -122,72 +136,56 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              uint32_t &nsteps, uint32_t &nhsteps) {
   Blend r;
   r.C0 = r.C1 = r.C2 = 0.0f;
-  r.T = T0;
-  r.consumed = ce - cs;
+  r.T = x.inside ? T0 : 0.0f;
+  r.consumed = r.T >= T_STOP ? ce - cs : 0;
   r.wlast = 0;
-  bool alive = x.inside && T0 >= T_STOP;
-  if (!alive) r.consumed = 0;
-  uint64_t live = __ballot(alive);
+  bool live = wave_ballot(r.T >= T_STOP) != 0;
   const int lane = __lane_id();
   Pipe pp;
   if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce);
   for (int b = cs; b < ce && live; b += BATCH) {
-    uint64_t work[RB];
-#pragma unroll
-    for (int rr = 0; rr < RB; rr++) {
-      const bool cand = stage(pp.rec[rr], st, &sbuf[rr * GS_WAVE + lane]) && pp.idc[rr] >= 0;
-      work[rr] = __ballot(cand);
-    }
+    const bool cand = stage(pp.rec, st, &sbuf[lane]) && pp.idc >= 0;
+    const uint64_t work = wave_ballot(cand);
     pipe_advance(pp, splats, sids, b, ce);
     wave_sync();
-#pragma unroll
-    for (int rr = 0; rr < RB; rr++) {
-      while (work[rr] && live) {
-        const int j = __builtin_ctzll(work[rr]);
-        work[rr] &= work[rr] - 1;
-        const Splat s = sbuf[rr * GS_WAVE + j];
-        const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
-        const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
-        const bool hit = alive && (q <= s.p2.y);
-        const uint64_t hm = __ballot(hit);
-        nsteps++;
-        if (hm == 0) continue;
-        const int pos = b + rr * GS_WAVE + j - cs;
-        nhits += __popcll(hm);
-        nhsteps++;
-        r.wlast = pos + 1;
-        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-        const float al = hit ? fminf(0.99f, ex) : 0.0f;
-        const float w = al * r.T;
-        r.C0 = __builtin_fmaf(w, s.p1.z, r.C0);
-        r.C1 = __builtin_fmaf(w, s.p1.w, r.C1);
-        r.C2 = __builtin_fmaf(w, s.p2.x, r.C2);
-        r.T = r.T - w;
-        const bool stop = hit && (r.T < T_STOP);
-        if (__ballot(stop)) {
-          if (stop) {
-            alive = false;
-            r.consumed = pos + 1;
-          }
-          live = __ballot(alive);
-        }
-      }
-    }
+    const int base = b - cs;
+    walk_worklist(work, sbuf, [&](const Splat &s, int j) {
+      const int pos = base + j;
+      const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
+      const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
+      const bool alive = r.T >= T_STOP, inq = q <= s.p2.y;
+      const uint64_t hm = wave_ballot(alive) & wave_ballot(inq);
+      const bool hit = alive && inq;
+      nsteps++;
+      if (!hm) return true;  // no lane hits: nothing changes
+      nhits += __popcll(hm);
+      nhsteps++;
+      r.wlast = pos + 1;
+      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+      const float al = hit ? fminf(0.99f, ex) : 0.0f;
+      const float w = al * r.T;
+      r.C0 = __builtin_fmaf(w, s.p1.z, r.C0);
+      r.C1 = __builtin_fmaf(w, s.p1.w, r.C1);
+      r.C2 = __builtin_fmaf(w, s.p2.x, r.C2);
+      r.T = r.T - w;
+      r.consumed = (hit && r.T < T_STOP) ? pos + 1 : r.consumed;
+      live = wave_ballot(r.T >= T_STOP) != 0;
+      return live;
+    });
     wave_sync();
   }
-  (void)lane;
   return r;
 }
 
 // Pass A: transmittance product over the chunk; gives up when sat < chunk.
+// Lanes outside the image start at P = 0 (dead), as in blend_range.
 __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
                                                const int32_t *__restrict__ sids, int cs, int ce,
                                                const SubTile &st, const Px &x, Splat *sbuf,
                                                const int32_t *sat, int chunk, bool &gave_up,
                                                uint32_t &nsteps) {
-  float P = 1.0f;
-  bool alive = x.inside;
-  uint64_t live = __ballot(alive);
+  float P = x.inside ? 1.0f : 0.0f;
+  bool live = wave_ballot(P >= T_STOP) != 0;
   gave_up = false;
   const int lane = __lane_id();
   Pipe pp;
@@ -200,40 +198,27 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
       gave_up = true;
       break;
     }
-    uint64_t work[RB];
-#pragma unroll
-    for (int rr = 0; rr < RB; rr++) {
-      const bool cand = stage(pp.rec[rr], st, &sbuf[rr * GS_WAVE + lane]) && pp.idc[rr] >= 0;
-      work[rr] = __ballot(cand);
-    }
+    const bool cand = stage(pp.rec, st, &sbuf[lane]) && pp.idc >= 0;
+    const uint64_t work = wave_ballot(cand);
     pipe_advance(pp, splats, sids, b, ce);
     const int satn = __hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wave_sync();
-#pragma unroll
-    for (int rr = 0; rr < RB; rr++) {
-      while (work[rr] && live) {
-        const int j = __builtin_ctzll(work[rr]);
-        work[rr] &= work[rr] - 1;
-        const Splat s = sbuf[rr * GS_WAVE + j];
-        const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
-        const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
-        const bool hit = alive && (q <= s.p2.y);
-        nsteps++;
-        if (__ballot(hit) == 0) continue;
-        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-        const float al = hit ? fminf(0.99f, ex) : 0.0f;
-        P = P - al * P;
-        const bool stop = hit && (P < T_STOP);
-        if (__ballot(stop)) {
-          if (stop) alive = false;
-          live = __ballot(alive);
-        }
-      }
-    }
+    walk_worklist(work, sbuf, [&](const Splat &s, int) {
+      const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
+      const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
+      const bool alive = P >= T_STOP, inq = q <= s.p2.y;
+      const bool hit = alive && inq;
+      nsteps++;
+      if (!(wave_ballot(alive) & wave_ballot(inq))) return true;
+      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+      const float al = hit ? fminf(0.99f, ex) : 0.0f;
+      P = P - al * P;
+      live = wave_ballot(P >= T_STOP) != 0;
+      return live;
+    });
     satv = satn;
     wave_sync();
   }
-  (void)lane;
   return P;
 }
 
@@ -251,7 +236,7 @@ __device__ __forceinline__ int ld_i(const int32_t *p) {
 }
 
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
-__attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
+__attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
     int32_t *__restrict__ last, char *__restrict__ state, int T,
@@ -263,7 +248,8 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
   const int P = cam.width * cam.height;
   const int lane = __lane_id();
   uint32_t nhits = 0, nsteps = 0, nhsteps = 0;  // per worker; far below 2^32
-  Worker wk = make_worker();
+  __shared__ uint32_t drained;
+  Worker wk = make_worker(&drained);
   for (;;) {
     const int t = next_item(fs, 0, wk);
     if (t < 0) break;
@@ -303,7 +289,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
         Pp = product_range(splats, sorted_ids, cs, ce, st, x, sbuf, sat, p, gave_up, nsteps);
         if (gave_up) Pp = 0.0f;  // an earlier chunk already took every pixel below 1e-4
         // every pixel of the quarter below the threshold: later chunks may give up
-        if (!gave_up && __ballot(x.inside && Pp >= T_STOP) == 0 && lane == 0) atomicMin(sat, p);
+        if (!gave_up && wave_ballot(x.inside && Pp >= T_STOP) == 0 && lane == 0) atomicMin(sat, p);
       }
       fs.PA[(int64_t)ci * 64 + lane] = Pp;
       wave_release();
@@ -331,7 +317,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
         }
       }
     }
-    ok = __shfl(ok, 0, GS_WAVE);
+    ok = wave_first(ok);
     __threadfence();  // acquire: the producers' PA stores are visible from here
     for (int q = 0; q < p; q++)
       Tin = ok ? Tin * ld_f(&fs.PA[(int64_t)chunk_index(idx, q, quad, k) * 64 + lane]) : 0.0f;
@@ -357,7 +343,7 @@ __attribute__((amdgpu_waves_per_eu(8))) k_render_fwd(
     if (lane == 0)
       prev = __hip_atomic_fetch_add(&fs.doneB[idx * 4 + quad], 1, __ATOMIC_ACQ_REL,
                                     __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0, GS_WAVE);
+    prev = wave_first(prev);
     if (prev != k - 1 || st.empty) continue;
     // the last finisher of this quarter composes the chunks in depth order
     __threadfence();
