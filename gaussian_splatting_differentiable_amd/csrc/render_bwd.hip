@@ -118,31 +118,21 @@ __device__ __forceinline__ int wave_max(int v) {
   return wave_first(v);
 }
 
-constexpr int RB = 1;                // 64-splat rounds per batch
-constexpr int BATCH = RB * GS_WAVE;  // splats per staged batch
+constexpr int BATCH = GS_WAVE;  // splats per staged batch
 
 // Two-stage load pipeline for the back-to-front walk: the ids of the batch
 // after next and the records of the next batch are in flight while a batch is
 // processed. Slots outside the range carry id -1 (and read record 0).
-__device__ __forceinline__ void load_ids(const int32_t *__restrict__ sids, int lo, int hi,
-                                         int (&id)[RB]) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int r = 0; r < RB; r++) {
-    const int e = lo + r * GS_WAVE + lane;
-    id[r] = e < hi ? sids[e] : -1;
-  }
-}
-
-__device__ __forceinline__ void load_recs(const Splat *__restrict__ splats, const int (&id)[RB],
-                                          Splat (&rec)[RB]) {
-#pragma unroll
-  for (int r = 0; r < RB; r++) rec[r] = splats[id[r] >= 0 ? id[r] : 0];
+__device__ __forceinline__ int load_id(const int32_t *__restrict__ sids, int lo, int hi) {
+  const int e = lo + __lane_id();
+  return e < hi ? sids[e] : -1;
 }
 
 // Walk positions [cs, cs + kmax) back to front for one quarter. Lane state:
 // T (transmittance after the lane's last consumed entry), accum, and lastp,
-// the number of entries the lane consumed from cs.
+// the number of entries the lane consumed from cs. Each staged record carries
+// 1/o, 2b and log2(o) in place of o, depth and pad, so the per-entry work has
+// no reciprocal of o, no doubling and no logarithm.
 __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
                                           const int32_t *__restrict__ sids, int cs, int kmax,
                                           const SubTile &st, float fx, float fy, int lastp,
@@ -152,74 +142,68 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
   const int comp = comp_of_lane(lane);
   int hiE = cs + kmax;
   int lo = max(cs, hiE - BATCH);
-  int idc[RB], idn[RB];
-  Splat rec[RB];
+  int idc = -1, idn = -1;
+  Splat rec;
   if (hiE > cs) {
-    load_ids(sids, lo, hiE, idc);
-    load_recs(splats, idc, rec);
-    load_ids(sids, max(cs, lo - BATCH), lo, idn);
+    idc = load_id(sids, lo, hiE);
+    rec = splats[idc >= 0 ? idc : 0];
+    idn = load_id(sids, max(cs, lo - BATCH), lo);
   }
   while (hiE > cs) {
-    uint64_t work[RB];
-#pragma unroll
-    for (int r = 0; r < RB; r++) {
-      Splat s = rec[r];
-      const bool cand = idc[r] >= 0 && rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x,
-                                                    s.p2.y, st.hx0, st.hx1, st.hy0, st.hy1);
-      s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
-      sbuf[r * GS_WAVE + lane] = s;
-      sid[r * GS_WAVE + lane] = idc[r];
-      work[r] = wave_ballot(cand);
-    }
+    Splat s = rec;
+    const bool cand = idc >= 0 && rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y,
+                                                st.hx0, st.hx1, st.hy0, st.hy1);
+    s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
+    s.p2.z = 2.0f * s.p0.w;
+    s.p1.y = __builtin_amdgcn_rcpf(s.p1.y);
+    sbuf[lane] = s;
+    sid[lane] = idc;
+    const uint64_t work = wave_ballot(cand);
     const int nhi = lo, nlo = max(cs, lo - BATCH);
     // records of [nlo, nhi), ids of the batch below it
-#pragma unroll
-    for (int r = 0; r < RB; r++) idc[r] = idn[r];
-    load_recs(splats, idc, rec);
-    load_ids(sids, max(cs, nlo - BATCH), nlo, idn);
+    idc = idn;
+    rec = splats[idc >= 0 ? idc : 0];
+    idn = load_id(sids, max(cs, nlo - BATCH), nlo);
     wave_sync();
-#pragma unroll
-    for (int rr = RB - 1; rr >= 0; rr--) {
-      while (work[rr]) {
-        const int j = 63 - __builtin_clzll(work[rr]);  // back to front
-        work[rr] &= ~(1ull << j);
-        const int slot = rr * GS_WAVE + j;
-        const Splat s = sbuf[slot];
-        const int rel = lo + slot - cs;
-        const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
-        const float dx = fx - s.p0.x, dy = fy - s.p0.y;
-        const float adx = a * dx, cdy = c * dy;
-        const float q = __builtin_fmaf(cdy, dy, __builtin_fmaf((2.0f * b) * dx, dy, adx * dx));
-        const bool hit = rel < lastp && (q <= s.p2.y);
-        if (wave_ballot(hit) == 0) continue;
-        // branchless: a missed pixel takes alpha = 0, which leaves T and accum
-        // unchanged and contributes zero to every sum
-        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-        const float oG = hit ? ex : 0.0f;  // o G
-        const float al = fminf(0.99f, oG);
-        T = T * __builtin_amdgcn_rcpf(1.0f - al);  // T before this splat
-        const float cg = __builtin_fmaf(s.p1.z, g0, __builtin_fmaf(s.p1.w, g1, s.p2.x * g2));
-        const float diff = cg - accum;
-        const float dal = T * diff;  // dL/dalpha
-        accum = __builtin_fmaf(al, diff, accum);
-        const float w = al * T;
-        const bool live_g = oG < 0.99f;  // a clamped alpha passes no gradient
-        const float m = live_g ? al * dal : 0.0f;  // -2 dL/dq
-        float gr[9];
-        gr[0] = m * __builtin_fmaf(b, dy, adx);  // dq/dmx = -2 (a dx + b dy)
-        gr[1] = m * __builtin_fmaf(b, dx, cdy);
-        gr[2] = (-0.5f * m) * (dx * dx);
-        gr[3] = -(m * (dx * dy));
-        gr[4] = (-0.5f * m) * (dy * dy);
-        gr[5] = live_g ? oG * dal : 0.0f;  // o G dL/dalpha
-        gr[6] = w * g0;
-        gr[7] = w * g1;
-        gr[8] = w * g2;
-        float out = reduce_scatter9(gr);
-        if (comp == 5) out *= __builtin_amdgcn_rcpf(s.p1.y);
-        if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[slot] + comp], out);
-      }
-    }
+    const int base = lo - cs;
+    walk_worklist<true>(work, sbuf, [&](const Splat &s, int j) {
+      const int rel = base + j;
+      const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
+      const float dx = fx - s.p0.x, dy = fy - s.p0.y;
+      const float adx = a * dx, cdy = c * dy;
+      // canon_q with the staged 2b
+      const float q = __builtin_fmaf(cdy, dy, __builtin_fmaf(s.p2.z * dx, dy, adx * dx));
+      const bool inr = rel < lastp, inq = q <= s.p2.y;
+      if (!(wave_ballot(inr) & wave_ballot(inq))) return true;
+      const bool hit = inr && inq;
+      // branchless: a missed pixel takes alpha = 0, which leaves T and accum
+      // unchanged and contributes zero to every sum
+      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
+      const float oG = hit ? ex : 0.0f;  // o G
+      const float al = fminf(0.99f, oG);
+      T = T * __builtin_amdgcn_rcpf(1.0f - al);  // T before this splat
+      const float cg = __builtin_fmaf(s.p1.z, g0, __builtin_fmaf(s.p1.w, g1, s.p2.x * g2));
+      const float diff = cg - accum;
+      const float dal = T * diff;  // dL/dalpha
+      accum = __builtin_fmaf(al, diff, accum);
+      const float w = al * T;
+      const bool live_g = oG < 0.99f;  // a clamped alpha passes no gradient
+      const float m = live_g ? al * dal : 0.0f;  // -2 dL/dq
+      float gr[9];
+      gr[0] = m * __builtin_fmaf(b, dy, adx);  // dq/dmx = -2 (a dx + b dy)
+      gr[1] = m * __builtin_fmaf(b, dx, cdy);
+      gr[2] = (-0.5f * m) * (dx * dx);
+      gr[3] = -(m * (dx * dy));
+      gr[4] = (-0.5f * m) * (dy * dy);
+      gr[5] = live_g ? oG * dal : 0.0f;  // o G dL/dalpha
+      gr[6] = w * g0;
+      gr[7] = w * g1;
+      gr[8] = w * g2;
+      float out = reduce_scatter9(gr);
+      if (comp == 5) out *= s.p1.y;  // divide o back out
+      if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[j] + comp], out);
+      return true;
+    });
     wave_sync();
     hiE = nhi;
     lo = nlo;

@@ -94,30 +94,6 @@ __device__ __forceinline__ void pipe_advance(Pipe &pp, const Splat *__restrict__
   pp.idn = load_id(sids, b + 2 * BATCH, ce);
 }
 
-// Walk the staged worklist (set bits of work, lowest slot first), calling
-// f(record, slot) on each until f returns false. The LDS read of the next
-// entry's record is issued before f runs on the current one, so its latency
-// overlaps the blending; two record buffers alternate, so no copies are made.
-template <class F>
-__device__ __forceinline__ void walk_worklist(uint64_t w, const Splat *sbuf, F &&f) {
-  if (!w) return;
-  int j0 = __builtin_ctzll(w);
-  w &= w - 1;
-  Splat s0 = sbuf[j0];
-  for (;;) {
-    const bool more1 = w != 0;
-    const int j1 = more1 ? __builtin_ctzll(w) : j0;
-    w &= w - 1;
-    const Splat s1 = sbuf[j1];
-    if (!f(s0, j0) || !more1) return;
-    const bool more0 = w != 0;
-    j0 = more0 ? __builtin_ctzll(w) : j1;
-    w &= w - 1;
-    s0 = sbuf[j0];
-    if (!f(s1, j1) || !more0) return;
-  }
-}
-
 struct Blend {
   float C0, C1, C2, T;
   int consumed;  // list entries consumed (relative to the range start)
@@ -149,7 +125,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
     pipe_advance(pp, splats, sids, b, ce);
     wave_sync();
     const int base = b - cs;
-    walk_worklist(work, sbuf, [&](const Splat &s, int j) {
+    walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
       const int pos = base + j;
       const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
       const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
@@ -203,7 +179,7 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
     pipe_advance(pp, splats, sids, b, ce);
     const int satn = __hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wave_sync();
-    walk_worklist(work, sbuf, [&](const Splat &s, int) {
+    walk_worklist<false>(work, sbuf, [&](const Splat &s, int) {
       const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
       const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
       const bool alive = P >= T_STOP, inq = q <= s.p2.y;

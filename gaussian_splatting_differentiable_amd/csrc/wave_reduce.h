@@ -1,18 +1,23 @@
 // Wave64 reduce-scatter of the 9 per-lane gradient values of one splat.
 //
 // "What the 3DGS Literature Left on the Table", Step 2 (Figure 6): instead of 9
-// full butterflies, halve the set of live components at each exchange so that
-// the sums end on distinct lanes and one atomic instruction with 9 active lanes
-// writes them all. On gfx950 the first two exchanges are the lane-half swaps
-// v_permlane32_swap (lanes 0-31 <-> 32-63) and v_permlane16_swap (rows 0,2 <->
-// rows 1,3); each swap moves one component pair across, so one add per pair
-// sums it. The last 16 lanes of each row are summed with four DPP row
-// rotations (ror 8, 4, 2, 1), which fold into v_add_f32_dpp.
+// full butterflies, halve the set of live values at each exchange so that the
+// sums end on distinct lanes and one atomic instruction with 9 active lanes
+// writes them all. On gfx950:
 //
-//   after swap32 : lanes 0-31 hold components 0-4, lanes 32-63 hold 5-9 (9 = 0)
-//   after swap16 : row 0 {0,1,2}, row 1 {3,4,-}, row 2 {5,6,7}, row 3 {8,-,-}
-//   row sums     : every lane of a row holds its row's (up to) three sums
-// Lane 16 r + s (s < 3) then owns component comp_of(r, s).
+//   swap32 (v_permlane32_swap, lanes 0-31 <-> 32-63), pairs (0,5) (1,6) (2,7)
+//          (3,8) (4,-): lanes 0-31 keep components 0-4, lanes 32-63 keep 5-8;
+//   swap16 (v_permlane16_swap, rows 0,2 <-> rows 1,3), pairs (t0,t1) (t2,t3)
+//          (t4,-): row 0 keeps {0,2,4}, row 1 {1,3,-}, row 2 {5,7,-}, row 3
+//          {6,8,-}; every lane now holds three partial sums of 4 lanes each;
+//   ror8   (DPP row_ror:8, lane s <-> s^8) on the pair (u0,u1): lanes 0-7 keep
+//          u0, lanes 8-15 keep u1; u2 is summed on all 16 lanes;
+//   mirror (DPP row_half_mirror, lane s <-> 7-s within each 8) on (v,u2):
+//          lanes 0-3 and 8-11 keep v, lanes 4-7 and 12-15 keep u2;
+//   two quad_perm adds finish each group of 4 lanes.
+//
+// Lane 16 r + s then owns: s = 0 -> {0,1,5,6}[r], s = 8 -> {2,3,7,8}[r],
+// s = 4 and r = 0 -> 4. 27 instructions for the 9 sums.
 #pragma once
 #include "gs_common.h"
 
@@ -26,44 +31,44 @@ __device__ __forceinline__ float swap_sum16(float x, float y) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// a + (b as seen through the DPP control CTRL)
 template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int m = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
-  return v + __int_as_float(m);
+__device__ __forceinline__ float dpp_add(float a, float b) {
+  const int m = __builtin_amdgcn_update_dpp(0, __float_as_int(b), CTRL, 0xF, 0xF, false);
+  return a + __int_as_float(m);
 }
 
-// sum over the 16 lanes of each row; every lane ends with its row's sum
-__device__ __forceinline__ float row_sum16(float v) {
-  v = dpp_add<0x128>(v);  // row_ror:8
-  v = dpp_add<0x124>(v);  // row_ror:4
-  v = dpp_add<0x122>(v);  // row_ror:2
-  v = dpp_add<0x121>(v);  // row_ror:1
-  return v;
-}
+constexpr int DPP_ROW_ROR8 = 0x128;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_QUAD_1032 = 0xB1;  // quad_perm [1,0,3,2]
 
 // Component owned by lane (row r, slot s), or -1.
 __device__ __forceinline__ int comp_of_lane(int lane) {
   const int r = lane >> 4, s = lane & 15;
-  if (s >= 3) return -1;
-  // row 0: 0 1 2 | row 1: 3 4 - | row 2: 5 6 7 | row 3: 8 - -
-  const int base = (r == 0) ? 0 : (r == 1) ? 3 : (r == 2) ? 5 : 8;
-  const int cnt = (r == 0 || r == 2) ? 3 : (r == 1) ? 2 : 1;
-  return s < cnt ? base + s : -1;
+  if (s == 0) return r < 2 ? r : r + 3;      // 0 1 5 6
+  if (s == 8) return r < 2 ? r + 2 : r + 5;  // 2 3 7 8
+  if (s == 4 && r == 0) return 4;
+  return -1;
 }
 
 // Reduce g[0..8] over the wave; returns the sum of component comp_of_lane(lane)
-// on the lanes that own one (garbage elsewhere).
+// on the lanes that own one (partial sums elsewhere).
 __device__ __forceinline__ float reduce_scatter9(const float g[9]) {
-  // lanes 0-31 keep components j, lanes 32-63 keep j+5
   const float t0 = swap_sum32(g[0], g[5]);
   const float t1 = swap_sum32(g[1], g[6]);
   const float t2 = swap_sum32(g[2], g[7]);
   const float t3 = swap_sum32(g[3], g[8]);
   const float t4 = swap_sum32(g[4], 0.0f);
-  // even rows keep t0..t2, odd rows keep t3, t4, 0
-  const float u0 = row_sum16(swap_sum16(t0, t3));
-  const float u1 = row_sum16(swap_sum16(t1, t4));
-  const float u2 = row_sum16(swap_sum16(t2, 0.0f));
+  const float u0 = swap_sum16(t0, t1);
+  const float u1 = swap_sum16(t2, t3);
+  const float u2 = swap_sum16(t4, 0.0f);
   const int s = __lane_id() & 15;
-  return s == 0 ? u0 : (s == 1 ? u1 : u2);
+  const bool lo8 = s < 8, lo4 = (s & 4) == 0;
+  const float v = dpp_add<DPP_ROW_ROR8>(lo8 ? u0 : u1, lo8 ? u1 : u0);
+  const float w = dpp_add<DPP_ROW_ROR8>(u2, u2);
+  float x = dpp_add<DPP_ROW_HALF_MIRROR>(lo4 ? v : w, lo4 ? w : v);
+  x = dpp_add<DPP_QUAD_2301>(x, x);
+  x = dpp_add<DPP_QUAD_1032>(x, x);
+  return x;
 }
