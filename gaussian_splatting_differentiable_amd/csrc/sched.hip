@@ -17,7 +17,8 @@
 // and this TU is compiled with -ffp-contract=off, so a host copy of the policy
 // returns the same (h, k).
 //
-// One workgroup of 1024 threads does everything; T <= 65535 tiles.
+// One workgroup of 1024 threads does everything; T <= 65535 tiles, in LDS up to
+// 8192 tiles.
 #include "render_common.h"
 
 namespace {
@@ -142,17 +143,105 @@ __device__ void block_radix_pass(const uint32_t *__restrict__ kin, const int32_t
 }
 
 constexpr int NCLS = 2 * GS_GROUPS;  // (group, chunked?) classes of the LPT positions
+constexpr int HMAX = GS_HK_MAX / 2;  // the largest h of any policy candidate
+// Frames of up to TL tiles are scheduled in LDS: the sort buffers, the policy's
+// prefix sums and the queue partition live in one dynamic LDS block, so the
+// workgroup makes a handful of global round trips instead of two per pass.
+constexpr int TL = 8192;
+constexpr size_t POLICY_BYTES = 8 * (HMAX + 1) + 4 * (HMAX + 1);
+constexpr size_t LDS_BYTES = 16 * (size_t)TL;  // four arrays of TL words
+
+__device__ __forceinline__ void block_min_idx(double &best, int &idx) {
+  __shared__ double wb[NW];
+  __shared__ int wi[NW];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const double ob = __shfl_xor(best, d, 64);
+    const int oi = __shfl_xor(idx, d, 64);
+    if (ob < best || (ob == best && oi < idx)) {
+      best = ob;
+      idx = oi;
+    }
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    wb[threadIdx.x >> 6] = best;
+    wi[threadIdx.x >> 6] = idx;
+  }
+  __syncthreads();
+  best = wb[0];
+  idx = wi[0];
+  for (int w = 1; w < NW; w++)
+    if (wb[w] < best || (wb[w] == best && wi[w] < idx)) {
+      best = wb[w];
+      idx = wi[w];
+    }
+  __syncthreads();
+}
+
+// Stable partition of the LPT positions e in [0, T) by class
+// c(e) = 2 group(order[e]) + (e >= h): perm lists the positions class by class,
+// each class in LPT order; ccount/cstart get the class sizes and starts.
+__device__ void class_partition(const int32_t *order, int T, int h, int tiles_x, int32_t *perm,
+                                int *ccount, int *cstart) {
+  __shared__ int pc[NW][NCLS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x < NW * NCLS) (&pc[0][0])[threadIdx.x] = 0;
+  __syncthreads();
+  const int chunk = (T + NW - 1) / NW;
+  const int c0 = min(T, w * chunk), c1 = min(T, c0 + chunk);
+  auto cls = [&](int e) { return 2 * tile_group(order[e], tiles_x) + (e >= h ? 1 : 0); };
+  for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&pc[w][cls(e)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int c = 0; c < NCLS; c++) {
+      cstart[c] = run;
+      for (int q = 0; q < NW; q++) {
+        const int v = pc[q][c];
+        pc[q][c] = run;
+        run += v;
+      }
+      ccount[c] = run - cstart[c];
+    }
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int base = c0; base < c1; base += 64) {
+    const int e = base + lane;
+    const bool valid = e < c1;
+    const int c = valid ? cls(e) : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const uint64_t bal = __ballot((c >> b) & 1);
+      peers &= ((c >> b) & 1) ? bal : ~bal;
+    }
+    if (valid) {
+      const int below = __popcll(peers & lt);
+      const int pos = pc[w][c] + below;
+      perm[pos] = e;
+      if (below == __popcll(peers) - 1) pc[w][c] = pos + 1;
+    }
+  }
+  __syncthreads();
+}
 
 __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges, int T, int tiles_x,
                                                  int chunk_mode, int force_k, int force_h,
                                                  double lambda_, double beta, double eps,
                                                  int nblocks, char *__restrict__ fwd_state,
                                                  unsigned long long *__restrict__ stats) {
+  extern __shared__ __align__(16) uint32_t dyn[];
   FwdState fs = fwd_state_at(fwd_state, T);
   const double workers = (double)(nblocks * GS_WAVES_PER_BLOCK) / 4.0;  // four waves per tile
-  uint32_t *tmp_k = reinterpret_cast<uint32_t *>(fs.items);
-  int32_t *tmp_v = fs.items + T;
-  uint32_t *key = reinterpret_cast<uint32_t *>(fs.counts);
+  // working arrays: LDS for frames of up to TL tiles, else the forward state's
+  // item and bound arrays (written for real only after they served here)
+  const bool lds = T <= TL;
+  uint32_t *key = lds ? dyn : reinterpret_cast<uint32_t *>(fs.counts);
+  int32_t *ord = lds ? reinterpret_cast<int32_t *>(dyn + TL) : fs.order;
+  uint32_t *tmp_k = lds ? dyn + 2 * TL : reinterpret_cast<uint32_t *>(fs.items);
+  int32_t *tmp_v = lds ? reinterpret_cast<int32_t *>(dyn + 3 * TL) : fs.items + T;
   // 1. counts and the (bit-limited) descending key
   uint32_t mx = 0;
   for (int t0 = threadIdx.x; t0 < T; t0 += NT * RB_ROUNDS) {
@@ -168,7 +257,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
       if (t < T) {
         const uint32_t c = (uint32_t)max(0, rr[r].y - rr[r].x);
         key[t] = c;
-        fs.order[t] = t;
+        ord[t] = t;
         mx = max(mx, c);
       }
     }
@@ -184,23 +273,25 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   const int npass = (bits + 7) / 8;
   for (int pass = 0; pass < npass; pass++) {
     const bool even = (pass & 1) == 0;
-    block_radix_pass(even ? key : tmp_k, even ? fs.order : tmp_v, even ? tmp_k : key,
-                     even ? tmp_v : fs.order, T, 8 * pass);
+    block_radix_pass(even ? key : tmp_k, even ? ord : tmp_v, even ? tmp_k : key,
+                     even ? tmp_v : ord, T, 8 * pass);
   }
   if (npass & 1) {
     for (int t = threadIdx.x; t < T; t += NT) {
       key[t] = tmp_k[t];
-      fs.order[t] = tmp_v[t];
+      ord[t] = tmp_v[t];
     }
     __syncthreads();
   }
-  for (int t0 = threadIdx.x; t0 < T; t0 += NT * RB_ROUNDS) {
-    uint32_t kk[RB_ROUNDS];
-#pragma unroll
-    for (int r = 0; r < RB_ROUNDS; r++) kk[r] = t0 + r * NT < T ? key[t0 + r * NT] : 0u;
-#pragma unroll
-    for (int r = 0; r < RB_ROUNDS; r++)
-      if (t0 + r * NT < T) fs.counts[t0 + r * NT] = (int32_t)(full - kk[r]);
+  // sorted counts: the forward state keeps them and the LPT order
+  int32_t *cnts = lds ? reinterpret_cast<int32_t *>(tmp_k) : fs.counts;
+  for (int t = threadIdx.x; t < T; t += NT) {
+    const int32_t c = (int32_t)(full - key[t]);
+    cnts[t] = c;
+    if (lds) {
+      fs.counts[t] = c;
+      fs.order[t] = ord[t];
+    }
   }
   __syncthreads();
 
@@ -211,19 +302,17 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     h = force_h <= 0 ? T : min(force_h, T);
     h = min(h, GS_HK_MAX / k);
   } else if (chunk_mode == 1 && T > 0) {
-    constexpr int HMAX = GS_HK_MAX / 2;  // the largest h of any candidate
-    __shared__ long long sS[HMAX + 1];   // sS[h] = N_1 + ... + N_h (exact)
-    __shared__ int sN[HMAX + 1];         // sN[h] = N_{h+1} (0 past the last tile)
-    __shared__ double s_best[NT];
-    __shared__ int s_idx[NT];
+    // sS[h] = N_1 + ... + N_h (exact), sN[h] = N_{h+1} (0 past the last tile)
+    long long *sS = reinterpret_cast<long long *>(dyn);
+    int *sN = reinterpret_cast<int *>(sS + HMAX + 1);
     long long total_ll = 0;
-    for (int t = threadIdx.x; t < T; t += NT) total_ll += fs.counts[t];
+    for (int t = threadIdx.x; t < T; t += NT) total_ll += cnts[t];
     long long tot;
     (void)block_excl_scan<long long>(total_ll, tot);
     {
       static_assert(HMAX == 2 * NT, "two prefix entries per thread");
       const int i0 = 2 * threadIdx.x;
-      const long long a = i0 < T ? fs.counts[i0] : 0, b = i0 + 1 < T ? fs.counts[i0 + 1] : 0;
+      const long long a = i0 < T ? cnts[i0] : 0, b = i0 + 1 < T ? cnts[i0 + 1] : 0;
       long long all;
       const long long before = block_excl_scan<long long>(a + b, all);
       sS[i0 + 1] = before + a;
@@ -232,11 +321,11 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
       sN[i0 + 1] = (int)b;
       if (threadIdx.x == 0) {
         sS[0] = 0;
-        sN[HMAX] = HMAX < T ? fs.counts[HMAX] : 0;
+        sN[HMAX] = HMAX < T ? cnts[HMAX] : 0;
       }
     }
     __syncthreads();
-    const double Nt = (double)tot, N1 = (double)fs.counts[0];
+    const double Nt = (double)tot, N1 = (double)cnts[0];
     const double T0 = fmax(Nt / workers, N1) + beta * N1;
     // candidates in (k ascending, h ascending) order
     int len[4], off[5];
@@ -260,25 +349,11 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
         bidx = i;
       }
     }
-    s_best[threadIdx.x] = best;
-    s_idx[threadIdx.x] = bidx;
-    __syncthreads();
-    for (int sft = NT / 2; sft > 0; sft >>= 1) {
-      if ((int)threadIdx.x < sft) {
-        const double ob = s_best[threadIdx.x + sft];
-        const int oi = s_idx[threadIdx.x + sft];
-        if (ob < s_best[threadIdx.x] || (ob == s_best[threadIdx.x] && oi < s_idx[threadIdx.x])) {
-          s_best[threadIdx.x] = ob;
-          s_idx[threadIdx.x] = oi;
-        }
-      }
-      __syncthreads();
-    }
-    const int bi = s_idx[0];
-    if (bi != 0x7FFFFFFF && s_best[0] <= (1.0 - eps) * T0) {
-      const int q = bi < off[1] ? 0 : (bi < off[2] ? 1 : (bi < off[3] ? 2 : 3));
+    block_min_idx(best, bidx);
+    if (bidx != 0x7FFFFFFF && best <= (1.0 - eps) * T0) {
+      const int q = bidx < off[1] ? 0 : (bidx < off[2] ? 1 : (bidx < off[3] ? 2 : 3));
       k = 2 << q;
-      h = bi - off[q] + 1;
+      h = bidx - off[q] + 1;
     }
     __syncthreads();
   }
@@ -286,41 +361,12 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
 
   // 4. queues. The LPT positions e in [0, T) fall into classes (group of the
   //    tile, chunked iff e < h); a stable partition by class keeps the LPT order
-  //    inside every class. The per-quarter bounds array (written by the forward
-  //    pass later) holds the partition's temporaries.
-  uint32_t *ck = reinterpret_cast<uint32_t *>(fs.sub_last);
-  int32_t *cv = fs.sub_last + T;
-  uint32_t *ck2 = reinterpret_cast<uint32_t *>(fs.sub_last + 2 * T);
-  int32_t *perm = fs.sub_last + 3 * T;
+  //    inside every class.
+  int32_t *perm = lds ? reinterpret_cast<int32_t *>(dyn + 2 * TL) : fs.sub_last;
   __shared__ int ccount[NCLS], cstart[NCLS], qoff[GS_GROUPS + 1];
-  if (threadIdx.x < NCLS) ccount[threadIdx.x] = 0;
-  __syncthreads();
-  for (int e0 = threadIdx.x; e0 < T; e0 += NT * RB_ROUNDS) {
-    int tl[RB_ROUNDS];
-#pragma unroll
-    for (int r = 0; r < RB_ROUNDS; r++) {
-      const int e = e0 + r * NT;
-      tl[r] = e < T ? fs.order[e] : 0;
-    }
-#pragma unroll
-    for (int r = 0; r < RB_ROUNDS; r++) {
-      const int e = e0 + r * NT;
-      if (e < T) {
-        const uint32_t c = 2u * (uint32_t)tile_group(tl[r], tiles_x) + (e >= h ? 1u : 0u);
-        ck[e] = c;
-        cv[e] = e;
-        atomicAdd(&ccount[c], 1);
-      }
-    }
-  }
-  __syncthreads();
-  block_radix_pass(ck, cv, ck2, perm, T, 0);
+  class_partition(ord, T, h, tiles_x, perm, ccount, cstart);
   if (threadIdx.x == 0) {
-    int run = 0, q = 0;
-    for (int c = 0; c < NCLS; c++) {
-      cstart[c] = run;
-      run += ccount[c];
-    }
+    int q = 0;
     for (int g = 0; g < GS_GROUPS; g++) {
       qoff[g] = q;
       q += 8 * k * ccount[2 * g] + 4 * ccount[2 * g + 1];
@@ -328,22 +374,10 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     qoff[GS_GROUPS] = q;
   }
   __syncthreads();
-  for (int i0 = threadIdx.x; i0 < T; i0 += NT * RB_ROUNDS) {
-    int ee[RB_ROUNDS], cc[RB_ROUNDS], tl[RB_ROUNDS];
-#pragma unroll
-    for (int u = 0; u < RB_ROUNDS; u++) {
-      const int i = i0 + u * NT;
-      ee[u] = i < T ? perm[i] : 0;
-      cc[u] = i < T ? (int)ck2[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < RB_ROUNDS; u++) tl[u] = fs.order[ee[u]];
-#pragma unroll
-    for (int u = 0; u < RB_ROUNDS; u++) {
-    const int i = i0 + u * NT;
-    if (i >= T) continue;
-    const int e = ee[u];
-    const int c = cc[u];
+  for (int i = threadIdx.x; i < T; i += NT) {
+    const int e = perm[i];
+    const int tile = ord[e];
+    const int c = 2 * tile_group(tile, tiles_x) + (e >= h ? 1 : 0);
     const int g = c >> 1, r = i - cstart[c];
     if ((c & 1) == 0) {  // chunked: LPT slot e
       const int a0 = qoff[g] + 4 * k * r, b0 = a0 + 4 * k * ccount[c];
@@ -354,9 +388,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
         }
     } else {
       const int p0 = qoff[g] + 8 * k * ccount[c - 1] + 4 * r;
-      const int tile = tl[u];
       for (int q = 0; q < 4; q++) fs.items[p0 + q] = make_item(ITEM_PLAIN, q, 0, tile);
-    }
     }
   }
   const int nA = 4 * h * k;
@@ -398,7 +430,12 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_
                               int force_h, double lambda_, double beta, double eps, int nblocks,
                               void *fwd_state, int64_t *stats, hipStream_t st) {
   const int T = cam.tiles_x * cam.tiles_y;
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(NT), 0, st, reinterpret_cast<const int2 *>(ranges), T,
+  const size_t lds = T <= TL ? LDS_BYTES : POLICY_BYTES;
+  static_assert(POLICY_BYTES <= 4 * (size_t)TL, "the policy arrays fit in the first LDS array");
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_schedule),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(NT), lds, st, reinterpret_cast<const int2 *>(ranges), T,
                      cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, nblocks,
                      reinterpret_cast<char *>(fwd_state),
                      reinterpret_cast<unsigned long long *>(stats));

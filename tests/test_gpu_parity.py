@@ -344,16 +344,16 @@ def _policy_frame(gsr, counts, W, H):
 
 
 @pytest.mark.parametrize("case", ["pareto", "one_outlier", "flat", "two_level"])
-def test_device_policy_equals_host_policy(case):
+@pytest.mark.parametrize("W,H", [(1920, 1080), (3840, 2160)])  # 8160 tiles (LDS path), 32400
+def test_device_policy_equals_host_policy(case, W, H):
     gsr = _gsr()
     rng = np.random.default_rng(abs(hash(case)) % 1000)
-    W, H = 1920, 1080
     T = ((W + 15) // 16) * ((H + 15) // 16)
     if case == "pareto":
         counts = (rng.pareto(1.2, T) * 300).astype(np.int64)
     elif case == "one_outlier":
         counts = rng.integers(50, 400, T)
-        counts[1234] = 250_000
+        counts[1234 % T] = 250_000
     elif case == "flat":
         counts = np.full(T, 700)
     else:
@@ -370,6 +370,7 @@ def test_device_policy_equals_host_policy(case):
                                f32(gsr.DEFAULT_BETA), f32(gsr.DEFAULT_EPS), gsr.HK_MAX)
     assert (plan["h"], plan["k"] if plan["h"] else 1) == (h, k), (plan["h"], plan["k"], h, k)
     assert plan["nA"] == 4 * h * (k if h else 0)
+    check_queues(plan, (W + 15) // 16)
     assert plan["qoff"][0] == 0 and np.all(np.diff(plan["qoff"]) >= 0)
     check_queues(plan, (W + 15) // 16)
     if case == "one_outlier":
