@@ -227,6 +227,9 @@ __device__ void class_partition(const int32_t *order, int T, int h, int tiles_x,
   __syncthreads();
 }
 
+// LDS: the frame has at most TL tiles and its working arrays live in LDS (an
+// instantiation of its own, so that every access to them is an LDS access).
+template <bool LDS>
 __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges, int T, int tiles_x,
                                                  int chunk_mode, int force_k, int force_h,
                                                  double lambda_, double beta, double eps,
@@ -237,7 +240,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   const double workers = (double)(nblocks * GS_WAVES_PER_BLOCK) / 4.0;  // four waves per tile
   // working arrays: LDS for frames of up to TL tiles, else the forward state's
   // item and bound arrays (written for real only after they served here)
-  const bool lds = T <= TL;
+  constexpr bool lds = LDS;
   uint32_t *key = lds ? dyn : reinterpret_cast<uint32_t *>(fs.counts);
   int32_t *ord = lds ? reinterpret_cast<int32_t *>(dyn + TL) : fs.order;
   uint32_t *tmp_k = lds ? dyn + 2 * TL : reinterpret_cast<uint32_t *>(fs.items);
@@ -432,10 +435,11 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_
   const int T = cam.tiles_x * cam.tiles_y;
   const size_t lds = T <= TL ? LDS_BYTES : POLICY_BYTES;
   static_assert(POLICY_BYTES <= 4 * (size_t)TL, "the policy arrays fit in the first LDS array");
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_schedule),
+  auto kern = T <= TL ? k_schedule<true> : k_schedule<false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(NT), lds, st, reinterpret_cast<const int2 *>(ranges), T,
+  hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, st, reinterpret_cast<const int2 *>(ranges), T,
                      cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, nblocks,
                      reinterpret_cast<char *>(fwd_state),
                      reinterpret_cast<unsigned long long *>(stats));
