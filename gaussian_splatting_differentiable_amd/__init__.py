@@ -25,7 +25,7 @@ GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED = -3, -4, -5
 SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
 
 EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_bin_tiles",
-           "gs_sort_keys", "gs_render_fwd", "gs_render_bwd")
+           "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start", "gs_timing_read")
 
 
 class GsError(RuntimeError):
@@ -67,7 +67,10 @@ def lib():
     L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, sz, P]
     L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
-    for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd"):
+    L.gs_timing_start.argtypes = []
+    L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
+    for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
+                 "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -172,6 +175,20 @@ def gs_render_bwd(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, 
                                _ptr(dL_dsplat), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_render_bwd")
+
+
+def gs_timing_start():
+    _check(lib().gs_timing_start(), "gs_timing_start")
+
+
+def gs_timing_read(which: int, cap: int = 512):
+    """Durations (ms) of the raster kernel launches recorded since gs_timing_start;
+    which 0 = k_render_fwd, 1 = k_render_bwd."""
+    buf = (C.c_float * cap)()
+    n = lib().gs_timing_read(int(which), buf, int(cap))
+    if n < 0:
+        raise GsError(n, "gs_timing_read")
+    return [float(buf[i]) for i in range(n)]
 
 
 # ------------------------------------------------------------------ frame driver

@@ -19,11 +19,13 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
 hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
-                                int64_t *stats, int workers_waves, hipStream_t st);
+                                int64_t *stats, int workers_waves, hipEvent_t ev0, hipEvent_t ev1,
+                                hipStream_t st);
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                float *grads, int n, int workers_waves, hipStream_t st);
+                                float *grads, int n, int workers_waves, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t st);
 
 namespace {
 
@@ -53,6 +55,26 @@ bool prep_camera(const gs_camera *c, CamK *k) {
   k->znear = c->znear;
   k->lowpass = c->lowpass;
   return true;
+}
+
+// Per-launch timing of the raster kernels (measurement only): a ring of event
+// pairs per kernel, filled by the render calls while timing is on.
+constexpr int TIMING_SLOTS = 512;
+struct Timing {
+  bool on = false, made = false;
+  int used[2] = {0, 0};
+  hipEvent_t ev[2][TIMING_SLOTS][2] = {};
+};
+Timing g_timing;
+
+// The event pair for the next launch of kernel `which` (0 forward, 1 backward),
+// or nulls when timing is off or the ring is full.
+void timing_slot(int which, hipEvent_t &a, hipEvent_t &b) {
+  a = b = nullptr;
+  if (!g_timing.on || g_timing.used[which] >= TIMING_SLOTS) return;
+  const int i = g_timing.used[which]++;
+  a = g_timing.ev[which][i][0];
+  b = g_timing.ev[which][i][1];
 }
 
 int64_t num_tiles(int32_t w, int32_t h) { return (int64_t)((w + 15) / 16) * ((h + 15) / 16); }
@@ -176,8 +198,11 @@ int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
   const int workers = worker_waves();
   if (workers <= 0) return GS_ERR_HIP;
   (void)workspace; (void)workspace_bytes;
+  hipEvent_t e0, e1;
+  timing_slot(0, e0, e1);
   return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
-                                         last, fwd_state, stats, workers, (hipStream_t)stream));
+                                         last, fwd_state, stats, workers, e0, e1,
+                                         (hipStream_t)stream));
 }
 
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -198,9 +223,38 @@ int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
   const int workers = worker_waves();
   if (workers <= 0) return GS_ERR_HIP;
   (void)workspace; (void)workspace_bytes;
+  hipEvent_t e0, e1;
+  timing_slot(1, e0, e1);
   return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
-                                         fwd_state, dL_drgb, dL_dsplat, n, workers,
+                                         fwd_state, dL_drgb, dL_dsplat, n, workers, e0, e1,
                                          (hipStream_t)stream));
+}
+
+int32_t gs_timing_start(void) {
+  if (!g_timing.made) {
+    for (int w = 0; w < 2; w++)
+      for (int i = 0; i < TIMING_SLOTS; i++)
+        for (int j = 0; j < 2; j++)
+          if (hipEventCreate(&g_timing.ev[w][i][j]) != hipSuccess) return GS_ERR_HIP;
+    g_timing.made = true;
+  }
+  g_timing.used[0] = g_timing.used[1] = 0;
+  g_timing.on = true;
+  return GS_OK;
+}
+
+int32_t gs_timing_read(int32_t which, float *ms, int32_t cap) {
+  if (which < 0 || which > 1 || cap < 0 || (cap > 0 && !ms)) return GS_ERR_INVALID_ARGUMENT;
+  g_timing.on = false;
+  if (!g_timing.made) return 0;
+  const int n = g_timing.used[which] < cap ? g_timing.used[which] : cap;
+  for (int i = 0; i < n; i++) {
+    if (hipEventSynchronize(g_timing.ev[which][i][1]) != hipSuccess) return GS_ERR_HIP;
+    if (hipEventElapsedTime(&ms[i], g_timing.ev[which][i][0], g_timing.ev[which][i][1]) !=
+        hipSuccess)
+      return GS_ERR_HIP;
+  }
+  return n;
 }
 
 }  // extern "C"

@@ -291,7 +291,8 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                float *grads, int n, int workers_waves, hipStream_t st) {
+                                float *grads, int n, int workers_waves, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const FwdState fs = fwd_state_at(fwd_state, ntiles);
@@ -300,10 +301,16 @@ hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                      reinterpret_cast<char *>(fwd_state), ntiles, nblocks);
   hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng,
                      fs.hdr, queue_head(fs, 1, 0));
+  if (ev0) {
+    const hipError_t e = hipEventRecord(ev0, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_render_bwd, dim3(nblocks),
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles, dL, grads);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
+  return e;
 }

@@ -362,7 +362,8 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_
 hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
-                                int64_t *stats, int workers_waves, hipStream_t st) {
+                                int64_t *stats, int workers_waves, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t st) {
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   hipError_t e = gs_launch_schedule(ranges, cam, sched.chunk_mode, sched.force_k, sched.force_h,
@@ -371,10 +372,13 @@ hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
   if (e != hipSuccess) return e;
   // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
   // queues empty exit at once
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_render_fwd, dim3(nblocks), dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,
                      reinterpret_cast<unsigned long long *>(stats));
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
+  return e;
 }

@@ -186,6 +186,22 @@ int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const float *dL_drgb, float *dL_dsplat, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* Kernel timing, for measurement only (no paper passage: it lets a benchmark
+ * divide algorithmic bytes by the raster kernel's own duration rather than by
+ * the whole call's, which also zeroes the gradients and orders the backward's
+ * items). Not thread-safe; one device per process while it is on.
+ * gs_timing_start: the next up to 512 calls each of gs_render_fwd and
+ *   gs_render_bwd record a pair of HIP events on their stream, just before and
+ *   after their raster kernel (k_render_fwd / k_render_bwd). The events are
+ *   created on the first call (current device) and kept until the process ends.
+ *   Returns GS_OK or GS_ERR_HIP.
+ * gs_timing_read(which, ms, cap): ends the recording, waits for the recorded
+ *   launches of kernel `which` (0 forward, 1 backward) and writes up to cap of
+ *   their durations in ms, in launch order, to the HOST array ms. Returns the
+ *   number written, or GS_ERR_INVALID_ARGUMENT / GS_ERR_HIP. */
+int32_t gs_timing_start(void);
+int32_t gs_timing_read(int32_t which, float *ms, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif
