@@ -14,7 +14,7 @@
 // also clears the look-back words of every radix pass of the frame.
 //
 // gs_sort_keys then runs:
-//   - four onesweep LSD passes over the visible splats' depth keys (4096-key
+//   - four onesweep LSD passes over the visible splats' depth keys (8192-key
 //     partitions), the last of which also writes each splat's pair count in
 //     depth order;
 //   - an exclusive scan of those counts: the pair offsets in depth order, and
@@ -46,7 +46,7 @@ constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pair
 constexpr int BIN_T = 256, BIN_BLOCKS_MAX = 512;
 
 // partitions: depth passes and tile passes
-constexpr int DS_THREADS = 256, DS_ITEMS = 16, DS_PART = DS_THREADS * DS_ITEMS;
+constexpr int DS_THREADS = 1024, DS_ITEMS = 8, DS_PART = DS_THREADS * DS_ITEMS;
 constexpr int TS_THREADS = 512, TS_ITEMS = 16, TS_PART = TS_THREADS * TS_ITEMS;
 
 // Per-frame control block at the start of the workspace.
@@ -278,6 +278,12 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __shared__ uint32_t s_gbase[B];
   __shared__ int s_part, s_nvalid;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  {
+    // blocks beyond the frame's partitions take no ticket (the launch is sized
+    // for the capacity); exactly the first parts_of(n) block indices remain
+    const int n_pre = SRC == SRC_DEPTH0 ? n_max : clamp_n(*n_dev, n_max);
+    if ((int64_t)blockIdx.x * PART >= (int64_t)n_pre) return;
+  }
   if (tid == 0) s_part = atomicAdd(ticket, 1);
   for (int i = tid; i < NWV * B; i += NT) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
