@@ -69,7 +69,9 @@ hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t ca
   // exclusive scan of the n counts, total in offsets[n]
   e = gs_launch_scan_i32(offsets, offsets, n, scan_buf, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bin_emit, grid, block, 0, st, n, sp, cam.width, cam.height, cam.tiles_x,
+  // without keys/ids to write, one workgroup sets the status
+  hipLaunchKernelGGL(k_bin_emit, keys ? grid : dim3(1), block, 0, st, n, sp, cam.width, cam.height,
+                     cam.tiles_x,
                      cam.tiles_y, offsets, capacity, keys, ids, status);
   return hipGetLastError();
 }

@@ -247,6 +247,85 @@ __global__ void __launch_bounds__(256) k_depth_bases(SortCtl *__restrict__ ctl,
 
 // ---------------------------------------------------------------- onesweep pass
 
+// Tile counts, ranges and the tile-digit offsets, by one workgroup of 1024
+// threads (it runs as an extra workgroup of the first depth pass, which does
+// not depend on it).
+__device__ void tile_bases_block(SortCtl *__restrict__ ctl, const int32_t *__restrict__ tile_diff,
+                                 int32_t *__restrict__ tile_counts, int tiles_x, int tiles_y,
+                                 int b0, int32_t *__restrict__ ranges) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  __shared__ uint32_t lo_hist[256];
+  const int ntiles = tiles_x * tiles_y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const bool overflow = ctl->overflow != 0;
+  // per-tile counts: every row of the difference array sums to zero (each span
+  // adds +1 and -1 in its own row), so the inclusive prefix of the whole array,
+  // taken row-major, is the count of each tile
+  const int stride = tiles_x + 1, ndiff = tiles_y * stride;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < ndiff; c0 += 1024) {
+    const int i = c0 + threadIdx.x;
+    const int x = i < ndiff ? tile_diff[i] : 0;
+    int v = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(v, d, 64);
+      if (lane >= d) v += o;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    int base = carry, tot = 0;
+    for (int q = 0; q < 16; q++) {
+      base += (q < wid) ? wsum[q] : 0;
+      tot += wsum[q];
+    }
+    if (i < ndiff) {
+      const int ty = i / stride, tx = i - ty * stride;
+      if (tx < tiles_x) tile_counts[ty * tiles_x + tx] = base + v;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) carry = 0;
+  if (threadIdx.x < 256) lo_hist[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t mask0 = (1u << b0) - 1u;
+  for (int c0 = 0; c0 < ntiles; c0 += 1024) {
+    const int t = c0 + threadIdx.x;
+    const int x = (t < ntiles && !overflow) ? tile_counts[t] : 0;
+    if (x) atomicAdd(&lo_hist[t & mask0], (uint32_t)x);
+    int v = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(v, d, 64);
+      if (lane >= d) v += o;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    int base = carry, tot = 0;
+    for (int q = 0; q < 16; q++) {
+      base += (q < wid) ? wsum[q] : 0;
+      tot += wsum[q];
+    }
+    if (t < ntiles) {
+      ranges[2 * t] = base + v - x;
+      ranges[2 * t + 1] = base + v;
+      if ((t & mask0) == 0) ctl->tbase[1][t >> b0] = (uint32_t)(base + v - x);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  // low-digit offsets: every thread takes part in the scan
+  const int v = threadIdx.x <= (int)mask0 ? (int)lo_hist[threadIdx.x] : 0;
+  int tot;
+  const int incl = block_scan<1024>(v, tot);
+  if (threadIdx.x <= (int)mask0) ctl->tbase[0][threadIdx.x] = (uint32_t)(incl - v);
+}
+
 enum Src { SRC_KEYS = 0, SRC_DEPTH0 = 1, SRC_EMIT = 2 };
 
 // Inputs of one pass beyond the (key, value) arrays.
@@ -259,7 +338,10 @@ struct PassIn {
   const int32_t *doff;         // SRC_EMIT: pair offsets in depth order
   const int32_t *part_first;   // SRC_EMIT
   const Splat *splats;         // SRC_EMIT
-  int W, H, tiles_x, tiles_y;  // SRC_EMIT
+  int W, H, tiles_x, tiles_y;  // SRC_EMIT; SRC_DEPTH0's extra workgroup (tiles)
+  const int32_t *tile_diff;    // SRC_DEPTH0's extra workgroup: tile counts and ranges
+  int32_t *tile_counts, *ranges;
+  int b0;
 };
 
 template <int NT, int ITEMS, int BITS, int SRC>
@@ -278,6 +360,14 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __shared__ uint32_t s_gbase[B];
   __shared__ int s_part, s_nvalid;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if constexpr (SRC == SRC_DEPTH0) {
+    static_assert(SRC != SRC_DEPTH0 || NT == 1024, "the tile-bases workgroup has 1024 threads");
+    if (in.ranges && blockIdx.x == gridDim.x - 1) {
+      tile_bases_block(const_cast<SortCtl *>(in.ctl), in.tile_diff, in.tile_counts, in.tiles_x,
+                       in.tiles_y, in.b0, in.ranges);
+      return;
+    }
+  }
   {
     // blocks beyond the frame's partitions take no ticket (the launch is sized
     // for the capacity); exactly the first parts_of(n) block indices remain
@@ -544,84 +634,6 @@ __global__ void __launch_bounds__(SCAN_T) k_dscan_apply(SortCtl *__restrict__ ct
 // the two tile passes: the low digit groups tiles by t mod 2^b0, the high digit
 // by t >> b0, whose offset is the start of tile d << b0. An overflowing frame
 // gets empty ranges.
-__global__ void __launch_bounds__(1024) k_tile_bases(SortCtl *__restrict__ ctl,
-                                                     const int32_t *__restrict__ tile_diff,
-                                                     int32_t *__restrict__ tile_counts, int tiles_x,
-                                                     int tiles_y, int b0,
-                                                     int32_t *__restrict__ ranges) {
-  __shared__ int wsum[16];
-  __shared__ int carry;
-  __shared__ uint32_t lo_hist[256];
-  const int ntiles = tiles_x * tiles_y;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const bool overflow = ctl->overflow != 0;
-  // per-tile counts: every row of the difference array sums to zero (each span
-  // adds +1 and -1 in its own row), so the inclusive prefix of the whole array,
-  // taken row-major, is the count of each tile
-  const int stride = tiles_x + 1, ndiff = tiles_y * stride;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int c0 = 0; c0 < ndiff; c0 += 1024) {
-    const int i = c0 + threadIdx.x;
-    const int x = i < ndiff ? tile_diff[i] : 0;
-    int v = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(v, d, 64);
-      if (lane >= d) v += o;
-    }
-    if (lane == 63) wsum[wid] = v;
-    __syncthreads();
-    int base = carry, tot = 0;
-    for (int q = 0; q < 16; q++) {
-      base += (q < wid) ? wsum[q] : 0;
-      tot += wsum[q];
-    }
-    if (i < ndiff) {
-      const int ty = i / stride, tx = i - ty * stride;
-      if (tx < tiles_x) tile_counts[ty * tiles_x + tx] = base + v;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) carry = 0;
-  if (threadIdx.x < 256) lo_hist[threadIdx.x] = 0;
-  __syncthreads();
-  const uint32_t mask0 = (1u << b0) - 1u;
-  for (int c0 = 0; c0 < ntiles; c0 += 1024) {
-    const int t = c0 + threadIdx.x;
-    const int x = (t < ntiles && !overflow) ? tile_counts[t] : 0;
-    if (x) atomicAdd(&lo_hist[t & mask0], (uint32_t)x);
-    int v = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(v, d, 64);
-      if (lane >= d) v += o;
-    }
-    if (lane == 63) wsum[wid] = v;
-    __syncthreads();
-    int base = carry, tot = 0;
-    for (int q = 0; q < 16; q++) {
-      base += (q < wid) ? wsum[q] : 0;
-      tot += wsum[q];
-    }
-    if (t < ntiles) {
-      ranges[2 * t] = base + v - x;
-      ranges[2 * t + 1] = base + v;
-      if ((t & mask0) == 0) ctl->tbase[1][t >> b0] = (uint32_t)(base + v - x);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
-    __syncthreads();
-  }
-  // low-digit offsets: every thread takes part in the scan
-  const int v = threadIdx.x <= (int)mask0 ? (int)lo_hist[threadIdx.x] : 0;
-  int tot;
-  const int incl = block_scan<1024>(v, tot);
-  if (threadIdx.x <= (int)mask0) ctl->tbase[0][threadIdx.x] = (uint32_t)(incl - v);
-}
-
 __global__ void __launch_bounds__(256) k_sorted_keys(const SortCtl *__restrict__ ctl, int cap,
                                                      const uint32_t *__restrict__ tiles,
                                                      const uint32_t *__restrict__ ids,
@@ -678,12 +690,21 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
 
   hipLaunchKernelGGL(k_depth_bases, dim3(1), dim3(256), 0, st, ctl, offsets, n, cap);
   // depth sort of the visible splats: 4 passes of 8 bits; the last also writes
-  // each splat's pair count in depth order
+  // each splat's pair count in depth order. The first pass has one extra
+  // workgroup that turns the binning pass's difference array into tile counts,
+  // tile ranges and the tile-digit offsets.
   const int npd = (int)(parts_of(n, DS_PART) > 1 ? parts_of(n, DS_PART) : 1);
+  const int b0 = 8;
   {
     PassIn a = in;
     a.dkey = w.dkey;
-    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_DEPTH0>), dim3(npd),
+    a.tile_diff = w.tile_diff;
+    a.tile_counts = w.tile_counts;
+    a.ranges = ranges;
+    a.tiles_x = cam.tiles_x;
+    a.tiles_y = cam.tiles_y;
+    a.b0 = b0;
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_DEPTH0>), dim3(npd + 1),
                        dim3(DS_THREADS), 0, st, nullptr, nullptr, w.dk[1], w.dv[1], nullptr, n, 0,
                        dbase(0), w.status, ticket(0), err, a);
   }
@@ -706,12 +727,8 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   hipLaunchKernelGGL(k_dscan_reduce, dim3(nb), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum);
   hipLaunchKernelGGL(k_dscan_apply, dim3(nb + 1), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum,
                      w.doff, w.part_first);
-  // tile ranges and the tile digit offsets (counts from the binning pass)
   int tbits = 1;
   while ((1 << tbits) < ntiles) tbits++;
-  const int b0 = 8;
-  hipLaunchKernelGGL(k_tile_bases, dim3(1), dim3(1024), 0, st, ctl, w.tile_diff, w.tile_counts,
-                     cam.tiles_x, cam.tiles_y, b0, ranges);
   // tile passes: the first generates its partition's pairs itself
   const int npt = (int)(parts_of(cap, TS_PART) > 1 ? parts_of(cap, TS_PART) : 1);
   uint32_t *status_t0 = w.status + 4 * w.pd, *status_t1 = status_t0 + w.pt;
