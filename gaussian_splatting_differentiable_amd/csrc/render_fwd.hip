@@ -105,6 +105,7 @@ struct Blend {
 // colour and T unchanged bit for bit. A lane is alive exactly while its T is at
 // least 1e-4 (lanes outside the image start at T = 0), so the hit mask is the
 // AND of two compare ballots and needs no per-lane flag.
+template <bool STATS>
 __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int cs, int ce,
                                              const SubTile &st, const Px &x, float T0,
@@ -132,10 +133,12 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
       const bool alive = r.T >= T_STOP, inq = q <= s.p2.y;
       const uint64_t hm = wave_ballot(alive) & wave_ballot(inq);
       const bool hit = alive && inq;
-      nsteps++;
+      if constexpr (STATS) nsteps++;
       if (!hm) return true;  // no lane hits: nothing changes
-      nhits += __popcll(hm);
-      nhsteps++;
+      if constexpr (STATS) {
+        nhits += __popcll(hm);
+        nhsteps++;
+      }
       r.wlast = pos + 1;
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
       const float al = hit ? fminf(0.99f, ex) : 0.0f;
@@ -155,6 +158,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
 
 // Pass A: transmittance product over the chunk; gives up when sat < chunk.
 // Lanes outside the image start at P = 0 (dead), as in blend_range.
+template <bool STATS>
 __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
                                                const int32_t *__restrict__ sids, int cs, int ce,
                                                const SubTile &st, const Px &x, Splat *sbuf,
@@ -184,7 +188,7 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
       const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
       const bool alive = P >= T_STOP, inq = q <= s.p2.y;
       const bool hit = alive && inq;
-      nsteps++;
+      if constexpr (STATS) nsteps++;
       if (!(wave_ballot(alive) & wave_ballot(inq))) return true;
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
       const float al = hit ? fminf(0.99f, ex) : 0.0f;
@@ -211,6 +215,9 @@ __device__ __forceinline__ int ld_i(const int32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// STATS: count hits, tested entries and sub-tile hits (only when the caller asks
+// for them: the counters cost a few scalar instructions per entry).
+template <bool STATS>
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
 __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
@@ -242,8 +249,8 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
         if (lane == 0) fs.sub_last[tile * 4 + quad] = 0;
         continue;
       }
-      const Blend r = blend_range(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits, nsteps,
-                                    nhsteps);
+      const Blend r = blend_range<STATS>(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits,
+                                           nsteps, nhsteps);
       if (x.inside) {
         rgb[x.p] = r.C0;
         rgb[P + x.p] = r.C1;
@@ -262,7 +269,8 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       float Pp = 0.0f;
       if (!st.empty) {
         bool gave_up = false;
-        Pp = product_range(splats, sorted_ids, cs, ce, st, x, sbuf, sat, p, gave_up, nsteps);
+        Pp = product_range<STATS>(splats, sorted_ids, cs, ce, st, x, sbuf, sat, p, gave_up,
+                                  nsteps);
         if (gave_up) Pp = 0.0f;  // an earlier chunk already took every pixel below 1e-4
         // every pixel of the quarter below the threshold: later chunks may give up
         if (!gave_up && wave_ballot(x.inside && Pp >= T_STOP) == 0 && lane == 0) atomicMin(sat, p);
@@ -304,7 +312,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     r.wlast = 0;
     const bool skip = st.empty || ld_i(sat) < p;
     if (!skip) {
-      r = blend_range(splats, sorted_ids, cs, ce, st, x, Tin, sbuf, nhits, nsteps, nhsteps);
+      r = blend_range<STATS>(splats, sorted_ids, cs, ce, st, x, Tin, sbuf, nhits, nsteps, nhsteps);
       if (!(x.inside && Tin >= T_STOP)) r.consumed = -1;  // stopped before this chunk
     }
     const int64_t cp = (int64_t)ci * 64 + lane;
@@ -346,7 +354,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       last[x.p] = lastv;
     }
   }
-  if (stats && lane == 0) {
+  if (STATS && lane == 0) {
     atomicAdd(&stats[0], (unsigned long long)nhits);
     atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
     atomicAdd(&stats[2], (unsigned long long)nhsteps);
@@ -373,7 +381,8 @@ hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
   // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
   // queues empty exit at once
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_render_fwd, dim3(nblocks), dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
+  hipLaunchKernelGGL(stats ? k_render_fwd<true> : k_render_fwd<false>, dim3(nblocks),
+                     dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,
