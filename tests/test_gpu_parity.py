@@ -370,10 +370,57 @@ def test_device_policy_equals_host_policy(case, W, H):
                                f32(gsr.DEFAULT_BETA), f32(gsr.DEFAULT_EPS), gsr.HK_MAX)
     assert (plan["h"], plan["k"] if plan["h"] else 1) == (h, k), (plan["h"], plan["k"], h, k)
     assert plan["nA"] == 4 * h * (k if h else 0)
-    check_queues(plan, (W + 15) // 16)
     assert plan["qoff"][0] == 0 and np.all(np.diff(plan["qoff"]) >= 0)
     check_queues(plan, (W + 15) // 16)
     if case == "one_outlier":
         assert h >= 1
     if case == "flat":
         assert h == 0
+
+
+def test_forward_without_stats_is_identical():
+    """The production forward (no statistics buffer) is a separate instantiation
+    of the kernel: it must give the same images, bit for bit, as the counting
+    one that the parity tests above check against the oracle, on a chunked and
+    an unchunked plan."""
+    gsr = _gsr()
+    sc, ref = reference(1)
+    n, npairs = sc.n, len(ref["sorted_ids"])
+    for sched in (None, gsr.make_sched(chunk_mode=2, force_k=4, force_h=6)):
+        r = gsr.Rasterizer(sc.camera, capacity=max(npairs, 1), sched=sched)
+        r._ensure(n, max(npairs, 1))
+        r.splats[:n].copy_(dev(ref["splats"]))
+        r.sorted_ids[:npairs].copy_(dev(ref["sorted_ids"]))
+        r.ranges.copy_(dev(ref["ranges"]))
+        r.render_fwd(n, stats=True)
+        a = [host(t).copy() for t in (r.rgb, r.T, r.last)]
+        r.render_fwd(n, stats=False)
+        b = [host(t) for t in (r.rgb, r.T, r.last)]
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+        check_forward(ref, dict(rgb=b[0], T=b[1], last=b[2], stats=host(r.stats)))
+
+
+def test_kernel_timing_entry_points():
+    """gs_timing_start / gs_timing_read record one duration per raster kernel
+    launch, in launch order, and stop recording when read."""
+    gsr = _gsr()
+    sc, ref = reference(1)
+    n, npairs = sc.n, len(ref["sorted_ids"])
+    r = gsr.Rasterizer(sc.camera, capacity=max(npairs, 1))
+    r._ensure(n, max(npairs, 1))
+    r.splats[:n].copy_(dev(ref["splats"]))
+    r.sorted_ids[:npairs].copy_(dev(ref["sorted_ids"]))
+    r.ranges.copy_(dev(ref["ranges"]))
+    dL = dev(sc.dL_drgb)
+    gsr.gs_timing_start()
+    for _ in range(3):
+        r.render_fwd(n)
+        r.render_bwd(n, dL)
+    fwd, bwd = gsr.gs_timing_read(0), gsr.gs_timing_read(1)
+    assert len(fwd) == 3 and len(bwd) == 3
+    assert all(0.0 < t < 1000.0 for t in fwd + bwd)
+    r.render_fwd(n)  # not recorded any more
+    assert len(gsr.gs_timing_read(0)) == 3
+    with pytest.raises(gsr.GsError):
+        gsr.gs_timing_read(2)
