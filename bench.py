@@ -38,8 +38,20 @@ BWD_FLOPS_PER_HIT = 54
 PAIR_BYTES = 52
 PIXEL_BYTES = 20
 ATOMIC_BYTES = 36
+# Binning and sort move 48 B per Gaussian read + 4 B per Gaussian of offsets
+# (bin), then 12 B per pair written, 12 B read and 4 B of ids written + 8 B per
+# tile of ranges (sort). Projection reads 44 B per Gaussian (mean, log-scales,
+# quaternion, opacity), 192 B of SH per visible Gaussian at degree 3, and writes
+# its 48-byte record.
+BIN_BYTES_PER_GAUSSIAN = 52
+SORT_BYTES_PER_PAIR = 28
+SORT_BYTES_PER_TILE = 8
+PROJ_BYTES_PER_GAUSSIAN = 44 + 48
 PEAK_FP32_TFLOPS = 157.3     # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0        # MI355X published HBM3E bandwidth
+# exp and reciprocal issue at a quarter of the fp32 lane rate:
+# 256 CUs x 64 lanes / 4 x 2.4 GHz
+PEAK_TRANS_GPS = 256 * 64 / 4 * 2.4
 
 CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_amd", "csrc")
 KERNEL_SOURCES = {
@@ -216,7 +228,9 @@ def main():
         gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats)
         pe[2 * k + 1].record(stream)
     torch.cuda.synchronize()
-    ms_project = float(np.median([pe[2 * k].elapsed_time(pe[2 * k + 1]) for k in range(args.steps)]))
+    per["project"] = [pe[2 * k].elapsed_time(pe[2 * k + 1]) for k in range(args.steps)]
+    ms_project = float(np.median(per["project"]))
+    n_vis = int((r.splats[:, 9] > 0).sum().item())
 
     # roofline of the longest raster kernel: algorithmic bytes and flops per launch
     P = cam.width * cam.height
@@ -248,6 +262,33 @@ def main():
     ms_raster = ms["fwd"] + ms["bwd"]
     raster_frac = (t_roof["fwd"] + t_roof["bwd"]) / (ms_raster * 1e-3)
 
+    # every stage against the three ceilings: t_roof = max(F/P_F, X/P_X, B/P_B)
+    sh_bytes = 4 * 3 * (sc.sh_degree + 1) ** 2
+    stage_work = {
+        "project": dict(flops=0, trans=0,
+                        bytes=PROJ_BYTES_PER_GAUSSIAN * n + sh_bytes * n_vis),
+        "bin": dict(flops=0, trans=0, bytes=BIN_BYTES_PER_GAUSSIAN * n),
+        "sort": dict(flops=0, trans=0,
+                     bytes=SORT_BYTES_PER_PAIR * npairs + SORT_BYTES_PER_TILE * cam.num_tiles),
+        "fwd": dict(work["fwd"], trans=hits),
+        "bwd": dict(work["bwd"], trans=2 * hits),
+    }
+    stage_lines = {}
+    for s_name, sw in stage_work.items():
+        parts = {"fp32": sw["flops"] / (PEAK_FP32_TFLOPS * 1e12),
+                 "trans": sw["trans"] / (PEAK_TRANS_GPS * 1e9),
+                 "hbm": sw["bytes"] / (PEAK_HBM_GBS * 1e9)}
+        bound = max(parts, key=parts.get)
+        v = per[s_name]
+        stage_lines[s_name] = {
+            "ms": round(float(np.median(v)), 4), "ms_p10": round(float(np.percentile(v, 10)), 4),
+            "ms_p90": round(float(np.percentile(v, 90)), 4), "ms_min": round(float(np.min(v)), 4),
+            "pairs_per_s": round(npairs / (float(np.median(v)) * 1e-3), 1),
+            "bytes": sw["bytes"], "flops": sw["flops"], "transcendentals": sw["trans"],
+            "bound": bound, "t_roof_ms": round(parts[bound] * 1e3, 4),
+            "roofline_frac": round(parts[bound] / (float(np.median(v)) * 1e-3), 4)}
+    ms_fwd_total = ms["bin"] + ms["sort"] + ms["fwd"]
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(sc, npairs)
 
     line = {
@@ -270,6 +311,11 @@ def main():
         "ms_kernels": {f"k_render_{k}": round(v, 4) for k, v in kernel_ms.items()},
         "raster_pairs_per_s": round(npairs / (ms_raster * 1e-3), 1),
         "raster_roofline_frac": round(raster_frac, 4),
+        "ms_fwd": round(ms_fwd_total, 4), "ms_bwd": round(ms["bwd"], 4),
+        "ms_fwd_bwd": round(ms_fwd_total + ms["bwd"], 4),
+        "ms_frame": round(ms_project + ms_fwd_total + ms["bwd"], 4),
+        "n_visible": n_vis,
+        "stages": stage_lines,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

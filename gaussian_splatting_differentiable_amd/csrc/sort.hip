@@ -21,7 +21,8 @@
 //     for every 16384-pair partition the splat its first pair belongs to;
 //   - the first tile pass (low 8 bits of the tile id) with the emission fused
 //     in: a partition generates its own pairs into LDS from the splats that
-//     cover it, so the depth-ordered pair list is never written to memory;
+//     cover it, one record per tile row, so the depth-ordered pair list is
+//     never written to memory;
 //   - the second tile pass (the high bits), writing the sorted ids.
 //
 // A onesweep pass: a workgroup takes a partition by atomic ticket, ranks its
@@ -359,6 +360,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __shared__ int s_lbase[B];
   __shared__ uint32_t s_gbase[B];
   __shared__ int s_part, s_nvalid;
+  __shared__ uint32_t s_mark[SRC == SRC_EMIT ? PART / 32 : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if constexpr (SRC == SRC_DEPTH0) {
     static_assert(SRC != SRC_DEPTH0 || NT == 1024, "the tile-bases workgroup has 1024 threads");
@@ -386,9 +388,15 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     if (p0 >= n) return;  // past the last key: no later partition waits on it
   }
   if constexpr (SRC == SRC_EMIT) {
-    // generate this partition's pairs into LDS, in depth order; each thread
-    // takes GEN splats at a time with all their loads in flight together
+    // generate this partition's pairs, in depth order: every tile row of a
+    // splat that reaches into the partition leaves one record at the position
+    // of its first pair here (s_key: that pair's tile, s_val: the splat) and
+    // sets that position's bit in s_mark; a pair's key is then its row's first
+    // tile plus its distance from the row start. Each thread takes GEN splats
+    // at a time with all their loads in flight together.
     constexpr int GEN = 4;
+    for (int i = tid; i < PART / 32; i += NT) s_mark[i] = 0u;
+    __syncthreads();
     const int nv = (int)min((int64_t)PART, n - p0);
     const int m = in.ctl->m;
     const int nparts = (int)parts_of(n, PART);
@@ -417,16 +425,14 @@ __global__ void __launch_bounds__(NT) k_onesweep(
           int a, b;
           row_span(rs, ty, in.W, in.H, in.tiles_x, a, b);
           if (b <= a) continue;
-          if (q + (b - a) <= p0) {
-            q += b - a;
-            continue;
+          if (q + (b - a) > p0) {
+            const int64_t q0 = q > p0 ? q : p0;
+            const int sl = (int)(q0 - p0);
+            s_key[sl] = (uint32_t)(ty * in.tiles_x + a + (int)(q0 - q));
+            s_val[sl] = (uint32_t)g;
+            atomicOr(&s_mark[sl >> 5], 1u << (sl & 31));
           }
-          for (int tx = a; tx < b; tx++, q++) {
-            if (q >= p0 && q < p0 + nv) {
-              s_key[q - p0] = (uint32_t)(ty * in.tiles_x + tx);
-              s_val[q - p0] = (uint32_t)g;
-            }
-          }
+          q += b - a;
         }
       }
     }
@@ -448,8 +454,15 @@ __global__ void __launch_bounds__(NT) k_onesweep(
         k = in.dkey[e];
         v = (uint32_t)e;
       } else if constexpr (SRC == SRC_EMIT) {
-        k = s_key[e - p0];
-        v = s_val[e - p0];
+        // the nearest row start at or before this pair (position 0 always
+        // starts one: the partition's first pair opens a row record)
+        const int x = (int)(e - p0);
+        int wi = x >> 5;
+        uint32_t bits = s_mark[wi] & (0xFFFFFFFFu >> (31 - (x & 31)));
+        while (bits == 0u && wi > 0) bits = s_mark[--wi];
+        const int st = bits ? wi * 32 + 31 - (int)__clz(bits) : 0;
+        k = s_key[st] + (uint32_t)(x - st);
+        v = s_val[st];
       } else {
         k = kin[e];
         v = vin[e];
