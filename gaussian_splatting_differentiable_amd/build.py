@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgs.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "project.hip", "bin.hip", "scan.hip", "sort.hip", "sched.hip",
+SOURCES = ["api.hip", "project.hip", "bin.hip", "sort.hip", "sched.hip",
            "render_fwd.hip", "render_bwd.hip"]
 # translation units whose decisions must be reproducible bit for bit
 NO_CONTRACT = {"bin.hip", "sort.hip", "sched.hip"}

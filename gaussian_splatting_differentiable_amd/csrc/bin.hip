@@ -12,11 +12,11 @@
 // -ffp-contract=off: every operation below rounds on its own and fmaf appears
 // only where written, so the emitted pairs are reproducible bit for bit.
 //
-// Kernels: the counting pass (sort.hip: per-splat pair counts into offsets[],
-// plus what the sort needs from the same pass over the records), a device-wide
-// exclusive scan (scan.hip), then k_bin_emit (status; keys/ids at the offsets
-// in splat-id order when the caller asks for them). The sort stage re-emits the
-// pairs directly in depth order, so the frame does not need the id-order list.
+// Kernels: the counting pass and the prefix sum of the counts (sort.hip: the
+// offsets and the status, plus what the sort needs from the same pass over the
+// records), then, only when the caller asks for them, k_bin_emit (keys/ids at
+// the offsets in splat-id order). The sort stage re-emits the pairs directly
+// in depth order, so the frame does not need the id-order list.
 #include "bin_spans.h"
 
 namespace {
@@ -25,16 +25,10 @@ __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict
                                                   int H, int tiles_x, int tiles_y,
                                                   const int32_t *__restrict__ offsets,
                                                   int64_t capacity, uint64_t *__restrict__ keys,
-                                                  int32_t *__restrict__ ids,
-                                                  int32_t *__restrict__ status) {
+                                                  int32_t *__restrict__ ids) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = offsets[n];
-  if (total > capacity) {
-    if (i == 0) *status = GS_ERR_CAPACITY;
-    return;
-  }
-  if (i == 0) *status = GS_OK;
-  if (!keys || i >= n) return;
+  if (total > capacity || i >= n) return;
   const Splat s = splats[i];
   const RowSpans r = spans_setup(s, tiles_y);
   if (!r.ok) return;
@@ -53,25 +47,17 @@ __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict
 
 }  // namespace
 
-hipError_t gs_launch_scan_i32(const int32_t *in, int32_t *out, int n, int32_t *block_buf,
-                              hipStream_t st);
 hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int64_t cap,
-                               int32_t *counts, void *ws, int32_t **scan_buf, hipStream_t st);
+                               int32_t *offsets, int32_t *status, void *ws, hipStream_t st);
 
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
                          int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
                          hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   dim3 block(256), grid(gs_div_up(n > 0 ? n : 1, 256));
-  int32_t *scan_buf = nullptr;
-  hipError_t e = gs_launch_bin_count(n, splats, cam, capacity, offsets, ws, &scan_buf, st);
-  if (e != hipSuccess) return e;
-  // exclusive scan of the n counts, total in offsets[n]
-  e = gs_launch_scan_i32(offsets, offsets, n, scan_buf, st);
-  if (e != hipSuccess) return e;
-  // without keys/ids to write, one workgroup sets the status
-  hipLaunchKernelGGL(k_bin_emit, keys ? grid : dim3(1), block, 0, st, n, sp, cam.width, cam.height,
-                     cam.tiles_x,
-                     cam.tiles_y, offsets, capacity, keys, ids, status);
+  hipError_t e = gs_launch_bin_count(n, splats, cam, capacity, offsets, status, ws, st);
+  if (e != hipSuccess || !keys) return e;
+  hipLaunchKernelGGL(k_bin_emit, grid, block, 0, st, n, sp, cam.width, cam.height, cam.tiles_x,
+                     cam.tiles_y, offsets, capacity, keys, ids);
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@ constexpr int SPIN_LIMIT = 1 << 22;
 constexpr int HIST_TILES_LDS = 16384;  // tile histogram kept in LDS up to this many tiles
 constexpr int SCAN_T = 256, SCAN_I = 8, SCAN_TILE = SCAN_T * SCAN_I;
 constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pairs (a NaN pattern)
-constexpr int BIN_T = 256, BIN_BLOCKS_MAX = 512;
+constexpr int BIN_T = 256, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
 
 // partitions: depth passes and tile passes
 constexpr int DS_THREADS = 1024, DS_ITEMS = 8, DS_PART = DS_THREADS * DS_ITEMS;
@@ -72,19 +72,19 @@ __device__ __forceinline__ void st_status(uint32_t *p, uint32_t v) {
 }
 
 // Inclusive scan over a block of NT threads; total of the block in `total`.
-template <int NT>
-__device__ __forceinline__ int block_scan(int v, int &total) {
+template <int NT, typename T = int>
+__device__ __forceinline__ T block_scan(T v, T &total) {
   constexpr int NWV = NT / 64;
-  __shared__ int wsum[NWV];
+  __shared__ T wsum[NWV];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
+    const T t = __shfl_up(v, d, 64);
     if (lane >= d) v += t;
   }
   if (lane == 63) wsum[wid] = v;
   __syncthreads();
-  int base = 0, tot = 0;
+  T base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NWV; w++) {
     base += (w < wid) ? wsum[w] : 0;
@@ -99,6 +99,14 @@ __device__ __forceinline__ int block_scan(int v, int &total) {
 
 __host__ __device__ inline int64_t parts_of(int64_t n, int part) { return (n + part - 1) / part; }
 
+// Splats per counting block: a multiple of the block size, at most
+// BIN_BLOCKS_MAX blocks.
+__host__ __device__ inline int bin_chunk(int n) {
+  const int per = (int)parts_of(n > 0 ? n : 1, BIN_BLOCKS_MAX);
+  return (int)parts_of(per, BIN_T) * BIN_T;
+}
+__host__ __device__ inline int bin_blocks(int n) { return (int)parts_of(n > 0 ? n : 1, bin_chunk(n)); }
+
 struct SortWs {
   SortCtl *ctl;
   int32_t *tile_counts;     // T
@@ -111,13 +119,13 @@ struct SortWs {
   int32_t *bsum;            // block sums of the depth-order scan
   uint32_t *tk[2], *tv[2];  // capacity each: tile passes
   uint32_t *status;         // look-back words: 4 depth passes, then 2 tile passes
-  int32_t *scan_buf;        // the binning scan's block buffer
+  int32_t *bin_sum;         // pair count of every counting block's chunk
   int64_t pd, pt;           // status words per depth pass / per tile pass
   int64_t nstatus;
   size_t bytes;
 };
 
-SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y, int scan_elems) {
+SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y) {
   const int ntiles = tiles_x * tiles_y;
   size_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -143,7 +151,7 @@ SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y, int scan_
   w.pt = (parts_of(cap, TS_PART) + 1) * 256;
   w.nstatus = 4 * w.pd + 2 * w.pt;
   w.status = (uint32_t *)take(4 * w.nstatus);
-  w.scan_buf = (int32_t *)take(4 * (int64_t)scan_elems);
+  w.bin_sum = (int32_t *)take(4 * ((int64_t)bin_blocks(n) + 1));
   w.bytes = off;
   return w;
 }
@@ -158,14 +166,16 @@ __global__ void __launch_bounds__(1024) k_bin_init(SortCtl *__restrict__ ctl,
   for (int i = threadIdx.x; i < ndiff; i += blockDim.x) tile_diff[i] = 0;
 }
 
-// Per-splat pair counts (exact spans), plus the depth keys, the depth-digit
-// histograms and the per-row difference array of the tile counts (+1 where a
-// row span starts, -1 where it ends: two updates per row, however long the
-// span) for the sort; clears the sort's look-back words.
+// Per-splat pair counts (exact spans) and every block's chunk sum, plus the
+// depth keys, the depth-digit histograms and the per-row difference array of
+// the tile counts (+1 where a row span starts, -1 where it ends: two updates
+// per row, however long the span) for the sort; clears the sort's look-back
+// words. Block b counts the splats [b chunk, (b + 1) chunk).
 __global__ void __launch_bounds__(BIN_T) k_bin_count(
     int n, const Splat *__restrict__ splats, int W, int H, int tiles_x, int tiles_y,
-    int32_t *__restrict__ counts, uint32_t *__restrict__ dkey, SortCtl *__restrict__ ctl,
-    int32_t *__restrict__ tile_diff, uint32_t *__restrict__ status, int64_t nstatus) {
+    int32_t *__restrict__ counts, int chunk, int32_t *__restrict__ bin_sum,
+    uint32_t *__restrict__ dkey, SortCtl *__restrict__ ctl, int32_t *__restrict__ tile_diff,
+    uint32_t *__restrict__ status, int64_t nstatus) {
   __shared__ uint32_t dh[4][256];
   extern __shared__ int th[];  // the difference array, when it fits (sized at launch)
   const int stride = tiles_x + 1;
@@ -178,7 +188,10 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
        i += (int64_t)gridDim.x * BIN_T)
     status[i] = 0;
   __syncthreads();
-  for (int i = blockIdx.x * BIN_T + threadIdx.x; i < n; i += gridDim.x * BIN_T) {
+  const int i0 = blockIdx.x * chunk;
+  const int i1 = (int)min((int64_t)n, (int64_t)i0 + chunk);
+  int csum = 0;
+  for (int i = i0 + threadIdx.x; i < i1; i += BIN_T) {
     const Splat s = splats[i];
     const RowSpans r = spans_setup(s, tiles_y);
     int cnt = 0;
@@ -195,6 +208,7 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
       }
     }
     counts[i] = cnt;
+    csum += cnt;
     uint32_t k = NO_DEPTH;
     if (cnt > 0) {
       k = __float_as_uint(s.p2.z);
@@ -214,7 +228,9 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
       todo &= ~same;
     }
   }
-  __syncthreads();
+  int ctot;
+  block_scan<BIN_T>(csum, ctot);  // ends with a barrier: the LDS histograms are complete
+  if (threadIdx.x == 0) bin_sum[blockIdx.x] = ctot;
   for (int i = threadIdx.x; i < 1024; i += BIN_T) {
     const uint32_t v = (&dh[0][0])[i];
     if (v) atomicAdd(&ctl->dhist[0][0] + i, v);
@@ -224,27 +240,49 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
       if (th[i]) atomicAdd(&tile_diff[i], th[i]);
 }
 
-// ---------------------------------------------------------------- sort setup
-
-// Depth digit offsets and the number of visible splats; an overflowing frame
-// sorts nothing.
-__global__ void __launch_bounds__(256) k_depth_bases(SortCtl *__restrict__ ctl,
-                                                     const int32_t *__restrict__ offsets, int n,
-                                                     int64_t cap) {
-  const bool overflow = (int64_t)offsets[n] > cap;
-  if (threadIdx.x < 8) ctl->tickets[threadIdx.x] = 0;
-  if (threadIdx.x == 0) ctl->err = 0;
-  for (int p = 0; p < 4; p++) {
-    int tot;
-    const int v = overflow ? 0 : (int)ctl->dhist[p][threadIdx.x];
-    const int incl = block_scan<256>(v, tot);
-    ctl->dbase[p][threadIdx.x] = (uint32_t)(incl - v);
-    if (p == 0 && threadIdx.x == 0) {
-      ctl->m = tot;
-      ctl->overflow = overflow ? 1 : 0;
+// Exclusive prefix of the counts in place (offsets[0, n)), offsets[n] = I and
+// the status: block b scans its own chunk, starting from the sum of the chunk
+// sums before it.
+__global__ void __launch_bounds__(BIN_T) k_bin_offsets(int n, int chunk,
+                                                       const int32_t *__restrict__ bin_sum,
+                                                       int32_t *__restrict__ offsets,
+                                                       int64_t capacity,
+                                                       int32_t *__restrict__ status) {
+  int64_t pre = 0;
+  for (int b = threadIdx.x; b < (int)blockIdx.x; b += BIN_T) pre += bin_sum[b];
+  int64_t base;
+  block_scan<BIN_T, int64_t>(pre, base);
+  const int i0 = blockIdx.x * chunk;
+  const int i1 = (int)min((int64_t)n, (int64_t)i0 + chunk);
+  int64_t carry = base;
+  for (int t0 = i0; t0 < i1; t0 += BIN_TILE) {
+    constexpr int IT = BIN_TILE / BIN_T;
+    int x[IT];
+    int v = 0;
+#pragma unroll
+    for (int j = 0; j < IT; j++) {
+      const int idx = t0 + threadIdx.x * IT + j;
+      x[j] = idx < i1 ? offsets[idx] : 0;
+      v += x[j];
     }
+    int tot;
+    const int incl = block_scan<BIN_T>(v, tot);
+    int run = (int)carry + incl - v;
+#pragma unroll
+    for (int j = 0; j < IT; j++) {
+      const int idx = t0 + threadIdx.x * IT + j;
+      if (idx < i1) offsets[idx] = run;
+      run += x[j];
+    }
+    carry += tot;
+  }
+  if ((int)blockIdx.x == (int)gridDim.x - 1 && threadIdx.x == 0) {
+    offsets[n] = (int32_t)min(carry, (int64_t)INT32_MAX);
+    *status = carry > capacity ? GS_ERR_CAPACITY : GS_OK;
   }
 }
+
+// ---------------------------------------------------------------- sort setup
 
 // ---------------------------------------------------------------- onesweep pass
 
@@ -253,13 +291,24 @@ __global__ void __launch_bounds__(256) k_depth_bases(SortCtl *__restrict__ ctl,
 // not depend on it).
 __device__ void tile_bases_block(SortCtl *__restrict__ ctl, const int32_t *__restrict__ tile_diff,
                                  int32_t *__restrict__ tile_counts, int tiles_x, int tiles_y,
-                                 int b0, int32_t *__restrict__ ranges) {
+                                 int b0, int32_t *__restrict__ ranges, bool overflow) {
   __shared__ int wsum[16];
   __shared__ int carry;
   __shared__ uint32_t lo_hist[256];
   const int ntiles = tiles_x * tiles_y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const bool overflow = ctl->overflow != 0;
+  // the frame's sort state for the later passes: visible splats, the overflow
+  // flag and the depth digit offsets (an overflowing frame sorts nothing)
+  for (int p = 0; p < 4; p++) {
+    const int v = (threadIdx.x < 256 && !overflow) ? (int)ctl->dhist[p][threadIdx.x] : 0;
+    int tot;
+    const int incl = block_scan<1024>(v, tot);
+    if (threadIdx.x < 256) ctl->dbase[p][threadIdx.x] = (uint32_t)(incl - v);
+    if (p == 0 && threadIdx.x == 0) {
+      ctl->m = tot;
+      ctl->overflow = overflow ? 1 : 0;
+    }
+  }
   // per-tile counts: every row of the difference array sums to zero (each span
   // adds +1 and -1 in its own row), so the inclusive prefix of the whole array,
   // taken row-major, is the count of each tile
@@ -332,8 +381,9 @@ enum Src { SRC_KEYS = 0, SRC_DEPTH0 = 1, SRC_EMIT = 2 };
 // Inputs of one pass beyond the (key, value) arrays.
 struct PassIn {
   const SortCtl *ctl;
+  int64_t cap;                 // SRC_DEPTH0: the pair capacity (offsets[n_max] above it: overflow)
   const uint32_t *dkey;        // SRC_DEPTH0
-  const int32_t *offsets;      // last depth pass: pair counts
+  const int32_t *offsets;      // SRC_DEPTH0 (the pair total) and the last depth pass (counts)
   int32_t *cout;               // last depth pass: pair counts in depth order (or null)
   const uint32_t *dval;        // SRC_EMIT: splat ids in depth order
   const int32_t *doff;         // SRC_EMIT: pair offsets in depth order
@@ -362,13 +412,22 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __shared__ int s_part, s_nvalid;
   __shared__ uint32_t s_mark[SRC == SRC_EMIT ? PART / 32 : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the first depth pass takes its digit offsets and the number of visible
+  // splats from the binning pass's histogram itself
+  uint32_t dbase0 = 0;
+  int m0 = 0;
+  bool overflow = false;
   if constexpr (SRC == SRC_DEPTH0) {
     static_assert(SRC != SRC_DEPTH0 || NT == 1024, "the tile-bases workgroup has 1024 threads");
+    overflow = (int64_t)in.offsets[n_max] > in.cap;
     if (in.ranges && blockIdx.x == gridDim.x - 1) {
       tile_bases_block(const_cast<SortCtl *>(in.ctl), in.tile_diff, in.tile_counts, in.tiles_x,
-                       in.tiles_y, in.b0, in.ranges);
+                       in.tiles_y, in.b0, in.ranges, overflow);
       return;
     }
+    const int v = (tid < B && !overflow) ? (int)in.ctl->dhist[0][tid] : 0;
+    const int incl = block_scan<NT>(v, m0);
+    dbase0 = (uint32_t)(incl - v);
   }
   {
     // blocks beyond the frame's partitions take no ticket (the launch is sized
@@ -442,8 +501,6 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t key[ITEMS], val[ITEMS];
   int rnk[ITEMS];
-  bool overflow = false;
-  if constexpr (SRC == SRC_DEPTH0) overflow = in.ctl->overflow != 0;
   // all of this thread's keys are loaded before any is ranked
 #pragma unroll
   for (int r = 0; r < ITEMS; r++) {
@@ -548,7 +605,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
       }
       st_status(&status[me], ST_INC | (excl + (uint32_t)total));
     }
-    s_gbase[tid] = digit_base[tid] + excl;
+    s_gbase[tid] = (SRC == SRC_DEPTH0 ? dbase0 : digit_base[tid]) + excl;
   }
   if (tid == 0) s_nvalid = ntot;
   __syncthreads();
@@ -564,7 +621,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   }
   __syncthreads();
   const int nv = s_nvalid;
-  const int bound = SRC == SRC_DEPTH0 ? in.ctl->m : n;
+  const int bound = SRC == SRC_DEPTH0 ? m0 : n;
   for (int i = tid; i < nv; i += NT) {
     const uint32_t k = s_key[i];
     const uint32_t d = (k >> shift) & (B - 1);
@@ -659,26 +716,26 @@ __global__ void __launch_bounds__(256) k_sorted_keys(const SortCtl *__restrict__
 
 }  // namespace
 
-int gs_scan_buf_elems(int n_max);
-
 size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y) {
-  return carve(nullptr, n, cap, tiles_x, tiles_y, gs_scan_buf_elems(n)).bytes + 256;
+  return carve(nullptr, n, cap, tiles_x, tiles_y).bytes + 256;
 }
 
-// gs_bin_tiles' counting kernels; the per-splat counts go to counts[0, n).
+// gs_bin_tiles' counting kernels and the prefix sum: offsets[0, n] and the
+// status (GS_OK, or GS_ERR_CAPACITY when the pairs exceed cap).
 hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int64_t cap,
-                               int32_t *counts, void *ws, int32_t **scan_buf, hipStream_t st) {
-  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y,
-                   gs_scan_buf_elems(n));
-  *scan_buf = w.scan_buf;
+                               int32_t *offsets, int32_t *status, void *ws, hipStream_t st) {
+  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
   hipLaunchKernelGGL(k_bin_init, dim3(1), dim3(1024), 0, st, w.ctl, w.tile_diff,
                      cam.tiles_y * (cam.tiles_x + 1));
-  const int blocks = max(1, min(BIN_BLOCKS_MAX, gs_div_up(n > 0 ? n : 1, BIN_T)));
+  const int chunk = bin_chunk(n), blocks = bin_blocks(n);
   const int ndiff = cam.tiles_y * (cam.tiles_x + 1);
   const size_t lds = ndiff <= HIST_TILES_LDS ? 4 * (size_t)ndiff : 0;
   hipLaunchKernelGGL(k_bin_count, dim3(blocks), dim3(BIN_T), lds, st, n,
                      reinterpret_cast<const Splat *>(splats), cam.width, cam.height, cam.tiles_x,
-                     cam.tiles_y, counts, w.dkey, w.ctl, w.tile_diff, w.status, w.nstatus);
+                     cam.tiles_y, offsets, chunk, w.bin_sum, w.dkey, w.ctl, w.tile_diff, w.status,
+                     w.nstatus);
+  hipLaunchKernelGGL(k_bin_offsets, dim3(blocks), dim3(BIN_T), 0, st, n, chunk, w.bin_sum,
+                     offsets, cap, status);
   return hipGetLastError();
 }
 
@@ -687,8 +744,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
                           int32_t *ranges, void *ws, hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   const int ntiles = cam.tiles_x * cam.tiles_y;
-  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y,
-                   gs_scan_buf_elems(n));
+  SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
   SortCtl *ctl = w.ctl;
   char *cb = reinterpret_cast<char *>(ctl);
   auto dbase = [&](int p) { return reinterpret_cast<uint32_t *>(cb + offsetof(SortCtl, dbase)) + 256 * p; };
@@ -701,7 +757,6 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   PassIn in{};
   in.ctl = ctl;
 
-  hipLaunchKernelGGL(k_depth_bases, dim3(1), dim3(256), 0, st, ctl, offsets, n, cap);
   // depth sort of the visible splats: 4 passes of 8 bits; the last also writes
   // each splat's pair count in depth order. The first pass has one extra
   // workgroup that turns the binning pass's difference array into tile counts,
@@ -711,6 +766,8 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   {
     PassIn a = in;
     a.dkey = w.dkey;
+    a.offsets = offsets;
+    a.cap = cap;
     a.tile_diff = w.tile_diff;
     a.tile_counts = w.tile_counts;
     a.ranges = ranges;
@@ -719,7 +776,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
     a.b0 = b0;
     hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_DEPTH0>), dim3(npd + 1),
                        dim3(DS_THREADS), 0, st, nullptr, nullptr, w.dk[1], w.dv[1], nullptr, n, 0,
-                       dbase(0), w.status, ticket(0), err, a);
+                       nullptr, w.status, ticket(0), err, a);
   }
   int cur = 1;
   for (int pass = 1; pass < 4; pass++) {
