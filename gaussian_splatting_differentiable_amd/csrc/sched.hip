@@ -25,18 +25,29 @@ namespace {
 
 constexpr int NT = 1024, NW = NT / 64;
 
-__device__ __forceinline__ uint32_t block_max(uint32_t v) {
-  __shared__ uint32_t ws[NW];
+// Block-wide maximum and sum, in one exchange.
+__device__ __forceinline__ void block_max_sum(uint32_t &mx, long long &sum) {
+  __shared__ uint32_t wm[NW];
+  __shared__ long long wsum[NW];
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
+  for (int d = 32; d >= 1; d >>= 1) {
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+    sum += __shfl_xor(sum, d, 64);
+  }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) {
+    wm[threadIdx.x >> 6] = mx;
+    wsum[threadIdx.x >> 6] = sum;
+  }
   __syncthreads();
-  uint32_t t = 0;
+  mx = 0;
+  sum = 0;
 #pragma unroll
-  for (int w = 0; w < NW; w++) t = max(t, ws[w]);
+  for (int w = 0; w < NW; w++) {
+    mx = max(mx, wm[w]);
+    sum += wsum[w];
+  }
   __syncthreads();
-  return t;
 }
 
 // Block-wide exclusive prefix sum of one value per thread; `total` gets the sum.
@@ -95,20 +106,23 @@ __device__ void block_radix_pass(const uint32_t *__restrict__ kin, const int32_t
       if (base + 64 * r + lane < c1) atomicAdd(&cnt[w][(kk[r] >> shift) & 255], 1);
   }
   __syncthreads();
-  // offsets in (digit, wave) order: within a digit over the waves, then the
-  // digit totals scanned by the whole block
-  int dtot = 0;
-  if (threadIdx.x < 256) {
-    for (int q = 0; q < NW; q++) {
-      const int c = cnt[q][threadIdx.x];
-      cnt[q][threadIdx.x] = dtot;
-      dtot += c;
-    }
+  // offsets in (digit, wave) order: thread t scans the counts of digit t / 4
+  // in waves 4 (t % 4) .. 4 (t % 4) + 3, then one block scan joins them
+  static_assert(NW * 256 == 4 * NT, "four (digit, wave) counts per thread");
+  const int dg = threadIdx.x >> 2, q0 = 4 * (threadIdx.x & 3);
+  int cc[4], loc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    cc[j] = cnt[q0 + j][dg];
+    loc += cc[j];
   }
   int all;
-  const int dbase = block_excl_scan<int>(dtot, all);
-  if (threadIdx.x < 256)
-    for (int q = 0; q < NW; q++) cnt[q][threadIdx.x] += dbase;
+  int run = block_excl_scan<int>(loc, all);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    cnt[q0 + j][dg] = run;
+    run += cc[j];
+  }
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int base = c0; base < c1; base += 64 * RB_ROUNDS) {
@@ -151,31 +165,31 @@ constexpr int TL = 8192;
 constexpr size_t POLICY_BYTES = 8 * (HMAX + 1) + 4 * (HMAX + 1);
 constexpr size_t LDS_BYTES = 16 * (size_t)TL;  // four arrays of TL words
 
+// The block's lexicographic minimum of (best, idx), by two LDS atomics on an
+// order-preserving 64-bit image of the (non-NaN) doubles.
 __device__ __forceinline__ void block_min_idx(double &best, int &idx) {
-  __shared__ double wb[NW];
-  __shared__ int wi[NW];
+  __shared__ unsigned long long sb;
+  __shared__ int si;
+  if (threadIdx.x == 0) {
+    sb = ~0ull;
+    si = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  const unsigned long long u = (unsigned long long)__double_as_longlong(best);
+  const unsigned long long key = (u >> 63) ? ~u : (u | (1ull << 63));
+  unsigned long long wmin = key;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
-    const double ob = __shfl_xor(best, d, 64);
-    const int oi = __shfl_xor(idx, d, 64);
-    if (ob < best || (ob == best && oi < idx)) {
-      best = ob;
-      idx = oi;
-    }
+    const unsigned long long o = __shfl_xor(wmin, d, 64);
+    wmin = o < wmin ? o : wmin;
   }
+  if ((threadIdx.x & 63) == 0) atomicMin(&sb, wmin);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    wb[threadIdx.x >> 6] = best;
-    wi[threadIdx.x >> 6] = idx;
-  }
+  if (key == sb) atomicMin(&si, idx);
   __syncthreads();
-  best = wb[0];
-  idx = wi[0];
-  for (int w = 1; w < NW; w++)
-    if (wb[w] < best || (wb[w] == best && wi[w] < idx)) {
-      best = wb[w];
-      idx = wi[w];
-    }
+  const unsigned long long kb = sb;
+  best = __longlong_as_double((long long)((kb >> 63) ? (kb & ~(1ull << 63)) : ~kb));
+  idx = si;
   __syncthreads();
 }
 
@@ -193,19 +207,24 @@ __device__ void class_partition(const int32_t *order, int T, int h, int tiles_x,
   auto cls = [&](int e) { return 2 * tile_group(order[e], tiles_x) + (e >= h ? 1 : 0); };
   for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&pc[w][cls(e)], 1);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int c = 0; c < NCLS; c++) {
-      cstart[c] = run;
-      for (int q = 0; q < NW; q++) {
-        const int v = pc[q][c];
-        pc[q][c] = run;
-        run += v;
-      }
-      ccount[c] = run - cstart[c];
+  {
+    // offsets in (class, wave) order
+    static_assert(NCLS * NW <= NT, "one (class, wave) count per thread");
+    const int c = threadIdx.x / NW, q = threadIdx.x % NW;
+    const bool mine = threadIdx.x < NCLS * NW;
+    const int v = mine ? pc[q][c] : 0;
+    int all;
+    const int ex = block_excl_scan<int>(v, all);
+    if (mine) {
+      pc[q][c] = ex;
+      if (q == 0) cstart[c] = ex;
+    }
+    __syncthreads();
+    if (threadIdx.x < NCLS) {
+      const int cc = threadIdx.x;
+      ccount[cc] = (cc + 1 < NCLS ? cstart[cc + 1] : T) - cstart[cc];
     }
   }
-  __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int base = c0; base < c1; base += 64) {
     const int e = base + lane;
@@ -247,6 +266,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
   int32_t *tmp_v = lds ? reinterpret_cast<int32_t *>(dyn + 3 * TL) : fs.items + T;
   // 1. counts and the (bit-limited) descending key
   uint32_t mx = 0;
+  long long tot = 0;
   for (int t0 = threadIdx.x; t0 < T; t0 += NT * RB_ROUNDS) {
     int2 rr[RB_ROUNDS];
 #pragma unroll
@@ -262,10 +282,11 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
         key[t] = c;
         ord[t] = t;
         mx = max(mx, c);
+        tot += c;
       }
     }
   }
-  mx = block_max(mx);
+  block_max_sum(mx, tot);
   int bits = 0;
   while (bits < 32 && (mx >> bits) != 0u) bits++;
   const uint32_t full = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
@@ -308,10 +329,6 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     // sS[h] = N_1 + ... + N_h (exact), sN[h] = N_{h+1} (0 past the last tile)
     long long *sS = reinterpret_cast<long long *>(dyn);
     int *sN = reinterpret_cast<int *>(sS + HMAX + 1);
-    long long total_ll = 0;
-    for (int t = threadIdx.x; t < T; t += NT) total_ll += cnts[t];
-    long long tot;
-    (void)block_excl_scan<long long>(total_ll, tot);
     {
       static_assert(HMAX == 2 * NT, "two prefix entries per thread");
       const int i0 = 2 * threadIdx.x;
