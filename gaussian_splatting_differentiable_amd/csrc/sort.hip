@@ -44,7 +44,7 @@ constexpr int SPIN_LIMIT = 1 << 22;
 constexpr int HIST_TILES_LDS = 16384;  // tile histogram kept in LDS up to this many tiles
 constexpr int SCAN_T = 256, SCAN_I = 8, SCAN_TILE = SCAN_T * SCAN_I;
 constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pairs (a NaN pattern)
-constexpr int BIN_T = 256, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
+constexpr int BIN_T = 512, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
 
 // partitions: depth passes and tile passes
 constexpr int DS_THREADS = 1024, DS_ITEMS = 8, DS_PART = DS_THREADS * DS_ITEMS;
