@@ -140,6 +140,9 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
                                           Splat *sbuf, int *sid, float *__restrict__ grads) {
   const int lane = __lane_id();
   const int comp = comp_of_lane(lane);
+  // the constant factor each owner lane applies to its sum after the reduction
+  // (a power of two: exact): -1/2 for the two squared offsets
+  const float post = (comp == 2 || comp == 4) ? -0.5f : 1.0f;
   int hiE = cs + kmax;
   int lo = max(cs, hiE - BATCH);
   int idc = -1, idn = -1;
@@ -188,19 +191,23 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
       accum = __builtin_fmaf(al, diff, accum);
       const float w = al * T;
       const bool live_g = oG < 0.99f;  // a clamped alpha passes no gradient
-      const float m = live_g ? al * dal : 0.0f;  // -2 dL/dq
+      // -2 dL/dq, which is also o G dL/dalpha: an unclamped alpha is o G
+      const float m = live_g ? al * dal : 0.0f;
       float gr[9];
       gr[0] = m * __builtin_fmaf(b, dy, adx);  // dq/dmx = -2 (a dx + b dy)
       gr[1] = m * __builtin_fmaf(b, dx, cdy);
-      gr[2] = (-0.5f * m) * (dx * dx);
+      gr[2] = m * (dx * dx);                   // times -1/2 after the sum
       gr[3] = -(m * (dx * dy));
-      gr[4] = (-0.5f * m) * (dy * dy);
-      gr[5] = live_g ? oG * dal : 0.0f;  // o G dL/dalpha
+      gr[4] = m * (dy * dy);                   // times -1/2 after the sum
+      gr[5] = m;                               // divided by o after the sum
       gr[6] = w * g0;
       gr[7] = w * g1;
       gr[8] = w * g2;
       float out = reduce_scatter9(gr);
-      if (comp == 5) out *= s.p1.y;  // divide o back out
+      // finish the sum here, where its last exchange fuses into the add,
+      // rather than inside the owner lanes' branch
+      __asm__ volatile("" : "+v"(out));
+      out *= comp == 5 ? s.p1.y : post;
       if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[j] + comp], out);
       return true;
     });
