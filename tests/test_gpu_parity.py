@@ -160,6 +160,30 @@ def test_ragged_scenes(seed, W, H, n):
     check_backward(ref, out)
 
 
+def test_large_splats_sort_matches_oracle():
+    """Splats covering several tile rows each (about seven on average): the
+    pairs the sort generates row by row, their order and the tile ranges are
+    the oracle's, bit for bit."""
+    gsr = _gsr()
+    sc = scenegen.random_scene(104, 2000, 160, 150, 150.0, degree=1, log_scale=(-0.7, 0.3),
+                               opacity=(1.0, 1.0))
+    ref = oracle.frame(sc, fwd=False)
+    vis = np.diff(ref["offsets"]) > 0
+    tiles_x = (sc.camera.width + 15) // 16
+    ty = (ref["keys"] >> np.uint64(32)).astype(np.int64) // tiles_x
+    rows = len(np.unique(ref["ids"].astype(np.int64) * 4096 + ty))
+    assert rows > 5 * vis.sum()
+    cam = sc.camera
+    r = gsr.Rasterizer(cam, capacity=len(ref["sorted_ids"]))
+    r._ensure(sc.n, len(ref["sorted_ids"]))
+    r.splats[:sc.n].copy_(dev(ref["splats"]))
+    I = r.bin_and_sort(sc.n, want_keys=True)
+    assert I == len(ref["sorted_ids"])
+    assert np.array_equal(host(r.sorted_keys)[:I].view(np.uint64), ref["sorted_keys"])
+    assert np.array_equal(host(r.sorted_ids)[:I], ref["sorted_ids"])
+    assert np.array_equal(host(r.ranges), ref["ranges"])
+
+
 def test_capacity_overflow_reports_and_recovers():
     gsr = _gsr()
     sc, ref = reference(1)
