@@ -146,14 +146,24 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
   int hiE = cs + kmax;
   int lo = max(cs, hiE - BATCH);
   int idc = -1, idn = -1;
-  Splat rec;
+  // the next batch's record of this lane, as three registers of four (kept out
+  // of any aggregate: the compiler parked part of one in memory and waited for
+  // its load right after issuing it)
+  const float4 *rec4 = reinterpret_cast<const float4 *>(splats);
+  float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
   if (hiE > cs) {
     idc = load_id(sids, lo, hiE);
-    rec = splats[idc >= 0 ? idc : 0];
+    const int64_t ri = 3 * (int64_t)(idc >= 0 ? idc : 0);
+    r0 = rec4[ri];
+    r1 = rec4[ri + 1];
+    r2 = rec4[ri + 2];
     idn = load_id(sids, max(cs, lo - BATCH), lo);
   }
   while (hiE > cs) {
-    Splat s = rec;
+    Splat s;
+    s.p0 = r0;
+    s.p1 = r1;
+    s.p2 = r2;
     const bool cand = idc >= 0 && rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y,
                                                 st.hx0, st.hx1, st.hy0, st.hy1);
     s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
@@ -165,7 +175,12 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
     const int nhi = lo, nlo = max(cs, lo - BATCH);
     // records of [nlo, nhi), ids of the batch below it
     idc = idn;
-    rec = splats[idc >= 0 ? idc : 0];
+    {
+      const int64_t ri = 3 * (int64_t)(idc >= 0 ? idc : 0);
+      r0 = rec4[ri];
+      r1 = rec4[ri + 1];
+      r2 = rec4[ri + 2];
+    }
     idn = load_id(sids, max(cs, nlo - BATCH), nlo);
     wave_sync();
     const int base = lo - cs;
