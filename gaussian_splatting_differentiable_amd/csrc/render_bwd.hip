@@ -26,17 +26,6 @@ namespace {
 
 constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 
-// Zero the gradient output and rewind the backward queues of this frame.
-__global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n,
-                                              const PlanHdr *__restrict__ hdr,
-                                              int32_t *__restrict__ bwd_heads) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < GS_GROUPS) bwd_heads[i * GS_HEAD_STRIDE] = hdr->init_b[i];
-  const int64_t n4 = n / 4;
-  if (i < n4) reinterpret_cast<float4 *>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (i < n - 4 * n4) p[4 * n4 + i] = 0.0f;
-}
-
 // Backward queue order. The forward pass leaves every item's walk length (the
 // quarter's or chunk's last hit), so the backward can serve its items longest
 // first exactly ([LOAD-IMB] section 4.1 orders by N_t, which overstates the work
@@ -53,8 +42,18 @@ __device__ __forceinline__ uint32_t order_bin(const FwdState &fs, int it, int k)
   return (uint32_t)(BO_BINS - 1 - min(b, BO_BINS - 1));  // ascending bin = longest first
 }
 
-__global__ void __launch_bounds__(BO_T) k_bwd_order(char *__restrict__ state, int ntiles,
-                                                   int nblocks) {
+// The backward's preparation in one launch: workgroup g < GS_GROUPS orders
+// group g's items and rewinds its queue; the others zero the gradient output.
+__global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int ntiles,
+                                                  int nblocks, float *__restrict__ grads,
+                                                  int64_t ng) {
+  if (blockIdx.x >= GS_GROUPS) {
+    const int64_t i = (int64_t)(blockIdx.x - GS_GROUPS) * BO_T + threadIdx.x;
+    const int64_t n4 = ng / 4;
+    if (i < n4) reinterpret_cast<float4 *>(grads)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < ng - 4 * n4) grads[4 * n4 + i] = 0.0f;
+    return;
+  }
   __shared__ int cnt[BO_W][BO_BINS];
   FwdState fs = fwd_state_at(state, ntiles);
   const int g = blockIdx.x, k = fs.hdr->k;
@@ -317,12 +316,10 @@ hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 hipEvent_t ev1, hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
   const int ntiles = cam.tiles_x * cam.tiles_y;
-  const FwdState fs = fwd_state_at(fwd_state, ntiles);
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
-  hipLaunchKernelGGL(k_bwd_order, dim3(GS_GROUPS), dim3(BO_T), 0, st,
-                     reinterpret_cast<char *>(fwd_state), ntiles, nblocks);
-  hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng,
-                     fs.hdr, queue_head(fs, 1, 0));
+  const int zero_blocks = (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
+  hipLaunchKernelGGL(k_bwd_prep, dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
+                     reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, st);
     if (e != hipSuccess) return e;
