@@ -193,13 +193,18 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_start
+    # the stage breakdown: the same steps again with HIP events between the calls
+    # (kept out of the timed loop above, whose steps they would lengthen)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
     # the raster kernels' own durations: the same steps again, with a pair of HIP
     # events recorded on the stream around each raster kernel launch (kept out
     # of the timed loop above, whose calls they would otherwise lengthen)
