@@ -65,6 +65,9 @@ def _load():
     sig = {
         "or_sh_basis": [i32, P, P],
         "or_project": [i32, P, P, P, P, P, i32, C.POINTER(Camera), P, P],
+        "or_project64": [i32, P, P, P, P, P, i32, C.POINTER(Camera), P],
+        "or_sh_cart": [i32, P, P, P],
+        "or_project_bwd": [i32, P, P, P, P, P, i32, C.POINTER(Camera), P, P, P, P, P, P],
         "or_bin_count": [i32, P, i32, i32, P],
         "or_bin_emit": [i32, P, i32, i32, P, P, P],
         "or_sort_pairs": [i64, P, P, P, P],
@@ -114,6 +117,44 @@ def project(means, log_scales, quats, opacities, sh, sh_degree, camera, want_f64
     lib.or_project(n, _p(means), _p(log_scales), _p(quats), _p(opacities), _p(sh),
                    int(sh_degree), C.byref(cam), _p(out), _p(out64))
     return (out, out64) if want_f64 else out
+
+
+def project64(means, log_scales, quats, opacities, sh, sh_degree, camera):
+    """The projection on fp64 inputs; fp64 records (for finite differences)."""
+    args = [_c(a, np.float64) for a in (means, log_scales, quats, opacities, sh)]
+    n = args[0].shape[0]
+    out = np.zeros((n, 12), np.float64)
+    cam = _camera(camera)
+    _load().or_project64(n, *[_p(a) for a in args], int(sh_degree), C.byref(cam), _p(out))
+    return out
+
+
+def sh_cart(degree: int, d):
+    """The SH basis as polynomials of the direction and their gradients."""
+    d = _c(d, np.float64)
+    Y = np.zeros(16, np.float64)
+    dY = np.zeros((16, 3), np.float64)
+    _load().or_sh_cart(degree, _p(d), _p(Y), _p(dY))
+    K = (degree + 1) ** 2
+    return Y[:K], dY[:K]
+
+
+def project_bwd(means, log_scales, quats, opacities, sh, sh_degree, camera, dsplat):
+    """Backward of the projection in fp64: dL/d(means, log_scales, quats,
+    opacities, sh) from dL/d of the records' first nine entries."""
+    lib = _load()
+    means, log_scales, quats = _c(means, np.float32), _c(log_scales, np.float32), _c(quats, np.float32)
+    opacities, sh = _c(opacities, np.float32), _c(sh, np.float32)
+    n = means.shape[0]
+    K = (sh_degree + 1) ** 2
+    dsplat = _c(np.asarray(dsplat)[:, :9], np.float64)
+    out = dict(means=np.zeros((n, 3)), log_scales=np.zeros((n, 3)), quats=np.zeros((n, 4)),
+               opacities=np.zeros(n), sh=np.zeros((n, K, 3)))
+    cam = _camera(camera)
+    lib.or_project_bwd(n, _p(means), _p(log_scales), _p(quats), _p(opacities), _p(sh),
+                       int(sh_degree), C.byref(cam), _p(dsplat), _p(out["means"]),
+                       _p(out["log_scales"]), _p(out["quats"]), _p(out["opacities"]), _p(out["sh"]))
+    return out
 
 
 def project_scene(scene, want_f64=False):

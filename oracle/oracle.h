@@ -42,6 +42,24 @@ void or_project(int n, const float *means, const float *log_scales, const float 
                 const float *opac, const float *sh, int degree, const or_camera *cam,
                 float *splats, double *splats64);
 
+/* The projection on fp64 inputs (fp64 records only): the reference for finite
+   differences of or_project_bwd. */
+void or_project64(int n, const double *means, const double *log_scales, const double *quats,
+                  const double *opac, const double *sh, int degree, const or_camera *cam,
+                  double *splats64);
+
+/* The SH basis of or_sh_basis as polynomials of the direction, with their
+   gradients dY[3k + j] = dY_k/dd_j (degree <= 3). */
+void or_sh_cart(int degree, const double *d, double *Y, double *dY);
+
+/* Backward of the projection: dL/d(mean, log-scales, quaternion, opacity, SH)
+   from dL/d of the record's first nine entries (dsplat [n][9]), in fp64.
+   Culled Gaussians get zeros. */
+void or_project_bwd(int n, const float *means, const float *log_scales, const float *quats,
+                    const float *opac, const float *sh, int degree, const or_camera *cam,
+                    const double *dsplat, double *gmeans, double *gls, double *gquats,
+                    double *gopac, double *gsh);
+
 /* Opacity-aware exact conic-tile binning ([3DGS-CUDA] Step 1 (b), Figure 3). */
 void or_bin_count(int n, const float *splats, int width, int height, int32_t *counts);
 void or_bin_emit(int n, const float *splats, int width, int height, const int64_t *offsets,
