@@ -24,8 +24,9 @@ GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY = 0, -1, -2
 GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED = -3, -4, -5
 SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
 
-EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_bin_tiles",
-           "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start", "gs_timing_read")
+EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_project_bwd",
+           "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
+           "gs_timing_read")
 
 
 class GsError(RuntimeError):
@@ -63,14 +64,15 @@ def lib():
     L.gs_workspace_size.argtypes, L.gs_workspace_size.restype = [i32, i32, i32, i64], sz
     L.gs_fwd_state_size.argtypes, L.gs_fwd_state_size.restype = [i32, i32], sz
     L.gs_project.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P]
+    L.gs_project_bwd.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P, P, P, P, P, P]
     L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, sz, P]
     L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, sz, P]
     L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
     L.gs_timing_start.argtypes = []
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
-    for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
-                 "gs_timing_start", "gs_timing_read"):
+    for name in ("gs_project", "gs_project_bwd", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
+                 "gs_render_bwd", "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -138,6 +140,16 @@ def gs_project(n, means, log_scales, quats, opacities, sh, sh_degree, cam, splat
     _check(lib().gs_project(int(n), _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacities),
                             _ptr(sh), int(sh_degree), C.byref(cam), _ptr(splats), _stream(stream)),
            "gs_project")
+
+
+def gs_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, cam, dL_dsplat,
+                   dL_dmeans, dL_dlog_scales, dL_dquats, dL_dopacities, dL_dsh, stream=None):
+    _check(lib().gs_project_bwd(int(n), _ptr(means), _ptr(log_scales), _ptr(quats),
+                                _ptr(opacities), _ptr(sh), int(sh_degree), C.byref(cam),
+                                _ptr(dL_dsplat), _ptr(dL_dmeans), _ptr(dL_dlog_scales),
+                                _ptr(dL_dquats), _ptr(dL_dopacities), _ptr(dL_dsh),
+                                _stream(stream)),
+           "gs_project_bwd")
 
 
 def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace, stream=None):
@@ -272,3 +284,19 @@ class Rasterizer:
         gs_render_bwd(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.T, self.last,
                       self.fwd_state, dL_drgb, self.grads, self.workspace)
         return self.grads[:n]
+
+    def project_bwd(self, means, log_scales, quats, opacities, sh, sh_degree, dL_dsplat=None):
+        """Per-Gaussian gradients from the screen-space ones (by default the last
+        render_bwd's). Returns a dict of new device tensors."""
+        n = int(means.shape[0])
+        dsp = self.grads[:n] if dL_dsplat is None else dL_dsplat
+        dev = means.device
+        K = (int(sh_degree) + 1) ** 2
+        out = dict(means=torch.empty((n, 3), dtype=torch.float32, device=dev),
+                   log_scales=torch.empty((n, 3), dtype=torch.float32, device=dev),
+                   quats=torch.empty((n, 4), dtype=torch.float32, device=dev),
+                   opacities=torch.empty(n, dtype=torch.float32, device=dev),
+                   sh=torch.empty((n, K, 3), dtype=torch.float32, device=dev))
+        gs_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, dsp,
+                       out["means"], out["log_scales"], out["quats"], out["opacities"], out["sh"])
+        return out

@@ -9,6 +9,11 @@
 hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
                              const float *opac, const float *sh, int degree, const CamK &cam,
                              float *splats, hipStream_t st);
+hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_scales,
+                                 const float *quats, const float *opac, const float *sh,
+                                 int degree, const CamK &cam, const float *dsplat, float *gmeans,
+                                 float *gls, float *gquats, float *gopac, float *gsh,
+                                 hipStream_t st);
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
                          int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
                          hipStream_t st);
@@ -142,6 +147,24 @@ int32_t gs_project(int32_t n, const float *means, const float *log_scales, const
   if (!aligned(quats, 16) || !aligned(splats, 16) || !aligned(sh, 4)) return GS_ERR_INVALID_ARGUMENT;
   return hip_status(gs_launch_project(n, means, log_scales, quats, opacities, sh, sh_degree, k,
                                       splats, (hipStream_t)stream));
+}
+
+int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, const float *quats,
+                       const float *opacities, const float *sh, int32_t sh_degree,
+                       const gs_camera *cam, const float *dL_dsplat, float *dL_dmeans,
+                       float *dL_dlog_scales, float *dL_dquats, float *dL_dopacities,
+                       float *dL_dsh, void *stream) {
+  CamK k;
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GS_OK;
+  if (!means || !log_scales || !quats || !opacities || !sh || !dL_dsplat || !dL_dmeans ||
+      !dL_dlog_scales || !dL_dquats || !dL_dopacities || !dL_dsh)
+    return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(quats, 16) || !aligned(dL_dquats, 16) || !aligned(sh, 4) || !aligned(dL_dsh, 4))
+    return GS_ERR_INVALID_ARGUMENT;
+  return hip_status(gs_launch_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, k,
+                                          dL_dsplat, dL_dmeans, dL_dlog_scales, dL_dquats,
+                                          dL_dopacities, dL_dsh, (hipStream_t)stream));
 }
 
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,

@@ -149,7 +149,219 @@ __global__ void __launch_bounds__(256) k_project(int n, const float *__restrict_
   out[i] = s;
 }
 
+// Accumulate sum_k grad Y_k(x, y, z) w_k into (g0, g1, g2): the gradients of
+// the polynomials of sh_eval in R^3 (the caller keeps the part tangent to the
+// sphere).
+__device__ __forceinline__ void sh_grad_acc(int K, float x, float y, float z, const float *w,
+                                            float &g0, float &g1, float &g2) {
+  if (K <= 1) return;
+  const float c1 = 0.4886025119029199f;
+  g0 = fmaf(c1, w[3], g0);
+  g1 = fmaf(c1, w[1], g1);
+  g2 = fmaf(c1, w[2], g2);
+  if (K <= 4) return;
+  const float c2a = 1.0925484305920792f, c2b = 0.31539156525252005f, c2c = 0.5462742152960396f;
+  // Y4 = c2a x y, Y5 = c2a y z, Y6 = c2b (3 z^2 - 1), Y7 = c2a x z, Y8 = c2c (x^2 - y^2)
+  g0 += c2a * (y * w[4] + z * w[7]) + 2.0f * c2c * x * w[8];
+  g1 += c2a * (x * w[4] + z * w[5]) - 2.0f * c2c * y * w[8];
+  g2 += c2a * (y * w[5] + x * w[7]) + 6.0f * c2b * z * w[6];
+  if (K <= 9) return;
+  const float c3a = 0.5900435899266435f, c3b = 2.890611442640554f, c3c = 0.4570457994644658f,
+              c3d = 0.3731763325901154f, c3e = 1.445305721320277f;
+  const float xx = x * x, yy = y * y, zz = z * z;
+  // Y9 = c3a y (3x^2 - y^2), Y10 = c3b x y z, Y11 = c3c y (5z^2 - 1), Y12 = c3d z (5z^2 - 3),
+  // Y13 = c3c x (5z^2 - 1), Y14 = c3e z (x^2 - y^2), Y15 = c3a x (x^2 - 3y^2)
+  g0 += 6.0f * c3a * x * y * w[9] + c3b * y * z * w[10] + c3c * (5.0f * zz - 1.0f) * w[13] +
+        2.0f * c3e * x * z * w[14] + 3.0f * c3a * (xx - yy) * w[15];
+  g1 += 3.0f * c3a * (xx - yy) * w[9] + c3b * x * z * w[10] + c3c * (5.0f * zz - 1.0f) * w[11] -
+        2.0f * c3e * y * z * w[14] - 6.0f * c3a * x * y * w[15];
+  g2 += c3b * x * y * w[10] + 10.0f * c3c * y * z * w[11] + c3d * (15.0f * zz - 3.0f) * w[12] +
+        10.0f * c3c * x * z * w[13] + c3e * (xx - yy) * w[14];
+}
+
+// Backward of k_project: the 9 screen-space gradients of a splat record (mx, my,
+// a, b, c, o, r, g, b) chained to the Gaussian's mean, log-scales, quaternion,
+// opacity and SH coefficients ([LOAD-IMB] section 2.1 Eq. 1 differentiated;
+// [3DGS-CUDA] Step 3: dL/ds_k = Y_k(d) dL/dc plus the view-direction term).
+// The forward's intermediates are recomputed. tau and depth pass no gradient;
+// every output row is written (zeros for a culled Gaussian).
+template <int K>
+__global__ void __launch_bounds__(256) k_project_bwd(
+    int n, const float *__restrict__ means, const float *__restrict__ log_scales,
+    const float4 *__restrict__ quats, const float *__restrict__ opac, const float *__restrict__ sh,
+    CamK cam, const float *__restrict__ dsplat, float *__restrict__ gmeans,
+    float *__restrict__ gls, float4 *__restrict__ gquats, float *__restrict__ gopac,
+    float *__restrict__ gsh) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float m0 = means[3 * i], m1 = means[3 * i + 1], m2 = means[3 * i + 2];
+  const float *R = cam.R;
+  const float tx = fmaf(R[0], m0, fmaf(R[1], m1, fmaf(R[2], m2, cam.t[0])));
+  const float ty = fmaf(R[3], m0, fmaf(R[4], m1, fmaf(R[5], m2, cam.t[1])));
+  const float tz = fmaf(R[6], m0, fmaf(R[7], m1, fmaf(R[8], m2, cam.t[2])));
+  const float o = opac[i];
+  const float tau = 2.0f * logf(255.0f * o);
+  const float4 q4 = quats[i];
+  const float qn2 = q4.x * q4.x + q4.y * q4.y + q4.z * q4.z + q4.w * q4.w;
+  float *gsh_i = gsh + (size_t)i * (K * 3);
+  auto write_zero = [&]() {
+    gmeans[3 * i] = gmeans[3 * i + 1] = gmeans[3 * i + 2] = 0.0f;
+    gls[3 * i] = gls[3 * i + 1] = gls[3 * i + 2] = 0.0f;
+    gquats[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    gopac[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K * 3; j++) gsh_i[j] = 0.0f;
+  };
+  if (!(tz > cam.znear) || !(tau > 0.0f) || !(qn2 > 0.0f)) {
+    write_zero();
+    return;
+  }
+  const float qi = 1.0f / sqrtf(qn2);
+  const float w = q4.x * qi, x = q4.y * qi, y = q4.z * qi, z = q4.w * qi;
+  float rq[3][3] = {{1.f - 2.f * (y * y + z * z), 2.f * (x * y - w * z), 2.f * (x * z + w * y)},
+                    {2.f * (x * y + w * z), 1.f - 2.f * (x * x + z * z), 2.f * (y * z - w * x)},
+                    {2.f * (x * z - w * y), 2.f * (y * z + w * x), 1.f - 2.f * (x * x + y * y)}};
+  const float sc[3] = {expf(log_scales[3 * i]), expf(log_scales[3 * i + 1]),
+                       expf(log_scales[3 * i + 2])};
+  // M = R (Rq S), u and v the rows of J M (as in the forward pass)
+  float M[3][3];
+#pragma unroll
+  for (int r = 0; r < 3; r++)
+#pragma unroll
+    for (int c = 0; c < 3; c++)
+      M[r][c] = (R[3 * r] * rq[0][c] + R[3 * r + 1] * rq[1][c] + R[3 * r + 2] * rq[2][c]) * sc[c];
+  const float iz = 1.0f / tz;
+  const float ux = tx * iz, uy = ty * iz;
+  const float fxz = cam.fx * iz, fyz = cam.fy * iz;
+  float u[3], v[3];
+#pragma unroll
+  for (int c = 0; c < 3; c++) {
+    u[c] = fxz * (M[0][c] - ux * M[2][c]);
+    v[c] = fyz * (M[1][c] - uy * M[2][c]);
+  }
+  const float uu = u[0] * u[0] + u[1] * u[1] + u[2] * u[2];
+  const float vv = v[0] * v[0] + v[1] * v[1] + v[2] * v[2];
+  const float uv = u[0] * v[0] + u[1] * v[1] + u[2] * v[2];
+  const float cx0 = u[1] * v[2] - u[2] * v[1], cx1 = u[2] * v[0] - u[0] * v[2],
+              cx2 = u[0] * v[1] - u[1] * v[0];
+  const float lp = cam.lowpass;
+  const float sxx = uu + lp, syy = vv + lp;
+  const float det = (cx0 * cx0 + cx1 * cx1 + cx2 * cx2) + lp * (uu + vv) + lp * lp;
+  if (!(det > 0.0f)) {
+    write_zero();
+    return;
+  }
+  const float idet = 1.0f / det;
+  const float ca = syy * idet, cb = -uv * idet, cc = sxx * idet;
+  const float *gsp = dsplat + 9 * (size_t)i;
+  const float gmx = gsp[0], gmy = gsp[1], ga = gsp[2], gb = gsp[3], gc = gsp[4];
+  // conic -> Sigma': dL/dSigma' = -Lambda G Lambda, G = [[ga, gb/2], [gb/2, gc]]
+  const float p00 = fmaf(ca, ga, 0.5f * cb * gb), p01 = fmaf(0.5f * ca, gb, cb * gc);
+  const float p10 = fmaf(cb, ga, 0.5f * cc * gb), p11 = fmaf(0.5f * cb, gb, cc * gc);
+  const float dsxx = -fmaf(p00, ca, p01 * cb);
+  const float duv = -2.0f * fmaf(p00, cb, p01 * cc);
+  const float dsyy = -fmaf(p10, cb, p11 * cc);
+  // Sigma' -> u, v -> M and t
+  float dM[3][3];
+  float sx = 0.f, sy = 0.f, sz = 0.f;
+#pragma unroll
+  for (int c = 0; c < 3; c++) {
+    const float du = fmaf(2.0f * dsxx, u[c], duv * v[c]);
+    const float dv = fmaf(2.0f * dsyy, v[c], duv * u[c]);
+    dM[0][c] = fxz * du;
+    dM[1][c] = fyz * dv;
+    dM[2][c] = -(fxz * ux * du + fyz * uy * dv);
+    sx = fmaf(du, M[2][c], sx);
+    sy = fmaf(dv, M[2][c], sy);
+    sz += du * (fxz * ux * M[2][c] - u[c]) + dv * (fyz * uy * M[2][c] - v[c]);
+  }
+  const float dtx = fxz * (gmx - iz * sx);
+  const float dty = fyz * (gmy - iz * sy);
+  const float dtz = iz * sz - gmx * fxz * ux - gmy * fyz * uy;
+  // M = R A -> A = Rq S -> scales and rotation entries
+  float dls[3], dRq[3][3];
+#pragma unroll
+  for (int c = 0; c < 3; c++) {
+    float ds = 0.f;
+#pragma unroll
+    for (int r = 0; r < 3; r++) {
+      const float dA = R[r] * dM[0][c] + R[3 + r] * dM[1][c] + R[6 + r] * dM[2][c];
+      ds = fmaf(dA, rq[r][c], ds);
+      dRq[r][c] = dA * sc[c];
+    }
+    dls[c] = ds * sc[c];
+  }
+  // rotation entries -> unit quaternion -> quaternion
+  const float gw = 2.f * (-z * dRq[0][1] + y * dRq[0][2] + z * dRq[1][0] - x * dRq[1][2] -
+                          y * dRq[2][0] + x * dRq[2][1]);
+  const float gx = 2.f * (y * dRq[0][1] + z * dRq[0][2] + y * dRq[1][0] - 2.f * x * dRq[1][1] -
+                          w * dRq[1][2] + z * dRq[2][0] + w * dRq[2][1] - 2.f * x * dRq[2][2]);
+  const float gy = 2.f * (-2.f * y * dRq[0][0] + x * dRq[0][1] + w * dRq[0][2] + x * dRq[1][0] +
+                          z * dRq[1][2] - w * dRq[2][0] + z * dRq[2][1] - 2.f * y * dRq[2][2]);
+  const float gz = 2.f * (-2.f * z * dRq[0][0] - w * dRq[0][1] + x * dRq[0][2] + w * dRq[1][0] -
+                          2.f * z * dRq[1][1] + y * dRq[1][2] + x * dRq[2][0] + y * dRq[2][1]);
+  const float qd = w * gw + x * gx + y * gy + z * gz;
+  gquats[i] = make_float4((gw - w * qd) * qi, (gx - x * qd) * qi, (gy - y * qd) * qi,
+                          (gz - z * qd) * qi);
+  gls[3 * i] = dls[0];
+  gls[3 * i + 1] = dls[1];
+  gls[3 * i + 2] = dls[2];
+  gopac[i] = gsp[5];
+  // t = R mu + t_cam
+  float g0 = R[0] * dtx + R[3] * dty + R[6] * dtz;
+  float g1 = R[1] * dtx + R[4] * dty + R[7] * dtz;
+  float g2 = R[2] * dtx + R[5] * dty + R[8] * dtz;
+  // colour: dL/ds_k = Y_k(d) dL/dc, and the view direction's share of dL/dmu
+  float d0 = m0 - cam.centre[0], d1 = m1 - cam.centre[1], d2 = m2 - cam.centre[2];
+  const float dn2 = d0 * d0 + d1 * d1 + d2 * d2;
+  const float gr = gsp[6], gg = gsp[7], gbl = gsp[8];
+  if (dn2 > 0.0f) {
+    const float dinv = 1.0f / sqrtf(dn2);
+    d0 *= dinv; d1 *= dinv; d2 *= dinv;
+    float Y[16], wk[16];
+    sh_eval(K, d0, d1, d2, Y);
+    const float *shi = sh + (size_t)i * (K * 3);
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      wk[k] = fmaf(shi[3 * k], gr, fmaf(shi[3 * k + 1], gg, shi[3 * k + 2] * gbl));
+      gsh_i[3 * k] = Y[k] * gr;
+      gsh_i[3 * k + 1] = Y[k] * gg;
+      gsh_i[3 * k + 2] = Y[k] * gbl;
+    }
+    float e0 = 0.f, e1 = 0.f, e2 = 0.f;
+    sh_grad_acc(K, d0, d1, d2, wk, e0, e1, e2);
+    const float ed = e0 * d0 + e1 * d1 + e2 * d2;
+    g0 = fmaf(e0 - d0 * ed, dinv, g0);
+    g1 = fmaf(e1 - d1 * ed, dinv, g1);
+    g2 = fmaf(e2 - d2 * ed, dinv, g2);
+  } else {
+#pragma unroll
+    for (int j = 0; j < K * 3; j++) gsh_i[j] = 0.0f;
+  }
+  gmeans[3 * i] = g0;
+  gmeans[3 * i + 1] = g1;
+  gmeans[3 * i + 2] = g2;
+}
+
 }  // namespace
+
+hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_scales,
+                                 const float *quats, const float *opac, const float *sh,
+                                 int degree, const CamK &cam, const float *dsplat, float *gmeans,
+                                 float *gls, float *gquats, float *gopac, float *gsh,
+                                 hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  dim3 grid(gs_div_up(n, 256)), block(256);
+  const float4 *q4 = reinterpret_cast<const float4 *>(quats);
+  float4 *gq4 = reinterpret_cast<float4 *>(gquats);
+  switch (degree) {
+    case 0: hipLaunchKernelGGL(k_project_bwd<1>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    case 1: hipLaunchKernelGGL(k_project_bwd<4>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    case 2: hipLaunchKernelGGL(k_project_bwd<9>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    default: hipLaunchKernelGGL(k_project_bwd<16>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
                              const float *opac, const float *sh, int degree, const CamK &cam,

@@ -111,6 +111,25 @@ int32_t gs_project(int32_t n, const float *means, const float *log_scales, const
                    const float *opacities, const float *sh, int32_t sh_degree,
                    const gs_camera *cam, float *splats, void *stream);
 
+/* Backward of gs_project: the 9 screen-space gradients of each record chained
+ * to the Gaussian's parameters (Eq. 1 of the load-imbalance page differentiated
+ * through Lambda = Sigma'^-1, the Jacobian J(t), the view transform and
+ * Sigma = Rq diag(exp(2 s)) Rq^T; Step 3 of the literature page for the colour:
+ * dL/ds_k = Y_k(d) dL/dc, plus the view direction's share of dL/dmean).
+ *   means, log_scales, quats, opacities, sh, sh_degree, cam: as for gs_project
+ *   dL_dsplat [n][9] <- read: dL/d(mx, my, a, b, c, o, r, g, b) (gs_render_bwd's
+ *     output); tau and depth pass no gradient (a threshold and a sort key)
+ *   dL_dmeans [n][3], dL_dlog_scales [n][3], dL_dquats [n][4] (with respect to
+ *     the quaternion as given, not normalised), dL_dopacities [n],
+ *     dL_dsh [n][(deg+1)^2][3] <- fully overwritten; rows of Gaussians that
+ *     gs_project culls are 0.
+ * quats and dL_dquats 16-byte aligned. */
+int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, const float *quats,
+                       const float *opacities, const float *sh, int32_t sh_degree,
+                       const gs_camera *cam, const float *dL_dsplat, float *dL_dmeans,
+                       float *dL_dlog_scales, float *dL_dquats, float *dL_dopacities,
+                       float *dL_dsh, void *stream);
+
 /* Exact opacity-aware conic-tile binning (Step 1 (b) of the literature page).
  * A tile is emitted for splat i when the ellipse q <= tau (1 + 2^-10) meets the
  * tile's pixel-sample hull widened by 2^-8 px; spans are solved per tile row

@@ -53,6 +53,17 @@ def test_argument_validation_needs_no_gpu(gsr):
     assert L.gs_project(4, None, None, None, None, None, 7, C.byref(cam), None, None) == -1
     bad = gsr.GsCamera()
     assert L.gs_project(1, None, None, None, None, None, 0, C.byref(bad), None, None) == -1
+    # the projection backward: the same checks, plus missing outputs and misaligned quaternions
+    nul = [None] * 6
+    assert L.gs_project_bwd(-1, None, None, None, None, None, 0, C.byref(cam), *nul, None) == -1
+    assert L.gs_project_bwd(4, None, None, None, None, None, 4, C.byref(cam), *nul, None) == -1
+    assert L.gs_project_bwd(1, None, None, None, None, None, 0, C.byref(bad), *nul, None) == -1
+    p16 = C.c_void_p(16)
+    assert L.gs_project_bwd(1, p16, p16, p16, p16, p16, 0, C.byref(cam), p16, p16, p16, p16, p16,
+                            None, None) == -1
+    assert L.gs_project_bwd(1, p16, p16, C.c_void_p(20), p16, p16, 0, C.byref(cam), p16, p16, p16,
+                            p16, p16, p16, None) == -1
+    assert L.gs_project_bwd(0, None, None, None, None, None, 0, C.byref(cam), *nul, None) == 0
     big = gsr.GsCamera()
     big.width, big.height, big.fx, big.fy = 1 << 14, 1 << 14, 1.0, 1.0
     assert L.gs_bin_tiles(1, C.c_void_p(16), C.byref(big), 10, C.c_void_p(16), C.c_void_p(16),
