@@ -47,6 +47,11 @@ BIN_BYTES_PER_GAUSSIAN = 52
 SORT_BYTES_PER_PAIR = 28
 SORT_BYTES_PER_TILE = 8
 PROJ_BYTES_PER_GAUSSIAN = 44 + 48
+# The projection's backward reads the 44 B of parameters and the 36 B of
+# screen-space gradients of every Gaussian and its SH (12 B per coefficient)
+# when visible, and writes 44 B of parameter gradients and the SH gradient of
+# every Gaussian (zeros for culled ones).
+PROJ_BWD_BYTES_PER_GAUSSIAN = 44 + 36 + 44
 PEAK_FP32_TFLOPS = 157.3     # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0        # MI355X published HBM3E bandwidth
 # exp and reciprocal issue at a quarter of the fp32 lane rate:
@@ -235,6 +240,20 @@ def main():
     torch.cuda.synchronize()
     per["project"] = [pe[2 * k].elapsed_time(pe[2 * k + 1]) for k in range(args.steps)]
     ms_project = float(np.median(per["project"]))
+    # the projection's backward (the next stage of a training step), in its own loop
+    pb = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    K = (sc.sh_degree + 1) ** 2
+    pgrads = [torch.empty(shape, dtype=torch.float32, device=dev)
+              for shape in ((n, 3), (n, 3), (n, 4), (n,), (n, K, 3))]
+    for k in range(args.steps + 1):
+        if k:
+            pb[2 * k - 2].record(stream)
+        gsr.gs_project_bwd(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.grads, *pgrads)
+        if k:
+            pb[2 * k - 1].record(stream)
+    torch.cuda.synchronize()
+    per["project_bwd"] = [pb[2 * k].elapsed_time(pb[2 * k + 1]) for k in range(args.steps)]
+    ms_project_bwd = float(np.median(per["project_bwd"]))
     n_vis = int((r.splats[:, 9] > 0).sum().item())
 
     # roofline of the longest raster kernel: algorithmic bytes and flops per launch
@@ -272,6 +291,8 @@ def main():
     stage_work = {
         "project": dict(flops=0, trans=0,
                         bytes=PROJ_BYTES_PER_GAUSSIAN * n + sh_bytes * n_vis),
+        "project_bwd": dict(flops=0, trans=0,
+                            bytes=(PROJ_BWD_BYTES_PER_GAUSSIAN + sh_bytes) * n + sh_bytes * n_vis),
         "bin": dict(flops=0, trans=0, bytes=BIN_BYTES_PER_GAUSSIAN * n),
         "sort": dict(flops=0, trans=0,
                      bytes=SORT_BYTES_PER_PAIR * npairs + SORT_BYTES_PER_TILE * cam.num_tiles),
@@ -312,6 +333,7 @@ def main():
         "ms": {k: round(v, 4) for k, v in ms.items()},
         "ms_min": {k: round(v, 4) for k, v in ms_min.items()},
         "ms_project": round(ms_project, 4),
+        "ms_project_bwd": round(ms_project_bwd, 4),
         "ms_raster_fwd_bwd": round(ms_raster, 4),
         "ms_kernels": {f"k_render_{k}": round(v, 4) for k, v in kernel_ms.items()},
         "raster_pairs_per_s": round(npairs / (ms_raster * 1e-3), 1),

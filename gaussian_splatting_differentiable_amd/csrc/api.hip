@@ -160,7 +160,9 @@ int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, c
   if (!means || !log_scales || !quats || !opacities || !sh || !dL_dsplat || !dL_dmeans ||
       !dL_dlog_scales || !dL_dquats || !dL_dopacities || !dL_dsh)
     return GS_ERR_INVALID_ARGUMENT;
-  if (!aligned(quats, 16) || !aligned(dL_dquats, 16) || !aligned(sh, 4) || !aligned(dL_dsh, 4))
+  const bool rows16 = (3 * (sh_degree + 1) * (sh_degree + 1)) % 4 == 0;  // degrees 1 and 3
+  if (!aligned(quats, 16) || !aligned(dL_dquats, 16) || !aligned(sh, rows16 ? 16 : 4) ||
+      !aligned(dL_dsh, rows16 ? 16 : 4))
     return GS_ERR_INVALID_ARGUMENT;
   return hip_status(gs_launch_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, k,
                                           dL_dsplat, dL_dmeans, dL_dlog_scales, dL_dquats,

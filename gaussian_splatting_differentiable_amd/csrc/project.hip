@@ -204,13 +204,27 @@ __global__ void __launch_bounds__(256) k_project_bwd(
   const float4 q4 = quats[i];
   const float qn2 = q4.x * q4.x + q4.y * q4.y + q4.z * q4.z + q4.w * q4.w;
   float *gsh_i = gsh + (size_t)i * (K * 3);
+  // an SH row of K * 3 floats, stored as 16-byte vectors when it is a multiple of four
+  auto store_sh = [&](const float *row) {
+    if constexpr ((K * 3) % 4 == 0) {
+      float4 *g4 = reinterpret_cast<float4 *>(gsh_i);
+#pragma unroll
+      for (int j = 0; j < K * 3 / 4; j++)
+        g4[j] = make_float4(row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < K * 3; j++) gsh_i[j] = row[j];
+    }
+  };
   auto write_zero = [&]() {
     gmeans[3 * i] = gmeans[3 * i + 1] = gmeans[3 * i + 2] = 0.0f;
     gls[3 * i] = gls[3 * i + 1] = gls[3 * i + 2] = 0.0f;
     gquats[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     gopac[i] = 0.0f;
+    float zero[K * 3];
 #pragma unroll
-    for (int j = 0; j < K * 3; j++) gsh_i[j] = 0.0f;
+    for (int j = 0; j < K * 3; j++) zero[j] = 0.0f;
+    store_sh(zero);
   };
   if (!(tz > cam.znear) || !(tau > 0.0f) || !(qn2 > 0.0f)) {
     write_zero();
@@ -318,16 +332,28 @@ __global__ void __launch_bounds__(256) k_project_bwd(
   if (dn2 > 0.0f) {
     const float dinv = 1.0f / sqrtf(dn2);
     d0 *= dinv; d1 *= dinv; d2 *= dinv;
-    float Y[16], wk[16];
+    float Y[16], wk[16], row[K * 3], buf[K * 3];
     sh_eval(K, d0, d1, d2, Y);
     const float *shi = sh + (size_t)i * (K * 3);
+    if constexpr ((K * 3) % 4 == 0) {
+      const float4 *sh4 = reinterpret_cast<const float4 *>(shi);
+#pragma unroll
+      for (int j = 0; j < K * 3 / 4; j++) {
+        const float4 v4 = sh4[j];
+        buf[4 * j] = v4.x; buf[4 * j + 1] = v4.y; buf[4 * j + 2] = v4.z; buf[4 * j + 3] = v4.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K * 3; j++) buf[j] = shi[j];
+    }
 #pragma unroll
     for (int k = 0; k < K; k++) {
-      wk[k] = fmaf(shi[3 * k], gr, fmaf(shi[3 * k + 1], gg, shi[3 * k + 2] * gbl));
-      gsh_i[3 * k] = Y[k] * gr;
-      gsh_i[3 * k + 1] = Y[k] * gg;
-      gsh_i[3 * k + 2] = Y[k] * gbl;
+      wk[k] = fmaf(buf[3 * k], gr, fmaf(buf[3 * k + 1], gg, buf[3 * k + 2] * gbl));
+      row[3 * k] = Y[k] * gr;
+      row[3 * k + 1] = Y[k] * gg;
+      row[3 * k + 2] = Y[k] * gbl;
     }
+    store_sh(row);
     float e0 = 0.f, e1 = 0.f, e2 = 0.f;
     sh_grad_acc(K, d0, d1, d2, wk, e0, e1, e2);
     const float ed = e0 * d0 + e1 * d1 + e2 * d2;
@@ -335,8 +361,10 @@ __global__ void __launch_bounds__(256) k_project_bwd(
     g1 = fmaf(e1 - d1 * ed, dinv, g1);
     g2 = fmaf(e2 - d2 * ed, dinv, g2);
   } else {
+    float zero[K * 3];
 #pragma unroll
-    for (int j = 0; j < K * 3; j++) gsh_i[j] = 0.0f;
+    for (int j = 0; j < K * 3; j++) zero[j] = 0.0f;
+    store_sh(zero);
   }
   gmeans[3 * i] = g0;
   gmeans[3 * i + 1] = g1;

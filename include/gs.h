@@ -123,7 +123,9 @@ int32_t gs_project(int32_t n, const float *means, const float *log_scales, const
  *     the quaternion as given, not normalised), dL_dopacities [n],
  *     dL_dsh [n][(deg+1)^2][3] <- fully overwritten; rows of Gaussians that
  *     gs_project culls are 0.
- * quats and dL_dquats 16-byte aligned. */
+ * quats and dL_dquats 16-byte aligned; sh and dL_dsh 16-byte aligned for SH
+ * degrees 1 and 3 (rows of 12 and 48 floats, read and written as vectors),
+ * 4-byte aligned otherwise. */
 int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, const float *quats,
                        const float *opacities, const float *sh, int32_t sh_degree,
                        const gs_camera *cam, const float *dL_dsplat, float *dL_dmeans,
