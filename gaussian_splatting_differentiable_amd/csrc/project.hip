@@ -184,7 +184,9 @@ __device__ __forceinline__ void sh_grad_acc(int K, float x, float y, float z, co
 // opacity and SH coefficients ([LOAD-IMB] section 2.1 Eq. 1 differentiated;
 // [3DGS-CUDA] Step 3: dL/ds_k = Y_k(d) dL/dc plus the view-direction term).
 // The forward's intermediates are recomputed. tau and depth pass no gradient;
-// every output row is written (zeros for a culled Gaussian).
+// every output row is written (zeros for a culled Gaussian). A Gaussian no
+// pixel touched has an all-zero gradient row, hence all-zero outputs: its
+// parameters and SH are not read ([3DGS-CUDA] Step 4, touched-gating).
 template <int K>
 __global__ void __launch_bounds__(256) k_project_bwd(
     int n, const float *__restrict__ means, const float *__restrict__ log_scales,
@@ -194,15 +196,12 @@ __global__ void __launch_bounds__(256) k_project_bwd(
     float *__restrict__ gsh) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const float m0 = means[3 * i], m1 = means[3 * i + 1], m2 = means[3 * i + 2];
-  const float *R = cam.R;
-  const float tx = fmaf(R[0], m0, fmaf(R[1], m1, fmaf(R[2], m2, cam.t[0])));
-  const float ty = fmaf(R[3], m0, fmaf(R[4], m1, fmaf(R[5], m2, cam.t[1])));
-  const float tz = fmaf(R[6], m0, fmaf(R[7], m1, fmaf(R[8], m2, cam.t[2])));
-  const float o = opac[i];
-  const float tau = 2.0f * logf(255.0f * o);
-  const float4 q4 = quats[i];
-  const float qn2 = q4.x * q4.x + q4.y * q4.y + q4.z * q4.z + q4.w * q4.w;
+  float gsp[9];
+#pragma unroll
+  for (int j = 0; j < 9; j++) gsp[j] = dsplat[9 * (size_t)i + j];
+  bool touched = false;
+#pragma unroll
+  for (int j = 0; j < 9; j++) touched = touched || gsp[j] != 0.0f;
   float *gsh_i = gsh + (size_t)i * (K * 3);
   // an SH row of K * 3 floats, stored as 16-byte vectors when it is a multiple of four
   auto store_sh = [&](const float *row) {
@@ -226,6 +225,19 @@ __global__ void __launch_bounds__(256) k_project_bwd(
     for (int j = 0; j < K * 3; j++) zero[j] = 0.0f;
     store_sh(zero);
   };
+  if (!touched) {
+    write_zero();
+    return;
+  }
+  const float m0 = means[3 * i], m1 = means[3 * i + 1], m2 = means[3 * i + 2];
+  const float *R = cam.R;
+  const float tx = fmaf(R[0], m0, fmaf(R[1], m1, fmaf(R[2], m2, cam.t[0])));
+  const float ty = fmaf(R[3], m0, fmaf(R[4], m1, fmaf(R[5], m2, cam.t[1])));
+  const float tz = fmaf(R[6], m0, fmaf(R[7], m1, fmaf(R[8], m2, cam.t[2])));
+  const float o = opac[i];
+  const float tau = 2.0f * logf(255.0f * o);
+  const float4 q4 = quats[i];
+  const float qn2 = q4.x * q4.x + q4.y * q4.y + q4.z * q4.z + q4.w * q4.w;
   if (!(tz > cam.znear) || !(tau > 0.0f) || !(qn2 > 0.0f)) {
     write_zero();
     return;
@@ -267,7 +279,6 @@ __global__ void __launch_bounds__(256) k_project_bwd(
   }
   const float idet = 1.0f / det;
   const float ca = syy * idet, cb = -uv * idet, cc = sxx * idet;
-  const float *gsp = dsplat + 9 * (size_t)i;
   const float gmx = gsp[0], gmy = gsp[1], ga = gsp[2], gb = gsp[3], gc = gsp[4];
   // conic -> Sigma': dL/dSigma' = -Lambda G Lambda, G = [[ga, gb/2], [gb/2, gc]]
   const float p00 = fmaf(ca, ga, 0.5f * cb * gb), p01 = fmaf(0.5f * ca, gb, cb * gc);

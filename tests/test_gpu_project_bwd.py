@@ -39,13 +39,16 @@ def host(t):
 def _run(gsr, arrs, degree, cam, seed):
     means, ls, qs, op, sh = arrs
     n = means.shape[0]
-    g = np.random.default_rng(seed).normal(0, 1, (n, 9)).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    g = rng.normal(0, 1, (n, 9)).astype(np.float32)
+    g[rng.random(n) < 0.3] = 0.0     # Gaussians no pixel touched: zero rows in, zero rows out
     r = gsr.Rasterizer(cam, capacity=16)
     d = [dev(a) for a in arrs]
     splats = host(r.project(*d, degree)).copy()
     out = r.project_bwd(*d, degree, dL_dsplat=dev(g))
     gpu = {k: host(v) for k, v in out.items()}
     ref = oracle.project_bwd(means, ls, qs, op, sh, degree, cam, g)
+    ref["touched"] = np.any(g != 0, axis=1)
     rsplats = oracle.project(means, ls, qs, op, sh, degree, cam)
     return splats, rsplats, gpu, ref
 
@@ -59,6 +62,7 @@ def _check(splats, rsplats, gpu, ref, min_visible=0.5):
     for k in NAMES:
         g = gpu[k].reshape(len(gvis), -1)
         assert np.all(g[~gvis] == 0), k
+        assert np.all(g[~ref["touched"]] == 0), k
         a = g[both].astype(np.float64)
         b = ref[k].reshape(len(gvis), -1)[both]
         err = np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30)
