@@ -52,6 +52,8 @@ PROJ_BYTES_PER_GAUSSIAN = 44 + 48
 # when visible, and writes 44 B of parameter gradients and the SH gradient of
 # every Gaussian (zeros for culled ones).
 PROJ_BWD_BYTES_PER_GAUSSIAN = 44 + 36 + 44
+# With the SH coefficients stored as bf16 both read 6 B per coefficient instead
+# of 12; the SH gradient stays fp32.
 PEAK_FP32_TFLOPS = 157.3     # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0        # MI355X published HBM3E bandwidth
 # exp and reciprocal issue at a quarter of the fp32 lane rate:
@@ -231,28 +233,37 @@ def main():
     ms_min = {s: float(np.min(v)) for s, v in per.items()}
     ms_step = t_wall * 1e3 / args.steps
 
-    # the feeder, in its own loop
-    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    for k in range(args.steps):
-        pe[2 * k].record(stream)
-        gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats)
-        pe[2 * k + 1].record(stream)
-    torch.cuda.synchronize()
-    per["project"] = [pe[2 * k].elapsed_time(pe[2 * k + 1]) for k in range(args.steps)]
-    ms_project = float(np.median(per["project"]))
-    # the projection's backward (the next stage of a training step), in its own loop
-    pb = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    def launch_times(call):
+        """Per-launch milliseconds of `call` over args.steps launches (HIP events
+        on the stream it runs on), after one untimed launch."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+        call()
+        for k in range(args.steps):
+            ev[2 * k].record(stream)
+            call()
+            ev[2 * k + 1].record(stream)
+        torch.cuda.synchronize()
+        return [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]
+
+    # the feeder and the projection's backward (the next stage of a training
+    # step), each in its own loop; then both with the SH coefficients stored as
+    # bf16 (the same values rounded to nearest even), the splats restored after
     K = (sc.sh_degree + 1) ** 2
     pgrads = [torch.empty(shape, dtype=torch.float32, device=dev)
               for shape in ((n, 3), (n, 3), (n, 4), (n,), (n, K, 3))]
-    for k in range(args.steps + 1):
-        if k:
-            pb[2 * k - 2].record(stream)
-        gsr.gs_project_bwd(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.grads, *pgrads)
-        if k:
-            pb[2 * k - 1].record(stream)
-    torch.cuda.synchronize()
-    per["project_bwd"] = [pb[2 * k].elapsed_time(pb[2 * k + 1]) for k in range(args.steps)]
+    sh16 = sh.to(torch.bfloat16)
+    per["project"] = launch_times(
+        lambda: gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats))
+    per["project_bwd"] = launch_times(
+        lambda: gsr.gs_project_bwd(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.grads,
+                                   *pgrads))
+    per["project_bf16sh"] = launch_times(
+        lambda: gsr.gs_project_bf16sh(n, means, ls, qs, op, sh16, sc.sh_degree, r.cam, r.splats))
+    per["project_bwd_bf16sh"] = launch_times(
+        lambda: gsr.gs_project_bwd_bf16sh(n, means, ls, qs, op, sh16, sc.sh_degree, r.cam,
+                                          r.grads, *pgrads))
+    gsr.gs_project(n, means, ls, qs, op, sh, sc.sh_degree, r.cam, r.splats)
+    ms_project = float(np.median(per["project"]))
     ms_project_bwd = float(np.median(per["project_bwd"]))
     n_vis = int((r.splats[:, 9] > 0).sum().item())
 
@@ -293,6 +304,11 @@ def main():
                         bytes=PROJ_BYTES_PER_GAUSSIAN * n + sh_bytes * n_vis),
         "project_bwd": dict(flops=0, trans=0,
                             bytes=(PROJ_BWD_BYTES_PER_GAUSSIAN + sh_bytes) * n + sh_bytes * n_vis),
+        "project_bf16sh": dict(flops=0, trans=0,
+                               bytes=PROJ_BYTES_PER_GAUSSIAN * n + sh_bytes // 2 * n_vis),
+        "project_bwd_bf16sh": dict(flops=0, trans=0,
+                                   bytes=(PROJ_BWD_BYTES_PER_GAUSSIAN + sh_bytes) * n
+                                   + sh_bytes // 2 * n_vis),
         "bin": dict(flops=0, trans=0, bytes=BIN_BYTES_PER_GAUSSIAN * n),
         "sort": dict(flops=0, trans=0,
                      bytes=SORT_BYTES_PER_PAIR * npairs + SORT_BYTES_PER_TILE * cam.num_tiles),

@@ -25,7 +25,7 @@ GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED = -3, -4, -5
 SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
 
 EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_project_bwd",
-           "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
+           "gs_project_bf16sh", "gs_project_bwd_bf16sh", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
            "gs_timing_read")
 
 
@@ -65,13 +65,16 @@ def lib():
     L.gs_fwd_state_size.argtypes, L.gs_fwd_state_size.restype = [i32, i32], sz
     L.gs_project.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P]
     L.gs_project_bwd.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P, P, P, P, P, P]
+    L.gs_project_bf16sh.argtypes = L.gs_project.argtypes
+    L.gs_project_bwd_bf16sh.argtypes = L.gs_project_bwd.argtypes
     L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, sz, P]
     L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, sz, P]
     L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
     L.gs_timing_start.argtypes = []
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
-    for name in ("gs_project", "gs_project_bwd", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
+    for name in ("gs_project", "gs_project_bwd", "gs_project_bf16sh", "gs_project_bwd_bf16sh",
+                 "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
@@ -150,6 +153,25 @@ def gs_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, cam, d
                                 _ptr(dL_dquats), _ptr(dL_dopacities), _ptr(dL_dsh),
                                 _stream(stream)),
            "gs_project_bwd")
+
+
+def gs_project_bf16sh(n, means, log_scales, quats, opacities, sh, sh_degree, cam, splats,
+                      stream=None):
+    _check(lib().gs_project_bf16sh(int(n), _ptr(means), _ptr(log_scales), _ptr(quats),
+                                   _ptr(opacities), _ptr(sh), int(sh_degree), C.byref(cam),
+                                   _ptr(splats), _stream(stream)),
+           "gs_project_bf16sh")
+
+
+def gs_project_bwd_bf16sh(n, means, log_scales, quats, opacities, sh, sh_degree, cam, dL_dsplat,
+                          dL_dmeans, dL_dlog_scales, dL_dquats, dL_dopacities, dL_dsh,
+                          stream=None):
+    _check(lib().gs_project_bwd_bf16sh(int(n), _ptr(means), _ptr(log_scales), _ptr(quats),
+                                       _ptr(opacities), _ptr(sh), int(sh_degree), C.byref(cam),
+                                       _ptr(dL_dsplat), _ptr(dL_dmeans), _ptr(dL_dlog_scales),
+                                       _ptr(dL_dquats), _ptr(dL_dopacities), _ptr(dL_dsh),
+                                       _stream(stream)),
+           "gs_project_bwd_bf16sh")
 
 
 def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace, stream=None):
@@ -249,9 +271,11 @@ class Rasterizer:
             self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
     def project(self, means, log_scales, quats, opacities, sh, sh_degree):
+        """sh as float32, or as bfloat16 (then gs_project_bf16sh reads its bits)."""
         n = int(means.shape[0])
         self._ensure(n, self.capacity)
-        gs_project(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, self.splats)
+        call = gs_project_bf16sh if sh.dtype == torch.bfloat16 else gs_project
+        call(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, self.splats)
         return self.splats[:n]
 
     def bin_and_sort(self, n, want_keys=False, want_emission=False):
@@ -297,6 +321,7 @@ class Rasterizer:
                    quats=torch.empty((n, 4), dtype=torch.float32, device=dev),
                    opacities=torch.empty(n, dtype=torch.float32, device=dev),
                    sh=torch.empty((n, K, 3), dtype=torch.float32, device=dev))
-        gs_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, dsp,
-                       out["means"], out["log_scales"], out["quats"], out["opacities"], out["sh"])
+        call = gs_project_bwd_bf16sh if sh.dtype == torch.bfloat16 else gs_project_bwd
+        call(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, dsp,
+             out["means"], out["log_scales"], out["quats"], out["opacities"], out["sh"])
         return out

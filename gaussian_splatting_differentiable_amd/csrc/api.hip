@@ -7,13 +7,13 @@
 #include "render_common.h"
 
 hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
-                             const float *opac, const float *sh, int degree, const CamK &cam,
-                             float *splats, hipStream_t st);
+                             const float *opac, const void *sh, bool sh_bf16, int degree,
+                             const CamK &cam, float *splats, hipStream_t st);
 hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_scales,
-                                 const float *quats, const float *opac, const float *sh,
-                                 int degree, const CamK &cam, const float *dsplat, float *gmeans,
-                                 float *gls, float *gquats, float *gopac, float *gsh,
-                                 hipStream_t st);
+                                 const float *quats, const float *opac, const void *sh,
+                                 bool sh_bf16, int degree, const CamK &cam, const float *dsplat,
+                                 float *gmeans, float *gls, float *gquats, float *gopac,
+                                 float *gsh, hipStream_t st);
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
                          int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
                          hipStream_t st);
@@ -111,6 +111,47 @@ gs_sched default_sched() {
   return s;
 }
 
+// Byte alignment the SH rows of one Gaussian are read with: fp32 rows of 12 or
+// 48 floats (degrees 1, 3) as 16-byte vectors; bf16 rows of 48 values
+// (degree 3) as 16-byte and of 12 (degree 1) as 8-byte vectors; else scalars.
+size_t sh_align(int degree, bool bf16) {
+  const int e = 3 * (degree + 1) * (degree + 1);
+  if (!bf16) return e % 4 == 0 ? 16 : 4;
+  return e % 8 == 0 ? 16 : e % 4 == 0 ? 8 : 2;
+}
+
+int32_t project_impl(int32_t n, const float *means, const float *log_scales, const float *quats,
+                     const float *opacities, const void *sh, bool bf16, int32_t sh_degree,
+                     const gs_camera *cam, float *splats, void *stream) {
+  CamK k;
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GS_OK;
+  if (!means || !log_scales || !quats || !opacities || !sh || !splats) return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(quats, 16) || !aligned(splats, 16) || !aligned(sh, sh_align(sh_degree, bf16)))
+    return GS_ERR_INVALID_ARGUMENT;
+  return hip_status(gs_launch_project(n, means, log_scales, quats, opacities, sh, bf16, sh_degree,
+                                      k, splats, (hipStream_t)stream));
+}
+
+int32_t project_bwd_impl(int32_t n, const float *means, const float *log_scales,
+                         const float *quats, const float *opacities, const void *sh, bool bf16,
+                         int32_t sh_degree, const gs_camera *cam, const float *dL_dsplat,
+                         float *dL_dmeans, float *dL_dlog_scales, float *dL_dquats,
+                         float *dL_dopacities, float *dL_dsh, void *stream) {
+  CamK k;
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GS_OK;
+  if (!means || !log_scales || !quats || !opacities || !sh || !dL_dsplat || !dL_dmeans ||
+      !dL_dlog_scales || !dL_dquats || !dL_dopacities || !dL_dsh)
+    return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(quats, 16) || !aligned(dL_dquats, 16) || !aligned(sh, sh_align(sh_degree, bf16)) ||
+      !aligned(dL_dsh, sh_align(sh_degree, false)))
+    return GS_ERR_INVALID_ARGUMENT;
+  return hip_status(gs_launch_project_bwd(n, means, log_scales, quats, opacities, sh, bf16,
+                                          sh_degree, k, dL_dsplat, dL_dmeans, dL_dlog_scales,
+                                          dL_dquats, dL_dopacities, dL_dsh, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,13 +181,15 @@ size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_
 int32_t gs_project(int32_t n, const float *means, const float *log_scales, const float *quats,
                    const float *opacities, const float *sh, int32_t sh_degree, const gs_camera *cam,
                    float *splats, void *stream) {
-  CamK k;
-  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
-  if (n == 0) return GS_OK;
-  if (!means || !log_scales || !quats || !opacities || !sh || !splats) return GS_ERR_INVALID_ARGUMENT;
-  if (!aligned(quats, 16) || !aligned(splats, 16) || !aligned(sh, 4)) return GS_ERR_INVALID_ARGUMENT;
-  return hip_status(gs_launch_project(n, means, log_scales, quats, opacities, sh, sh_degree, k,
-                                      splats, (hipStream_t)stream));
+  return project_impl(n, means, log_scales, quats, opacities, sh, false, sh_degree, cam, splats,
+                      stream);
+}
+
+int32_t gs_project_bf16sh(int32_t n, const float *means, const float *log_scales,
+                          const float *quats, const float *opacities, const uint16_t *sh,
+                          int32_t sh_degree, const gs_camera *cam, float *splats, void *stream) {
+  return project_impl(n, means, log_scales, quats, opacities, sh, true, sh_degree, cam, splats,
+                      stream);
 }
 
 int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, const float *quats,
@@ -154,19 +197,19 @@ int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, c
                        const gs_camera *cam, const float *dL_dsplat, float *dL_dmeans,
                        float *dL_dlog_scales, float *dL_dquats, float *dL_dopacities,
                        float *dL_dsh, void *stream) {
-  CamK k;
-  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
-  if (n == 0) return GS_OK;
-  if (!means || !log_scales || !quats || !opacities || !sh || !dL_dsplat || !dL_dmeans ||
-      !dL_dlog_scales || !dL_dquats || !dL_dopacities || !dL_dsh)
-    return GS_ERR_INVALID_ARGUMENT;
-  const bool rows16 = (3 * (sh_degree + 1) * (sh_degree + 1)) % 4 == 0;  // degrees 1 and 3
-  if (!aligned(quats, 16) || !aligned(dL_dquats, 16) || !aligned(sh, rows16 ? 16 : 4) ||
-      !aligned(dL_dsh, rows16 ? 16 : 4))
-    return GS_ERR_INVALID_ARGUMENT;
-  return hip_status(gs_launch_project_bwd(n, means, log_scales, quats, opacities, sh, sh_degree, k,
-                                          dL_dsplat, dL_dmeans, dL_dlog_scales, dL_dquats,
-                                          dL_dopacities, dL_dsh, (hipStream_t)stream));
+  return project_bwd_impl(n, means, log_scales, quats, opacities, sh, false, sh_degree, cam,
+                          dL_dsplat, dL_dmeans, dL_dlog_scales, dL_dquats, dL_dopacities, dL_dsh,
+                          stream);
+}
+
+int32_t gs_project_bwd_bf16sh(int32_t n, const float *means, const float *log_scales,
+                              const float *quats, const float *opacities, const uint16_t *sh,
+                              int32_t sh_degree, const gs_camera *cam, const float *dL_dsplat,
+                              float *dL_dmeans, float *dL_dlog_scales, float *dL_dquats,
+                              float *dL_dopacities, float *dL_dsh, void *stream) {
+  return project_bwd_impl(n, means, log_scales, quats, opacities, sh, true, sh_degree, cam,
+                          dL_dsplat, dL_dmeans, dL_dlog_scales, dL_dquats, dL_dopacities, dL_dsh,
+                          stream);
 }
 
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,

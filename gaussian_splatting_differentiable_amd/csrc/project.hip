@@ -40,12 +40,63 @@ __device__ __forceinline__ void sh_eval(int K, float x, float y, float z, float 
   Y[15] = 0.5900435899266435f * x * (xx - 3.0f * yy);
 }
 
+// One Gaussian's K x 3 SH coefficients into fp32 registers. Stored as fp32 (read
+// as 16-byte vectors when the row is a multiple of four floats) or as bf16 bits
+// (widened exactly: the 16 bits are the high half of the fp32 word; read as 16-
+// or 8-byte vectors when the row allows).
 template <int K>
+__device__ __forceinline__ void load_sh_row(const float *shi, float *buf) {
+  if constexpr ((K * 3) % 4 == 0) {
+    const float4 *sh4 = reinterpret_cast<const float4 *>(shi);
+#pragma unroll
+    for (int j = 0; j < K * 3 / 4; j++) {
+      const float4 v4 = sh4[j];
+      buf[4 * j] = v4.x; buf[4 * j + 1] = v4.y; buf[4 * j + 2] = v4.z; buf[4 * j + 3] = v4.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K * 3; j++) buf[j] = shi[j];
+  }
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+template <int K>
+__device__ __forceinline__ void load_sh_row(const uint16_t *shi, float *buf) {
+  if constexpr ((K * 3) % 8 == 0) {
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(shi);
+#pragma unroll
+    for (int j = 0; j < K * 3 / 8; j++) {
+      const uint4 v = s4[j];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        buf[8 * j + 2 * h] = bf16_to_f32(w[h] & 0xFFFFu);
+        buf[8 * j + 2 * h + 1] = bf16_to_f32(w[h] >> 16);
+      }
+    }
+  } else if constexpr ((K * 3) % 4 == 0) {
+    const uint2 *s2 = reinterpret_cast<const uint2 *>(shi);
+#pragma unroll
+    for (int j = 0; j < K * 3 / 4; j++) {
+      const uint2 v = s2[j];
+      buf[4 * j] = bf16_to_f32(v.x & 0xFFFFu);
+      buf[4 * j + 1] = bf16_to_f32(v.x >> 16);
+      buf[4 * j + 2] = bf16_to_f32(v.y & 0xFFFFu);
+      buf[4 * j + 3] = bf16_to_f32(v.y >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K * 3; j++) buf[j] = bf16_to_f32(shi[j]);
+  }
+}
+
+template <int K, typename ShT>
 __global__ void __launch_bounds__(256) k_project(int n, const float *__restrict__ means,
                                                  const float *__restrict__ log_scales,
                                                  const float4 *__restrict__ quats,
                                                  const float *__restrict__ opac,
-                                                 const float *__restrict__ sh, CamK cam,
+                                                 const ShT *__restrict__ sh, CamK cam,
                                                  Splat *__restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -117,30 +168,14 @@ __global__ void __launch_bounds__(256) k_project(int n, const float *__restrict_
   if (dn2 > 0.0f) {
     const float dinv = 1.0f / sqrtf(dn2);
     d0 *= dinv; d1 *= dinv; d2 *= dinv;
-    float Y[16];
+    float Y[16], buf[K * 3];
     sh_eval(K, d0, d1, d2, Y);
-    const float *shi = sh + (size_t)i * (K * 3);
-    if constexpr ((K * 3) % 4 == 0) {
-      const float4 *sh4 = reinterpret_cast<const float4 *>(shi);
-      float buf[K * 3];
+    load_sh_row<K>(sh + (size_t)i * (K * 3), buf);
 #pragma unroll
-      for (int j = 0; j < K * 3 / 4; j++) {
-        const float4 v4 = sh4[j];
-        buf[4 * j] = v4.x; buf[4 * j + 1] = v4.y; buf[4 * j + 2] = v4.z; buf[4 * j + 3] = v4.w;
-      }
-#pragma unroll
-      for (int k = 0; k < K; k++) {
-        rgb[0] = fmaf(Y[k], buf[3 * k], rgb[0]);
-        rgb[1] = fmaf(Y[k], buf[3 * k + 1], rgb[1]);
-        rgb[2] = fmaf(Y[k], buf[3 * k + 2], rgb[2]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; k++) {
-        rgb[0] = fmaf(Y[k], shi[3 * k], rgb[0]);
-        rgb[1] = fmaf(Y[k], shi[3 * k + 1], rgb[1]);
-        rgb[2] = fmaf(Y[k], shi[3 * k + 2], rgb[2]);
-      }
+    for (int k = 0; k < K; k++) {
+      rgb[0] = fmaf(Y[k], buf[3 * k], rgb[0]);
+      rgb[1] = fmaf(Y[k], buf[3 * k + 1], rgb[1]);
+      rgb[2] = fmaf(Y[k], buf[3 * k + 2], rgb[2]);
     }
   }
   s.p0 = make_float4(fmaf(cam.fx, ux, cam.cx), fmaf(cam.fy, uy, cam.cy), syy * idet, -uv * idet);
@@ -187,10 +222,10 @@ __device__ __forceinline__ void sh_grad_acc(int K, float x, float y, float z, co
 // every output row is written (zeros for a culled Gaussian). A Gaussian no
 // pixel touched has an all-zero gradient row, hence all-zero outputs: its
 // parameters and SH are not read ([3DGS-CUDA] Step 4, touched-gating).
-template <int K>
+template <int K, typename ShT>
 __global__ void __launch_bounds__(256) k_project_bwd(
     int n, const float *__restrict__ means, const float *__restrict__ log_scales,
-    const float4 *__restrict__ quats, const float *__restrict__ opac, const float *__restrict__ sh,
+    const float4 *__restrict__ quats, const float *__restrict__ opac, const ShT *__restrict__ sh,
     CamK cam, const float *__restrict__ dsplat, float *__restrict__ gmeans,
     float *__restrict__ gls, float4 *__restrict__ gquats, float *__restrict__ gopac,
     float *__restrict__ gsh) {
@@ -345,18 +380,7 @@ __global__ void __launch_bounds__(256) k_project_bwd(
     d0 *= dinv; d1 *= dinv; d2 *= dinv;
     float Y[16], wk[16], row[K * 3], buf[K * 3];
     sh_eval(K, d0, d1, d2, Y);
-    const float *shi = sh + (size_t)i * (K * 3);
-    if constexpr ((K * 3) % 4 == 0) {
-      const float4 *sh4 = reinterpret_cast<const float4 *>(shi);
-#pragma unroll
-      for (int j = 0; j < K * 3 / 4; j++) {
-        const float4 v4 = sh4[j];
-        buf[4 * j] = v4.x; buf[4 * j + 1] = v4.y; buf[4 * j + 2] = v4.z; buf[4 * j + 3] = v4.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < K * 3; j++) buf[j] = shi[j];
-    }
+    load_sh_row<K>(sh + (size_t)i * (K * 3), buf);
 #pragma unroll
     for (int k = 0; k < K; k++) {
       wk[k] = fmaf(buf[3 * k], gr, fmaf(buf[3 * k + 1], gg, buf[3 * k + 2] * gbl));
@@ -382,38 +406,63 @@ __global__ void __launch_bounds__(256) k_project_bwd(
   gmeans[3 * i + 2] = g2;
 }
 
-}  // namespace
 
-hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_scales,
-                                 const float *quats, const float *opac, const float *sh,
-                                 int degree, const CamK &cam, const float *dsplat, float *gmeans,
-                                 float *gls, float *gquats, float *gopac, float *gsh,
-                                 hipStream_t st) {
+template <typename ShT>
+hipError_t launch_project_bwd(int n, const float *means, const float *log_scales,
+                              const float *quats, const float *opac, const ShT *sh, int degree,
+                              const CamK &cam, const float *dsplat, float *gmeans, float *gls,
+                              float *gquats, float *gopac, float *gsh, hipStream_t st) {
   if (n == 0) return hipSuccess;
   dim3 grid(gs_div_up(n, 256)), block(256);
   const float4 *q4 = reinterpret_cast<const float4 *>(quats);
   float4 *gq4 = reinterpret_cast<float4 *>(gquats);
   switch (degree) {
-    case 0: hipLaunchKernelGGL(k_project_bwd<1>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
-    case 1: hipLaunchKernelGGL(k_project_bwd<4>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
-    case 2: hipLaunchKernelGGL(k_project_bwd<9>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
-    default: hipLaunchKernelGGL(k_project_bwd<16>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    case 0: hipLaunchKernelGGL((k_project_bwd<1, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    case 1: hipLaunchKernelGGL((k_project_bwd<4, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    case 2: hipLaunchKernelGGL((k_project_bwd<9, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    default: hipLaunchKernelGGL((k_project_bwd<16, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
   }
   return hipGetLastError();
 }
 
-hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
-                             const float *opac, const float *sh, int degree, const CamK &cam,
-                             float *splats, hipStream_t st) {
+template <typename ShT>
+hipError_t launch_project(int n, const float *means, const float *log_scales, const float *quats,
+                          const float *opac, const ShT *sh, int degree, const CamK &cam,
+                          float *splats, hipStream_t st) {
   if (n == 0) return hipSuccess;
   dim3 grid(gs_div_up(n, 256)), block(256);
   const float4 *q4 = reinterpret_cast<const float4 *>(quats);
   Splat *out = reinterpret_cast<Splat *>(splats);
   switch (degree) {
-    case 0: hipLaunchKernelGGL(k_project<1>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
-    case 1: hipLaunchKernelGGL(k_project<4>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
-    case 2: hipLaunchKernelGGL(k_project<9>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
-    default: hipLaunchKernelGGL(k_project<16>, grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
+    case 0: hipLaunchKernelGGL((k_project<1, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
+    case 1: hipLaunchKernelGGL((k_project<4, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
+    case 2: hipLaunchKernelGGL((k_project<9, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
+    default: hipLaunchKernelGGL((k_project<16, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, out); break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// SH stored as fp32 (sh_bf16 == false) or as bf16 bits (true).
+hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
+                             const float *opac, const void *sh, bool sh_bf16, int degree,
+                             const CamK &cam, float *splats, hipStream_t st) {
+  return sh_bf16 ? launch_project(n, means, log_scales, quats, opac,
+                                  static_cast<const uint16_t *>(sh), degree, cam, splats, st)
+                 : launch_project(n, means, log_scales, quats, opac, static_cast<const float *>(sh),
+                                  degree, cam, splats, st);
+}
+
+hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_scales,
+                                 const float *quats, const float *opac, const void *sh,
+                                 bool sh_bf16, int degree, const CamK &cam, const float *dsplat,
+                                 float *gmeans, float *gls, float *gquats, float *gopac,
+                                 float *gsh, hipStream_t st) {
+  return sh_bf16 ? launch_project_bwd(n, means, log_scales, quats, opac,
+                                      static_cast<const uint16_t *>(sh), degree, cam, dsplat,
+                                      gmeans, gls, gquats, gopac, gsh, st)
+                 : launch_project_bwd(n, means, log_scales, quats, opac,
+                                      static_cast<const float *>(sh), degree, cam, dsplat, gmeans,
+                                      gls, gquats, gopac, gsh, st);
 }

@@ -132,6 +132,25 @@ int32_t gs_project_bwd(int32_t n, const float *means, const float *log_scales, c
                        float *dL_dlog_scales, float *dL_dquats, float *dL_dopacities,
                        float *dL_dsh, void *stream);
 
+/* gs_project and gs_project_bwd with the SH coefficients stored as bfloat16
+ * (Step 3 and Step 6 of the literature page keep the SH parameters in bf16 to
+ * halve their bytes): sh [n][(deg+1)^2][3] holds the upper 16 bits of each
+ * fp32 value (bf16 bit patterns). Each value is widened exactly to fp32 in
+ * registers and all arithmetic is fp32, so the results equal those of
+ * gs_project / gs_project_bwd called with the widened coefficients, bit for
+ * bit. dL_dsh stays fp32 (same layout and alignment as for gs_project_bwd).
+ * sh 16-byte aligned for SH degree 3 (rows of 48 values, read as 16-byte
+ * vectors), 8-byte aligned for degree 1 (rows of 12), 2-byte aligned for
+ * degrees 0 and 2. Other arguments, outputs and errors as for the fp32 calls. */
+int32_t gs_project_bf16sh(int32_t n, const float *means, const float *log_scales,
+                          const float *quats, const float *opacities, const uint16_t *sh,
+                          int32_t sh_degree, const gs_camera *cam, float *splats, void *stream);
+int32_t gs_project_bwd_bf16sh(int32_t n, const float *means, const float *log_scales,
+                              const float *quats, const float *opacities, const uint16_t *sh,
+                              int32_t sh_degree, const gs_camera *cam, const float *dL_dsplat,
+                              float *dL_dmeans, float *dL_dlog_scales, float *dL_dquats,
+                              float *dL_dopacities, float *dL_dsh, void *stream);
+
 /* Exact opacity-aware conic-tile binning (Step 1 (b) of the literature page).
  * A tile is emitted for splat i when the ellipse q <= tau (1 + 2^-10) meets the
  * tile's pixel-sample hull widened by 2^-8 px; spans are solved per tile row

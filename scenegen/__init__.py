@@ -285,3 +285,16 @@ def random_scene(seed: int, n: int, width: int, height: int, f: float,
     cam = pinhole(width, height, f)
     return _finish(f"random{seed}", st, m, log_scale[0], log_scale[1],
                    opacity[0], opacity[1], degree, cam)
+
+
+def to_bf16(x):
+    """Round fp32 values to bfloat16, nearest with ties to even (the IEEE rule):
+    returns the 16-bit patterns (uint16, the upper half of the fp32 word) and
+    the same values widened back to fp32 exactly. NaNs keep a set quiet bit."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = np.where(nan, (u >> 16) | 0x40, r).astype(np.uint16)
+    wide = (r.astype(np.uint32) << 16).view(np.float32)
+    return r.reshape(np.shape(x)), wide.reshape(np.shape(x))

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "gs.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gs_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gs_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -64,6 +64,18 @@ def test_argument_validation_needs_no_gpu(gsr):
     assert L.gs_project_bwd(1, p16, p16, C.c_void_p(20), p16, p16, 0, C.byref(cam), p16, p16, p16,
                             p16, p16, p16, None) == -1
     assert L.gs_project_bwd(0, None, None, None, None, None, 0, C.byref(cam), *nul, None) == 0
+    # bf16 SH: rows of degree 3 need 16-byte, of degree 1 8-byte, else 2-byte alignment
+    for deg, addr in ((3, 24), (1, 20), (0, 17), (2, 33)):
+        sh = C.c_void_p(addr)
+        assert L.gs_project_bf16sh(1, p16, p16, p16, p16, sh, deg, C.byref(cam), p16, None) == -1
+        assert L.gs_project_bwd_bf16sh(1, p16, p16, p16, p16, sh, deg, C.byref(cam), p16, p16,
+                                       p16, p16, p16, p16, None) == -1
+    # the SH gradient stays fp32: 16-byte aligned rows for degrees 1 and 3
+    assert L.gs_project_bwd_bf16sh(1, p16, p16, p16, p16, p16, 3, C.byref(cam), p16, p16, p16,
+                                   p16, p16, C.c_void_p(24), None) == -1
+    assert L.gs_project_bf16sh(-1, None, None, None, None, None, 0, C.byref(cam), None, None) == -1
+    assert L.gs_project_bwd_bf16sh(0, None, None, None, None, None, 0, C.byref(cam), *nul,
+                                   None) == 0
     big = gsr.GsCamera()
     big.width, big.height, big.fx, big.fy = 1 << 14, 1 << 14, 1.0, 1.0
     assert L.gs_bin_tiles(1, C.c_void_p(16), C.byref(big), 10, C.c_void_p(16), C.c_void_p(16),

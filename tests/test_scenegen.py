@@ -59,3 +59,25 @@ def test_room_and_urban_shapes():
     assert u.means[:, 2].min() >= 2.0 and u.means[:, 2].max() <= 200.0
     lg = _logit(u.opacities)
     assert abs(lg.std() - np.sqrt(2.0)) < 0.01
+
+
+def test_bf16_rounding_is_ieee_nearest_even():
+    # known patterns, the two tie directions, and the carry into the exponent
+    x = np.array([1.0, -2.0, 0.5, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20,
+                  2 - 2 ** -9, 0.0, -0.0, np.inf, 3.0e38], dtype=np.float32)
+    bits, wide = scenegen.to_bf16(x)
+    assert list(bits) == [0x3F80, 0xC000, 0x3F00, 0x3F80, 0x3F82, 0x3F81, 0x4000, 0, 0x8000,
+                          0x7F80, 0x7F62]
+    big = np.array([0x7F620000], dtype=np.uint32).view(np.float32)[0]
+    np.testing.assert_array_equal(wide, np.array([1.0, -2.0, 0.5, 1.0, 1 + 2 ** -6, 1 + 2 ** -7,
+                                                  2.0, 0.0, -0.0, np.inf, big], dtype=np.float32))
+    assert np.signbit(wide[8])
+    # within half a bf16 ulp, and the same as torch's conversion on random data
+    rng = np.random.default_rng(5)
+    y = rng.normal(0, 0.3, 100_000).astype(np.float32)
+    b, w = scenegen.to_bf16(y)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(y).astype(np.float64))[1] - 8)
+    assert np.all(np.abs(w.astype(np.float64) - y) <= 0.5 * ulp)
+    torch = pytest.importorskip("torch")
+    tb = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(b, tb)
