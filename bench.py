@@ -47,11 +47,14 @@ BIN_BYTES_PER_GAUSSIAN = 52
 SORT_BYTES_PER_PAIR = 28
 SORT_BYTES_PER_TILE = 8
 PROJ_BYTES_PER_GAUSSIAN = 44 + 48
-# The projection's backward reads the 44 B of parameters and the 36 B of
-# screen-space gradients of every Gaussian and its SH (12 B per coefficient)
-# when visible, and writes 44 B of parameter gradients and the SH gradient of
-# every Gaussian (zeros for culled ones).
-PROJ_BWD_BYTES_PER_GAUSSIAN = 44 + 36 + 44
+# The projection's backward reads the 36 B of screen-space gradients of every
+# Gaussian, the 44 B of parameters of every Gaussian whose gradient row is not
+# all zero (a Gaussian no pixel touched has zero gradients throughout) and its
+# SH (12 B per coefficient) when it is also visible, and writes 44 B of
+# parameter gradients and the SH gradient of every Gaussian (zeros for culled
+# and untouched ones).
+PROJ_BWD_BYTES_PER_GAUSSIAN = 36 + 44
+PROJ_BWD_BYTES_PER_TOUCHED = 44
 # With the SH coefficients stored as bf16 both read 6 B per coefficient instead
 # of 12; the SH gradient stays fp32.
 PEAK_FP32_TFLOPS = 157.3     # MI355X published fp32 vector peak
@@ -266,6 +269,9 @@ def main():
     ms_project = float(np.median(per["project"]))
     ms_project_bwd = float(np.median(per["project_bwd"]))
     n_vis = int((r.splats[:, 9] > 0).sum().item())
+    touched = (r.grads[:n] != 0).any(dim=1)
+    n_touched = int(touched.sum().item())
+    n_touched_vis = int((touched & (r.splats[:n, 9] > 0)).sum().item())
 
     # roofline of the longest raster kernel: algorithmic bytes and flops per launch
     P = cam.width * cam.height
@@ -303,12 +309,14 @@ def main():
         "project": dict(flops=0, trans=0,
                         bytes=PROJ_BYTES_PER_GAUSSIAN * n + sh_bytes * n_vis),
         "project_bwd": dict(flops=0, trans=0,
-                            bytes=(PROJ_BWD_BYTES_PER_GAUSSIAN + sh_bytes) * n + sh_bytes * n_vis),
+                            bytes=(PROJ_BWD_BYTES_PER_GAUSSIAN + sh_bytes) * n
+                            + PROJ_BWD_BYTES_PER_TOUCHED * n_touched + sh_bytes * n_touched_vis),
         "project_bf16sh": dict(flops=0, trans=0,
                                bytes=PROJ_BYTES_PER_GAUSSIAN * n + sh_bytes // 2 * n_vis),
         "project_bwd_bf16sh": dict(flops=0, trans=0,
                                    bytes=(PROJ_BWD_BYTES_PER_GAUSSIAN + sh_bytes) * n
-                                   + sh_bytes // 2 * n_vis),
+                                   + PROJ_BWD_BYTES_PER_TOUCHED * n_touched
+                                   + sh_bytes // 2 * n_touched_vis),
         "bin": dict(flops=0, trans=0, bytes=BIN_BYTES_PER_GAUSSIAN * n),
         "sort": dict(flops=0, trans=0,
                      bytes=SORT_BYTES_PER_PAIR * npairs + SORT_BYTES_PER_TILE * cam.num_tiles),
@@ -357,7 +365,7 @@ def main():
         "ms_fwd": round(ms_fwd_total, 4), "ms_bwd": round(ms["bwd"], 4),
         "ms_fwd_bwd": round(ms_fwd_total + ms["bwd"], 4),
         "ms_frame": round(ms_project + ms_fwd_total + ms["bwd"], 4),
-        "n_visible": n_vis,
+        "n_visible": n_vis, "n_touched": n_touched, "n_touched_visible": n_touched_vis,
         "stages": stage_lines,
         "roofline": roofline,
         "cpu_baseline": cpu,

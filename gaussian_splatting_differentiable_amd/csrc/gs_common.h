@@ -31,6 +31,14 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // the ballot, with no round trip through a 0/1 vector register).
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// Orders this wave's LDS stores before its later LDS loads (and the reverse),
+// for LDS that only this wave uses: no workgroup barrier is needed.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Value of v in the first active lane, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_first(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

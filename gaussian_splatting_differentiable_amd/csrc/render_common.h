@@ -172,13 +172,6 @@ __device__ __forceinline__ int wave_in_block() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x / GS_WAVE);
 }
 
-// Orders this wave's LDS stores before its later LDS loads (and the reverse):
-// the workers of a workgroup never share LDS, so no workgroup barrier is needed.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Wave-uniform queue pop: one lane advances the head, every lane gets the ticket.
 __device__ __forceinline__ int queue_pop(int32_t *head) {

@@ -72,10 +72,10 @@ def _load():
         "or_bin_emit": [i32, P, i32, i32, P, P, P],
         "or_sort_pairs": [i64, P, P, P, P],
         "or_tile_ranges": [i64, P, i32, P],
-        "or_render_fwd": [P, P, P, i32, i32, P, P, P, P, P, P],
+        "or_render_fwd": [P, P, P, i32, i32, P, P, P, P, P, P, P],
         "or_render_fwd_untiled": [i32, P, i32, i32, P, P],
-        "or_render_fwd_values": [P, P, P, P, i32, i32, P, P, P],
-        "or_render_bwd": [P, P, P, i32, i32, P, P, i32, P],
+        "or_render_fwd_values": [P, P, P, P, i32, i32, P, P, P, P],
+        "or_render_bwd": [P, P, P, i32, i32, P, P, P, P, i32, P],
         "or_chunk_policy": [i32, P, dbl, dbl, dbl, dbl, i32, P, P],
     }
     for name, args in sig.items():
@@ -199,8 +199,13 @@ def tile_ranges(sorted_keys, ntiles) -> np.ndarray:
     return ranges
 
 
-def render_fwd(splats, sorted_ids, ranges, width, height, tile_mask=None):
-    """Mirror forward. Returns dict(rgb[3,H,W], T[H,W], last[H,W], knife[H,W], hits, evals)."""
+def _bg(bg, dtype):
+    return None if bg is None else np.ascontiguousarray(np.asarray(bg, dtype).reshape(3))
+
+
+def render_fwd(splats, sorted_ids, ranges, width, height, tile_mask=None, bg=None):
+    """Mirror forward (bg: background colour, black when None).
+    Returns dict(rgb[3,H,W], T[H,W], last[H,W], knife[H,W], hits, evals)."""
     splats, sorted_ids = _c(splats, np.float32), _c(sorted_ids, np.int32)
     ranges = _c(ranges, np.int32)
     rgb = np.zeros((3, height, width), np.float32)
@@ -209,8 +214,9 @@ def render_fwd(splats, sorted_ids, ranges, width, height, tile_mask=None):
     knife = np.zeros((height, width), np.uint8)
     stats = np.zeros(2, np.int64)
     mask = _c(tile_mask, np.uint8) if tile_mask is not None else None
+    bg = _bg(bg, np.float32)
     _load().or_render_fwd(_p(splats), _p(sorted_ids), _p(ranges), int(width), int(height),
-                          _p(mask), _p(rgb), _p(T), _p(last), _p(knife), _p(stats))
+                          _p(mask), _p(bg), _p(rgb), _p(T), _p(last), _p(knife), _p(stats))
     return dict(rgb=rgb, T=T, last=last, knife=knife.astype(bool), hits=int(stats[0]),
                 evals=int(stats[1]))
 
@@ -224,23 +230,28 @@ def render_fwd_untiled(splats, width, height):
     return rgb, T
 
 
-def render_fwd_values(splats_dec, splats_val, sorted_ids, ranges, width, height, last):
+def render_fwd_values(splats_dec, splats_val, sorted_ids, ranges, width, height, last, bg=None):
     splats_dec, splats_val = _c(splats_dec, np.float32), _c(splats_val, np.float64)
     sorted_ids, ranges, last = _c(sorted_ids, np.int32), _c(ranges, np.int32), _c(last, np.int32)
     rgb = np.zeros((3, height, width), np.float64)
     T = np.zeros((height, width), np.float64)
+    bg = _bg(bg, np.float64)
     _load().or_render_fwd_values(_p(splats_dec), _p(splats_val), _p(sorted_ids), _p(ranges),
-                                 int(width), int(height), _p(last), _p(rgb), _p(T))
+                                 int(width), int(height), _p(last), _p(bg), _p(rgb), _p(T))
     return rgb, T
 
 
-def render_bwd(splats, sorted_ids, ranges, width, height, last, dL_drgb) -> np.ndarray:
+def render_bwd(splats, sorted_ids, ranges, width, height, last, dL_drgb, bg=None,
+               dL_dT=None) -> np.ndarray:
+    """grads[n][9] of sum(dL_drgb * rgb) + sum(dL_dT * T) (bg: background colour)."""
     splats, sorted_ids = _c(splats, np.float32), _c(sorted_ids, np.int32)
     ranges, last, dL = _c(ranges, np.int32), _c(last, np.int32), _c(dL_drgb, np.float32)
+    bg = _bg(bg, np.float32)
+    dT = None if dL_dT is None else _c(dL_dT, np.float32)
     n = splats.shape[0]
     grads = np.zeros((n, 9), np.float64)
     _load().or_render_bwd(_p(splats), _p(sorted_ids), _p(ranges), int(width), int(height),
-                          _p(last), _p(dL), n, _p(grads))
+                          _p(last), _p(dL), _p(bg), _p(dT), n, _p(grads))
     return grads
 
 
@@ -253,8 +264,9 @@ def chunk_policy(counts_desc, workers, lambda_, beta, eps=0.10, max_items=1 << 3
     return int(h[0]), int(k[0])
 
 
-def frame(scene, fwd=True, bwd=True):
-    """Whole oracle chain on a scene: project, bin, sort, ranges, forward, backward."""
+def frame(scene, fwd=True, bwd=True, bg=None, dL_dT=None):
+    """Whole oracle chain on a scene: project, bin, sort, ranges, forward, backward
+    (bg: background colour; dL_dT: gradient of the final transmittance)."""
     cam = scene.camera
     W, H = cam.width, cam.height
     splats = project_scene(scene)
@@ -264,7 +276,8 @@ def frame(scene, fwd=True, bwd=True):
     out = dict(splats=splats, offsets=offsets, keys=keys, ids=ids, sorted_keys=skeys,
                sorted_ids=sids, ranges=ranges)
     if fwd:
-        out["fwd"] = render_fwd(splats, sids, ranges, W, H)
+        out["fwd"] = render_fwd(splats, sids, ranges, W, H, bg=bg)
     if fwd and bwd:
-        out["grads"] = render_bwd(splats, sids, ranges, W, H, out["fwd"]["last"], scene.dL_drgb)
+        out["grads"] = render_bwd(splats, sids, ranges, W, H, out["fwd"]["last"], scene.dL_drgb,
+                                  bg=bg, dL_dT=dL_dT)
     return out

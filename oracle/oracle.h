@@ -75,8 +75,8 @@ void or_tile_ranges(int64_t npairs, const uint64_t *sorted_keys, int ntiles, int
    tile_mask (nullable) restricts the work to tiles with a nonzero byte; other
    pixels are left untouched. stats (nullable) += {hits, evaluations}. */
 void or_render_fwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
-                   int width, int height, const uint8_t *tile_mask, float *rgb, float *T_final,
-                   int32_t *last, uint8_t *knife, int64_t *stats);
+                   int width, int height, const uint8_t *tile_mask, const float *bg, float *rgb,
+                   float *T_final, int32_t *last, uint8_t *knife, int64_t *stats);
 
 /* Untiled brute force: every pixel walks every visible splat in (depth, id) order. */
 void or_render_fwd_untiled(int n, const float *splats, int width, int height,
@@ -86,12 +86,14 @@ void or_render_fwd_untiled(int n, const float *splats, int width, int height,
    splats_dec, stop from last; values from splats_val (fp64 records). */
 void or_render_fwd_values(const float *splats_dec, const double *splats_val,
                           const int32_t *sorted_ids, const int32_t *ranges, int width, int height,
-                          const int32_t *last, double *rgb, double *T_final);
+                          const int32_t *last, const double *bg, double *rgb, double *T_final);
 
-/* Analytic backward, truth mode: grads[n][9] (overwritten) of L = sum_p g_p . C_p. */
+/* Analytic backward, truth mode: grads[n][9] (overwritten) of
+   L = sum_p g_p . C_p + dL_dT_p T_final,p with C_p including T_final,p bg
+   (bg, dL_dT: NULL for none). */
 void or_render_bwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
                    int width, int height, const int32_t *last, const float *dL_drgb,
-                   int n, double *grads);
+                   const float *bg, const float *dL_dT, int n, double *grads);
 
 /* Per-frame chunking policy (Eq. 6 of [LOAD-IMB]). counts_desc: tile counts in
    descending order. Writes h (tiles to chunk) and k (chunks per tile; 1 when off);

@@ -13,6 +13,12 @@
  * Readings: pixel (px, py) is sampled at (px + 0.5, py + 0.5); q = a dx^2 +
  * 2 b dx dy + c dy^2; alpha is clamped to 0.99; the stop test T < 1e-4 comes
  * after the blend, so the splat that crosses is blended.
+ *
+ * Background (not on the pages; the usual completion of Eq. 3): the light that
+ * passes every blended splat shows a background colour bg, so
+ * C = sum_i c_i alpha_i T_i + T_final bg, with T_final the transmittance after
+ * the last blended splat (the T output). A NULL bg is black. The backward also
+ * takes an optional per-pixel dL/dT_final.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -28,8 +34,9 @@ static inline float canon_q(const float *s, float dx, float dy) {
 }
 
 void or_render_fwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
-                   int width, int height, const uint8_t *tile_mask, float *rgb, float *T_final,
-                   int32_t *last, uint8_t *knife, int64_t *stats) {
+                   int width, int height, const uint8_t *tile_mask, const float *bg, float *rgb,
+                   float *T_final, int32_t *last, uint8_t *knife, int64_t *stats) {
+  const float b0 = bg ? bg[0] : 0.0f, b1 = bg ? bg[1] : 0.0f, b2 = bg ? bg[2] : 0.0f;
   const int tiles_x = (width + 15) / 16;
   const int64_t P = (int64_t)width * height;
   int64_t hits = 0, evals = 0;
@@ -63,9 +70,9 @@ void or_render_fwd(const float *splats, const int32_t *sorted_ids, const int32_t
         break;
       }
     }
-    rgb[p] = C0;
-    rgb[P + p] = C1;
-    rgb[2 * P + p] = C2;
+    rgb[p] = C0 + T * b0;
+    rgb[P + p] = C1 + T * b1;
+    rgb[2 * P + p] = C2 + T * b2;
     T_final[p] = T;
     last[p] = consumed;
     if (knife) knife[p] = kn;
@@ -130,7 +137,7 @@ void or_render_fwd_untiled(int n, const float *splats, int width, int height, fl
 
 void or_render_fwd_values(const float *splats_dec, const double *splats_val,
                           const int32_t *sorted_ids, const int32_t *ranges, int width, int height,
-                          const int32_t *last, double *rgb, double *T_final) {
+                          const int32_t *last, const double *bg, double *rgb, double *T_final) {
   const int tiles_x = (width + 15) / 16;
   const int64_t P = (int64_t)width * height;
 #pragma omp parallel for schedule(dynamic, 64)
@@ -151,7 +158,7 @@ void or_render_fwd_values(const float *splats_dec, const double *splats_val,
       for (int ch = 0; ch < 3; ch++) C[ch] += s[6 + ch] * alpha * T;
       T *= (1.0 - alpha);
     }
-    for (int ch = 0; ch < 3; ch++) rgb[ch * P + p] = C[ch];
+    for (int ch = 0; ch < 3; ch++) rgb[ch * P + p] = C[ch] + (bg ? T * bg[ch] : 0.0);
     T_final[p] = T;
   }
 }
@@ -163,8 +170,8 @@ typedef struct {
 } hit_t;
 
 void or_render_bwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
-                   int width, int height, const int32_t *last, const float *dL_drgb, int n,
-                   double *grads) {
+                   int width, int height, const int32_t *last, const float *dL_drgb,
+                   const float *bg, const float *dL_dT, int n, double *grads) {
   const int tiles_x = (width + 15) / 16, tiles_y = (height + 15) / 16;
   const int64_t P = (int64_t)width * height;
   int maxlen = 1;
@@ -204,8 +211,12 @@ void or_render_bwd(const float *splats, const int32_t *sorted_ids, const int32_t
         h->cg = (double)s[6] * g[0] + (double)s[7] * g[1] + (double)s[8] * g[2];
         T *= (1.0 - h->alpha);
       }
-      /* dC/dalpha_k = T_k c_k - sum_{j>k} alpha_j T_j c_j / (1 - alpha_k) */
-      double suffix = 0.0;
+      /* dC/dalpha_k = T_k c_k - (sum_{j>k} alpha_j T_j c_j + T_final bg) / (1 - alpha_k)
+       * and dT_final/dalpha_k = -T_final / (1 - alpha_k): both behind-terms start the
+       * suffix (T holds T_final here) */
+      const double bgg = bg ? (double)bg[0] * g[0] + (double)bg[1] * g[1] + (double)bg[2] * g[2]
+                            : 0.0;
+      double suffix = T * (bgg + (dL_dT ? (double)dL_dT[p] : 0.0));
       for (int j = m - 1; j >= 0; j--) {
         const hit_t *h = &H[j];
         const float *s = splats + 12 * h->id;

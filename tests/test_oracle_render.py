@@ -217,3 +217,73 @@ def test_backward_zero_for_splats_behind_the_stop():
     assert np.all(G[2] == 0)
     # every hit sits in the alpha = 0.99 clamp: only the colour receives gradient
     assert np.all(G[:2, :6] == 0) and np.all(G[:2, 6] != 0)
+
+
+# ------------------------------------------------ background and dL/dT_final
+
+def test_background_closed_form_single_splat():
+    """C = c alpha + (1 - alpha) bg for one splat; T is unchanged by the background."""
+    W, H = 45, 37
+    s = _splat(20.3, 17.8, 4.0, 0.8, [0.5, -0.25, 1.0], 3.0)[None]
+    si, r = _frame_from_splats(s, W, H)
+    bg = np.array([0.25, 0.5, -1.0], np.float32)
+    f = oracle.render_fwd(s, si, r, W, H, bg=bg)
+    f0 = oracle.render_fwd(s, si, r, W, H)
+    py, px = np.mgrid[0:H, 0:W]
+    al = _alpha_closed(s[0], px, py)
+    for ch in range(3):
+        np.testing.assert_allclose(f["rgb"][ch], s[0, 6 + ch] * al + (1 - al) * bg[ch], atol=3e-7)
+    assert np.array_equal(f["T"], f0["T"]) and np.array_equal(f["last"], f0["last"])
+
+
+def test_white_splats_on_white_background_give_one():
+    sc = scenegen.random_scene(21, 300, 50, 41, 50.0, log_scale=(-2.5, 0.4))
+    s = oracle.project_scene(sc)
+    s[:, 6:9] = 1.0
+    si, r = _frame_from_splats(s, 50, 41)
+    f = oracle.render_fwd(s, si, r, 50, 41, bg=[1.0, 1.0, 1.0])
+    np.testing.assert_allclose(f["rgb"], 1.0, atol=2e-6)
+
+
+@pytest.mark.parametrize("seed,o_range,n", [(45, (0.2, 0.95), 25), (46, (0.6, 1.0), 90)])
+def test_backward_with_background_and_dT_matches_central_differences(seed, o_range, n):
+    """L = sum g . C + sum gT T_final with C including T_final bg."""
+    s, g, W, H = _fd_scene(seed, o_range, n)
+    rng = np.random.default_rng(seed + 100)
+    bg = rng.uniform(-1, 1, 3).astype(np.float32)
+    gT = rng.standard_normal((H, W)).astype(np.float32)
+    si, r = _frame_from_splats(s, W, H)
+    f = oracle.render_fwd(s, si, r, W, H, bg=bg)
+    grads = oracle.render_bwd(s, si, r, W, H, f["last"], g, bg=bg, dL_dT=gT)
+    base = s.astype(np.float64)
+    g64, gT64 = g.astype(np.float64), gT.astype(np.float64)
+    fd = np.zeros_like(grads)
+    for i in range(len(s)):
+        for j in range(9):
+            h = 1e-6 * max(1.0, abs(base[i, j]))
+            vals = []
+            for sign in (1, -1):
+                v = base.copy()
+                v[i, j] += sign * h
+                rgb, T = oracle.render_fwd_values(s, v, si, r, W, H, f["last"], bg=bg)
+                vals.append(float((rgb * g64).sum() + (T * gT64).sum()))
+            fd[i, j] = (vals[0] - vals[1]) / (2 * h)
+    scale = np.abs(grads).max(axis=0) + 1e-12
+    err = np.abs(fd - grads) / scale
+    assert err.max() < 1e-6, (err.max(axis=0))
+    # the extra terms change the gradient: without them the FD check would fail
+    plain = oracle.render_bwd(s, si, r, W, H, f["last"], g)
+    assert np.abs(plain - grads).max() > 1e-3 * np.abs(grads).max()
+
+
+def test_background_acts_as_a_transmittance_gradient():
+    """T_final bg . g enters L like T_final with weight bg . g, so a background
+    equals an extra dL/dT_final of bg . g (up to the fp32 rounding of that sum)."""
+    s, g, W, H = _fd_scene(47)
+    bg = np.array([0.5, -0.25, 0.75], np.float32)
+    si, r = _frame_from_splats(s, W, H)
+    f = oracle.render_fwd(s, si, r, W, H, bg=bg)
+    G1 = oracle.render_bwd(s, si, r, W, H, f["last"], g, bg=bg)
+    dT = np.einsum("c,chw->hw", bg.astype(np.float64), g.astype(np.float64)).astype(np.float32)
+    G2 = oracle.render_bwd(s, si, r, W, H, f["last"], g, dL_dT=dT)
+    np.testing.assert_allclose(G1, G2, rtol=1e-6, atol=1e-9 * np.abs(G1).max())
