@@ -25,7 +25,8 @@ GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED = -3, -4, -5
 SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
 
 EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_project_bwd",
-           "gs_project_bf16sh", "gs_project_bwd_bf16sh", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
+           "gs_project_bf16sh", "gs_project_bwd_bf16sh", "gs_bin_tiles",
+           "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
            "gs_timing_read")
 
 
@@ -71,10 +72,12 @@ def lib():
     L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, sz, P]
     L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
+    L.gs_render_fwd_bg.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P]
+    L.gs_render_bwd_bg.argtypes = L.gs_render_bwd.argtypes[:-1] + [P, P, P]
     L.gs_timing_start.argtypes = []
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
     for name in ("gs_project", "gs_project_bwd", "gs_project_bf16sh", "gs_project_bwd_bf16sh",
-                 "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
+                 "gs_bin_tiles", "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
@@ -211,6 +214,38 @@ def gs_render_bwd(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, 
            "gs_render_bwd")
 
 
+def _bg3(background):
+    """A host array of 3 floats for the C call, or None (black)."""
+    if background is None:
+        return None
+    vals = [float(v) for v in background]
+    if len(vals) != 3:
+        raise ValueError("background takes 3 values")
+    return (C.c_float * 3)(*vals)
+
+
+def gs_render_fwd_bg(n, splats, sorted_ids, ranges, cam, sched, rgb, T_final, last, fwd_state,
+                     stats, workspace, background, stream=None):
+    _check(lib().gs_render_fwd_bg(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
+                                  C.byref(cam), C.byref(sched) if sched is not None else None,
+                                  _ptr(rgb), _ptr(T_final), _ptr(last), _ptr(fwd_state),
+                                  fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _bg3(background), _stream(stream)),
+           "gs_render_fwd_bg")
+
+
+def gs_render_bwd_bg(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, dL_drgb,
+                     dL_dsplat, workspace, background, dL_dT, stream=None):
+    _check(lib().gs_render_bwd_bg(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
+                                  C.byref(cam), _ptr(T_final), _ptr(last), _ptr(fwd_state),
+                                  fwd_state.numel() * fwd_state.element_size(), _ptr(dL_drgb),
+                                  _ptr(dL_dsplat), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _bg3(background), _ptr(dL_dT), _stream(stream)),
+           "gs_render_bwd_bg")
+
+
 def gs_timing_start():
     _check(lib().gs_timing_start(), "gs_timing_start")
 
@@ -296,17 +331,26 @@ class Rasterizer:
             self._ensure(n, max(need + need // 8, 1024))
         raise GsError(GS_ERR_CAPACITY, "bin_and_sort")
 
-    def render_fwd(self, n, stats=False):
+    def render_fwd(self, n, stats=False, background=None):
+        """background: 3 floats (host), or None for black (gs_render_fwd)."""
         if stats:
             self.stats.zero_()
-        gs_render_fwd(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched, self.rgb,
-                      self.T, self.last, self.fwd_state, self.stats if stats else None,
-                      self.workspace)
+        args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched, self.rgb,
+                self.T, self.last, self.fwd_state, self.stats if stats else None, self.workspace)
+        if background is None:
+            gs_render_fwd(*args)
+        else:
+            gs_render_fwd_bg(*args, background)
         return self.rgb, self.T, self.last
 
-    def render_bwd(self, n, dL_drgb):
-        gs_render_bwd(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.T, self.last,
-                      self.fwd_state, dL_drgb, self.grads, self.workspace)
+    def render_bwd(self, n, dL_drgb, background=None, dL_dT=None):
+        """background as for render_fwd; dL_dT [H][W] on the device, or None."""
+        args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.T, self.last,
+                self.fwd_state, dL_drgb, self.grads, self.workspace)
+        if background is None and dL_dT is None:
+            gs_render_bwd(*args)
+        else:
+            gs_render_bwd_bg(*args, background, dL_dT)
         return self.grads[:n]
 
     def project_bwd(self, means, log_scales, quats, opacities, sh, sh_degree, dL_dsplat=None):

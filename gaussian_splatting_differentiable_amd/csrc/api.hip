@@ -29,8 +29,8 @@ hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                float *grads, int n, int workers_waves, hipEvent_t ev0,
-                                hipEvent_t ev1, hipStream_t st);
+                                const float *dT, float *grads, int n, int workers_waves,
+                                hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 
 namespace {
 
@@ -59,6 +59,19 @@ bool prep_camera(const gs_camera *c, CamK *k) {
     k->centre[j] = -(k->R[j] * k->t[0] + k->R[3 + j] * k->t[1] + k->R[6 + j] * k->t[2]);
   k->znear = c->znear;
   k->lowpass = c->lowpass;
+  k->bg[0] = k->bg[1] = k->bg[2] = 0.0f;
+  k->bg_on = 0;
+  return true;
+}
+
+// Background colour (host, 3 floats, or NULL for black) into the kernel camera.
+bool set_background(const float *bg, CamK *k) {
+  if (!bg) return true;
+  for (int c = 0; c < 3; c++) {
+    if (!isfinite(bg[c])) return false;
+    k->bg[c] = bg[c];
+    if (bg[c] != 0.0f) k->bg_on = 1;
+  }
   return true;
 }
 
@@ -246,13 +259,15 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
                                    tile_ranges, workspace, (hipStream_t)stream));
 }
 
-int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
-                      const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
-                      float *rgb, float *T_final, int32_t *last, void *fwd_state,
-                      size_t fwd_state_bytes, int64_t *stats, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
+                         const int32_t *tile_ranges, const gs_camera *cam,
+                         const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
+                         void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                         void *workspace, size_t workspace_bytes, const float *background,
+                         void *stream) {
   CamK k;
-  if (n < 0 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n < 0 || !prep_camera(cam, &k) || !set_background(background, &k))
+    return GS_ERR_INVALID_ARGUMENT;
   if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
   if (!tile_ranges || !rgb || !T_final || !last || !fwd_state) return GS_ERR_INVALID_ARGUMENT;
   if (n > 0 && (!splats || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
@@ -273,18 +288,31 @@ int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                                          (hipStream_t)stream));
 }
 
-int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
-                      const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
-                      const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
-                      const float *dL_drgb, float *dL_dsplat, void *workspace,
+int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
+                      const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
+                      float *rgb, float *T_final, int32_t *last, void *fwd_state,
+                      size_t fwd_state_bytes, int64_t *stats, void *workspace,
                       size_t workspace_bytes, void *stream) {
+  return gs_render_fwd_bg(n, splats, sorted_ids, tile_ranges, cam, sched, rgb, T_final, last,
+                          fwd_state, fwd_state_bytes, stats, workspace, workspace_bytes, nullptr,
+                          stream);
+}
+
+int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
+                         const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
+                         const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
+                         const float *dL_drgb, float *dL_dsplat, void *workspace,
+                         size_t workspace_bytes, const float *background, const float *dL_dT,
+                         void *stream) {
   CamK k;
-  if (n < 0 || !prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n < 0 || !prep_camera(cam, &k) || !set_background(background, &k))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (dL_dT) k.bg_on = 1;
   if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
   if (!tile_ranges || !T_final || !last || !fwd_state || !dL_drgb) return GS_ERR_INVALID_ARGUMENT;
   if (n > 0 && (!splats || !sorted_ids || !dL_dsplat)) return GS_ERR_INVALID_ARGUMENT;
   if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8) ||
-      (dL_dsplat && !aligned(dL_dsplat, 16)))
+      (dL_dsplat && !aligned(dL_dsplat, 16)) || (dL_dT && !aligned(dL_dT, 4)))
     return GS_ERR_INVALID_ARGUMENT;
   if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
   if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
@@ -294,8 +322,18 @@ int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
   hipEvent_t e0, e1;
   timing_slot(1, e0, e1);
   return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
-                                         fwd_state, dL_drgb, dL_dsplat, n, workers, e0, e1,
-                                         (hipStream_t)stream));
+                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, n, workers, e0,
+                                         e1, (hipStream_t)stream));
+}
+
+int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
+                      const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
+                      const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
+                      const float *dL_drgb, float *dL_dsplat, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return gs_render_bwd_bg(n, splats, sorted_ids, tile_ranges, cam, T_final, last, fwd_state,
+                          fwd_state_bytes, dL_drgb, dL_dsplat, workspace, workspace_bytes, nullptr,
+                          nullptr, stream);
 }
 
 int32_t gs_timing_start(void) {

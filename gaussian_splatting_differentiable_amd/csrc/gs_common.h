@@ -23,6 +23,8 @@ struct CamK {
   float t[3];
   float centre[3];  // camera centre in world coordinates, -R^T t
   float znear, lowpass;
+  float bg[3];      // background colour seen through the final transmittance
+  int bg_on;        // bg is not black (or the backward has a dL/dT_final)
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -236,7 +236,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
-    const float *__restrict__ dL, float *__restrict__ grads) {
+    const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads) {
   __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
   __shared__ int sid_all[GS_WAVES_PER_BLOCK][BATCH];
   Splat *sbuf = sbuf_all[wave_in_block()];
@@ -262,10 +262,17 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const int64_t pix = (int64_t)py * cam.width + px;
     const int2 rg = ranges[tile];
     float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+    // what lies behind the last blended splat, per unit of final transmittance:
+    // the background's bg . dL/dC and dL/dT_final (0 when neither is given)
+    float extra = 0.f;
     if (inside) {
       g0 = dL[pix];
       g1 = dL[P + pix];
       g2 = dL[2 * P + pix];
+      if (cam.bg_on) {
+        extra = fmaf(cam.bg[0], g0, fmaf(cam.bg[1], g1, cam.bg[2] * g2));
+        if (dT) extra += dT[pix];
+      }
     }
     const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
     if (kind == ITEM_PLAIN) {
@@ -276,7 +283,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
         lastp = last[pix];
       }
       const int kmax = min(wave_max(lastp), fs.sub_last[tile * 4 + quad]);
-      walk_back(splats, sorted_ids, rg.x, kmax, st, fx, fy, lastp, T, 0.0f, g0, g1, g2, sbuf,
+      walk_back(splats, sorted_ids, rg.x, kmax, st, fx, fy, lastp, T, extra, g0, g1, g2, sbuf,
                 sid, grads);
       continue;
     }
@@ -297,6 +304,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
                                 __builtin_fmaf(fs.CB[3 * c2 + 1], g1,
                                                __builtin_fmaf(fs.CB[3 * c2 + 2], g2, behind)));
       }
+      if (cam.bg_on) behind = fmaf(Tfin[pix], extra, behind);
       accum = behind / T;
     } else {
       lb = 0;
@@ -312,8 +320,8 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
 hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                float *grads, int n, int workers_waves, hipEvent_t ev0,
-                                hipEvent_t ev1, hipStream_t st) {
+                                const float *dT, float *grads, int n, int workers_waves,
+                                hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
@@ -328,7 +336,7 @@ hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
-                     reinterpret_cast<char *>(fwd_state), ntiles, dL, grads);
+                     reinterpret_cast<char *>(fwd_state), ntiles, dL, dT, grads);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
   return e;

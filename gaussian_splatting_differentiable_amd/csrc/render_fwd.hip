@@ -252,9 +252,9 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       const Blend r = blend_range<STATS>(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits,
                                            nsteps, nhsteps);
       if (x.inside) {
-        rgb[x.p] = r.C0;
-        rgb[P + x.p] = r.C1;
-        rgb[2 * P + x.p] = r.C2;
+        rgb[x.p] = cam.bg_on ? fmaf(r.T, cam.bg[0], r.C0) : r.C0;
+        rgb[P + x.p] = cam.bg_on ? fmaf(r.T, cam.bg[1], r.C1) : r.C1;
+        rgb[2 * P + x.p] = cam.bg_on ? fmaf(r.T, cam.bg[2], r.C2) : r.C2;
         Tout[x.p] = r.T;
         last[x.p] = r.consumed;
       }
@@ -347,9 +347,9 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       if (Tf < T_STOP) break;
     }
     if (x.inside) {
-      rgb[x.p] = C0;
-      rgb[P + x.p] = C1;
-      rgb[2 * P + x.p] = C2;
+      rgb[x.p] = cam.bg_on ? fmaf(Tf, cam.bg[0], C0) : C0;
+      rgb[P + x.p] = cam.bg_on ? fmaf(Tf, cam.bg[1], C1) : C1;
+      rgb[2 * P + x.p] = cam.bg_on ? fmaf(Tf, cam.bg[2], C2) : C2;
       Tout[x.p] = Tf;
       last[x.p] = lastv;
     }

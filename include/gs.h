@@ -226,6 +226,31 @@ int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const float *dL_drgb, float *dL_dsplat, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* gs_render_fwd and gs_render_bwd with a background colour and a gradient of
+ * the final transmittance (not on the pages, which blend onto black; the usual
+ * completion of Eq. 3): the light that passes every blended splat shows the
+ * background, C = sum_i c_i alpha_i T_i + T_final bg. In the backward both
+ * terms sit behind the last blended splat, so each pixel's accumulator starts
+ * at bg . dL/dC + dL/dT_final instead of 0 (and a chunk's at the later chunks'
+ * colour plus T_final (bg . dL/dC + dL/dT_final), over its own T_end).
+ *   background: host pointer to 3 floats (read during the call; finite), or
+ *     NULL for black. The two calls of a frame take the same colour.
+ *   dL_dT [H][W] or NULL: dL/dT_final per pixel (device, 4-byte aligned).
+ * With NULL for both the results are those of gs_render_fwd / gs_render_bwd,
+ * bit for bit. Other arguments, outputs and errors as for those calls. */
+int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
+                         const int32_t *tile_ranges, const gs_camera *cam,
+                         const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
+                         void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                         void *workspace, size_t workspace_bytes, const float *background,
+                         void *stream);
+int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
+                         const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
+                         const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
+                         const float *dL_drgb, float *dL_dsplat, void *workspace,
+                         size_t workspace_bytes, const float *background, const float *dL_dT,
+                         void *stream);
+
 /* Kernel timing, for measurement only (no paper passage: it lets a benchmark
  * divide algorithmic bytes by the raster kernel's own duration rather than by
  * the whole call's, which also zeroes the gradients and orders the backward's

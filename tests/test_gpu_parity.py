@@ -69,8 +69,9 @@ def check_projection(sc, ref_splats, gpu_splats):
     assert np.all(gpu_splats[~gvis][:, 9] == -1) and np.all(gpu_splats[~gvis][:, [0, 1, 2, 5, 10]] == 0)
 
 
-def run_stages(gsr, sc, ref, capacity=None, sched=None):
-    """GPU bin/sort/fwd/bwd fed the oracle's splats. Returns host arrays."""
+def run_stages(gsr, sc, ref, capacity=None, sched=None, background=None, dL_dT=None):
+    """GPU bin/sort/fwd/bwd fed the oracle's splats. Returns host arrays.
+    background / dL_dT (host arrays) select gs_render_fwd_bg / gs_render_bwd_bg."""
     cam = sc.camera
     n = sc.n
     npairs = len(ref["sorted_ids"])
@@ -85,8 +86,9 @@ def run_stages(gsr, sc, ref, capacity=None, sched=None):
     # forward/backward on the oracle's sorted list (stage isolation)
     r.sorted_ids[:npairs].copy_(dev(ref["sorted_ids"]))
     r.ranges.copy_(dev(ref["ranges"]))
-    r.render_fwd(n, stats=True)
-    grads = r.render_bwd(n, dev(sc.dL_drgb))
+    r.render_fwd(n, stats=True, background=background)
+    grads = r.render_bwd(n, dev(sc.dL_drgb), background=background,
+                         dL_dT=None if dL_dT is None else dev(dL_dT))
     out.update(rgb=host(r.rgb), T=host(r.T), last=host(r.last), grads=host(grads),
                stats=host(r.stats), plan=read_plan(r))
     return out

@@ -76,6 +76,15 @@ def test_argument_validation_needs_no_gpu(gsr):
     assert L.gs_project_bf16sh(-1, None, None, None, None, None, 0, C.byref(cam), None, None) == -1
     assert L.gs_project_bwd_bf16sh(0, None, None, None, None, None, 0, C.byref(cam), *nul,
                                    None) == 0
+    # background: non-finite values and a misaligned dL/dT_final are rejected before any HIP call
+    nanbg = (C.c_float * 3)(float("nan"), 0.0, 0.0)
+    st256 = C.c_void_p(256)
+    assert L.gs_render_fwd_bg(1, p16, p16, p16, C.byref(cam), None, p16, p16, p16, st256, 1 << 30,
+                              None, None, 0, nanbg, None) == -1
+    assert L.gs_render_bwd_bg(1, p16, p16, p16, C.byref(cam), p16, p16, st256, 1 << 30, p16, p16,
+                              None, 0, nanbg, None, None) == -1
+    assert L.gs_render_bwd_bg(1, p16, p16, p16, C.byref(cam), p16, p16, st256, 1 << 30, p16, p16,
+                              None, 0, None, C.c_void_p(18), None) == -1
     big = gsr.GsCamera()
     big.width, big.height, big.fx, big.fy = 1 << 14, 1 << 14, 1.0, 1.0
     assert L.gs_bin_tiles(1, C.c_void_p(16), C.byref(big), 10, C.c_void_p(16), C.c_void_p(16),
