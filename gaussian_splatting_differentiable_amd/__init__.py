@@ -26,7 +26,9 @@ SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
 
 EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_project_bwd",
            "gs_project_bf16sh", "gs_project_bwd_bf16sh", "gs_bin_tiles",
-           "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
+           "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_workspace_size_views",
+           "gs_fwd_state_size_views", "gs_project_views", "gs_project_bwd_views",
+           "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
            "gs_timing_read")
 
 
@@ -74,10 +76,22 @@ def lib():
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
     L.gs_render_fwd_bg.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P]
     L.gs_render_bwd_bg.argtypes = L.gs_render_bwd.argtypes[:-1] + [P, P, P]
+    L.gs_workspace_size_views.argtypes = [i32, i32, i32, i32, i64]
+    L.gs_workspace_size_views.restype = sz
+    L.gs_fwd_state_size_views.argtypes, L.gs_fwd_state_size_views.restype = [i32, i32, i32], sz
+    L.gs_project_views.argtypes = [i32, P, P, P, P, P, i32, cam_p, i32, P, P]
+    L.gs_project_bwd_views.argtypes = [i32, P, P, P, P, P, i32, cam_p, i32, P, P, P, P, P, P, P]
+    L.gs_bin_tiles_views.argtypes = [i32, P, cam_p, i32, i64, P, P, P, P, P, sz, P]
+    L.gs_sort_keys_views.argtypes = [i32, P, P, i64, cam_p, i32, P, P, P, P, sz, P]
+    L.gs_render_fwd_views.argtypes = [i32, P, P, P, cam_p, i32, C.POINTER(GsSched), P, P, P, P,
+                                      sz, P, P, P]
+    L.gs_render_bwd_views.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P]
     L.gs_timing_start.argtypes = []
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
     for name in ("gs_project", "gs_project_bwd", "gs_project_bf16sh", "gs_project_bwd_bf16sh",
-                 "gs_bin_tiles", "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_sort_keys", "gs_render_fwd",
+                 "gs_bin_tiles", "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_project_views",
+                 "gs_project_bwd_views", "gs_bin_tiles_views", "gs_sort_keys_views",
+                 "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
@@ -138,6 +152,85 @@ def workspace_size(n, width, height, capacity) -> int:
 
 def fwd_state_size(width, height) -> int:
     return int(lib().gs_fwd_state_size(int(width), int(height)))
+
+
+def workspace_size_views(n, width, height, n_views, capacity) -> int:
+    return int(lib().gs_workspace_size_views(int(n), int(width), int(height), int(n_views),
+                                             int(capacity)))
+
+
+def fwd_state_size_views(width, height, n_views) -> int:
+    return int(lib().gs_fwd_state_size_views(int(width), int(height), int(n_views)))
+
+
+def _cams(cams):
+    """A C array of cameras from scenegen cameras or GsCamera values."""
+    arr = (GsCamera * len(cams))()
+    for i, c in enumerate(cams):
+        arr[i] = c if isinstance(c, GsCamera) else make_camera(c)
+    return arr
+
+
+def gs_project_views(n, means, log_scales, quats, opacities, sh, sh_degree, cams, splats,
+                     stream=None):
+    arr = _cams(cams)
+    _check(lib().gs_project_views(int(n), _ptr(means), _ptr(log_scales), _ptr(quats),
+                                  _ptr(opacities), _ptr(sh), int(sh_degree), arr, len(cams),
+                                  _ptr(splats), _stream(stream)),
+           "gs_project_views")
+
+
+def gs_project_bwd_views(n, means, log_scales, quats, opacities, sh, sh_degree, cams, dL_dsplat,
+                         dL_dmeans, dL_dlog_scales, dL_dquats, dL_dopacities, dL_dsh,
+                         stream=None):
+    arr = _cams(cams)
+    _check(lib().gs_project_bwd_views(int(n), _ptr(means), _ptr(log_scales), _ptr(quats),
+                                      _ptr(opacities), _ptr(sh), int(sh_degree), arr, len(cams),
+                                      _ptr(dL_dsplat), _ptr(dL_dmeans), _ptr(dL_dlog_scales),
+                                      _ptr(dL_dquats), _ptr(dL_dopacities), _ptr(dL_dsh),
+                                      _stream(stream)),
+           "gs_project_bwd_views")
+
+
+def gs_bin_tiles_views(n, splats, cam, n_views, capacity, offsets, keys, ids, status, workspace,
+                       stream=None):
+    _check(lib().gs_bin_tiles_views(int(n), _ptr(splats), C.byref(cam), int(n_views),
+                                    int(capacity), _ptr(offsets), _ptr(keys), _ptr(ids),
+                                    _ptr(status), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)),
+           "gs_bin_tiles_views")
+
+
+def gs_sort_keys_views(n, splats, offsets, capacity, cam, n_views, sorted_keys, sorted_ids,
+                       ranges, workspace, stream=None):
+    _check(lib().gs_sort_keys_views(int(n), _ptr(splats), _ptr(offsets), int(capacity),
+                                    C.byref(cam), int(n_views), _ptr(sorted_keys),
+                                    _ptr(sorted_ids), _ptr(ranges), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)),
+           "gs_sort_keys_views")
+
+
+def gs_render_fwd_views(n, splats, sorted_ids, ranges, cam, n_views, sched, rgb, T_final, last,
+                        fwd_state, stats, background=None, stream=None):
+    _check(lib().gs_render_fwd_views(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
+                                     C.byref(cam), int(n_views),
+                                     C.byref(sched) if sched is not None else None, _ptr(rgb),
+                                     _ptr(T_final), _ptr(last), _ptr(fwd_state),
+                                     fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
+                                     _bg3(background), _stream(stream)),
+           "gs_render_fwd_views")
+
+
+def gs_render_bwd_views(n, splats, sorted_ids, ranges, cam, n_views, T_final, last, fwd_state,
+                        dL_drgb, dL_dsplat, background=None, dL_dT=None, stream=None):
+    _check(lib().gs_render_bwd_views(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
+                                     C.byref(cam), int(n_views), _ptr(T_final), _ptr(last),
+                                     _ptr(fwd_state), fwd_state.numel() * fwd_state.element_size(),
+                                     _ptr(dL_drgb), _ptr(dL_dsplat), _bg3(background),
+                                     _ptr(dL_dT), _stream(stream)),
+           "gs_render_bwd_views")
 
 
 # ------------------------------------------------------------------ C-named calls
@@ -269,19 +362,25 @@ class Rasterizer:
     reported by gs_bin_tiles is handled by growing and running the frame again.
     """
 
-    def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None):
+    def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None, n_views=1):
+        """n_views > 1: a batch of views of camera's size (the *_views calls); the
+        outputs stack the views' rows and `n` counts splat records."""
         self.cam = make_camera(camera)
+        self.V = int(n_views)
         self.W, self.H = int(camera.width), int(camera.height)
-        self.tiles = ((self.W + 15) // 16) * ((self.H + 15) // 16)
+        self.tiles = ((self.W + 15) // 16) * ((self.H + 15) // 16) * self.V
         self.device = torch.device(device)
         self.sched = sched if sched is not None else make_sched()
         self.capacity = int(capacity)
         self.n = -1
         dev = self.device
-        self.rgb = torch.empty((3, self.H, self.W), dtype=torch.float32, device=dev)
-        self.T = torch.empty((self.H, self.W), dtype=torch.float32, device=dev)
-        self.last = torch.empty((self.H, self.W), dtype=torch.int32, device=dev)
-        self.fwd_state = torch.empty(fwd_state_size(self.W, self.H), dtype=torch.uint8, device=dev)
+        VH = self.V * self.H
+        self.rgb = torch.empty((3, VH, self.W), dtype=torch.float32, device=dev)
+        self.T = torch.empty((VH, self.W), dtype=torch.float32, device=dev)
+        self.last = torch.empty((VH, self.W), dtype=torch.int32, device=dev)
+        fs = (fwd_state_size(self.W, self.H) if self.V == 1
+              else fwd_state_size_views(self.W, self.H, self.V))
+        self.fwd_state = torch.empty(fs, dtype=torch.uint8, device=dev)
         self.ranges = torch.empty((self.tiles, 2), dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.stats = torch.zeros(4, dtype=torch.int64, device=dev)
@@ -302,7 +401,8 @@ class Rasterizer:
             self.sorted_ids = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
             self.workspace = None
         if self.workspace is None:
-            ws = workspace_size(n, self.W, self.H, self.capacity)
+            ws = (workspace_size(n, self.W, self.H, self.capacity) if self.V == 1
+                  else workspace_size_views(n, self.W, self.H, self.V, self.capacity))
             self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
     def project(self, means, log_scales, quats, opacities, sh, sh_degree):
@@ -319,12 +419,19 @@ class Rasterizer:
         want_emission also writes the id-order (keys, ids) list of gs_bin_tiles;
         want_keys writes the sorted keys."""
         for _ in range(3):
-            gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets,
-                         self.keys if want_emission else None, self.ids if want_emission else None,
-                         self.status, self.workspace)
-            gs_sort_keys(n, self.splats, self.offsets, self.capacity, self.cam,
-                         self.sorted_keys if want_keys else None, self.sorted_ids, self.ranges,
-                         self.workspace)
+            keys = self.keys if want_emission else None
+            ids = self.ids if want_emission else None
+            skeys = self.sorted_keys if want_keys else None
+            if self.V == 1:
+                gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets, keys, ids,
+                             self.status, self.workspace)
+                gs_sort_keys(n, self.splats, self.offsets, self.capacity, self.cam, skeys,
+                             self.sorted_ids, self.ranges, self.workspace)
+            else:
+                gs_bin_tiles_views(n, self.splats, self.cam, self.V, self.capacity, self.offsets,
+                                   keys, ids, self.status, self.workspace)
+                gs_sort_keys_views(n, self.splats, self.offsets, self.capacity, self.cam, self.V,
+                                   skeys, self.sorted_ids, self.ranges, self.workspace)
             if int(self.status.item()) == GS_OK:
                 return int(self.offsets[n].item())
             need = int(self.offsets[n].item())
@@ -335,6 +442,11 @@ class Rasterizer:
         """background: 3 floats (host), or None for black (gs_render_fwd)."""
         if stats:
             self.stats.zero_()
+        if self.V > 1:
+            gs_render_fwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
+                                self.sched, self.rgb, self.T, self.last, self.fwd_state,
+                                self.stats if stats else None, background)
+            return self.rgb, self.T, self.last
         args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched, self.rgb,
                 self.T, self.last, self.fwd_state, self.stats if stats else None, self.workspace)
         if background is None:
@@ -345,6 +457,11 @@ class Rasterizer:
 
     def render_bwd(self, n, dL_drgb, background=None, dL_dT=None):
         """background as for render_fwd; dL_dT [H][W] on the device, or None."""
+        if self.V > 1:
+            gs_render_bwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
+                                self.T, self.last, self.fwd_state, dL_drgb, self.grads,
+                                background, dL_dT)
+            return self.grads[:n]
         args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.T, self.last,
                 self.fwd_state, dL_drgb, self.grads, self.workspace)
         if background is None and dL_dT is None:
@@ -368,4 +485,28 @@ class Rasterizer:
         call = gs_project_bwd_bf16sh if sh.dtype == torch.bfloat16 else gs_project_bwd
         call(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, dsp,
              out["means"], out["log_scales"], out["quats"], out["opacities"], out["sh"])
+        return out
+
+    def project_views(self, cams, means, log_scales, quats, opacities, sh, sh_degree):
+        """Records of every view of the batch (rows [v n, (v + 1) n) for cams[v])."""
+        n = int(means.shape[0])
+        self._ensure(n * len(cams), self.capacity)
+        gs_project_views(n, means, log_scales, quats, opacities, sh, sh_degree, cams, self.splats)
+        return self.splats[:n * len(cams)]
+
+    def project_bwd_views(self, cams, means, log_scales, quats, opacities, sh, sh_degree,
+                          dL_dsplat=None):
+        """Per-Gaussian gradients summed over the views, as a dict of new tensors."""
+        n = int(means.shape[0])
+        dsp = self.grads[:n * len(cams)] if dL_dsplat is None else dL_dsplat
+        dev = means.device
+        K = (int(sh_degree) + 1) ** 2
+        out = dict(means=torch.empty((n, 3), dtype=torch.float32, device=dev),
+                   log_scales=torch.empty((n, 3), dtype=torch.float32, device=dev),
+                   quats=torch.empty((n, 4), dtype=torch.float32, device=dev),
+                   opacities=torch.empty(n, dtype=torch.float32, device=dev),
+                   sh=torch.empty((n, K, 3), dtype=torch.float32, device=dev))
+        gs_project_bwd_views(n, means, log_scales, quats, opacities, sh, sh_degree, cams, dsp,
+                             out["means"], out["log_scales"], out["quats"], out["opacities"],
+                             out["sh"])
         return out

@@ -13,7 +13,7 @@ hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_sca
                                  const float *quats, const float *opac, const void *sh,
                                  bool sh_bf16, int degree, const CamK &cam, const float *dsplat,
                                  float *gmeans, float *gls, float *gquats, float *gopac,
-                                 float *gsh, hipStream_t st);
+                                 float *gsh, bool accumulate, hipStream_t st);
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
                          int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
                          hipStream_t st);
@@ -61,8 +61,22 @@ bool prep_camera(const gs_camera *c, CamK *k) {
   k->lowpass = c->lowpass;
   k->bg[0] = k->bg[1] = k->bg[2] = 0.0f;
   k->bg_on = 0;
+  k->views = 1;
+  k->vty = k->tiles_y;
+  k->view = 0;
   return true;
 }
+
+// A batch of n_views views of cam's size, stacked: tile rows and output pixel
+// rows of view v follow those of view v - 1.
+bool prep_views(const gs_camera *c, int32_t n_views, CamK *k) {
+  if (n_views < 1 || n_views > GS_MAX_VIEWS || !prep_camera(c, k)) return false;
+  k->views = n_views;
+  k->tiles_y = k->vty * n_views;
+  return true;
+}
+
+int64_t batch_tiles(const CamK &k) { return (int64_t)k.tiles_x * k.tiles_y; }
 
 // Background colour (host, 3 floats, or NULL for black) into the kernel camera.
 bool set_background(const float *bg, CamK *k) {
@@ -162,7 +176,8 @@ int32_t project_bwd_impl(int32_t n, const float *means, const float *log_scales,
     return GS_ERR_INVALID_ARGUMENT;
   return hip_status(gs_launch_project_bwd(n, means, log_scales, quats, opacities, sh, bf16,
                                           sh_degree, k, dL_dsplat, dL_dmeans, dL_dlog_scales,
-                                          dL_dquats, dL_dopacities, dL_dsh, (hipStream_t)stream));
+                                          dL_dquats, dL_dopacities, dL_dsh, false,
+                                          (hipStream_t)stream));
 }
 
 }  // namespace
@@ -225,38 +240,119 @@ int32_t gs_project_bwd_bf16sh(int32_t n, const float *means, const float *log_sc
                           stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+int32_t bin_impl(int32_t n, const float *splats, const CamK &k, int64_t pair_capacity,
+                 int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!offsets || !device_status || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
+  if ((keys == nullptr) != (ids == nullptr)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8))) return GS_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < gs_sort_ws_bytes(n, pair_capacity, k.tiles_x, k.tiles_y))
+    return GS_ERR_WORKSPACE;
+  return hip_status(gs_launch_bin(n, splats, k, pair_capacity, offsets, keys, ids, device_status,
+                                  workspace, (hipStream_t)stream));
+}
+
+int32_t sort_impl(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
+                  const CamK &k, uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!offsets || !tile_ranges || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
+  if (pair_capacity > 0 && !sorted_ids) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (sorted_keys && !aligned(sorted_keys, 8)) ||
+      !aligned(tile_ranges, 8))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < gs_sort_ws_bytes(n, pair_capacity, k.tiles_x, k.tiles_y))
+    return GS_ERR_WORKSPACE;
+  return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
+                                   tile_ranges, workspace, (hipStream_t)stream));
+}
+
+int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
+                 const int32_t *tile_ranges, CamK k, const gs_sched *sched, float *rgb,
+                 float *T_final, int32_t *last, void *fwd_state, size_t fwd_state_bytes,
+                 int64_t *stats, const float *background, void *stream) {
+  if (n < 0 || !set_background(background, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!tile_ranges || !rgb || !T_final || !last || !fwd_state) return GS_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (!splats || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8)) return GS_ERR_INVALID_ARGUMENT;
+  if (fwd_state_bytes < fwd_layout((int)batch_tiles(k)).total) return GS_ERR_WORKSPACE;
+  if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
+  const gs_sched sc = sched ? *sched : default_sched();
+  if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
+      !(sc.beta >= 0.0f))
+    return GS_ERR_INVALID_ARGUMENT;
+  const int workers = worker_waves();
+  if (workers <= 0) return GS_ERR_HIP;
+  hipEvent_t e0, e1;
+  timing_slot(0, e0, e1);
+  return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
+                                         last, fwd_state, stats, workers, e0, e1,
+                                         (hipStream_t)stream));
+}
+
+int32_t bwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
+                 const int32_t *tile_ranges, CamK k, const float *T_final, const int32_t *last,
+                 void *fwd_state, size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
+                 const float *background, const float *dL_dT, void *stream) {
+  if (n < 0 || !set_background(background, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (dL_dT) k.bg_on = 1;
+  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!tile_ranges || !T_final || !last || !fwd_state || !dL_drgb) return GS_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (!splats || !sorted_ids || !dL_dsplat)) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8) ||
+      (dL_dsplat && !aligned(dL_dsplat, 16)) || (dL_dT && !aligned(dL_dT, 4)))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (fwd_state_bytes < fwd_layout((int)batch_tiles(k)).total) return GS_ERR_WORKSPACE;
+  if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
+  const int workers = worker_waves();
+  if (workers <= 0) return GS_ERR_HIP;
+  hipEvent_t e0, e1;
+  timing_slot(1, e0, e1);
+  return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
+                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, n, workers, e0,
+                                         e1, (hipStream_t)stream));
+}
+
+// The camera of view 0 of a batch, with every view checked to be valid and of
+// its size.
+bool prep_batch_cams(const gs_camera *cams, int32_t n_views) {
+  if (!cams || n_views < 1 || n_views > GS_MAX_VIEWS) return false;
+  CamK k;
+  for (int v = 0; v < n_views; v++) {
+    if (!prep_camera(&cams[v], &k)) return false;
+    if (cams[v].width != cams[0].width || cams[v].height != cams[0].height) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
                      int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
                      void *workspace, size_t workspace_bytes, void *stream) {
   CamK k;
-  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX || !prep_camera(cam, &k))
-    return GS_ERR_INVALID_ARGUMENT;
-  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!offsets || !device_status || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
-  if ((keys == nullptr) != (ids == nullptr)) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8))) return GS_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
-    return GS_ERR_WORKSPACE;
-  return hip_status(gs_launch_bin(n, splats, k, pair_capacity, offsets, keys, ids, device_status,
-                                  workspace, (hipStream_t)stream));
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return bin_impl(n, splats, k, pair_capacity, offsets, keys, ids, device_status, workspace,
+                  workspace_bytes, stream);
 }
 
 int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
                      const gs_camera *cam, uint64_t *sorted_keys, int32_t *sorted_ids,
                      int32_t *tile_ranges, void *workspace, size_t workspace_bytes, void *stream) {
   CamK k;
-  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX || !prep_camera(cam, &k))
-    return GS_ERR_INVALID_ARGUMENT;
-  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!offsets || !tile_ranges || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
-  if (pair_capacity > 0 && !sorted_ids) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || (sorted_keys && !aligned(sorted_keys, 8)) ||
-      !aligned(tile_ranges, 8))
-    return GS_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < gs_workspace_size(n, cam->width, cam->height, pair_capacity))
-    return GS_ERR_WORKSPACE;
-  return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
-                                   tile_ranges, workspace, (hipStream_t)stream));
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
+                   workspace, workspace_bytes, stream);
 }
 
 int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -266,26 +362,10 @@ int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
                          void *workspace, size_t workspace_bytes, const float *background,
                          void *stream) {
   CamK k;
-  if (n < 0 || !prep_camera(cam, &k) || !set_background(background, &k))
-    return GS_ERR_INVALID_ARGUMENT;
-  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!tile_ranges || !rgb || !T_final || !last || !fwd_state) return GS_ERR_INVALID_ARGUMENT;
-  if (n > 0 && (!splats || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8)) return GS_ERR_INVALID_ARGUMENT;
-  if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
-  if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
-  const gs_sched sc = sched ? *sched : default_sched();
-  if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
-      !(sc.beta >= 0.0f))
-    return GS_ERR_INVALID_ARGUMENT;
-  const int workers = worker_waves();
-  if (workers <= 0) return GS_ERR_HIP;
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   (void)workspace; (void)workspace_bytes;
-  hipEvent_t e0, e1;
-  timing_slot(0, e0, e1);
-  return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
-                                         last, fwd_state, stats, workers, e0, e1,
-                                         (hipStream_t)stream));
+  return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
+                  fwd_state_bytes, stats, background, stream);
 }
 
 int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -305,25 +385,10 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
                          size_t workspace_bytes, const float *background, const float *dL_dT,
                          void *stream) {
   CamK k;
-  if (n < 0 || !prep_camera(cam, &k) || !set_background(background, &k))
-    return GS_ERR_INVALID_ARGUMENT;
-  if (dL_dT) k.bg_on = 1;
-  if (num_tiles(cam->width, cam->height) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!tile_ranges || !T_final || !last || !fwd_state || !dL_drgb) return GS_ERR_INVALID_ARGUMENT;
-  if (n > 0 && (!splats || !sorted_ids || !dL_dsplat)) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8) ||
-      (dL_dsplat && !aligned(dL_dsplat, 16)) || (dL_dT && !aligned(dL_dT, 4)))
-    return GS_ERR_INVALID_ARGUMENT;
-  if (fwd_state_bytes < gs_fwd_state_size(cam->width, cam->height)) return GS_ERR_WORKSPACE;
-  if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
-  const int workers = worker_waves();
-  if (workers <= 0) return GS_ERR_HIP;
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   (void)workspace; (void)workspace_bytes;
-  hipEvent_t e0, e1;
-  timing_slot(1, e0, e1);
-  return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
-                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, n, workers, e0,
-                                         e1, (hipStream_t)stream));
+  return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
+                  fwd_state_bytes, dL_drgb, dL_dsplat, background, dL_dT, stream);
 }
 
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -334,6 +399,115 @@ int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
   return gs_render_bwd_bg(n, splats, sorted_ids, tile_ranges, cam, T_final, last, fwd_state,
                           fwd_state_bytes, dL_drgb, dL_dsplat, workspace, workspace_bytes, nullptr,
                           nullptr, stream);
+}
+
+// ---------------------------------------------------------------- batches of views
+
+size_t gs_workspace_size_views(int32_t n, int32_t width, int32_t height, int32_t n_views,
+                               int64_t pair_capacity) {
+  if (n < 0 || width <= 0 || height <= 0 || pair_capacity < 0 || n_views < 1 ||
+      n_views > GS_MAX_VIEWS)
+    return 0;
+  return gs_sort_ws_bytes(n, pair_capacity, (width + 15) / 16, ((height + 15) / 16) * n_views);
+}
+
+size_t gs_fwd_state_size_views(int32_t width, int32_t height, int32_t n_views) {
+  if (width <= 0 || height <= 0 || n_views < 1 || n_views > GS_MAX_VIEWS) return 0;
+  const int64_t t = num_tiles(width, height) * n_views;
+  if (t > GS_MAX_TILES) return 0;
+  return fwd_layout((int)t).total;
+}
+
+int32_t gs_project_views(int32_t n, const float *means, const float *log_scales,
+                         const float *quats, const float *opacities, const float *sh,
+                         int32_t sh_degree, const gs_camera *cams, int32_t n_views,
+                         float *splats, void *stream) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_batch_cams(cams, n_views))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GS_OK;
+  if (!means || !log_scales || !quats || !opacities || !sh || !splats) return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(quats, 16) || !aligned(splats, 16) || !aligned(sh, sh_align(sh_degree, false)))
+    return GS_ERR_INVALID_ARGUMENT;
+  for (int v = 0; v < n_views; v++) {
+    CamK k;
+    prep_camera(&cams[v], &k);
+    k.view = v;
+    const hipError_t e = gs_launch_project(n, means, log_scales, quats, opacities, sh, false,
+                                           sh_degree, k, splats + (size_t)v * n * 12,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return GS_ERR_HIP;
+  }
+  return GS_OK;
+}
+
+int32_t gs_project_bwd_views(int32_t n, const float *means, const float *log_scales,
+                             const float *quats, const float *opacities, const float *sh,
+                             int32_t sh_degree, const gs_camera *cams, int32_t n_views,
+                             const float *dL_dsplat, float *dL_dmeans, float *dL_dlog_scales,
+                             float *dL_dquats, float *dL_dopacities, float *dL_dsh,
+                             void *stream) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !prep_batch_cams(cams, n_views))
+    return GS_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GS_OK;
+  if (!means || !log_scales || !quats || !opacities || !sh || !dL_dsplat || !dL_dmeans ||
+      !dL_dlog_scales || !dL_dquats || !dL_dopacities || !dL_dsh)
+    return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(quats, 16) || !aligned(dL_dquats, 16) ||
+      !aligned(sh, sh_align(sh_degree, false)) || !aligned(dL_dsh, sh_align(sh_degree, false)))
+    return GS_ERR_INVALID_ARGUMENT;
+  for (int v = 0; v < n_views; v++) {
+    CamK k;
+    prep_camera(&cams[v], &k);
+    k.view = v;
+    const hipError_t e = gs_launch_project_bwd(
+        n, means, log_scales, quats, opacities, sh, false, sh_degree, k,
+        dL_dsplat + (size_t)v * n * 9, dL_dmeans, dL_dlog_scales, dL_dquats, dL_dopacities,
+        dL_dsh, v > 0, (hipStream_t)stream);
+    if (e != hipSuccess) return GS_ERR_HIP;
+  }
+  return GS_OK;
+}
+
+int32_t gs_bin_tiles_views(int32_t n, const float *splats, const gs_camera *cam, int32_t n_views,
+                           int64_t pair_capacity, int32_t *offsets, uint64_t *keys, int32_t *ids,
+                           int32_t *device_status, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  CamK k;
+  if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return bin_impl(n, splats, k, pair_capacity, offsets, keys, ids, device_status, workspace,
+                  workspace_bytes, stream);
+}
+
+int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offsets,
+                           int64_t pair_capacity, const gs_camera *cam, int32_t n_views,
+                           uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  CamK k;
+  if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
+                   workspace, workspace_bytes, stream);
+}
+
+int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
+                            const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
+                            const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
+                            void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                            const float *background, void *stream) {
+  CamK k;
+  if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
+                  fwd_state_bytes, stats, background, stream);
+}
+
+int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
+                            const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
+                            const float *T_final, const int32_t *last, void *fwd_state,
+                            size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
+                            const float *background, const float *dL_dT, void *stream) {
+  CamK k;
+  if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
+                  fwd_state_bytes, dL_drgb, dL_dsplat, background, dL_dT, stream);
 }
 
 int32_t gs_timing_start(void) {

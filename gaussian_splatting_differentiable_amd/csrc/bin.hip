@@ -22,7 +22,7 @@
 namespace {
 
 __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict__ splats, int W,
-                                                  int H, int tiles_x, int tiles_y,
+                                                  int H, int tiles_x, int vty, int views,
                                                   const int32_t *__restrict__ offsets,
                                                   int64_t capacity, uint64_t *__restrict__ keys,
                                                   int32_t *__restrict__ ids) {
@@ -30,7 +30,7 @@ __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict
   const int64_t total = offsets[n];
   if (total > capacity || i >= n) return;
   const Splat s = splats[i];
-  const RowSpans r = spans_setup(s, tiles_y);
+  const RowSpans r = spans_setup(s, vty, views);
   if (!r.ok) return;
   const uint64_t depth_bits = (uint64_t)__float_as_uint(s.p2.z);
   int64_t pos = offsets[i];
@@ -38,7 +38,7 @@ __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict
     int a, b;
     row_span(r, ty, W, H, tiles_x, a, b);
     for (int tx = a; tx < b; tx++) {
-      keys[pos] = ((uint64_t)(uint32_t)(ty * tiles_x + tx) << 32) | depth_bits;
+      keys[pos] = ((uint64_t)(uint32_t)((r.row0 + ty) * tiles_x + tx) << 32) | depth_bits;
       ids[pos] = i;
       pos++;
     }
@@ -58,6 +58,6 @@ hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t ca
   hipError_t e = gs_launch_bin_count(n, splats, cam, capacity, offsets, status, ws, st);
   if (e != hipSuccess || !keys) return e;
   hipLaunchKernelGGL(k_bin_emit, grid, block, 0, st, n, sp, cam.width, cam.height, cam.tiles_x,
-                     cam.tiles_y, offsets, capacity, keys, ids);
+                     cam.vty, cam.views, offsets, capacity, keys, ids);
   return hipGetLastError();
 }

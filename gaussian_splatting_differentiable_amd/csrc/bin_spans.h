@@ -19,19 +19,26 @@
 
 struct RowSpans {
   float mx, my, a, b, c, det, at, rx, ry, dys;
-  int ty_a, ty_b;
+  int ty_a, ty_b;  // tile rows of the record's own view, [0, vty)
+  int row0;        // the view's first tile row in the batch image
   bool ok;
 };
 
 __device__ __forceinline__ float clampf(float v, float lo, float hi) { return fminf(fmaxf(v, lo), hi); }
 
-__device__ __forceinline__ RowSpans spans_setup(const Splat &s, int tiles_y) {
+// vty: tile rows per view; views: views in the batch. Spans are solved in the
+// record's own view (its coordinates); a tile row ty of that view is row
+// row0 + ty of the batch image. A record naming no view of the batch has none.
+__device__ __forceinline__ RowSpans spans_setup(const Splat &s, int vty, int views) {
   RowSpans r;
   r.mx = s.p0.x; r.my = s.p0.y; r.a = s.p0.z; r.b = s.p0.w; r.c = s.p1.x;
   const float tau = s.p2.y;
+  const int view = record_view(s);
   r.ok = false;
   r.ty_a = r.ty_b = 0;
-  if (!(tau > 0.0f)) return r;
+  r.row0 = view * vty;
+  const int tiles_y = vty;
+  if (!(tau > 0.0f) || view < 0 || view >= views) return r;
   const float tb = tau * GUARD_TAU;
   r.det = __builtin_fmaf(r.a, r.c, -(r.b * r.b));
   if (!(r.det > 0.0f) || !(r.a > 0.0f) || !(r.c > 0.0f)) return r;

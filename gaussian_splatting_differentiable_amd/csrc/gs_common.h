@@ -25,7 +25,16 @@ struct CamK {
   float znear, lowpass;
   float bg[3];      // background colour seen through the final transmittance
   int bg_on;        // bg is not black (or the backward has a dL/dT_final)
+  // A batch of `views` cameras of one size is one image of views x vty tile
+  // rows: view v owns tile rows [v vty, (v + 1) vty) and pixel rows
+  // [v height, (v + 1) height) of the outputs; tiles_y = views x vty. A splat
+  // record carries its view in its pad word (int bits; 0 for a single view).
+  int views, vty;
+  int view;         // the projection's camera index within its batch
 };
+
+// View index stored in a splat record's pad word.
+__device__ __forceinline__ int record_view(const Splat &s) { return __float_as_int(s.p2.w); }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -125,15 +125,26 @@ __device__ __forceinline__ void stage_rows_in(const uint4 *__restrict__ src, uin
   wave_sync();
 }
 
-// Store this wave's LDS rows [0, rows) to dst (row w0) with whole-wave vectors.
+// Store this wave's LDS rows [0, rows) to dst (row w0) with whole-wave vectors;
+// with acc, add them (as floats) to what dst holds.
 template <int V, int SV>
 __device__ __forceinline__ void stage_rows_out(uint4 *__restrict__ dst, int rows, const uint4 *lds,
-                                               int lane) {
+                                               int lane, bool acc = false) {
   wave_sync();
 #pragma unroll
   for (int j = 0; j < V; j++) {
     const int f = j * 64 + lane, r = f / V;
-    if (r < rows) dst[f] = lds[r * SV + (f - r * V)];
+    if (r < rows) {
+      uint4 v = lds[r * SV + (f - r * V)];
+      if (acc) {
+        const uint4 o = dst[f];
+        v = make_uint4(__float_as_uint(__uint_as_float(o.x) + __uint_as_float(v.x)),
+                       __float_as_uint(__uint_as_float(o.y) + __uint_as_float(v.y)),
+                       __float_as_uint(__uint_as_float(o.z) + __uint_as_float(v.z)),
+                       __float_as_uint(__uint_as_float(o.w) + __uint_as_float(v.w)));
+      }
+      dst[f] = v;
+    }
   }
 }
 
@@ -192,7 +203,8 @@ __global__ void __launch_bounds__(256) k_project(int n, const float *__restrict_
   Splat s;
   s.p0 = make_float4(0.f, 0.f, 0.f, 0.f);
   s.p1 = make_float4(0.f, 0.f, 0.f, 0.f);
-  s.p2 = make_float4(0.f, -1.0f, 0.f, 0.f);
+  const float vbits = __int_as_float(cam.view);  // the record's view (pad word)
+  s.p2 = make_float4(0.f, -1.0f, 0.f, vbits);
   bool need_sh = false;
   float d0 = 0.f, d1 = 0.f, d2 = 0.f;
   if (i < n) {
@@ -250,7 +262,7 @@ __global__ void __launch_bounds__(256) k_project(int n, const float *__restrict_
         s.p0 = make_float4(fmaf(cam.fx, ux, cam.cx), fmaf(cam.fy, uy, cam.cy), syy * idet,
                            -uv * idet);
         s.p1 = make_float4(sxx * idet, o, 0.f, 0.f);
-        s.p2 = make_float4(0.f, tau, tz, 0.0f);
+        s.p2 = make_float4(0.f, tau, tz, vbits);
         // colour from the view direction
         d0 = m0 - cam.centre[0]; d1 = m1 - cam.centre[1]; d2 = m2 - cam.centre[2];
         const float dn2 = d0 * d0 + d1 * d1 + d2 * d2;
@@ -338,7 +350,7 @@ __global__ void __launch_bounds__(256) k_project_bwd(
     const float4 *__restrict__ quats, const float *__restrict__ opac, const ShT *__restrict__ sh,
     CamK cam, const float *__restrict__ dsplat, float *__restrict__ gmeans,
     float *__restrict__ gls, float4 *__restrict__ gquats, float *__restrict__ gopac,
-    float *__restrict__ gsh) {
+    float *__restrict__ gsh, bool acc) {
   using RI = RowVecs<K * 3 * (int)sizeof(ShT)>;  // SH rows read
   using RO = RowVecs<K * 3 * 4>;                 // SH gradient rows written (fp32)
   constexpr int SV = RI::SV > RO::SV ? RI::SV : RO::SV;
@@ -491,7 +503,17 @@ __global__ void __launch_bounds__(256) k_project_bwd(
     g1 = fmaf(e1 - d1 * ed, dinv, g1);
     g2 = fmaf(e2 - d2 * ed, dinv, g2);
   }
-  if (i < n) {
+  if (i < n && acc) {  // another view's share of the same Gaussians' gradients
+    gmeans[3 * i] += g0;
+    gmeans[3 * i + 1] += g1;
+    gmeans[3 * i + 2] += g2;
+    gls[3 * i] += dls[0];
+    gls[3 * i + 1] += dls[1];
+    gls[3 * i + 2] += dls[2];
+    const float4 o4 = gquats[i];
+    gquats[i] = make_float4(o4.x + gq.x, o4.y + gq.y, o4.z + gq.z, o4.w + gq.w);
+    gopac[i] += gop;
+  } else if (i < n) {
     gmeans[3 * i] = g0;
     gmeans[3 * i + 1] = g1;
     gmeans[3 * i + 2] = g2;
@@ -513,12 +535,12 @@ __global__ void __launch_bounds__(256) k_project_bwd(
             make_uint4(__float_as_uint(row[4 * j]), __float_as_uint(row[4 * j + 1]),
                        __float_as_uint(row[4 * j + 2]), __float_as_uint(row[4 * j + 3]));
       stage_rows_out<RO::V, RO::SV>(reinterpret_cast<uint4 *>(gsh) + (size_t)w0 * RO::V,
-                                    min(64, n - w0), lds_wave, lane);
+                                    min(64, n - w0), lds_wave, lane, acc);
     }
   } else if (i < n) {
     float *gsh_i = gsh + (size_t)i * (K * 3);
 #pragma unroll
-    for (int j = 0; j < K * 3; j++) gsh_i[j] = row[j];
+    for (int j = 0; j < K * 3; j++) gsh_i[j] = acc ? gsh_i[j] + row[j] : row[j];
   }
 }
 
@@ -526,16 +548,16 @@ template <typename ShT>
 hipError_t launch_project_bwd(int n, const float *means, const float *log_scales,
                               const float *quats, const float *opac, const ShT *sh, int degree,
                               const CamK &cam, const float *dsplat, float *gmeans, float *gls,
-                              float *gquats, float *gopac, float *gsh, hipStream_t st) {
+                              float *gquats, float *gopac, float *gsh, bool acc, hipStream_t st) {
   if (n == 0) return hipSuccess;
   dim3 grid(gs_div_up(n, 256)), block(256);
   const float4 *q4 = reinterpret_cast<const float4 *>(quats);
   float4 *gq4 = reinterpret_cast<float4 *>(gquats);
   switch (degree) {
-    case 0: hipLaunchKernelGGL((k_project_bwd<1, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
-    case 1: hipLaunchKernelGGL((k_project_bwd<4, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
-    case 2: hipLaunchKernelGGL((k_project_bwd<9, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
-    default: hipLaunchKernelGGL((k_project_bwd<16, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh); break;
+    case 0: hipLaunchKernelGGL((k_project_bwd<1, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh, acc); break;
+    case 1: hipLaunchKernelGGL((k_project_bwd<4, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh, acc); break;
+    case 2: hipLaunchKernelGGL((k_project_bwd<9, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh, acc); break;
+    default: hipLaunchKernelGGL((k_project_bwd<16, ShT>), grid, block, 0, st, n, means, log_scales, q4, opac, sh, cam, dsplat, gmeans, gls, gq4, gopac, gsh, acc); break;
   }
   return hipGetLastError();
 }
@@ -573,11 +595,11 @@ hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_sca
                                  const float *quats, const float *opac, const void *sh,
                                  bool sh_bf16, int degree, const CamK &cam, const float *dsplat,
                                  float *gmeans, float *gls, float *gquats, float *gopac,
-                                 float *gsh, hipStream_t st) {
+                                 float *gsh, bool acc, hipStream_t st) {
   return sh_bf16 ? launch_project_bwd(n, means, log_scales, quats, opac,
                                       static_cast<const uint16_t *>(sh), degree, cam, dsplat,
-                                      gmeans, gls, gquats, gopac, gsh, st)
+                                      gmeans, gls, gquats, gopac, gsh, acc, st)
                  : launch_project_bwd(n, means, log_scales, quats, opac,
                                       static_cast<const float *>(sh), degree, cam, dsplat, gmeans,
-                                      gls, gquats, gopac, gsh, st);
+                                      gls, gquats, gopac, gsh, acc, st);
 }

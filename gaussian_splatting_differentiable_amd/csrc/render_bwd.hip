@@ -243,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
   int *sid = sid_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
   const int k = fs.hdr->k;
-  const int64_t P = (int64_t)cam.width * cam.height;
+  const int64_t P = (int64_t)cam.width * cam.height * cam.views;
   const int lane = __lane_id();
   __shared__ uint32_t drained;
   Worker wk = make_worker(&drained);
@@ -259,7 +259,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     if (st.empty) continue;
     const int px = st.x0 + (lane & 7), py = st.y0 + (lane >> 3);
     const bool inside = px < cam.width && py < cam.height;
-    const int64_t pix = (int64_t)py * cam.width + px;
+    const int64_t pix = (int64_t)(st.prow + py) * cam.width + px;
     const int2 rg = ranges[tile];
     float g0 = 0.f, g1 = 0.f, g2 = 0.f;
     // what lies behind the last blended splat, per unit of final transmittance:

@@ -145,7 +145,8 @@ __device__ __forceinline__ void chunk_range(int start, int end, int p, int k, in
 }
 
 struct SubTile {
-  int tile, quad, x0, y0;
+  int tile, quad, x0, y0;    // x0, y0 in the coordinates of the tile's view
+  int prow;                  // the view's first pixel row in the batch outputs
   float hx0, hx1, hy0, hy1;  // sample hull of the 8x8 quarter
   bool empty;
 };
@@ -154,7 +155,9 @@ __device__ __forceinline__ SubTile subtile_of(int tile, int quad, const CamK &ca
   SubTile st;
   st.tile = tile;
   st.quad = quad;
-  const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
+  const int tx = tile % cam.tiles_x, tyb = tile / cam.tiles_x;
+  const int view = tyb / cam.vty, ty = tyb - view * cam.vty;
+  st.prow = view * cam.height;
   st.x0 = tx * 16 + (quad & 1) * 8;
   st.y0 = ty * 16 + (quad >> 1) * 8;
   st.empty = st.x0 >= cam.width || st.y0 >= cam.height;

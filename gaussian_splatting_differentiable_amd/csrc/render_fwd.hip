@@ -50,7 +50,7 @@ __device__ __forceinline__ Px pixel_of(const SubTile &st, const CamK &cam) {
   x.inside = px < cam.width && py < cam.height;
   x.fx = (float)px + 0.5f;
   x.fy = (float)py + 0.5f;
-  x.p = py * cam.width + px;
+  x.p = (st.prow + py) * cam.width + px;
   return x;
 }
 
@@ -228,7 +228,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
   Splat *sbuf = sbuf_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, T);
   const int k = fs.hdr->k;
-  const int P = cam.width * cam.height;
+  const int P = cam.width * cam.height * cam.views;
   const int lane = __lane_id();
   uint32_t nhits = 0, nsteps = 0, nhsteps = 0;  // per worker; far below 2^32
   __shared__ uint32_t drained;

@@ -172,8 +172,8 @@ __global__ void __launch_bounds__(1024) k_bin_init(SortCtl *__restrict__ ctl,
 // per row, however long the span) for the sort; clears the sort's look-back
 // words. Block b counts the splats [b chunk, (b + 1) chunk).
 __global__ void __launch_bounds__(BIN_T) k_bin_count(
-    int n, const Splat *__restrict__ splats, int W, int H, int tiles_x, int tiles_y,
-    int32_t *__restrict__ counts, int chunk, int32_t *__restrict__ bin_sum,
+    int n, const Splat *__restrict__ splats, int W, int H, int tiles_x, int tiles_y, int vty,
+    int views, int32_t *__restrict__ counts, int chunk, int32_t *__restrict__ bin_sum,
     uint32_t *__restrict__ dkey, SortCtl *__restrict__ ctl, int32_t *__restrict__ tile_diff,
     uint32_t *__restrict__ status, int64_t nstatus) {
   __shared__ uint32_t dh[4][256];
@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
   int csum = 0;
   for (int i = i0 + threadIdx.x; i < i1; i += BIN_T) {
     const Splat s = splats[i];
-    const RowSpans r = spans_setup(s, tiles_y);
+    const RowSpans r = spans_setup(s, vty, views);
     int cnt = 0;
     if (r.ok) {
       for (int ty = r.ty_a; ty < r.ty_b; ty++) {
@@ -201,8 +201,8 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
         row_span(r, ty, W, H, tiles_x, a, b);
         if (b > a) {
           int32_t *h = lds_hist ? th : tile_diff;
-          atomicAdd(&h[ty * stride + a], 1);
-          atomicAdd(&h[ty * stride + b], -1);
+          atomicAdd(&h[(r.row0 + ty) * stride + a], 1);
+          atomicAdd(&h[(r.row0 + ty) * stride + b], -1);
           cnt += b - a;
         }
       }
@@ -390,6 +390,7 @@ struct PassIn {
   const int32_t *part_first;   // SRC_EMIT
   const Splat *splats;         // SRC_EMIT
   int W, H, tiles_x, tiles_y;  // SRC_EMIT; SRC_DEPTH0's extra workgroup (tiles)
+  int vty, views;              // SRC_EMIT: the batch's views
   const int32_t *tile_diff;    // SRC_DEPTH0's extra workgroup: tile counts and ranges
   int32_t *tile_counts, *ranges;
   int b0;
@@ -478,7 +479,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
         if (gg[u] < 0) continue;
         const int g = gg[u];
         int64_t q = qq[u];
-        const RowSpans rs = spans_setup(sp[u], in.tiles_y);
+        const RowSpans rs = spans_setup(sp[u], in.vty, in.views);
         if (!rs.ok) continue;
         for (int ty = rs.ty_a; ty < rs.ty_b && q < p0 + nv; ty++) {
           int a, b;
@@ -487,7 +488,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
           if (q + (b - a) > p0) {
             const int64_t q0 = q > p0 ? q : p0;
             const int sl = (int)(q0 - p0);
-            s_key[sl] = (uint32_t)(ty * in.tiles_x + a + (int)(q0 - q));
+            s_key[sl] = (uint32_t)((rs.row0 + ty) * in.tiles_x + a + (int)(q0 - q));
             s_val[sl] = (uint32_t)g;
             atomicOr(&s_mark[sl >> 5], 1u << (sl & 31));
           }
@@ -732,8 +733,8 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
   const size_t lds = ndiff <= HIST_TILES_LDS ? 4 * (size_t)ndiff : 0;
   hipLaunchKernelGGL(k_bin_count, dim3(blocks), dim3(BIN_T), lds, st, n,
                      reinterpret_cast<const Splat *>(splats), cam.width, cam.height, cam.tiles_x,
-                     cam.tiles_y, offsets, chunk, w.bin_sum, w.dkey, w.ctl, w.tile_diff, w.status,
-                     w.nstatus);
+                     cam.tiles_y, cam.vty, cam.views, offsets, chunk, w.bin_sum, w.dkey, w.ctl,
+                     w.tile_diff, w.status, w.nstatus);
   hipLaunchKernelGGL(k_bin_offsets, dim3(blocks), dim3(BIN_T), 0, st, n, chunk, w.bin_sum,
                      offsets, cap, status);
   return hipGetLastError();
@@ -812,6 +813,8 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   e.H = cam.height;
   e.tiles_x = cam.tiles_x;
   e.tiles_y = cam.tiles_y;
+  e.vty = cam.vty;
+  e.views = cam.views;
   uint32_t *final_tiles = nullptr;
   if (tbits <= 8) {
     final_tiles = sorted_keys ? w.tk[1] : nullptr;

@@ -24,10 +24,13 @@
  *
  * Data layouts
  *   splat record (GS_SPLAT_FLOATS = 12 floats, 48 B, 16-B aligned):
- *       mx, my, a, b, c, o, r, g, b, tau, depth, 0
+ *       mx, my, a, b, c, o, r, g, b, tau, depth, view
  *     (mx, my) centre in pixels; (a, b, c) the conic Sigma'^-1 = [[a,b],[b,c]];
  *     o opacity; (r, g, b) colour; tau = 2 ln(255 o), the alpha >= 1/255
- *     cutoff as a bound on q; depth = camera-space z. Culled: tau = -1, rest 0.
+ *     cutoff as a bound on q; depth = camera-space z; view: the record's view
+ *     in a batch of views, as int bits (0, i.e. 0.0f, outside batches; a record
+ *     whose view is not in the batch emits no pairs). Culled: tau = -1, the
+ *     others 0 but view.
  *   pixel (px, py) is sampled at (px + 0.5, py + 0.5);
  *     q = a dx^2 + 2 b dx dy + c dy^2, evaluated in the canonical fp32 form
  *     fma(c*dy, dy, fma((2b)*dx, dy, (a*dx)*dx)); a pixel is hit iff q <= tau.
@@ -58,6 +61,7 @@ typedef enum {
 #define GS_TILE 16
 #define GS_SPLAT_FLOATS 12
 #define GS_GRAD_FLOATS 9
+#define GS_MAX_VIEWS 16 /* views in one batch (the *_views calls) */
 
 /* Pinhole camera, passed by HOST pointer. world_to_cam is row-major [R | t]
  * (camera: +x right, +y down, +z forward). Gaussians with t_z <= znear are
@@ -250,6 +254,59 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
                          const float *dL_drgb, float *dL_dsplat, void *workspace,
                          size_t workspace_bytes, const float *background, const float *dL_dT,
                          void *stream);
+
+/* Batches of views: n_views cameras of one size (1 <= n_views <= GS_MAX_VIEWS)
+ * rendered as one image, so that binning, sorting and each of the two
+ * persistent raster kernels run once for the whole batch (one schedule, one
+ * longest-first queue over every view's tiles). Not on the pages; each view's
+ * results are those of the single-view calls on that view.
+ *   Layout: view v's splat records are rows [v n, (v + 1) n) of splats (n
+ *   Gaussians per view; the record's pad word holds v as int bits; the bin,
+ *   sort and render calls take the record count n_views n as their n); its tiles
+ *   are tile rows [v ty, (v + 1) ty) of the batch (ty = ceil(height / 16)),
+ *   so tile ids run over tiles_x x (n_views ty) tiles; its pixels are rows
+ *   [v height, (v + 1) height) of rgb [3][n_views height][width], T_final and
+ *   last [n_views height][width], and of dL_drgb and dL_dT.
+ *   cam (bin, sort, render): any camera of the batch (only its size is used).
+ *   Sizes: gs_workspace_size_views and gs_fwd_state_size_views (0 on invalid
+ *   arguments or more than 65535 tiles in the batch).
+ *   gs_project_views: splats [n_views n][12] <- gs_project with cams[v] for
+ *     rows of view v. cams[n_views], all of one width and height.
+ *   gs_project_bwd_views: dL_dsplat [n_views n][9] -> the per-Gaussian outputs
+ *     of gs_project_bwd, summed over the views (fully overwritten).
+ *   Everything else as for the single-view calls (the render calls take the
+ *   background and dL/dT_final arguments of gs_render_fwd_bg/gs_render_bwd_bg). */
+size_t gs_workspace_size_views(int32_t n, int32_t width, int32_t height, int32_t n_views,
+                               int64_t pair_capacity);
+size_t gs_fwd_state_size_views(int32_t width, int32_t height, int32_t n_views);
+int32_t gs_project_views(int32_t n, const float *means, const float *log_scales,
+                         const float *quats, const float *opacities, const float *sh,
+                         int32_t sh_degree, const gs_camera *cams, int32_t n_views,
+                         float *splats, void *stream);
+int32_t gs_project_bwd_views(int32_t n, const float *means, const float *log_scales,
+                             const float *quats, const float *opacities, const float *sh,
+                             int32_t sh_degree, const gs_camera *cams, int32_t n_views,
+                             const float *dL_dsplat, float *dL_dmeans, float *dL_dlog_scales,
+                             float *dL_dquats, float *dL_dopacities, float *dL_dsh,
+                             void *stream);
+int32_t gs_bin_tiles_views(int32_t n, const float *splats, const gs_camera *cam, int32_t n_views,
+                           int64_t pair_capacity, int32_t *offsets, uint64_t *keys, int32_t *ids,
+                           int32_t *device_status, void *workspace, size_t workspace_bytes,
+                           void *stream);
+int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offsets,
+                           int64_t pair_capacity, const gs_camera *cam, int32_t n_views,
+                           uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
+                           void *workspace, size_t workspace_bytes, void *stream);
+int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
+                            const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
+                            const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
+                            void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                            const float *background, void *stream);
+int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
+                            const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
+                            const float *T_final, const int32_t *last, void *fwd_state,
+                            size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
+                            const float *background, const float *dL_dT, void *stream);
 
 /* Kernel timing, for measurement only (no paper passage: it lets a benchmark
  * divide algorithmic bytes by the raster kernel's own duration rather than by

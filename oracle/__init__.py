@@ -281,3 +281,45 @@ def frame(scene, fwd=True, bwd=True, bg=None, dL_dT=None):
         out["grads"] = render_bwd(splats, sids, ranges, W, H, out["fwd"]["last"], scene.dL_drgb,
                                   bg=bg, dL_dT=dL_dT)
     return out
+
+
+def frame_views(scene, cams, dL_drgbs, bg=None, dL_dTs=None):
+    """A batch of views as the batch calls lay it out, built from one oracle frame
+    per view: view v's records are rows [v n, (v + 1) n) with v in their pad word,
+    its tiles follow the tiles of the views before it, its pixels their rows.
+    dL_drgbs[v] [3][H][W] and dL_dTs[v] [H][W] (or None) are view v's gradients."""
+    import dataclasses
+    n = scene.n
+    per = []
+    for v, cam in enumerate(cams):
+        sc = dataclasses.replace(scene, camera=cam, dL_drgb=dL_drgbs[v])
+        per.append(frame(sc, bg=bg, dL_dT=None if dL_dTs is None else dL_dTs[v]))
+    T1 = cams[0].num_tiles
+    splats, offs, keys, ids, skeys, sids, ranges = [], [], [], [], [], [], []
+    base = 0
+    for v, f in enumerate(per):
+        s = f["splats"].copy()
+        s[:, 11] = np.array([v], np.int32).view(np.float32)[0]
+        splats.append(s)
+        offs.append(f["offsets"][:-1] + base)
+        shift = np.uint64(v * T1) << np.uint64(32)
+        keys.append(f["keys"] + shift)
+        ids.append(f["ids"] + v * n)
+        skeys.append(f["sorted_keys"] + shift)
+        sids.append(f["sorted_ids"] + v * n)
+        ranges.append(f["ranges"] + base)
+        base += len(f["ids"])
+    out = dict(splats=np.concatenate(splats), offsets=np.concatenate(offs + [np.array([base])]),
+               keys=np.concatenate(keys), ids=np.concatenate(ids).astype(np.int32),
+               sorted_keys=np.concatenate(skeys), sorted_ids=np.concatenate(sids).astype(np.int32),
+               ranges=np.concatenate(ranges).astype(np.int32))
+    if "fwd" in per[0]:
+        fw = [f["fwd"] for f in per]
+        out["fwd"] = dict(rgb=np.concatenate([f["rgb"] for f in fw], axis=1),
+                          T=np.concatenate([f["T"] for f in fw]),
+                          last=np.concatenate([f["last"] for f in fw]),
+                          knife=np.concatenate([f["knife"] for f in fw]),
+                          hits=sum(f["hits"] for f in fw), evals=sum(f["evals"] for f in fw))
+    if "grads" in per[0]:
+        out["grads"] = np.concatenate([f["grads"] for f in per])
+    return out
