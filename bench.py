@@ -106,6 +106,8 @@ def parse():
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--chunk-mode", type=int, default=1)
+    p.add_argument("--views", type=int, default=4,
+                   help="views of the batched-views stage (below 2: skip it)")
     return p.parse_args()
 
 
@@ -132,6 +134,94 @@ def cpu_baseline(sc, npairs_gpu):
             "sample": f"{frames} whole frames of the same scene through the oracle's bin, sort, "
                       f"forward and backward ({t_total:.1f} s; {pairs // frames} pairs per frame, "
                       f"GPU {npairs_gpu})"}
+
+
+def views_stage(args, sc, gsr, dev, means, ls, qs, op, sh):
+    """The same scene seen by V cameras (the scene's own and V - 1 moved ones):
+    one batch (the *_views calls: one bin, sort, forward and backward launch
+    sequence for all views) against V single-view frames one after another.
+    Both are timed over the same steps with the wall clock (bin, sort, forward,
+    backward; the projections stay outside, as in the main step)."""
+    import numpy as np
+    import torch
+    import scenegen
+    V = args.views
+    rng = np.random.default_rng(77)
+    c0 = sc.camera
+    M0 = np.asarray(c0.world_to_cam, np.float64).reshape(3, 4)
+    cams = [c0]
+    for _ in range(V - 1):
+        a = rng.normal(0, 0.05, 3)
+        K = np.array([[0, -a[2], a[1]], [a[2], 0, -a[0]], [-a[1], a[0], 0]])
+        R = np.linalg.qr(np.eye(3) + K)[0]
+        R *= np.sign(np.diag(R))[None, :]   # the rotation near the identity
+        cams.append(scenegen.pinhole(c0.width, c0.height, float(c0.fx),
+                                     np.concatenate([R @ M0[:, :3],
+                                                     (M0[:, 3] + rng.normal(0, 0.05, 3))[:, None]],
+                                                    1)))
+    n = sc.n
+    gen = torch.Generator(device=dev).manual_seed(78)
+    dL = torch.randn((3, V * c0.height, c0.width), generator=gen, device=dev)
+
+    def grow(r, nrec):
+        I = r.bin_and_sort(nrec)
+        r._ensure(nrec, max(r.capacity, I + I // 8))
+        return r.bin_and_sort(nrec)
+
+    def step(r, nrec, dLv):
+        # the raw calls, as in the main step (no host synchronisation inside)
+        if r.V > 1:
+            gsr.gs_bin_tiles_views(nrec, r.splats, r.cam, r.V, r.capacity, r.offsets, None, None,
+                                   r.status, r.workspace)
+            gsr.gs_sort_keys_views(nrec, r.splats, r.offsets, r.capacity, r.cam, r.V, None,
+                                   r.sorted_ids, r.ranges, r.workspace)
+            gsr.gs_render_fwd_views(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.V, r.sched,
+                                    r.rgb, r.T, r.last, r.fwd_state, None)
+            gsr.gs_render_bwd_views(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.V, r.T,
+                                    r.last, r.fwd_state, dLv, r.grads)
+        else:
+            gsr.gs_bin_tiles(nrec, r.splats, r.cam, r.capacity, r.offsets, None, None, r.status,
+                             r.workspace)
+            gsr.gs_sort_keys(nrec, r.splats, r.offsets, r.capacity, r.cam, None, r.sorted_ids,
+                             r.ranges, r.workspace)
+            gsr.gs_render_fwd(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
+                              r.last, r.fwd_state, None, r.workspace)
+            gsr.gs_render_bwd(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last,
+                              r.fwd_state, dLv, r.grads, r.workspace)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / args.steps
+
+    rb = gsr.Rasterizer(c0, device=dev, capacity=1 << 24, n_views=V)
+    rb.project_views(cams, means, ls, qs, op, sh, sc.sh_degree)
+    pairs_b = grow(rb, V * n)
+    ms_b = timed(lambda: step(rb, V * n, dL))
+    if int(rb.status.item()) != gsr.GS_OK:
+        raise SystemExit("pair buffer overflow in the batched-views stage")
+    del rb
+    ms_seq, pairs_seq = 0.0, 0
+    H = c0.height
+    for v, cam in enumerate(cams):
+        r = gsr.Rasterizer(cam, device=dev, capacity=1 << 23)
+        r.project(means, ls, qs, op, sh, sc.sh_degree)
+        pairs_seq += grow(r, n)
+        dLv = dL[:, v * H:(v + 1) * H].contiguous()
+        ms_seq += timed(lambda: step(r, n, dLv))
+        if int(r.status.item()) != gsr.GS_OK:
+            raise SystemExit("pair buffer overflow in the batched-views stage")
+        del r
+    torch.cuda.synchronize()
+    return {"n_views": V, "pairs": pairs_b, "pairs_single_views": pairs_seq,
+            "ms_batch_step": round(ms_b, 4), "ms_single_view_steps": round(ms_seq, 4),
+            "pairs_per_s_batch": round(pairs_b / (ms_b * 1e-3), 1),
+            "pairs_per_s_single_views": round(pairs_seq / (ms_seq * 1e-3), 1)}
 
 
 def main():
@@ -339,6 +429,8 @@ def main():
             "roofline_frac": round(parts[bound] / (float(np.median(v)) * 1e-3), 4)}
     ms_fwd_total = ms["bin"] + ms["sort"] + ms["fwd"]
 
+    views = None if args.views < 2 else views_stage(args, sc, gsr, dev, means, ls, qs, op, sh)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(sc, npairs)
 
     line = {
@@ -367,6 +459,7 @@ def main():
         "ms_frame": round(ms_project + ms_fwd_total + ms["bwd"], 4),
         "n_visible": n_vis, "n_touched": n_touched, "n_touched_visible": n_touched_vis,
         "stages": stage_lines,
+        "views": views,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

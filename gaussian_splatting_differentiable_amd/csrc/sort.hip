@@ -41,7 +41,11 @@ namespace {
 
 constexpr uint32_t ST_AGG = 1u << 30, ST_INC = 2u << 30, ST_CNT = (1u << 30) - 1;
 constexpr int SPIN_LIMIT = 1 << 22;
-constexpr int HIST_TILES_LDS = 16384;  // tile histogram kept in LDS up to this many tiles
+// The counting kernel keeps its workgroup's tile-count difference array in LDS
+// up to this many words (144 KB: a batch of views has several images' tiles);
+// beyond it, or if the device refuses that much LDS, it adds to the global
+// array directly, which costs far more in atomics.
+constexpr int HIST_TILES_LDS = 36864;
 constexpr int SCAN_T = 256, SCAN_I = 8, SCAN_TILE = SCAN_T * SCAN_I;
 constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pairs (a NaN pattern)
 constexpr int BIN_T = 512, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
@@ -175,12 +179,11 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
     int n, const Splat *__restrict__ splats, int W, int H, int tiles_x, int tiles_y, int vty,
     int views, int32_t *__restrict__ counts, int chunk, int32_t *__restrict__ bin_sum,
     uint32_t *__restrict__ dkey, SortCtl *__restrict__ ctl, int32_t *__restrict__ tile_diff,
-    uint32_t *__restrict__ status, int64_t nstatus) {
+    uint32_t *__restrict__ status, int64_t nstatus, bool lds_hist) {
   __shared__ uint32_t dh[4][256];
-  extern __shared__ int th[];  // the difference array, when it fits (sized at launch)
+  extern __shared__ int th[];  // the difference array, when lds_hist (sized at launch)
   const int stride = tiles_x + 1;
   const int ndiff = tiles_y * stride;
-  const bool lds_hist = ndiff <= HIST_TILES_LDS;
   for (int i = threadIdx.x; i < 1024; i += BIN_T) (&dh[0][0])[i] = 0;
   if (lds_hist)
     for (int i = threadIdx.x; i < ndiff; i += BIN_T) th[i] = 0;
@@ -730,11 +733,17 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
                      cam.tiles_y * (cam.tiles_x + 1));
   const int chunk = bin_chunk(n), blocks = bin_blocks(n);
   const int ndiff = cam.tiles_y * (cam.tiles_x + 1);
-  const size_t lds = ndiff <= HIST_TILES_LDS ? 4 * (size_t)ndiff : 0;
+  size_t lds = ndiff <= HIST_TILES_LDS ? 4 * (size_t)ndiff : 0;
+  if (lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(k_bin_count),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    (void)hipGetLastError();
+    lds = 0;
+  }
   hipLaunchKernelGGL(k_bin_count, dim3(blocks), dim3(BIN_T), lds, st, n,
                      reinterpret_cast<const Splat *>(splats), cam.width, cam.height, cam.tiles_x,
                      cam.tiles_y, cam.vty, cam.views, offsets, chunk, w.bin_sum, w.dkey, w.ctl,
-                     w.tile_diff, w.status, w.nstatus);
+                     w.tile_diff, w.status, w.nstatus, lds > 0);
   hipLaunchKernelGGL(k_bin_offsets, dim3(blocks), dim3(BIN_T), 0, st, n, chunk, w.bin_sum,
                      offsets, cap, status);
   return hipGetLastError();
