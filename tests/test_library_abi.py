@@ -85,6 +85,21 @@ def test_argument_validation_needs_no_gpu(gsr):
                               None, 0, nanbg, None, None) == -1
     assert L.gs_render_bwd_bg(1, p16, p16, p16, C.byref(cam), p16, p16, st256, 1 << 30, p16, p16,
                               None, 0, None, C.c_void_p(18), None) == -1
+    # batches of views: sizes are those of the stacked image; bad batches are rejected
+    assert L.gs_fwd_state_size_views(64, 45, 3) == L.gs_fwd_state_size(64, 3 * 48)
+    assert L.gs_workspace_size_views(1000, 83, 45, 4, 5000) == L.gs_workspace_size(1000, 83, 4 * 48,
+                                                                                    5000)
+    assert L.gs_fwd_state_size_views(64, 64, 0) == 0 and L.gs_fwd_state_size_views(64, 64, 17) == 0
+    assert L.gs_bin_tiles_views(1, p16, C.byref(cam), 0, 10, p16, None, None, p16, p16, 1 << 30,
+                                None) == -1
+    assert L.gs_render_fwd_views(1, p16, p16, p16, C.byref(cam), 17, None, p16, p16, p16, st256,
+                                 1 << 30, None, None, None) == -1
+    assert L.gs_project_views(1, p16, p16, p16, p16, p16, 0, None, 2, p16, None) == -1
+    cams2 = (gsr.GsCamera * 2)(cam, cam)
+    cams2[1].width = 80                                   # views of different sizes
+    assert L.gs_project_views(1, p16, p16, p16, p16, p16, 0, cams2, 2, p16, None) == -1
+    assert L.gs_project_bwd_views(1, p16, p16, p16, p16, p16, 0, cams2, 2, p16, p16, p16, p16, p16,
+                                  p16, None) == -1
     big = gsr.GsCamera()
     big.width, big.height, big.fx, big.fy = 1 << 14, 1 << 14, 1.0, 1.0
     assert L.gs_bin_tiles(1, C.c_void_p(16), C.byref(big), 10, C.c_void_p(16), C.c_void_p(16),
