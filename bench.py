@@ -106,8 +106,9 @@ def parse():
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--chunk-mode", type=int, default=1)
-    p.add_argument("--views", type=int, default=4,
-                   help="views of the batched-views stage (below 2: skip it)")
+    p.add_argument("--views", type=int, default=0,
+                   help="also time a batch of this many views against as many single-view "
+                        "steps (below 2, the default: skip)")
     return p.parse_args()
 
 
