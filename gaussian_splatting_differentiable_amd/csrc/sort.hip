@@ -51,7 +51,7 @@ constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pair
 constexpr int BIN_T = 512, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
 
 // partitions: depth passes and tile passes
-constexpr int DS_THREADS = 1024, DS_ITEMS = 8, DS_PART = DS_THREADS * DS_ITEMS;
+constexpr int DS_THREADS = 1024, DS_ITEMS = 6, DS_PART = DS_THREADS * DS_ITEMS;
 constexpr int TS_THREADS = 512, TS_ITEMS = 16, TS_PART = TS_THREADS * TS_ITEMS;
 
 // Per-frame control block at the start of the workspace.
