@@ -46,7 +46,7 @@ constexpr int SPIN_LIMIT = 1 << 22;
 // beyond it, or if the device refuses that much LDS, it adds to the global
 // array directly, which costs far more in atomics.
 constexpr int HIST_TILES_LDS = 36864;
-constexpr int SCAN_T = 256, SCAN_I = 8, SCAN_TILE = SCAN_T * SCAN_I;
+constexpr int SCAN_T = 256, SCAN_I = 4, SCAN_TILE = SCAN_T * SCAN_I;
 constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pairs (a NaN pattern)
 constexpr int BIN_T = 512, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
 
@@ -578,7 +578,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
       st_status(&status[me], ST_AGG | (uint32_t)total);
       // walk back LBW predecessors per round trip: sum aggregates up to the
       // first inclusive prefix; wait where a predecessor has not published
-      constexpr int LBW = 16;
+      constexpr int LBW = 4;
       int p = part - 1;
       int spins = 0;
       while (p >= 0) {
