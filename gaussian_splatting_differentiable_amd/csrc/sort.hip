@@ -456,8 +456,9 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     // of its first pair here (s_key: that pair's tile, s_val: the splat) and
     // sets that position's bit in s_mark; a pair's key is then its row's first
     // tile plus its distance from the row start. Each thread takes GEN splats
-    // at a time with all their loads in flight together.
-    constexpr int GEN = 4;
+    // at a time with their loads in flight together (one: more splats per
+    // thread measured slower, 2 µs per added splat per frame).
+    constexpr int GEN = 1;
     for (int i = tid; i < PART / 32; i += NT) s_mark[i] = 0u;
     __syncthreads();
     const int nv = (int)min((int64_t)PART, n - p0);
