@@ -72,8 +72,8 @@ def _load():
         "or_bin_emit": [i32, P, i32, i32, P, P, P],
         "or_sort_pairs": [i64, P, P, P, P],
         "or_tile_ranges": [i64, P, i32, P],
-        "or_render_fwd": [P, P, P, i32, i32, P, P, P, P, P, P, P],
-        "or_render_fwd_untiled": [i32, P, i32, i32, P, P],
+        "or_render_fwd": [P, P, P, i32, i32, P, P, P, P, P, P, P, P, P],
+        "or_render_fwd_untiled": [i32, P, i32, i32, P, P, P],
         "or_render_fwd_values": [P, P, P, P, i32, i32, P, P, P, P],
         "or_render_bwd": [P, P, P, i32, i32, P, P, P, P, i32, P],
         "or_chunk_policy": [i32, P, dbl, dbl, dbl, dbl, i32, P, P],
@@ -83,6 +83,7 @@ def _load():
         fn.argtypes = args
         fn.restype = None
     lib.or_num_threads.argtypes, lib.or_num_threads.restype = [], C.c_int
+    lib.or_set_num_threads.argtypes, lib.or_set_num_threads.restype = [C.c_int], None
     _lib = lib
     return lib
 
@@ -97,6 +98,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's later parallel loops."""
+    _load().or_set_num_threads(int(n))
 
 
 def sh_basis(degree: int, d) -> np.ndarray:
@@ -205,29 +211,38 @@ def _bg(bg, dtype):
 
 def render_fwd(splats, sorted_ids, ranges, width, height, tile_mask=None, bg=None):
     """Mirror forward (bg: background colour, black when None).
-    Returns dict(rgb[3,H,W], T[H,W], last[H,W], knife[H,W], hits, evals)."""
+    Returns dict(rgb[3,H,W], T[H,W], last[H,W], knife[H,W], hits, evals,
+    pixel_hits[H,W] (splats blended per pixel), pair_quarters[I] (bit q: some
+    pixel of quarter q of the pair's tile blended it))."""
     splats, sorted_ids = _c(splats, np.float32), _c(sorted_ids, np.int32)
     ranges = _c(ranges, np.int32)
     rgb = np.zeros((3, height, width), np.float32)
     T = np.zeros((height, width), np.float32)
     last = np.zeros((height, width), np.int32)
     knife = np.zeros((height, width), np.uint8)
+    pixel_hits = np.zeros((height, width), np.int32)
+    npairs = int(ranges[-1, 1]) if len(ranges) else 0
+    pq = np.zeros(max(npairs, 1), np.uint8)
     stats = np.zeros(2, np.int64)
     mask = _c(tile_mask, np.uint8) if tile_mask is not None else None
     bg = _bg(bg, np.float32)
     _load().or_render_fwd(_p(splats), _p(sorted_ids), _p(ranges), int(width), int(height),
-                          _p(mask), _p(bg), _p(rgb), _p(T), _p(last), _p(knife), _p(stats))
+                          _p(mask), _p(bg), _p(rgb), _p(T), _p(last), _p(knife), _p(stats),
+                          _p(pixel_hits), _p(pq))
     return dict(rgb=rgb, T=T, last=last, knife=knife.astype(bool), hits=int(stats[0]),
-                evals=int(stats[1]))
+                evals=int(stats[1]), pixel_hits=pixel_hits, pair_quarters=pq[:npairs])
 
 
-def render_fwd_untiled(splats, width, height):
+def render_fwd_untiled(splats, width, height, want_hits=False):
+    """Every pixel over every visible splat in (depth, id) order: (rgb, T), plus
+    the per-pixel hit counts when want_hits."""
     splats = _c(splats, np.float32)
     rgb = np.zeros((3, height, width), np.float32)
     T = np.zeros((height, width), np.float32)
+    hits = np.zeros((height, width), np.int32)
     _load().or_render_fwd_untiled(splats.shape[0], _p(splats), int(width), int(height),
-                                  _p(rgb), _p(T))
-    return rgb, T
+                                  _p(rgb), _p(T), _p(hits))
+    return (rgb, T, hits) if want_hits else (rgb, T)
 
 
 def render_fwd_values(splats_dec, splats_val, sorted_ids, ranges, width, height, last, bg=None):
@@ -319,6 +334,8 @@ def frame_views(scene, cams, dL_drgbs, bg=None, dL_dTs=None):
                           T=np.concatenate([f["T"] for f in fw]),
                           last=np.concatenate([f["last"] for f in fw]),
                           knife=np.concatenate([f["knife"] for f in fw]),
+                          pixel_hits=np.concatenate([f["pixel_hits"] for f in fw]),
+                          pair_quarters=np.concatenate([f["pair_quarters"] for f in fw]),
                           hits=sum(f["hits"] for f in fw), evals=sum(f["evals"] for f in fw))
     if "grads" in per[0]:
         out["grads"] = np.concatenate([f["grads"] for f in per])

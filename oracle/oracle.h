@@ -73,14 +73,22 @@ void or_tile_ranges(int64_t npairs, const uint64_t *sorted_keys, int ntiles, int
 /* Forward blend, mirror mode (Eq. 2-3 of [LOAD-IMB]). last[p] = number of list
    entries consumed by the pixel (stop index + 1, or the full tile length).
    tile_mask (nullable) restricts the work to tiles with a nonzero byte; other
-   pixels are left untouched. stats (nullable) += {hits, evaluations}. */
+   pixels are left untouched. stats (nullable) += {hits, evaluations}.
+   pixel_hits (nullable) <- the number of splats each pixel blended.
+   pair_quarters (nullable, one byte per list position, zeroed by the caller)
+   |= bit q for every 8x8 quarter q of the position's tile (q = 0 upper left,
+   1 upper right, 2 lower left, 3 lower right) in which at least one pixel
+   blended that splat ([3DGS-CUDA] Step 4: the forward pass records which
+   splats contributed to which part of the tile). */
 void or_render_fwd(const float *splats, const int32_t *sorted_ids, const int32_t *ranges,
                    int width, int height, const uint8_t *tile_mask, const float *bg, float *rgb,
-                   float *T_final, int32_t *last, uint8_t *knife, int64_t *stats);
+                   float *T_final, int32_t *last, uint8_t *knife, int64_t *stats,
+                   int32_t *pixel_hits, uint8_t *pair_quarters);
 
-/* Untiled brute force: every pixel walks every visible splat in (depth, id) order. */
+/* Untiled brute force: every pixel walks every visible splat in (depth, id) order.
+   pixel_hits (nullable) <- the number of splats each pixel blended. */
 void or_render_fwd_untiled(int n, const float *splats, int width, int height,
-                           float *rgb, float *T_final);
+                           float *rgb, float *T_final, int32_t *pixel_hits);
 
 /* Forward values in fp64 with frozen decisions: hits from the fp32 records
    splats_dec, stop from last; values from splats_val (fp64 records). */
@@ -103,5 +111,7 @@ void or_chunk_policy(int ntiles, const int32_t *counts_desc, double workers, dou
 
 /* OpenMP threads used by the parallel loops (for reporting). */
 int or_num_threads(void);
+/* Sets the OpenMP thread count of later parallel loops (n >= 1). */
+void or_set_num_threads(int n);
 
 #endif

@@ -67,3 +67,12 @@ int or_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count of the parallel loops that follow (no effect without OpenMP). */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

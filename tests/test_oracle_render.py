@@ -107,10 +107,93 @@ def test_tiled_equals_untiled_bitwise(seed, W, H, n):
     s[::7, 10] = s[3, 10]                          # force exact depth ties
     si, r = _frame_from_splats(s, W, H)
     f = oracle.render_fwd(s, si, r, W, H)
-    rgb_u, T_u = oracle.render_fwd_untiled(s, W, H)
+    rgb_u, T_u, hits_u = oracle.render_fwd_untiled(s, W, H, want_hits=True)
     assert np.array_equal(f["rgb"], rgb_u)
     assert np.array_equal(f["T"], T_u)
+    assert np.array_equal(f["pixel_hits"], hits_u)  # the same splats blended, pixel by pixel
+    assert f["pixel_hits"].sum() == f["hits"]
     assert (f["T"] < 1e-4).sum() > 0                # the stop rule is exercised
+
+
+def _f32(x):
+    return np.float32(x) if np.isscalar(x) else np.asarray(x, np.float32)
+
+
+def _fma32(a, b, c):
+    """fp32 fused multiply-add: the fp32 product is exact in fp64, and the sum is
+    rounded to fp64 then fp32 (a double rounding that differs from a single one
+    only at a fp32 midpoint, which these inputs never reach in practice)."""
+    return (np.asarray(a, np.float64) * np.asarray(b, np.float64) +
+            np.asarray(c, np.float64)).astype(np.float32)
+
+
+def _hits_numpy(s, si, r, W, H, last):
+    """Brute force in numpy, independent of the C code: the canonical fp32 q of
+    every (pixel, list entry) of its tile before the pixel's stop, and the hit
+    decision q <= tau. Returns the per-pixel hit counts and, per list position,
+    the bits of the tile quarters with at least one hit."""
+    tx = (W + 15) // 16
+    hits = np.zeros((H, W), np.int32)
+    pq = np.zeros(len(si), np.uint8)
+    for t in range(len(r)):
+        a0, a1 = int(r[t, 0]), int(r[t, 1])
+        if a1 == a0:
+            continue
+        x0, y0 = 16 * (t % tx), 16 * (t // tx)
+        py, px = np.mgrid[y0:min(y0 + 16, H), x0:min(x0 + 16, W)]
+        fx, fy = _f32(px + 0.5), _f32(py + 0.5)
+        rec = s[si[a0:a1]]                                   # [m, 12]
+        dx = fx[None] - rec[:, 0, None, None]
+        dy = fy[None] - rec[:, 1, None, None]
+        A, B2, Cc = rec[:, 2, None, None], _f32(2) * rec[:, 3, None, None], rec[:, 4, None, None]
+        inner = _fma32(B2 * dx, dy, (A * dx) * dx)
+        q = _fma32(Cc * dy, dy, inner)
+        pos = np.arange(a1 - a0)[:, None, None]
+        hit = (q <= rec[:, 9, None, None]) & (pos < last[py, px][None])
+        hits[py, px] = hit.sum(axis=0)
+        quad = ((px - x0) >> 3) | (((py - y0) >> 3) << 1)
+        for qd in range(4):
+            anyq = (hit & (quad == qd)[None]).reshape(len(rec), -1).any(axis=1)
+            pq[a0:a1] |= (anyq.astype(np.uint8) << qd)
+    return hits, pq
+
+
+@pytest.mark.parametrize("seed,W,H,n", [(41, 64, 64, 600), (42, 83, 45, 900)])
+def test_pixel_hits_and_quarter_contributors_brute_force(seed, W, H, n):
+    """The per-pixel hit counts and the per-quarter contributor bits of every
+    list position ([3DGS-CUDA] Step 4: which splats blended into which part of
+    a tile) equal an independent numpy evaluation of the canonical q."""
+    sc = scenegen.random_scene(seed, n, W, H, 0.9 * W, degree=1, log_scale=(-1.5, 0.5),
+                               opacity=(1.0, 2.0))
+    s = oracle.project_scene(sc)
+    si, r = _frame_from_splats(s, W, H)
+    f = oracle.render_fwd(s, si, r, W, H)
+    hits, pq = _hits_numpy(s, si, r, W, H, f["last"])
+    assert np.array_equal(f["pixel_hits"], hits)
+    assert np.array_equal(f["pair_quarters"], pq)
+    assert 0 < (pq == 0).sum() < len(pq)          # some positions blend nowhere (occluded)
+    assert len(np.unique(pq)) >= 8                 # many quarter combinations occur
+
+
+def test_backward_is_deterministic_across_thread_counts():
+    """The oracle's per-splat sums run in a fixed order: 1, 3 and 8 threads give
+    the same bits."""
+    sc = scenegen.random_scene(44, 1500, 83, 45, 70.0, degree=1, log_scale=(-1.5, 0.5),
+                               opacity=(1.0, 2.0))
+    s = oracle.project_scene(sc)
+    si, r = _frame_from_splats(s, 83, 45)
+    f = oracle.render_fwd(s, si, r, 83, 45)
+    outs = []
+    before = oracle.num_threads()
+    try:
+        for nt in (1, 3, 8):
+            oracle.set_num_threads(nt)
+            outs.append(oracle.render_bwd(s, si, r, 83, 45, f["last"], sc.dL_drgb))
+    finally:
+        oracle.set_num_threads(before)
+    assert np.any(outs[0] != 0)
+    for g in outs[1:]:
+        assert np.array_equal(g.view(np.uint64), outs[0].view(np.uint64))
 
 
 def test_transmittance_bounds_and_last():
