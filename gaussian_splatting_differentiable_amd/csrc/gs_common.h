@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "gs.h"
+#include "cull.h"
 
 #define GS_WAVE 64
 #define GS_TILE_PX 256
@@ -52,39 +53,5 @@ __device__ __forceinline__ void wave_sync() {
 
 // Value of v in the first active lane, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_first(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Canonical fp32 quadratic form of the conic at offset (dx, dy). Forward,
-// backward and the sub-tile cull must all take the hit decision from exactly
-// this expression (Step 5 of the literature page: fwd and bwd agree bit-for-bit).
-__device__ __forceinline__ float canon_q(float a, float b2, float c, float dx, float dy) {
-  return __builtin_fmaf(c * dy, dy, __builtin_fmaf(b2 * dx, dy, (a * dx) * dx));
-}
-
-// Conservative test: can the ellipse q <= tau touch any sample point of the
-// rectangle [x0,x1] x [y0,y1] (pixel-centre coordinates)? Computes the minimum
-// of q over the rectangle widened by 1/64 px, compared with tau * (1 + 2^-7).
-// Never rejects a rectangle that holds a hit pixel; may accept a few extra.
-__device__ __forceinline__ bool rect_may_hit(float mx, float my, float a, float b, float c,
-                                             float tau, float x0, float x1, float y0, float y1) {
-  if (!(tau > 0.0f)) return false;
-  const float g = 0.015625f;
-  x0 -= g; x1 += g; y0 -= g; y1 += g;
-  const float cxp = fminf(fmaxf(mx, x0), x1);
-  const float cyp = fminf(fmaxf(my, y0), y1);
-  if (cxp == mx && cyp == my) return true;
-  float qmin = 3.0e38f;
-  // a horizontal edge faces the centre when the centre lies above/below the box
-  if (cyp != my) {
-    const float dy = cyp - my;
-    const float dx = fminf(fmaxf(-b * dy / a, x0 - mx), x1 - mx);
-    qmin = fminf(qmin, a * dx * dx + 2.0f * b * dx * dy + c * dy * dy);
-  }
-  if (cxp != mx) {
-    const float dx = cxp - mx;
-    const float dy = fminf(fmaxf(-b * dx / c, y0 - my), y1 - my);
-    qmin = fminf(qmin, a * dx * dx + 2.0f * b * dx * dy + c * dy * dy);
-  }
-  return qmin <= tau * 1.0078125f;
-}
 
 static inline int gs_div_up(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

@@ -223,3 +223,62 @@ def test_tile_ranges_partition():
     assert r[0, 0] == 0 and r[-1, 1] == len(keys)
     assert np.array_equal(r[1:, 0], r[:-1, 1])
     assert oracle.tile_ranges(np.zeros(0, np.uint64), 5).sum() == 0
+
+
+def _fma32(a, b, c):
+    return (np.asarray(a, np.float64) * np.asarray(b, np.float64) +
+            np.asarray(c, np.float64)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["needle", "needle_far", "screen"])
+def test_superset_of_canonical_hits_for_extreme_splats(kind):
+    """Every pixel that the renderer counts as a hit (the canonical fp32 q <= tau,
+    no margin) lies in an emitted tile, also for long, thin, tilted splats
+    (covariance eigenvalues 0.3 and up to 3e6 px^2), such splats centred up to
+    300 px off screen, and splats larger than the image: the guard band of the
+    closed-form spans covers the rounding of q where its terms cancel. (Needles
+    of more than 1e6 px^2 centred some 1500 px off screen, where the rounding of
+    q in fp32 reaches the size of tau itself, can lose a tile: one splat in 600
+    in a probe of that regime.)"""
+    rng = np.random.default_rng({"needle": 21, "needle_far": 22, "screen": 23}[kind])
+    W, H, n = 160, 120, 300
+    th = rng.uniform(0, np.pi, n)
+    if kind == "screen":
+        l1 = np.exp(rng.uniform(np.log(1e3), np.log(1e5), n))
+        l2 = np.exp(rng.uniform(np.log(1e3), np.log(1e6), n))
+        far = 100
+    else:
+        l1 = 0.3 + rng.uniform(0, 0.05, n)
+        l2 = np.exp(rng.uniform(np.log(300), np.log(3e5 if kind == "needle" else 3e6), n))
+        far = 50 if kind == "needle" else 300
+    cs, sn = np.cos(th), np.sin(th)
+    sxx, syy, sxy = cs * cs * l1 + sn * sn * l2, sn * sn * l1 + cs * cs * l2, cs * sn * (l1 - l2)
+    det = sxx * syy - sxy * sxy
+    s = np.zeros((n, 12), np.float32)
+    s[:, 0] = rng.uniform(-far, W + far, n)
+    s[:, 1] = rng.uniform(-far, H + far, n)
+    if kind == "needle_far":
+        # long axis (-sin th, cos th) aimed at a random point of the image
+        tx, ty = rng.uniform(0, W, n) - s[:, 0], rng.uniform(0, H, n) - s[:, 1]
+        th = np.arctan2(-tx, ty)
+        cs, sn = np.cos(th), np.sin(th)
+        sxx, syy, sxy = cs * cs * l1 + sn * sn * l2, sn * sn * l1 + cs * cs * l2, cs * sn * (l1 - l2)
+        det = sxx * syy - sxy * sxy
+    s[:, 2], s[:, 3], s[:, 4] = syy / det, -sxy / det, sxx / det
+    o = np.clip(1 / (1 + np.exp(-rng.normal(0, 2, n))), 0.005, 0.999)
+    s[:, 5] = o
+    s[:, 9] = (2 * np.log(255 * o)).astype(np.float32)
+    s[:, 10] = rng.uniform(1, 10, n)
+    off, keys, ids = oracle.bin_tiles(s, W, H)
+    emitted = _emitted(keys, ids, n)
+    py, px = np.mgrid[0:H, 0:W]
+    fx, fy = (px + 0.5).astype(np.float32), (py + 0.5).astype(np.float32)
+    tile = (py // 16) * ((W + 15) // 16) + px // 16
+    checked = 0
+    for i in range(n):
+        dx, dy = fx - s[i, 0], fy - s[i, 1]
+        q = _fma32(s[i, 4] * dy, dy, _fma32(np.float32(2) * s[i, 3] * dx, dy, (s[i, 2] * dx) * dx))
+        need = set(np.unique(tile[q <= s[i, 9]]).tolist())
+        assert need <= emitted[i], (kind, i, sorted(need - emitted[i])[:5])
+        checked += len(need)
+    assert checked > 100
