@@ -175,20 +175,20 @@ def views_stage(args, sc, gsr, dev, means, ls, qs, op, sh):
             gsr.gs_bin_tiles_views(nrec, r.splats, r.cam, r.V, r.capacity, r.offsets, None, None,
                                    r.status, r.workspace)
             gsr.gs_sort_keys_views(nrec, r.splats, r.offsets, r.capacity, r.cam, r.V, None,
-                                   r.sorted_ids, r.ranges, r.workspace)
+                                   r.sorted_ids, r.ranges, r.status, r.workspace)
             gsr.gs_render_fwd_views(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.V, r.sched,
-                                    r.rgb, r.T, r.last, r.fwd_state, None)
+                                    r.rgb, r.T, r.last, r.fwd_state, None, None, r.status)
             gsr.gs_render_bwd_views(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.V, r.T,
-                                    r.last, r.fwd_state, dLv, r.grads)
+                                    r.last, r.fwd_state, dLv, r.grads, r.status)
         else:
             gsr.gs_bin_tiles(nrec, r.splats, r.cam, r.capacity, r.offsets, None, None, r.status,
                              r.workspace)
             gsr.gs_sort_keys(nrec, r.splats, r.offsets, r.capacity, r.cam, None, r.sorted_ids,
-                             r.ranges, r.workspace)
+                             r.ranges, r.status, r.workspace)
             gsr.gs_render_fwd(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
-                              r.last, r.fwd_state, None, r.workspace)
+                              r.last, r.fwd_state, None, None, r.status)
             gsr.gs_render_bwd(nrec, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last,
-                              r.fwd_state, dLv, r.grads, r.workspace)
+                              r.fwd_state, dLv, r.grads, r.status)
 
     def timed(fn):
         for _ in range(3):
@@ -205,7 +205,7 @@ def views_stage(args, sc, gsr, dev, means, ls, qs, op, sh):
     pairs_b = grow(rb, V * n)
     ms_b = timed(lambda: step(rb, V * n, dL))
     if int(rb.status.item()) != gsr.GS_OK:
-        raise SystemExit("pair buffer overflow in the batched-views stage")
+        raise SystemExit(f"batched-views frame failed: {gsr.strerror(int(rb.status.item()))}")
     del rb
     ms_seq, pairs_seq = 0.0, 0
     H = c0.height
@@ -216,7 +216,7 @@ def views_stage(args, sc, gsr, dev, means, ls, qs, op, sh):
         dLv = dL[:, v * H:(v + 1) * H].contiguous()
         ms_seq += timed(lambda: step(r, n, dLv))
         if int(r.status.item()) != gsr.GS_OK:
-            raise SystemExit("pair buffer overflow in the batched-views stage")
+            raise SystemExit(f"single-view frame failed: {gsr.strerror(int(r.status.item()))}")
         del r
     torch.cuda.synchronize()
     return {"n_views": V, "pairs": pairs_b, "pairs_single_views": pairs_seq,
@@ -280,15 +280,15 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         gsr.gs_sort_keys(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids, r.ranges,
-                         r.workspace)
+                         r.status, r.workspace)
         if ev is not None:
             ev[2].record(stream)
         gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T, r.last,
-                          r.fwd_state, None, r.workspace)
+                          r.fwd_state, None, None, r.status)
         if ev is not None:
             ev[3].record(stream)
         gsr.gs_render_bwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last, r.fwd_state,
-                          dL, r.grads, r.workspace)
+                          dL, r.grads, r.status)
         if ev is not None:
             ev[4].record(stream)
 
@@ -315,9 +315,9 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = {"fwd": float(np.median(gsr.gs_timing_read(0))),
                  "bwd": float(np.median(gsr.gs_timing_read(1)))}
-    status = int(r.status.item())
+    status = int(r.status.item())  # the frames' status word, read once after all of them
     if status != gsr.GS_OK:
-        raise SystemExit(f"pair buffer overflow during the timed loop: {gsr.strerror(status)}")
+        raise SystemExit(f"a frame of the timed loop failed: {gsr.strerror(status)}")
 
     per = {s: [] for s in stages}
     for ev in events:

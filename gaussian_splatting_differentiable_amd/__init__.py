@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY = 0, -1, -2
-GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED = -3, -4, -5
+GS_ERR_WORKSPACE, GS_ERR_HIP, GS_ERR_UNSUPPORTED, GS_ERR_TIMEOUT = -3, -4, -5, -6
 SPLAT_FLOATS, GRAD_FLOATS, TILE = 12, 9, 16
 
 EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project", "gs_project_bwd",
@@ -65,27 +65,29 @@ def lib():
     cam_p = C.POINTER(GsCamera)
     L.gs_strerror.argtypes, L.gs_strerror.restype = [i32], C.c_char_p
     L.gs_workspace_size.argtypes, L.gs_workspace_size.restype = [i32, i32, i32, i64], sz
-    L.gs_fwd_state_size.argtypes, L.gs_fwd_state_size.restype = [i32, i32], sz
+    L.gs_fwd_state_size.argtypes, L.gs_fwd_state_size.restype = [i32, i32, i64], sz
     L.gs_project.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P]
     L.gs_project_bwd.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P, P, P, P, P, P]
     L.gs_project_bf16sh.argtypes = L.gs_project.argtypes
     L.gs_project_bwd_bf16sh.argtypes = L.gs_project_bwd.argtypes
     L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, sz, P]
-    L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, sz, P]
-    L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, sz, P]
-    L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, sz, P]
+    L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, P, sz, P]
+    L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, P,
+                                P]
+    L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, P]
     L.gs_render_fwd_bg.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P]
     L.gs_render_bwd_bg.argtypes = L.gs_render_bwd.argtypes[:-1] + [P, P, P]
     L.gs_workspace_size_views.argtypes = [i32, i32, i32, i32, i64]
     L.gs_workspace_size_views.restype = sz
-    L.gs_fwd_state_size_views.argtypes, L.gs_fwd_state_size_views.restype = [i32, i32, i32], sz
+    L.gs_fwd_state_size_views.argtypes = [i32, i32, i32, i64]
+    L.gs_fwd_state_size_views.restype = sz
     L.gs_project_views.argtypes = [i32, P, P, P, P, P, i32, cam_p, i32, P, P]
     L.gs_project_bwd_views.argtypes = [i32, P, P, P, P, P, i32, cam_p, i32, P, P, P, P, P, P, P]
     L.gs_bin_tiles_views.argtypes = [i32, P, cam_p, i32, i64, P, P, P, P, P, sz, P]
-    L.gs_sort_keys_views.argtypes = [i32, P, P, i64, cam_p, i32, P, P, P, P, sz, P]
+    L.gs_sort_keys_views.argtypes = [i32, P, P, i64, cam_p, i32, P, P, P, P, P, sz, P]
     L.gs_render_fwd_views.argtypes = [i32, P, P, P, cam_p, i32, C.POINTER(GsSched), P, P, P, P,
-                                      sz, P, P, P]
-    L.gs_render_bwd_views.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P]
+                                      sz, P, P, P, P, P]
+    L.gs_render_bwd_views.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P, P]
     L.gs_timing_start.argtypes = []
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
     for name in ("gs_project", "gs_project_bwd", "gs_project_bf16sh", "gs_project_bwd_bf16sh",
@@ -150,8 +152,8 @@ def workspace_size(n, width, height, capacity) -> int:
     return int(lib().gs_workspace_size(int(n), int(width), int(height), int(capacity)))
 
 
-def fwd_state_size(width, height) -> int:
-    return int(lib().gs_fwd_state_size(int(width), int(height)))
+def fwd_state_size(width, height, capacity) -> int:
+    return int(lib().gs_fwd_state_size(int(width), int(height), int(capacity)))
 
 
 def workspace_size_views(n, width, height, n_views, capacity) -> int:
@@ -159,8 +161,9 @@ def workspace_size_views(n, width, height, n_views, capacity) -> int:
                                              int(capacity)))
 
 
-def fwd_state_size_views(width, height, n_views) -> int:
-    return int(lib().gs_fwd_state_size_views(int(width), int(height), int(n_views)))
+def fwd_state_size_views(width, height, n_views, capacity) -> int:
+    return int(lib().gs_fwd_state_size_views(int(width), int(height), int(n_views),
+                                             int(capacity)))
 
 
 def _cams(cams):
@@ -203,33 +206,34 @@ def gs_bin_tiles_views(n, splats, cam, n_views, capacity, offsets, keys, ids, st
 
 
 def gs_sort_keys_views(n, splats, offsets, capacity, cam, n_views, sorted_keys, sorted_ids,
-                       ranges, workspace, stream=None):
+                       ranges, status, workspace, stream=None):
     _check(lib().gs_sort_keys_views(int(n), _ptr(splats), _ptr(offsets), int(capacity),
                                     C.byref(cam), int(n_views), _ptr(sorted_keys),
-                                    _ptr(sorted_ids), _ptr(ranges), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(),
+                                    _ptr(sorted_ids), _ptr(ranges), _ptr(status),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)),
            "gs_sort_keys_views")
 
 
 def gs_render_fwd_views(n, splats, sorted_ids, ranges, cam, n_views, sched, rgb, T_final, last,
-                        fwd_state, stats, background=None, stream=None):
+                        fwd_state, stats, pixel_hits, status, background=None, stream=None):
     _check(lib().gs_render_fwd_views(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
                                      C.byref(cam), int(n_views),
                                      C.byref(sched) if sched is not None else None, _ptr(rgb),
                                      _ptr(T_final), _ptr(last), _ptr(fwd_state),
                                      fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
-                                     _bg3(background), _stream(stream)),
+                                     _ptr(pixel_hits), _ptr(status), _bg3(background),
+                                     _stream(stream)),
            "gs_render_fwd_views")
 
 
 def gs_render_bwd_views(n, splats, sorted_ids, ranges, cam, n_views, T_final, last, fwd_state,
-                        dL_drgb, dL_dsplat, background=None, dL_dT=None, stream=None):
+                        dL_drgb, dL_dsplat, status, background=None, dL_dT=None, stream=None):
     _check(lib().gs_render_bwd_views(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
                                      C.byref(cam), int(n_views), _ptr(T_final), _ptr(last),
                                      _ptr(fwd_state), fwd_state.numel() * fwd_state.element_size(),
-                                     _ptr(dL_drgb), _ptr(dL_dsplat), _bg3(background),
-                                     _ptr(dL_dT), _stream(stream)),
+                                     _ptr(dL_drgb), _ptr(dL_dsplat), _ptr(status),
+                                     _bg3(background), _ptr(dL_dT), _stream(stream)),
            "gs_render_bwd_views")
 
 
@@ -277,33 +281,31 @@ def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace
            "gs_bin_tiles")
 
 
-def gs_sort_keys(n, splats, offsets, capacity, cam, sorted_keys, sorted_ids, ranges, workspace,
-                 stream=None):
+def gs_sort_keys(n, splats, offsets, capacity, cam, sorted_keys, sorted_ids, ranges, status,
+                 workspace, stream=None):
     _check(lib().gs_sort_keys(int(n), _ptr(splats), _ptr(offsets), int(capacity), C.byref(cam),
-                              _ptr(sorted_keys), _ptr(sorted_ids),
-                              _ptr(ranges), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(stream)),
+                              _ptr(sorted_keys), _ptr(sorted_ids), _ptr(ranges), _ptr(status),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)),
            "gs_sort_keys")
 
 
 def gs_render_fwd(n, splats, sorted_ids, ranges, cam, sched, rgb, T_final, last, fwd_state,
-                  stats, workspace, stream=None):
+                  stats, pixel_hits, status, stream=None):
     _check(lib().gs_render_fwd(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges), C.byref(cam),
                                C.byref(sched) if sched is not None else None, _ptr(rgb),
                                _ptr(T_final), _ptr(last), _ptr(fwd_state),
                                fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream(stream)),
+                               _ptr(pixel_hits), _ptr(status), _stream(stream)),
            "gs_render_fwd")
 
 
 def gs_render_bwd(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, dL_drgb,
-                  dL_dsplat, workspace, stream=None):
+                  dL_dsplat, status, stream=None):
     _check(lib().gs_render_bwd(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges), C.byref(cam),
                                _ptr(T_final), _ptr(last), _ptr(fwd_state),
                                fwd_state.numel() * fwd_state.element_size(), _ptr(dL_drgb),
-                               _ptr(dL_dsplat), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)),
+                               _ptr(dL_dsplat), _ptr(status), _stream(stream)),
            "gs_render_bwd")
 
 
@@ -318,24 +320,23 @@ def _bg3(background):
 
 
 def gs_render_fwd_bg(n, splats, sorted_ids, ranges, cam, sched, rgb, T_final, last, fwd_state,
-                     stats, workspace, background, stream=None):
+                     stats, pixel_hits, status, background, stream=None):
     _check(lib().gs_render_fwd_bg(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
                                   C.byref(cam), C.byref(sched) if sched is not None else None,
                                   _ptr(rgb), _ptr(T_final), _ptr(last), _ptr(fwd_state),
                                   fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _bg3(background), _stream(stream)),
+                                  _ptr(pixel_hits), _ptr(status), _bg3(background),
+                                  _stream(stream)),
            "gs_render_fwd_bg")
 
 
 def gs_render_bwd_bg(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, dL_drgb,
-                     dL_dsplat, workspace, background, dL_dT, stream=None):
+                     dL_dsplat, status, background, dL_dT, stream=None):
     _check(lib().gs_render_bwd_bg(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
                                   C.byref(cam), _ptr(T_final), _ptr(last), _ptr(fwd_state),
                                   fwd_state.numel() * fwd_state.element_size(), _ptr(dL_drgb),
-                                  _ptr(dL_dsplat), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(),
-                                  _bg3(background), _ptr(dL_dT), _stream(stream)),
+                                  _ptr(dL_dsplat), _ptr(status), _bg3(background), _ptr(dL_dT),
+                                  _stream(stream)),
            "gs_render_bwd_bg")
 
 
@@ -358,8 +359,10 @@ def gs_timing_read(which: int, cap: int = 512):
 class Rasterizer:
     """Owns the per-frame buffers for one image size and chains the five calls.
 
-    Buffers grow when needed (more Gaussians, more pairs); a pair overflow
-    reported by gs_bin_tiles is handled by growing and running the frame again.
+    Every call only enqueues work on the current stream. The frame's device
+    status word is read once, after the frame (``frame_status``); ``run_frame``
+    chains a whole frame and, when the pairs overflowed the buffers, grows them
+    and runs the frame again.
     """
 
     def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None, n_views=1):
@@ -378,12 +381,11 @@ class Rasterizer:
         self.rgb = torch.empty((3, VH, self.W), dtype=torch.float32, device=dev)
         self.T = torch.empty((VH, self.W), dtype=torch.float32, device=dev)
         self.last = torch.empty((VH, self.W), dtype=torch.int32, device=dev)
-        fs = (fwd_state_size(self.W, self.H) if self.V == 1
-              else fwd_state_size_views(self.W, self.H, self.V))
-        self.fwd_state = torch.empty(fs, dtype=torch.uint8, device=dev)
+        self.pixel_hits = torch.zeros((VH, self.W), dtype=torch.int32, device=dev)
         self.ranges = torch.empty((self.tiles, 2), dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.stats = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.fwd_state = None
 
     def _ensure(self, n, capacity):
         dev = self.device
@@ -400,10 +402,15 @@ class Rasterizer:
             self.sorted_keys = torch.empty(max(capacity, 1), dtype=torch.int64, device=dev)
             self.sorted_ids = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
             self.workspace = None
+            self.fwd_state = None
         if self.workspace is None:
             ws = (workspace_size(n, self.W, self.H, self.capacity) if self.V == 1
                   else workspace_size_views(n, self.W, self.H, self.V, self.capacity))
             self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        if self.fwd_state is None:
+            fs = (fwd_state_size(self.W, self.H, self.capacity) if self.V == 1
+                  else fwd_state_size_views(self.W, self.H, self.V, self.capacity))
+            self.fwd_state = torch.empty(fs, dtype=torch.uint8, device=dev)
 
     def project(self, means, log_scales, quats, opacities, sh, sh_degree):
         """sh as float32, or as bfloat16 (then gs_project_bf16sh reads its bits)."""
@@ -413,42 +420,60 @@ class Rasterizer:
         call(n, means, log_scales, quats, opacities, sh, sh_degree, self.cam, self.splats)
         return self.splats[:n]
 
-    def bin_and_sort(self, n, want_keys=False, want_emission=False):
-        """Bin and sort the current splats; grows the pair buffers on overflow.
+    def enqueue_bin_sort(self, n, want_keys=False, want_emission=False):
+        """Enqueue binning and sorting of the current splats (no synchronisation).
 
         want_emission also writes the id-order (keys, ids) list of gs_bin_tiles;
         want_keys writes the sorted keys."""
+        self._ensure(n, self.capacity)
+        keys = self.keys if want_emission else None
+        ids = self.ids if want_emission else None
+        skeys = self.sorted_keys if want_keys else None
+        if self.V == 1:
+            gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets, keys, ids,
+                         self.status, self.workspace)
+            gs_sort_keys(n, self.splats, self.offsets, self.capacity, self.cam, skeys,
+                         self.sorted_ids, self.ranges, self.status, self.workspace)
+        else:
+            gs_bin_tiles_views(n, self.splats, self.cam, self.V, self.capacity, self.offsets,
+                               keys, ids, self.status, self.workspace)
+            gs_sort_keys_views(n, self.splats, self.offsets, self.capacity, self.cam, self.V,
+                               skeys, self.sorted_ids, self.ranges, self.status, self.workspace)
+
+    def frame_status(self, n):
+        """(device status, pair count I) of the frame, read once (synchronises)."""
+        both = torch.cat([self.status, self.offsets[n:n + 1]]).cpu()
+        return int(both[0]), int(both[1])
+
+    def bin_and_sort(self, n, want_keys=False, want_emission=False):
+        """Bin and sort, then read the frame's status once; on a pair overflow grow
+        the buffers and run again. Returns I."""
         for _ in range(3):
-            keys = self.keys if want_emission else None
-            ids = self.ids if want_emission else None
-            skeys = self.sorted_keys if want_keys else None
-            if self.V == 1:
-                gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets, keys, ids,
-                             self.status, self.workspace)
-                gs_sort_keys(n, self.splats, self.offsets, self.capacity, self.cam, skeys,
-                             self.sorted_ids, self.ranges, self.workspace)
-            else:
-                gs_bin_tiles_views(n, self.splats, self.cam, self.V, self.capacity, self.offsets,
-                                   keys, ids, self.status, self.workspace)
-                gs_sort_keys_views(n, self.splats, self.offsets, self.capacity, self.cam, self.V,
-                                   skeys, self.sorted_ids, self.ranges, self.workspace)
-            if int(self.status.item()) == GS_OK:
-                return int(self.offsets[n].item())
-            need = int(self.offsets[n].item())
-            self._ensure(n, max(need + need // 8, 1024))
+            self.enqueue_bin_sort(n, want_keys, want_emission)
+            st, I = self.frame_status(n)
+            if st == GS_OK:
+                return I
+            if st != GS_ERR_CAPACITY:
+                raise GsError(st, "bin_and_sort")
+            self._ensure(n, max(I + I // 8, 1024))
         raise GsError(GS_ERR_CAPACITY, "bin_and_sort")
 
     def render_fwd(self, n, stats=False, background=None):
-        """background: 3 floats (host), or None for black (gs_render_fwd)."""
+        """Enqueue the forward. stats: also count hits (self.stats, self.pixel_hits,
+        both cleared first). background: 3 floats (host), or None for black."""
+        self._ensure(n, self.capacity)
+        st = ph = None
         if stats:
             self.stats.zero_()
+            self.pixel_hits.zero_()
+            st, ph = self.stats, self.pixel_hits
         if self.V > 1:
             gs_render_fwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
-                                self.sched, self.rgb, self.T, self.last, self.fwd_state,
-                                self.stats if stats else None, background)
+                                self.sched, self.rgb, self.T, self.last, self.fwd_state, st, ph,
+                                self.status, background)
             return self.rgb, self.T, self.last
         args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched, self.rgb,
-                self.T, self.last, self.fwd_state, self.stats if stats else None, self.workspace)
+                self.T, self.last, self.fwd_state, st, ph, self.status)
         if background is None:
             gs_render_fwd(*args)
         else:
@@ -456,19 +481,43 @@ class Rasterizer:
         return self.rgb, self.T, self.last
 
     def render_bwd(self, n, dL_drgb, background=None, dL_dT=None):
-        """background as for render_fwd; dL_dT [H][W] on the device, or None."""
+        """Enqueue the backward. background as for render_fwd; dL_dT [H][W] on the
+        device, or None."""
         if self.V > 1:
             gs_render_bwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
                                 self.T, self.last, self.fwd_state, dL_drgb, self.grads,
-                                background, dL_dT)
+                                self.status, background, dL_dT)
             return self.grads[:n]
         args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.T, self.last,
-                self.fwd_state, dL_drgb, self.grads, self.workspace)
+                self.fwd_state, dL_drgb, self.grads, self.status)
         if background is None and dL_dT is None:
             gs_render_bwd(*args)
         else:
             gs_render_bwd_bg(*args, background, dL_dT)
         return self.grads[:n]
+
+    def check(self, what="frame"):
+        """Read the frame's status once and raise GsError unless it is GS_OK."""
+        st = int(self.status.cpu()[0])
+        if st != GS_OK:
+            raise GsError(st, what)
+
+    def run_frame(self, n, dL_drgb=None, stats=False, background=None, dL_dT=None):
+        """Bin, sort, forward and (with dL_drgb) backward of the current splats,
+        then one read of the frame's status; a pair overflow grows the buffers and
+        runs the frame again. Returns I."""
+        for _ in range(3):
+            self.enqueue_bin_sort(n)
+            self.render_fwd(n, stats=stats, background=background)
+            if dL_drgb is not None:
+                self.render_bwd(n, dL_drgb, background=background, dL_dT=dL_dT)
+            st, I = self.frame_status(n)
+            if st == GS_OK:
+                return I
+            if st != GS_ERR_CAPACITY:
+                raise GsError(st, "run_frame")
+            self._ensure(n, max(I + I // 8, 1024))
+        raise GsError(GS_ERR_CAPACITY, "run_frame")
 
     def project_bwd(self, means, log_scales, quats, opacities, sh, sh_degree, dL_dsplat=None):
         """Per-Gaussian gradients from the screen-space ones (by default the last

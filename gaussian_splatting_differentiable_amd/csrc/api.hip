@@ -20,16 +20,17 @@ hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t ca
 size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y);
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
-                          int32_t *ranges, void *ws, hipStream_t st);
-hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
+                          int32_t *ranges, int32_t *status, void *ws, hipStream_t st);
+hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
-                                int64_t *stats, int workers_waves, hipEvent_t ev0, hipEvent_t ev1,
-                                hipStream_t st);
-hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
+                                int64_t cap_pairs, int64_t *stats, int32_t *pixel_hits,
+                                int32_t *status, int workers_waves, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t st);
+hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                const float *dT, float *grads, int n, int workers_waves,
+                                const float *dT, float *grads, int32_t *status, int workers_waves,
                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 
 namespace {
@@ -110,6 +111,10 @@ void timing_slot(int which, hipEvent_t &a, hipEvent_t &b) {
 }
 
 int64_t num_tiles(int32_t w, int32_t h) { return (int64_t)((w + 15) / 16) * ((h + 15) / 16); }
+
+// Splat counts and pair capacities from 2^30 up are refused: the radix passes'
+// look-back words hold 30-bit counts.
+constexpr int64_t GS_COUNT_LIMIT = (int64_t)1 << 30;
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -192,13 +197,15 @@ const char *gs_strerror(int32_t s) {
     case GS_ERR_WORKSPACE: return "workspace or forward state too small";
     case GS_ERR_HIP: return "HIP runtime error";
     case GS_ERR_UNSUPPORTED: return "unsupported size";
+    case GS_ERR_TIMEOUT: return "a bounded device-side wait gave up: the frame's results are invalid";
     default: return "unknown status";
   }
 }
 
-size_t gs_fwd_state_size(int32_t width, int32_t height) {
+size_t gs_fwd_state_size(int32_t width, int32_t height, int64_t pair_capacity) {
   if (width <= 0 || height <= 0 || num_tiles(width, height) > GS_MAX_TILES) return 0;
-  return fwd_layout((int)num_tiles(width, height)).total;
+  if (pair_capacity < 0 || pair_capacity >= GS_COUNT_LIMIT) return 0;
+  return fwd_layout((int)num_tiles(width, height), pair_capacity).total;
 }
 
 size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity) {
@@ -247,8 +254,9 @@ namespace {
 int32_t bin_impl(int32_t n, const float *splats, const CamK &k, int64_t pair_capacity,
                  int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
                  void *workspace, size_t workspace_bytes, void *stream) {
-  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX) return GS_ERR_INVALID_ARGUMENT;
-  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (n < 0 || pair_capacity < 0) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT || pair_capacity >= GS_COUNT_LIMIT)
+    return GS_ERR_UNSUPPORTED;
   if (!offsets || !device_status || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
   if ((keys == nullptr) != (ids == nullptr)) return GS_ERR_INVALID_ARGUMENT;
   if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8))) return GS_ERR_INVALID_ARGUMENT;
@@ -260,10 +268,12 @@ int32_t bin_impl(int32_t n, const float *splats, const CamK &k, int64_t pair_cap
 
 int32_t sort_impl(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
                   const CamK &k, uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
-                  void *workspace, size_t workspace_bytes, void *stream) {
-  if (n < 0 || pair_capacity < 0 || pair_capacity > INT32_MAX) return GS_ERR_INVALID_ARGUMENT;
-  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!offsets || !tile_ranges || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
+                  int32_t *device_status, void *workspace, size_t workspace_bytes, void *stream) {
+  if (n < 0 || pair_capacity < 0) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT || pair_capacity >= GS_COUNT_LIMIT)
+    return GS_ERR_UNSUPPORTED;
+  if (!offsets || !tile_ranges || !workspace || !device_status || (n > 0 && !splats))
+    return GS_ERR_INVALID_ARGUMENT;
   if (pair_capacity > 0 && !sorted_ids) return GS_ERR_INVALID_ARGUMENT;
   if ((splats && !aligned(splats, 16)) || (sorted_keys && !aligned(sorted_keys, 8)) ||
       !aligned(tile_ranges, 8))
@@ -271,19 +281,26 @@ int32_t sort_impl(int32_t n, const float *splats, const int32_t *offsets, int64_
   if (workspace_bytes < gs_sort_ws_bytes(n, pair_capacity, k.tiles_x, k.tiles_y))
     return GS_ERR_WORKSPACE;
   return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
-                                   tile_ranges, workspace, (hipStream_t)stream));
+                                   tile_ranges, device_status, workspace, (hipStream_t)stream));
 }
 
 int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
                  const int32_t *tile_ranges, CamK k, const gs_sched *sched, float *rgb,
                  float *T_final, int32_t *last, void *fwd_state, size_t fwd_state_bytes,
-                 int64_t *stats, const float *background, void *stream) {
+                 int64_t *stats, int32_t *pixel_hits, int32_t *device_status,
+                 const float *background, void *stream) {
   if (n < 0 || !set_background(background, &k)) return GS_ERR_INVALID_ARGUMENT;
-  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!tile_ranges || !rgb || !T_final || !last || !fwd_state) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT) return GS_ERR_UNSUPPORTED;
+  if (!tile_ranges || !rgb || !T_final || !last || !fwd_state || !device_status)
+    return GS_ERR_INVALID_ARGUMENT;
   if (n > 0 && (!splats || !sorted_ids)) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8)) return GS_ERR_INVALID_ARGUMENT;
-  if (fwd_state_bytes < fwd_layout((int)batch_tiles(k)).total) return GS_ERR_WORKSPACE;
+  if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8) ||
+      (pixel_hits && !aligned(pixel_hits, 4)))
+    return GS_ERR_INVALID_ARGUMENT;
+  // the pairs the state's contributor bitmap can hold; the schedule reports a
+  // frame with more through device_status
+  const int64_t cap_pairs = fwd_state_capacity((int)batch_tiles(k), fwd_state_bytes);
+  if (cap_pairs < 0) return GS_ERR_WORKSPACE;
   if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
   const gs_sched sc = sched ? *sched : default_sched();
   if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
@@ -293,32 +310,34 @@ int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
   if (workers <= 0) return GS_ERR_HIP;
   hipEvent_t e0, e1;
   timing_slot(0, e0, e1);
-  return hip_status(gs_launch_render_fwd(splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
-                                         last, fwd_state, stats, workers, e0, e1,
-                                         (hipStream_t)stream));
+  return hip_status(gs_launch_render_fwd(n, splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
+                                         last, fwd_state, cap_pairs, stats, pixel_hits,
+                                         device_status, workers, e0, e1, (hipStream_t)stream));
 }
 
 int32_t bwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
                  const int32_t *tile_ranges, CamK k, const float *T_final, const int32_t *last,
                  void *fwd_state, size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
-                 const float *background, const float *dL_dT, void *stream) {
+                 int32_t *device_status, const float *background, const float *dL_dT,
+                 void *stream) {
   if (n < 0 || !set_background(background, &k)) return GS_ERR_INVALID_ARGUMENT;
   if (dL_dT) k.bg_on = 1;
-  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
-  if (!tile_ranges || !T_final || !last || !fwd_state || !dL_drgb) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT) return GS_ERR_UNSUPPORTED;
+  if (!tile_ranges || !T_final || !last || !fwd_state || !dL_drgb || !device_status)
+    return GS_ERR_INVALID_ARGUMENT;
   if (n > 0 && (!splats || !sorted_ids || !dL_dsplat)) return GS_ERR_INVALID_ARGUMENT;
   if ((splats && !aligned(splats, 16)) || !aligned(tile_ranges, 8) ||
       (dL_dsplat && !aligned(dL_dsplat, 16)) || (dL_dT && !aligned(dL_dT, 4)))
     return GS_ERR_INVALID_ARGUMENT;
-  if (fwd_state_bytes < fwd_layout((int)batch_tiles(k)).total) return GS_ERR_WORKSPACE;
+  if (fwd_state_capacity((int)batch_tiles(k), fwd_state_bytes) < 0) return GS_ERR_WORKSPACE;
   if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
   const int workers = worker_waves();
   if (workers <= 0) return GS_ERR_HIP;
   hipEvent_t e0, e1;
   timing_slot(1, e0, e1);
-  return hip_status(gs_launch_render_bwd(splats, sorted_ids, tile_ranges, k, T_final, last,
-                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, n, workers, e0,
-                                         e1, (hipStream_t)stream));
+  return hip_status(gs_launch_render_bwd(n, splats, sorted_ids, tile_ranges, k, T_final, last,
+                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, device_status,
+                                         workers, e0, e1, (hipStream_t)stream));
 }
 
 // The camera of view 0 of a batch, with every view checked to be valid and of
@@ -348,57 +367,55 @@ int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64
 
 int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
                      const gs_camera *cam, uint64_t *sorted_keys, int32_t *sorted_ids,
-                     int32_t *tile_ranges, void *workspace, size_t workspace_bytes, void *stream) {
+                     int32_t *tile_ranges, int32_t *device_status, void *workspace,
+                     size_t workspace_bytes, void *stream) {
   CamK k;
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
-                   workspace, workspace_bytes, stream);
+                   device_status, workspace, workspace_bytes, stream);
 }
 
 int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
                          const int32_t *tile_ranges, const gs_camera *cam,
                          const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
                          void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
-                         void *workspace, size_t workspace_bytes, const float *background,
+                         int32_t *pixel_hits, int32_t *device_status, const float *background,
                          void *stream) {
   CamK k;
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
-  (void)workspace; (void)workspace_bytes;
   return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
-                  fwd_state_bytes, stats, background, stream);
+                  fwd_state_bytes, stats, pixel_hits, device_status, background, stream);
 }
 
 int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
                       float *rgb, float *T_final, int32_t *last, void *fwd_state,
-                      size_t fwd_state_bytes, int64_t *stats, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+                      size_t fwd_state_bytes, int64_t *stats, int32_t *pixel_hits,
+                      int32_t *device_status, void *stream) {
   return gs_render_fwd_bg(n, splats, sorted_ids, tile_ranges, cam, sched, rgb, T_final, last,
-                          fwd_state, fwd_state_bytes, stats, workspace, workspace_bytes, nullptr,
+                          fwd_state, fwd_state_bytes, stats, pixel_hits, device_status, nullptr,
                           stream);
 }
 
 int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
                          const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
                          const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
-                         const float *dL_drgb, float *dL_dsplat, void *workspace,
-                         size_t workspace_bytes, const float *background, const float *dL_dT,
-                         void *stream) {
+                         const float *dL_drgb, float *dL_dsplat, int32_t *device_status,
+                         const float *background, const float *dL_dT, void *stream) {
   CamK k;
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
-  (void)workspace; (void)workspace_bytes;
   return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
-                  fwd_state_bytes, dL_drgb, dL_dsplat, background, dL_dT, stream);
+                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, stream);
 }
 
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
                       const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
-                      const float *dL_drgb, float *dL_dsplat, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+                      const float *dL_drgb, float *dL_dsplat, int32_t *device_status,
+                      void *stream) {
   return gs_render_bwd_bg(n, splats, sorted_ids, tile_ranges, cam, T_final, last, fwd_state,
-                          fwd_state_bytes, dL_drgb, dL_dsplat, workspace, workspace_bytes, nullptr,
-                          nullptr, stream);
+                          fwd_state_bytes, dL_drgb, dL_dsplat, device_status, nullptr, nullptr,
+                          stream);
 }
 
 // ---------------------------------------------------------------- batches of views
@@ -411,11 +428,13 @@ size_t gs_workspace_size_views(int32_t n, int32_t width, int32_t height, int32_t
   return gs_sort_ws_bytes(n, pair_capacity, (width + 15) / 16, ((height + 15) / 16) * n_views);
 }
 
-size_t gs_fwd_state_size_views(int32_t width, int32_t height, int32_t n_views) {
+size_t gs_fwd_state_size_views(int32_t width, int32_t height, int32_t n_views,
+                               int64_t pair_capacity) {
   if (width <= 0 || height <= 0 || n_views < 1 || n_views > GS_MAX_VIEWS) return 0;
+  if (pair_capacity < 0 || pair_capacity >= GS_COUNT_LIMIT) return 0;
   const int64_t t = num_tiles(width, height) * n_views;
   if (t > GS_MAX_TILES) return 0;
-  return fwd_layout((int)t).total;
+  return fwd_layout((int)t, pair_capacity).total;
 }
 
 int32_t gs_project_views(int32_t n, const float *means, const float *log_scales,
@@ -481,33 +500,36 @@ int32_t gs_bin_tiles_views(int32_t n, const float *splats, const gs_camera *cam,
 int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offsets,
                            int64_t pair_capacity, const gs_camera *cam, int32_t n_views,
                            uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+                           int32_t *device_status, void *workspace, size_t workspace_bytes,
+                           void *stream) {
   CamK k;
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
-                   workspace, workspace_bytes, stream);
+                   device_status, workspace, workspace_bytes, stream);
 }
 
 int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
                             const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
                             const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
                             void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                            int32_t *pixel_hits, int32_t *device_status,
                             const float *background, void *stream) {
   CamK k;
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
-                  fwd_state_bytes, stats, background, stream);
+                  fwd_state_bytes, stats, pixel_hits, device_status, background, stream);
 }
 
 int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
                             const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
                             const float *T_final, const int32_t *last, void *fwd_state,
                             size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
-                            const float *background, const float *dL_dT, void *stream) {
+                            int32_t *device_status, const float *background,
+                            const float *dL_dT, void *stream) {
   CamK k;
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
-                  fwd_state_bytes, dL_drgb, dL_dsplat, background, dL_dT, stream);
+                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, stream);
 }
 
 int32_t gs_timing_start(void) {

@@ -51,6 +51,11 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// First error of a frame wins: the status word keeps the first non-OK code.
+__device__ __forceinline__ void report_status(int32_t *status, int32_t code) {
+  atomicCAS(status, (int32_t)GS_OK, code);
+}
+
 // Value of v in the first active lane, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_first(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -5,20 +5,27 @@
 // derivatives summed over a wave before global atomics; Step 1 (e) the scalar
 // accumulator accum = c_behind . dL/dC; Step 2 the reduce-scatter that leaves
 // the 9 sums on 9 lanes for one atomic instruction; Step 4 the walk from the
-// last contributor back to the front; Step 5 branchless alpha = 0 predication
-// for missed pixels and one canonical q shared with the forward pass; Step 6.3
-// the per-splat term alpha T (c . dL/dC - accum), with log2(o) folded into the
-// exponent and o divided back out once after the sum.
+// last contributor back to the front over the contributors the forward pass
+// recorded (here a bitmap per quarter and 64-entry batch), with no geometric
+// sub-tile test; Step 5 branchless alpha = 0 predication for missed pixels and
+// one canonical q shared with the forward pass; Step 6.1 two vertically
+// adjacent pixels per lane, sharing the column terms of q and summed in
+// registers before the reduction; Step 6.3 the per-splat term
+// alpha T (c . dL/dC - accum), with log2(o) folded into the exponent and o
+// divided back out once after the sum; Step 6.4 the two rows' offsets combined
+// without per-row products by the row index.
 // "Mitigating SM-Level Load Imbalance in 3D Gaussian Splatting on GPUs",
 // section 4: the same persistent longest-first queue as the forward pass; a
 // chunk of a heavy tile is differentiated on its own from the forward pass's
 // chunk state: it starts from the transmittance after its last processed
 // splat, T_end, with accum = (sum over later chunks of C_chunk . dL/dC) / T_end.
 //
-// gfx950 mapping: one wavefront per item (an 8x8 quarter), LDS-staged batches
-// of 64 splats walked back to front with the next batch fetched ahead; the
-// per-wave cull ballot skips splats that miss the quarter and a second ballot
-// skips splats no live pixel hits.
+// gfx950 mapping: one wavefront per item, an 8-column half of a tile (or of a
+// chunk): lane l holds column l mod 8 and rows 2 (l / 8), 2 (l / 8) + 1, so
+// lanes 0-31 cover the half's upper quarter and lanes 32-63 its lower one. The
+// item's non-empty batches come from one vector load of its contributor words;
+// each batch stages only its contributors' records in LDS (the next batch's
+// ids and records in flight) and walks them back to front on the scalar unit.
 #include "render_common.h"
 #include "wave_reduce.h"
 
@@ -33,20 +40,29 @@ constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 // group's backward items stably by a quarter-octave bucket of that length.
 constexpr int BO_T = 1024, BO_W = BO_T / 64, BO_BITS = 6, BO_BINS = 1 << BO_BITS;
 
-__device__ __forceinline__ uint32_t order_bin(const FwdState &fs, int it, int k) {
-  const int quad = item_quad(it), idx = item_index(it);
-  const int len = item_kind(it) == ITEM_PLAIN
-                      ? fs.sub_last[idx * 4 + quad]
-                      : fs.chunk_last[chunk_index(idx, item_chunk(it), quad, k)];
+// Walk length of a backward item: the longer of its two quarters' last hits.
+__device__ __forceinline__ int item_len(const FwdState &fs, int it, int k) {
+  const int half = item_quad(it), idx = item_index(it);
+  if (item_kind(it) == ITEM_PLAIN)
+    return max(fs.sub_last[idx * 4 + half], fs.sub_last[idx * 4 + half + 2]);
+  const int p = item_chunk(it);
+  return max(fs.chunk_last[chunk_index(idx, p, half, k)],
+             fs.chunk_last[chunk_index(idx, p, half + 2, k)]);
+}
+
+__device__ __forceinline__ uint32_t order_bin(int len) {
   const int b = (int)(4.0f * __log2f((float)max(len, 0) + 1.0f));
   return (uint32_t)(BO_BINS - 1 - min(b, BO_BINS - 1));  // ascending bin = longest first
 }
 
-// The backward's preparation in one launch: workgroup g < GS_GROUPS orders
-// group g's items and rewinds its queue; the others zero the gradient output.
+// The backward's preparation in one launch: workgroup g < GS_GROUPS builds group
+// g's backward queue: the forward's plain and pass-B items of quarters 0 and 1
+// become the left and right halves (each covers quarters h and h + 2), stably
+// sorted longest first; the others zero the gradient output. The frame runs only
+// if its status is still GS_OK.
 __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int ntiles,
                                                   int nblocks, float *__restrict__ grads,
-                                                  int64_t ng) {
+                                                  int64_t ng, const int32_t *__restrict__ status) {
   if (blockIdx.x >= GS_GROUPS) {
     const int64_t i = (int64_t)(blockIdx.x - GS_GROUPS) * BO_T + threadIdx.x;
     const int64_t n4 = ng / 4;
@@ -55,22 +71,25 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
     return;
   }
   __shared__ int cnt[BO_W][BO_BINS];
+  __shared__ int run;
   FwdState fs = fwd_state_at(state, ntiles);
-  const int g = blockIdx.x, k = fs.hdr->k;
-  const int lo = fs.hdr->qoff[g] + fs.hdr->qa[g], hi = fs.hdr->qoff[g + 1];
-  const int n = hi - lo;
-  // the backward's own hand-out: the first items go to its workers without a pop
   if (threadIdx.x == 0) {
-    const int init = min(n, group_workers(g, nblocks));
-    fs.hdr->init_b[g] = init;
-    queue_head(fs, 1, g)[0] = init;
+    run = fs.hdr->run_f && *status == GS_OK;
+    if (blockIdx.x == 0) fs.hdr->run_b = run;
   }
+  __syncthreads();
+  const int g = blockIdx.x, k = fs.hdr->k;
+  const int lo = fs.hdr->qoff[g] + fs.hdr->qa[g], hi = run ? fs.hdr->qoff[g + 1] : lo;
+  const int n = hi - lo;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < BO_W * BO_BINS; i += BO_T) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const int chunk = (n + BO_W - 1) / BO_W;
   const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
-  for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&cnt[w][order_bin(fs, fs.items[lo + e], k)], 1);
+  for (int e = c0 + lane; e < c1; e += 64) {
+    const int it = fs.items[lo + e];
+    if (item_quad(it) < 2) atomicAdd(&cnt[w][order_bin(item_len(fs, it, k))], 1);
+  }
   __syncthreads();
   __shared__ int btot[BO_BINS];
   if (threadIdx.x < BO_BINS) {
@@ -81,21 +100,29 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   __syncthreads();
   if (threadIdx.x < BO_BINS) {
     // exclusive offsets in (bin, wave) order
-    int run = 0;
-    for (int d = 0; d < (int)threadIdx.x; d++) run += btot[d];
+    int run_ = 0;
+    for (int d = 0; d < (int)threadIdx.x; d++) run_ += btot[d];
     for (int q = 0; q < BO_W; q++) {
       const int c = cnt[q][threadIdx.x];
-      cnt[q][threadIdx.x] = run;
-      run += c;
+      cnt[q][threadIdx.x] = run_;
+      run_ += c;
+    }
+    if (threadIdx.x == BO_BINS - 1) {
+      // the backward's own hand-out: the first items go to its workers without a pop
+      const int nb = run_;
+      const int init = min(nb, group_workers(g, nblocks));
+      fs.hdr->nb[g] = nb;
+      fs.hdr->init_b[g] = init;
+      queue_head(fs, 1, g)[0] = init;
     }
   }
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int base = c0; base < c1; base += 64) {
     const int e = base + lane;
-    const bool valid = e < c1;
-    const int it = valid ? fs.items[lo + e] : 0;
-    const uint32_t d = valid ? order_bin(fs, it, k) : 0u;
+    const int it = e < c1 ? fs.items[lo + e] : 0;
+    const bool valid = e < c1 && item_quad(it) < 2;
+    const uint32_t d = valid ? order_bin(item_len(fs, it, k)) : 0u;
     uint64_t peers = wave_ballot(valid);
 #pragma unroll
     for (int b = 0; b < BO_BITS; b++) {
@@ -111,129 +138,175 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   }
 }
 
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, GS_WAVE));
-  return wave_first(v);
+constexpr int BATCH = GS_WAVE;  // entries per batch (one contributor word)
+
+__device__ __forceinline__ bool valid_id(int id, int n) { return (unsigned)id < (unsigned)n; }
+
+// This lane's list entry of a batch, if the batch's word marks it (else -1).
+__device__ __forceinline__ int load_marked_id(const int32_t *__restrict__ sids, int64_t b,
+                                              uint64_t word) {
+  return (word >> __lane_id()) & 1ull ? sids[b + __lane_id()] : -1;
 }
 
-constexpr int BATCH = GS_WAVE;  // splats per staged batch
-
-// Two-stage load pipeline for the back-to-front walk: the ids of the batch
-// after next and the records of the next batch are in flight while a batch is
-// processed. Slots outside the range carry id -1 (and read record 0).
-__device__ __forceinline__ int load_id(const int32_t *__restrict__ sids, int lo, int hi) {
-  const int e = lo + __lane_id();
-  return e < hi ? sids[e] : -1;
+// The 64-bit contributor word of batch m held by lane m of the current round.
+__device__ __forceinline__ uint64_t word_of(uint32_t lo, uint32_t hi, int m) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, m) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)lo, m);
 }
 
-// Walk positions [cs, cs + kmax) back to front for one quarter. Lane state:
-// T (transmittance after the lane's last consumed entry), accum, and lastp,
-// the number of entries the lane consumed from cs. Each staged record carries
-// 1/o, 2b and log2(o) in place of o, depth and pad, so the per-entry work has
-// no reciprocal of o, no doubling and no logarithm.
-__device__ __forceinline__ void walk_back(const Splat *__restrict__ splats,
-                                          const int32_t *__restrict__ sids, int cs, int kmax,
-                                          const SubTile &st, float fx, float fy, int lastp,
-                                          float T, float accum, float g0, float g1, float g2,
-                                          Splat *sbuf, int *sid, float *__restrict__ grads) {
+// Per-lane state of the two pixels of a lane (rows 0 and 1 of its pair).
+struct Pix2 {
+  float fx, fy0, fy1;        // sample positions
+  float T0, T1, acc0, acc1;  // transmittance after the pixel's last entry; accumulator
+  float g00, g01, g02, g10, g11, g12;  // dL/dC of the two pixels
+  int last0, last1;          // entries the pixel consumed from the walk's start
+};
+
+// Walk the item's batches back to front. cw_top / cw_bot: the contributor words
+// of the two quarters at the walk's first batch; nb_top / nb_bot: how many of
+// them are current (the rest were not written for this frame); list: the walk's
+// first list position. Each staged record carries 1/o, 2b and log2(o) in place
+// of o, depth and pad, so the per-entry work has no reciprocal of o, no doubling
+// and no logarithm.
+__device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int n,
+                                          const int32_t *__restrict__ sids, int64_t list,
+                                          const uint64_t *__restrict__ cw_top, int nb_top,
+                                          const uint64_t *__restrict__ cw_bot, int nb_bot,
+                                          Pix2 &x, Splat *sbuf, int *sid,
+                                          float *__restrict__ grads) {
   const int lane = __lane_id();
   const int comp = comp_of_lane(lane);
   // the constant factor each owner lane applies to its sum after the reduction
-  // (a power of two: exact): -1/2 for the two squared offsets
+  // (powers of two: exact): -1/2 for the two squared offsets
   const float post = (comp == 2 || comp == 4) ? -0.5f : 1.0f;
-  int hiE = cs + kmax;
-  int lo = max(cs, hiE - BATCH);
-  int idc = -1, idn = -1;
-  // the next batch's record of this lane, as three registers of four (kept out
-  // of any aggregate: the compiler parked part of one in memory and waited for
-  // its load right after issuing it)
   const float4 *rec4 = reinterpret_cast<const float4 *>(splats);
-  float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
-  if (hiE > cs) {
-    idc = load_id(sids, lo, hiE);
-    const int64_t ri = 3 * (int64_t)(idc >= 0 ? idc : 0);
-    r0 = rec4[ri];
-    r1 = rec4[ri + 1];
-    r2 = rec4[ri + 2];
-    idn = load_id(sids, max(cs, lo - BATCH), lo);
-  }
-  while (hiE > cs) {
-    Splat s;
-    s.p0 = r0;
-    s.p1 = r1;
-    s.p2 = r2;
-    const bool cand = idc >= 0 && rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y,
-                                                st.hx0, st.hx1, st.hy0, st.hy1);
-    s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
-    s.p2.z = 2.0f * s.p0.w;
-    s.p1.y = __builtin_amdgcn_rcpf(s.p1.y);
-    sbuf[lane] = s;
-    sid[lane] = idc;
-    const uint64_t work = wave_ballot(cand);
-    const int nhi = lo, nlo = max(cs, lo - BATCH);
-    // records of [nlo, nhi), ids of the batch below it
-    idc = idn;
-    {
-      const int64_t ri = 3 * (int64_t)(idc >= 0 ? idc : 0);
-      r0 = rec4[ri];
-      r1 = rec4[ri + 1];
-      r2 = rec4[ri + 2];
+  const int nbat = max(nb_top, nb_bot);
+  for (int r0 = (nbat - 1) & ~63; r0 >= 0; r0 -= 64) {
+    // lane i holds the word of batch r0 + i (both quarters' contributors)
+    const int m = r0 + lane;
+    uint64_t wv = 0;
+    if (m < nb_top) wv |= cw_top[m];
+    if (m < nb_bot) wv |= cw_bot[m];
+    const uint32_t wlo = (uint32_t)wv, whi = (uint32_t)(wv >> 32);
+    uint64_t todo = wave_ballot(wv != 0);
+    if (!todo) continue;
+    // pipeline: the records of the batch being staged and the ids of the next
+    // non-empty batch are in flight while a batch is walked
+    int mc = 63 - __builtin_clzll(todo);
+    todo &= ~(1ull << mc);
+    uint64_t wc = word_of(wlo, whi, mc);
+    int idc = load_marked_id(sids, list + 64 * (int64_t)(r0 + mc), wc);
+    const int64_t ri = 3 * (int64_t)(valid_id(idc, n) ? idc : 0);
+    float4 q0 = rec4[ri], q1 = rec4[ri + 1], q2 = rec4[ri + 2];
+    int mn = -1, idn = -1;
+    uint64_t wn = 0;
+    if (todo) {
+      mn = 63 - __builtin_clzll(todo);
+      todo &= ~(1ull << mn);
+      wn = word_of(wlo, whi, mn);
+      idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mn), wn);
     }
-    idn = load_id(sids, max(cs, nlo - BATCH), nlo);
-    wave_sync();
-    const int base = lo - cs;
-    walk_worklist<true>(work, sbuf, [&](const Splat &s, int j) {
-      const int rel = base + j;
-      const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
-      const float dx = fx - s.p0.x, dy = fy - s.p0.y;
-      const float adx = a * dx, cdy = c * dy;
-      // canon_q with the staged 2b
-      const float q = __builtin_fmaf(cdy, dy, __builtin_fmaf(s.p2.z * dx, dy, adx * dx));
-      const bool inr = rel < lastp, inq = q <= s.p2.y;
-      if (!(wave_ballot(inr) & wave_ballot(inq))) return true;
-      const bool hit = inr && inq;
-      // branchless: a missed pixel takes alpha = 0, which leaves T and accum
-      // unchanged and contributes zero to every sum
-      const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-      const float oG = hit ? ex : 0.0f;  // o G
-      const float al = fminf(0.99f, oG);
-      T = T * __builtin_amdgcn_rcpf(1.0f - al);  // T before this splat
-      const float cg = __builtin_fmaf(s.p1.z, g0, __builtin_fmaf(s.p1.w, g1, s.p2.x * g2));
-      const float diff = cg - accum;
-      const float dal = T * diff;  // dL/dalpha
-      accum = __builtin_fmaf(al, diff, accum);
-      const float w = al * T;
-      const bool live_g = oG < 0.99f;  // a clamped alpha passes no gradient
-      // -2 dL/dq, which is also o G dL/dalpha: an unclamped alpha is o G
-      const float m = live_g ? al * dal : 0.0f;
-      float gr[9];
-      gr[0] = m * __builtin_fmaf(b, dy, adx);  // dq/dmx = -2 (a dx + b dy)
-      gr[1] = m * __builtin_fmaf(b, dx, cdy);
-      gr[2] = m * (dx * dx);                   // times -1/2 after the sum
-      gr[3] = -(m * (dx * dy));
-      gr[4] = m * (dy * dy);                   // times -1/2 after the sum
-      gr[5] = m;                               // divided by o after the sum
-      gr[6] = w * g0;
-      gr[7] = w * g1;
-      gr[8] = w * g2;
-      float out = reduce_scatter9(gr);
-      // finish the sum here, where its last exchange fuses into the add,
-      // rather than inside the owner lanes' branch
-      __asm__ volatile("" : "+v"(out));
-      out *= comp == 5 ? s.p1.y : post;
-      if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[j] + comp], out);
-      return true;
-    });
-    wave_sync();
-    hiE = nhi;
-    lo = nlo;
+    for (;;) {
+      Splat s;
+      s.p0 = q0;
+      s.p1 = q1;
+      s.p2 = q2;
+      s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
+      s.p2.z = 2.0f * s.p0.w;
+      s.p1.y = __builtin_amdgcn_rcpf(s.p1.y);
+      sbuf[lane] = s;
+      sid[lane] = idc;
+      // records of the next batch, ids of the one after it
+      idc = idn;
+      {
+        const int64_t rj = 3 * (int64_t)(valid_id(idc, n) ? idc : 0);
+        q0 = rec4[rj];
+        q1 = rec4[rj + 1];
+        q2 = rec4[rj + 2];
+      }
+      int mnn = -1;
+      uint64_t wnn = 0;
+      idn = -1;
+      if (todo) {
+        mnn = 63 - __builtin_clzll(todo);
+        todo &= ~(1ull << mnn);
+        wnn = word_of(wlo, whi, mnn);
+        idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mnn), wnn);
+      }
+      wave_sync();
+      const int base = 64 * (r0 + mc);
+      // an id outside [0, n) (only a failed sort could leave one) is skipped
+      const uint64_t work = wc & wave_ballot(valid_id(sid[lane], n));
+      walk_worklist<true>(work, sbuf, [&](const Splat &s, int j) {
+        const int rel = base + j;
+        const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
+        // the column terms of the canonical q are shared by the lane's two rows
+        const float dx = x.fx - s.p0.x;
+        const float adx = a * dx;
+        const float adxdx = adx * dx, b2dx = s.p2.z * dx;
+        const float dy0 = x.fy0 - s.p0.y, dy1 = x.fy1 - s.p0.y;
+        const float cdy0 = c * dy0, cdy1 = c * dy1;
+        const float qa = __builtin_fmaf(cdy0, dy0, __builtin_fmaf(b2dx, dy0, adxdx));
+        const float qb = __builtin_fmaf(cdy1, dy1, __builtin_fmaf(b2dx, dy1, adxdx));
+        const bool h0 = rel < x.last0 && qa <= s.p2.y;
+        const bool h1 = rel < x.last1 && qb <= s.p2.y;
+        // branchless: a missed pixel takes alpha = 0, which leaves T and accum
+        // unchanged and contributes zero to every sum
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(qa, NEG_HALF_LOG2E, s.p2.w));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(qb, NEG_HALF_LOG2E, s.p2.w));
+        const float oG0 = h0 ? e0 : 0.0f, oG1 = h1 ? e1 : 0.0f;  // o G
+        const float al0 = fminf(0.99f, oG0), al1 = fminf(0.99f, oG1);
+        x.T0 = x.T0 * __builtin_amdgcn_rcpf(1.0f - al0);  // T before this splat
+        x.T1 = x.T1 * __builtin_amdgcn_rcpf(1.0f - al1);
+        const float cg0 = __builtin_fmaf(s.p1.z, x.g00, __builtin_fmaf(s.p1.w, x.g01, s.p2.x * x.g02));
+        const float cg1 = __builtin_fmaf(s.p1.z, x.g10, __builtin_fmaf(s.p1.w, x.g11, s.p2.x * x.g12));
+        const float d0 = cg0 - x.acc0, d1 = cg1 - x.acc1;
+        const float dal0 = x.T0 * d0, dal1 = x.T1 * d1;  // dL/dalpha
+        x.acc0 = __builtin_fmaf(al0, d0, x.acc0);
+        x.acc1 = __builtin_fmaf(al1, d1, x.acc1);
+        const float w0 = al0 * x.T0, w1 = al1 * x.T1;
+        // -2 dL/dq, which is also o G dL/dalpha: an unclamped alpha is o G; a
+        // clamped alpha passes no gradient
+        const float m0 = oG0 < 0.99f ? al0 * dal0 : 0.0f;
+        const float m1 = oG1 < 0.99f ? al1 * dal1 : 0.0f;
+        // the lane's two rows summed: with M = m0 + m1, Sy = m0 dy0 + m1 dy1 and
+        // Syy = m0 dy0^2 + m1 dy1^2, each derivative needs dx once
+        const float M = m0 + m1;
+        const float my0 = m0 * dy0, my1 = m1 * dy1;
+        const float Sy = my0 + my1;
+        float gr[9];
+        gr[0] = __builtin_fmaf(adx, M, b * Sy);     // dq/dmx = -2 (a dx + b dy)
+        gr[1] = __builtin_fmaf(b * dx, M, c * Sy);  // dq/dmy = -2 (b dx + c dy)
+        gr[2] = (dx * dx) * M;                      // times -1/2 after the sum
+        gr[3] = -(dx * Sy);
+        gr[4] = __builtin_fmaf(my1, dy1, my0 * dy0);  // times -1/2 after the sum
+        gr[5] = M;                                    // divided by o after the sum
+        gr[6] = __builtin_fmaf(w1, x.g10, w0 * x.g00);
+        gr[7] = __builtin_fmaf(w1, x.g11, w0 * x.g01);
+        gr[8] = __builtin_fmaf(w1, x.g12, w0 * x.g02);
+        float out = reduce_scatter9(gr);
+        // finish the sum here, where its last exchange fuses into the add,
+        // rather than inside the owner lanes' branch
+        __asm__ volatile("" : "+v"(out));
+        out *= comp == 5 ? s.p1.y : post;
+        if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[j] + comp], out);
+        return true;
+      });
+      wave_sync();
+      if (mn < 0) break;
+      mc = mn;
+      wc = wn;
+      mn = mnn;
+      wn = wnn;
+    }
   }
 }
 
+__device__ __forceinline__ int ceil64(int v) { return (max(v, 0) + 63) >> 6; }
+
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
 __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
-    const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
+    const Splat *__restrict__ splats, int n, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
     const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads) {
@@ -242,9 +315,12 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
   Splat *sbuf = sbuf_all[wave_in_block()];
   int *sid = sid_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
+  if (!fs.hdr->run_b) return;  // the frame failed earlier: nothing to differentiate
+  fs.nw = fs.hdr->nw;
   const int k = fs.hdr->k;
   const int64_t P = (int64_t)cam.width * cam.height * cam.views;
   const int lane = __lane_id();
+  const int col = lane & 7, rp = lane >> 3;
   __shared__ uint32_t drained;
   Worker wk = make_worker(&drained);
   for (;;) {
@@ -252,89 +328,123 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     if (t < 0) break;
     wk.round++;
     const int it = fs.bitems[t];
-    const int kind = item_kind(it), quad = item_quad(it), p = item_chunk(it);
+    const int kind = item_kind(it), half = item_quad(it), p = item_chunk(it);
     const int idx = item_index(it);
     const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
-    const SubTile st = subtile_of(tile, quad, cam);
+    const SubTile st = subtile_of(tile, half, cam);  // the half's upper quarter
     if (st.empty) continue;
-    const int px = st.x0 + (lane & 7), py = st.y0 + (lane >> 3);
-    const bool inside = px < cam.width && py < cam.height;
-    const int64_t pix = (int64_t)(st.prow + py) * cam.width + px;
+    const int px = st.x0 + col, py0 = st.y0 + 2 * rp, py1 = py0 + 1;
+    const bool in0 = px < cam.width && py0 < cam.height;
+    const bool in1 = px < cam.width && py1 < cam.height;
+    const int64_t pix0 = (int64_t)(st.prow + py0) * cam.width + px;
+    const int64_t pix1 = pix0 + cam.width;
     const int2 rg = ranges[tile];
-    float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+    Pix2 x;
+    x.fx = (float)px + 0.5f;
+    x.fy0 = (float)py0 + 0.5f;
+    x.fy1 = (float)py1 + 0.5f;
+    x.g00 = x.g01 = x.g02 = x.g10 = x.g11 = x.g12 = 0.f;
     // what lies behind the last blended splat, per unit of final transmittance:
     // the background's bg . dL/dC and dL/dT_final (0 when neither is given)
-    float extra = 0.f;
-    if (inside) {
-      g0 = dL[pix];
-      g1 = dL[P + pix];
-      g2 = dL[2 * P + pix];
+    float ex0 = 0.f, ex1 = 0.f;
+    if (in0) {
+      x.g00 = dL[pix0];
+      x.g01 = dL[P + pix0];
+      x.g02 = dL[2 * P + pix0];
       if (cam.bg_on) {
-        extra = fmaf(cam.bg[0], g0, fmaf(cam.bg[1], g1, cam.bg[2] * g2));
-        if (dT) extra += dT[pix];
+        ex0 = fmaf(cam.bg[0], x.g00, fmaf(cam.bg[1], x.g01, cam.bg[2] * x.g02));
+        if (dT) ex0 += dT[pix0];
       }
     }
-    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
-    if (kind == ITEM_PLAIN) {
-      float T = 1.0f;
-      int lastp = 0;
-      if (inside) {
-        T = Tfin[pix];
-        lastp = last[pix];
+    if (in1) {
+      x.g10 = dL[pix1];
+      x.g11 = dL[P + pix1];
+      x.g12 = dL[2 * P + pix1];
+      if (cam.bg_on) {
+        ex1 = fmaf(cam.bg[0], x.g10, fmaf(cam.bg[1], x.g11, cam.bg[2] * x.g12));
+        if (dT) ex1 += dT[pix1];
       }
-      const int kmax = min(wave_max(lastp), fs.sub_last[tile * 4 + quad]);
-      walk_back(splats, sorted_ids, rg.x, kmax, st, fx, fy, lastp, T, extra, g0, g1, g2, sbuf,
-                sid, grads);
+    }
+    const int qtop = half, qbot = half + 2;
+    if (kind == ITEM_PLAIN) {
+      x.T0 = in0 ? Tfin[pix0] : 1.0f;
+      x.T1 = in1 ? Tfin[pix1] : 1.0f;
+      x.last0 = in0 ? last[pix0] : 0;
+      x.last1 = in1 ? last[pix1] : 0;
+      x.acc0 = ex0;
+      x.acc1 = ex1;
+      walk_back(splats, n, sorted_ids, rg.x, contrib_base(fs, qtop, tile, rg.x),
+                ceil64(fs.sub_last[tile * 4 + qtop]), contrib_base(fs, qbot, tile, rg.x),
+                ceil64(fs.sub_last[tile * 4 + qbot]), x, sbuf, sid, grads);
       continue;
     }
-    // a chunk of a heavy tile
+    // a chunk of a heavy tile: the lane's two pixels lie in one quarter, at
+    // positions ql and ql + 8 of that quarter's chunk state
     int cs, ce;
     chunk_range(rg.x, rg.y, p, k, cs, ce);
-    const int ci = chunk_index(idx, p, quad, k);
-    const int64_t cp = (int64_t)ci * 64 + lane;
-    int lb = inside ? fs.LB[cp] : -1;
-    float T = 1.0f, accum = 0.0f;
-    if (lb > 0) {
-      T = fs.TB[cp];
-      float behind = 0.0f;  // sum over later chunks of C . dL/dC
-      for (int q = p + 1; q < k; q++) {
-        const int64_t c2 = (int64_t)chunk_index(idx, q, quad, k) * 64 + lane;
-        if (fs.LB[c2] < 0) break;
-        behind = __builtin_fmaf(fs.CB[3 * c2], g0,
-                                __builtin_fmaf(fs.CB[3 * c2 + 1], g1,
-                                               __builtin_fmaf(fs.CB[3 * c2 + 2], g2, behind)));
+    const int q = rp < 4 ? qtop : qbot;
+    const int ql = col + 8 * ((2 * rp) & 7);
+    const int ci = chunk_index(idx, p, q, k);
+    float Tc[2] = {1.0f, 1.0f}, ac[2] = {0.f, 0.f};
+    int lc[2] = {0, 0};
+    const bool inr[2] = {in0, in1};
+    const float exr[2] = {ex0, ex1};
+    const int64_t pixr[2] = {pix0, pix1};
+    const float gr0[2] = {x.g00, x.g10}, gr1[2] = {x.g01, x.g11}, gr2[2] = {x.g02, x.g12};
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      const int64_t cp = (int64_t)ci * 64 + ql + 8 * r;
+      int lb = inr[r] ? fs.LB[cp] : -1;
+      if (lb > 0) {
+        Tc[r] = fs.TB[cp];
+        float behind = 0.0f;  // sum over later chunks of C . dL/dC
+        for (int q2 = p + 1; q2 < k; q2++) {
+          const int64_t c2 = (int64_t)chunk_index(idx, q2, q, k) * 64 + ql + 8 * r;
+          if (fs.LB[c2] < 0) break;
+          behind = __builtin_fmaf(fs.CB[3 * c2], gr0[r],
+                                  __builtin_fmaf(fs.CB[3 * c2 + 1], gr1[r],
+                                                 __builtin_fmaf(fs.CB[3 * c2 + 2], gr2[r], behind)));
+        }
+        if (cam.bg_on) behind = fmaf(Tfin[pixr[r]], exr[r], behind);
+        ac[r] = behind / Tc[r];
+      } else {
+        lb = 0;
       }
-      if (cam.bg_on) behind = fmaf(Tfin[pix], extra, behind);
-      accum = behind / T;
-    } else {
-      lb = 0;
+      lc[r] = lb;
     }
-    const int kmax = min(wave_max(lb), fs.chunk_last[ci]);
-    walk_back(splats, sorted_ids, cs, kmax, st, fx, fy, lb, T, accum, g0, g1, g2, sbuf, sid,
-              grads);
+    x.T0 = Tc[0];
+    x.T1 = Tc[1];
+    x.acc0 = ac[0];
+    x.acc1 = ac[1];
+    x.last0 = lc[0];
+    x.last1 = lc[1];
+    const uint64_t *cw0 = contrib_base(fs, qtop, tile, rg.x) + ((cs - rg.x) >> 6);
+    const uint64_t *cw1 = contrib_base(fs, qbot, tile, rg.x) + ((cs - rg.x) >> 6);
+    walk_back(splats, n, sorted_ids, cs, cw0, ceil64(fs.chunk_last[chunk_index(idx, p, qtop, k)]),
+              cw1, ceil64(fs.chunk_last[chunk_index(idx, p, qbot, k)]), x, sbuf, sid, grads);
   }
 }
 
 }  // namespace
 
-hipError_t gs_launch_render_bwd(const float *splats, const int32_t *sorted_ids,
+hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                const float *dT, float *grads, int n, int workers_waves,
+                                const float *dT, float *grads, int32_t *status, int workers_waves,
                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   const int zero_blocks = (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
   hipLaunchKernelGGL(k_bwd_prep, dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
-                     reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng);
+                     reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng, status);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_render_bwd, dim3(nblocks),
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
-                     reinterpret_cast<const Splat *>(splats), sorted_ids,
+                     reinterpret_cast<const Splat *>(splats), n, sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles, dL, dT, grads);
   hipError_t e = hipGetLastError();

@@ -50,15 +50,35 @@ struct PlanHdr {
   // its index within its group (in the forward only in groups without chunk
   // items, since a pass-B item waits on items in front of it).
   int32_t init_f[GS_GROUPS], init_b[GS_GROUPS];
+  // The backward's items of group g (half tiles) are bitems[qoff[g] + qa[g], + nb[g]).
+  int32_t nb[GS_GROUPS];
+  // The raster kernels run only when these are set: the frame's device status
+  // was GS_OK when the schedule (forward) or the backward's preparation ran.
+  int32_t run_f, run_b;
+  int64_t nw;  // contributor words per quarter (from the state's capacity)
 };
 
-// Byte layout of fwd_state for T tiles.
+// Contributor record of the forward pass ("What the 3DGS Literature Left on the
+// Table", Step 4, kept as a bitmap instead of a compacted list): for every
+// quarter q of a tile and every 64-entry batch m of the tile's list (batches are
+// aligned to the tile's first entry; chunk boundaries are multiples of 64
+// entries), one 64-bit word whose bit j says that some pixel of the quarter
+// blended entry 64 m + j. Quarter q's words of tile t start at word
+// (start_t >> 6) + t of array q: disjoint per tile, at most ceil(cap / 64) + T + 2
+// words per quarter. The forward writes every batch it walks, so words below
+// ceil(last hit / 64) are current; the backward ignores the rest.
+__host__ __device__ inline int64_t contrib_words(int T, int64_t cap) {
+  return (cap + 63) / 64 + T + 2;
+}
+
+// Byte layout of fwd_state for T tiles and a pair capacity cap (the contributor
+// bitmap comes last, so the capacity a state serves follows from its size).
 struct FwdLayout {
   size_t hdr, heads, sub_last, order, counts, items, sat, doneA, doneB, chunk_last, PA, CB, TB,
-      LB, bitems, total;
+      LB, HB, bitems, contrib, total;
 };
 
-__host__ __device__ inline FwdLayout fwd_layout(int T) {
+__host__ __device__ inline FwdLayout fwd_layout(int T, int64_t cap) {
   FwdLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -81,9 +101,19 @@ __host__ __device__ inline FwdLayout fwd_layout(int T) {
   L.CB = take(4 * cq * 64 * 3);
   L.TB = take(4 * cq * 64);
   L.LB = take(4 * cq * 64);
+  L.HB = take(4 * cq * 64);
   L.bitems = take(4 * ((size_t)T * 4 + 2 * cq));
+  L.contrib = take(8 * 4 * (size_t)contrib_words(T, cap));
   L.total = off;
   return L;
+}
+
+// The largest pair capacity whose forward state fits in `bytes` (-1 if none).
+__host__ __device__ inline int64_t fwd_state_capacity(int T, size_t bytes) {
+  const FwdLayout L = fwd_layout(T, 0);
+  if (bytes < L.total) return -1;
+  const int64_t words = (int64_t)((bytes - L.contrib) / 32);
+  return (words - T - 2) * 64;
 }
 
 struct FwdState {
@@ -92,11 +122,16 @@ struct FwdState {
   int32_t *sub_last, *order, *counts, *items, *sat, *doneA, *doneB, *chunk_last;
   float *PA, *CB, *TB;
   int32_t *LB;
+  int32_t *HB;      // pass B's per-pixel hit counts (only when the forward counts)
   int32_t *bitems;  // the backward's queue items, longest walk first within each group
+  uint64_t *contrib;  // [4][nw] contributor words
+  int64_t nw;         // words per quarter: the schedule sets hdr->nw, kernels copy it here
 };
 
+// Only the contributor bitmap's word count depends on the state's capacity, and
+// the bitmap comes last, so the arrays are found from T alone.
 __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
-  const FwdLayout L = fwd_layout(T);
+  const FwdLayout L = fwd_layout(T, 0);
   char *b = reinterpret_cast<char *>(base);
   FwdState s;
   s.hdr = reinterpret_cast<PlanHdr *>(b + L.hdr);
@@ -113,8 +148,17 @@ __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
   s.CB = reinterpret_cast<float *>(b + L.CB);
   s.TB = reinterpret_cast<float *>(b + L.TB);
   s.LB = reinterpret_cast<int32_t *>(b + L.LB);
+  s.HB = reinterpret_cast<int32_t *>(b + L.HB);
   s.bitems = reinterpret_cast<int32_t *>(b + L.bitems);
+  s.contrib = reinterpret_cast<uint64_t *>(b + L.contrib);
+  s.nw = 0;
   return s;
+}
+
+// First contributor word of quarter q of the tile whose list starts at `start`.
+__host__ __device__ __forceinline__ uint64_t *contrib_base(const FwdState &fs, int q, int tile,
+                                                         int start) {
+  return fs.contrib + (int64_t)q * fs.nw + (start >> 6) + tile;
 }
 
 __host__ __device__ __forceinline__ int32_t *queue_head(const FwdState &fs, int pass, int g) {
@@ -136,13 +180,16 @@ __host__ __device__ __forceinline__ int tile_group(int tile, int tiles_x) {
 // Index of (slot s, chunk p, quad q) among the chunk items.
 __device__ __forceinline__ int chunk_index(int s, int p, int q, int k) { return (s * k + p) * 4 + q; }
 
-// Chunk p of k over [start, end): equal contiguous pieces of ceil(N/k).
+// Chunk p of k over [start, end): contiguous pieces of ceil(N/k) entries rounded
+// up to a multiple of 64 (so every chunk starts on a contributor word; the last
+// pieces may be shorter or empty).
 __device__ __forceinline__ void chunk_range(int start, int end, int p, int k, int &cs, int &ce) {
   const int N = end - start;
-  const int csize = (N + k - 1) / k;
+  const int csize = ((N + k - 1) / k + 63) & ~63;
   cs = min(end, start + p * csize);
   ce = min(end, cs + csize);
 }
+
 
 struct SubTile {
   int tile, quad, x0, y0;    // x0, y0 in the coordinates of the tile's view
@@ -252,7 +299,8 @@ __device__ __forceinline__ void walk_worklist(uint64_t w, const Rec *sbuf, F &&f
 // g is recorded as drained in the wave and in the workgroup's LDS mask).
 __device__ __forceinline__ int pop_group(const FwdState &fs, int pass, Worker &w, int g) {
   const PlanHdr *hd = fs.hdr;
-  const int lo = hd->qoff[g] + (pass ? hd->qa[g] : 0), hi = hd->qoff[g + 1];
+  const int lo = hd->qoff[g] + (pass ? hd->qa[g] : 0);
+  const int hi = pass ? lo + hd->nb[g] : hd->qoff[g + 1];
   if (lo < hi) {
     const int t = queue_pop(queue_head(fs, pass, g));
     if (lo + t < hi) return lo + t;
@@ -263,9 +311,10 @@ __device__ __forceinline__ int pop_group(const FwdState &fs, int pass, Worker &w
   return -1;
 }
 
-// Next item (an index into items[]) of a worker, or -1 when every queue is
-// empty. pass 0 (forward) serves every item of a group; pass 1 (backward)
-// skips the pass-A items. The first item comes without a pop: the queue heads
+// Next item (an index into items[], or bitems[] for the backward) of a worker,
+// or -1 when every queue is empty. pass 0 (forward) serves every item of a
+// group; pass 1 (backward) serves the nb[g] half-tile items that its
+// preparation wrote where the group's plain and pass-B items start. The first item comes without a pop: the queue heads
 // start past the items handed out that way, so a frame's first wave of work
 // does not serialise on the heads. After that the worker pops its home group,
 // then the others nearest first (+1, -1, +2, ...), neighbouring strips sharing

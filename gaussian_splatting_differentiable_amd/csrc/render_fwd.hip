@@ -54,6 +54,10 @@ __device__ __forceinline__ Px pixel_of(const SubTile &st, const CamK &cam) {
   return x;
 }
 
+// An id outside [0, n) (which only a frame whose sort failed could hold) is an
+// empty slot: it is neither read nor blended.
+__device__ __forceinline__ bool valid_id(int id, int n) { return (unsigned)id < (unsigned)n; }
+
 // Stage one splat record for the worklist: 2b and log2(o) replace b and pad.
 __device__ __forceinline__ bool stage(Splat s, const SubTile &st, Splat *slot) {
   const bool cand = rect_may_hit(s.p0.x, s.p0.y, s.p0.z, s.p0.w, s.p1.x, s.p2.y, st.hx0, st.hx1,
@@ -79,18 +83,20 @@ __device__ __forceinline__ int load_id(const int32_t *__restrict__ sids, int b, 
 }
 
 __device__ __forceinline__ void pipe_start(Pipe &pp, const Splat *__restrict__ splats,
-                                           const int32_t *__restrict__ sids, int cs, int ce) {
+                                           const int32_t *__restrict__ sids, int cs, int ce,
+                                           int n) {
   pp.idc = load_id(sids, cs, ce);
-  pp.rec = splats[pp.idc >= 0 ? pp.idc : 0];
+  pp.rec = splats[valid_id(pp.idc, n) ? pp.idc : 0];
   pp.idn = load_id(sids, cs + BATCH, ce);
 }
 
 // After the batch at b is staged: start the records of b + BATCH and the ids of
 // b + 2 BATCH.
 __device__ __forceinline__ void pipe_advance(Pipe &pp, const Splat *__restrict__ splats,
-                                             const int32_t *__restrict__ sids, int b, int ce) {
+                                             const int32_t *__restrict__ sids, int b, int ce,
+                                             int n) {
   pp.idc = pp.idn;
-  pp.rec = splats[pp.idc >= 0 ? pp.idc : 0];
+  pp.rec = splats[valid_id(pp.idc, n) ? pp.idc : 0];
   pp.idn = load_id(sids, b + 2 * BATCH, ce);
 }
 
@@ -98,6 +104,7 @@ struct Blend {
   float C0, C1, C2, T;
   int consumed;  // list entries consumed (relative to the range start)
   int wlast;     // 1 + last position any lane hit (relative), 0 if none
+  int nh;        // this lane's hits (counted only when STATS)
 };
 
 // Blend [cs, ce) into pixels that start with transmittance T0. Branchless per
@@ -105,27 +112,32 @@ struct Blend {
 // colour and T unchanged bit for bit. A lane is alive exactly while its T is at
 // least 1e-4 (lanes outside the image start at T = 0), so the hit mask is the
 // AND of two compare ballots and needs no per-lane flag.
+// cw: the quarter's contributor word of the range's first batch; every batch
+// walked writes its word (bit j: some lane blended entry j of the batch).
 template <bool STATS>
 __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int cs, int ce,
-                                             const SubTile &st, const Px &x, float T0,
-                                             Splat *sbuf, uint32_t &nhits,
-                                             uint32_t &nsteps, uint32_t &nhsteps) {
+                                             int n, const SubTile &st, const Px &x, float T0,
+                                             Splat *sbuf, uint64_t *__restrict__ cw,
+                                             uint32_t &nhits, uint32_t &nsteps,
+                                             uint32_t &nhsteps) {
   Blend r;
   r.C0 = r.C1 = r.C2 = 0.0f;
   r.T = x.inside ? T0 : 0.0f;
   r.consumed = r.T >= T_STOP ? ce - cs : 0;
   r.wlast = 0;
+  r.nh = 0;
   bool live = wave_ballot(r.T >= T_STOP) != 0;
   const int lane = __lane_id();
   Pipe pp;
-  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce);
+  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
   for (int b = cs; b < ce && live; b += BATCH) {
-    const bool cand = stage(pp.rec, st, &sbuf[lane]) && pp.idc >= 0;
+    const bool cand = stage(pp.rec, st, &sbuf[lane]) && valid_id(pp.idc, n);
     const uint64_t work = wave_ballot(cand);
-    pipe_advance(pp, splats, sids, b, ce);
+    pipe_advance(pp, splats, sids, b, ce, n);
     wave_sync();
     const int base = b - cs;
+    uint64_t bm = 0;  // the batch's entries that some lane blended
     walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
       const int pos = base + j;
       const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
@@ -138,7 +150,9 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
       if constexpr (STATS) {
         nhits += __popcll(hm);
         nhsteps++;
+        r.nh += hit ? 1 : 0;
       }
+      bm |= 1ull << j;
       r.wlast = pos + 1;
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
       const float al = hit ? fminf(0.99f, ex) : 0.0f;
@@ -151,6 +165,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
       live = wave_ballot(r.T >= T_STOP) != 0;
       return live;
     });
+    if (lane == 0) cw[base >> 6] = bm;
     wave_sync();
   }
   return r;
@@ -161,15 +176,15 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
 template <bool STATS>
 __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
                                                const int32_t *__restrict__ sids, int cs, int ce,
-                                               const SubTile &st, const Px &x, Splat *sbuf,
-                                               const int32_t *sat, int chunk, bool &gave_up,
-                                               uint32_t &nsteps) {
+                                               int n, const SubTile &st, const Px &x,
+                                               Splat *sbuf, const int32_t *sat, int chunk,
+                                               bool &gave_up, uint32_t &nsteps) {
   float P = x.inside ? 1.0f : 0.0f;
   bool live = wave_ballot(P >= T_STOP) != 0;
   gave_up = false;
   const int lane = __lane_id();
   Pipe pp;
-  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce);
+  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
   // sat is read one batch late: the load goes out with the batch prefetch, so
   // waiting for it costs nothing beyond the wait for the prefetch itself
   int satv = chunk;
@@ -178,9 +193,9 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
       gave_up = true;
       break;
     }
-    const bool cand = stage(pp.rec, st, &sbuf[lane]) && pp.idc >= 0;
+    const bool cand = stage(pp.rec, st, &sbuf[lane]) && valid_id(pp.idc, n);
     const uint64_t work = wave_ballot(cand);
-    pipe_advance(pp, splats, sids, b, ce);
+    pipe_advance(pp, splats, sids, b, ce, n);
     const int satn = __hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wave_sync();
     walk_worklist<false>(work, sbuf, [&](const Splat &s, int) {
@@ -220,13 +235,16 @@ __device__ __forceinline__ int ld_i(const int32_t *p) {
 template <bool STATS>
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
 __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
-    const Splat *__restrict__ splats, const int32_t *__restrict__ sorted_ids,
+    const Splat *__restrict__ splats, int n, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
     int32_t *__restrict__ last, char *__restrict__ state, int T,
-    unsigned long long *__restrict__ stats) {
+    unsigned long long *__restrict__ stats, int32_t *__restrict__ pixel_hits,
+    int32_t *__restrict__ status) {
   __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
   Splat *sbuf = sbuf_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, T);
+  if (!fs.hdr->run_f) return;  // the frame failed earlier: the schedule planned nothing
+  fs.nw = fs.hdr->nw;
   const int k = fs.hdr->k;
   const int P = cam.width * cam.height * cam.views;
   const int lane = __lane_id();
@@ -249,14 +267,16 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
         if (lane == 0) fs.sub_last[tile * 4 + quad] = 0;
         continue;
       }
-      const Blend r = blend_range<STATS>(splats, sorted_ids, rg.x, rg.y, st, x, 1.0f, sbuf, nhits,
-                                           nsteps, nhsteps);
+      const Blend r = blend_range<STATS>(splats, sorted_ids, rg.x, rg.y, n, st, x, 1.0f, sbuf,
+                                           contrib_base(fs, quad, tile, rg.x), nhits, nsteps,
+                                           nhsteps);
       if (x.inside) {
         rgb[x.p] = cam.bg_on ? fmaf(r.T, cam.bg[0], r.C0) : r.C0;
         rgb[P + x.p] = cam.bg_on ? fmaf(r.T, cam.bg[1], r.C1) : r.C1;
         rgb[2 * P + x.p] = cam.bg_on ? fmaf(r.T, cam.bg[2], r.C2) : r.C2;
         Tout[x.p] = r.T;
         last[x.p] = r.consumed;
+        if (STATS && pixel_hits) pixel_hits[x.p] += r.nh;
       }
       if (lane == 0) fs.sub_last[tile * 4 + quad] = r.wlast;
       continue;
@@ -269,7 +289,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       float Pp = 0.0f;
       if (!st.empty) {
         bool gave_up = false;
-        Pp = product_range<STATS>(splats, sorted_ids, cs, ce, st, x, sbuf, sat, p, gave_up,
+        Pp = product_range<STATS>(splats, sorted_ids, cs, ce, n, st, x, sbuf, sat, p, gave_up,
                                   nsteps);
         if (gave_up) Pp = 0.0f;  // an earlier chunk already took every pixel below 1e-4
         // every pixel of the quarter below the threshold: later chunks may give up
@@ -289,6 +309,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
         while (ld_flag(&fs.doneA[chunk_index(idx, q, quad, k)]) == 0) {
           if (++spins > GS_SPIN_LIMIT) {
             atomicOr(&fs.hdr->err, 1);
+            report_status(status, GS_ERR_TIMEOUT);
             ok = 0;
             break;
           }
@@ -310,9 +331,12 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     r.T = Tin;
     r.consumed = -1;
     r.wlast = 0;
+    r.nh = 0;
     const bool skip = st.empty || ld_i(sat) < p;
     if (!skip) {
-      r = blend_range<STATS>(splats, sorted_ids, cs, ce, st, x, Tin, sbuf, nhits, nsteps, nhsteps);
+      r = blend_range<STATS>(splats, sorted_ids, cs, ce, n, st, x, Tin, sbuf,
+                             contrib_base(fs, quad, tile, rg.x) + ((cs - rg.x) >> 6), nhits,
+                             nsteps, nhsteps);
       if (!(x.inside && Tin >= T_STOP)) r.consumed = -1;  // stopped before this chunk
     }
     const int64_t cp = (int64_t)ci * 64 + lane;
@@ -321,6 +345,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     fs.CB[3 * cp + 2] = r.C2;
     fs.TB[cp] = r.T;
     fs.LB[cp] = r.consumed;
+    if (STATS) fs.HB[cp] = r.nh;
     if (lane == 0) fs.chunk_last[ci] = r.wlast;
     wave_release();
     int prev = 0;
@@ -329,32 +354,44 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
                                     __HIP_MEMORY_SCOPE_AGENT);
     prev = wave_first(prev);
     if (prev != k - 1 || st.empty) continue;
-    // the last finisher of this quarter composes the chunks in depth order
+    // the last finisher of this quarter composes the chunks in depth order. The
+    // image ends at the first chunk after which T is below 1e-4; a later chunk
+    // that pass A's products still let through (rounding at a knife edge) is
+    // marked as not reached, so the backward takes exactly the composed chunks.
     __threadfence();
     float C0 = 0.f, C1 = 0.f, C2 = 0.f, Tf = 1.0f;
-    int lastv = 0;
+    int lastv = 0, nhv = 0, qend = k;
     for (int q = 0; q < k; q++) {
       const int64_t c2 = (int64_t)chunk_index(idx, q, quad, k) * 64 + lane;
       const int lb = ld_i(&fs.LB[c2]);
-      if (lb < 0) break;
+      if (lb < 0) {
+        qend = q;
+        break;
+      }
       C0 += ld_f(&fs.CB[3 * c2]);
       C1 += ld_f(&fs.CB[3 * c2 + 1]);
       C2 += ld_f(&fs.CB[3 * c2 + 2]);
       Tf = ld_f(&fs.TB[c2]);
+      if (STATS) nhv += ld_i(&fs.HB[c2]);
       int qs, qe;
       chunk_range(rg.x, rg.y, q, k, qs, qe);
       lastv = qs - rg.x + lb;
-      if (Tf < T_STOP) break;
+      if (Tf < T_STOP) {
+        qend = q + 1;
+        break;
+      }
     }
+    for (int q = qend; q < k; q++) fs.LB[(int64_t)chunk_index(idx, q, quad, k) * 64 + lane] = -1;
     if (x.inside) {
       rgb[x.p] = cam.bg_on ? fmaf(Tf, cam.bg[0], C0) : C0;
       rgb[P + x.p] = cam.bg_on ? fmaf(Tf, cam.bg[1], C1) : C1;
       rgb[2 * P + x.p] = cam.bg_on ? fmaf(Tf, cam.bg[2], C2) : C2;
       Tout[x.p] = Tf;
       last[x.p] = lastv;
+      if (STATS && pixel_hits) pixel_hits[x.p] += nhv;
     }
   }
-  if (STATS && lane == 0) {
+  if (STATS && stats && lane == 0) {
     atomicAdd(&stats[0], (unsigned long long)nhits);
     atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
     atomicAdd(&stats[2], (unsigned long long)nhsteps);
@@ -365,28 +402,31 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
 
 hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
                               int force_h, double lambda_, double beta, double eps, int nblocks,
-                              void *fwd_state, int64_t *stats, hipStream_t st);
+                              void *fwd_state, int64_t *stats, int32_t *status,
+                              int64_t cap_pairs, hipStream_t st);
 
-hipError_t gs_launch_render_fwd(const float *splats, const int32_t *sorted_ids,
+hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
-                                int64_t *stats, int workers_waves, hipEvent_t ev0,
+                                int64_t cap_pairs, int64_t *stats, int32_t *pixel_hits,
+                                int32_t *status, int workers_waves, hipEvent_t ev0,
                                 hipEvent_t ev1, hipStream_t st) {
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   hipError_t e = gs_launch_schedule(ranges, cam, sched.chunk_mode, sched.force_k, sched.force_h,
                                     sched.lambda_, sched.beta, sched.eps, nblocks, fwd_state,
-                                    stats, st);
+                                    stats, status, cap_pairs, st);
   if (e != hipSuccess) return e;
   // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
   // queues empty exit at once
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(stats ? k_render_fwd<true> : k_render_fwd<false>, dim3(nblocks),
+  const bool count = stats || pixel_hits;
+  hipLaunchKernelGGL(count ? k_render_fwd<true> : k_render_fwd<false>, dim3(nblocks),
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
-                     reinterpret_cast<const Splat *>(splats), sorted_ids,
+                     reinterpret_cast<const Splat *>(splats), n, sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,
-                     reinterpret_cast<unsigned long long *>(stats));
+                     reinterpret_cast<unsigned long long *>(stats), pixel_hits, status);
   e = hipGetLastError();
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
   return e;

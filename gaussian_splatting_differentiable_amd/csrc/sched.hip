@@ -253,9 +253,39 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
                                                  int chunk_mode, int force_k, int force_h,
                                                  double lambda_, double beta, double eps,
                                                  int nblocks, char *__restrict__ fwd_state,
-                                                 unsigned long long *__restrict__ stats) {
+                                                 unsigned long long *__restrict__ stats,
+                                                 int32_t *__restrict__ status, int64_t cap_pairs) {
   extern __shared__ __align__(16) uint32_t dyn[];
   FwdState fs = fwd_state_at(fwd_state, T);
+  // 0. the frame runs only if every earlier call of it succeeded and its pairs
+  //    fit the state's contributor bitmap; otherwise the plan is empty
+  __shared__ int run;
+  if (threadIdx.x == 0) {
+    const int st = *status;
+    const int64_t npairs = T > 0 ? (int64_t)ranges[T - 1].y : 0;
+    run = st == GS_OK && npairs <= cap_pairs;
+    if (st == GS_OK && npairs > cap_pairs) report_status(status, GS_ERR_WORKSPACE);
+    fs.hdr->run_f = run;
+    fs.hdr->run_b = 0;
+    fs.hdr->nw = contrib_words(T, cap_pairs);
+    fs.hdr->err = 0;
+    fs.hdr->ntiles = T;
+  }
+  __syncthreads();
+  if (!run) {
+    if (threadIdx.x <= GS_GROUPS) fs.hdr->qoff[threadIdx.x] = 0;
+    if (threadIdx.x < GS_GROUPS) {
+      fs.hdr->qa[threadIdx.x] = fs.hdr->init_f[threadIdx.x] = fs.hdr->init_b[threadIdx.x] = 0;
+      fs.hdr->nb[threadIdx.x] = 0;
+      queue_head(fs, 0, threadIdx.x)[0] = queue_head(fs, 1, threadIdx.x)[0] = 0;
+    }
+    if (threadIdx.x == 0) {
+      fs.hdr->h = 0;
+      fs.hdr->k = 1;
+      fs.hdr->nA = fs.hdr->nplain = 0;
+    }
+    return;
+  }
   const double workers = (double)(nblocks * GS_WAVES_PER_BLOCK) / 4.0;  // four waves per tile
   // working arrays: LDS for frames of up to TL tiles, else the forward state's
   // item and bound arrays (written for real only after they served here)
@@ -438,8 +468,6 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     fs.hdr->k = k;
     fs.hdr->nA = nA;
     fs.hdr->nplain = 4 * (T - h);
-    fs.hdr->err = 0;
-    fs.hdr->ntiles = T;
     if (stats) atomicAdd(&stats[3], (unsigned long long)h);
   }
 }
@@ -448,7 +476,8 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
 
 hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
                               int force_h, double lambda_, double beta, double eps, int nblocks,
-                              void *fwd_state, int64_t *stats, hipStream_t st) {
+                              void *fwd_state, int64_t *stats, int32_t *status,
+                              int64_t cap_pairs, hipStream_t st) {
   const int T = cam.tiles_x * cam.tiles_y;
   const size_t lds = T <= TL ? LDS_BYTES : POLICY_BYTES;
   static_assert(POLICY_BYTES <= 4 * (size_t)TL, "the policy arrays fit in the first LDS array");
@@ -459,6 +488,6 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_
   hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, st, reinterpret_cast<const int2 *>(ranges), T,
                      cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, nblocks,
                      reinterpret_cast<char *>(fwd_state),
-                     reinterpret_cast<unsigned long long *>(stats));
+                     reinterpret_cast<unsigned long long *>(stats), status, cap_pairs);
   return hipGetLastError();
 }

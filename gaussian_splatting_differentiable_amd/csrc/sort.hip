@@ -49,6 +49,7 @@ constexpr int HIST_TILES_LDS = 36864;
 constexpr int SCAN_T = 256, SCAN_I = 4, SCAN_TILE = SCAN_T * SCAN_I;
 constexpr uint32_t NO_DEPTH = 0xFFFFFFFFu;  // depth key of a splat without pairs (a NaN pattern)
 constexpr int BIN_T = 512, BIN_BLOCKS_MAX = 1024, BIN_TILE = 2048;
+constexpr uint32_t WS_MAGIC = 0x47534254u;  // a binning pass's state is present
 
 // partitions: depth passes and tile passes
 constexpr int DS_THREADS = 1024, DS_ITEMS = 6, DS_PART = DS_THREADS * DS_ITEMS;
@@ -59,7 +60,13 @@ struct SortCtl {
   int32_t m;               // visible splats (with at least one pair)
   int32_t npairs;          // pairs of this frame (0 after an overflow)
   int32_t err;             // a look-back wait hit its bound (never expected)
-  int32_t overflow;        // the frame's pairs exceed the capacity
+  int32_t overflow;        // the frame's pairs exceed the capacity, or the frame failed
+  // Tag of the binning pass that filled this workspace: gs_sort_keys checks it
+  // against its own arguments and clears it, so a sort without a matching
+  // binning pass of its own is reported instead of reading stale state.
+  uint32_t magic;
+  int32_t tag_n, tag_tiles_x, tag_tiles_y;
+  int64_t tag_cap;
   int32_t tickets[8];      // partition tickets, one per radix pass
   uint32_t dhist[4][256];  // depth digit histograms
   uint32_t dbase[4][256];  // depth digit exclusive offsets
@@ -163,11 +170,21 @@ SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y) {
 // ---------------------------------------------------------------- binning side
 
 __global__ void __launch_bounds__(1024) k_bin_init(SortCtl *__restrict__ ctl,
-                                                   int32_t *__restrict__ tile_diff, int ndiff) {
+                                                   int32_t *__restrict__ tile_diff, int ndiff,
+                                                   int n, int64_t cap, int tiles_x,
+                                                   int tiles_y) {
   int32_t *w = reinterpret_cast<int32_t *>(ctl);
   const int nw = (int)(sizeof(SortCtl) / 4);
   for (int i = threadIdx.x; i < nw; i += blockDim.x) w[i] = 0;
   for (int i = threadIdx.x; i < ndiff; i += blockDim.x) tile_diff[i] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ctl->tag_n = n;
+    ctl->tag_cap = cap;
+    ctl->tag_tiles_x = tiles_x;
+    ctl->tag_tiles_y = tiles_y;
+    ctl->magic = WS_MAGIC;
+  }
 }
 
 // Per-splat pair counts (exact spans) and every block's chunk sum, plus the
@@ -397,6 +414,7 @@ struct PassIn {
   const int32_t *tile_diff;    // SRC_DEPTH0's extra workgroup: tile counts and ranges
   int32_t *tile_counts, *ranges;
   int b0;
+  int32_t *status;             // the frame's device status (bounded waits report here)
 };
 
 template <int NT, int ITEMS, int BITS, int SRC>
@@ -423,7 +441,13 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   bool overflow = false;
   if constexpr (SRC == SRC_DEPTH0) {
     static_assert(SRC != SRC_DEPTH0 || NT == 1024, "the tile-bases workgroup has 1024 threads");
-    overflow = (int64_t)in.offsets[n_max] > in.cap;
+    // a frame sorts nothing when its pairs overflowed, an earlier call failed,
+    // or the workspace does not hold a binning pass of these sizes
+    const SortCtl *c = in.ctl;
+    const bool tag_ok = c->magic == WS_MAGIC && c->tag_n == n_max && c->tag_cap == in.cap &&
+                        c->tag_tiles_x == in.tiles_x && c->tag_tiles_y == in.tiles_y;
+    overflow = !tag_ok || *in.status != GS_OK || (int64_t)in.offsets[n_max] > in.cap;
+    if (!tag_ok && blockIdx.x == 0 && tid == 0) report_status(in.status, GS_ERR_WORKSPACE);
     if (in.ranges && blockIdx.x == gridDim.x - 1) {
       tile_bases_block(const_cast<SortCtl *>(in.ctl), in.tile_diff, in.tile_counts, in.tiles_x,
                        in.tiles_y, in.b0, in.ranges, overflow);
@@ -603,6 +627,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
         if (used < LBW) {  // stopped at an unpublished predecessor
           if (++spins > SPIN_LIMIT) {
             atomicOr(err, 1);
+            report_status(in.status, GS_ERR_TIMEOUT);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
@@ -677,6 +702,7 @@ __global__ void __launch_bounds__(SCAN_T) k_dscan_apply(SortCtl *__restrict__ ct
     if (threadIdx.x == 0) {
       doff[m] = block_base;
       ctl->npairs = ctl->overflow ? 0 : block_base;
+      ctl->magic = 0u;  // every depth pass has read the tag: this binning pass is used up
     }
     return;
   }
@@ -731,7 +757,7 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
                                int32_t *offsets, int32_t *status, void *ws, hipStream_t st) {
   SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
   hipLaunchKernelGGL(k_bin_init, dim3(1), dim3(1024), 0, st, w.ctl, w.tile_diff,
-                     cam.tiles_y * (cam.tiles_x + 1));
+                     cam.tiles_y * (cam.tiles_x + 1), n, cap, cam.tiles_x, cam.tiles_y);
   const int chunk = bin_chunk(n), blocks = bin_blocks(n);
   const int ndiff = cam.tiles_y * (cam.tiles_x + 1);
   size_t lds = ndiff <= HIST_TILES_LDS ? 4 * (size_t)ndiff : 0;
@@ -752,7 +778,7 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
 
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
-                          int32_t *ranges, void *ws, hipStream_t st) {
+                          int32_t *ranges, int32_t *status, void *ws, hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   const int ntiles = cam.tiles_x * cam.tiles_y;
   SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
@@ -767,6 +793,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   const int capi = (int)cap;
   PassIn in{};
   in.ctl = ctl;
+  in.status = status;
 
   // depth sort of the visible splats: 4 passes of 8 bits; the last also writes
   // each splat's pair count in depth order. The first pass has one extra

@@ -13,14 +13,24 @@
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
- *     The library allocates nothing and keeps no global mutable state.
+ *     The library allocates nothing. Its only global mutable state is the
+ *     optional measurement timer (gs_timing_start / gs_timing_read); apart from
+ *     it, calls on different streams with their own buffers are independent.
  *   - `stream` is a hipStream_t (NULL = the default stream). Each call only
  *     enqueues kernels on it and returns; it never synchronises.
  *   - Synchronous errors (argument validation, HIP launch errors) return a
  *     negative gs_status; after an error nothing more is enqueued by that call,
  *     and outputs are undefined only if a launch error occurred mid-call.
+ *   - Asynchronous errors go to the frame's device status word (int32, device
+ *     memory, one per frame): gs_bin_tiles starts it at GS_OK (or
+ *     GS_ERR_CAPACITY); gs_sort_keys, gs_render_fwd and gs_render_bwd take the
+ *     same word, do nothing when it is not GS_OK on entry, and store the first
+ *     error they find (a later error never overwrites an earlier one). The
+ *     caller reads it once, after the frame; a frame whose word is not GS_OK
+ *     has undefined rgb, T_final, last and ranges, and zero gradients.
  *   - All floating-point arithmetic is fp32. Keys, ids, counts and ranges are
- *     integers.
+ *     integers. Splat counts n and pair capacities must be below 2^30
+ *     (GS_ERR_UNSUPPORTED).
  *
  * Data layouts
  *   splat record (GS_SPLAT_FLOATS = 12 floats, 48 B, 16-B aligned):
@@ -55,7 +65,9 @@ typedef enum {
   GS_ERR_CAPACITY = -2,         /* pair buffer too small (reported on the device) */
   GS_ERR_WORKSPACE = -3,        /* workspace or fwd_state smaller than required */
   GS_ERR_HIP = -4,              /* a HIP runtime call or kernel launch failed */
-  GS_ERR_UNSUPPORTED = -5       /* image too large for this build (> 65535 tiles) */
+  GS_ERR_UNSUPPORTED = -5,      /* image too large (> 65535 tiles), n or capacity >= 2^30 */
+  GS_ERR_TIMEOUT = -6           /* a bounded device-side wait gave up (reported on the
+                                   device; never expected): the frame's results are invalid */
 } gs_status;
 
 #define GS_TILE 16
@@ -102,8 +114,12 @@ const char *gs_strerror(int32_t status);
 size_t gs_workspace_size(int32_t n, int32_t width, int32_t height, int64_t pair_capacity);
 
 /* Bytes of the opaque per-frame state that gs_render_fwd writes and
- * gs_render_bwd reads (per-subtile bounds, chunk plan and chunk partials). */
-size_t gs_fwd_state_size(int32_t width, int32_t height);
+ * gs_render_bwd reads: the schedule (LPT order, chunk plan, work queues), the
+ * per-sub-tile walk bounds, the chunk partials, and the contributor record
+ * (Step 4 of the literature page: which list entries blended into which 8x8
+ * quarter of their tile, one bit per entry and quarter), which needs room for
+ * pair_capacity entries. 0 on invalid arguments. */
+size_t gs_fwd_state_size(int32_t width, int32_t height, int64_t pair_capacity);
 
 /* Projection (Eq. 1 of the load-imbalance page) and SH colour.
  *   means [n][3], log_scales [n][3], quats [n][4] (w,x,y,z; need not be unit),
@@ -182,16 +198,25 @@ int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64
  * visible splats (those with offsets[i+1] > offsets[i]) by fp32 depth bits,
  * emission of their tile keys in that order (the same canonical spans as
  * gs_bin_tiles), then a stable radix sort by tile id.
- * Reads the state gs_bin_tiles of the same frame left in `workspace`: call it
- * once after every gs_bin_tiles, with the same workspace, splats, offsets,
- * camera and pair_capacity.
+ * Reads the state gs_bin_tiles of the same frame left in `workspace` (so it
+ * takes no key, id or per-tile count arrays: the pairs are emitted again, in
+ * depth order, inside the first tile pass, and the per-tile counts come from
+ * the binning pass's row histogram; a tile's count is
+ * tile_ranges[t][1] - tile_ranges[t][0]). Call it once after every
+ * gs_bin_tiles, with the same workspace, n, splats, offsets, camera and
+ * pair_capacity: the binning pass tags the workspace with n, the capacity and
+ * the tile grid, and this call uses the tag up; a workspace without a
+ * matching tag sets device_status to GS_ERR_WORKSPACE and sorts nothing.
  *   sorted_ids [pair_capacity] <- splat ids in that order
  *   sorted_keys [pair_capacity] or NULL <- (tile << 32) | float_bits(depth)
  *   tile_ranges [T][2] <- [start, end) of every tile (empty tiles: start = end
- *     = number of pairs of lower tiles). */
+ *     = number of pairs of lower tiles; all zero when the frame failed)
+ *   device_status [1]: the frame's status word (conventions above); a radix
+ *     pass whose bounded look-back wait gives up stores GS_ERR_TIMEOUT. */
 int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
                      const gs_camera *cam, uint64_t *sorted_keys, int32_t *sorted_ids,
-                     int32_t *tile_ranges, void *workspace, size_t workspace_bytes, void *stream);
+                     int32_t *tile_ranges, int32_t *device_status, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* Forward blend (Eq. 2-3): per pixel, front to back over its tile's list;
  * alpha = min(0.99, o exp(-q/2)) on hits (q <= tau); C += alpha T c;
@@ -202,33 +227,44 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
  *   rgb [3][H][W], T_final [H][W] <- colour and final transmittance
  *   last [H][W] <- list entries the pixel consumed (stop index + 1, or the
  *                  tile's full length when it never stopped)
- *   fwd_state <- opaque, gs_fwd_state_size bytes, consumed by gs_render_bwd
+ *   fwd_state <- opaque, gs_fwd_state_size(W, H, capacity) bytes (256-byte
+ *     aligned), consumed by gs_render_bwd; a frame with more pairs than the
+ *     capacity it was sized for sets device_status to GS_ERR_WORKSPACE
  *   stats [4] or NULL <- += {hits: (pixel, splat) pairs blended; lane evaluations:
  *                          64 x (8x8 sub-tile, splat) pairs tested; sub-tile hits:
- *                          (8x8 sub-tile, splat) pairs with at least one hit, which
- *                          is the number of gradient atomics the backward issues;
- *                          chunked tiles h} */
+ *                          (8x8 sub-tile, splat) pairs with at least one hit;
+ *                          chunked tiles h}
+ *   pixel_hits [H][W] or NULL <- += the number of splats each pixel blended
+ *     (for checking; with stats or pixel_hits the forward runs a counting
+ *     instantiation of its kernel, which gives the same images bit for bit)
+ *   device_status [1]: the frame's status word (conventions above); a chunk
+ *     whose bounded wait for the chunks in front of it gives up stores
+ *     GS_ERR_TIMEOUT. Ids in sorted_ids outside [0, n) are skipped. */
 int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const int32_t *tile_ranges, const gs_camera *cam, const gs_sched *sched,
                       float *rgb, float *T_final, int32_t *last, void *fwd_state,
-                      size_t fwd_state_bytes, int64_t *stats, void *workspace,
-                      size_t workspace_bytes, void *stream);
+                      size_t fwd_state_bytes, int64_t *stats, int32_t *pixel_hits,
+                      int32_t *device_status, void *stream);
 
 /* Backward of the forward blend with respect to the 9 screen-space splat
  * parameters (Step 1 (a), (e) of the literature page), given dL/dC per pixel.
- * Each pixel walks its list back from `last`, recovers T by division by
+ * Each pixel walks the list entries the forward pass recorded as contributors
+ * of its quarter (Step 4) back from `last`, recovers T by division by
  * (1 - alpha), keeps the scalar accumulator accum = c_behind . dL/dC, and
  * forms dL/dalpha = T (c . dL/dC - accum). Per-wave sums go to the output
  * with float atomics, so low-order bits depend on the atomic order.
- *   fwd_state: the state gs_render_fwd left for this frame; the backward also
- *     keeps its own work queue in it (so it is not const), and may run again
- *     on the same state.
- *   dL_dsplat [n][9] <- fully overwritten (rows of culled splats are 0). */
+ *   fwd_state: the state gs_render_fwd left for this frame (same size). The
+ *     backward keeps its own work queue in it, so it is not const: a frame's
+ *     state is the forward-to-backward record of that frame, and the backward
+ *     may run again on it.
+ *   dL_dsplat [n][9] <- fully overwritten (rows of culled splats are 0; all
+ *     rows 0 when device_status is not GS_OK on entry).
+ *   device_status [1]: the frame's status word (conventions above). */
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
                       const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
                       const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
-                      const float *dL_drgb, float *dL_dsplat, void *workspace,
-                      size_t workspace_bytes, void *stream);
+                      const float *dL_drgb, float *dL_dsplat, int32_t *device_status,
+                      void *stream);
 
 /* gs_render_fwd and gs_render_bwd with a background colour and a gradient of
  * the final transmittance (not on the pages, which blend onto black; the usual
@@ -246,14 +282,13 @@ int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
                          const int32_t *tile_ranges, const gs_camera *cam,
                          const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
                          void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
-                         void *workspace, size_t workspace_bytes, const float *background,
+                         int32_t *pixel_hits, int32_t *device_status, const float *background,
                          void *stream);
 int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
                          const int32_t *tile_ranges, const gs_camera *cam, const float *T_final,
                          const int32_t *last, void *fwd_state, size_t fwd_state_bytes,
-                         const float *dL_drgb, float *dL_dsplat, void *workspace,
-                         size_t workspace_bytes, const float *background, const float *dL_dT,
-                         void *stream);
+                         const float *dL_drgb, float *dL_dsplat, int32_t *device_status,
+                         const float *background, const float *dL_dT, void *stream);
 
 /* Batches of views: n_views cameras of one size (1 <= n_views <= GS_MAX_VIEWS)
  * rendered as one image, so that binning, sorting and each of the two
@@ -278,7 +313,8 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
  *   background and dL/dT_final arguments of gs_render_fwd_bg/gs_render_bwd_bg). */
 size_t gs_workspace_size_views(int32_t n, int32_t width, int32_t height, int32_t n_views,
                                int64_t pair_capacity);
-size_t gs_fwd_state_size_views(int32_t width, int32_t height, int32_t n_views);
+size_t gs_fwd_state_size_views(int32_t width, int32_t height, int32_t n_views,
+                               int64_t pair_capacity);
 int32_t gs_project_views(int32_t n, const float *means, const float *log_scales,
                          const float *quats, const float *opacities, const float *sh,
                          int32_t sh_degree, const gs_camera *cams, int32_t n_views,
@@ -296,17 +332,20 @@ int32_t gs_bin_tiles_views(int32_t n, const float *splats, const gs_camera *cam,
 int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offsets,
                            int64_t pair_capacity, const gs_camera *cam, int32_t n_views,
                            uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
-                           void *workspace, size_t workspace_bytes, void *stream);
+                           int32_t *device_status, void *workspace, size_t workspace_bytes,
+                           void *stream);
 int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
                             const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
                             const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
                             void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                            int32_t *pixel_hits, int32_t *device_status,
                             const float *background, void *stream);
 int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
                             const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
                             const float *T_final, const int32_t *last, void *fwd_state,
                             size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
-                            const float *background, const float *dL_dT, void *stream);
+                            int32_t *device_status, const float *background,
+                            const float *dL_dT, void *stream);
 
 /* Kernel timing, for measurement only (no paper passage: it lets a benchmark
  * divide algorithmic bytes by the raster kernel's own duration rather than by

@@ -1,12 +1,22 @@
-// Host-side check of the raster kernels' sub-tile cull (cull.h): for every 8x8
-// sub-tile of the image that a splat record could touch, whether some pixel of
-// it passes the canonical hit test, and whether the cull keeps it. Built for the
+// Host-side checks of code the raster kernels share with the host: the sub-tile
+// cull (cull.h) and the forward state's layout (render_common.h). Built for the
 // host only by the CPU tests; it calls the same inline functions the kernels do.
 #include <stdint.h>
 #include <math.h>
 
 #include "cull.h"
+#include "render_common.h"
 
+// Bytes of the forward state for T tiles and a pair capacity, and the pair
+// capacity a state of `bytes` bytes serves (what the forward checks a frame
+// against).
+extern "C" int64_t state_bytes(int T, int64_t cap) { return (int64_t)fwd_layout(T, cap).total; }
+extern "C" int64_t state_capacity(int T, int64_t bytes) {
+  return fwd_state_capacity(T, (size_t)bytes);
+}
+
+// For every sub-tile that a splat record could touch, whether some pixel of it
+// passes the canonical hit test, and whether the cull keeps it.
 // records [n][12] (mx, my, a, b, c, o, r, g, b, tau, depth, view).
 // out[0] += sub-tiles holding a hit that the cull rejects (must stay 0)
 // out[1] += sub-tiles holding a hit; out[2] += sub-tiles kept without a hit.

@@ -1,4 +1,4 @@
-"""The raster kernels' sub-tile cull, run on the CPU.
+"""The raster kernels' sub-tile cull and forward-state layout, run on the CPU.
 
 "What the 3DGS Literature Left on the Table", Step 1 (c): a staged batch of
 splats is culled against each wavefront's part of the tile, and Step 5: the
@@ -27,15 +27,17 @@ def cull():
     hipcc = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
     if not hipcc:
         pytest.skip("hipcc not available")
-    d = tempfile.mkdtemp(prefix="cullchk")
-    so = os.path.join(d, "cull_check.so")
+    d = tempfile.mkdtemp(prefix="hostchk")
+    so = os.path.join(d, "host_checks.so")
     cmd = [hipcc, "-x", "hip", "--offload-host-only", "-O2", "-std=c++17", "-fPIC", "-shared",
            "-I", CSRC, "-I", os.path.join(ROOT, "include"),
-           os.path.join(ROOT, "tests", "native", "cull_check.hip"), "-o", so]
+           os.path.join(ROOT, "tests", "native", "host_checks.hip"), "-o", so]
     subprocess.run(cmd, check=True, capture_output=True)
     L = C.CDLL(so)
     L.cull_check.argtypes = [C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
     L.cull_check.restype = None
+    L.state_bytes.argtypes, L.state_bytes.restype = [C.c_int, C.c_int64], C.c_int64
+    L.state_capacity.argtypes, L.state_capacity.restype = [C.c_int, C.c_int64], C.c_int64
     yield L
     shutil.rmtree(d, ignore_errors=True)
 
@@ -128,3 +130,19 @@ def test_cull_with_the_cutoff_through_a_pixel(cull, case, far):
         assert missed == 0, (case, rep, missed)
         total_hits += with_hit
     assert total_hits > 1000
+
+
+@pytest.mark.parametrize("T", [1, 16, 4346, 8160, 65535])
+def test_forward_state_serves_the_capacity_it_was_sized_for(cull, T):
+    """A forward state of gs_fwd_state_size(W, H, cap) bytes holds the
+    contributor record of any frame of up to cap pairs (the forward refuses a
+    frame with more pairs than the state serves), for capacities that are and
+    are not multiples of the 64-entry batch."""
+    L = cull
+    base = L.state_bytes(T, 0)
+    assert L.state_capacity(T, base - 1) == -1
+    for cap in [0, 1, 63, 64, 65, 4095, 7_913_276, 9_033_723, (1 << 30) - 1]:
+        b = L.state_bytes(T, cap)
+        assert b % 256 == 0 and b >= base
+        got = L.state_capacity(T, b)
+        assert cap <= got < cap + 64 * 9, (T, cap, got)

@@ -5,8 +5,10 @@ rounding difference in one stage cannot change the decisions of the next:
   projection     tolerance (fp32 vs the oracle's fp64)
   binning        offsets, keys, ids bit-exact
   sort, ranges   sorted keys, ids and tile ranges bit-exact
-  forward        rgb and T within 1e-5 (2e-4 on knife-edge pixels), last exact
-                 away from knife edges, hit count within the knife-edge slack
+  forward        rgb and T within 1e-5 (2e-4 on knife-edge pixels); last and the
+                 number of splats each pixel blended exact away from knife
+                 edges; the contributor record (which entries blended into
+                 which quarter of their tile) exact away from knife edges
   backward       relative L2 per gradient column <= 1e-3 against the fp64 truth
 The end-to-end chain (GPU projection onward) is checked loosely.
 """
@@ -83,14 +85,18 @@ def run_stages(gsr, sc, ref, capacity=None, sched=None, background=None, dL_dT=N
     out = dict(I=I, offsets=host(r.offsets), keys=host(r.keys)[:I].view(np.uint64),
                ids=host(r.ids)[:I], sorted_keys=host(r.sorted_keys)[:I].view(np.uint64),
                sorted_ids=host(r.sorted_ids)[:I], ranges=host(r.ranges))
-    # forward/backward on the oracle's sorted list (stage isolation)
+    # forward/backward on the oracle's sorted list (stage isolation); the state is
+    # cleared so that contributor words the forward does not write read as zero
     r.sorted_ids[:npairs].copy_(dev(ref["sorted_ids"]))
     r.ranges.copy_(dev(ref["ranges"]))
+    r.fwd_state.zero_()
     r.render_fwd(n, stats=True, background=background)
+    out["contrib"] = read_contrib(r, ref["ranges"])
     grads = r.render_bwd(n, dev(sc.dL_drgb), background=background,
                          dL_dT=None if dL_dT is None else dev(dL_dT))
+    r.check("stage parity frame")
     out.update(rgb=host(r.rgb), T=host(r.T), last=host(r.last), grads=host(grads),
-               stats=host(r.stats), plan=read_plan(r))
+               stats=host(r.stats), pixel_hits=host(r.pixel_hits), plan=read_plan(r))
     return out
 
 
@@ -116,8 +122,33 @@ def check_forward(ref, out):
     assert d_T[~knife].max(initial=0) <= FWD_TOL, d_T[~knife].max()
     assert d_rgb[knife].max(initial=0) <= KNIFE_TOL and d_T[knife].max(initial=0) <= KNIFE_TOL
     assert np.array_equal(out["last"][~knife], f["last"][~knife])
-    slack = int(knife.sum()) * 8 + 16
-    assert abs(int(out["stats"][0]) - f["hits"]) <= slack, (out["stats"][0], f["hits"])
+    # every pixel blended exactly the oracle's splats (a dropped or extra hit of
+    # any depth shows here, however small its colour)
+    ph = out["pixel_hits"]
+    bad = (ph != f["pixel_hits"]) & ~knife
+    assert not bad.any(), (np.argwhere(bad)[:5], int(bad.sum()))
+    assert int(out["stats"][0]) == int(ph.sum())
+    if "contrib" in out:
+        check_contrib(ref, out["contrib"])
+
+
+def check_contrib(ref, contrib):
+    """The forward's contributor record equals the oracle's per-quarter hits of
+    every list entry, except in quarters that hold a knife-edge pixel."""
+    f = ref["fwd"]
+    H, W = f["T"].shape
+    tx = (W + 15) // 16
+    ranges = ref["ranges"]
+    knife_q = np.zeros(len(ranges) * 4, bool)
+    ky, kx = np.nonzero(f["knife"])
+    knife_q[((ky // 16) * tx + kx // 16) * 4 + ((kx % 16) // 8) + 2 * ((ky % 16) // 8)] = True
+    tile_of = np.repeat(np.arange(len(ranges)), ranges[:, 1] - ranges[:, 0])
+    pq = f["pair_quarters"]
+    for q in range(4):
+        exp = (pq >> q) & 1
+        got = contrib[q]
+        ok = knife_q[tile_of * 4 + q] | (exp == got)
+        assert ok.all(), (q, np.nonzero(~ok)[0][:5], int((~ok).sum()))
 
 
 def check_backward(ref, out):
@@ -193,13 +224,19 @@ def test_capacity_overflow_reports_and_recovers():
     r = gsr.Rasterizer(sc.camera, capacity=16)
     r._ensure(sc.n, 16)
     r.splats[:sc.n].copy_(dev(ref["splats"]))
+    r.ranges.fill_(-7)
+    r.rgb.fill_(5.0)
     gsr.gs_bin_tiles(sc.n, r.splats, r.cam, 16, r.offsets, r.keys, r.ids, r.status, r.workspace)
     gsr.gs_sort_keys(sc.n, r.splats, r.offsets, 16, r.cam, None, r.sorted_ids, r.ranges,
-                     r.workspace)
-    assert int(host(r.status)[0]) == gsr.GS_ERR_CAPACITY
-    assert int(host(r.offsets)[sc.n]) == npairs
+                     r.status, r.workspace)
+    r.render_fwd(sc.n)
+    g = r.render_bwd(sc.n, dev(sc.dL_drgb))
+    st, I = r.frame_status(sc.n)                  # read once, after the frame
+    assert st == gsr.GS_ERR_CAPACITY and I == npairs
     assert np.all(host(r.ranges) == 0)          # later calls do nothing for the frame
-    I = r.bin_and_sort(sc.n)                      # the driver grows and re-runs
+    assert np.all(host(r.rgb) == 5.0)           # the forward did not run
+    assert np.all(host(g) == 0)                 # the backward only zeroed its output
+    I = r.run_frame(sc.n, dev(sc.dL_drgb))        # the driver grows and re-runs
     assert I == npairs and r.capacity >= npairs
     assert np.array_equal(host(r.sorted_ids)[:I], ref["sorted_ids"])
 
@@ -249,8 +286,77 @@ def test_full_size_configs(cfg):
     check_sort(ref, out)
     check_forward(ref, out)
     check_backward(ref, out)
-    print(f"config {cfg}: pairs {out['I']}, hits {int(out['stats'][0])}, "
-          f"knife-edge pixels {int(ref['fwd']['knife'].sum())}", flush=True)
+    if cfg == 5:
+        assert int(out["stats"][3]) >= 1   # the policy chunks urban's heaviest tiles
+    print(f"config {cfg}: pairs {out['I']}, hits {int(out['stats'][0])}, chunked tiles "
+          f"{int(out['stats'][3])}, knife-edge pixels {int(ref['fwd']['knife'].sum())}",
+          flush=True)
+
+
+def test_frame_of_more_than_8192_tiles():
+    """A 1600x1400 frame with a ragged last row and column (8800 tiles): the
+    schedule keeps its working arrays in the forward state instead of LDS, and
+    every stage still matches the oracle."""
+    gsr = _gsr()
+    sc = scenegen.random_scene(105, 120_000, 1601, 1399, 1400.0, degree=1,
+                               log_scale=(-3.0, 0.6), opacity=(0.5, 1.5))
+    assert sc.camera.num_tiles > 8192
+    ref = oracle.frame(sc)
+    out = run_stages(gsr, sc, ref)
+    check_binning(ref, out)
+    check_sort(ref, out)
+    check_forward(ref, out)
+    check_backward(ref, out)
+    check_queues(out["plan"], (sc.camera.width + 15) // 16)
+
+
+def test_sort_rejects_a_workspace_without_its_binning_pass():
+    """The binning pass tags the workspace with its sizes and the sort uses the
+    tag up: a second sort of the same frame, or a sort whose sizes differ from
+    the binning pass's, reports GS_ERR_WORKSPACE through the status word and
+    leaves empty ranges."""
+    gsr = _gsr()
+    sc, ref = reference(1)
+    n, npairs = sc.n, len(ref["sorted_ids"])
+    r = gsr.Rasterizer(sc.camera, capacity=npairs + 64)
+    r._ensure(n, npairs + 64)
+    r.splats[:n].copy_(dev(ref["splats"]))
+    assert r.bin_and_sort(n) == npairs
+    gsr.gs_sort_keys(n, r.splats, r.offsets, r.capacity, r.cam, None, r.sorted_ids, r.ranges,
+                     r.status, r.workspace)
+    assert r.frame_status(n)[0] == gsr.GS_ERR_WORKSPACE
+    assert np.all(host(r.ranges) == 0)
+    # sizes that differ from the binning pass's: n - 1 splats
+    gsr.gs_bin_tiles(n, r.splats, r.cam, r.capacity, r.offsets, None, None, r.status, r.workspace)
+    gsr.gs_sort_keys(n - 1, r.splats, r.offsets, r.capacity, r.cam, None, r.sorted_ids, r.ranges,
+                     r.status, r.workspace)
+    assert r.frame_status(n)[0] == gsr.GS_ERR_WORKSPACE
+    # an error is never overwritten by the later calls of the frame
+    r.render_fwd(n)
+    r.render_bwd(n, dev(sc.dL_drgb))
+    assert r.frame_status(n)[0] == gsr.GS_ERR_WORKSPACE
+    # and the next frame starts clean
+    assert r.run_frame(n, dev(sc.dL_drgb)) == npairs
+
+
+def test_state_too_small_for_the_frame_is_reported():
+    """A forward state sized for fewer pairs than the frame holds: the schedule
+    reports GS_ERR_WORKSPACE and neither raster kernel runs."""
+    gsr = _gsr()
+    sc, ref = reference(1)
+    n, npairs = sc.n, len(ref["sorted_ids"])
+    r = gsr.Rasterizer(sc.camera, capacity=npairs)
+    r._ensure(n, npairs)
+    r.splats[:n].copy_(dev(ref["splats"]))
+    assert r.bin_and_sort(n) == npairs
+    small = torch.empty(gsr.fwd_state_size(sc.camera.width, sc.camera.height, 0),
+                        dtype=torch.uint8, device="cuda")
+    r.fwd_state = small
+    r.rgb.fill_(3.0)
+    r.render_fwd(n)
+    g = r.render_bwd(n, dev(sc.dL_drgb))
+    assert r.frame_status(n)[0] == gsr.GS_ERR_WORKSPACE
+    assert np.all(host(r.rgb) == 3.0) and np.all(host(g) == 0)
 
 
 # ---------------------------------------------------------------- scheduling and chunking
@@ -258,30 +364,58 @@ def test_full_size_configs(cfg):
 def _plan_layout(T):
     """Offsets into the opaque forward state, read here for checking only:
     header (h, k, nA, nplain, err, ntiles, group offsets, pass-A counts, static
-    hand-out counts), queue heads, per-quarter bounds, LPT order, sorted counts,
-    the queue items."""
+    hand-out counts, ...), queue heads, per-quarter bounds, LPT order, sorted
+    counts, the queue items, ..., the contributor words (last)."""
     rnd = lambda b: (b + 255) // 256 * 256
+    cq = 4096 * 4
     hdr = 0
-    heads = rnd(4 * 39)
+    heads = rnd(208)
     sub_last = heads + rnd(4 * 2 * 8 * 16)
     order = sub_last + rnd(16 * T)
     counts = order + rnd(4 * T)
     items = counts + rnd(4 * T)
-    return dict(hdr=hdr, heads=heads, order=order, counts=counts, items=items)
+    off = items + rnd(4 * (4 * T + 2 * cq))
+    for b in (4 * 2048 * 4, 4 * cq, 4 * 2048 * 4, 4 * cq, 4 * cq * 64, 4 * cq * 64 * 3,
+              4 * cq * 64, 4 * cq * 64, 4 * cq * 64, 4 * (4 * T + 2 * cq)):
+        off += rnd(b)
+    return dict(hdr=hdr, heads=heads, order=order, counts=counts, items=items, contrib=off)
+
+
+def read_contrib(r, ranges):
+    """The forward's contributor record as one 0/1 array per quarter over the
+    list positions: quarter q's word for tile t and batch m is word
+    (start_t >> 6) + t + m of array q (nw words each, from the header)."""
+    T = r.tiles
+    L = _plan_layout(T)
+    raw = host(r.fwd_state)
+    nw = int(raw[200:208].view(np.int64)[0])
+    assert nw >= r.capacity // 64 + T + 2
+    words = raw[L["contrib"]:L["contrib"] + 8 * 4 * nw].view(np.uint64).reshape(4, nw)
+    npairs = int(ranges[-1, 1]) if len(ranges) else 0
+    out = np.zeros((4, npairs), np.uint8)
+    for t in range(T):
+        s, e = int(ranges[t, 0]), int(ranges[t, 1])
+        if e == s:
+            continue
+        k = np.arange(e - s)
+        w = words[:, (s >> 6) + t + (k >> 6)]
+        out[:, s:e] = ((w >> (k & 63).astype(np.uint64)) & np.uint64(1)).astype(np.uint8)
+    return out
 
 
 def read_plan(r):
     T = r.tiles
     L = _plan_layout(T)
     raw = host(r.fwd_state)
-    hdr = raw[L["hdr"]:L["hdr"] + 156].view(np.int32)
+    hdr = raw[L["hdr"]:L["hdr"] + 208].view(np.int32)
     order = raw[L["order"]:L["order"] + 4 * T].view(np.int32)
     counts = raw[L["counts"]:L["counts"] + 4 * T].view(np.int32)
     qoff = hdr[6:15].copy()
     items = raw[L["items"]:L["items"] + 4 * int(qoff[-1])].view(np.int32)
     assert int(hdr[5]) == T
     return dict(h=int(hdr[0]), k=int(hdr[1]), nA=int(hdr[2]), err=int(hdr[4]), order=order,
-                counts=counts, qoff=qoff, qa=hdr[15:23].copy(), items=items.copy())
+                counts=counts, qoff=qoff, qa=hdr[15:23].copy(), items=items.copy(),
+                run_f=int(hdr[47]))
 
 
 def check_queues(plan, tiles_x):
@@ -373,7 +507,7 @@ def _policy_frame(gsr, counts, W, H):
 @pytest.mark.parametrize("W,H", [(1920, 1080), (3840, 2160)])  # 8160 tiles (LDS path), 32400
 def test_device_policy_equals_host_policy(case, W, H):
     gsr = _gsr()
-    rng = np.random.default_rng(abs(hash(case)) % 1000)
+    rng = np.random.default_rng({"pareto": 1, "one_outlier": 2, "flat": 3, "two_level": 4}[case])
     T = ((W + 15) // 16) * ((H + 15) // 16)
     if case == "pareto":
         counts = (rng.pareto(1.2, T) * 300).astype(np.int64)
@@ -386,7 +520,7 @@ def test_device_policy_equals_host_policy(case, W, H):
         counts = np.where(rng.random(T) < 0.02, 40_000, 900)
     counts = np.minimum(counts, 2_000_000).astype(np.int32)
     plan = _policy_frame(gsr, counts, W, H)
-    assert plan["err"] == 0
+    assert plan["err"] == 0 and plan["run_f"] == 1
     # exact LPT order: count descending, ties by tile id
     ref_order = np.lexsort((np.arange(T), -counts.astype(np.int64)))
     assert np.array_equal(plan["order"], ref_order)
@@ -424,7 +558,8 @@ def test_forward_without_stats_is_identical():
         b = [host(t) for t in (r.rgb, r.T, r.last)]
         for x, y in zip(a, b):
             assert np.array_equal(x, y)
-        check_forward(ref, dict(rgb=b[0], T=b[1], last=b[2], stats=host(r.stats)))
+        check_forward(ref, dict(rgb=b[0], T=b[1], last=b[2], stats=host(r.stats),
+                                pixel_hits=host(r.pixel_hits)))
 
 
 def test_kernel_timing_entry_points():

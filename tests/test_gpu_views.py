@@ -62,8 +62,9 @@ def _run(gsr, sc, cams, ref, dL, sched=None, background=None, dT=None):
     dL_all = dev(np.concatenate(dL, axis=1))
     dT_all = None if dT is None else dev(np.concatenate(dT))
     grads = r.render_bwd(n_rec, dL_all, background=background, dL_dT=dT_all)
+    r.check("views frame")
     out.update(rgb=host(r.rgb), T=host(r.T), last=host(r.last), grads=host(grads),
-               stats=host(r.stats))
+               stats=host(r.stats), pixel_hits=host(r.pixel_hits))
     return out
 
 
@@ -123,9 +124,10 @@ def test_one_view_batch_equals_plain_calls():
             gsr.gs_bin_tiles_views(n, r.splats, r.cam, 1, r.capacity, r.offsets, None, None,
                                    r.status, r.workspace)
             gsr.gs_sort_keys_views(n, r.splats, r.offsets, r.capacity, r.cam, 1, None,
-                                   r.sorted_ids, r.ranges, r.workspace)
+                                   r.sorted_ids, r.ranges, r.status, r.workspace)
             gsr.gs_render_fwd_views(n, r.splats, r.sorted_ids, r.ranges, r.cam, 1, r.sched,
-                                    r.rgb, r.T, r.last, r.fwd_state, None)
+                                    r.rgb, r.T, r.last, r.fwd_state, None, None, r.status)
+            r.check("one-view batch")
         else:
             r.bin_and_sort(n)
             r.render_fwd(n)
@@ -184,6 +186,7 @@ def test_views_reject_bad_batches():
     d = [dev(a) for a in (sc.means, sc.log_scales, sc.quats, sc.opacities, sc.sh)]
     with pytest.raises(gsr.GsError):
         r.project_views([cams[0], other], *d, sc.sh_degree)
-    assert gsr.fwd_state_size_views(64, 64, 0) == 0
-    assert gsr.fwd_state_size_views(64, 64, 17) == 0
+    assert gsr.fwd_state_size_views(64, 64, 0, 100) == 0
+    assert gsr.fwd_state_size_views(64, 64, 17, 100) == 0
+    assert gsr.fwd_state_size_views(64, 64, 2, -1) == 0
     assert gsr.workspace_size_views(10, 64, 64, 17, 100) == 0

@@ -37,11 +37,15 @@ def test_every_declared_symbol_is_exported(gsr):
 def test_strerror_and_sizes(gsr):
     assert gsr.strerror(0) == "ok"
     assert "capacity" in gsr.strerror(gsr.GS_ERR_CAPACITY)
+    assert "wait" in gsr.strerror(gsr.GS_ERR_TIMEOUT)
     ws = gsr.workspace_size(1_535_033, 1297, 840, 8_000_000)
     assert ws > 8_000_000 * 16
     assert gsr.workspace_size(-1, 10, 10, 0) == 0
-    assert gsr.fwd_state_size(1297, 840) >= 4346 * 4 * 4
-    assert gsr.fwd_state_size(0, 10) == 0
+    # the forward state grows by the contributor record: 4 bits per pair
+    a, b = gsr.fwd_state_size(1297, 840, 0), gsr.fwd_state_size(1297, 840, 8_000_000)
+    assert a >= 4346 * 4 * 4 and 8_000_000 // 2 <= b - a <= 8_000_000 // 2 + 32 * 4346 + 512
+    assert gsr.fwd_state_size(0, 10, 100) == 0
+    assert gsr.fwd_state_size(10, 10, -1) == 0 and gsr.fwd_state_size(10, 10, 1 << 30) == 0
 
 
 def test_argument_validation_needs_no_gpu(gsr):
@@ -80,20 +84,44 @@ def test_argument_validation_needs_no_gpu(gsr):
     nanbg = (C.c_float * 3)(float("nan"), 0.0, 0.0)
     st256 = C.c_void_p(256)
     assert L.gs_render_fwd_bg(1, p16, p16, p16, C.byref(cam), None, p16, p16, p16, st256, 1 << 30,
-                              None, None, 0, nanbg, None) == -1
+                              None, None, p16, nanbg, None) == -1
     assert L.gs_render_bwd_bg(1, p16, p16, p16, C.byref(cam), p16, p16, st256, 1 << 30, p16, p16,
-                              None, 0, nanbg, None, None) == -1
+                              p16, nanbg, None, None) == -1
     assert L.gs_render_bwd_bg(1, p16, p16, p16, C.byref(cam), p16, p16, st256, 1 << 30, p16, p16,
-                              None, 0, None, C.c_void_p(18), None) == -1
+                              p16, None, C.c_void_p(18), None) == -1
+    # the frame's device status word is required by the sort and the raster calls
+    assert L.gs_render_fwd(1, p16, p16, p16, C.byref(cam), None, p16, p16, p16, st256, 1 << 30,
+                           None, None, None, None) == -1
+    assert L.gs_render_bwd(1, p16, p16, p16, C.byref(cam), p16, p16, st256, 1 << 30, p16, p16,
+                           None, None) == -1
+    assert L.gs_sort_keys(10, p16, p16, 100, C.byref(cam), None, p16, p16, None, p16, 1 << 30,
+                          None) == -1
+    # a forward state too small for even an empty contributor record
+    small = L.gs_fwd_state_size(64, 64, 0) - 256
+    assert L.gs_render_fwd(1, p16, p16, p16, C.byref(cam), None, p16, p16, p16, st256, small,
+                           None, None, p16, None) == -3
+    assert L.gs_render_bwd(1, p16, p16, p16, C.byref(cam), p16, p16, st256, small, p16, p16,
+                           p16, None) == -3
+    # counts from 2^30 up: the radix passes' look-back words hold 30-bit counts
+    big_ws = C.c_size_t(1 << 62)
+    assert L.gs_bin_tiles(1 << 30, p16, C.byref(cam), 100, p16, None, None, p16, p16, big_ws,
+                          None) == -5
+    assert L.gs_bin_tiles(10, p16, C.byref(cam), 1 << 30, p16, None, None, p16, p16, big_ws,
+                          None) == -5
+    assert L.gs_sort_keys(10, p16, p16, 1 << 30, C.byref(cam), None, p16, p16, p16, p16, big_ws,
+                          None) == -5
+    assert L.gs_render_fwd(1 << 30, p16, p16, p16, C.byref(cam), None, p16, p16, p16, st256,
+                           1 << 40, None, None, p16, None) == -5
     # batches of views: sizes are those of the stacked image; bad batches are rejected
-    assert L.gs_fwd_state_size_views(64, 45, 3) == L.gs_fwd_state_size(64, 3 * 48)
+    assert L.gs_fwd_state_size_views(64, 45, 3, 500) == L.gs_fwd_state_size(64, 3 * 48, 500)
     assert L.gs_workspace_size_views(1000, 83, 45, 4, 5000) == L.gs_workspace_size(1000, 83, 4 * 48,
                                                                                     5000)
-    assert L.gs_fwd_state_size_views(64, 64, 0) == 0 and L.gs_fwd_state_size_views(64, 64, 17) == 0
+    assert L.gs_fwd_state_size_views(64, 64, 0, 8) == 0
+    assert L.gs_fwd_state_size_views(64, 64, 17, 8) == 0
     assert L.gs_bin_tiles_views(1, p16, C.byref(cam), 0, 10, p16, None, None, p16, p16, 1 << 30,
                                 None) == -1
     assert L.gs_render_fwd_views(1, p16, p16, p16, C.byref(cam), 17, None, p16, p16, p16, st256,
-                                 1 << 30, None, None, None) == -1
+                                 1 << 30, None, None, p16, None, None) == -1
     assert L.gs_project_views(1, p16, p16, p16, p16, p16, 0, None, 2, p16, None) == -1
     cams2 = (gsr.GsCamera * 2)(cam, cam)
     cams2[1].width = 80                                   # views of different sizes
