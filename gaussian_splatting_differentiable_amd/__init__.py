@@ -28,8 +28,10 @@ EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project"
            "gs_project_bf16sh", "gs_project_bwd_bf16sh", "gs_bin_tiles",
            "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_workspace_size_views",
            "gs_fwd_state_size_views", "gs_project_views", "gs_project_bwd_views",
-           "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_timing_start",
-           "gs_timing_read")
+           "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views",
+           "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
+           "gs_sort_keys_noalloc", "gs_timing_start", "gs_timing_read")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GsError(RuntimeError):
@@ -88,13 +90,14 @@ def lib():
     L.gs_render_fwd_views.argtypes = [i32, P, P, P, cam_p, i32, C.POINTER(GsSched), P, P, P, P,
                                       sz, P, P, P, P, P]
     L.gs_render_bwd_views.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P, P]
+    L.gs_sort_keys_noalloc.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, P]
     L.gs_timing_start.argtypes = []
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
     for name in ("gs_project", "gs_project_bwd", "gs_project_bf16sh", "gs_project_bwd_bf16sh",
                  "gs_bin_tiles", "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_project_views",
                  "gs_project_bwd_views", "gs_bin_tiles_views", "gs_sort_keys_views",
                  "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
-                 "gs_render_bwd", "gs_timing_start", "gs_timing_read"):
+                 "gs_render_bwd", "gs_sort_keys_noalloc", "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -307,6 +310,14 @@ def gs_render_bwd(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_state, 
                                fwd_state.numel() * fwd_state.element_size(), _ptr(dL_drgb),
                                _ptr(dL_dsplat), _ptr(status), _stream(stream)),
            "gs_render_bwd")
+
+
+def gs_sort_keys_noalloc(n, splats, cam, capacity, offsets, sorted_keys, sorted_ids, ranges,
+                         status, stream=None):
+    _check(lib().gs_sort_keys_noalloc(int(n), _ptr(splats), C.byref(cam), int(capacity),
+                                      _ptr(offsets), _ptr(sorted_keys), _ptr(sorted_ids),
+                                      _ptr(ranges), _ptr(status), _stream(stream)),
+           "gs_sort_keys_noalloc")
 
 
 def _bg3(background):

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "render_common.h"
 
 hipError_t gs_launch_project(int n, const float *means, const float *log_scales, const float *quats,
@@ -530,6 +532,67 @@ int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorte
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
                   fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free sort
+
+}  // extern "C"
+
+// The allocation-free sort's workspace: one array per GPU, held until the
+// process ends. Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not device memory): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[GS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_DEVICES] = {};
+
+// The current device's scratch address (nullptr on a HIP error).
+void *scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gs_sort_keys_noalloc(int32_t n, const float *splats, const gs_camera *cam,
+                             int64_t pair_capacity, int32_t *offsets, uint64_t *sorted_keys,
+                             int32_t *sorted_ids, int32_t *tile_ranges, int32_t *device_status,
+                             void *stream) {
+  CamK k;
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (n < 0 || pair_capacity < 0) return GS_ERR_INVALID_ARGUMENT;
+  if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT || pair_capacity >= GS_COUNT_LIMIT)
+    return GS_ERR_UNSUPPORTED;
+  if (!offsets || !tile_ranges || !device_status || (n > 0 && !splats) ||
+      (pair_capacity > 0 && !sorted_ids))
+    return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (sorted_keys && !aligned(sorted_keys, 8)) ||
+      !aligned(tile_ranges, 8))
+    return GS_ERR_INVALID_ARGUMENT;
+  // the frame must fit the static workspace: checked before any HIP call
+  if (gs_sort_ws_bytes(n, pair_capacity, k.tiles_x, k.tiles_y) > GS_NOALLOC_SCRATCH_BYTES)
+    return GS_ERR_WORKSPACE;
+  void *ws = scratch_on_current_device();
+  if (!ws) return GS_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = gs_launch_bin(n, splats, k, pair_capacity, offsets, nullptr, nullptr,
+                               device_status, ws, st);
+  if (e != hipSuccess) return GS_ERR_HIP;
+  return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
+                                   tile_ranges, device_status, ws, st));
 }
 
 int32_t gs_timing_start(void) {

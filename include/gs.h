@@ -347,6 +347,28 @@ int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorte
                             int32_t *device_status, const float *background,
                             const float *dL_dT, void *stream);
 
+/* Allocation-free sort, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): gs_bin_tiles (without the id-order keys and ids) followed by
+ * gs_sort_keys, with both calls' workspace taken from the library's own static
+ * device array of GS_NOALLOC_SCRATCH_BYTES per GPU instead of a caller's
+ * buffer. The array belongs to the library, lives on every GPU the library
+ * runs on until the process ends, and is shared by every call on that GPU: it
+ * keeps the last call's contents, so calls that overlap on one GPU (on two
+ * streams, or from two threads) race and must not be issued. The first call on
+ * a device looks up that device's array address (hipGetSymbolAddress) with the
+ * device current; no call allocates.
+ *   Arguments and outputs: as for gs_bin_tiles and gs_sort_keys (offsets,
+ *   device_status, sorted_keys or NULL, sorted_ids, tile_ranges).
+ *   Limit: a frame whose workspace (gs_workspace_size(n, W, H, pair_capacity))
+ *   exceeds GS_NOALLOC_SCRATCH_BYTES returns GS_ERR_WORKSPACE before any HIP
+ *   call (about 1M Gaussians with a capacity of 2M pairs fit). */
+#define GS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t gs_sort_keys_noalloc(int32_t n, const float *splats, const gs_camera *cam,
+                             int64_t pair_capacity, int32_t *offsets, uint64_t *sorted_keys,
+                             int32_t *sorted_ids, int32_t *tile_ranges, int32_t *device_status,
+                             void *stream);
+
 /* Kernel timing, for measurement only (no paper passage: it lets a benchmark
  * divide algorithmic bytes by the raster kernel's own duration rather than by
  * the whole call's, which also zeroes the gradients and orders the backward's
