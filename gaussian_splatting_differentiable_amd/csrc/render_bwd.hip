@@ -154,6 +154,47 @@ __device__ __forceinline__ uint64_t word_of(uint32_t lo, uint32_t hi, int m) {
          (uint32_t)__builtin_amdgcn_readlane((int)lo, m);
 }
 
+// A staged entry (64 bytes): the record with 2b, log2(o) and 1/o in place of
+// depth, pad and o, and the splat id. Slot 64 of a wave's stage is a dead
+// entry (tau = -1, never hit) that a half with no entry left reads.
+struct __align__(16) Staged {
+  float4 p0;  // mx, my, a, b
+  float4 p1;  // c, 1/o, r, g
+  float4 p2;  // b (colour), tau, 2b, log2(o)
+  int4 p3;    // id, live (1) or dead (0), -, -
+};
+constexpr int SLOTS = BATCH + 1;
+
+__device__ __forceinline__ int top_bit(uint64_t w) { return w ? 63 - __builtin_clzll(w) : BATCH; }
+__device__ __forceinline__ bool has_bit(uint64_t w, int j) { return j < BATCH && ((w >> j) & 1ull); }
+
+// The next step of a batch's walk: the entries the upper and lower quarter take
+// (BATCH, the dead slot, for none), removed from their words. Each quarter
+// takes its own entries back to front. An entry both quarters blended is taken
+// by both in the same step (shared: the halves' sums are added and written
+// once); otherwise the higher entry goes to its quarter, and the other quarter
+// takes its own next entry in the same step unless that entry is still to come
+// for the first quarter too (then it waits, so that the two meet on it).
+struct Pair {
+  int jt, jb;
+  bool shared;
+};
+__device__ __forceinline__ Pair next_pair(uint64_t &wt, uint64_t &wb) {
+  Pair p;
+  const int ht = top_bit(wt), hb = top_bit(wb);
+  p.shared = ht == hb && ht < BATCH;
+  if (p.shared || ht > hb) {
+    p.jt = ht;
+    p.jb = p.shared ? hb : (has_bit(wt, hb) ? BATCH : hb);
+  } else {
+    p.jb = hb;
+    p.jt = has_bit(wb, ht) ? BATCH : ht;
+  }
+  if (p.jt < BATCH) wt &= ~(1ull << p.jt);
+  if (p.jb < BATCH) wb &= ~(1ull << p.jb);
+  return p;
+}
+
 // Per-lane state of the two pixels of a lane (rows 0 and 1 of its pair).
 struct Pix2 {
   float fx, fy0, fy1;        // sample positions
@@ -165,57 +206,68 @@ struct Pix2 {
 // Walk the item's batches back to front. cw_top / cw_bot: the contributor words
 // of the two quarters at the walk's first batch; nb_top / nb_bot: how many of
 // them are current (the rest were not written for this frame); list: the walk's
-// first list position. Each staged record carries 1/o, 2b and log2(o) in place
-// of o, depth and pad, so the per-entry work has no reciprocal of o, no doubling
-// and no logarithm.
+// first list position. Lanes 0-31 (the upper quarter) and 32-63 (the lower
+// one) take the entries of their own quarter's word, back to front (next_pair):
+// a step evaluates one splat for both halves or two different splats, one per
+// half, and a half with no entry in the step reads the dead slot.
 __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int n,
                                           const int32_t *__restrict__ sids, int64_t list,
                                           const uint64_t *__restrict__ cw_top, int nb_top,
                                           const uint64_t *__restrict__ cw_bot, int nb_bot,
-                                          Pix2 &x, Splat *sbuf, int *sid,
-                                          float *__restrict__ grads) {
+                                          Pix2 &x, Staged *stage, float *__restrict__ grads) {
   const int lane = __lane_id();
-  const int comp = comp_of_lane(lane);
+  const bool top = lane < 32;
+  const int comp = comp_of_half_lane(lane);
   // the constant factor each owner lane applies to its sum after the reduction
   // (powers of two: exact): -1/2 for the two squared offsets
   const float post = (comp == 2 || comp == 4) ? -0.5f : 1.0f;
+  float zero = 0.0f;
+  __asm__ volatile("" : "+v"(zero));  // a register, not a constant, for the unpaired swap
   const float4 *rec4 = reinterpret_cast<const float4 *>(splats);
+  // the next batch's record of this lane, as three registers of four (kept out
+  // of any aggregate: the compiler parks part of one in memory otherwise)
+  float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0, q2 = q0;
   const int nbat = max(nb_top, nb_bot);
   for (int r0 = (nbat - 1) & ~63; r0 >= 0; r0 -= 64) {
-    // lane i holds the word of batch r0 + i (both quarters' contributors)
+    // lane i holds the words of batch r0 + i, one per quarter
     const int m = r0 + lane;
-    uint64_t wv = 0;
-    if (m < nb_top) wv |= cw_top[m];
-    if (m < nb_bot) wv |= cw_bot[m];
-    const uint32_t wlo = (uint32_t)wv, whi = (uint32_t)(wv >> 32);
-    uint64_t todo = wave_ballot(wv != 0);
+    const uint64_t wtv = m < nb_top ? cw_top[m] : 0ull;
+    const uint64_t wbv = m < nb_bot ? cw_bot[m] : 0ull;
+    const uint32_t tlo = (uint32_t)wtv, thi = (uint32_t)(wtv >> 32);
+    const uint32_t blo = (uint32_t)wbv, bhi = (uint32_t)(wbv >> 32);
+    uint64_t todo = wave_ballot((wtv | wbv) != 0);
     if (!todo) continue;
     // pipeline: the records of the batch being staged and the ids of the next
     // non-empty batch are in flight while a batch is walked
     int mc = 63 - __builtin_clzll(todo);
     todo &= ~(1ull << mc);
-    uint64_t wc = word_of(wlo, whi, mc);
-    int idc = load_marked_id(sids, list + 64 * (int64_t)(r0 + mc), wc);
-    const int64_t ri = 3 * (int64_t)(valid_id(idc, n) ? idc : 0);
-    float4 q0 = rec4[ri], q1 = rec4[ri + 1], q2 = rec4[ri + 2];
+    uint64_t wt = word_of(tlo, thi, mc), wb = word_of(blo, bhi, mc);
+    int idc = load_marked_id(sids, list + 64 * (int64_t)(r0 + mc), wt | wb);
+    {
+      const int64_t ri = 3 * (int64_t)(valid_id(idc, n) ? idc : 0);
+      q0 = rec4[ri];
+      q1 = rec4[ri + 1];
+      q2 = rec4[ri + 2];
+    }
     int mn = -1, idn = -1;
-    uint64_t wn = 0;
+    uint64_t wtn = 0, wbn = 0;
     if (todo) {
       mn = 63 - __builtin_clzll(todo);
       todo &= ~(1ull << mn);
-      wn = word_of(wlo, whi, mn);
-      idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mn), wn);
+      wtn = word_of(tlo, thi, mn);
+      wbn = word_of(blo, bhi, mn);
+      idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mn), wtn | wbn);
     }
     for (;;) {
-      Splat s;
-      s.p0 = q0;
-      s.p1 = q1;
-      s.p2 = q2;
-      s.p2.w = __log2f(s.p1.y);  // the forward pass folds log2(o) the same way
-      s.p2.z = 2.0f * s.p0.w;
-      s.p1.y = __builtin_amdgcn_rcpf(s.p1.y);
-      sbuf[lane] = s;
-      sid[lane] = idc;
+      {
+        // 2b, log2(o) (the forward pass folds it the same way) and 1/o
+        const float4 p1 = make_float4(q1.x, __builtin_amdgcn_rcpf(q1.y), q1.z, q1.w);
+        const float4 p2 = make_float4(q2.x, q2.y, 2.0f * q0.w, __log2f(q1.y));
+        stage[lane].p0 = q0;
+        stage[lane].p1 = p1;
+        stage[lane].p2 = p2;
+        stage[lane].p3 = make_int4(idc, valid_id(idc, n) ? 1 : 0, 0, 0);
+      }
       // records of the next batch, ids of the one after it
       idc = idn;
       {
@@ -225,20 +277,21 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         q2 = rec4[rj + 2];
       }
       int mnn = -1;
-      uint64_t wnn = 0;
+      uint64_t wtnn = 0, wbnn = 0;
       idn = -1;
       if (todo) {
         mnn = 63 - __builtin_clzll(todo);
         todo &= ~(1ull << mnn);
-        wnn = word_of(wlo, whi, mnn);
-        idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mnn), wnn);
+        wtnn = word_of(tlo, thi, mnn);
+        wbnn = word_of(blo, bhi, mnn);
+        idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mnn), wtnn | wbnn);
       }
       wave_sync();
       const int base = 64 * (r0 + mc);
-      // an id outside [0, n) (only a failed sort could leave one) is skipped
-      const uint64_t work = wc & wave_ballot(valid_id(sid[lane], n));
-      walk_worklist<true>(work, sbuf, [&](const Splat &s, int j) {
-        const int rel = base + j;
+      // a pixel takes entry j only below its own stop: j < last - base (the
+      // dead slot, j = 64, never hits)
+      const int lim0 = x.last0 - base, lim1 = x.last1 - base;
+      auto step = [&](const Staged &s, int j, bool shared) {
         const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
         // the column terms of the canonical q are shared by the lane's two rows
         const float dx = x.fx - s.p0.x;
@@ -248,8 +301,8 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         const float cdy0 = c * dy0, cdy1 = c * dy1;
         const float qa = __builtin_fmaf(cdy0, dy0, __builtin_fmaf(b2dx, dy0, adxdx));
         const float qb = __builtin_fmaf(cdy1, dy1, __builtin_fmaf(b2dx, dy1, adxdx));
-        const bool h0 = rel < x.last0 && qa <= s.p2.y;
-        const bool h1 = rel < x.last1 && qb <= s.p2.y;
+        const bool h0 = j < lim0 && qa <= s.p2.y;
+        const bool h1 = j < lim1 && qb <= s.p2.y;
         // branchless: a missed pixel takes alpha = 0, which leaves T and accum
         // unchanged and contributes zero to every sum
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(qa, NEG_HALF_LOG2E, s.p2.w));
@@ -260,44 +313,71 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         x.T1 = x.T1 * __builtin_amdgcn_rcpf(1.0f - al1);
         const float cg0 = __builtin_fmaf(s.p1.z, x.g00, __builtin_fmaf(s.p1.w, x.g01, s.p2.x * x.g02));
         const float cg1 = __builtin_fmaf(s.p1.z, x.g10, __builtin_fmaf(s.p1.w, x.g11, s.p2.x * x.g12));
-        const float d0 = cg0 - x.acc0, d1 = cg1 - x.acc1;
-        const float dal0 = x.T0 * d0, dal1 = x.T1 * d1;  // dL/dalpha
+        const float d0 = cg0 - x.acc0, d1 = cg1 - x.acc1;  // dL/dalpha = T d
         x.acc0 = __builtin_fmaf(al0, d0, x.acc0);
         x.acc1 = __builtin_fmaf(al1, d1, x.acc1);
         const float w0 = al0 * x.T0, w1 = al1 * x.T1;
-        // -2 dL/dq, which is also o G dL/dalpha: an unclamped alpha is o G; a
-        // clamped alpha passes no gradient
-        const float m0 = oG0 < 0.99f ? al0 * dal0 : 0.0f;
-        const float m1 = oG1 < 0.99f ? al1 * dal1 : 0.0f;
-        // the lane's two rows summed: with M = m0 + m1, Sy = m0 dy0 + m1 dy1 and
-        // Syy = m0 dy0^2 + m1 dy1^2, each derivative needs dx once
+        // -2 dL/dq = alpha T d, which is also o G dL/dalpha: an unclamped alpha
+        // is o G; a clamped alpha passes no gradient
+        const float m0 = oG0 < 0.99f ? w0 * d0 : 0.0f;
+        const float m1 = oG1 < 0.99f ? w1 * d1 : 0.0f;
+        // the lane's two rows, dy1 = dy0 + 1: with M = m0 + m1,
+        // Sy = m0 dy0 + m1 dy1 = M dy0 + m1 and Syy = m0 dy0^2 + m1 dy1^2 =
+        // dy0 (Sy + m1) + m1, and X = M dx, each derivative needs dx once
         const float M = m0 + m1;
-        const float my0 = m0 * dy0, my1 = m1 * dy1;
-        const float Sy = my0 + my1;
+        const float Sy = __builtin_fmaf(M, dy0, m1);
+        const float X = M * dx;
         float gr[9];
-        gr[0] = __builtin_fmaf(adx, M, b * Sy);     // dq/dmx = -2 (a dx + b dy)
-        gr[1] = __builtin_fmaf(b * dx, M, c * Sy);  // dq/dmy = -2 (b dx + c dy)
-        gr[2] = (dx * dx) * M;                      // times -1/2 after the sum
+        gr[0] = __builtin_fmaf(a, X, b * Sy);  // dq/dmx = -2 (a dx + b dy)
+        gr[1] = __builtin_fmaf(b, X, c * Sy);  // dq/dmy = -2 (b dx + c dy)
+        gr[2] = X * dx;                        // times -1/2 after the sum
         gr[3] = -(dx * Sy);
-        gr[4] = __builtin_fmaf(my1, dy1, my0 * dy0);  // times -1/2 after the sum
-        gr[5] = M;                                    // divided by o after the sum
+        gr[4] = __builtin_fmaf(dy0, Sy + m1, m1);  // times -1/2 after the sum
+        gr[5] = M;                                 // divided by o after the sum
         gr[6] = __builtin_fmaf(w1, x.g10, w0 * x.g00);
         gr[7] = __builtin_fmaf(w1, x.g11, w0 * x.g01);
         gr[8] = __builtin_fmaf(w1, x.g12, w0 * x.g02);
-        float out = reduce_scatter9(gr);
+        float out = reduce_scatter9_half(gr, zero);
+        // one splat in both halves: add the lower half's sums to the upper's
+        // (the owners sit at the same place in both halves), written once
+        if (shared) out = swap_sum32(out, out);
         // finish the sum here, where its last exchange fuses into the add,
         // rather than inside the owner lanes' branch
         __asm__ volatile("" : "+v"(out));
         out *= comp == 5 ? s.p1.y : post;
-        if (comp >= 0) unsafeAtomicAdd(&grads[9 * (int64_t)sid[j] + comp], out);
-        return true;
-      });
+        if (comp >= 0 && s.p3.y && (top || !shared))
+          unsafeAtomicAdd(&grads[9 * (int64_t)s.p3.x + comp], out);
+      };
+      // the next step's reads from the stage go out before the current step
+      // runs (two buffers alternate)
+      Pair pc = next_pair(wt, wb);
+      int j0 = top ? pc.jt : pc.jb;
+      bool sh0 = pc.shared;
+      Staged s0 = stage[j0];
+      for (;;) {
+        const bool more1 = (wt | wb) != 0;
+        pc = next_pair(wt, wb);
+        const int j1 = top ? pc.jt : pc.jb;
+        const bool sh1 = pc.shared;
+        const Staged s1 = stage[j1];
+        step(s0, j0, sh0);
+        if (!more1) break;
+        const bool more0 = (wt | wb) != 0;
+        pc = next_pair(wt, wb);
+        j0 = top ? pc.jt : pc.jb;
+        sh0 = pc.shared;
+        s0 = stage[j0];
+        step(s1, j1, sh1);
+        if (!more0) break;
+      }
       wave_sync();
       if (mn < 0) break;
       mc = mn;
-      wc = wn;
+      wt = wtn;
+      wb = wbn;
       mn = mnn;
-      wn = wnn;
+      wtn = wtnn;
+      wbn = wbnn;
     }
   }
 }
@@ -310,12 +390,17 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
     const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads) {
-  __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
-  __shared__ int sid_all[GS_WAVES_PER_BLOCK][BATCH];
-  Splat *sbuf = sbuf_all[wave_in_block()];
-  int *sid = sid_all[wave_in_block()];
+  __shared__ Staged stage_all[GS_WAVES_PER_BLOCK][SLOTS];
+  Staged *stage = stage_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
   if (!fs.hdr->run_b) return;  // the frame failed earlier: nothing to differentiate
+  if (__lane_id() == 0) {
+    Staged dead;
+    dead.p0 = dead.p1 = dead.p2 = make_float4(0.f, 0.f, 0.f, 0.f);
+    dead.p2.y = -1.0f;  // tau < 0: q <= tau never holds
+    dead.p3 = make_int4(0, 0, 0, 0);
+    stage[BATCH] = dead;
+  }
   fs.nw = fs.hdr->nw;
   const int k = fs.hdr->k;
   const int64_t P = (int64_t)cam.width * cam.height * cam.views;
@@ -375,7 +460,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
       x.acc1 = ex1;
       walk_back(splats, n, sorted_ids, rg.x, contrib_base(fs, qtop, tile, rg.x),
                 ceil64(fs.sub_last[tile * 4 + qtop]), contrib_base(fs, qbot, tile, rg.x),
-                ceil64(fs.sub_last[tile * 4 + qbot]), x, sbuf, sid, grads);
+                ceil64(fs.sub_last[tile * 4 + qbot]), x, stage, grads);
       continue;
     }
     // a chunk of a heavy tile: the lane's two pixels lie in one quarter, at
@@ -421,7 +506,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const uint64_t *cw0 = contrib_base(fs, qtop, tile, rg.x) + ((cs - rg.x) >> 6);
     const uint64_t *cw1 = contrib_base(fs, qbot, tile, rg.x) + ((cs - rg.x) >> 6);
     walk_back(splats, n, sorted_ids, cs, cw0, ceil64(fs.chunk_last[chunk_index(idx, p, qtop, k)]),
-              cw1, ceil64(fs.chunk_last[chunk_index(idx, p, qbot, k)]), x, sbuf, sid, grads);
+              cw1, ceil64(fs.chunk_last[chunk_index(idx, p, qbot, k)]), x, stage, grads);
   }
 }
 
