@@ -26,6 +26,8 @@
 // item's non-empty batches come from one vector load of its contributor words;
 // each batch stages only its contributors' records in LDS (the next batch's
 // ids and records in flight) and walks them back to front on the scalar unit.
+#include <type_traits>
+
 #include "render_common.h"
 #include "wave_reduce.h"
 
@@ -259,6 +261,11 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
       idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mn), wtn | wbn);
     }
     for (;;) {
+      // whether any splat of the batch can reach the 0.99 clamp: o G < 0.99
+      // whenever o <= 0.985 (G <= 1; the margin covers the rounding of
+      // exp2(log2 o)), so most batches take the step without the clamp's
+      // select and compare, with the same results bit for bit
+      const bool bclamp = wave_ballot(valid_id(idc, n) && q1.y > 0.985f) != 0;
       {
         // 2b, log2(o) (the forward pass folds it the same way) and 1/o
         const float4 p1 = make_float4(q1.x, __builtin_amdgcn_rcpf(q1.y), q1.z, q1.w);
@@ -291,7 +298,8 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
       // a pixel takes entry j only below its own stop: j < last - base (the
       // dead slot, j = 64, never hits)
       const int lim0 = x.last0 - base, lim1 = x.last1 - base;
-      auto step = [&](const Staged &s, int j, bool shared) {
+      auto step = [&](auto clamp_t, const Staged &s, int j, bool shared) {
+        constexpr bool CLAMP = decltype(clamp_t)::value;
         const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
         // the column terms of the canonical q are shared by the lane's two rows
         const float dx = x.fx - s.p0.x;
@@ -308,7 +316,8 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(qa, NEG_HALF_LOG2E, s.p2.w));
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(qb, NEG_HALF_LOG2E, s.p2.w));
         const float oG0 = h0 ? e0 : 0.0f, oG1 = h1 ? e1 : 0.0f;  // o G
-        const float al0 = fminf(0.99f, oG0), al1 = fminf(0.99f, oG1);
+        const float al0 = CLAMP ? fminf(0.99f, oG0) : oG0;
+        const float al1 = CLAMP ? fminf(0.99f, oG1) : oG1;
         x.T0 = x.T0 * __builtin_amdgcn_rcpf(1.0f - al0);  // T before this splat
         x.T1 = x.T1 * __builtin_amdgcn_rcpf(1.0f - al1);
         const float cg0 = __builtin_fmaf(s.p1.z, x.g00, __builtin_fmaf(s.p1.w, x.g01, s.p2.x * x.g02));
@@ -319,8 +328,8 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         const float w0 = al0 * x.T0, w1 = al1 * x.T1;
         // -2 dL/dq = alpha T d, which is also o G dL/dalpha: an unclamped alpha
         // is o G; a clamped alpha passes no gradient
-        const float m0 = oG0 < 0.99f ? w0 * d0 : 0.0f;
-        const float m1 = oG1 < 0.99f ? w1 * d1 : 0.0f;
+        const float m0 = !CLAMP || oG0 < 0.99f ? w0 * d0 : 0.0f;
+        const float m1 = !CLAMP || oG1 < 0.99f ? w1 * d1 : 0.0f;
         // the lane's two rows, dy1 = dy0 + 1: with M = m0 + m1,
         // Sy = m0 dy0 + m1 dy1 = M dy0 + m1 and Syy = m0 dy0^2 + m1 dy1^2 =
         // dy0 (Sy + m1) + m1, and X = M dx, each derivative needs dx once
@@ -350,26 +359,32 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
       };
       // the next step's reads from the stage go out before the current step
       // runs (two buffers alternate)
-      Pair pc = next_pair(wt, wb);
-      int j0 = top ? pc.jt : pc.jb;
-      bool sh0 = pc.shared;
-      Staged s0 = stage[j0];
-      for (;;) {
-        const bool more1 = (wt | wb) != 0;
-        pc = next_pair(wt, wb);
-        const int j1 = top ? pc.jt : pc.jb;
-        const bool sh1 = pc.shared;
-        const Staged s1 = stage[j1];
-        step(s0, j0, sh0);
-        if (!more1) break;
-        const bool more0 = (wt | wb) != 0;
-        pc = next_pair(wt, wb);
-        j0 = top ? pc.jt : pc.jb;
-        sh0 = pc.shared;
-        s0 = stage[j0];
-        step(s1, j1, sh1);
-        if (!more0) break;
-      }
+      auto walk = [&](auto clamp_t) {
+        Pair pc = next_pair(wt, wb);
+        int j0 = top ? pc.jt : pc.jb;
+        bool sh0 = pc.shared;
+        Staged s0 = stage[j0];
+        for (;;) {
+          const bool more1 = (wt | wb) != 0;
+          pc = next_pair(wt, wb);
+          const int j1 = top ? pc.jt : pc.jb;
+          const bool sh1 = pc.shared;
+          const Staged s1 = stage[j1];
+          step(clamp_t, s0, j0, sh0);
+          if (!more1) break;
+          const bool more0 = (wt | wb) != 0;
+          pc = next_pair(wt, wb);
+          j0 = top ? pc.jt : pc.jb;
+          sh0 = pc.shared;
+          s0 = stage[j0];
+          step(clamp_t, s1, j1, sh1);
+          if (!more0) break;
+        }
+      };
+      if (bclamp)
+        walk(std::true_type{});
+      else
+        walk(std::false_type{});
       wave_sync();
       if (mn < 0) break;
       mc = mn;

@@ -15,8 +15,9 @@
 //   two quad_perm adds (s <-> s^2 on the pair (v, u2), then s <-> s^1).
 //
 // Lane (r, s) then owns: s = 0 -> {0,5}[r], s = 8 -> {1,6}[r], s = 4 ->
-// {2,7}[r], s = 12 -> {3,8}[r], s = 2 and r = 0 -> 4. 25 instructions for two
-// splats' 9 sums (the zero operand of the unpaired swap stays in a register).
+// {2,7}[r], s = 12 -> {3,8}[r], s = 2 and r = 0 -> 4. 22 VALU instructions for
+// two splats' 9 sums (the zero operand of the unpaired swap stays in a
+// register; the bank-aligned exchanges need no selects).
 #pragma once
 #include "gs_common.h"
 
@@ -53,6 +54,30 @@ __device__ __forceinline__ int comp_of_half_lane(int lane) {
   return -1;
 }
 
+// The pair exchanges of the two bank-aligned levels: lanes of the DPP banks in
+// the first mask keep x summed with its partner, the others y. Two DPP adds
+// with complementary bank masks write every lane, so no select is needed. The
+// s_nop gives the two wait states a DPP read of a VGPR needs after the VALU
+// instruction that wrote it.
+__device__ __forceinline__ float pair_ror8(float x, float y) {
+  float r;
+  __asm__("s_nop 1\n\t"
+          "v_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3 bound_ctrl:1\n\t"
+          "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc bound_ctrl:1"
+          : "=&v"(r)
+          : "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ float pair_mirror(float x, float y) {
+  float r;
+  __asm__("s_nop 1\n\t"
+          "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5 bound_ctrl:1\n\t"
+          "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa bound_ctrl:1"
+          : "=&v"(r)
+          : "v"(x), "v"(y));
+  return r;
+}
+
 // Reduce g[0..8] over each 32-lane half; returns the half's sum of component
 // comp_of_half_lane(lane) on the lanes that own one (partial sums elsewhere).
 // zero: a register holding 0.0f (the partner of the unpaired component).
@@ -62,12 +87,13 @@ __device__ __forceinline__ float reduce_scatter9_half(const float g[9], float ze
   const float t2 = swap_sum16(g[2], g[7]);
   const float t3 = swap_sum16(g[3], g[8]);
   const float t4 = swap_sum16(g[4], zero);
-  const int s = __lane_id() & 15;
-  const bool lo8 = s < 8, lo4 = (s & 4) == 0, lo2 = (s & 2) == 0;
-  const float u0 = dpp_add<DPP_ROW_ROR8>(lo8 ? t0 : t1, lo8 ? t1 : t0);
-  const float u1 = dpp_add<DPP_ROW_ROR8>(lo8 ? t2 : t3, lo8 ? t3 : t2);
+  const bool lo2 = (__lane_id() & 2) == 0;
+  // lanes s < 8 of each row (banks 0, 1) keep t0 / t2, lanes s >= 8 t1 / t3
+  const float u0 = pair_ror8(t0, t1);
+  const float u1 = pair_ror8(t2, t3);
   const float u2 = dpp_add<DPP_ROW_ROR8>(t4, t4);
-  const float v = dpp_add<DPP_ROW_HALF_MIRROR>(lo4 ? u0 : u1, lo4 ? u1 : u0);
+  // lanes s mod 8 < 4 (banks 0, 2) keep u0, the others u1
+  const float v = pair_mirror(u0, u1);
   const float w = dpp_add<DPP_ROW_HALF_MIRROR>(u2, u2);
   float x = dpp_add<DPP_QUAD_2301>(lo2 ? v : w, lo2 ? w : v);
   x = dpp_add<DPP_QUAD_1032>(x, x);
