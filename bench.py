@@ -2,9 +2,11 @@
 
 Workload: the garden-shaped scene, 1,535,033 Gaussians, SH degree 3,
 1297x840 image (82 x 53 = 4346 tiles), seeded synthetic data already resident
-in HBM. A step runs gs_bin_tiles, gs_sort_keys, gs_render_fwd (tile schedule
-included) and gs_render_bwd on one HIP stream over the projected splats;
-gs_project (the feeder) is timed in its own loop and reported beside it. The
+in HBM. A step runs gs_bin_tiles, gs_sort_keys, gs_render_fwd and
+gs_render_bwd on one HIP stream over the projected splats, and gs_plan_tiles
+(the tile schedule, from the binning pass's tile counts) on a second stream
+while the sort runs; the forward waits for it. gs_project (the feeder) is
+timed in its own loop and reported beside it. The
 headline value is tile-Gaussian pairs per second over the step. The roofline
 object covers the longest raster kernel, with algorithmic work per unit as
 defined below, and the CPU oracle is timed on the host beside it (a baseline
@@ -270,19 +272,31 @@ def main():
           f"{sub_hits}, chunked tiles {chunked} x {chunks}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # the schedule, built beside the sort
+    ev_bin, ev_plan = torch.cuda.Event(), torch.cuda.Event()
     cap = r.capacity
     stages = ["bin", "sort", "fwd", "bwd"]
 
-    def step(ev=None):
+    def step(ev=None, evp=None):
         if ev is not None:
             ev[0].record(stream)
-        gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status, r.workspace)
+        gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status, r.workspace,
+                         tile_counts=r.tile_counts)
+        ev_bin.record(stream)
+        side.wait_event(ev_bin)
+        if evp is not None:
+            evp[0].record(side)
+        gsr.gs_plan_tiles(r.tile_counts, r.cam, r.sched, r.fwd_state, r.status, stream=side)
+        if evp is not None:
+            evp[1].record(side)
+        ev_plan.record(side)
         if ev is not None:
             ev[1].record(stream)
         gsr.gs_sort_keys(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids, r.ranges,
                          r.status, r.workspace)
         if ev is not None:
             ev[2].record(stream)
+        stream.wait_event(ev_plan)
         gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T, r.last,
                           r.fwd_state, None, None, r.status)
         if ev is not None:
@@ -303,8 +317,10 @@ def main():
     # the stage breakdown: the same steps again with HIP events between the calls
     # (kept out of the timed loop above, whose steps they would lengthen)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    pevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.steps)]
     for k in range(args.steps):
-        step(events[k])
+        step(events[k], pevents[k])
     torch.cuda.synchronize()
     # the raster kernels' own durations: the same steps again, with a pair of HIP
     # events recorded on the stream around each raster kernel launch (kept out
@@ -323,6 +339,8 @@ def main():
     for ev in events:
         for i, s in enumerate(stages):
             per[s].append(ev[i].elapsed_time(ev[i + 1]))
+    # the schedule on the side stream (overlapped with the sort, not a stage)
+    per["plan"] = [e[0].elapsed_time(e[1]) for e in pevents]
     ms = {s: float(np.median(v)) for s, v in per.items()}
     ms_min = {s: float(np.min(v)) for s, v in per.items()}
     ms_step = t_wall * 1e3 / args.steps

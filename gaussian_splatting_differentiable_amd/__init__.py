@@ -30,7 +30,8 @@ EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project"
            "gs_fwd_state_size_views", "gs_project_views", "gs_project_bwd_views",
            "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views",
            "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
-           "gs_sort_keys_noalloc", "gs_timing_start", "gs_timing_read")
+           "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views", "gs_timing_start",
+           "gs_timing_read")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -72,7 +73,7 @@ def lib():
     L.gs_project_bwd.argtypes = [i32, P, P, P, P, P, i32, cam_p, P, P, P, P, P, P, P]
     L.gs_project_bf16sh.argtypes = L.gs_project.argtypes
     L.gs_project_bwd_bf16sh.argtypes = L.gs_project_bwd.argtypes
-    L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, sz, P]
+    L.gs_bin_tiles.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, P, sz, P]
     L.gs_sort_keys.argtypes = [i32, P, P, i64, cam_p, P, P, P, P, P, sz, P]
     L.gs_render_fwd.argtypes = [i32, P, P, P, cam_p, C.POINTER(GsSched), P, P, P, P, sz, P, P, P,
                                 P]
@@ -85,7 +86,9 @@ def lib():
     L.gs_fwd_state_size_views.restype = sz
     L.gs_project_views.argtypes = [i32, P, P, P, P, P, i32, cam_p, i32, P, P]
     L.gs_project_bwd_views.argtypes = [i32, P, P, P, P, P, i32, cam_p, i32, P, P, P, P, P, P, P]
-    L.gs_bin_tiles_views.argtypes = [i32, P, cam_p, i32, i64, P, P, P, P, P, sz, P]
+    L.gs_bin_tiles_views.argtypes = [i32, P, cam_p, i32, i64, P, P, P, P, P, P, sz, P]
+    L.gs_plan_tiles.argtypes = [P, cam_p, C.POINTER(GsSched), P, sz, P, P]
+    L.gs_plan_tiles_views.argtypes = [P, cam_p, i32, C.POINTER(GsSched), P, sz, P, P]
     L.gs_sort_keys_views.argtypes = [i32, P, P, i64, cam_p, i32, P, P, P, P, P, sz, P]
     L.gs_render_fwd_views.argtypes = [i32, P, P, P, cam_p, i32, C.POINTER(GsSched), P, P, P, P,
                                       sz, P, P, P, P, P]
@@ -97,7 +100,8 @@ def lib():
                  "gs_bin_tiles", "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_project_views",
                  "gs_project_bwd_views", "gs_bin_tiles_views", "gs_sort_keys_views",
                  "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
-                 "gs_render_bwd", "gs_sort_keys_noalloc", "gs_timing_start", "gs_timing_read"):
+                 "gs_render_bwd", "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views",
+                 "gs_timing_start", "gs_timing_read"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -199,9 +203,10 @@ def gs_project_bwd_views(n, means, log_scales, quats, opacities, sh, sh_degree, 
 
 
 def gs_bin_tiles_views(n, splats, cam, n_views, capacity, offsets, keys, ids, status, workspace,
-                       stream=None):
+                       stream=None, tile_counts=None):
     _check(lib().gs_bin_tiles_views(int(n), _ptr(splats), C.byref(cam), int(n_views),
-                                    int(capacity), _ptr(offsets), _ptr(keys), _ptr(ids),
+                                    int(capacity), _ptr(offsets), _ptr(tile_counts), _ptr(keys),
+                                    _ptr(ids),
                                     _ptr(status), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(stream)),
@@ -277,11 +282,29 @@ def gs_project_bwd_bf16sh(n, means, log_scales, quats, opacities, sh, sh_degree,
            "gs_project_bwd_bf16sh")
 
 
-def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace, stream=None):
+def gs_bin_tiles(n, splats, cam, capacity, offsets, keys, ids, status, workspace, stream=None,
+                 tile_counts=None):
     _check(lib().gs_bin_tiles(int(n), _ptr(splats), C.byref(cam), int(capacity), _ptr(offsets),
-                              _ptr(keys), _ptr(ids), _ptr(status), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(stream)),
+                              _ptr(tile_counts), _ptr(keys), _ptr(ids), _ptr(status),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)),
            "gs_bin_tiles")
+
+
+def gs_plan_tiles(tile_counts, cam, sched, fwd_state, status, stream=None):
+    _check(lib().gs_plan_tiles(_ptr(tile_counts), C.byref(cam),
+                               C.byref(sched) if sched is not None else None, _ptr(fwd_state),
+                               fwd_state.numel() * fwd_state.element_size(), _ptr(status),
+                               _stream(stream)),
+           "gs_plan_tiles")
+
+
+def gs_plan_tiles_views(tile_counts, cam, n_views, sched, fwd_state, status, stream=None):
+    _check(lib().gs_plan_tiles_views(_ptr(tile_counts), C.byref(cam), int(n_views),
+                                     C.byref(sched) if sched is not None else None,
+                                     _ptr(fwd_state), fwd_state.numel() * fwd_state.element_size(),
+                                     _ptr(status), _stream(stream)),
+           "gs_plan_tiles_views")
 
 
 def gs_sort_keys(n, splats, offsets, capacity, cam, sorted_keys, sorted_ids, ranges, status,
@@ -373,10 +396,13 @@ class Rasterizer:
     Every call only enqueues work on the current stream. The frame's device
     status word is read once, after the frame (``frame_status``); ``run_frame``
     chains a whole frame and, when the pairs overflowed the buffers, grows them
-    and runs the frame again.
+    and runs the frame again. With plan_ahead the tile schedule is built from
+    the binning pass's tile counts on a second stream while the sort runs
+    (gs_plan_tiles), and the forward uses it.
     """
 
-    def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None, n_views=1):
+    def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None, n_views=1,
+                 plan_ahead=True):
         """n_views > 1: a batch of views of camera's size (the *_views calls); the
         outputs stack the views' rows and `n` counts splat records."""
         self.cam = make_camera(camera)
@@ -396,7 +422,10 @@ class Rasterizer:
         self.ranges = torch.empty((self.tiles, 2), dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.stats = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.tile_counts = torch.zeros(self.tiles, dtype=torch.int32, device=dev)
         self.fwd_state = None
+        self.plan_ahead = bool(plan_ahead)
+        self._side = None
 
     def _ensure(self, n, capacity):
         dev = self.device
@@ -440,16 +469,42 @@ class Rasterizer:
         keys = self.keys if want_emission else None
         ids = self.ids if want_emission else None
         skeys = self.sorted_keys if want_keys else None
+        tc = self.tile_counts if self.plan_ahead else None
         if self.V == 1:
             gs_bin_tiles(n, self.splats, self.cam, self.capacity, self.offsets, keys, ids,
-                         self.status, self.workspace)
+                         self.status, self.workspace, tile_counts=tc)
+        else:
+            gs_bin_tiles_views(n, self.splats, self.cam, self.V, self.capacity, self.offsets,
+                               keys, ids, self.status, self.workspace, tile_counts=tc)
+        if self.plan_ahead:
+            self._enqueue_plan()
+        if self.V == 1:
             gs_sort_keys(n, self.splats, self.offsets, self.capacity, self.cam, skeys,
                          self.sorted_ids, self.ranges, self.status, self.workspace)
         else:
-            gs_bin_tiles_views(n, self.splats, self.cam, self.V, self.capacity, self.offsets,
-                               keys, ids, self.status, self.workspace)
             gs_sort_keys_views(n, self.splats, self.offsets, self.capacity, self.cam, self.V,
                                skeys, self.sorted_ids, self.ranges, self.status, self.workspace)
+        if self.plan_ahead:
+            torch.cuda.current_stream(self.device).wait_event(self._ev_plan)
+
+    def _enqueue_plan(self):
+        """gs_plan_tiles on the side stream, after the binning pass of the current
+        stream; the caller makes the current stream wait for self._ev_plan."""
+        main = torch.cuda.current_stream(self.device)
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)
+            self._ev_bin, self._ev_plan = torch.cuda.Event(), torch.cuda.Event()
+        self._ev_bin.record(main)
+        self._side.wait_event(self._ev_bin)
+        for t in (self.tile_counts, self.fwd_state, self.status):
+            t.record_stream(self._side)  # not reused while the side stream may use it
+        if self.V == 1:
+            gs_plan_tiles(self.tile_counts, self.cam, self.sched, self.fwd_state, self.status,
+                          stream=self._side)
+        else:
+            gs_plan_tiles_views(self.tile_counts, self.cam, self.V, self.sched, self.fwd_state,
+                                self.status, stream=self._side)
+        self._ev_plan.record(self._side)
 
     def frame_status(self, n):
         """(device status, pair count I) of the frame, read once (synchronises)."""

@@ -17,8 +17,8 @@ hipError_t gs_launch_project_bwd(int n, const float *means, const float *log_sca
                                  float *gmeans, float *gls, float *gquats, float *gopac,
                                  float *gsh, bool accumulate, hipStream_t st);
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
-                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
-                         hipStream_t st);
+                         int32_t *offsets, int32_t *tile_counts, uint64_t *keys, int32_t *ids,
+                         int32_t *status, void *ws, hipStream_t st);
 size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y);
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
@@ -29,6 +29,11 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                                 int64_t cap_pairs, int64_t *stats, int32_t *pixel_hits,
                                 int32_t *status, int workers_waves, hipEvent_t ev0,
                                 hipEvent_t ev1, hipStream_t st);
+hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, const CamK &cam,
+                              int chunk_mode, int force_k, int force_h, double lambda_,
+                              double beta, double eps, int nblocks, void *fwd_state,
+                              int64_t *stats, int32_t *status, int64_t cap_pairs,
+                              hipStream_t st);
 hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
@@ -254,18 +259,20 @@ int32_t gs_project_bwd_bf16sh(int32_t n, const float *means, const float *log_sc
 namespace {
 
 int32_t bin_impl(int32_t n, const float *splats, const CamK &k, int64_t pair_capacity,
-                 int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+                 int32_t *offsets, int32_t *tile_counts, uint64_t *keys, int32_t *ids,
+                 int32_t *device_status, void *workspace, size_t workspace_bytes, void *stream) {
   if (n < 0 || pair_capacity < 0) return GS_ERR_INVALID_ARGUMENT;
   if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT || pair_capacity >= GS_COUNT_LIMIT)
     return GS_ERR_UNSUPPORTED;
   if (!offsets || !device_status || !workspace || (n > 0 && !splats)) return GS_ERR_INVALID_ARGUMENT;
   if ((keys == nullptr) != (ids == nullptr)) return GS_ERR_INVALID_ARGUMENT;
-  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8))) return GS_ERR_INVALID_ARGUMENT;
+  if ((splats && !aligned(splats, 16)) || (keys && !aligned(keys, 8)) ||
+      (tile_counts && !aligned(tile_counts, 4)))
+    return GS_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < gs_sort_ws_bytes(n, pair_capacity, k.tiles_x, k.tiles_y))
     return GS_ERR_WORKSPACE;
-  return hip_status(gs_launch_bin(n, splats, k, pair_capacity, offsets, keys, ids, device_status,
-                                  workspace, (hipStream_t)stream));
+  return hip_status(gs_launch_bin(n, splats, k, pair_capacity, offsets, tile_counts, keys, ids,
+                                  device_status, workspace, (hipStream_t)stream));
 }
 
 int32_t sort_impl(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
@@ -317,6 +324,25 @@ int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
                                          device_status, workers, e0, e1, (hipStream_t)stream));
 }
 
+int32_t plan_impl(const int32_t *tile_counts, const CamK &k, const gs_sched *sched,
+                  void *fwd_state, size_t fwd_state_bytes, int32_t *device_status, void *stream) {
+  if (batch_tiles(k) > GS_MAX_TILES) return GS_ERR_UNSUPPORTED;
+  if (!tile_counts || !fwd_state || !device_status) return GS_ERR_INVALID_ARGUMENT;
+  if (!aligned(tile_counts, 4) || !aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
+  const int64_t cap_pairs = fwd_state_capacity((int)batch_tiles(k), fwd_state_bytes);
+  if (cap_pairs < 0) return GS_ERR_WORKSPACE;
+  const gs_sched sc = sched ? *sched : default_sched();
+  if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
+      !(sc.beta >= 0.0f))
+    return GS_ERR_INVALID_ARGUMENT;
+  const int workers = worker_waves();
+  if (workers <= 0) return GS_ERR_HIP;
+  return hip_status(gs_launch_schedule(nullptr, tile_counts, k, sc.chunk_mode, sc.force_k,
+                                       sc.force_h, sc.lambda_, sc.beta, sc.eps,
+                                       workers / GS_WAVES_PER_BLOCK, fwd_state, nullptr,
+                                       device_status, cap_pairs, (hipStream_t)stream));
+}
+
 int32_t bwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
                  const int32_t *tile_ranges, CamK k, const float *T_final, const int32_t *last,
                  void *fwd_state, size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
@@ -359,12 +385,13 @@ bool prep_batch_cams(const gs_camera *cams, int32_t n_views) {
 extern "C" {
 
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
-                     int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
-                     void *workspace, size_t workspace_bytes, void *stream) {
+                     int32_t *offsets, int32_t *tile_counts, uint64_t *keys, int32_t *ids,
+                     int32_t *device_status, void *workspace, size_t workspace_bytes,
+                     void *stream) {
   CamK k;
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
-  return bin_impl(n, splats, k, pair_capacity, offsets, keys, ids, device_status, workspace,
-                  workspace_bytes, stream);
+  return bin_impl(n, splats, k, pair_capacity, offsets, tile_counts, keys, ids, device_status,
+                  workspace, workspace_bytes, stream);
 }
 
 int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
@@ -375,6 +402,14 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
                    device_status, workspace, workspace_bytes, stream);
+}
+
+int32_t gs_plan_tiles(const int32_t *tile_counts, const gs_camera *cam, const gs_sched *sched,
+                      void *fwd_state, size_t fwd_state_bytes, int32_t *device_status,
+                      void *stream) {
+  CamK k;
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return plan_impl(tile_counts, k, sched, fwd_state, fwd_state_bytes, device_status, stream);
 }
 
 int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -490,13 +525,13 @@ int32_t gs_project_bwd_views(int32_t n, const float *means, const float *log_sca
 }
 
 int32_t gs_bin_tiles_views(int32_t n, const float *splats, const gs_camera *cam, int32_t n_views,
-                           int64_t pair_capacity, int32_t *offsets, uint64_t *keys, int32_t *ids,
-                           int32_t *device_status, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           int64_t pair_capacity, int32_t *offsets, int32_t *tile_counts,
+                           uint64_t *keys, int32_t *ids, int32_t *device_status, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   CamK k;
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
-  return bin_impl(n, splats, k, pair_capacity, offsets, keys, ids, device_status, workspace,
-                  workspace_bytes, stream);
+  return bin_impl(n, splats, k, pair_capacity, offsets, tile_counts, keys, ids, device_status,
+                  workspace, workspace_bytes, stream);
 }
 
 int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offsets,
@@ -508,6 +543,14 @@ int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offset
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
                    device_status, workspace, workspace_bytes, stream);
+}
+
+int32_t gs_plan_tiles_views(const int32_t *tile_counts, const gs_camera *cam, int32_t n_views,
+                            const gs_sched *sched, void *fwd_state, size_t fwd_state_bytes,
+                            int32_t *device_status, void *stream) {
+  CamK k;
+  if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return plan_impl(tile_counts, k, sched, fwd_state, fwd_state_bytes, device_status, stream);
 }
 
 int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -588,7 +631,7 @@ int32_t gs_sort_keys_noalloc(int32_t n, const float *splats, const gs_camera *ca
   void *ws = scratch_on_current_device();
   if (!ws) return GS_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = gs_launch_bin(n, splats, k, pair_capacity, offsets, nullptr, nullptr,
+  hipError_t e = gs_launch_bin(n, splats, k, pair_capacity, offsets, nullptr, nullptr, nullptr,
                                device_status, ws, st);
   if (e != hipSuccess) return GS_ERR_HIP;
   return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,

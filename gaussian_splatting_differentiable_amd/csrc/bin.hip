@@ -48,14 +48,15 @@ __global__ void __launch_bounds__(256) k_bin_emit(int n, const Splat *__restrict
 }  // namespace
 
 hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int64_t cap,
-                               int32_t *offsets, int32_t *status, void *ws, hipStream_t st);
+                               int32_t *offsets, int32_t *tile_counts, int32_t *status, void *ws,
+                               hipStream_t st);
 
 hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t capacity,
-                         int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *status, void *ws,
-                         hipStream_t st) {
+                         int32_t *offsets, int32_t *tile_counts, uint64_t *keys, int32_t *ids,
+                         int32_t *status, void *ws, hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   dim3 block(256), grid(gs_div_up(n > 0 ? n : 1, 256));
-  hipError_t e = gs_launch_bin_count(n, splats, cam, capacity, offsets, status, ws, st);
+  hipError_t e = gs_launch_bin_count(n, splats, cam, capacity, offsets, tile_counts, status, ws, st);
   if (e != hipSuccess || !keys) return e;
   hipLaunchKernelGGL(k_bin_emit, grid, block, 0, st, n, sp, cam.width, cam.height, cam.tiles_x,
                      cam.vty, cam.views, offsets, capacity, keys, ids);

@@ -56,7 +56,15 @@ struct PlanHdr {
   // was GS_OK when the schedule (forward) or the backward's preparation ran.
   int32_t run_f, run_b;
   int64_t nw;  // contributor words per quarter (from the state's capacity)
+  // PLAN_READY while a plan built ahead of the forward (from the binning pass's
+  // tile counts) waits for it; plan_pairs is the pair total it was built for,
+  // the rest the knobs and worker count it was built with.
+  int32_t planned, plan_pairs;
+  int32_t plan_mode, plan_force_k, plan_force_h, plan_nblocks;
+  double plan_lambda, plan_beta, plan_eps;
 };
+static_assert(sizeof(PlanHdr) <= 256, "the plan header fills one 256-byte slot");
+constexpr int32_t PLAN_READY = 0x504C414E;
 
 // Contributor record of the forward pass ("What the 3DGS Literature Left on the
 // Table", Step 4, kept as a bitmap instead of a compacted list): for every

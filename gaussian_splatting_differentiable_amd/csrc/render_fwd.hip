@@ -110,8 +110,12 @@ struct Blend {
 // Blend [cs, ce) into pixels that start with transmittance T0. Branchless per
 // entry: a lane that misses (or has stopped) takes alpha = 0, which leaves its
 // colour and T unchanged bit for bit. A lane is alive exactly while its T is at
-// least 1e-4 (lanes outside the image start at T = 0), so the hit mask is the
-// AND of two compare ballots and needs no per-lane flag.
+// least 1e-4 (lanes outside the image start at T = 0); the wave carries the
+// alive lanes as a scalar mask, so the hit mask is that mask AND the ballot of
+// q <= tau, and a lane stops where it was hit and the new ballot of T >= 1e-4
+// drops it (one vector compare each, the rest on the scalar unit).
+// A batch whose staged opacities are all at most 0.985 cannot reach the 0.99
+// clamp (alpha <= o), so its entries are blended without the min.
 // cw: the quarter's contributor word of the range's first batch; every batch
 // walked writes its word (bit j: some lane blended entry j of the batch).
 template <bool STATS>
@@ -127,26 +131,27 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
   r.consumed = r.T >= T_STOP ? ce - cs : 0;
   r.wlast = 0;
   r.nh = 0;
-  bool live = wave_ballot(r.T >= T_STOP) != 0;
+  uint64_t alive = wave_ballot(r.T >= T_STOP);
   const int lane = __lane_id();
   Pipe pp;
-  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
-  for (int b = cs; b < ce && live; b += BATCH) {
+  if (alive && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
+  for (int b = cs; b < ce && alive; b += BATCH) {
     const bool cand = stage(pp.rec, st, &sbuf[lane]) && valid_id(pp.idc, n);
     const uint64_t work = wave_ballot(cand);
+    const bool clamp = wave_ballot(cand && pp.rec.p1.y > 0.985f) != 0;
     pipe_advance(pp, splats, sids, b, ce, n);
     wave_sync();
     const int base = b - cs;
     uint64_t bm = 0;  // the batch's entries that some lane blended
-    walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
+    auto step = [&](const Splat &s, int j, auto clamp_tag) {
+      constexpr bool CLAMP = decltype(clamp_tag)::value;
       const int pos = base + j;
       const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
       const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
-      const bool alive = r.T >= T_STOP, inq = q <= s.p2.y;
-      const uint64_t hm = wave_ballot(alive) & wave_ballot(inq);
-      const bool hit = alive && inq;
+      const uint64_t hm = alive & wave_ballot(q <= s.p2.y);
       if constexpr (STATS) nsteps++;
       if (!hm) return true;  // no lane hits: nothing changes
+      const bool hit = __builtin_amdgcn_inverse_ballot_w64(hm);
       if constexpr (STATS) {
         nhits += __popcll(hm);
         nhsteps++;
@@ -155,16 +160,26 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
       bm |= 1ull << j;
       r.wlast = pos + 1;
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-      const float al = hit ? fminf(0.99f, ex) : 0.0f;
+      const float al = hit ? (CLAMP ? fminf(0.99f, ex) : ex) : 0.0f;
       const float w = al * r.T;
       r.C0 = __builtin_fmaf(w, s.p1.z, r.C0);
       r.C1 = __builtin_fmaf(w, s.p1.w, r.C1);
       r.C2 = __builtin_fmaf(w, s.p2.x, r.C2);
       r.T = r.T - w;
-      r.consumed = (hit && r.T < T_STOP) ? pos + 1 : r.consumed;
-      live = wave_ballot(r.T >= T_STOP) != 0;
-      return live;
-    });
+      const uint64_t now = wave_ballot(r.T >= T_STOP);
+      const uint64_t died = hm & ~now;
+      if (died) r.consumed = __builtin_amdgcn_inverse_ballot_w64(died) ? pos + 1 : r.consumed;
+      alive = now;
+      return alive != 0;
+    };
+    if (clamp)
+      walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
+        return step(s, j, std::true_type{});
+      });
+    else
+      walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
+        return step(s, j, std::false_type{});
+      });
     if (lane == 0) cw[base >> 6] = bm;
     wave_sync();
   }
@@ -180,15 +195,15 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
                                                Splat *sbuf, const int32_t *sat, int chunk,
                                                bool &gave_up, uint32_t &nsteps) {
   float P = x.inside ? 1.0f : 0.0f;
-  bool live = wave_ballot(P >= T_STOP) != 0;
+  uint64_t alive = wave_ballot(P >= T_STOP);
   gave_up = false;
   const int lane = __lane_id();
   Pipe pp;
-  if (live && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
+  if (alive && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
   // sat is read one batch late: the load goes out with the batch prefetch, so
   // waiting for it costs nothing beyond the wait for the prefetch itself
   int satv = chunk;
-  for (int b = cs; b < ce && live; b += BATCH) {
+  for (int b = cs; b < ce && alive; b += BATCH) {
     if (satv < chunk) {
       gave_up = true;
       break;
@@ -201,15 +216,14 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
     walk_worklist<false>(work, sbuf, [&](const Splat &s, int) {
       const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
       const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
-      const bool alive = P >= T_STOP, inq = q <= s.p2.y;
-      const bool hit = alive && inq;
+      const uint64_t hm = alive & wave_ballot(q <= s.p2.y);
       if constexpr (STATS) nsteps++;
-      if (!(wave_ballot(alive) & wave_ballot(inq))) return true;
+      if (!hm) return true;
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
-      const float al = hit ? fminf(0.99f, ex) : 0.0f;
+      const float al = __builtin_amdgcn_inverse_ballot_w64(hm) ? fminf(0.99f, ex) : 0.0f;
       P = P - al * P;
-      live = wave_ballot(P >= T_STOP) != 0;
-      return live;
+      alive = wave_ballot(P >= T_STOP);
+      return alive != 0;
     });
     satv = satn;
     wave_sync();
@@ -400,10 +414,11 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
 
 }  // namespace
 
-hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
-                              int force_h, double lambda_, double beta, double eps, int nblocks,
-                              void *fwd_state, int64_t *stats, int32_t *status,
-                              int64_t cap_pairs, hipStream_t st);
+hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, const CamK &cam,
+                              int chunk_mode, int force_k, int force_h, double lambda_,
+                              double beta, double eps, int nblocks, void *fwd_state,
+                              int64_t *stats, int32_t *status, int64_t cap_pairs,
+                              hipStream_t st);
 
 hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
@@ -413,7 +428,7 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                                 hipEvent_t ev1, hipStream_t st) {
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
-  hipError_t e = gs_launch_schedule(ranges, cam, sched.chunk_mode, sched.force_k, sched.force_h,
+  hipError_t e = gs_launch_schedule(ranges, nullptr, cam, sched.chunk_mode, sched.force_k, sched.force_h,
                                     sched.lambda_, sched.beta, sched.eps, nblocks, fwd_state,
                                     stats, status, cap_pairs, st);
   if (e != hipSuccess) return e;

@@ -246,25 +246,70 @@ __device__ void class_partition(const int32_t *order, int T, int h, int tiles_x,
   __syncthreads();
 }
 
+// The plan of a frame that does not run: no items in any queue.
+__device__ void empty_plan(const FwdState &fs) {
+  if (threadIdx.x <= GS_GROUPS) fs.hdr->qoff[threadIdx.x] = 0;
+  if (threadIdx.x < GS_GROUPS) {
+    fs.hdr->qa[threadIdx.x] = fs.hdr->init_f[threadIdx.x] = fs.hdr->init_b[threadIdx.x] = 0;
+    fs.hdr->nb[threadIdx.x] = 0;
+    queue_head(fs, 0, threadIdx.x)[0] = queue_head(fs, 1, threadIdx.x)[0] = 0;
+  }
+  if (threadIdx.x == 0) {
+    fs.hdr->h = 0;
+    fs.hdr->k = 1;
+    fs.hdr->nA = fs.hdr->nplain = 0;
+  }
+}
+
 // LDS: the frame has at most TL tiles and its working arrays live in LDS (an
 // instantiation of its own, so that every access to them is an LDS access).
+// Two callers:
+//   counts == null (the forward call): the tile counts come from the ranges.
+//     If a plan built ahead for this frame waits in the state (planned), the
+//     kernel only checks it against the frame (tile grid and pair total) and
+//     the frame's status, and hands it over;
+//   counts != null (the plan built ahead, beside the sort): the per-tile
+//     counts of the binning pass; the plan is marked as waiting.
 template <bool LDS>
-__global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges, int T, int tiles_x,
-                                                 int chunk_mode, int force_k, int force_h,
-                                                 double lambda_, double beta, double eps,
-                                                 int nblocks, char *__restrict__ fwd_state,
+__global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges,
+                                                 const int32_t *__restrict__ counts_in, int T,
+                                                 int tiles_x, int chunk_mode, int force_k,
+                                                 int force_h, double lambda_, double beta,
+                                                 double eps, int nblocks,
+                                                 char *__restrict__ fwd_state,
                                                  unsigned long long *__restrict__ stats,
                                                  int32_t *__restrict__ status, int64_t cap_pairs) {
   extern __shared__ __align__(16) uint32_t dyn[];
   FwdState fs = fwd_state_at(fwd_state, T);
+  const bool ahead = counts_in != nullptr;
   // 0. the frame runs only if every earlier call of it succeeded and its pairs
   //    fit the state's contributor bitmap; otherwise the plan is empty
-  __shared__ int run;
+  __shared__ int run, handed;
   if (threadIdx.x == 0) {
+    // every word this decision reads is loaded at once (one memory round trip)
     const int st = *status;
-    const int64_t npairs = T > 0 ? (int64_t)ranges[T - 1].y : 0;
-    run = st == GS_OK && npairs <= cap_pairs;
-    if (st == GS_OK && npairs > cap_pairs) report_status(status, GS_ERR_WORKSPACE);
+    const int64_t npairs = T > 0 && !ahead ? (int64_t)ranges[T - 1].y : 0;
+    const PlanHdr hd = *fs.hdr;
+    handed = 0;
+    const bool waiting =
+        (hd.planned == PLAN_READY) & (hd.ntiles == T) & (hd.nw == contrib_words(T, cap_pairs)) &
+        (hd.plan_mode == chunk_mode) & (hd.plan_force_k == force_k) &
+        (hd.plan_force_h == force_h) & (hd.plan_nblocks == nblocks) &
+        (hd.plan_lambda == lambda_) & (hd.plan_beta == beta) & (hd.plan_eps == eps);
+    if (!ahead && waiting) {
+      // built ahead: valid for any frame of this grid (a plan only orders and
+      // splits the tiles), checked against the pair total to catch a stale one
+      const bool same = npairs == (int64_t)hd.plan_pairs;
+      if (st == GS_OK && !same) report_status(status, GS_ERR_WORKSPACE);
+      run = hd.run_f && st == GS_OK && same;
+      handed = 1;
+      fs.hdr->planned = 0;
+      if (run && stats) atomicAdd(&stats[3], (unsigned long long)hd.h);
+    } else {
+      run = st == GS_OK && npairs <= cap_pairs;
+      if (st == GS_OK && npairs > cap_pairs) report_status(status, GS_ERR_WORKSPACE);
+      fs.hdr->planned = 0;
+    }
     fs.hdr->run_f = run;
     fs.hdr->run_b = 0;
     fs.hdr->nw = contrib_words(T, cap_pairs);
@@ -272,20 +317,8 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     fs.hdr->ntiles = T;
   }
   __syncthreads();
-  if (!run) {
-    if (threadIdx.x <= GS_GROUPS) fs.hdr->qoff[threadIdx.x] = 0;
-    if (threadIdx.x < GS_GROUPS) {
-      fs.hdr->qa[threadIdx.x] = fs.hdr->init_f[threadIdx.x] = fs.hdr->init_b[threadIdx.x] = 0;
-      fs.hdr->nb[threadIdx.x] = 0;
-      queue_head(fs, 0, threadIdx.x)[0] = queue_head(fs, 1, threadIdx.x)[0] = 0;
-    }
-    if (threadIdx.x == 0) {
-      fs.hdr->h = 0;
-      fs.hdr->k = 1;
-      fs.hdr->nA = fs.hdr->nplain = 0;
-    }
-    return;
-  }
+  if (!run) empty_plan(fs);
+  if (!run || handed) return;
   const double workers = (double)(nblocks * GS_WAVES_PER_BLOCK) / 4.0;  // four waves per tile
   // working arrays: LDS for frames of up to TL tiles, else the forward state's
   // item and bound arrays (written for real only after they served here)
@@ -302,7 +335,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
 #pragma unroll
     for (int r = 0; r < RB_ROUNDS; r++) {
       const int t = t0 + r * NT;
-      rr[r] = t < T ? ranges[t] : make_int2(0, 0);
+      rr[r] = t >= T ? make_int2(0, 0) : (ahead ? make_int2(0, counts_in[t]) : ranges[t]);
     }
 #pragma unroll
     for (int r = 0; r < RB_ROUNDS; r++) {
@@ -317,6 +350,15 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     }
   }
   block_max_sum(mx, tot);
+  if (ahead && tot > cap_pairs) {
+    // built ahead: the pair total is known only now
+    if (threadIdx.x == 0) {
+      if (*status == GS_OK) report_status(status, GS_ERR_WORKSPACE);
+      fs.hdr->run_f = 0;
+    }
+    empty_plan(fs);
+    return;
+  }
   int bits = 0;
   while (bits < 32 && (mx >> bits) != 0u) bits++;
   const uint32_t full = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
@@ -469,15 +511,29 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     fs.hdr->nA = nA;
     fs.hdr->nplain = 4 * (T - h);
     if (stats) atomicAdd(&stats[3], (unsigned long long)h);
+    if (ahead) {
+      fs.hdr->plan_pairs = (int32_t)tot;
+      fs.hdr->plan_mode = chunk_mode;
+      fs.hdr->plan_force_k = force_k;
+      fs.hdr->plan_force_h = force_h;
+      fs.hdr->plan_nblocks = nblocks;
+      fs.hdr->plan_lambda = lambda_;
+      fs.hdr->plan_beta = beta;
+      fs.hdr->plan_eps = eps;
+      fs.hdr->planned = PLAN_READY;
+    }
   }
 }
 
 }  // namespace
 
-hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_mode, int force_k,
-                              int force_h, double lambda_, double beta, double eps, int nblocks,
-                              void *fwd_state, int64_t *stats, int32_t *status,
-                              int64_t cap_pairs, hipStream_t st) {
+// ranges: the frame's tile ranges (the forward call), or null with counts: the
+// per-tile pair counts of the binning pass (the plan built ahead).
+hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, const CamK &cam,
+                              int chunk_mode, int force_k, int force_h, double lambda_,
+                              double beta, double eps, int nblocks, void *fwd_state,
+                              int64_t *stats, int32_t *status, int64_t cap_pairs,
+                              hipStream_t st) {
   const int T = cam.tiles_x * cam.tiles_y;
   const size_t lds = T <= TL ? LDS_BYTES : POLICY_BYTES;
   static_assert(POLICY_BYTES <= 4 * (size_t)TL, "the policy arrays fit in the first LDS array");
@@ -485,8 +541,8 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const CamK &cam, int chunk_
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, st, reinterpret_cast<const int2 *>(ranges), T,
-                     cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, nblocks,
+  hipLaunchKernelGGL(kern, dim3(1), dim3(NT), lds, st, reinterpret_cast<const int2 *>(ranges),
+                     counts, T, cam.tiles_x, chunk_mode, force_k, force_h, lambda_, beta, eps, nblocks,
                      reinterpret_cast<char *>(fwd_state),
                      reinterpret_cast<unsigned long long *>(stats), status, cap_pairs);
   return hipGetLastError();

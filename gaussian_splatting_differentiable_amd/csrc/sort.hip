@@ -260,14 +260,58 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
       if (th[i]) atomicAdd(&tile_diff[i], th[i]);
 }
 
+// Per-tile pair counts from the binning pass's row difference array: each row
+// of it sums to zero (a span adds +1 where it starts and -1 where it ends), so
+// the inclusive prefix along a row is the count of each of its tiles. One wave
+// per row (row = wave index over the extra blocks); the row's entries are
+// loaded before any is scanned, 64 per register.
+constexpr int TC_ROW_REGS = 4;  // rows of up to 256 tiles in one load round
+__device__ void tile_counts_rows(const int32_t *__restrict__ tile_diff, int tiles_x, int tiles_y,
+                                 int32_t *__restrict__ tile_counts, int row0) {
+  const int lane = threadIdx.x & 63, ty = row0 + (threadIdx.x >> 6);
+  if (ty >= tiles_y) return;
+  const int32_t *row = tile_diff + (int64_t)ty * (tiles_x + 1);
+  int32_t *out = tile_counts + (int64_t)ty * tiles_x;
+  int carry = 0;
+  for (int x0 = 0; x0 < tiles_x; x0 += 64 * TC_ROW_REGS) {
+    int v[TC_ROW_REGS];
+#pragma unroll
+    for (int r = 0; r < TC_ROW_REGS; r++) {
+      const int x = x0 + 64 * r + lane;
+      v[r] = x < tiles_x ? row[x] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < TC_ROW_REGS; r++) {
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v[r], d, 64);
+        if (lane >= d) v[r] += o;
+      }
+      const int x = x0 + 64 * r + lane;
+      if (x < tiles_x) out[x] = carry + v[r];
+      carry += __shfl(v[r], 63, 64);
+    }
+  }
+}
+
 // Exclusive prefix of the counts in place (offsets[0, n)), offsets[n] = I and
 // the status: block b scans its own chunk, starting from the sum of the chunk
-// sums before it.
+// sums before it. With tile_counts, extra blocks after those write the per-tile
+// counts (a wave per tile row).
 __global__ void __launch_bounds__(BIN_T) k_bin_offsets(int n, int chunk,
                                                        const int32_t *__restrict__ bin_sum,
                                                        int32_t *__restrict__ offsets,
                                                        int64_t capacity,
-                                                       int32_t *__restrict__ status) {
+                                                       int32_t *__restrict__ status,
+                                                       const int32_t *__restrict__ tile_diff,
+                                                       int tiles_x, int tiles_y,
+                                                       int32_t *__restrict__ tile_counts) {
+  const int nrb = tile_counts ? (tiles_y + BIN_T / 64 - 1) / (BIN_T / 64) : 0;
+  if ((int)blockIdx.x >= (int)gridDim.x - nrb) {
+    tile_counts_rows(tile_diff, tiles_x, tiles_y, tile_counts,
+                     ((int)blockIdx.x - ((int)gridDim.x - nrb)) * (BIN_T / 64));
+    return;
+  }
   int64_t pre = 0;
   for (int b = threadIdx.x; b < (int)blockIdx.x; b += BIN_T) pre += bin_sum[b];
   int64_t base;
@@ -296,7 +340,7 @@ __global__ void __launch_bounds__(BIN_T) k_bin_offsets(int n, int chunk,
     }
     carry += tot;
   }
-  if ((int)blockIdx.x == (int)gridDim.x - 1 && threadIdx.x == 0) {
+  if ((int)blockIdx.x == (int)gridDim.x - 1 - nrb && threadIdx.x == 0) {
     offsets[n] = (int32_t)min(carry, (int64_t)INT32_MAX);
     *status = carry > capacity ? GS_ERR_CAPACITY : GS_OK;
   }
@@ -751,10 +795,12 @@ size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y) {
   return carve(nullptr, n, cap, tiles_x, tiles_y).bytes + 256;
 }
 
-// gs_bin_tiles' counting kernels and the prefix sum: offsets[0, n] and the
-// status (GS_OK, or GS_ERR_CAPACITY when the pairs exceed cap).
+// gs_bin_tiles' counting kernels and the prefix sum: offsets[0, n], the
+// status (GS_OK, or GS_ERR_CAPACITY when the pairs exceed cap) and, when
+// tile_counts is not null, the per-tile pair counts.
 hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int64_t cap,
-                               int32_t *offsets, int32_t *status, void *ws, hipStream_t st) {
+                               int32_t *offsets, int32_t *tile_counts, int32_t *status, void *ws,
+                               hipStream_t st) {
   SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
   hipLaunchKernelGGL(k_bin_init, dim3(1), dim3(1024), 0, st, w.ctl, w.tile_diff,
                      cam.tiles_y * (cam.tiles_x + 1), n, cap, cam.tiles_x, cam.tiles_y);
@@ -771,8 +817,10 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
                      reinterpret_cast<const Splat *>(splats), cam.width, cam.height, cam.tiles_x,
                      cam.tiles_y, cam.vty, cam.views, offsets, chunk, w.bin_sum, w.dkey, w.ctl,
                      w.tile_diff, w.status, w.nstatus, lds > 0);
-  hipLaunchKernelGGL(k_bin_offsets, dim3(blocks), dim3(BIN_T), 0, st, n, chunk, w.bin_sum,
-                     offsets, cap, status);
+  const int nrb = tile_counts ? (cam.tiles_y + BIN_T / 64 - 1) / (BIN_T / 64) : 0;
+  hipLaunchKernelGGL(k_bin_offsets, dim3(blocks + nrb), dim3(BIN_T), 0, st, n,
+                     chunk, w.bin_sum, offsets, cap, status, w.tile_diff, cam.tiles_x,
+                     cam.tiles_y, tile_counts);
   return hipGetLastError();
 }
 

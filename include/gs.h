@@ -177,6 +177,9 @@ int32_t gs_project_bwd_bf16sh(int32_t n, const float *means, const float *log_sc
  * in closed form with the canonical fp32 operation sequence (bit-exact).
  *   offsets [n+1] <- exclusive prefix sum of per-splat pair counts;
  *                    offsets[n] = I, the number of pairs (always written).
+ *   tile_counts [T] or NULL <- the number of pairs of every tile (T = tiles_x
+ *     x tiles_y, row-major), for gs_plan_tiles; gs_sort_keys does not read it
+ *     (it recomputes the counts from its own record in the workspace).
  *   keys, ids [pair_capacity] or both NULL <- (tile << 32) | float_bits(depth)
  *     and the splat id of every pair, in splat-id order, tiles of one splat
  *     ascending. The frame does not need them (gs_sort_keys emits the pairs
@@ -190,8 +193,9 @@ int32_t gs_project_bwd_bf16sh(int32_t n, const float *means, const float *log_sc
  *     pair histograms, and cleared radix look-back words. Pass the same
  *     workspace, untouched, to the gs_sort_keys call of the same frame. */
 int32_t gs_bin_tiles(int32_t n, const float *splats, const gs_camera *cam, int64_t pair_capacity,
-                     int32_t *offsets, uint64_t *keys, int32_t *ids, int32_t *device_status,
-                     void *workspace, size_t workspace_bytes, void *stream);
+                     int32_t *offsets, int32_t *tile_counts, uint64_t *keys, int32_t *ids,
+                     int32_t *device_status, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /* Order the pairs by (tile, depth, splat id) and cut the per-tile ranges
  * (Step 1 (d), Figure 5 of the literature page): stable radix sort of the
@@ -218,12 +222,35 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
                      int32_t *tile_ranges, int32_t *device_status, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* The frame's tile schedule, built ahead of gs_render_fwd from the per-tile
+ * counts of gs_bin_tiles (section 4 of the load-imbalance page: the
+ * longest-first order of the tiles by pair count, the Eq. 6 chunking policy and
+ * the work queues). Only the counts feed the schedule, so it can be built
+ * while gs_sort_keys runs, on a second stream that waits for gs_bin_tiles;
+ * the stream of gs_render_fwd then waits for this call. gs_render_fwd finds
+ * the plan in fwd_state and uses it in place of building its own (it checks
+ * the tile grid and that the pair total matches its tile_ranges; a mismatch
+ * sets device_status to GS_ERR_WORKSPACE). Without this call gs_render_fwd
+ * builds the same plan itself.
+ *   tile_counts [T]: as written by gs_bin_tiles for this frame.
+ *   sched: as for gs_render_fwd (NULL = defaults); pass the same to both.
+ *   fwd_state <- the plan; the state must not be in use by a gs_render_bwd of
+ *     an earlier frame while this runs (order the streams accordingly).
+ *   device_status [1]: read when the call starts (a frame that already failed
+ *     gets no plan, and gs_render_fwd then plans and skips it itself);
+ *     GS_ERR_WORKSPACE when the pairs exceed the state's capacity. */
+int32_t gs_plan_tiles(const int32_t *tile_counts, const gs_camera *cam, const gs_sched *sched,
+                      void *fwd_state, size_t fwd_state_bytes, int32_t *device_status,
+                      void *stream);
+
 /* Forward blend (Eq. 2-3): per pixel, front to back over its tile's list;
  * alpha = min(0.99, o exp(-q/2)) on hits (q <= tau); C += alpha T c;
  * T *= (1 - alpha); the pixel stops after the splat that takes T below 1e-4.
  * Tiles are served by a persistent longest-first queue; heavy tiles may be
  * split into depth chunks (Eq. 4-5) with saturation signalling, exactly:
- * results do not depend on the schedule beyond fp32 rounding.
+ * results do not depend on the schedule beyond fp32 rounding. The schedule is
+ * the one gs_plan_tiles built ahead for this frame, if it did, else the call
+ * builds it first.
  *   rgb [3][H][W], T_final [H][W] <- colour and final transmittance
  *   last [H][W] <- list entries the pixel consumed (stop index + 1, or the
  *                  tile's full length when it never stopped)
@@ -302,7 +329,8 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
  *   so tile ids run over tiles_x x (n_views ty) tiles; its pixels are rows
  *   [v height, (v + 1) height) of rgb [3][n_views height][width], T_final and
  *   last [n_views height][width], and of dL_drgb and dL_dT.
- *   cam (bin, sort, render): any camera of the batch (only its size is used).
+ *   cam (bin, sort, plan, render): any camera of the batch (only its size is
+ *   used).
  *   Sizes: gs_workspace_size_views and gs_fwd_state_size_views (0 on invalid
  *   arguments or more than 65535 tiles in the batch).
  *   gs_project_views: splats [n_views n][12] <- gs_project with cams[v] for
@@ -326,14 +354,17 @@ int32_t gs_project_bwd_views(int32_t n, const float *means, const float *log_sca
                              float *dL_dquats, float *dL_dopacities, float *dL_dsh,
                              void *stream);
 int32_t gs_bin_tiles_views(int32_t n, const float *splats, const gs_camera *cam, int32_t n_views,
-                           int64_t pair_capacity, int32_t *offsets, uint64_t *keys, int32_t *ids,
-                           int32_t *device_status, void *workspace, size_t workspace_bytes,
-                           void *stream);
+                           int64_t pair_capacity, int32_t *offsets, int32_t *tile_counts,
+                           uint64_t *keys, int32_t *ids, int32_t *device_status, void *workspace,
+                           size_t workspace_bytes, void *stream);
 int32_t gs_sort_keys_views(int32_t n, const float *splats, const int32_t *offsets,
                            int64_t pair_capacity, const gs_camera *cam, int32_t n_views,
                            uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
                            int32_t *device_status, void *workspace, size_t workspace_bytes,
                            void *stream);
+int32_t gs_plan_tiles_views(const int32_t *tile_counts, const gs_camera *cam, int32_t n_views,
+                            const gs_sched *sched, void *fwd_state, size_t fwd_state_bytes,
+                            int32_t *device_status, void *stream);
 int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,
                             const int32_t *tile_ranges, const gs_camera *cam, int32_t n_views,
                             const gs_sched *sched, float *rgb, float *T_final, int32_t *last,

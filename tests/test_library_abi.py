@@ -104,10 +104,10 @@ def test_argument_validation_needs_no_gpu(gsr):
                            p16, None) == -3
     # counts from 2^30 up: the radix passes' look-back words hold 30-bit counts
     big_ws = C.c_size_t(1 << 62)
-    assert L.gs_bin_tiles(1 << 30, p16, C.byref(cam), 100, p16, None, None, p16, p16, big_ws,
-                          None) == -5
-    assert L.gs_bin_tiles(10, p16, C.byref(cam), 1 << 30, p16, None, None, p16, p16, big_ws,
-                          None) == -5
+    assert L.gs_bin_tiles(1 << 30, p16, C.byref(cam), 100, p16, None, None, None, p16, p16,
+                          big_ws, None) == -5
+    assert L.gs_bin_tiles(10, p16, C.byref(cam), 1 << 30, p16, None, None, None, p16, p16,
+                          big_ws, None) == -5
     assert L.gs_sort_keys(10, p16, p16, 1 << 30, C.byref(cam), None, p16, p16, p16, p16, big_ws,
                           None) == -5
     assert L.gs_render_fwd(1 << 30, p16, p16, p16, C.byref(cam), None, p16, p16, p16, st256,
@@ -118,8 +118,8 @@ def test_argument_validation_needs_no_gpu(gsr):
                                                                                     5000)
     assert L.gs_fwd_state_size_views(64, 64, 0, 8) == 0
     assert L.gs_fwd_state_size_views(64, 64, 17, 8) == 0
-    assert L.gs_bin_tiles_views(1, p16, C.byref(cam), 0, 10, p16, None, None, p16, p16, 1 << 30,
-                                None) == -1
+    assert L.gs_bin_tiles_views(1, p16, C.byref(cam), 0, 10, p16, None, None, None, p16, p16,
+                                1 << 30, None) == -1
     assert L.gs_render_fwd_views(1, p16, p16, p16, C.byref(cam), 17, None, p16, p16, p16, st256,
                                  1 << 30, None, None, p16, None, None) == -1
     assert L.gs_project_views(1, p16, p16, p16, p16, p16, 0, None, 2, p16, None) == -1
@@ -130,8 +130,27 @@ def test_argument_validation_needs_no_gpu(gsr):
                                   p16, None) == -1
     big = gsr.GsCamera()
     big.width, big.height, big.fx, big.fy = 1 << 14, 1 << 14, 1.0, 1.0
-    assert L.gs_bin_tiles(1, C.c_void_p(16), C.byref(big), 10, C.c_void_p(16), C.c_void_p(16),
-                          C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 1 << 30, None) == -5
+    assert L.gs_bin_tiles(1, C.c_void_p(16), C.byref(big), 10, C.c_void_p(16), None,
+                          C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 1 << 30,
+                          None) == -5
     # undersized workspace
-    assert L.gs_bin_tiles(10, C.c_void_p(16), C.byref(cam), 100, C.c_void_p(16), C.c_void_p(16),
-                          C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 8, None) == -3
+    assert L.gs_bin_tiles(10, C.c_void_p(16), C.byref(cam), 100, C.c_void_p(16), None,
+                          C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 8,
+                          None) == -3
+    # a misaligned tile-count array
+    assert L.gs_bin_tiles(10, p16, C.byref(cam), 100, p16, C.c_void_p(18), None, None, p16, p16,
+                          1 << 30, None) == -1
+    # the plan built ahead: counts, state and status are required; the state must
+    # hold the header and arrays; knobs are checked as for the forward
+    assert L.gs_plan_tiles(None, C.byref(cam), None, st256, 1 << 30, p16, None) == -1
+    assert L.gs_plan_tiles(p16, C.byref(cam), None, None, 1 << 30, p16, None) == -1
+    assert L.gs_plan_tiles(p16, C.byref(cam), None, st256, 1 << 30, None, None) == -1
+    assert L.gs_plan_tiles(C.c_void_p(18), C.byref(cam), None, st256, 1 << 30, p16, None) == -1
+    assert L.gs_plan_tiles(p16, C.byref(cam), None, C.c_void_p(272), 1 << 30, p16, None) == -1
+    assert L.gs_plan_tiles(p16, C.byref(cam), None, st256, small, p16, None) == -3
+    bad_sched = gsr.make_sched(chunk_mode=3)
+    assert L.gs_plan_tiles(p16, C.byref(cam), C.byref(bad_sched), st256, 1 << 30, p16,
+                           None) == -1
+    assert L.gs_plan_tiles(p16, C.byref(bad), None, st256, 1 << 30, p16, None) == -1
+    assert L.gs_plan_tiles_views(p16, C.byref(cam), 17, None, st256, 1 << 30, p16, None) == -1
+    assert L.gs_plan_tiles(p16, C.byref(big), None, st256, 1 << 40, p16, None) == -5
