@@ -14,7 +14,7 @@
 // also clears the look-back words of every radix pass of the frame.
 //
 // gs_sort_keys then runs:
-//   - four onesweep LSD passes over the visible splats' depth keys (8192-key
+//   - four onesweep LSD passes over the visible splats' depth keys (6144-key
 //     partitions), the last of which also writes each splat's pair count in
 //     depth order;
 //   - an exclusive scan of those counts: the pair offsets in depth order, and
@@ -53,7 +53,7 @@ constexpr uint32_t WS_MAGIC = 0x47534254u;  // a binning pass's state is present
 
 // partitions: depth passes and tile passes
 constexpr int DS_THREADS = 1024, DS_ITEMS = 6, DS_PART = DS_THREADS * DS_ITEMS;
-constexpr int TS_THREADS = 512, TS_ITEMS = 16, TS_PART = TS_THREADS * TS_ITEMS;
+constexpr int TS_THREADS = 1024, TS_ITEMS = 16, TS_PART = TS_THREADS * TS_ITEMS;
 
 // Per-frame control block at the start of the workspace.
 struct SortCtl {
