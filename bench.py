@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -108,21 +110,42 @@ def parse():
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--chunk-mode", type=int, default=1)
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-configuration diagnostics of configs 1-5")
+    p.add_argument("--config-steps", type=int, default=10)
     p.add_argument("--views", type=int, default=0,
                    help="also time a batch of this many views against as many single-view "
                         "steps (below 2, the default: skip)")
     return p.parse_args()
 
 
-def cpu_baseline(sc, npairs_gpu):
-    """The oracle's bin, sort, forward and backward on the same scene, repeated
-    for about 10 s of host time (projection once, outside the clock)."""
-    import oracle
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_frames(oracle, sc, splats, budget_s, max_frames):
+    """Whole frames (bin, sort, forward, backward) through the oracle until the
+    time budget is spent; returns (frames, pairs, seconds)."""
     cam = sc.camera
     W, H = cam.width, cam.height
-    splats = oracle.project_scene(sc)
     frames, pairs, t_total = 0, 0, 0.0
-    while t_total < 10.0 and frames < 20:
+    while frames == 0 or (t_total < budget_s and frames < max_frames):
         t0 = time.perf_counter()
         offsets, keys, ids = oracle.bin_tiles(splats, W, H)
         skeys, sids = oracle.sort_pairs(keys, ids)
@@ -132,11 +155,168 @@ def cpu_baseline(sc, npairs_gpu):
         t_total += time.perf_counter() - t0
         frames += 1
         pairs += len(sids)
+    return frames, pairs, t_total
+
+
+def cpu_baseline(sc, npairs_gpu):
+    """The oracle's bin, sort, forward and backward on the same scene: about
+    10 s of frames on every host thread, then one frame on one thread
+    (projection once, outside the clock)."""
+    import oracle
+    splats = oracle.project_scene(sc)
+    threads = oracle.num_threads()
+    frames, pairs, t_total = _oracle_frames(oracle, sc, splats, 10.0, 20)
+    oracle.set_num_threads(1)
+    try:
+        f1, p1, t1 = _oracle_frames(oracle, sc, splats, 0.0, 1)
+    finally:
+        oracle.set_num_threads(threads)
     return {"value": round(pairs / t_total, 1), "unit": "tile-pairs/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": f"{frames} whole frames of the same scene through the oracle's bin, sort, "
-                      f"forward and backward ({t_total:.1f} s; {pairs // frames} pairs per frame, "
-                      f"GPU {npairs_gpu})"}
+                      f"forward and backward on {threads} threads ({t_total:.1f} s; "
+                      f"{pairs // frames} pairs per frame, GPU {npairs_gpu}); one more frame "
+                      f"on 1 thread",
+            "value_1_thread": round(p1 / t1, 1), "seconds_1_thread": round(t1, 2),
+            "cpu_model": cpu_model(), "cpu_count": os.cpu_count()}
+
+
+def oracle_frame_counts(sc):
+    """Knife-edge pixels and the exact hit and live-entry counts of one frame,
+    from the oracle's fp32 decision mirror (the oracle's forward on its own
+    projection, binning and sort)."""
+    import oracle
+    cam = sc.camera
+    splats = oracle.project_scene(sc)
+    offsets, keys, ids = oracle.bin_tiles(splats, cam.width, cam.height)
+    skeys, sids = oracle.sort_pairs(keys, ids)
+    ranges = oracle.tile_ranges(skeys, cam.num_tiles)
+    f = oracle.render_fwd(splats, sids, ranges, cam.width, cam.height)
+    return {"knife_pixels": int(f["knife"].sum()), "pairs": int(len(sids)),
+            "hits": int(f["hits"]), "live_entries": int(f["last"].astype(np.int64).sum())}
+
+
+def frame_diagnostics(gsr, sc, r, n, cus):
+    """Per-frame quantities of the scene already binned, sorted and rendered by r
+    (with stats): visible splats, pairs, hits, live entries (sum over pixels of
+    the list entries walked before the pixel stopped), the per-tile pair counts
+    and the chunk plan."""
+    import torch
+    ranges = r.ranges.cpu().numpy().astype(np.int64)
+    Nt = ranges[:, 1] - ranges[:, 0]
+    I = int(Nt.sum())
+    st = r.stats.cpu().numpy()
+    plan = r.fwd_state[:8].cpu().numpy().view(np.int32)
+    nonempty = Nt[Nt > 0]
+    return {
+        "gaussians": n, "visible": int((r.splats[:n, 9] > 0).sum().item()), "pairs": I,
+        "hits": int(st[0]), "live_entries": int(r.last.to(torch.int64).sum().item()),
+        "lane_evaluations": int(st[1]), "subtile_hits": int(st[2]),
+        "tiles": int(len(Nt)), "tiles_empty": int((Nt == 0).sum()),
+        "pairs_per_tile": {"max": int(Nt.max(initial=0)), "min": int(Nt.min(initial=0)),
+                           "mean": round(float(Nt.mean()) if len(Nt) else 0.0, 2),
+                           "min_nonempty": int(nonempty.min()) if len(nonempty) else 0},
+        # the load-imbalance page's ratio of the heaviest tile to the mean work of
+        # one compute unit (K = the device's compute units)
+        "imbalance_nmax_over_I_per_K": round(float(Nt.max(initial=0)) / max(I / cus, 1e-9), 3),
+        "chunk_plan": {"chunked_tiles": int(plan[0]), "chunks_per_tile": int(plan[1])},
+    }
+
+
+def stage_times(gsr, r, n, dL, steps, warmup):
+    """Median ms of bin, sort (with the schedule built beside it), forward and
+    backward over `steps` frames, HIP events between the calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ev_bin, ev_plan = torch.cuda.Event(), torch.cuda.Event()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gsr.gs_bin_tiles(n, r.splats, r.cam, r.capacity, r.offsets, None, None, r.status,
+                         r.workspace, tile_counts=r.tile_counts)
+        ev_bin.record(stream)
+        side.wait_event(ev_bin)
+        gsr.gs_plan_tiles(r.tile_counts, r.cam, r.sched, r.fwd_state, r.status, stream=side)
+        ev_plan.record(side)
+        if ev is not None:
+            ev[1].record(stream)
+        gsr.gs_sort_keys(n, r.splats, r.offsets, r.capacity, r.cam, None, r.sorted_ids,
+                         r.ranges, r.status, r.workspace)
+        if ev is not None:
+            ev[2].record(stream)
+        stream.wait_event(ev_plan)
+        gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
+                          r.last, r.fwd_state, None, None, r.status)
+        if ev is not None:
+            ev[3].record(stream)
+        gsr.gs_render_bwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last, r.fwd_state,
+                          dL, r.grads, r.status)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    st = int(r.status.item())
+    if st != gsr.GS_OK:
+        raise SystemExit(f"a frame failed: {gsr.strerror(st)}")
+    names = ["bin", "sort", "fwd", "bwd"]
+    ms = {s: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
+          for i, s in enumerate(names)}
+    return ms_step, ms
+
+
+def raster_roofline(hits, npairs, pixels, sub_hits, ms_fwd, ms_bwd):
+    """t_roof of render_fwd + render_bwd (the larger of the fp32 and the HBM time
+    of each) over their measured time."""
+    t_fwd = max(FWD_FLOPS_PER_HIT * hits / (PEAK_FP32_TFLOPS * 1e12),
+                (PAIR_BYTES * npairs + PIXEL_BYTES * pixels) / (PEAK_HBM_GBS * 1e9))
+    t_bwd = max(BWD_FLOPS_PER_HIT * hits / (PEAK_FP32_TFLOPS * 1e12),
+                (PAIR_BYTES * npairs + PIXEL_BYTES * pixels + ATOMIC_BYTES * sub_hits)
+                / (PEAK_HBM_GBS * 1e9))
+    return (t_fwd + t_bwd) / ((ms_fwd + ms_bwd) * 1e-3)
+
+
+def config_line(gsr, dev, cfg, args, cus):
+    """One configuration: its scene, one counted frame (diagnostics), then timed
+    frames (stage medians, tile-pairs per second, raster roofline fraction)."""
+    import torch
+    import scenegen
+    sc = scenegen.make_config(cfg)
+    n = sc.n
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    r = gsr.Rasterizer(sc.camera, device=dev, capacity=1 << 20)
+    r.project(up(sc.means), up(sc.log_scales), up(sc.quats), up(sc.opacities), up(sc.sh),
+              sc.sh_degree)
+    I = r.bin_and_sort(n)
+    r._ensure(n, max(r.capacity, I + I // 8))
+    r.bin_and_sort(n)
+    r.render_fwd(n, stats=True)
+    diag = frame_diagnostics(gsr, sc, r, n, cus)
+    dL = up(sc.dL_drgb)
+    ms_step, ms = stage_times(gsr, r, n, dL, args.config_steps, 3)
+    P = sc.camera.width * sc.camera.height
+    diag.update(
+        workload=f"{sc.name}: {n} Gaussians, SH degree {sc.sh_degree}, "
+                 f"{sc.camera.width}x{sc.camera.height} image",
+        ms_per_step=round(ms_step, 4), ms={k: round(v, 4) for k, v in ms.items()},
+        tile_pairs_per_s=round(I / (ms_step * 1e-3), 1),
+        raster_roofline_frac=round(raster_roofline(diag["hits"], I, P, diag["subtile_hits"],
+                                                   ms["fwd"], ms["bwd"]), 4))
+    del r
+    torch.cuda.empty_cache()
+    return sc, diag
 
 
 def views_stage(args, sc, gsr, dev, means, ls, qs, op, sh):
@@ -452,6 +632,31 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(sc, npairs)
 
+    # every configuration (the headline one from the frames above), with the
+    # oracle's knife-edge count and exact hit counts beside it when the CPU leg runs
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    head = frame_diagnostics(gsr, sc, r, n, cus)
+    head.update(workload=f"{sc.name}: {n} Gaussians, SH degree {sc.sh_degree}, "
+                         f"{cam.width}x{cam.height} image",
+                ms_per_step=round(ms_step, 4), ms={k: round(ms[k], 4) for k in stages},
+                tile_pairs_per_s=round(npairs / (ms_step * 1e-3), 1),
+                raster_roofline_frac=round(raster_frac, 4))
+    configs = {str(args.config): head}
+    if not args.no_cpu_baseline:
+        head["oracle"] = oracle_frame_counts(sc)
+    if not args.no_configs:
+        del r
+        torch.cuda.empty_cache()
+        for cfg in (1, 2, 3, 4, 5):
+            if cfg == args.config:
+                continue
+            print(f"[bench] configuration {cfg}", file=sys.stderr, flush=True)
+            sc_c, diag = config_line(gsr, dev, cfg, args, cus)
+            if not args.no_cpu_baseline:
+                diag["oracle"] = oracle_frame_counts(sc_c)
+            configs[str(cfg)] = diag
+            del sc_c
+
     line = {
         "metric": METRIC,
         "value": round(npairs / (ms_step * 1e-3), 1),
@@ -479,6 +684,7 @@ def main():
         "n_visible": n_vis, "n_touched": n_touched, "n_touched_visible": n_touched_vis,
         "stages": stage_lines,
         "views": views,
+        "configs": configs,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
