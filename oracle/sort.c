@@ -1,10 +1,10 @@
 /* Oracle: (tile, depth) key order and tile ranges. TEST INFRASTRUCTURE ONLY.
  *
- * [LOAD-IMB] section 2.1: within each tile the Gaussians are ordered front to
- * back by camera-space depth. [3DGS-CUDA] Step 1 (d): the key is the pair
- * (tile | depth); positive fp32 depths order like their bit patterns.
- * Reading: ties in (tile, depth) are broken by Gaussian id. The order is the
- * total order on (key, id); the C library qsort is the sorting step.
+ * Order of the pairs, as [LOAD-IMB] section 2.1 and [3DGS-CUDA] Step 1 (d)
+ * define it: (tile id, depth bits, Gaussian id) ascending, where the key packs
+ * the tile above the fp32 depth bits (positive depths compare like their bit
+ * patterns) and the Gaussian id breaks ties (a reading: the pages leave ties
+ * open). The C library qsort over (key, id) is the sorting step.
  */
 #include <stdlib.h>
 #include <string.h>
