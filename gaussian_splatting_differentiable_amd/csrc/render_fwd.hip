@@ -158,7 +158,6 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
         r.nh += hit ? 1 : 0;
       }
       bm |= 1ull << j;
-      r.wlast = pos + 1;
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
       const float al = hit ? (CLAMP ? fminf(0.99f, ex) : ex) : 0.0f;
       const float w = al * r.T;
@@ -173,13 +172,14 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
       return alive != 0;
     };
     if (clamp)
-      walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
+      walk_worklist(work, sbuf, [&](const Splat &s, int j) {
         return step(s, j, std::true_type{});
       });
     else
-      walk_worklist<false>(work, sbuf, [&](const Splat &s, int j) {
+      walk_worklist(work, sbuf, [&](const Splat &s, int j) {
         return step(s, j, std::false_type{});
       });
+    if (bm) r.wlast = base + 64 - __builtin_clzll(bm);  // 1 + the last entry any lane blended
     if (lane == 0) cw[base >> 6] = bm;
     wave_sync();
   }
@@ -213,7 +213,7 @@ __device__ __forceinline__ float product_range(const Splat *__restrict__ splats,
     pipe_advance(pp, splats, sids, b, ce, n);
     const int satn = __hip_atomic_load(sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wave_sync();
-    walk_worklist<false>(work, sbuf, [&](const Splat &s, int) {
+    walk_worklist(work, sbuf, [&](const Splat &s, int) {
       const float dx = x.fx - s.p0.x, dy = x.fy - s.p0.y;
       const float q = canon_q(s.p0.z, s.p0.w, s.p1.x, dx, dy);
       const uint64_t hm = alive & wave_ballot(q <= s.p2.y);
