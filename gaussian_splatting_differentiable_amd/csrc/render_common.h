@@ -278,6 +278,16 @@ __device__ __forceinline__ int next_slot(uint64_t w) {
   return j & 63;
 }
 
+// w without slot j, and w with slot j (one scalar instruction each).
+__device__ __forceinline__ uint64_t clear_slot(uint64_t w, int j) {
+  __asm__("s_bitset0_b64 %0, %1" : "+s"(w) : "s"(j));
+  return w;
+}
+__device__ __forceinline__ uint64_t set_slot(uint64_t w, int j) {
+  __asm__("s_bitset1_b64 %0, %1" : "+s"(w) : "s"(j));
+  return w;
+}
+
 // Walk a staged worklist (the set bits of w, lowest slot first) and call
 // f(record, slot) on each until f returns false. The LDS read of the next
 // entry's record is issued before f runs on the current one, so its latency
@@ -287,19 +297,23 @@ template <class Rec, class F>
 __device__ __forceinline__ void walk_worklist(uint64_t w, const Rec *sbuf, F &&f) {
   if (!w) return;
   int j0 = next_slot(w);
-  w &= w - 1;
+  w = clear_slot(w, j0);
   Rec s0 = sbuf[j0];
   for (;;) {
     const bool more1 = w != 0;
     const int j1 = next_slot(w);
-    w &= w - 1;  // an empty set stays empty
+    w = clear_slot(w, j1);  // an empty set stays empty
     const Rec s1 = sbuf[j1];
-    if (!f(s0, j0) || !more1) return;
+    const bool go1 = f(s0, j0);
+    if (!more1) return;
+    if (!go1) return;
     const bool more0 = w != 0;
     j0 = next_slot(w);
-    w &= w - 1;
+    w = clear_slot(w, j0);
     s0 = sbuf[j0];
-    if (!f(s1, j1) || !more0) return;
+    const bool go0 = f(s1, j1);
+    if (!more0) return;
+    if (!go0) return;
   }
 }
 

@@ -157,7 +157,7 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
         nhsteps++;
         r.nh += hit ? 1 : 0;
       }
-      bm |= 1ull << j;
+      bm = set_slot(bm, j);
       const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(q, NEG_HALF_LOG2E, s.p2.w));
       const float al = hit ? (CLAMP ? fminf(0.99f, ex) : ex) : 0.0f;
       const float w = al * r.T;
