@@ -212,6 +212,7 @@ struct Pix2 {
 // one) take the entries of their own quarter's word, back to front (next_pair):
 // a step evaluates one splat for both halves or two different splats, one per
 // half, and a half with no entry in the step reads the dead slot.
+template <bool WIDE>
 __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int n,
                                           const int32_t *__restrict__ sids, int64_t list,
                                           const uint64_t *__restrict__ cw_top, int nb_top,
@@ -219,7 +220,9 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
                                           Pix2 &x, Staged *stage, float *__restrict__ grads) {
   const int lane = __lane_id();
   const bool top = lane < 32;
+  const int upper = top ? 1 : 0;
   const int comp = comp_of_half_lane(lane);
+  const int comp4 = 4 * comp;
   // the constant factor each owner lane applies to its sum after the reduction
   // (powers of two: exact): -1/2 for the two squared offsets
   const float post = (comp == 2 || comp == 4) ? -0.5f : 1.0f;
@@ -273,7 +276,8 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         stage[lane].p0 = q0;
         stage[lane].p1 = p1;
         stage[lane].p2 = p2;
-        stage[lane].p3 = make_int4(idc, valid_id(idc, n) ? 1 : 0, 0, 0);
+        // the gradient row's byte offset (rows of 36 bytes; only when it fits)
+        stage[lane].p3 = make_int4(idc, valid_id(idc, n) ? 1 : 0, WIDE ? 0 : (int)(36u * (uint32_t)idc), 0);
       }
       // records of the next batch, ids of the one after it
       idc = idn;
@@ -295,9 +299,10 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
       }
       wave_sync();
       const int base = 64 * (r0 + mc);
-      // a pixel takes entry j only below its own stop: j < last - base (the
-      // dead slot, j = 64, never hits)
-      const int lim0 = x.last0 - base, lim1 = x.last1 - base;
+      // a pixel takes entry j only below its own stop: j < last - base, here
+      // on the slot's byte offset in the stage, 64 j (the dead slot, j = 64,
+      // never hits)
+      const int lim0 = 64 * (x.last0 - base), lim1 = 64 * (x.last1 - base);
       auto step = [&](auto clamp_t, const Staged &s, int j, bool shared) {
         constexpr bool CLAMP = decltype(clamp_t)::value;
         const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
@@ -309,7 +314,7 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         const float cdy0 = c * dy0, cdy1 = c * dy1;
         const float qa = __builtin_fmaf(cdy0, dy0, __builtin_fmaf(b2dx, dy0, adxdx));
         const float qb = __builtin_fmaf(cdy1, dy1, __builtin_fmaf(b2dx, dy1, adxdx));
-        const bool h0 = j < lim0 && qa <= s.p2.y;
+        const bool h0 = j < lim0 && qa <= s.p2.y;  // j: the slot's byte offset
         const bool h1 = j < lim1 && qb <= s.p2.y;
         // branchless: a missed pixel takes alpha = 0, which leaves T and accum
         // unchanged and contributes zero to every sum
@@ -354,29 +359,45 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         // rather than inside the owner lanes' branch
         __asm__ volatile("" : "+v"(out));
         out *= comp == 5 ? s.p1.y : post;
-        if (comp >= 0 && s.p3.y && (top || !shared))
-          unsafeAtomicAdd(&grads[9 * (int64_t)s.p3.x + comp], out);
+        if (comp >= 0 && s.p3.y && (top || !shared)) {
+          if constexpr (WIDE)
+            unsafeAtomicAdd(&grads[9 * (int64_t)s.p3.x + comp], out);
+          else
+            unsafeAtomicAdd(reinterpret_cast<float *>(reinterpret_cast<char *>(grads) +
+                                                      ((uint32_t)s.p3.z + (uint32_t)comp4)),
+                            out);
+        }
       };
       // the next step's reads from the stage go out before the current step
       // runs (two buffers alternate)
+      // a lane's slot is jt in the upper half and jb in the lower one: its
+      // byte offset 64 jb + upper (64 (jt - jb)), one 24-bit multiply-add on
+      // the vector unit (the rest is scalar)
+      const char *stage_b = reinterpret_cast<const char *>(stage);
+      auto slot_off = [&](const Pair &p) {
+        int t;
+        __asm__("v_mul_i32_i24 %0, %1, %2" : "=v"(t) : "s"(64 * (p.jt - p.jb)), "v"(upper));
+        return t + 64 * p.jb;
+      };
+      auto at = [&](int off) { return *reinterpret_cast<const Staged *>(stage_b + off); };
       auto walk = [&](auto clamp_t) {
         Pair pc = next_pair(wt, wb);
-        int j0 = top ? pc.jt : pc.jb;
+        int j0 = slot_off(pc);
         bool sh0 = pc.shared;
-        Staged s0 = stage[j0];
+        Staged s0 = at(j0);
         for (;;) {
           const bool more1 = (wt | wb) != 0;
           pc = next_pair(wt, wb);
-          const int j1 = top ? pc.jt : pc.jb;
+          const int j1 = slot_off(pc);
           const bool sh1 = pc.shared;
-          const Staged s1 = stage[j1];
+          const Staged s1 = at(j1);
           step(clamp_t, s0, j0, sh0);
           if (!more1) break;
           const bool more0 = (wt | wb) != 0;
           pc = next_pair(wt, wb);
-          j0 = top ? pc.jt : pc.jb;
+          j0 = slot_off(pc);
           sh0 = pc.shared;
-          s0 = stage[j0];
+          s0 = at(j0);
           step(clamp_t, s1, j1, sh1);
           if (!more0) break;
         }
@@ -399,6 +420,9 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
 
 __device__ __forceinline__ int ceil64(int v) { return (max(v, 0) + 63) >> 6; }
 
+// WIDE: the gradient array is larger than 32-bit byte offsets reach (n above
+// 119M), so the atomics take 64-bit addresses.
+template <bool WIDE>
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
 __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const Splat *__restrict__ splats, int n, const int32_t *__restrict__ sorted_ids,
@@ -473,7 +497,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
       x.last1 = in1 ? last[pix1] : 0;
       x.acc0 = ex0;
       x.acc1 = ex1;
-      walk_back(splats, n, sorted_ids, rg.x, contrib_base(fs, qtop, tile, rg.x),
+      walk_back<WIDE>(splats, n, sorted_ids, rg.x, contrib_base(fs, qtop, tile, rg.x),
                 ceil64(fs.sub_last[tile * 4 + qtop]), contrib_base(fs, qbot, tile, rg.x),
                 ceil64(fs.sub_last[tile * 4 + qbot]), x, stage, grads);
       continue;
@@ -520,7 +544,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     x.last1 = lc[1];
     const uint64_t *cw0 = contrib_base(fs, qtop, tile, rg.x) + ((cs - rg.x) >> 6);
     const uint64_t *cw1 = contrib_base(fs, qbot, tile, rg.x) + ((cs - rg.x) >> 6);
-    walk_back(splats, n, sorted_ids, cs, cw0, ceil64(fs.chunk_last[chunk_index(idx, p, qtop, k)]),
+    walk_back<WIDE>(splats, n, sorted_ids, cs, cw0, ceil64(fs.chunk_last[chunk_index(idx, p, qtop, k)]),
               cw1, ceil64(fs.chunk_last[chunk_index(idx, p, qbot, k)]), x, stage, grads);
   }
 }
@@ -542,7 +566,8 @@ hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorte
     const hipError_t e = hipEventRecord(ev0, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_render_bwd, dim3(nblocks),
+  const bool wide = 36 * (int64_t)n >= (int64_t)UINT32_MAX - 64;
+  hipLaunchKernelGGL(wide ? k_render_bwd<true> : k_render_bwd<false>, dim3(nblocks),
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), n, sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
