@@ -31,7 +31,7 @@ EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project"
            "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views",
            "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
            "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views", "gs_timing_start",
-           "gs_timing_read")
+           "gs_timing_read", "gs_set_wait_limit")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -95,13 +95,14 @@ def lib():
     L.gs_render_bwd_views.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P, P]
     L.gs_sort_keys_noalloc.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, P]
     L.gs_timing_start.argtypes = []
+    L.gs_set_wait_limit.argtypes = [i32]
     L.gs_timing_read.argtypes = [i32, C.POINTER(C.c_float), i32]
     for name in ("gs_project", "gs_project_bwd", "gs_project_bf16sh", "gs_project_bwd_bf16sh",
                  "gs_bin_tiles", "gs_render_fwd_bg", "gs_render_bwd_bg", "gs_project_views",
                  "gs_project_bwd_views", "gs_bin_tiles_views", "gs_sort_keys_views",
                  "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views",
-                 "gs_timing_start", "gs_timing_read"):
+                 "gs_timing_start", "gs_timing_read", "gs_set_wait_limit"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -376,6 +377,12 @@ def gs_render_bwd_bg(n, splats, sorted_ids, ranges, cam, T_final, last, fwd_stat
 
 def gs_timing_start():
     _check(lib().gs_timing_start(), "gs_timing_start")
+
+
+def gs_set_wait_limit(probes: int) -> int:
+    """Probe limit of the bounded device-side waits (below 0: their defaults);
+    returns the previous setting. For tests of the give-up path."""
+    return int(lib().gs_set_wait_limit(int(probes)))
 
 
 def gs_timing_read(which: int, cap: int = 512):

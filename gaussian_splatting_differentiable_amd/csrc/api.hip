@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation, camera preparation, workspace and
 // forward-state layout, and the kernel launches of each stage. The functions
 // are declared (with their contracts) in include/gs.h.
+#include <atomic>
 #include <math.h>
 #include <string.h>
 
@@ -39,6 +40,15 @@ hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorte
                                 const int32_t *last, void *fwd_state, const float *dL,
                                 const float *dT, float *grads, int32_t *status, int workers_waves,
                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
+
+// The probe limit of the device-side bounded waits (below 0: each wait's own
+// default). Only tests of the give-up path change it.
+static std::atomic<int32_t> g_wait_limit{-1};
+
+int32_t gs_wait_limit(int32_t fallback) {
+  const int32_t v = g_wait_limit.load(std::memory_order_relaxed);
+  return v < 0 ? fallback : v;
+}
 
 namespace {
 
@@ -636,6 +646,10 @@ int32_t gs_sort_keys_noalloc(int32_t n, const float *splats, const gs_camera *ca
   if (e != hipSuccess) return GS_ERR_HIP;
   return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
                                    tile_ranges, device_status, ws, st));
+}
+
+int32_t gs_set_wait_limit(int32_t probes) {
+  return g_wait_limit.exchange(probes < 0 ? -1 : probes, std::memory_order_relaxed);
 }
 
 int32_t gs_timing_start(void) {

@@ -253,7 +253,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
     int32_t *__restrict__ last, char *__restrict__ state, int T,
     unsigned long long *__restrict__ stats, int32_t *__restrict__ pixel_hits,
-    int32_t *__restrict__ status) {
+    int32_t *__restrict__ status, int spin_limit) {
   __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
   Splat *sbuf = sbuf_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, T);
@@ -321,7 +321,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       for (int q = 0; q < p && ok; q++) {
         int spins = 0;
         while (ld_flag(&fs.doneA[chunk_index(idx, q, quad, k)]) == 0) {
-          if (++spins > GS_SPIN_LIMIT) {
+          if (++spins > spin_limit) {
             atomicOr(&fs.hdr->err, 1);
             report_status(status, GS_ERR_TIMEOUT);
             ok = 0;
@@ -420,6 +420,8 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, cons
                               int64_t *stats, int32_t *status, int64_t cap_pairs,
                               hipStream_t st);
 
+int32_t gs_wait_limit(int32_t fallback);
+
 hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
@@ -441,7 +443,8 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                      reinterpret_cast<const Splat *>(splats), n, sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,
-                     reinterpret_cast<unsigned long long *>(stats), pixel_hits, status);
+                     reinterpret_cast<unsigned long long *>(stats), pixel_hits, status,
+                     gs_wait_limit(GS_SPIN_LIMIT));
   e = hipGetLastError();
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
   return e;

@@ -459,6 +459,7 @@ struct PassIn {
   int32_t *tile_counts, *ranges;
   int b0;
   int32_t *status;             // the frame's device status (bounded waits report here)
+  int spin_limit;              // probes before a look-back wait gives up
 };
 
 template <int NT, int ITEMS, int BITS, int SRC>
@@ -507,10 +508,20 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     const int n_pre = SRC == SRC_DEPTH0 ? n_max : clamp_n(*n_dev, n_max);
     if ((int64_t)blockIdx.x * PART >= (int64_t)n_pre) return;
   }
-  if (tid == 0) s_part = atomicAdd(ticket, 1);
+  // after the first pass, a frame that has failed (here or in a call beside
+  // this one) sorts no further: its earlier passes may have left positions
+  // unwritten, and nothing downstream reads them. The status and the ticket
+  // are read together; a partition that stops never publishes, and a later one
+  // waiting for it stops as soon as it sees the status.
+  if (tid == 0) {
+    const int st = SRC != SRC_DEPTH0 ? *in.status : GS_OK;
+    const int t = atomicAdd(ticket, 1);
+    s_part = st != GS_OK ? -1 : t;
+  }
   for (int i = tid; i < NWV * B; i += NT) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
   const int part = s_part;
+  if (part < 0) return;
   const int n = SRC == SRC_DEPTH0 ? n_max : clamp_n(*n_dev, n_max);
   const int64_t p0 = (int64_t)part * PART;
   if constexpr (SRC == SRC_DEPTH0) {
@@ -669,7 +680,10 @@ __global__ void __launch_bounds__(NT) k_onesweep(
         if (done) break;
         p -= used;
         if (used < LBW) {  // stopped at an unpublished predecessor
-          if (++spins > SPIN_LIMIT) {
+          // a frame that failed meanwhile may leave it unpublished for good
+          if (__hip_atomic_load(in.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != GS_OK)
+            break;
+          if (++spins > in.spin_limit) {
             atomicOr(err, 1);
             report_status(in.status, GS_ERR_TIMEOUT);
             break;
@@ -710,10 +724,21 @@ __global__ void __launch_bounds__(NT) k_onesweep(
 
 // ---------------------------------------------------------------- depth-ordered pair offsets
 
+// Whether the frame still runs, read once per workgroup (the status word only
+// ever leaves GS_OK, so every thread of the block takes the same branch).
+__device__ __forceinline__ bool frame_ok(const int32_t *status) {
+  __shared__ int ok;
+  if (threadIdx.x == 0) ok = *status == GS_OK;
+  __syncthreads();
+  return ok != 0;
+}
+
 __global__ void __launch_bounds__(SCAN_T) k_dscan_reduce(const SortCtl *__restrict__ ctl,
                                                          int n_max,
                                                          const int32_t *__restrict__ dcnt,
-                                                         int32_t *__restrict__ bsum) {
+                                                         int32_t *__restrict__ bsum,
+                                                         const int32_t *__restrict__ status) {
+  if (!frame_ok(status)) return;
   const int m = clamp_n(ctl->m, n_max);
   const int base = blockIdx.x * SCAN_TILE;
   int v = 0;
@@ -734,7 +759,9 @@ __global__ void __launch_bounds__(SCAN_T) k_dscan_apply(SortCtl *__restrict__ ct
                                                         const int32_t *__restrict__ dcnt,
                                                         const int32_t *__restrict__ bsum,
                                                         int32_t *__restrict__ doff,
-                                                        int32_t *__restrict__ part_first) {
+                                                        int32_t *__restrict__ part_first,
+                                                        const int32_t *__restrict__ status) {
+  if (!frame_ok(status)) return;
   const int m = clamp_n(ctl->m, n_max);
   const int nb = (m + SCAN_TILE - 1) / SCAN_TILE;
   if ((int)blockIdx.x > nb) return;
@@ -783,7 +810,9 @@ __global__ void __launch_bounds__(256) k_sorted_keys(const SortCtl *__restrict__
                                                      const uint32_t *__restrict__ tiles,
                                                      const uint32_t *__restrict__ ids,
                                                      const Splat *__restrict__ splats,
-                                                     uint64_t *__restrict__ out) {
+                                                     uint64_t *__restrict__ out,
+                                                     const int32_t *__restrict__ status) {
+  if (!frame_ok(status)) return;
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= clamp_n(ctl->npairs, cap)) return;
   out[k] = ((uint64_t)tiles[k] << 32) | (uint64_t)__float_as_uint(splats[ids[k]].p2.z);
@@ -824,6 +853,8 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
   return hipGetLastError();
 }
 
+int32_t gs_wait_limit(int32_t fallback);
+
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
                           int32_t *ranges, int32_t *status, void *ws, hipStream_t st) {
@@ -842,6 +873,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   PassIn in{};
   in.ctl = ctl;
   in.status = status;
+  in.spin_limit = gs_wait_limit(SPIN_LIMIT);
 
   // depth sort of the visible splats: 4 passes of 8 bits; the last also writes
   // each splat's pair count in depth order. The first pass has one extra
@@ -880,9 +912,10 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   const uint32_t *dval = w.dv[cur];
   // pair offsets in depth order and the first splat of every tile partition
   const int nb = gs_div_up(n > 0 ? n : 1, SCAN_TILE);
-  hipLaunchKernelGGL(k_dscan_reduce, dim3(nb), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum);
+  hipLaunchKernelGGL(k_dscan_reduce, dim3(nb), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum,
+                     status);
   hipLaunchKernelGGL(k_dscan_apply, dim3(nb + 1), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum,
-                     w.doff, w.part_first);
+                     w.doff, w.part_first, status);
   int tbits = 1;
   while ((1 << tbits) < ntiles) tbits++;
   // tile passes: the first generates its partition's pairs itself
@@ -918,6 +951,6 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   if (sorted_keys)
     hipLaunchKernelGGL(k_sorted_keys, dim3(gs_div_up(cap > 0 ? cap : 1, 256)), dim3(256), 0, st,
                        ctl, capi, final_tiles, reinterpret_cast<const uint32_t *>(sorted_ids), sp,
-                       sorted_keys);
+                       sorted_keys, status);
   return hipGetLastError();
 }

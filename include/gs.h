@@ -13,9 +13,12 @@
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
- *     The library allocates nothing. Its only global mutable state is the
- *     optional measurement timer (gs_timing_start / gs_timing_read); apart from
- *     it, calls on different streams with their own buffers are independent.
+ *     The library allocates nothing. Its global mutable state is the optional
+ *     measurement timer (gs_timing_start / gs_timing_read), the probe limit of
+ *     the bounded device-side waits (gs_set_wait_limit, for tests of the
+ *     give-up path) and the static device array of gs_sort_keys_noalloc; apart
+ *     from these, calls on different streams with their own buffers are
+ *     independent.
  *   - `stream` is a hipStream_t (NULL = the default stream). Each call only
  *     enqueues kernels on it and returns; it never synchronises.
  *   - Synchronous errors (argument validation, HIP launch errors) return a
@@ -415,6 +418,18 @@ int32_t gs_sort_keys_noalloc(int32_t n, const float *splats, const gs_camera *ca
  *   number written, or GS_ERR_INVALID_ARGUMENT / GS_ERR_HIP. */
 int32_t gs_timing_start(void);
 int32_t gs_timing_read(int32_t which, float *ms, int32_t cap);
+
+/* The bounded device-side waits (the sort's look-back over earlier partitions,
+ * a chunk's wait for the chunks in front of it) give up after a number of
+ * probes and store GS_ERR_TIMEOUT in the frame's status word; the frame's later
+ * kernels then do nothing. For tests of that path (a caller that wants every
+ * wait to give up at its first unsuccessful probe sets 0):
+ *   probes >= 0: the limit for the calls enqueued from now on;
+ *   probes < 0: each wait's own default (1 << 22 probes in the sort, 1 << 20 in
+ *               the forward, seconds at the longest back-off).
+ * Returns the previous setting (-1 for the defaults). Host-side state shared by
+ * every device and thread of the process. */
+int32_t gs_set_wait_limit(int32_t probes);
 
 #ifdef __cplusplus
 }

@@ -137,6 +137,11 @@ def test_argument_validation_needs_no_gpu(gsr):
     assert L.gs_bin_tiles(10, C.c_void_p(16), C.byref(cam), 100, C.c_void_p(16), None,
                           C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), 8,
                           None) == -3
+    # the wait limit is host state: set, read back, restored
+    prev = L.gs_set_wait_limit(5)
+    assert prev == -1
+    assert L.gs_set_wait_limit(-3) == 5
+    assert L.gs_set_wait_limit(-1) == -1
     # a misaligned tile-count array
     assert L.gs_bin_tiles(10, p16, C.byref(cam), 100, p16, C.c_void_p(18), None, None, p16, p16,
                           1 << 30, None) == -1
