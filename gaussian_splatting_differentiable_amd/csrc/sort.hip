@@ -944,9 +944,16 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
                        0, st, nullptr, nullptr, w.tk[0], w.tv[0], i_dev, capi, 0, tbase(0),
                        status_t0, ticket(4), err, e);
     final_tiles = sorted_keys ? w.tk[1] : nullptr;
-    hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 8, SRC_KEYS>), dim3(npt), dim3(TS_THREADS),
-                       0, st, w.tk[0], w.tv[0], final_tiles, ids_out, i_dev, capi, b0, tbase(1),
-                       status_t1, ticket(5), err, in);
+    // the high digit has tbits - 8 significant bits: rank on 5 of them when
+    // they fit (up to 8192 tiles), which cuts the ballots and the look-back
+    if (tbits - b0 <= 5)
+      hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 5, SRC_KEYS>), dim3(npt),
+                         dim3(TS_THREADS), 0, st, w.tk[0], w.tv[0], final_tiles, ids_out, i_dev,
+                         capi, b0, tbase(1), status_t1, ticket(5), err, in);
+    else
+      hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 8, SRC_KEYS>), dim3(npt),
+                         dim3(TS_THREADS), 0, st, w.tk[0], w.tv[0], final_tiles, ids_out, i_dev,
+                         capi, b0, tbase(1), status_t1, ticket(5), err, in);
   }
   if (sorted_keys)
     hipLaunchKernelGGL(k_sorted_keys, dim3(gs_div_up(cap > 0 ? cap : 1, 256)), dim3(256), 0, st,
