@@ -9,14 +9,18 @@
 //
 // gs_bin_tiles counts every splat's pairs with the canonical row spans and, in
 // the same pass over the splat records, leaves in the workspace what the sort
-// needs: each splat's 32-bit depth key (or "no pairs"), the four depth-digit
-// histograms and the per-tile pair counts (LDS histograms per workgroup). It
-// also clears the look-back words of every radix pass of the frame.
+// needs: each splat's 32-bit depth key (or "no pairs"), the histograms of the
+// two low 9-bit depth digits, the range of the keys' exponent field and the
+// per-tile pair counts (LDS histograms per workgroup). It also clears the
+// look-back words of every radix pass of the frame.
 //
 // gs_sort_keys then runs:
-//   - four onesweep LSD passes over the visible splats' depth keys (6144-key
-//     partitions), the last of which also writes each splat's pair count in
-//     depth order;
+//   - three onesweep LSD passes of 9 bits over the visible splats' depth keys
+//     less the smallest exponent (key - (emin << 23): the depths are positive,
+//     so the order is kept, and 27 bits hold every key when the exponents span
+//     fewer than 16 values), and a fourth over bits 27-31 that runs only when
+//     they span more (6144-key partitions); the last also writes each splat's
+//     pair count in depth order;
 //   - an exclusive scan of those counts: the pair offsets in depth order, and
 //     for every 16384-pair partition the splat its first pair belongs to;
 //   - the first tile pass (low 8 bits of the tile id) with the emission fused
@@ -68,8 +72,13 @@ struct SortCtl {
   int32_t tag_n, tag_tiles_x, tag_tiles_y;
   int64_t tag_cap;
   int32_t tickets[8];      // partition tickets, one per radix pass
-  uint32_t dhist[4][256];  // depth digit histograms
-  uint32_t dbase[4][256];  // depth digit exclusive offsets
+  // Depth keys are sorted as key - (emin << 23), which keeps their order (the
+  // depths are positive): 9-bit digits at bits 0, 9 and 18, and bits 27-31 in
+  // a fourth pass only when the keys' exponent field spans 16 values or more.
+  uint32_t dhist[3][512];  // digit histograms (0, 1: binning pass; 2: first depth pass)
+  uint32_t dhist3[32];     // bits 27-31 (first depth pass, wide frames only)
+  int32_t emin, emax;      // the visible keys' exponent field range
+  int32_t wide;            // the fourth depth pass runs
   uint32_t tbase[2][256];  // tile digit exclusive offsets
 };
 
@@ -124,6 +133,7 @@ struct SortWs {
   int32_t *tile_diff;       // tiles_y x (tiles_x + 1): per-row difference array of pair counts
   uint32_t *dkey;           // n: depth key per splat (NO_DEPTH without pairs)
   uint32_t *dk[2], *dv[2];  // n each: depth passes
+  uint32_t *dfinal;         // n: splat ids in depth order (the last depth pass's output)
   int32_t *dcnt;            // n: pair counts in depth order
   int32_t *doff;            // n + 1: pair offsets in depth order
   int32_t *part_first;      // tile partitions: the splat (depth rank) of the first pair
@@ -152,13 +162,14 @@ SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y) {
   w.dkey = (uint32_t *)take(4 * n2);
   for (int i = 0; i < 2; i++) w.dk[i] = (uint32_t *)take(4 * n2);
   for (int i = 0; i < 2; i++) w.dv[i] = (uint32_t *)take(4 * n2);
+  w.dfinal = (uint32_t *)take(4 * n2);
   w.dcnt = (int32_t *)take(4 * n2);
   w.doff = (int32_t *)take(4 * n2);
   w.part_first = (int32_t *)take(4 * (parts_of(cap, TS_PART) + 2));
   w.bsum = (int32_t *)take(4 * ((int64_t)n / SCAN_TILE + 4));
   for (int i = 0; i < 2; i++) w.tk[i] = (uint32_t *)take(4 * (cap + 2));
   for (int i = 0; i < 2; i++) w.tv[i] = (uint32_t *)take(4 * (cap + 2));
-  w.pd = (parts_of(n, DS_PART) + 1) * 256;
+  w.pd = (parts_of(n, DS_PART) + 1) * 512;
   w.pt = (parts_of(cap, TS_PART) + 1) * 256;
   w.nstatus = 4 * w.pd + 2 * w.pt;
   w.status = (uint32_t *)take(4 * w.nstatus);
@@ -179,6 +190,7 @@ __global__ void __launch_bounds__(1024) k_bin_init(SortCtl *__restrict__ ctl,
   for (int i = threadIdx.x; i < ndiff; i += blockDim.x) tile_diff[i] = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
+    ctl->emin = 255;
     ctl->tag_n = n;
     ctl->tag_cap = cap;
     ctl->tag_tiles_x = tiles_x;
@@ -197,11 +209,17 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
     int views, int32_t *__restrict__ counts, int chunk, int32_t *__restrict__ bin_sum,
     uint32_t *__restrict__ dkey, SortCtl *__restrict__ ctl, int32_t *__restrict__ tile_diff,
     uint32_t *__restrict__ status, int64_t nstatus, bool lds_hist) {
-  __shared__ uint32_t dh[4][256];
+  __shared__ uint32_t dh[2][512];
+  __shared__ int s_emin, s_emax;
   extern __shared__ int th[];  // the difference array, when lds_hist (sized at launch)
   const int stride = tiles_x + 1;
   const int ndiff = tiles_y * stride;
   for (int i = threadIdx.x; i < 1024; i += BIN_T) (&dh[0][0])[i] = 0;
+  if (threadIdx.x == 0) {
+    s_emin = 255;
+    s_emax = 0;
+  }
+  int emin = 255, emax = 0;
   if (lds_hist)
     for (int i = threadIdx.x; i < ndiff; i += BIN_T) th[i] = 0;
   for (int64_t i = (int64_t)blockIdx.x * BIN_T + threadIdx.x; i < nstatus;
@@ -232,25 +250,33 @@ __global__ void __launch_bounds__(BIN_T) k_bin_count(
     uint32_t k = NO_DEPTH;
     if (cnt > 0) {
       k = __float_as_uint(s.p2.z);
-#pragma unroll
-      for (int p = 0; p < 3; p++) atomicAdd(&dh[p][(k >> (8 * p)) & 255], 1u);
+      atomicAdd(&dh[0][k & 511u], 1u);
+      atomicAdd(&dh[1][(k >> 9) & 511u], 1u);
+      const int e = (int)((k >> 23) & 255u);
+      emin = min(emin, e);
+      emax = max(emax, e);
     }
     dkey[i] = k;
-    // the top digit (sign and high exponent bits) takes a handful of values in
-    // a frame: count it once per distinct value in the wave, not per lane
-    uint64_t todo = __ballot(cnt > 0);
-    const uint32_t d3 = k >> 24;
-    while (todo) {
-      const int leader = __builtin_ctzll(todo);
-      const uint32_t dl = (uint32_t)__shfl((int)d3, leader, 64);
-      const uint64_t same = __ballot(cnt > 0 && d3 == dl) & todo;
-      if (__lane_id() == leader) atomicAdd(&dh[3][dl], (uint32_t)__popcll(same));
-      todo &= ~same;
-    }
+  }
+  // the block's exponent range: a wave reduction, then one LDS atomic per wave
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    emin = min(emin, __shfl_xor(emin, o, 64));
+    emax = max(emax, __shfl_xor(emax, o, 64));
+  }
+  if ((threadIdx.x & 63) == 0 && emin <= emax) {
+    atomicMin(&s_emin, emin);
+    atomicMax(&s_emax, emax);
   }
   int ctot;
   block_scan<BIN_T>(csum, ctot);  // ends with a barrier: the LDS histograms are complete
-  if (threadIdx.x == 0) bin_sum[blockIdx.x] = ctot;
+  if (threadIdx.x == 0) {
+    bin_sum[blockIdx.x] = ctot;
+    if (s_emin <= s_emax) {
+      atomicMin(&ctl->emin, s_emin);
+      atomicMax(&ctl->emax, s_emax);
+    }
+  }
   for (int i = threadIdx.x; i < 1024; i += BIN_T) {
     const uint32_t v = (&dh[0][0])[i];
     if (v) atomicAdd(&ctl->dhist[0][0] + i, v);
@@ -362,15 +388,16 @@ __device__ void tile_bases_block(SortCtl *__restrict__ ctl, const int32_t *__res
   const int ntiles = tiles_x * tiles_y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   // the frame's sort state for the later passes: visible splats, the overflow
-  // flag and the depth digit offsets (an overflowing frame sorts nothing)
-  for (int p = 0; p < 4; p++) {
-    const int v = (threadIdx.x < 256 && !overflow) ? (int)ctl->dhist[p][threadIdx.x] : 0;
+  // flag and whether the depth keys need the fourth pass (an overflowing frame
+  // sorts nothing)
+  {
+    const int v = (threadIdx.x < 512 && !overflow) ? (int)ctl->dhist[0][threadIdx.x] : 0;
     int tot;
-    const int incl = block_scan<1024>(v, tot);
-    if (threadIdx.x < 256) ctl->dbase[p][threadIdx.x] = (uint32_t)(incl - v);
-    if (p == 0 && threadIdx.x == 0) {
+    block_scan<1024>(v, tot);
+    if (threadIdx.x == 0) {
       ctl->m = tot;
       ctl->overflow = overflow ? 1 : 0;
+      ctl->wide = !overflow && tot > 0 && ctl->emax - ctl->emin > 15;
     }
   }
   // per-tile counts: every row of the difference array sums to zero (each span
@@ -440,7 +467,9 @@ __device__ void tile_bases_block(SortCtl *__restrict__ ctl, const int32_t *__res
   if (threadIdx.x <= (int)mask0) ctl->tbase[0][threadIdx.x] = (uint32_t)(incl - v);
 }
 
-enum Src { SRC_KEYS = 0, SRC_DEPTH0 = 1, SRC_EMIT = 2 };
+// SRC_WIDE: the fourth depth pass, which does nothing unless the frame's
+// depth keys need it.
+enum Src { SRC_KEYS = 0, SRC_DEPTH0 = 1, SRC_EMIT = 2, SRC_WIDE = 3 };
 
 // Inputs of one pass beyond the (key, value) arrays.
 struct PassIn {
@@ -459,6 +488,8 @@ struct PassIn {
   int32_t *tile_counts, *ranges;
   int b0;
   int32_t *status;             // the frame's device status (bounded waits report here)
+  const uint32_t *dhist_in;    // depth passes: this pass's digit histogram (offsets made in-block)
+  uint32_t *wide_kout, *wide_vout;  // third depth pass: its output when the fourth pass runs
   int spin_limit;              // probes before a look-back wait gives up
 };
 
@@ -478,12 +509,16 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __shared__ uint32_t s_gbase[B];
   __shared__ int s_part, s_nvalid;
   __shared__ uint32_t s_mark[SRC == SRC_EMIT ? PART / 32 : 1];
+  __shared__ uint32_t s_h2[SRC == SRC_DEPTH0 ? 512 : 1], s_h3[SRC == SRC_DEPTH0 ? 32 : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // the first depth pass takes its digit offsets and the number of visible
-  // splats from the binning pass's histogram itself
+  // a depth pass takes its digit offsets (and the first one the number of
+  // visible splats) from its digit histogram itself
   uint32_t dbase0 = 0;
   int m0 = 0;
   bool overflow = false;
+  if constexpr (SRC == SRC_WIDE) {
+    if (!in.ctl->wide) return;  // the frame's keys fit three passes
+  }
   if constexpr (SRC == SRC_DEPTH0) {
     static_assert(SRC != SRC_DEPTH0 || NT == 1024, "the tile-bases workgroup has 1024 threads");
     // a frame sorts nothing when its pairs overflowed, an earlier call failed,
@@ -498,7 +533,9 @@ __global__ void __launch_bounds__(NT) k_onesweep(
                        in.tiles_y, in.b0, in.ranges, overflow);
       return;
     }
-    const int v = (tid < B && !overflow) ? (int)in.ctl->dhist[0][tid] : 0;
+  }
+  if (in.dhist_in) {
+    const int v = (tid < B && !overflow) ? (int)in.dhist_in[tid] : 0;
     const int incl = block_scan<NT>(v, m0);
     dbase0 = (uint32_t)(incl - v);
   }
@@ -519,6 +556,10 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     s_part = st != GS_OK ? -1 : t;
   }
   for (int i = tid; i < NWV * B; i += NT) (&s_wcnt[0][0])[i] = 0;
+  if constexpr (SRC == SRC_DEPTH0) {
+    for (int i = tid; i < 512; i += NT) s_h2[i] = 0;
+    if (tid < 32) s_h3[tid] = 0;
+  }
   __syncthreads();
   const int part = s_part;
   if (part < 0) return;
@@ -581,6 +622,8 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     }
     __syncthreads();
   }
+  const int emin = SRC == SRC_DEPTH0 ? in.ctl->emin : 0;
+  const bool wide = SRC == SRC_DEPTH0 && in.ctl->emax - emin > 15;
   const int64_t base = p0 + (int64_t)w * (ITEMS * 64);
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t key[ITEMS], val[ITEMS];
@@ -593,6 +636,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     if (e < n) {
       if constexpr (SRC == SRC_DEPTH0) {
         k = in.dkey[e];
+        if (k != NO_DEPTH) k -= (uint32_t)emin << 23;  // order kept: positive depths
         v = (uint32_t)e;
       } else if constexpr (SRC == SRC_EMIT) {
         // the nearest row start at or before this pair (position 0 always
@@ -633,8 +677,20 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     }
     key[r] = k;
     rnk[r] = wr;
+    if constexpr (SRC == SRC_DEPTH0) {
+      if (valid) {
+        atomicAdd(&s_h2[(k >> 18) & 511u], 1u);
+        if (wide) atomicAdd(&s_h3[(k >> 27) & 31u], 1u);
+      }
+    }
   }
   __syncthreads();
+  if constexpr (SRC == SRC_DEPTH0) {
+    SortCtl *c = const_cast<SortCtl *>(in.ctl);
+    for (int i = tid; i < 512; i += NT)
+      if (s_h2[i]) atomicAdd(&c->dhist[2][i], s_h2[i]);
+    if (tid < 32 && s_h3[tid]) atomicAdd(&c->dhist3[tid], s_h3[tid]);
+  }
   // per digit: exclusive prefix over the waves and the block total
   int total = 0;
   if (tid < B) {
@@ -693,7 +749,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
       }
       st_status(&status[me], ST_INC | (excl + (uint32_t)total));
     }
-    s_gbase[tid] = (SRC == SRC_DEPTH0 ? dbase0 : digit_base[tid]) + excl;
+    s_gbase[tid] = (in.dhist_in ? dbase0 : digit_base[tid]) + excl;
   }
   if (tid == 0) s_nvalid = ntot;
   __syncthreads();
@@ -710,15 +766,19 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __syncthreads();
   const int nv = s_nvalid;
   const int bound = SRC == SRC_DEPTH0 ? m0 : n;
+  // the third depth pass hands its keys to the fourth when that one runs
+  const bool handoff = in.wide_vout && in.ctl->wide;
+  uint32_t *ko = handoff ? in.wide_kout : kout, *vo = handoff ? in.wide_vout : vout;
+  int32_t *co = handoff ? nullptr : in.cout;
   for (int i = tid; i < nv; i += NT) {
     const uint32_t k = s_key[i];
     const uint32_t d = (k >> shift) & (B - 1);
     const uint32_t dst = s_gbase[d] + (uint32_t)(i - s_lbase[d]);
     if (dst >= (uint32_t)bound) continue;  // only after a look-back bound was hit (err is set)
-    if (kout) kout[dst] = k;
+    if (ko) ko[dst] = k;
     const uint32_t v = s_val[i];
-    vout[dst] = v;
-    if (in.cout) in.cout[dst] = in.offsets[v + 1] - in.offsets[v];
+    vo[dst] = v;
+    if (co) co[dst] = in.offsets[v + 1] - in.offsets[v];
   }
 }
 
@@ -863,7 +923,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
   SortCtl *ctl = w.ctl;
   char *cb = reinterpret_cast<char *>(ctl);
-  auto dbase = [&](int p) { return reinterpret_cast<uint32_t *>(cb + offsetof(SortCtl, dbase)) + 256 * p; };
+  auto dhist = [&](int p) { return reinterpret_cast<const uint32_t *>(cb + offsetof(SortCtl, dhist)) + 512 * p; };
   auto tbase = [&](int p) { return reinterpret_cast<uint32_t *>(cb + offsetof(SortCtl, tbase)) + 256 * p; };
   auto ticket = [&](int p) { return reinterpret_cast<int32_t *>(cb + offsetof(SortCtl, tickets)) + p; };
   int32_t *err = reinterpret_cast<int32_t *>(cb + offsetof(SortCtl, err));
@@ -875,10 +935,12 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   in.status = status;
   in.spin_limit = gs_wait_limit(SPIN_LIMIT);
 
-  // depth sort of the visible splats: 4 passes of 8 bits; the last also writes
-  // each splat's pair count in depth order. The first pass has one extra
-  // workgroup that turns the binning pass's difference array into tile counts,
-  // tile ranges and the tile-digit offsets.
+  // depth sort of the visible splats by key - (emin << 23): three passes of 9
+  // bits, and a fourth over bits 27-31 that runs only when the keys' exponents
+  // span 16 values or more (the third then hands its output to it); the last
+  // pass also writes each splat's pair count in depth order. The first pass
+  // has one extra workgroup that turns the binning pass's difference array
+  // into tile counts, tile ranges and the tile-digit offsets.
   const int npd = (int)(parts_of(n, DS_PART) > 1 ? parts_of(n, DS_PART) : 1);
   const int b0 = 8;
   {
@@ -892,24 +954,39 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
     a.tiles_x = cam.tiles_x;
     a.tiles_y = cam.tiles_y;
     a.b0 = b0;
-    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_DEPTH0>), dim3(npd + 1),
+    a.dhist_in = dhist(0);
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 9, SRC_DEPTH0>), dim3(npd + 1),
                        dim3(DS_THREADS), 0, st, nullptr, nullptr, w.dk[1], w.dv[1], nullptr, n, 0,
                        nullptr, w.status, ticket(0), err, a);
   }
-  int cur = 1;
-  for (int pass = 1; pass < 4; pass++) {
+  {
     PassIn a = in;
-    if (pass == 3) {
-      a.offsets = offsets;
-      a.cout = w.dcnt;
-    }
-    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 8, SRC_KEYS>), dim3(npd), dim3(DS_THREADS),
-                       0, st, w.dk[cur], w.dv[cur], pass == 3 ? nullptr : w.dk[cur ^ 1],
-                       w.dv[cur ^ 1], m_dev, n, 8 * pass, dbase(pass), w.status + pass * w.pd,
-                       ticket(pass), err, a);
-    cur ^= 1;
+    a.dhist_in = dhist(1);
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 9, SRC_KEYS>), dim3(npd),
+                       dim3(DS_THREADS), 0, st, w.dk[1], w.dv[1], w.dk[0], w.dv[0], m_dev, n, 9,
+                       nullptr, w.status + w.pd, ticket(1), err, a);
   }
-  const uint32_t *dval = w.dv[cur];
+  {
+    PassIn a = in;
+    a.dhist_in = dhist(2);
+    a.offsets = offsets;
+    a.cout = w.dcnt;
+    a.wide_kout = w.dk[1];
+    a.wide_vout = w.dv[1];
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 9, SRC_KEYS>), dim3(npd),
+                       dim3(DS_THREADS), 0, st, w.dk[0], w.dv[0], nullptr, w.dfinal, m_dev, n, 18,
+                       nullptr, w.status + 2 * w.pd, ticket(2), err, a);
+  }
+  {
+    PassIn a = in;
+    a.dhist_in = reinterpret_cast<const uint32_t *>(cb + offsetof(SortCtl, dhist3));
+    a.offsets = offsets;
+    a.cout = w.dcnt;
+    hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 5, SRC_WIDE>), dim3(npd),
+                       dim3(DS_THREADS), 0, st, w.dk[1], w.dv[1], nullptr, w.dfinal, m_dev, n, 27,
+                       nullptr, w.status + 3 * w.pd, ticket(3), err, a);
+  }
+  const uint32_t *dval = w.dfinal;
   // pair offsets in depth order and the first splat of every tile partition
   const int nb = gs_div_up(n > 0 ? n : 1, SCAN_TILE);
   hipLaunchKernelGGL(k_dscan_reduce, dim3(nb), dim3(SCAN_T), 0, st, ctl, n, w.dcnt, w.bsum,

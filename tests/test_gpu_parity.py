@@ -217,6 +217,31 @@ def test_large_splats_sort_matches_oracle():
     assert np.array_equal(host(r.ranges), ref["ranges"])
 
 
+def test_depth_range_beyond_sixteen_exponents_sorts_exactly():
+    """Depths from about 0.3 to about 30,000: the keys' fp32 exponents span 16
+    values or more, so the depth sort needs its fourth pass (bits 27-31 of the
+    key less the smallest exponent). Half of the splats are moved 10^4 times
+    farther, with positions and scales grown alike so that they stay on screen."""
+    gsr = _gsr()
+    sc = scenegen.random_scene(107, 3000, 150, 110, 150.0, depth=(0.3, 3.0),
+                               log_scale=(-2.5, 0.3))
+    far = np.arange(sc.n) % 2 == 1
+    sc.means[far] *= np.float32(1.0e4)
+    sc.log_scales[far] += np.float32(np.log(1.0e4))
+    ref = oracle.frame(sc, fwd=False)
+    vis = np.diff(ref["offsets"]) > 0
+    e = (ref["splats"][vis, 10].view(np.uint32) >> np.uint32(23)) & np.uint32(255)
+    assert int(e.max()) - int(e.min()) >= 16, (int(e.min()), int(e.max()))
+    r = gsr.Rasterizer(sc.camera, capacity=len(ref["sorted_ids"]))
+    r._ensure(sc.n, len(ref["sorted_ids"]))
+    r.splats[:sc.n].copy_(dev(ref["splats"]))
+    I = r.bin_and_sort(sc.n, want_keys=True)
+    assert I == len(ref["sorted_ids"])
+    assert np.array_equal(host(r.sorted_keys)[:I].view(np.uint64), ref["sorted_keys"])
+    assert np.array_equal(host(r.sorted_ids)[:I], ref["sorted_ids"])
+    assert np.array_equal(host(r.ranges), ref["ranges"])
+
+
 def test_capacity_overflow_reports_and_recovers():
     gsr = _gsr()
     sc, ref = reference(1)
