@@ -75,7 +75,10 @@ struct SortCtl {
   // Depth keys are sorted as key - (emin << 23), which keeps their order (the
   // depths are positive): 9-bit digits at bits 0, 9 and 18, and bits 27-31 in
   // a fourth pass only when the keys' exponent field spans 16 values or more.
-  uint32_t dhist[3][512];  // digit histograms (0, 1: binning pass; 2: first depth pass)
+  uint32_t dhist[2][512];  // digit histograms 0 and 1 (binning pass)
+  // digit 2, by the first depth pass: eight copies (workgroup index mod 8), so
+  // that its workgroups' additions spread over eight times as many addresses
+  uint32_t dhist2[8][512];
   uint32_t dhist3[32];     // bits 27-31 (first depth pass, wide frames only)
   int32_t emin, emax;      // the visible keys' exponent field range
   int32_t wide;            // the fourth depth pass runs
@@ -489,6 +492,7 @@ struct PassIn {
   int b0;
   int32_t *status;             // the frame's device status (bounded waits report here)
   const uint32_t *dhist_in;    // depth passes: this pass's digit histogram (offsets made in-block)
+  int dhist_copies;            // ... as this many copies, B apart, to be summed
   uint32_t *wide_kout, *wide_vout;  // third depth pass: its output when the fourth pass runs
   int spin_limit;              // probes before a look-back wait gives up
 };
@@ -535,7 +539,9 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     }
   }
   if (in.dhist_in) {
-    const int v = (tid < B && !overflow) ? (int)in.dhist_in[tid] : 0;
+    int v = 0;
+    if (tid < B && !overflow)
+      for (int c = 0; c < in.dhist_copies; c++) v += (int)in.dhist_in[c * B + tid];
     const int incl = block_scan<NT>(v, m0);
     dbase0 = (uint32_t)(incl - v);
   }
@@ -687,8 +693,9 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __syncthreads();
   if constexpr (SRC == SRC_DEPTH0) {
     SortCtl *c = const_cast<SortCtl *>(in.ctl);
+    uint32_t *h2 = c->dhist2[blockIdx.x & 7];
     for (int i = tid; i < 512; i += NT)
-      if (s_h2[i]) atomicAdd(&c->dhist[2][i], s_h2[i]);
+      if (s_h2[i]) atomicAdd(&h2[i], s_h2[i]);
     if (tid < 32 && s_h3[tid]) atomicAdd(&c->dhist3[tid], s_h3[tid]);
   }
   // per digit: exclusive prefix over the waves and the block total
@@ -924,6 +931,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   SortCtl *ctl = w.ctl;
   char *cb = reinterpret_cast<char *>(ctl);
   auto dhist = [&](int p) { return reinterpret_cast<const uint32_t *>(cb + offsetof(SortCtl, dhist)) + 512 * p; };
+  const uint32_t *dhist2 = reinterpret_cast<const uint32_t *>(cb + offsetof(SortCtl, dhist2));
   auto tbase = [&](int p) { return reinterpret_cast<uint32_t *>(cb + offsetof(SortCtl, tbase)) + 256 * p; };
   auto ticket = [&](int p) { return reinterpret_cast<int32_t *>(cb + offsetof(SortCtl, tickets)) + p; };
   int32_t *err = reinterpret_cast<int32_t *>(cb + offsetof(SortCtl, err));
@@ -955,6 +963,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
     a.tiles_y = cam.tiles_y;
     a.b0 = b0;
     a.dhist_in = dhist(0);
+    a.dhist_copies = 1;
     hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 9, SRC_DEPTH0>), dim3(npd + 1),
                        dim3(DS_THREADS), 0, st, nullptr, nullptr, w.dk[1], w.dv[1], nullptr, n, 0,
                        nullptr, w.status, ticket(0), err, a);
@@ -962,13 +971,15 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   {
     PassIn a = in;
     a.dhist_in = dhist(1);
+    a.dhist_copies = 1;
     hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 9, SRC_KEYS>), dim3(npd),
                        dim3(DS_THREADS), 0, st, w.dk[1], w.dv[1], w.dk[0], w.dv[0], m_dev, n, 9,
                        nullptr, w.status + w.pd, ticket(1), err, a);
   }
   {
     PassIn a = in;
-    a.dhist_in = dhist(2);
+    a.dhist_in = dhist2;
+    a.dhist_copies = 8;
     a.offsets = offsets;
     a.cout = w.dcnt;
     a.wide_kout = w.dk[1];
@@ -980,6 +991,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
   {
     PassIn a = in;
     a.dhist_in = reinterpret_cast<const uint32_t *>(cb + offsetof(SortCtl, dhist3));
+    a.dhist_copies = 1;
     a.offsets = offsets;
     a.cout = w.dcnt;
     hipLaunchKernelGGL((k_onesweep<DS_THREADS, DS_ITEMS, 5, SRC_WIDE>), dim3(npd),
