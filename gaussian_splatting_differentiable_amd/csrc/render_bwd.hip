@@ -9,10 +9,10 @@
 // recorded (here a bitmap per quarter and 64-entry batch), with no geometric
 // sub-tile test; Step 5 branchless alpha = 0 predication for missed pixels and
 // one canonical q shared with the forward pass; Step 6.1 two vertically
-// adjacent pixels per lane, sharing the column terms of q and summed in
-// registers before the reduction; Step 6.3 the per-splat term
+// adjacent pixels per lane (here four), sharing the column terms of q and summed
+// in registers before the reduction; Step 6.3 the per-splat term
 // alpha T (c . dL/dC - accum), with log2(o) folded into the exponent and o
-// divided back out once after the sum; Step 6.4 the two rows' offsets combined
+// divided back out once after the sum; Step 6.4 the rows' offsets combined
 // without per-row products by the row index.
 // "Mitigating SM-Level Load Imbalance in 3D Gaussian Splatting on GPUs",
 // section 4: the same persistent longest-first queue as the forward pass; a
@@ -20,12 +20,13 @@
 // chunk state: it starts from the transmittance after its last processed
 // splat, T_end, with accum = (sum over later chunks of C_chunk . dL/dC) / T_end.
 //
-// gfx950 mapping: one wavefront per item, an 8-column half of a tile (or of a
-// chunk): lane l holds column l mod 8 and rows 2 (l / 8), 2 (l / 8) + 1, so
-// lanes 0-31 cover the half's upper quarter and lanes 32-63 its lower one. The
-// item's non-empty batches come from one vector load of its contributor words;
-// each batch stages only its contributors' records in LDS (the next batch's
-// ids and records in flight) and walks them back to front on the scalar unit.
+// gfx950 mapping: one wavefront per item, a whole tile (or chunk): row q of 16
+// lanes holds quarter q, lane s of the row column s mod 8 and rows 4 (s / 8) to
+// 4 (s / 8) + 3, so a row's DPP exchanges reduce its quarter's sums. Each row
+// walks its own quarter's contributors, so a step evaluates up to four splats.
+// The item's non-empty batches come from one vector load of the contributor
+// words; each batch stages only its contributors' records in LDS (the next
+// batch's ids and records in flight) and is walked on the scalar unit.
 #include <type_traits>
 
 #include "render_common.h"
@@ -42,14 +43,15 @@ constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 // group's backward items stably by a quarter-octave bucket of that length.
 constexpr int BO_T = 1024, BO_W = BO_T / 64, BO_BITS = 6, BO_BINS = 1 << BO_BITS;
 
-// Walk length of a backward item: the longer of its two quarters' last hits.
+// Walk length of a backward item: the longest of its four quarters' last hits.
 __device__ __forceinline__ int item_len(const FwdState &fs, int it, int k) {
-  const int half = item_quad(it), idx = item_index(it);
+  const int idx = item_index(it);
   if (item_kind(it) == ITEM_PLAIN)
-    return max(fs.sub_last[idx * 4 + half], fs.sub_last[idx * 4 + half + 2]);
+    return max(max(fs.sub_last[idx * 4], fs.sub_last[idx * 4 + 1]),
+               max(fs.sub_last[idx * 4 + 2], fs.sub_last[idx * 4 + 3]));
   const int p = item_chunk(it);
-  return max(fs.chunk_last[chunk_index(idx, p, half, k)],
-             fs.chunk_last[chunk_index(idx, p, half + 2, k)]);
+  return max(max(fs.chunk_last[chunk_index(idx, p, 0, k)], fs.chunk_last[chunk_index(idx, p, 1, k)]),
+             max(fs.chunk_last[chunk_index(idx, p, 2, k)], fs.chunk_last[chunk_index(idx, p, 3, k)]));
 }
 
 __device__ __forceinline__ uint32_t order_bin(int len) {
@@ -58,9 +60,9 @@ __device__ __forceinline__ uint32_t order_bin(int len) {
 }
 
 // The backward's preparation in one launch: workgroup g < GS_GROUPS builds group
-// g's backward queue: the forward's plain and pass-B items of quarters 0 and 1
-// become the left and right halves (each covers quarters h and h + 2), stably
-// sorted longest first; the others zero the gradient output. The frame runs only
+// g's backward queue: the forward's plain and pass-B items of quarter 0 stand
+// for their whole tile or chunk (a backward item covers all four quarters),
+// stably sorted longest first; the others zero the gradient output. The frame runs only
 // if its status is still GS_OK.
 __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int ntiles,
                                                   int nblocks, float *__restrict__ grads,
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
   for (int e = c0 + lane; e < c1; e += 64) {
     const int it = fs.items[lo + e];
-    if (item_quad(it) < 2) atomicAdd(&cnt[w][order_bin(item_len(fs, it, k))], 1);
+    if (item_quad(it) == 0) atomicAdd(&cnt[w][order_bin(item_len(fs, it, k))], 1);
   }
   __syncthreads();
   __shared__ int btot[BO_BINS];
@@ -123,7 +125,7 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   for (int base = c0; base < c1; base += 64) {
     const int e = base + lane;
     const int it = e < c1 ? fs.items[lo + e] : 0;
-    const bool valid = e < c1 && item_quad(it) < 2;
+    const bool valid = e < c1 && item_quad(it) == 0;
     const uint32_t d = valid ? order_bin(item_len(fs, it, k)) : 0u;
     uint64_t peers = wave_ballot(valid);
 #pragma unroll
@@ -158,96 +160,115 @@ __device__ __forceinline__ uint64_t word_of(uint32_t lo, uint32_t hi, int m) {
 
 // A staged entry (64 bytes): the record with 2b, log2(o) and 1/o in place of
 // depth, pad and o, and the splat id. Slot 64 of a wave's stage is a dead
-// entry (tau = -1, never hit) that a half with no entry left reads.
+// entry (tau = -1, never hit) that a quarter with no entry left reads.
 struct __align__(16) Staged {
   float4 p0;  // mx, my, a, b
   float4 p1;  // c, 1/o, r, g
   float4 p2;  // b (colour), tau, 2b, log2(o)
-  int4 p3;    // id, live (1) or dead (0), -, -
+  int4 p3;    // id, live (1) or dead (0), gradient row's byte offset, -
 };
 constexpr int SLOTS = BATCH + 1;
 
-__device__ __forceinline__ int top_bit(uint64_t w) { return w ? 63 - __builtin_clzll(w) : BATCH; }
-__device__ __forceinline__ bool has_bit(uint64_t w, int j) { return j < BATCH && ((w >> j) & 1ull); }
-
-// The next step of a batch's walk: the entries the upper and lower quarter take
-// (BATCH, the dead slot, for none), removed from their words. Each quarter
-// takes its own entries back to front. An entry both quarters blended is taken
-// by both in the same step (shared: the halves' sums are added and written
-// once); otherwise the higher entry goes to its quarter, and the other quarter
-// takes its own next entry in the same step unless that entry is still to come
-// for the first quarter too (then it waits, so that the two meet on it).
-struct Pair {
-  int jt, jb;
-  bool shared;
-};
-__device__ __forceinline__ Pair next_pair(uint64_t &wt, uint64_t &wb) {
-  Pair p;
-  const int ht = top_bit(wt), hb = top_bit(wb);
-  p.shared = ht == hb && ht < BATCH;
-  if (p.shared || ht > hb) {
-    p.jt = ht;
-    p.jb = p.shared ? hb : (has_bit(wt, hb) ? BATCH : hb);
-  } else {
-    p.jb = hb;
-    p.jt = has_bit(wb, ht) ? BATCH : ht;
-  }
-  if (p.jt < BATCH) wt &= ~(1ull << p.jt);
-  if (p.jb < BATCH) wb &= ~(1ull << p.jb);
-  return p;
+// The highest slot of w, removed from w; BATCH (the dead slot) when w is empty.
+// s_flbit gives the leading zeros, -1 for an empty word, so 63 - f is 64 there,
+// and clearing bit 64 mod 64 of an empty word leaves it empty.
+__device__ __forceinline__ int take_top(uint64_t &w) {
+  int f;
+  __asm__("s_flbit_i32_b64 %0, %1" : "=s"(f) : "s"(w));
+  const int j = 63 - f;
+  __asm__("s_bitset0_b64 %0, %1" : "+s"(w) : "s"(j));
+  return j;
 }
 
-// Per-lane state of the two pixels of a lane (rows 0 and 1 of its pair).
-struct Pix2 {
-  float fx, fy0, fy1;        // sample positions
-  float T0, T1, acc0, acc1;  // transmittance after the pixel's last entry; accumulator
-  float g00, g01, g02, g10, g11, g12;  // dL/dC of the two pixels
-  int last0, last1;          // entries the pixel consumed from the walk's start
+// One batch's gradient sums, from the LDS accumulators to the output: 63 lanes
+// take 7 slots' 9 sums at a time, so each atomic instruction writes 7 splats'
+// rows of 9 consecutive floats (a line or two each), once per splat per batch
+// whichever quarters blended it. The accumulators are left at zero.
+template <bool WIDE>
+__device__ __forceinline__ void flush(uint64_t staged, const Staged *stage, float *gacc,
+                                      float *__restrict__ grads) {
+  const int lane = __lane_id();
+  const int ds = lane / 9, c = lane - 9 * ds;  // slot within the group of 7, component
+#pragma unroll
+  for (int g0 = 0; g0 < BATCH; g0 += 7) {
+    if (((staged >> g0) & 0x7Full) == 0) continue;
+    const int slot = g0 + ds;
+    if (lane < 63 && slot < BATCH) {
+      const float v = gacc[9 * g0 + lane];
+      gacc[9 * g0 + lane] = 0.0f;
+      const int4 p3 = stage[slot].p3;
+      if (p3.y) {
+        if constexpr (WIDE)
+          unsafeAtomicAdd(&grads[9 * (int64_t)p3.x + c], v);
+        else
+          unsafeAtomicAdd(reinterpret_cast<float *>(reinterpret_cast<char *>(grads) +
+                                                    ((uint32_t)p3.z + 4u * (uint32_t)c)),
+                          v);
+      }
+    }
+  }
+}
+
+// Per-lane state: four vertically adjacent pixels of one column of a quarter.
+struct Pix4 {
+  float fx, fy[4];         // sample positions
+  float T[4], acc[4];      // transmittance after the pixel's last entry; accumulator
+  float g[4][3];           // dL/dC
+  int last[4];             // entries the pixel consumed from the walk's start
 };
 
-// Walk the item's batches back to front. cw_top / cw_bot: the contributor words
-// of the two quarters at the walk's first batch; nb_top / nb_bot: how many of
-// them are current (the rest were not written for this frame); list: the walk's
-// first list position. Lanes 0-31 (the upper quarter) and 32-63 (the lower
-// one) take the entries of their own quarter's word, back to front (next_pair):
-// a step evaluates one splat for both halves or two different splats, one per
-// half, and a half with no entry in the step reads the dead slot.
+// Walk the item's batches back to front. cw[q]: quarter q's contributor words
+// at the walk's first batch; nbw[q]: how many of them are current (the rest
+// were not written for this frame); list: the walk's first list position. The
+// 16 lanes of row q of the wave hold quarter q's pixels and take its entries
+// back to front, one per step: a step evaluates up to four different splats,
+// one per quarter, and a quarter with no entry left reads the dead slot.
 template <bool WIDE>
 __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int n,
                                           const int32_t *__restrict__ sids, int64_t list,
-                                          const uint64_t *__restrict__ cw_top, int nb_top,
-                                          const uint64_t *__restrict__ cw_bot, int nb_bot,
-                                          Pix2 &x, Staged *stage, float *__restrict__ grads) {
+                                          const uint64_t *cw0, int64_t nw, const int nbw[4],
+                                          Pix4 &x, Staged *stage, float *gacc,
+                                          float *__restrict__ grads) {
   const int lane = __lane_id();
-  const bool top = lane < 32;
-  const int upper = top ? 1 : 0;
-  const int comp = comp_of_half_lane(lane);
-  const int comp4 = 4 * comp;
+  const uint32_t shift = 8u * (uint32_t)(lane >> 4);  // this row's byte of the packed slots
+  const int comp = comp_of_row_lane(lane);
+  const bool lo2 = (lane & 2) == 0, lo1 = (lane & 1) == 0;
   // the constant factor each owner lane applies to its sum after the reduction
   // (powers of two: exact): -1/2 for the two squared offsets
   const float post = (comp == 2 || comp == 4) ? -0.5f : 1.0f;
-  float zero = 0.0f;
-  __asm__ volatile("" : "+v"(zero));  // a register, not a constant, for the unpaired swap
   const float4 *rec4 = reinterpret_cast<const float4 *>(splats);
   // the next batch's record of this lane, as three registers of four (kept out
   // of any aggregate: the compiler parks part of one in memory otherwise)
   float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0, q2 = q0;
-  const int nbat = max(nb_top, nb_bot);
+  // x.last becomes, per batch, the limit last - (the batch's first position)
+  int lbase = 0;
+  const int nbat = max(max(nbw[0], nbw[1]), max(nbw[2], nbw[3]));
   for (int r0 = (nbat - 1) & ~63; r0 >= 0; r0 -= 64) {
     // lane i holds the words of batch r0 + i, one per quarter
     const int m = r0 + lane;
-    const uint64_t wtv = m < nb_top ? cw_top[m] : 0ull;
-    const uint64_t wbv = m < nb_bot ? cw_bot[m] : 0ull;
-    const uint32_t tlo = (uint32_t)wtv, thi = (uint32_t)(wtv >> 32);
-    const uint32_t blo = (uint32_t)wbv, bhi = (uint32_t)(wbv >> 32);
-    uint64_t todo = wave_ballot((wtv | wbv) != 0);
+    uint32_t wlo[4], whi[4];
+    uint64_t any = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint64_t v = m < nbw[q] ? cw0[q * nw + m] : 0ull;
+      wlo[q] = (uint32_t)v;
+      whi[q] = (uint32_t)(v >> 32);
+      any |= v;
+    }
+    uint64_t todo = wave_ballot(any != 0);
     if (!todo) continue;
+    // every quarter's contributors of batch mb of this round
+    auto any_word = [&](int mb) {
+      uint64_t w = 0;
+#pragma unroll
+      for (int q = 0; q < 4; q++) w |= word_of(wlo[q], whi[q], mb);
+      return w;
+    };
     // pipeline: the records of the batch being staged and the ids of the next
     // non-empty batch are in flight while a batch is walked
     int mc = 63 - __builtin_clzll(todo);
     todo &= ~(1ull << mc);
-    uint64_t wt = word_of(tlo, thi, mc), wb = word_of(blo, bhi, mc);
-    int idc = load_marked_id(sids, list + 64 * (int64_t)(r0 + mc), wt | wb);
+    int idc = load_marked_id(sids, list + 64 * (int64_t)(r0 + mc), any_word(mc));
     {
       const int64_t ri = 3 * (int64_t)(valid_id(idc, n) ? idc : 0);
       q0 = rec4[ri];
@@ -255,13 +276,10 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
       q2 = rec4[ri + 2];
     }
     int mn = -1, idn = -1;
-    uint64_t wtn = 0, wbn = 0;
     if (todo) {
       mn = 63 - __builtin_clzll(todo);
       todo &= ~(1ull << mn);
-      wtn = word_of(tlo, thi, mn);
-      wbn = word_of(blo, bhi, mn);
-      idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mn), wtn | wbn);
+      idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mn), any_word(mn));
     }
     for (;;) {
       // whether any splat of the batch can reach the 0.99 clamp: o G < 0.99
@@ -277,7 +295,8 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         stage[lane].p1 = p1;
         stage[lane].p2 = p2;
         // the gradient row's byte offset (rows of 36 bytes; only when it fits)
-        stage[lane].p3 = make_int4(idc, valid_id(idc, n) ? 1 : 0, WIDE ? 0 : (int)(36u * (uint32_t)idc), 0);
+        stage[lane].p3 = make_int4(idc, valid_id(idc, n) ? 1 : 0,
+                                   WIDE ? 0 : (int)(36u * (uint32_t)idc), 0);
       }
       // records of the next batch, ids of the one after it
       idc = idn;
@@ -288,132 +307,119 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         q2 = rec4[rj + 2];
       }
       int mnn = -1;
-      uint64_t wtnn = 0, wbnn = 0;
       idn = -1;
       if (todo) {
         mnn = 63 - __builtin_clzll(todo);
         todo &= ~(1ull << mnn);
-        wtnn = word_of(tlo, thi, mnn);
-        wbnn = word_of(blo, bhi, mnn);
-        idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mnn), wtnn | wbnn);
+        idn = load_marked_id(sids, list + 64 * (int64_t)(r0 + mnn), any_word(mnn));
       }
       wave_sync();
+      // a pixel takes entry j only below its own stop: j < last - base (the
+      // dead slot, j = 64, never hits)
       const int base = 64 * (r0 + mc);
-      // a pixel takes entry j only below its own stop: j < last - base, here
-      // on the slot's byte offset in the stage, 64 j (the dead slot, j = 64,
-      // never hits)
-      const int lim0 = 64 * (x.last0 - base), lim1 = 64 * (x.last1 - base);
-      auto step = [&](auto clamp_t, const Staged &s, int j, bool shared) {
+#pragma unroll
+      for (int k = 0; k < 4; k++) x.last[k] -= base - lbase;
+      lbase = base;
+      uint64_t wc[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) wc[q] = word_of(wlo[q], whi[q], mc);
+      // steps of this batch: the most entries any quarter takes
+      const int nsteps =
+          max(max(__builtin_popcountll(wc[0]), __builtin_popcountll(wc[1])),
+              max(__builtin_popcountll(wc[2]), __builtin_popcountll(wc[3])));
+      auto step = [&](auto clamp_t, const Staged &s, int j) {
         constexpr bool CLAMP = decltype(clamp_t)::value;
         const float a = s.p0.z, b = s.p0.w, c = s.p1.x;
-        // the column terms of the canonical q are shared by the lane's two rows
+        // the column terms of the canonical q are shared by the lane's four rows
         const float dx = x.fx - s.p0.x;
-        const float adx = a * dx;
-        const float adxdx = adx * dx, b2dx = s.p2.z * dx;
-        const float dy0 = x.fy0 - s.p0.y, dy1 = x.fy1 - s.p0.y;
-        const float cdy0 = c * dy0, cdy1 = c * dy1;
-        const float qa = __builtin_fmaf(cdy0, dy0, __builtin_fmaf(b2dx, dy0, adxdx));
-        const float qb = __builtin_fmaf(cdy1, dy1, __builtin_fmaf(b2dx, dy1, adxdx));
-        const bool h0 = j < lim0 && qa <= s.p2.y;  // j: the slot's byte offset
-        const bool h1 = j < lim1 && qb <= s.p2.y;
-        // branchless: a missed pixel takes alpha = 0, which leaves T and accum
-        // unchanged and contributes zero to every sum
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(qa, NEG_HALF_LOG2E, s.p2.w));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(qb, NEG_HALF_LOG2E, s.p2.w));
-        const float oG0 = h0 ? e0 : 0.0f, oG1 = h1 ? e1 : 0.0f;  // o G
-        const float al0 = CLAMP ? fminf(0.99f, oG0) : oG0;
-        const float al1 = CLAMP ? fminf(0.99f, oG1) : oG1;
-        x.T0 = x.T0 * __builtin_amdgcn_rcpf(1.0f - al0);  // T before this splat
-        x.T1 = x.T1 * __builtin_amdgcn_rcpf(1.0f - al1);
-        const float cg0 = __builtin_fmaf(s.p1.z, x.g00, __builtin_fmaf(s.p1.w, x.g01, s.p2.x * x.g02));
-        const float cg1 = __builtin_fmaf(s.p1.z, x.g10, __builtin_fmaf(s.p1.w, x.g11, s.p2.x * x.g12));
-        const float d0 = cg0 - x.acc0, d1 = cg1 - x.acc1;  // dL/dalpha = T d
-        x.acc0 = __builtin_fmaf(al0, d0, x.acc0);
-        x.acc1 = __builtin_fmaf(al1, d1, x.acc1);
-        const float w0 = al0 * x.T0, w1 = al1 * x.T1;
-        // -2 dL/dq = alpha T d, which is also o G dL/dalpha: an unclamped alpha
-        // is o G; a clamped alpha passes no gradient
-        const float m0 = !CLAMP || oG0 < 0.99f ? w0 * d0 : 0.0f;
-        const float m1 = !CLAMP || oG1 < 0.99f ? w1 * d1 : 0.0f;
-        // the lane's two rows, dy1 = dy0 + 1: with M = m0 + m1,
-        // Sy = m0 dy0 + m1 dy1 = M dy0 + m1 and Syy = m0 dy0^2 + m1 dy1^2 =
-        // dy0 (Sy + m1) + m1, and X = M dx, each derivative needs dx once
-        const float M = m0 + m1;
-        const float Sy = __builtin_fmaf(M, dy0, m1);
+        const float adxdx = (a * dx) * dx, b2dx = s.p2.z * dx;
+        float mk[4], wk[4], dy0 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float dy = x.fy[k] - s.p0.y;
+          if (k == 0) dy0 = dy;
+          const float qk = __builtin_fmaf(c * dy, dy, __builtin_fmaf(b2dx, dy, adxdx));
+          const bool h = j < x.last[k] && qk <= s.p2.y;
+          // branchless: a missed pixel takes alpha = 0, which leaves T and accum
+          // unchanged and contributes zero to every sum
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(qk, NEG_HALF_LOG2E, s.p2.w));
+          const float oG = h ? e : 0.0f;  // o G
+          const float al = CLAMP ? fminf(0.99f, oG) : oG;
+          x.T[k] = x.T[k] * __builtin_amdgcn_rcpf(1.0f - al);  // T before this splat
+          const float cg = __builtin_fmaf(s.p1.z, x.g[k][0],
+                                          __builtin_fmaf(s.p1.w, x.g[k][1], s.p2.x * x.g[k][2]));
+          const float d = cg - x.acc[k];  // dL/dalpha = T d
+          x.acc[k] = __builtin_fmaf(al, d, x.acc[k]);
+          wk[k] = al * x.T[k];
+          // -2 dL/dq = alpha T d, which is also o G dL/dalpha: an unclamped
+          // alpha is o G; a clamped alpha passes no gradient
+          mk[k] = !CLAMP || oG < 0.99f ? wk[k] * d : 0.0f;
+        }
+        // the lane's rows, dy_k = dy0 + k: with M = sum m_k, R1 = sum k m_k and
+        // R2 = sum k^2 m_k, Sy = sum m_k dy_k = M dy0 + R1 and Syy = sum m_k
+        // dy_k^2 = dy0 (Sy + R1) + R2, and X = M dx: each derivative needs dx once
+        const float M = (mk[0] + mk[1]) + (mk[2] + mk[3]);
+        const float R1 = __builtin_fmaf(3.0f, mk[3], __builtin_fmaf(2.0f, mk[2], mk[1]));
+        const float R2 = __builtin_fmaf(9.0f, mk[3], __builtin_fmaf(4.0f, mk[2], mk[1]));
+        const float Sy = __builtin_fmaf(M, dy0, R1);
         const float X = M * dx;
         float gr[9];
         gr[0] = __builtin_fmaf(a, X, b * Sy);  // dq/dmx = -2 (a dx + b dy)
         gr[1] = __builtin_fmaf(b, X, c * Sy);  // dq/dmy = -2 (b dx + c dy)
         gr[2] = X * dx;                        // times -1/2 after the sum
         gr[3] = -(dx * Sy);
-        gr[4] = __builtin_fmaf(dy0, Sy + m1, m1);  // times -1/2 after the sum
+        gr[4] = __builtin_fmaf(dy0, Sy + R1, R2);  // times -1/2 after the sum
         gr[5] = M;                                 // divided by o after the sum
-        gr[6] = __builtin_fmaf(w1, x.g10, w0 * x.g00);
-        gr[7] = __builtin_fmaf(w1, x.g11, w0 * x.g01);
-        gr[8] = __builtin_fmaf(w1, x.g12, w0 * x.g02);
-        float out = reduce_scatter9_half(gr, zero);
-        // one splat in both halves: add the lower half's sums to the upper's
-        // (the owners sit at the same place in both halves), written once
-        if (shared) out = swap_sum32(out, out);
+#pragma unroll
+        for (int ch = 0; ch < 3; ch++)
+          gr[6 + ch] = __builtin_fmaf(wk[3], x.g[3][ch],
+                                      __builtin_fmaf(wk[2], x.g[2][ch],
+                                                     __builtin_fmaf(wk[1], x.g[1][ch],
+                                                                    wk[0] * x.g[0][ch])));
+        float out = reduce_scatter9_row(gr, lo2, lo1);
         // finish the sum here, where its last exchange fuses into the add,
         // rather than inside the owner lanes' branch
         __asm__ volatile("" : "+v"(out));
         out *= comp == 5 ? s.p1.y : post;
-        if (comp >= 0 && s.p3.y && (top || !shared)) {
-          if constexpr (WIDE)
-            unsafeAtomicAdd(&grads[9 * (int64_t)s.p3.x + comp], out);
-          else
-            unsafeAtomicAdd(reinterpret_cast<float *>(reinterpret_cast<char *>(grads) +
-                                                      ((uint32_t)s.p3.z + (uint32_t)comp4)),
-                            out);
-        }
+        // the row's 9 sums go to the slot's accumulators in LDS (rows that took
+        // the same splat add to the same ones; the dead slot collects zeros)
+        if (comp >= 0) atomicAdd(&gacc[9 * j + comp], out);
+      };
+      // the four quarters' slots of a step, packed a byte each on the scalar
+      // unit; a lane takes its row's byte (one bit-field extract)
+      auto next_slot4 = [&]() {
+        const uint32_t j0 = (uint32_t)take_top(wc[0]), j1 = (uint32_t)take_top(wc[1]);
+        const uint32_t j2 = (uint32_t)take_top(wc[2]), j3 = (uint32_t)take_top(wc[3]);
+        const uint32_t packed = j0 | (j1 << 8) | (j2 << 16) | (j3 << 24);
+        return (int)__builtin_amdgcn_ubfe(packed, shift, 8);
       };
       // the next step's reads from the stage go out before the current step
       // runs (two buffers alternate)
-      // a lane's slot is jt in the upper half and jb in the lower one: its
-      // byte offset 64 jb + upper (64 (jt - jb)), one 24-bit multiply-add on
-      // the vector unit (the rest is scalar)
-      const char *stage_b = reinterpret_cast<const char *>(stage);
-      auto slot_off = [&](const Pair &p) {
-        int t;
-        __asm__("v_mul_i32_i24 %0, %1, %2" : "=v"(t) : "s"(64 * (p.jt - p.jb)), "v"(upper));
-        return t + 64 * p.jb;
-      };
-      auto at = [&](int off) { return *reinterpret_cast<const Staged *>(stage_b + off); };
       auto walk = [&](auto clamp_t) {
-        Pair pc = next_pair(wt, wb);
-        int j0 = slot_off(pc);
-        bool sh0 = pc.shared;
-        Staged s0 = at(j0);
+        int left = nsteps;
+        int j0 = next_slot4();
+        Staged s0 = stage[j0];
         for (;;) {
-          const bool more1 = (wt | wb) != 0;
-          pc = next_pair(wt, wb);
-          const int j1 = slot_off(pc);
-          const bool sh1 = pc.shared;
-          const Staged s1 = at(j1);
-          step(clamp_t, s0, j0, sh0);
-          if (!more1) break;
-          const bool more0 = (wt | wb) != 0;
-          pc = next_pair(wt, wb);
-          j0 = slot_off(pc);
-          sh0 = pc.shared;
-          s0 = at(j0);
-          step(clamp_t, s1, j1, sh1);
-          if (!more0) break;
+          const int j1 = next_slot4();
+          const Staged s1 = stage[j1];
+          step(clamp_t, s0, j0);
+          if (--left == 0) break;
+          j0 = next_slot4();
+          s0 = stage[j0];
+          step(clamp_t, s1, j1);
+          if (--left == 0) break;
         }
       };
+      const uint64_t staged = wc[0] | wc[1] | wc[2] | wc[3];
       if (bclamp)
         walk(std::true_type{});
       else
         walk(std::false_type{});
       wave_sync();
+      flush<WIDE>(staged, stage, gacc, grads);
       if (mn < 0) break;
       mc = mn;
-      wt = wtn;
-      wb = wbn;
       mn = mnn;
-      wtn = wtnn;
-      wbn = wbnn;
     }
   }
 }
@@ -430,9 +436,12 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
     const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads) {
   __shared__ Staged stage_all[GS_WAVES_PER_BLOCK][SLOTS];
+  __shared__ float gacc_all[GS_WAVES_PER_BLOCK][9 * SLOTS];  // per-slot gradient sums
   Staged *stage = stage_all[wave_in_block()];
+  float *gacc = gacc_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
   if (!fs.hdr->run_b) return;  // the frame failed earlier: nothing to differentiate
+  for (int i = __lane_id(); i < 9 * SLOTS; i += GS_WAVE) gacc[i] = 0.0f;
   if (__lane_id() == 0) {
     Staged dead;
     dead.p0 = dead.p1 = dead.p2 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -444,7 +453,9 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
   const int k = fs.hdr->k;
   const int64_t P = (int64_t)cam.width * cam.height * cam.views;
   const int lane = __lane_id();
-  const int col = lane & 7, rp = lane >> 3;
+  // row q of the wave: quarter q of the tile; lane s of the row: column s mod 8,
+  // rows 4 (s / 8) to 4 (s / 8) + 3 of the quarter
+  const int quad = lane >> 4, col = lane & 7, r4 = 4 * ((lane >> 3) & 1);
   __shared__ uint32_t drained;
   Worker wk = make_worker(&drained);
   for (;;) {
@@ -452,100 +463,83 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     if (t < 0) break;
     wk.round++;
     const int it = fs.bitems[t];
-    const int kind = item_kind(it), half = item_quad(it), p = item_chunk(it);
+    const int kind = item_kind(it), p = item_chunk(it);
     const int idx = item_index(it);
     const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
-    const SubTile st = subtile_of(tile, half, cam);  // the half's upper quarter
-    if (st.empty) continue;
-    const int px = st.x0 + col, py0 = st.y0 + 2 * rp, py1 = py0 + 1;
-    const bool in0 = px < cam.width && py0 < cam.height;
-    const bool in1 = px < cam.width && py1 < cam.height;
-    const int64_t pix0 = (int64_t)(st.prow + py0) * cam.width + px;
-    const int64_t pix1 = pix0 + cam.width;
+    const SubTile st = subtile_of(tile, quad, cam);  // this lane's quarter
+    const int px = st.x0 + col;
     const int2 rg = ranges[tile];
-    Pix2 x;
+    Pix4 x;
     x.fx = (float)px + 0.5f;
-    x.fy0 = (float)py0 + 0.5f;
-    x.fy1 = (float)py1 + 0.5f;
-    x.g00 = x.g01 = x.g02 = x.g10 = x.g11 = x.g12 = 0.f;
-    // what lies behind the last blended splat, per unit of final transmittance:
-    // the background's bg . dL/dC and dL/dT_final (0 when neither is given)
-    float ex0 = 0.f, ex1 = 0.f;
-    if (in0) {
-      x.g00 = dL[pix0];
-      x.g01 = dL[P + pix0];
-      x.g02 = dL[2 * P + pix0];
-      if (cam.bg_on) {
-        ex0 = fmaf(cam.bg[0], x.g00, fmaf(cam.bg[1], x.g01, cam.bg[2] * x.g02));
-        if (dT) ex0 += dT[pix0];
+    bool in[4];
+    int64_t pix[4];
+    float ex[4];  // bg . dL/dC + dL/dT_final: what lies behind the last splat, per unit T
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int py = st.y0 + r4 + r;
+      x.fy[r] = (float)py + 0.5f;
+      in[r] = px < cam.width && py < cam.height;
+      pix[r] = (int64_t)(st.prow + py) * cam.width + px;
+      x.g[r][0] = x.g[r][1] = x.g[r][2] = 0.0f;
+      ex[r] = 0.0f;
+      if (in[r]) {
+        x.g[r][0] = dL[pix[r]];
+        x.g[r][1] = dL[P + pix[r]];
+        x.g[r][2] = dL[2 * P + pix[r]];
+        if (cam.bg_on) {
+          ex[r] = fmaf(cam.bg[0], x.g[r][0], fmaf(cam.bg[1], x.g[r][1], cam.bg[2] * x.g[r][2]));
+          if (dT) ex[r] += dT[pix[r]];
+        }
       }
     }
-    if (in1) {
-      x.g10 = dL[pix1];
-      x.g11 = dL[P + pix1];
-      x.g12 = dL[2 * P + pix1];
-      if (cam.bg_on) {
-        ex1 = fmaf(cam.bg[0], x.g10, fmaf(cam.bg[1], x.g11, cam.bg[2] * x.g12));
-        if (dT) ex1 += dT[pix1];
-      }
-    }
-    const int qtop = half, qbot = half + 2;
+    int nbw[4];
     if (kind == ITEM_PLAIN) {
-      x.T0 = in0 ? Tfin[pix0] : 1.0f;
-      x.T1 = in1 ? Tfin[pix1] : 1.0f;
-      x.last0 = in0 ? last[pix0] : 0;
-      x.last1 = in1 ? last[pix1] : 0;
-      x.acc0 = ex0;
-      x.acc1 = ex1;
-      walk_back<WIDE>(splats, n, sorted_ids, rg.x, contrib_base(fs, qtop, tile, rg.x),
-                ceil64(fs.sub_last[tile * 4 + qtop]), contrib_base(fs, qbot, tile, rg.x),
-                ceil64(fs.sub_last[tile * 4 + qbot]), x, stage, grads);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        x.T[r] = in[r] ? Tfin[pix[r]] : 1.0f;
+        x.last[r] = in[r] ? last[pix[r]] : 0;
+        x.acc[r] = ex[r];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q++) nbw[q] = ceil64(fs.sub_last[tile * 4 + q]);
+      walk_back<WIDE>(splats, n, sorted_ids, rg.x, contrib_base(fs, 0, tile, rg.x), fs.nw, nbw, x,
+                      stage, gacc, grads);
       continue;
     }
-    // a chunk of a heavy tile: the lane's two pixels lie in one quarter, at
-    // positions ql and ql + 8 of that quarter's chunk state
+    // a chunk of a heavy tile: the lane's pixels are positions ql + 8 r of its
+    // quarter's chunk state
     int cs, ce;
     chunk_range(rg.x, rg.y, p, k, cs, ce);
-    const int q = rp < 4 ? qtop : qbot;
-    const int ql = col + 8 * ((2 * rp) & 7);
-    const int ci = chunk_index(idx, p, q, k);
-    float Tc[2] = {1.0f, 1.0f}, ac[2] = {0.f, 0.f};
-    int lc[2] = {0, 0};
-    const bool inr[2] = {in0, in1};
-    const float exr[2] = {ex0, ex1};
-    const int64_t pixr[2] = {pix0, pix1};
-    const float gr0[2] = {x.g00, x.g10}, gr1[2] = {x.g01, x.g11}, gr2[2] = {x.g02, x.g12};
+    const int ql = col + 8 * r4;
+    const int ci = chunk_index(idx, p, quad, k);
 #pragma unroll
-    for (int r = 0; r < 2; r++) {
+    for (int r = 0; r < 4; r++) {
       const int64_t cp = (int64_t)ci * 64 + ql + 8 * r;
-      int lb = inr[r] ? fs.LB[cp] : -1;
+      int lb = in[r] ? fs.LB[cp] : -1;
+      float Tc = 1.0f, ac = 0.0f;
       if (lb > 0) {
-        Tc[r] = fs.TB[cp];
+        Tc = fs.TB[cp];
         float behind = 0.0f;  // sum over later chunks of C . dL/dC
         for (int q2 = p + 1; q2 < k; q2++) {
-          const int64_t c2 = (int64_t)chunk_index(idx, q2, q, k) * 64 + ql + 8 * r;
+          const int64_t c2 = (int64_t)chunk_index(idx, q2, quad, k) * 64 + ql + 8 * r;
           if (fs.LB[c2] < 0) break;
-          behind = __builtin_fmaf(fs.CB[3 * c2], gr0[r],
-                                  __builtin_fmaf(fs.CB[3 * c2 + 1], gr1[r],
-                                                 __builtin_fmaf(fs.CB[3 * c2 + 2], gr2[r], behind)));
+          behind = __builtin_fmaf(fs.CB[3 * c2], x.g[r][0],
+                                  __builtin_fmaf(fs.CB[3 * c2 + 1], x.g[r][1],
+                                                 __builtin_fmaf(fs.CB[3 * c2 + 2], x.g[r][2], behind)));
         }
-        if (cam.bg_on) behind = fmaf(Tfin[pixr[r]], exr[r], behind);
-        ac[r] = behind / Tc[r];
+        if (cam.bg_on) behind = fmaf(Tfin[pix[r]], ex[r], behind);
+        ac = behind / Tc;
       } else {
         lb = 0;
       }
-      lc[r] = lb;
+      x.T[r] = Tc;
+      x.acc[r] = ac;
+      x.last[r] = lb;
     }
-    x.T0 = Tc[0];
-    x.T1 = Tc[1];
-    x.acc0 = ac[0];
-    x.acc1 = ac[1];
-    x.last0 = lc[0];
-    x.last1 = lc[1];
-    const uint64_t *cw0 = contrib_base(fs, qtop, tile, rg.x) + ((cs - rg.x) >> 6);
-    const uint64_t *cw1 = contrib_base(fs, qbot, tile, rg.x) + ((cs - rg.x) >> 6);
-    walk_back<WIDE>(splats, n, sorted_ids, cs, cw0, ceil64(fs.chunk_last[chunk_index(idx, p, qtop, k)]),
-              cw1, ceil64(fs.chunk_last[chunk_index(idx, p, qbot, k)]), x, stage, grads);
+#pragma unroll
+    for (int q = 0; q < 4; q++) nbw[q] = ceil64(fs.chunk_last[chunk_index(idx, p, q, k)]);
+    walk_back<WIDE>(splats, n, sorted_ids, cs, contrib_base(fs, 0, tile, rg.x) + ((cs - rg.x) >> 6),
+                    fs.nw, nbw, x, stage, gacc, grads);
   }
 }
 
