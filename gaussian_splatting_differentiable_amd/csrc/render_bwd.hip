@@ -158,14 +158,13 @@ __device__ __forceinline__ uint64_t word_of(uint32_t lo, uint32_t hi, int m) {
          (uint32_t)__builtin_amdgcn_readlane((int)lo, m);
 }
 
-// A staged entry (64 bytes): the record with 2b, log2(o) and 1/o in place of
-// depth, pad and o, and the splat id. Slot 64 of a wave's stage is a dead
-// entry (tau = -1, never hit) that a quarter with no entry left reads.
+// A staged entry (48 bytes): the record with 2b, log2(o) and 1/o in place of
+// depth, pad and o. Slot 64 of a wave's stage is a dead entry (tau = -1, never
+// hit) that a quarter with no entry left reads.
 struct __align__(16) Staged {
   float4 p0;  // mx, my, a, b
   float4 p1;  // c, 1/o, r, g
   float4 p2;  // b (colour), tau, 2b, log2(o)
-  int4 p3;    // id, live (1) or dead (0), gradient row's byte offset, -
 };
 constexpr int SLOTS = BATCH + 1;
 
@@ -183,9 +182,11 @@ __device__ __forceinline__ int take_top(uint64_t &w) {
 // One batch's gradient sums, from the LDS accumulators to the output: 63 lanes
 // take 7 slots' 9 sums at a time, so each atomic instruction writes 7 splats'
 // rows of 9 consecutive floats (a line or two each), once per splat per batch
-// whichever quarters blended it. The accumulators are left at zero.
+// whichever quarters blended it. rows[j]: slot j's gradient row (its byte
+// offset, or its splat id when WIDE), -1 for a slot without an entry. The
+// accumulators are left at zero.
 template <bool WIDE>
-__device__ __forceinline__ void flush(uint64_t staged, const Staged *stage, float *gacc,
+__device__ __forceinline__ void flush(uint64_t staged, const int32_t *rows, float *gacc,
                                       float *__restrict__ grads) {
   const int lane = __lane_id();
   const int ds = lane / 9, c = lane - 9 * ds;  // slot within the group of 7, component
@@ -196,13 +197,13 @@ __device__ __forceinline__ void flush(uint64_t staged, const Staged *stage, floa
     if (lane < 63 && slot < BATCH) {
       const float v = gacc[9 * g0 + lane];
       gacc[9 * g0 + lane] = 0.0f;
-      const int4 p3 = stage[slot].p3;
-      if (p3.y) {
+      const int32_t row = rows[slot];
+      if (row != -1) {
         if constexpr (WIDE)
-          unsafeAtomicAdd(&grads[9 * (int64_t)p3.x + c], v);
+          unsafeAtomicAdd(&grads[9 * (int64_t)row + c], v);
         else
           unsafeAtomicAdd(reinterpret_cast<float *>(reinterpret_cast<char *>(grads) +
-                                                    ((uint32_t)p3.z + 4u * (uint32_t)c)),
+                                                    ((uint32_t)row + 4u * (uint32_t)c)),
                           v);
       }
     }
@@ -227,12 +228,13 @@ template <bool WIDE>
 __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int n,
                                           const int32_t *__restrict__ sids, int64_t list,
                                           const uint64_t *cw0, int64_t nw, const int nbw[4],
-                                          Pix4 &x, Staged *stage, float *gacc,
-                                          float *__restrict__ grads) {
+                                          Pix4 &x, Staged *stage, float *gacc2,
+                                          int32_t *rows2, float *__restrict__ grads) {
   const int lane = __lane_id();
   const uint32_t shift = 8u * (uint32_t)(lane >> 4);  // this row's byte of the packed slots
   const int comp = comp_of_row_lane(lane);
   const bool lo2 = (lane & 2) == 0, lo1 = (lane & 1) == 0;
+  float *gacc = gacc2;
   // the constant factor each owner lane applies to its sum after the reduction
   // (powers of two: exact): -1/2 for the two squared offsets
   const float post = (comp == 2 || comp == 4) ? -0.5f : 1.0f;
@@ -242,6 +244,12 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
   float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0, q2 = q0;
   // x.last becomes, per batch, the limit last - (the batch's first position)
   int lbase = 0;
+  // Two sets of accumulators and gradient rows alternate between batches: a
+  // batch's sums are flushed after the next batch is staged, so the atomics
+  // have that batch's walk to drain before the next wait on memory (one
+  // counter covers loads and stores).
+  int buf = 0;
+  uint64_t pend = 0;  // the batch waiting for its flush (in set buf ^ 1)
   const int nbat = max(max(nbw[0], nbw[1]), max(nbw[2], nbw[3]));
   for (int r0 = (nbat - 1) & ~63; r0 >= 0; r0 -= 64) {
     // lane i holds the words of batch r0 + i, one per quarter
@@ -294,10 +302,11 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         stage[lane].p0 = q0;
         stage[lane].p1 = p1;
         stage[lane].p2 = p2;
-        // the gradient row's byte offset (rows of 36 bytes; only when it fits)
-        stage[lane].p3 = make_int4(idc, valid_id(idc, n) ? 1 : 0,
-                                   WIDE ? 0 : (int)(36u * (uint32_t)idc), 0);
+        // the gradient row: its byte offset (rows of 36 bytes), or the id when WIDE
+        rows2[BATCH * buf + lane] =
+            valid_id(idc, n) ? (WIDE ? idc : (int)(36u * (uint32_t)idc)) : -1;
       }
+      if (pend) flush<WIDE>(pend, rows2 + BATCH * (buf ^ 1), gacc2 + 9 * SLOTS * (buf ^ 1), grads);
       // records of the next batch, ids of the one after it
       idc = idn;
       {
@@ -383,7 +392,7 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
         out *= comp == 5 ? s.p1.y : post;
         // the row's 9 sums go to the slot's accumulators in LDS (rows that took
         // the same splat add to the same ones; the dead slot collects zeros)
-        if (comp >= 0) atomicAdd(&gacc[9 * j + comp], out);
+        if (comp >= 0) atomicAdd(&gacc[9 * SLOTS * buf + 9 * j + comp], out);
       };
       // the four quarters' slots of a step, packed a byte each on the scalar
       // unit; a lane takes its row's byte (one bit-field extract)
@@ -416,12 +425,14 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
       else
         walk(std::false_type{});
       wave_sync();
-      flush<WIDE>(staged, stage, gacc, grads);
+      pend = staged;
+      buf ^= 1;
       if (mn < 0) break;
       mc = mn;
       mn = mnn;
     }
   }
+  if (pend) flush<WIDE>(pend, rows2 + BATCH * (buf ^ 1), gacc2 + 9 * SLOTS * (buf ^ 1), grads);
 }
 
 __device__ __forceinline__ int ceil64(int v) { return (max(v, 0) + 63) >> 6; }
@@ -436,17 +447,19 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
     const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads) {
   __shared__ Staged stage_all[GS_WAVES_PER_BLOCK][SLOTS];
-  __shared__ float gacc_all[GS_WAVES_PER_BLOCK][9 * SLOTS];  // per-slot gradient sums
+  // per-slot gradient sums and gradient rows, two sets per wave
+  __shared__ float gacc_all[GS_WAVES_PER_BLOCK][2 * 9 * SLOTS];
+  __shared__ int32_t rows_all[GS_WAVES_PER_BLOCK][2 * BATCH];
   Staged *stage = stage_all[wave_in_block()];
   float *gacc = gacc_all[wave_in_block()];
+  int32_t *rows = rows_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
   if (!fs.hdr->run_b) return;  // the frame failed earlier: nothing to differentiate
-  for (int i = __lane_id(); i < 9 * SLOTS; i += GS_WAVE) gacc[i] = 0.0f;
+  for (int i = __lane_id(); i < 2 * 9 * SLOTS; i += GS_WAVE) gacc[i] = 0.0f;
   if (__lane_id() == 0) {
     Staged dead;
     dead.p0 = dead.p1 = dead.p2 = make_float4(0.f, 0.f, 0.f, 0.f);
     dead.p2.y = -1.0f;  // tau < 0: q <= tau never holds
-    dead.p3 = make_int4(0, 0, 0, 0);
     stage[BATCH] = dead;
   }
   fs.nw = fs.hdr->nw;
@@ -503,7 +516,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
 #pragma unroll
       for (int q = 0; q < 4; q++) nbw[q] = ceil64(fs.sub_last[tile * 4 + q]);
       walk_back<WIDE>(splats, n, sorted_ids, rg.x, contrib_base(fs, 0, tile, rg.x), fs.nw, nbw, x,
-                      stage, gacc, grads);
+                      stage, gacc, rows, grads);
       continue;
     }
     // a chunk of a heavy tile: the lane's pixels are positions ql + 8 r of its
@@ -539,7 +552,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
 #pragma unroll
     for (int q = 0; q < 4; q++) nbw[q] = ceil64(fs.chunk_last[chunk_index(idx, p, q, k)]);
     walk_back<WIDE>(splats, n, sorted_ids, cs, contrib_base(fs, 0, tile, rg.x) + ((cs - rg.x) >> 6),
-                    fs.nw, nbw, x, stage, gacc, grads);
+                    fs.nw, nbw, x, stage, gacc, rows, grads);
   }
 }
 
