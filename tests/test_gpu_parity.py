@@ -242,6 +242,27 @@ def test_depth_range_beyond_sixteen_exponents_sorts_exactly():
     assert np.array_equal(host(r.ranges), ref["ranges"])
 
 
+@pytest.mark.parametrize("w,h", [(700, 500), (1600, 1400)])
+def test_tile_passes_without_keys_match_with_keys(w, h):
+    """The production path writes no sorted keys: its ids and ranges equal the
+    oracle's as those of the checking path do, on 1408 tiles (the high tile
+    digit ranked on 5 bits) and 8800 (on 8)."""
+    gsr = _gsr()
+    sc = scenegen.random_scene(w + h, 4000, w, h, 0.9 * w)
+    ref = oracle.frame(sc, fwd=False)
+    I0 = len(ref["sorted_ids"])
+    assert I0 > 0
+    for want_keys in (False, True):
+        r = gsr.Rasterizer(sc.camera, capacity=I0)
+        r._ensure(sc.n, I0)
+        r.splats[:sc.n].copy_(dev(ref["splats"]))
+        r.sorted_ids.fill_(-1)
+        I = r.bin_and_sort(sc.n, want_keys=want_keys)
+        assert I == I0
+        assert np.array_equal(host(r.sorted_ids)[:I], ref["sorted_ids"]), want_keys
+        assert np.array_equal(host(r.ranges), ref["ranges"]), want_keys
+
+
 def test_capacity_overflow_reports_and_recovers():
     gsr = _gsr()
     sc, ref = reference(1)
