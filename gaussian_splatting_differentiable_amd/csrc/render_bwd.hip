@@ -43,15 +43,38 @@ constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 // group's backward items stably by a quarter-octave bucket of that length.
 constexpr int BO_T = 1024, BO_W = BO_T / 64, BO_BITS = 6, BO_BINS = 1 << BO_BITS;
 
-// Walk length of a backward item: the longest of its four quarters' last hits.
+// Walk length of a backward item: its quarter's last hit, or the longest of
+// the four for a whole tile.
 __device__ __forceinline__ int item_len(const FwdState &fs, int it, int k) {
-  const int idx = item_index(it);
-  if (item_kind(it) == ITEM_PLAIN)
-    return max(max(fs.sub_last[idx * 4], fs.sub_last[idx * 4 + 1]),
-               max(fs.sub_last[idx * 4 + 2], fs.sub_last[idx * 4 + 3]));
-  const int p = item_chunk(it);
-  return max(max(fs.chunk_last[chunk_index(idx, p, 0, k)], fs.chunk_last[chunk_index(idx, p, 1, k)]),
-             max(fs.chunk_last[chunk_index(idx, p, 2, k)], fs.chunk_last[chunk_index(idx, p, 3, k)]));
+  const int idx = item_index(it), q = item_quad(it);
+  switch (item_kind(it)) {
+    case ITEM_PLAIN:
+      return max(max(fs.sub_last[idx * 4], fs.sub_last[idx * 4 + 1]),
+                 max(fs.sub_last[idx * 4 + 2], fs.sub_last[idx * 4 + 3]));
+    case ITEM_QUARTER:
+      return fs.sub_last[idx * 4 + q];
+    default:
+      return fs.chunk_last[chunk_index(idx, item_chunk(it), q, k)];
+  }
+}
+
+// A plain tile whose walk spans more entries than this is walked by quarters:
+// on a long list whose batches hold few contributors each, a batch costs about
+// one memory round trip for its records, and a whole tile visits every batch
+// where any of its quarters has a contributor.
+constexpr int SPLIT_WALK = 2048;
+
+// The backward item a forward item of the group's queue gives, or -1: a
+// chunk's quarter (pass B) gives itself; a plain tile gives one whole-tile
+// item (from its quarter 0), or one item per quarter when the frame has too
+// few tiles to keep the workers busy or the tile's walk is long.
+__device__ __forceinline__ int bwd_item(const FwdState &fs, int it, bool split) {
+  const int kind = item_kind(it), q = item_quad(it);
+  if (kind == ITEM_PASS_B) return it;
+  if (kind != ITEM_PLAIN) return -1;
+  if (split || item_len(fs, make_item(ITEM_PLAIN, 0, 0, item_index(it)), 0) > SPLIT_WALK)
+    return make_item(ITEM_QUARTER, q, 0, item_index(it));
+  return q == 0 ? it : -1;
 }
 
 __device__ __forceinline__ uint32_t order_bin(int len) {
@@ -90,9 +113,12 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   __syncthreads();
   const int chunk = (n + BO_W - 1) / BO_W;
   const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
+  // a frame with fewer tiles than half the workers walks its plain tiles by
+  // quarters: four times the items, each on one row of a wave
+  const bool split = 2 * ntiles < GS_WAVES_PER_BLOCK * nblocks;
   for (int e = c0 + lane; e < c1; e += 64) {
-    const int it = fs.items[lo + e];
-    if (item_quad(it) == 0) atomicAdd(&cnt[w][order_bin(item_len(fs, it, k))], 1);
+    const int it = bwd_item(fs, fs.items[lo + e], split);
+    if (it != -1) atomicAdd(&cnt[w][order_bin(item_len(fs, it, k))], 1);
   }
   __syncthreads();
   __shared__ int btot[BO_BINS];
@@ -124,8 +150,8 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int base = c0; base < c1; base += 64) {
     const int e = base + lane;
-    const int it = e < c1 ? fs.items[lo + e] : 0;
-    const bool valid = e < c1 && item_quad(it) == 0;
+    const int it = e < c1 ? bwd_item(fs, fs.items[lo + e], split) : -1;
+    const bool valid = it != -1;
     const uint32_t d = valid ? order_bin(item_len(fs, it, k)) : 0u;
     uint64_t peers = wave_ballot(valid);
 #pragma unroll
@@ -478,7 +504,11 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const int it = fs.bitems[t];
     const int kind = item_kind(it), p = item_chunk(it);
     const int idx = item_index(it);
-    const int tile = kind == ITEM_PLAIN ? idx : fs.order[idx];
+    const bool plain = kind == ITEM_PLAIN || kind == ITEM_QUARTER;
+    const int tile = plain ? idx : fs.order[idx];
+    // the quarters the item covers; the other rows have no pixels and no entries
+    const uint32_t qm = kind == ITEM_PLAIN ? 0xFu : 1u << item_quad(it);
+    const bool row_on = (qm >> quad) & 1u;
     const SubTile st = subtile_of(tile, quad, cam);  // this lane's quarter
     const int px = st.x0 + col;
     const int2 rg = ranges[tile];
@@ -491,7 +521,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     for (int r = 0; r < 4; r++) {
       const int py = st.y0 + r4 + r;
       x.fy[r] = (float)py + 0.5f;
-      in[r] = px < cam.width && py < cam.height;
+      in[r] = row_on && px < cam.width && py < cam.height;
       pix[r] = (int64_t)(st.prow + py) * cam.width + px;
       x.g[r][0] = x.g[r][1] = x.g[r][2] = 0.0f;
       ex[r] = 0.0f;
@@ -506,7 +536,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
       }
     }
     int nbw[4];
-    if (kind == ITEM_PLAIN) {
+    if (plain) {
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         x.T[r] = in[r] ? Tfin[pix[r]] : 1.0f;
@@ -514,7 +544,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
         x.acc[r] = ex[r];
       }
 #pragma unroll
-      for (int q = 0; q < 4; q++) nbw[q] = ceil64(fs.sub_last[tile * 4 + q]);
+      for (int q = 0; q < 4; q++) nbw[q] = (qm >> q) & 1u ? ceil64(fs.sub_last[tile * 4 + q]) : 0;
       walk_back<WIDE>(splats, n, sorted_ids, rg.x, contrib_base(fs, 0, tile, rg.x), fs.nw, nbw, x,
                       stage, gacc, rows, grads);
       continue;
@@ -550,7 +580,8 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
       x.last[r] = lb;
     }
 #pragma unroll
-    for (int q = 0; q < 4; q++) nbw[q] = ceil64(fs.chunk_last[chunk_index(idx, p, q, k)]);
+    for (int q = 0; q < 4; q++)
+      nbw[q] = (qm >> q) & 1u ? ceil64(fs.chunk_last[chunk_index(idx, p, q, k)]) : 0;
     walk_back<WIDE>(splats, n, sorted_ids, cs, contrib_base(fs, 0, tile, rg.x) + ((cs - rg.x) >> 6),
                     fs.nw, nbw, x, stage, gacc, rows, grads);
   }

@@ -16,7 +16,10 @@
 #define GS_SPIN_LIMIT (1 << 20)  // probes of a bounded wait (seconds at the longest back-off)
 
 // Item: kind (2 bits) | quad (2 bits) | chunk p (4 bits) | index (24 bits).
-enum ItemKind { ITEM_PLAIN = 0, ITEM_PASS_A = 1, ITEM_PASS_B = 2 };
+// The forward's items are quarters. The backward's: a whole plain tile
+// (ITEM_PLAIN), one quarter of a plain tile (ITEM_QUARTER) or one quarter of
+// a chunk (ITEM_PASS_B).
+enum ItemKind { ITEM_PLAIN = 0, ITEM_PASS_A = 1, ITEM_PASS_B = 2, ITEM_QUARTER = 3 };
 
 // Queues: one per XCD group. Tiles are grouped into GS_GROUPS vertical strips of
 // the image, so neighbouring tiles (which share splats) and the four quarters of
