@@ -31,7 +31,7 @@ EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project"
            "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views",
            "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
            "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views", "gs_timing_start",
-           "gs_timing_read", "gs_set_wait_limit")
+           "gs_timing_read", "gs_set_wait_limit", "gs_render_bwd_accumulate")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -93,6 +93,8 @@ def lib():
     L.gs_render_fwd_views.argtypes = [i32, P, P, P, cam_p, i32, C.POINTER(GsSched), P, P, P, P,
                                       sz, P, P, P, P, P]
     L.gs_render_bwd_views.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P, P]
+    L.gs_render_bwd_accumulate.argtypes = [i32, P, P, P, cam_p, i32, P, P, P, sz, P, P, P, P, P,
+                                           P]
     L.gs_sort_keys_noalloc.argtypes = [i32, P, cam_p, i64, P, P, P, P, P, P]
     L.gs_timing_start.argtypes = []
     L.gs_set_wait_limit.argtypes = [i32]
@@ -102,7 +104,8 @@ def lib():
                  "gs_project_bwd_views", "gs_bin_tiles_views", "gs_sort_keys_views",
                  "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views",
-                 "gs_timing_start", "gs_timing_read", "gs_set_wait_limit"):
+                 "gs_timing_start", "gs_timing_read", "gs_set_wait_limit",
+                 "gs_render_bwd_accumulate"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -244,6 +247,20 @@ def gs_render_bwd_views(n, splats, sorted_ids, ranges, cam, n_views, T_final, la
                                      _ptr(dL_drgb), _ptr(dL_dsplat), _ptr(status),
                                      _bg3(background), _ptr(dL_dT), _stream(stream)),
            "gs_render_bwd_views")
+
+
+def gs_render_bwd_accumulate(n, splats, sorted_ids, ranges, cam, n_views, T_final, last,
+                             fwd_state, dL_drgb, dL_dsplat, status, background=None, dL_dT=None,
+                             stream=None):
+    """gs_render_bwd_views (any n_views >= 1) adding into dL_dsplat, which the
+    caller initialises."""
+    _check(lib().gs_render_bwd_accumulate(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
+                                          C.byref(cam), int(n_views), _ptr(T_final), _ptr(last),
+                                          _ptr(fwd_state),
+                                          fwd_state.numel() * fwd_state.element_size(),
+                                          _ptr(dL_drgb), _ptr(dL_dsplat), _ptr(status),
+                                          _bg3(background), _ptr(dL_dT), _stream(stream)),
+           "gs_render_bwd_accumulate")
 
 
 # ------------------------------------------------------------------ C-named calls

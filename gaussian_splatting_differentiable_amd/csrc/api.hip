@@ -38,8 +38,8 @@ hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, cons
 hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                const float *dT, float *grads, int32_t *status, int workers_waves,
-                                hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
+                                const float *dT, float *grads, bool accumulate, int32_t *status,
+                                int workers_waves, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 
 // The probe limit of the device-side bounded waits (below 0: each wait's own
 // default). Only tests of the give-up path change it.
@@ -357,7 +357,7 @@ int32_t bwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
                  const int32_t *tile_ranges, CamK k, const float *T_final, const int32_t *last,
                  void *fwd_state, size_t fwd_state_bytes, const float *dL_drgb, float *dL_dsplat,
                  int32_t *device_status, const float *background, const float *dL_dT,
-                 void *stream) {
+                 bool accumulate, void *stream) {
   if (n < 0 || !set_background(background, &k)) return GS_ERR_INVALID_ARGUMENT;
   if (dL_dT) k.bg_on = 1;
   if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT) return GS_ERR_UNSUPPORTED;
@@ -374,8 +374,8 @@ int32_t bwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
   hipEvent_t e0, e1;
   timing_slot(1, e0, e1);
   return hip_status(gs_launch_render_bwd(n, splats, sorted_ids, tile_ranges, k, T_final, last,
-                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, device_status,
-                                         workers, e0, e1, (hipStream_t)stream));
+                                         fwd_state, dL_drgb, dL_dT, dL_dsplat, accumulate,
+                                         device_status, workers, e0, e1, (hipStream_t)stream));
 }
 
 // The camera of view 0 of a batch, with every view checked to be valid and of
@@ -452,7 +452,8 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
   CamK k;
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
-                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, stream);
+                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, false,
+                  stream);
 }
 
 int32_t gs_render_bwd(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -584,7 +585,21 @@ int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorte
   CamK k;
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
-                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, stream);
+                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, false,
+                  stream);
+}
+
+int32_t gs_render_bwd_accumulate(int32_t n, const float *splats, const int32_t *sorted_ids,
+                                 const int32_t *tile_ranges, const gs_camera *cam,
+                                 int32_t n_views, const float *T_final, const int32_t *last,
+                                 void *fwd_state, size_t fwd_state_bytes, const float *dL_drgb,
+                                 float *dL_dsplat, int32_t *device_status,
+                                 const float *background, const float *dL_dT, void *stream) {
+  CamK k;
+  if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
+  return bwd_impl(n, splats, sorted_ids, tile_ranges, k, T_final, last, fwd_state,
+                  fwd_state_bytes, dL_drgb, dL_dsplat, device_status, background, dL_dT, true,
+                  stream);
 }
 
 // ---------------------------------------------------------------- allocation-free sort

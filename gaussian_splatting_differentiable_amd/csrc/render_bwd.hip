@@ -592,12 +592,14 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
 hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const float *T,
                                 const int32_t *last, void *fwd_state, const float *dL,
-                                const float *dT, float *grads, int32_t *status, int workers_waves,
-                                hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
+                                const float *dT, float *grads, bool accumulate, int32_t *status,
+                                int workers_waves, hipEvent_t ev0, hipEvent_t ev1,
+                                hipStream_t st) {
   const int64_t ng = 9 * (int64_t)n;
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
-  const int zero_blocks = (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
+  // accumulating: the caller's gradient array is the starting point, not zeroed
+  const int zero_blocks = accumulate ? 0 : (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
   hipLaunchKernelGGL(k_bwd_prep, dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
                      reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng, status);
   if (ev0) {

@@ -320,6 +320,22 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
                          const float *dL_drgb, float *dL_dsplat, int32_t *device_status,
                          const float *background, const float *dL_dT, void *stream);
 
+/* gs_render_bwd_bg (n_views 1) or gs_render_bwd_views (n_views > 1) adding
+ * the gradients into dL_dsplat instead of overwriting it: the caller
+ * initialises the array (zeros for one frame's gradients, or the sums of
+ * earlier calls to accumulate over frames or batches). For callers that clear
+ * the array elsewhere, e.g. on another stream while the frame is sorted, so
+ * the call itself writes only the splats the frame touches. A frame whose
+ * device_status is not GS_OK on entry adds nothing. Float atomics make the
+ * low-order bits depend on the order of the additions. Other arguments,
+ * outputs and errors as for gs_render_bwd_views. */
+int32_t gs_render_bwd_accumulate(int32_t n, const float *splats, const int32_t *sorted_ids,
+                                 const int32_t *tile_ranges, const gs_camera *cam,
+                                 int32_t n_views, const float *T_final, const int32_t *last,
+                                 void *fwd_state, size_t fwd_state_bytes, const float *dL_drgb,
+                                 float *dL_dsplat, int32_t *device_status,
+                                 const float *background, const float *dL_dT, void *stream);
+
 /* Batches of views: n_views cameras of one size (1 <= n_views <= GS_MAX_VIEWS)
  * rendered as one image, so that binning, sorting and each of the two
  * persistent raster kernels run once for the whole batch (one schedule, one
