@@ -42,6 +42,7 @@ constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 // of tiles whose pixels saturate early). One workgroup per group sorts the
 // group's backward items stably by a quarter-octave bucket of that length.
 constexpr int BO_T = 1024, BO_W = BO_T / 64, BO_BITS = 6, BO_BINS = 1 << BO_BITS;
+constexpr int BO_IPL = 4;  // items per lane per span of the queue build
 
 // Walk length of a backward item: its quarter's last hit, or the longest of
 // the four for a whole tile.
@@ -64,16 +65,25 @@ __device__ __forceinline__ int item_len(const FwdState &fs, int it, int k) {
 // where any of its quarters has a contributor.
 constexpr int SPLIT_WALK = 2048;
 
-// The backward item a forward item of the group's queue gives, or -1: a
-// chunk's quarter (pass B) gives itself; a plain tile gives one whole-tile
-// item (from its quarter 0), or one item per quarter when the frame has too
-// few tiles to keep the workers busy or the tile's walk is long.
-__device__ __forceinline__ int bwd_item(const FwdState &fs, int it, bool split) {
-  const int kind = item_kind(it), q = item_quad(it);
-  if (kind == ITEM_PASS_B) return it;
+// The backward item a forward item of the group's queue gives, or -1, and its
+// walk length: a chunk's quarter (pass B) gives itself; a plain tile gives one
+// whole-tile item (from its quarter 0), or one item per quarter when the frame
+// has too few tiles to keep the workers busy or the tile's walk is long.
+__device__ __forceinline__ int bwd_item(const FwdState &fs, int it, bool split, int k, int &len) {
+  const int kind = item_kind(it), q = item_quad(it), idx = item_index(it);
+  len = 0;
+  if (kind == ITEM_PASS_B) {
+    len = item_len(fs, it, k);
+    return it;
+  }
   if (kind != ITEM_PLAIN) return -1;
-  if (split || item_len(fs, make_item(ITEM_PLAIN, 0, 0, item_index(it)), 0) > SPLIT_WALK)
-    return make_item(ITEM_QUARTER, q, 0, item_index(it));
+  const int4 v = *reinterpret_cast<const int4 *>(fs.sub_last + idx * 4);
+  const int whole = max(max(v.x, v.y), max(v.z, v.w));
+  if (split || whole > SPLIT_WALK) {
+    len = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+    return make_item(ITEM_QUARTER, q, 0, idx);
+  }
+  len = whole;
   return q == 0 ? it : -1;
 }
 
@@ -111,14 +121,38 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < BO_W * BO_BINS; i += BO_T) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  const int chunk = (n + BO_W - 1) / BO_W;
-  const int c0 = min(n, w * chunk), c1 = min(n, c0 + chunk);
   // a frame with fewer tiles than half the workers walks its plain tiles by
   // quarters: four times the items, each on one row of a wave
   const bool split = 2 * ntiles < GS_WAVES_PER_BLOCK * nblocks;
-  for (int e = c0 + lane; e < c1; e += 64) {
-    const int it = bwd_item(fs, fs.items[lo + e], split);
-    if (it != -1) atomicAdd(&cnt[w][order_bin(item_len(fs, it, k))], 1);
+  // the group's items in spans of BO_T * BO_IPL; wave w takes a contiguous
+  // piece of each, and a lane's items and their loads go out together (a span
+  // holds a garden-sized group, so its items stay in registers for the scatter)
+  constexpr int SPAN = BO_T * BO_IPL;
+  int itr[BO_IPL];
+  uint32_t dr[BO_IPL];
+  int c0 = 0;
+  auto load_span = [&](int o) {
+    const int m = min(SPAN, n - o), per = (m + BO_W - 1) / BO_W;
+    c0 = o + min(m, w * per);
+    const int c1 = o + min(m, w * per + per);
+    int raw[BO_IPL];
+#pragma unroll
+    for (int j = 0; j < BO_IPL; j++) {
+      const int e = c0 + lane + 64 * j;
+      raw[j] = e < c1 ? fs.items[lo + e] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < BO_IPL; j++) {
+      int len = 0;
+      itr[j] = raw[j] != -1 ? bwd_item(fs, raw[j], split, k, len) : -1;
+      dr[j] = order_bin(len);
+    }
+  };
+  for (int o = 0; o < n; o += SPAN) {
+    load_span(o);
+#pragma unroll
+    for (int j = 0; j < BO_IPL; j++)
+      if (itr[j] != -1) atomicAdd(&cnt[w][dr[j]], 1);
   }
   __syncthreads();
   __shared__ int btot[BO_BINS];
@@ -148,22 +182,24 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   }
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int base = c0; base < c1; base += 64) {
-    const int e = base + lane;
-    const int it = e < c1 ? bwd_item(fs, fs.items[lo + e], split) : -1;
-    const bool valid = it != -1;
-    const uint32_t d = valid ? order_bin(item_len(fs, it, k)) : 0u;
-    uint64_t peers = wave_ballot(valid);
+  for (int o = 0; o < n; o += SPAN) {
+    if (n > SPAN) load_span(o);
 #pragma unroll
-    for (int b = 0; b < BO_BITS; b++) {
-      const uint64_t bal = wave_ballot((d >> b) & 1u);
-      peers &= ((d >> b) & 1u) ? bal : ~bal;
-    }
-    if (valid) {
-      const int below = __popcll(peers & lt);
-      const int pos = cnt[w][d] + below;
-      fs.bitems[lo + pos] = it;
-      if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+    for (int j = 0; j < BO_IPL; j++) {
+      const bool valid = itr[j] != -1;
+      const uint32_t d = valid ? dr[j] : 0u;
+      uint64_t peers = wave_ballot(valid);
+#pragma unroll
+      for (int b = 0; b < BO_BITS; b++) {
+        const uint64_t bal = wave_ballot((d >> b) & 1u);
+        peers &= ((d >> b) & 1u) ? bal : ~bal;
+      }
+      if (valid) {
+        const int below = __popcll(peers & lt);
+        const int pos = cnt[w][d] + below;
+        fs.bitems[lo + pos] = itr[j];
+        if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+      }
     }
   }
 }
