@@ -92,11 +92,35 @@ __device__ __forceinline__ uint32_t order_bin(int len) {
   return (uint32_t)(BO_BINS - 1 - min(b, BO_BINS - 1));  // ascending bin = longest first
 }
 
+__device__ __forceinline__ int ceil64(int v) { return (max(v, 0) + 63) >> 6; }
+
+// Pieces of a plain walk of nb batches: one per cut below nb, and the rest.
+__device__ __forceinline__ int pieces_of(int nb) {
+  int p = 1;
+#pragma unroll
+  for (int c = 0; c < GS_NCUT; c++) p += cut_batch(c) < nb ? 1 : 0;
+  return p;
+}
+
+// Batches [a, e) of piece i of a plain walk of nb batches; piece i < the last
+// ends at cut i.
+__device__ __forceinline__ void piece_range(int i, int nb, int &a, int &e) {
+  a = i == 0 ? 0 : cut_batch(i - 1);
+  e = i < GS_NCUT && cut_batch(i) < nb ? cut_batch(i) : nb;
+}
+
+// In a frame with few tiles, a plain walk is cut into pieces when it spans at
+// least 3 batches and more than its group's batches per worker: only then can
+// one walk outlast the rest of the frame's work, and each piece costs a walk's
+// start-up (a chain of dependent loads) again.
+
 // The backward's preparation in one launch: workgroup g < GS_GROUPS builds group
-// g's backward queue: the forward's plain and pass-B items of quarter 0 stand
-// for their whole tile or chunk (a backward item covers all four quarters),
-// stably sorted longest first; the others zero the gradient output. The frame runs only
-// if its status is still GS_OK.
+// g's backward queue: each of the forward's plain and pass-B items gives its
+// backward items (a whole tile, or in a frame with few tiles (FEW) a quarter
+// or its pieces between cuts, or the chunk quarter), stably sorted longest
+// first; the others zero the gradient output. The frame runs only if its
+// status is still GS_OK.
+template <bool FEW>
 __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int ntiles,
                                                   int nblocks, float *__restrict__ grads,
                                                   int64_t ng, const int32_t *__restrict__ status) {
@@ -118,18 +142,20 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
   const int g = blockIdx.x, k = fs.hdr->k;
   const int lo = fs.hdr->qoff[g] + fs.hdr->qa[g], hi = run ? fs.hdr->qoff[g + 1] : lo;
   const int n = hi - lo;
+  const int blo = bwd_base(fs.hdr, g);  // at most GS_PIECES backward items per forward item
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ int load;  // the group's walks in batches
   for (int i = threadIdx.x; i < BO_W * BO_BINS; i += BO_T) (&cnt[0][0])[i] = 0;
+  if (threadIdx.x == 0) load = 0;
   __syncthreads();
-  // a frame with fewer tiles than half the workers walks its plain tiles by
-  // quarters: four times the items, each on one row of a wave
-  const bool split = 2 * ntiles < GS_WAVES_PER_BLOCK * nblocks;
   // the group's items in spans of BO_T * BO_IPL; wave w takes a contiguous
   // piece of each, and a lane's items and their loads go out together (a span
   // holds a garden-sized group, so its items stay in registers for the scatter)
   constexpr int SPAN = BO_T * BO_IPL;
-  int itr[BO_IPL];
-  uint32_t dr[BO_IPL];
+  int itr[BO_IPL], ln[BO_IPL], np[BO_IPL];
+  uint32_t dr[BO_IPL];  // the bin of the whole walk
+#pragma unroll
+  for (int j = 0; j < BO_IPL; j++) itr[j] = -1;
   int c0 = 0;
   auto load_span = [&](int o) {
     const int m = min(SPAN, n - o), per = (m + BO_W - 1) / BO_W;
@@ -143,16 +169,63 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
     }
 #pragma unroll
     for (int j = 0; j < BO_IPL; j++) {
-      int len = 0;
-      itr[j] = raw[j] != -1 ? bwd_item(fs, raw[j], split, k, len) : -1;
-      dr[j] = order_bin(len);
+      ln[j] = 0;
+      itr[j] = raw[j] != -1 ? bwd_item(fs, raw[j], FEW, k, ln[j]) : -1;
+      dr[j] = order_bin(ln[j]);
     }
   };
-  for (int o = 0; o < n; o += SPAN) {
-    load_span(o);
+  // 1. the group's load: its walks' batches (a frame with few tiles cuts the
+  //    walks longer than its batches per worker)
+  if constexpr (FEW) {
+    int mine = 0;
+    for (int o = 0; o < n; o += SPAN) {
+      load_span(o);
 #pragma unroll
-    for (int j = 0; j < BO_IPL; j++)
-      if (itr[j] != -1) atomicAdd(&cnt[w][dr[j]], 1);
+      for (int j = 0; j < BO_IPL; j++) mine += itr[j] != -1 ? ceil64(ln[j]) : 0;
+    }
+    if (mine) atomicAdd(&load, mine);
+    __syncthreads();
+  }
+  const int64_t wl = group_workers(g, nblocks);
+  auto set_pieces = [&]() {
+#pragma unroll
+    for (int j = 0; j < BO_IPL; j++) {
+      const int nb = ceil64(ln[j]);
+      np[j] = itr[j] == -1 ? 0
+              : FEW && item_kind(itr[j]) != ITEM_PASS_B && nb >= 3 && nb * wl > (int64_t)load
+                  ? pieces_of(nb)
+                  : 1;
+    }
+  };
+  // piece i of item j (its walk length in entries sets its bin)
+  auto piece = [&](int j, int i, uint32_t &bin) {
+    if (np[j] == 1) {
+      bin = dr[j];
+      return itr[j];
+    }
+    int a, e;
+    piece_range(i, ceil64(ln[j]), a, e);
+    bin = order_bin(min(ln[j], 64 * e) - 64 * a);
+    return itr[j] | ((i + 1) << 24);
+  };
+  // 2. counts per bin
+  if (FEW && n <= SPAN) set_pieces();
+  for (int o = 0; o < n; o += SPAN) {
+    if (!FEW || n > SPAN) load_span(o);
+    if constexpr (FEW) {
+      if (n > SPAN) set_pieces();
+#pragma unroll
+      for (int j = 0; j < BO_IPL; j++)
+        for (int i = 0; i < np[j]; i++) {
+          uint32_t d;
+          piece(j, i, d);
+          atomicAdd(&cnt[w][d], 1);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < BO_IPL; j++)
+        if (itr[j] != -1) atomicAdd(&cnt[w][dr[j]], 1);
+    }
   }
   __syncthreads();
   __shared__ int btot[BO_BINS];
@@ -181,24 +254,44 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
     }
   }
   __syncthreads();
+  // 3. scatter, in the order the counts were taken
   const uint64_t lt = (1ull << lane) - 1ull;
+  // piece i of a lane's item j (or the whole walk), ranked among the wave's
+  // lanes with the same bin
+  auto place = [&](int j, int i) {
+    const bool valid = FEW ? i < np[j] : itr[j] != -1;
+    uint32_t d = 0;
+    int item = -1;
+    if constexpr (FEW) {
+      if (valid) item = piece(j, i, d);
+    } else {
+      d = valid ? dr[j] : 0u;
+      item = itr[j];
+    }
+    uint64_t peers = wave_ballot(valid);
+#pragma unroll
+    for (int b = 0; b < BO_BITS; b++) {
+      const uint64_t bal = wave_ballot((d >> b) & 1u);
+      peers &= ((d >> b) & 1u) ? bal : ~bal;
+    }
+    if (valid) {
+      const int below = __popcll(peers & lt);
+      const int pos = cnt[w][d] + below;
+      fs.bitems[blo + pos] = item;
+      if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+    }
+  };
   for (int o = 0; o < n; o += SPAN) {
-    if (n > SPAN) load_span(o);
+    if (n > SPAN) {
+      load_span(o);
+      if constexpr (FEW) set_pieces();
+    }
 #pragma unroll
     for (int j = 0; j < BO_IPL; j++) {
-      const bool valid = itr[j] != -1;
-      const uint32_t d = valid ? dr[j] : 0u;
-      uint64_t peers = wave_ballot(valid);
-#pragma unroll
-      for (int b = 0; b < BO_BITS; b++) {
-        const uint64_t bal = wave_ballot((d >> b) & 1u);
-        peers &= ((d >> b) & 1u) ? bal : ~bal;
-      }
-      if (valid) {
-        const int below = __popcll(peers & lt);
-        const int pos = cnt[w][d] + below;
-        fs.bitems[lo + pos] = itr[j];
-        if (below == __popcll(peers) - 1) cnt[w][d] = pos + 1;
+      place(j, 0);
+      if constexpr (FEW) {
+        if (wave_ballot(np[j] > 1))
+          for (int i = 1; i < GS_PIECES; i++) place(j, i);
       }
     }
   }
@@ -497,8 +590,6 @@ __device__ __forceinline__ void walk_back(const Splat *__restrict__ splats, int 
   if (pend) flush<WIDE>(pend, rows2 + BATCH * (buf ^ 1), gacc2 + 9 * SLOTS * (buf ^ 1), grads);
 }
 
-__device__ __forceinline__ int ceil64(int v) { return (max(v, 0) + 63) >> 6; }
-
 // WIDE: the gradient array is larger than 32-bit byte offsets reach (n above
 // 119M), so the atomics take 64-bit addresses.
 template <bool WIDE>
@@ -579,10 +670,54 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
         x.last[r] = in[r] ? last[pix[r]] : 0;
         x.acc[r] = ex[r];
       }
+      int nb = 0;
 #pragma unroll
-      for (int q = 0; q < 4; q++) nbw[q] = (qm >> q) & 1u ? ceil64(fs.sub_last[tile * 4 + q]) : 0;
-      walk_back<WIDE>(splats, n, sorted_ids, rg.x, contrib_base(fs, 0, tile, rg.x), fs.nw, nbw, x,
-                      stage, gacc, rows, grads);
+      for (int q = 0; q < 4; q++) {
+        nbw[q] = (qm >> q) & 1u ? ceil64(fs.sub_last[tile * 4 + q]) : 0;
+        nb = max(nb, nbw[q]);
+      }
+      // piece p - 1 of the walk: batches [a, e); one that ends at a cut starts
+      // from the forward pass's state there, in the quarters whose walk reached it
+      int a = 0;
+      if (p > 0) {
+        int e;
+        piece_range(p - 1, nb, a, e);
+        const int c = p - 1;
+        const int qc = row_on ? fs.qcut[tile * 4 + quad] : 0;
+        if (e < nb && qc > c) {
+          const float *cr = fs.cut + (size_t)tile * GS_CUT_FLOATS + 64 * quad + col + 8 * r4;
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            if (!in[r]) continue;
+            const float *cp = cr + 8 * r;
+            const float Tc = cp[4 * 256 * c];
+            // the colour behind the cut: the segment after the last cut
+            // reached, then those that end at cuts c + 1 .. qc - 1
+            float cb[3];
+#pragma unroll
+            for (int ch = 0; ch < 3; ch++) cb[ch] = cp[4 * 256 * GS_NCUT + 256 * ch];
+#pragma unroll
+            for (int s2 = GS_NCUT - 1; s2 > 0; s2--)
+              if (s2 > c && s2 < qc) {
+#pragma unroll
+                for (int ch = 0; ch < 3; ch++) cb[ch] += cp[4 * 256 * s2 + 256 * (ch + 1)];
+              }
+            float behind = __builtin_fmaf(cb[0], x.g[r][0],
+                                          __builtin_fmaf(cb[1], x.g[r][1], cb[2] * x.g[r][2]));
+            behind = __builtin_fmaf(x.T[r], ex[r], behind);
+            // a pixel still blending at the cut has consumed every entry before it
+            if (Tc >= 1e-4f) x.last[r] = 64 * e;
+            x.acc[r] = behind / Tc;
+            x.T[r] = Tc;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) nbw[q] = max(0, min(nbw[q], e) - a);
+#pragma unroll
+        for (int r = 0; r < 4; r++) x.last[r] -= 64 * a;
+      }
+      walk_back<WIDE>(splats, n, sorted_ids, rg.x + 64 * a, contrib_base(fs, 0, tile, rg.x) + a,
+                      fs.nw, nbw, x, stage, gacc, rows, grads);
       continue;
     }
     // a chunk of a heavy tile: the lane's pixels are positions ql + 8 r of its
@@ -636,7 +771,8 @@ hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorte
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   // accumulating: the caller's gradient array is the starting point, not zeroed
   const int zero_blocks = accumulate ? 0 : (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
-  hipLaunchKernelGGL(k_bwd_prep, dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
+  hipLaunchKernelGGL(few_tiles(ntiles, nblocks) ? k_bwd_prep<true> : k_bwd_prep<false>,
+                     dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
                      reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng, status);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, st);

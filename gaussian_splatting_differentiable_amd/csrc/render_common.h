@@ -18,7 +18,8 @@
 // Item: kind (2 bits) | quad (2 bits) | chunk p (4 bits) | index (24 bits).
 // The forward's items are quarters. The backward's: a whole plain tile
 // (ITEM_PLAIN), one quarter of a plain tile (ITEM_QUARTER) or one quarter of
-// a chunk (ITEM_PASS_B).
+// a chunk (ITEM_PASS_B); for the first two, p = 0 is the whole walk and
+// p = i + 1 its piece i between cuts.
 enum ItemKind { ITEM_PLAIN = 0, ITEM_PASS_A = 1, ITEM_PASS_B = 2, ITEM_QUARTER = 3 };
 
 // Queues: one per XCD group. Tiles are grouped into GS_GROUPS vertical strips of
@@ -53,7 +54,8 @@ struct PlanHdr {
   // its index within its group (in the forward only in groups without chunk
   // items, since a pass-B item waits on items in front of it).
   int32_t init_f[GS_GROUPS], init_b[GS_GROUPS];
-  // The backward's items of group g (half tiles) are bitems[qoff[g] + qa[g], + nb[g]).
+  // The backward's items of group g are bitems[bwd_base(g), + nb[g]): at most
+  // GS_PIECES per forward item of the group's plain and pass-B items.
   int32_t nb[GS_GROUPS];
   // The raster kernels run only when these are set: the frame's device status
   // was GS_OK when the schedule (forward) or the backward's preparation ran.
@@ -82,11 +84,38 @@ __host__ __device__ inline int64_t contrib_words(int T, int64_t cap) {
   return (cap + 63) / 64 + T + 2;
 }
 
+// Cut points of a plain tile's walk. The backward may walk a long tile as
+// pieces between cuts, side by side: the piece that ends at a cut starts from
+// the state the forward pass left there: per pixel the transmittance T at the
+// cut, and the colour of every segment of the walk (the entries between two
+// cuts), so its accumulator is (the colours of the segments behind the cut) .
+// dL/dC + T_final (bg . dL/dC + dL/dT), divided by T at the cut: the sum over
+// everything behind the cut, per unit T, which walking back from the end would
+// have reached there. Cut c lies before batch cut_batch(c) of the tile's list.
+#define GS_NCUT 3
+#define GS_PIECES (GS_NCUT + 1)
+__host__ __device__ __forceinline__ int cut_batch(int c) { return 2 << c; }
+// A tile's cut record: floats [(4 c + ch) * 256 + 64 q + l] hold, for cut c and
+// pixel l of quarter q, ch 0 T at the cut and ch 1..3 the colour of the segment
+// that ends there; floats [(4 GS_NCUT + ch) * 256 + 64 q + l] the colour of the
+// segment after the last cut the walk reached. A quarter writes them when its
+// walk reaches a cut; qcut[4 tile + q] counts the cuts it reached.
+#define GS_CUT_FLOATS ((4 * GS_NCUT + 3) * 256)
+
+// A frame with fewer tiles than half the workers (nblocks workgroups) keeps
+// them busy only with smaller items: its backward walks plain tiles by
+// quarters, and only such a frame records cuts and walks long quarters in
+// pieces (with more tiles than that, the walks' start-up costs more than the
+// longest walks do).
+__host__ __device__ __forceinline__ bool few_tiles(int ntiles, int nblocks) {
+  return 2 * ntiles < GS_WAVES_PER_BLOCK * nblocks;
+}
+
 // Byte layout of fwd_state for T tiles and a pair capacity cap (the contributor
 // bitmap comes last, so the capacity a state serves follows from its size).
 struct FwdLayout {
   size_t hdr, heads, sub_last, order, counts, items, sat, doneA, doneB, chunk_last, PA, CB, TB,
-      LB, HB, bitems, contrib, total;
+      LB, HB, bitems, qcut, cut, contrib, total;
 };
 
 __host__ __device__ inline FwdLayout fwd_layout(int T, int64_t cap) {
@@ -113,7 +142,9 @@ __host__ __device__ inline FwdLayout fwd_layout(int T, int64_t cap) {
   L.TB = take(4 * cq * 64);
   L.LB = take(4 * cq * 64);
   L.HB = take(4 * cq * 64);
-  L.bitems = take(4 * ((size_t)T * 4 + 2 * cq));
+  L.bitems = take(4 * (size_t)GS_PIECES * ((size_t)T * 4 + 2 * cq));
+  L.qcut = take(4 * (size_t)T * 4);
+  L.cut = take(4 * (size_t)T * GS_CUT_FLOATS);
   L.contrib = take(8 * 4 * (size_t)contrib_words(T, cap));
   L.total = off;
   return L;
@@ -135,6 +166,8 @@ struct FwdState {
   int32_t *LB;
   int32_t *HB;      // pass B's per-pixel hit counts (only when the forward counts)
   int32_t *bitems;  // the backward's queue items, longest walk first within each group
+  int32_t *qcut;    // per quarter: the cuts its forward walk reached
+  float *cut;       // per tile: the cut record (GS_CUT_FLOATS)
   uint64_t *contrib;  // [4][nw] contributor words
   int64_t nw;         // words per quarter: the schedule sets hdr->nw, kernels copy it here
 };
@@ -161,6 +194,8 @@ __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
   s.LB = reinterpret_cast<int32_t *>(b + L.LB);
   s.HB = reinterpret_cast<int32_t *>(b + L.HB);
   s.bitems = reinterpret_cast<int32_t *>(b + L.bitems);
+  s.qcut = reinterpret_cast<int32_t *>(b + L.qcut);
+  s.cut = reinterpret_cast<float *>(b + L.cut);
   s.contrib = reinterpret_cast<uint64_t *>(b + L.contrib);
   s.nw = 0;
   return s;
@@ -174,6 +209,11 @@ __host__ __device__ __forceinline__ uint64_t *contrib_base(const FwdState &fs, i
 
 __host__ __device__ __forceinline__ int32_t *queue_head(const FwdState &fs, int pass, int g) {
   return fs.heads + (pass * GS_GROUPS + g) * GS_HEAD_STRIDE;
+}
+
+// First of group g's backward items in bitems[].
+__host__ __device__ __forceinline__ int bwd_base(const PlanHdr *hd, int g) {
+  return GS_PIECES * (hd->qoff[g] + hd->qa[g]);
 }
 
 
@@ -324,7 +364,7 @@ __device__ __forceinline__ void walk_worklist(uint64_t w, const Rec *sbuf, F &&f
 // g is recorded as drained in the wave and in the workgroup's LDS mask).
 __device__ __forceinline__ int pop_group(const FwdState &fs, int pass, Worker &w, int g) {
   const PlanHdr *hd = fs.hdr;
-  const int lo = hd->qoff[g] + (pass ? hd->qa[g] : 0);
+  const int lo = pass ? bwd_base(hd, g) : hd->qoff[g];
   const int hi = pass ? lo + hd->nb[g] : hd->qoff[g + 1];
   if (lo < hi) {
     const int t = queue_pop(queue_head(fs, pass, g));
@@ -338,8 +378,8 @@ __device__ __forceinline__ int pop_group(const FwdState &fs, int pass, Worker &w
 
 // Next item (an index into items[], or bitems[] for the backward) of a worker,
 // or -1 when every queue is empty. pass 0 (forward) serves every item of a
-// group; pass 1 (backward) serves the nb[g] half-tile items that its
-// preparation wrote where the group's plain and pass-B items start. The first item comes without a pop: the queue heads
+// group; pass 1 (backward) serves the nb[g] items that its preparation wrote
+// from bwd_base(g) on. The first item comes without a pop: the queue heads
 // start past the items handed out that way, so a frame's first wave of work
 // does not serialise on the heads. After that the worker pops its home group,
 // then the others nearest first (+1, -1, +2, ...), neighbouring strips sharing
@@ -355,7 +395,7 @@ __device__ __forceinline__ int next_item(const FwdState &fs, int pass, Worker &w
   const PlanHdr *hd = fs.hdr;
   if (w.round == 0) {
     const int init = pass ? hd->init_b[w.home] : hd->init_f[w.home];
-    if (w.wg < init) return hd->qoff[w.home] + (pass ? hd->qa[w.home] : 0) + w.wg;
+    if (w.wg < init) return (pass ? bwd_base(hd, w.home) : hd->qoff[w.home]) + w.wg;
   }
   for (int c = 0; c < GS_GROUPS; c++) {
     const int g = (w.home + (c + 1) / 2 * ((c & 1) ? 1 : -1) + GS_GROUPS) % GS_GROUPS;

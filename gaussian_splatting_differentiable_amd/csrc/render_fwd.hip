@@ -118,11 +118,19 @@ struct Blend {
 // clamp (alpha <= o), so its entries are blended without the min.
 // cw: the quarter's contributor word of the range's first batch; every batch
 // walked writes its word (bit j: some lane blended entry j of the batch).
-template <bool STATS>
+// CUTS (plain tiles of a frame with few tiles): cutp is this lane's pixel in
+// the tile's cut record; a walk that reaches a cut writes T there and the colour blended since
+// the previous cut, then blends on from zero, and writes the colour after its
+// last cut at the end; ncut counts the cuts reached. Every segment is a sum of
+// non-negative terms, so the backward's sums of the segments behind a cut keep
+// full relative precision (a difference of running totals would not); the
+// returned colour is the sum of the segments.
+template <bool STATS, bool CUTS>
 __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
                                              const int32_t *__restrict__ sids, int cs, int ce,
                                              int n, const SubTile &st, const Px &x, float T0,
                                              Splat *sbuf, uint64_t *__restrict__ cw,
+                                             float *__restrict__ cutp, int &ncut,
                                              uint32_t &nhits, uint32_t &nsteps,
                                              uint32_t &nhsteps) {
   Blend r;
@@ -135,7 +143,21 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
   const int lane = __lane_id();
   Pipe pp;
   if (alive && cs < ce) pipe_start(pp, splats, sids, cs, ce, n);
+  ncut = 0;
+  float D0 = 0.0f, D1 = 0.0f, D2 = 0.0f;  // the segments before the last cut reached
   for (int b = cs; b < ce && alive; b += BATCH) {
+    if (CUTS && ncut < GS_NCUT && b - cs == BATCH * cut_batch(ncut)) {
+      float *c = cutp + 4 * 256 * ncut;
+      c[0] = r.T;
+      c[256] = r.C0;
+      c[512] = r.C1;
+      c[768] = r.C2;
+      D0 += r.C0;
+      D1 += r.C1;
+      D2 += r.C2;
+      r.C0 = r.C1 = r.C2 = 0.0f;
+      ncut++;
+    }
     const bool cand = stage(pp.rec, st, &sbuf[lane]) && valid_id(pp.idc, n);
     const uint64_t work = wave_ballot(cand);
     const bool clamp = wave_ballot(cand && pp.rec.p1.y > 0.985f) != 0;
@@ -182,6 +204,15 @@ __device__ __forceinline__ Blend blend_range(const Splat *__restrict__ splats,
     if (bm) r.wlast = base + 64 - __builtin_clzll(bm);  // 1 + the last entry any lane blended
     if (lane == 0) cw[base >> 6] = bm;
     wave_sync();
+  }
+  if (CUTS && ncut > 0) {
+    float *c = cutp + 4 * 256 * GS_NCUT;
+    c[0] = r.C0;
+    c[256] = r.C1;
+    c[512] = r.C2;
+    r.C0 += D0;
+    r.C1 += D1;
+    r.C2 += D2;
   }
   return r;
 }
@@ -245,8 +276,9 @@ __device__ __forceinline__ int ld_i(const int32_t *p) {
 }
 
 // STATS: count hits, tested entries and sub-tile hits (only when the caller asks
-// for them: the counters cost a few scalar instructions per entry).
-template <bool STATS>
+// for them: the counters cost a few scalar instructions per entry). CUTS: the
+// frame has few tiles, and its plain walks record their state at the cuts.
+template <bool STATS, bool CUTS>
 __global__ void __launch_bounds__(GS_WAVE * GS_WAVES_PER_BLOCK)
 __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const Splat *__restrict__ splats, int n, const int32_t *__restrict__ sorted_ids,
@@ -278,12 +310,23 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const Px x = pixel_of(st, cam);
     if (kind == ITEM_PLAIN) {
       if (st.empty) {
-        if (lane == 0) fs.sub_last[tile * 4 + quad] = 0;
+        if (lane == 0) {
+          fs.sub_last[tile * 4 + quad] = 0;
+          fs.qcut[tile * 4 + quad] = 0;
+        }
         continue;
       }
-      const Blend r = blend_range<STATS>(splats, sorted_ids, rg.x, rg.y, n, st, x, 1.0f, sbuf,
-                                           contrib_base(fs, quad, tile, rg.x), nhits, nsteps,
-                                           nhsteps);
+      int ncut = 0;
+      Blend r;
+      if constexpr (CUTS)
+        r = blend_range<STATS, true>(splats, sorted_ids, rg.x, rg.y, n, st, x, 1.0f, sbuf,
+                                     contrib_base(fs, quad, tile, rg.x),
+                                     fs.cut + (size_t)tile * GS_CUT_FLOATS + 64 * quad + lane,
+                                     ncut, nhits, nsteps, nhsteps);
+      else
+        r = blend_range<STATS, false>(splats, sorted_ids, rg.x, rg.y, n, st, x, 1.0f, sbuf,
+                                      contrib_base(fs, quad, tile, rg.x), nullptr, ncut, nhits,
+                                      nsteps, nhsteps);
       if (x.inside) {
         rgb[x.p] = cam.bg_on ? fmaf(r.T, cam.bg[0], r.C0) : r.C0;
         rgb[P + x.p] = cam.bg_on ? fmaf(r.T, cam.bg[1], r.C1) : r.C1;
@@ -292,7 +335,10 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
         last[x.p] = r.consumed;
         if (STATS && pixel_hits) pixel_hits[x.p] += r.nh;
       }
-      if (lane == 0) fs.sub_last[tile * 4 + quad] = r.wlast;
+      if (lane == 0) {
+        fs.sub_last[tile * 4 + quad] = r.wlast;
+        fs.qcut[tile * 4 + quad] = ncut;
+      }
       continue;
     }
     int cs, ce;
@@ -348,9 +394,10 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     r.nh = 0;
     const bool skip = st.empty || ld_i(sat) < p;
     if (!skip) {
-      r = blend_range<STATS>(splats, sorted_ids, cs, ce, n, st, x, Tin, sbuf,
-                             contrib_base(fs, quad, tile, rg.x) + ((cs - rg.x) >> 6), nhits,
-                             nsteps, nhsteps);
+      int ncut = 0;
+      r = blend_range<STATS, false>(splats, sorted_ids, cs, ce, n, st, x, Tin, sbuf,
+                             contrib_base(fs, quad, tile, rg.x) + ((cs - rg.x) >> 6), nullptr,
+                             ncut, nhits, nsteps, nhsteps);
       if (!(x.inside && Tin >= T_STOP)) r.consumed = -1;  // stopped before this chunk
     }
     const int64_t cp = (int64_t)ci * 64 + lane;
@@ -437,8 +484,10 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
   // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
   // queues empty exit at once
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  const bool count = stats || pixel_hits;
-  hipLaunchKernelGGL(count ? k_render_fwd<true> : k_render_fwd<false>, dim3(nblocks),
+  const bool count = stats || pixel_hits, cuts = few_tiles(ntiles, nblocks);
+  auto kern = count ? (cuts ? k_render_fwd<true, true> : k_render_fwd<true, false>)
+                    : (cuts ? k_render_fwd<false, true> : k_render_fwd<false, false>);
+  hipLaunchKernelGGL(kern, dim3(nblocks),
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), n, sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,

@@ -96,7 +96,8 @@ def run_stages(gsr, sc, ref, capacity=None, sched=None, background=None, dL_dT=N
                          dL_dT=None if dL_dT is None else dev(dL_dT))
     r.check("stage parity frame")
     out.update(rgb=host(r.rgb), T=host(r.T), last=host(r.last), grads=host(grads),
-               stats=host(r.stats), pixel_hits=host(r.pixel_hits), plan=read_plan(r))
+               stats=host(r.stats), pixel_hits=host(r.pixel_hits), plan=read_plan(r),
+               bwd_queue=read_bwd_queue(r), tiles=r.tiles)
     return out
 
 
@@ -339,6 +340,26 @@ def test_full_size_configs(cfg):
           flush=True)
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_backward_pieces_between_cuts(cfg):
+    """In a frame with few tiles (tiny, small), long quarter walks are
+    differentiated as pieces between cuts, side by side, each from the forward
+    pass's state at its cut; garden (whole tiles) walks every tile whole. The
+    backward queue serves every walk once, and the gradients match the oracle
+    element by element."""
+    gsr = _gsr()
+    sc, ref = reference(cfg)
+    out = run_stages(gsr, sc, ref)
+    check_forward(ref, out)
+    check_backward(ref, out)
+    check_backward_elementwise(ref, out)
+    quarters = 2 * out["tiles"] < 4 * _workers()
+    assert quarters == (cfg != 3)
+    npieces = check_bwd_queue(*out["bwd_queue"], ref["ranges"], quarters)
+    assert npieces >= {1: 10, 2: 500, 3: 0}[cfg], npieces
+    print(f"config {cfg}: walks in pieces {npieces}", flush=True)
+
+
 def test_frame_of_more_than_8192_tiles():
     """A 1600x1400 frame with a ragged last row and column (8800 tiles): the
     schedule keeps its working arrays in the forward state instead of LDS, and
@@ -411,7 +432,8 @@ def _plan_layout(T):
     """Offsets into the opaque forward state, read here for checking only:
     header (h, k, nA, nplain, err, ntiles, group offsets, pass-A counts, static
     hand-out counts, ...), queue heads, per-quarter bounds, LPT order, sorted
-    counts, the queue items, ..., the contributor words (last)."""
+    counts, the queue items, ..., the backward's items (up to 4 per forward
+    item), the cut records, the contributor words (last)."""
     rnd = lambda b: (b + 255) // 256 * 256
     cq = 4096 * 4
     hdr = 0
@@ -422,9 +444,13 @@ def _plan_layout(T):
     items = counts + rnd(4 * T)
     off = items + rnd(4 * (4 * T + 2 * cq))
     for b in (4 * 2048 * 4, 4 * cq, 4 * 2048 * 4, 4 * cq, 4 * cq * 64, 4 * cq * 64 * 3,
-              4 * cq * 64, 4 * cq * 64, 4 * cq * 64, 4 * (4 * T + 2 * cq)):
+              4 * cq * 64, 4 * cq * 64, 4 * cq * 64):
         off += rnd(b)
-    return dict(hdr=hdr, heads=heads, order=order, counts=counts, items=items, contrib=off)
+    bitems = off
+    qcut = bitems + rnd(4 * 4 * (4 * T + 2 * cq))
+    off = qcut + rnd(4 * 4 * T) + rnd(4 * T * 15 * 256)
+    return dict(hdr=hdr, heads=heads, sub_last=sub_last, order=order, counts=counts, items=items,
+                bitems=bitems, qcut=qcut, contrib=off)
 
 
 def read_contrib(r, ranges):
@@ -462,6 +488,73 @@ def read_plan(r):
     return dict(h=int(hdr[0]), k=int(hdr[1]), nA=int(hdr[2]), err=int(hdr[4]), order=order,
                 counts=counts, qoff=qoff, qa=hdr[15:23].copy(), items=items.copy(),
                 run_f=int(hdr[47]))
+
+
+CUT_BATCHES = (2, 4, 8)  # a plain walk's cut points, in 64-entry batches
+
+
+def read_bwd_queue(r):
+    """The backward's items per group, and per quarter the forward's walk
+    length (1 + the last entry any pixel blended) and the cuts it reached."""
+    T = r.tiles
+    L = _plan_layout(T)
+    raw = host(r.fwd_state)
+    hdr = raw[:208].view(np.int32)
+    qoff, qa, nb = hdr[6:15], hdr[15:23], hdr[39:47]
+    groups = []
+    for g in range(8):
+        base = L["bitems"] + 4 * 4 * (int(qoff[g]) + int(qa[g]))
+        groups.append(raw[base:base + 4 * int(nb[g])].view(np.int32).copy())
+    sub_last = raw[L["sub_last"]:L["sub_last"] + 16 * T].view(np.int32).reshape(T, 4).copy()
+    qcut = raw[L["qcut"]:L["qcut"] + 16 * T].view(np.int32).reshape(T, 4).copy()
+    return groups, sub_last, qcut
+
+
+def check_bwd_queue(groups, sub_last, qcut, ranges, quarters):
+    """Every plain tile's walk (or, when quarters, every quarter's) is served
+    once: whole, or as all of its pieces between the cuts below its length;
+    a quarter reached every cut below its walk's end and none past its list.
+    Only a frame walked by quarters (few tiles) records cuts."""
+    items = np.concatenate(groups)
+    kind, quad, p, idx = (items >> 30) & 3, (items >> 28) & 3, (items >> 24) & 15, items & 0xFFFFFF
+    assert not np.any(kind == 1)
+    plain = kind != 2
+    seen = {}
+    for kd, q, pp, t in zip(kind[plain], quad[plain], p[plain], idx[plain]):
+        key = (int(t), int(q) if kd == 3 else -1)
+        assert (kd == 3) == quarters
+        seen.setdefault(key, []).append(int(pp))
+    T = len(ranges)
+    assert len(seen) == (4 * T if quarters else T)
+    npieces = 0
+    for (t, q), ps in seen.items():
+        walk = int(sub_last[t, q]) if q >= 0 else int(sub_last[t].max())
+        nb = (max(walk, 0) + 63) // 64
+        want = 1 + sum(c < nb for c in CUT_BATCHES)
+        assert sorted(ps) in ([0], list(range(1, want + 1))), (t, q, ps, nb)
+        npieces += len(ps) > 1
+    if not quarters:
+        assert npieces == 0 and not qcut.any()
+        return npieces
+    n_t = ranges[:, 1] - ranges[:, 0]
+    for c, b in enumerate(CUT_BATCHES):
+        assert np.all((qcut > c) >= (sub_last > 64 * b))
+        assert np.all((qcut > c) <= (n_t[:, None] > 64 * b))
+    return npieces
+
+
+def check_backward_elementwise(ref, out):
+    """Per gradient element: 99.9% within 5e-4 of |ref| + 1e-3 rms (the
+    component's), where the norm-wise check could hide a few bad splats. A
+    gradient is a sum over many pixels of terms of both signs, so fp32 leaves
+    up to a few 1e-4 on the worst of a thousand splats; a wrong term is off by
+    far more."""
+    g, gref = out["grads"].astype(np.float64), ref["grads"]
+    rms = np.sqrt((gref ** 2).mean(axis=0))
+    e = np.abs(g - gref) / (np.abs(gref) + 1e-3 * rms)
+    q = np.quantile(e, 0.999, axis=0)
+    assert np.all(q <= 5e-4), q
+    assert np.all(e.max(axis=0) <= 0.2), e.max(axis=0)
 
 
 def check_queues(plan, tiles_x):
