@@ -187,12 +187,14 @@ __global__ void __launch_bounds__(BO_T) k_bwd_prep(char *__restrict__ state, int
     __syncthreads();
   }
   const int64_t wl = group_workers(g, nblocks);
+  const bool cuts = records_cuts(ntiles, nblocks);  // the forward recorded the cuts
   auto set_pieces = [&]() {
 #pragma unroll
     for (int j = 0; j < BO_IPL; j++) {
       const int nb = ceil64(ln[j]);
       np[j] = itr[j] == -1 ? 0
-              : FEW && item_kind(itr[j]) != ITEM_PASS_B && nb >= 3 && nb * wl > (int64_t)load
+              : FEW && cuts && item_kind(itr[j]) != ITEM_PASS_B && nb >= 3 &&
+                        nb * wl > (int64_t)load
                   ? pieces_of(nb)
                   : 1;
     }

@@ -110,6 +110,12 @@ __host__ __device__ __forceinline__ int cut_batch(int c) { return 2 << c; }
 __host__ __device__ __forceinline__ bool few_tiles(int ntiles, int nblocks) {
   return 2 * ntiles < GS_WAVES_PER_BLOCK * nblocks;
 }
+// The forward state holds cut records for frames of up to GS_CUT_TILES_MAX
+// tiles (a frame with few tiles on 256 compute units has fewer than 2048).
+#define GS_CUT_TILES_MAX 2048
+__host__ __device__ __forceinline__ bool records_cuts(int ntiles, int nblocks) {
+  return few_tiles(ntiles, nblocks) && ntiles <= GS_CUT_TILES_MAX;
+}
 
 // Byte layout of fwd_state for T tiles and a pair capacity cap (the contributor
 // bitmap comes last, so the capacity a state serves follows from its size).
@@ -144,7 +150,7 @@ __host__ __device__ inline FwdLayout fwd_layout(int T, int64_t cap) {
   L.HB = take(4 * cq * 64);
   L.bitems = take(4 * (size_t)GS_PIECES * ((size_t)T * 4 + 2 * cq));
   L.qcut = take(4 * (size_t)T * 4);
-  L.cut = take(4 * (size_t)T * GS_CUT_FLOATS);
+  L.cut = take(4 * (size_t)(T <= GS_CUT_TILES_MAX ? T : 0) * GS_CUT_FLOATS);
   L.contrib = take(8 * 4 * (size_t)contrib_words(T, cap));
   L.total = off;
   return L;

@@ -484,7 +484,7 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
   // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
   // queues empty exit at once
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  const bool count = stats || pixel_hits, cuts = few_tiles(ntiles, nblocks);
+  const bool count = stats || pixel_hits, cuts = records_cuts(ntiles, nblocks);
   auto kern = count ? (cuts ? k_render_fwd<true, true> : k_render_fwd<true, false>)
                     : (cuts ? k_render_fwd<false, true> : k_render_fwd<false, false>);
   hipLaunchKernelGGL(kern, dim3(nblocks),

@@ -448,7 +448,7 @@ def _plan_layout(T):
         off += rnd(b)
     bitems = off
     qcut = bitems + rnd(4 * 4 * (4 * T + 2 * cq))
-    off = qcut + rnd(4 * 4 * T) + rnd(4 * T * 15 * 256)
+    off = qcut + rnd(4 * 4 * T) + rnd(4 * (T if T <= 2048 else 0) * 15 * 256)
     return dict(hdr=hdr, heads=heads, sub_last=sub_last, order=order, counts=counts, items=items,
                 bitems=bitems, qcut=qcut, contrib=off)
 
