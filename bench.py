@@ -247,12 +247,14 @@ def stage_times(gsr, r, n, dL, steps, warmup):
         if ev is not None:
             ev[2].record(stream)
         stream.wait_event(ev_plan)
-        gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
-                          r.last, r.fwd_state, None, None, r.status)
+        # the forward clears the gradient rows once its workers run out of
+        # tiles; the backward adds into them
+        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
+                               r.last, r.fwd_state, None, None, r.status, r.grads[:n])
         if ev is not None:
             ev[3].record(stream)
-        gsr.gs_render_bwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last, r.fwd_state,
-                          dL, r.grads, r.status)
+        gsr.gs_render_bwd_accumulate(n, r.splats, r.sorted_ids, r.ranges, r.cam, 1, r.T, r.last,
+                                     r.fwd_state, dL, r.grads, r.status)
         if ev is not None:
             ev[4].record(stream)
 
@@ -477,12 +479,14 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         stream.wait_event(ev_plan)
-        gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T, r.last,
-                          r.fwd_state, None, None, r.status)
+        # the forward clears the gradient rows once its workers run out of
+        # tiles; the backward adds into them
+        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
+                               r.last, r.fwd_state, None, None, r.status, r.grads[:n])
         if ev is not None:
             ev[3].record(stream)
-        gsr.gs_render_bwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.T, r.last, r.fwd_state,
-                          dL, r.grads, r.status)
+        gsr.gs_render_bwd_accumulate(n, r.splats, r.sorted_ids, r.ranges, r.cam, 1, r.T, r.last,
+                                     r.fwd_state, dL, r.grads, r.status)
         if ev is not None:
             ev[4].record(stream)
 

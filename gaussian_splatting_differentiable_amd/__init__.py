@@ -31,7 +31,8 @@ EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project"
            "gs_bin_tiles_views", "gs_sort_keys_views", "gs_render_fwd_views",
            "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
            "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views", "gs_timing_start",
-           "gs_timing_read", "gs_set_wait_limit", "gs_render_bwd_accumulate")
+           "gs_timing_read", "gs_set_wait_limit", "gs_render_bwd_accumulate",
+           "gs_render_fwd_zero")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -80,6 +81,7 @@ def lib():
     L.gs_render_bwd.argtypes = [i32, P, P, P, cam_p, P, P, P, sz, P, P, P, P]
     L.gs_render_fwd_bg.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P]
     L.gs_render_bwd_bg.argtypes = L.gs_render_bwd.argtypes[:-1] + [P, P, P]
+    L.gs_render_fwd_zero.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P, i64, P]
     L.gs_workspace_size_views.argtypes = [i32, i32, i32, i32, i64]
     L.gs_workspace_size_views.restype = sz
     L.gs_fwd_state_size_views.argtypes = [i32, i32, i32, i64]
@@ -105,7 +107,7 @@ def lib():
                  "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views",
                  "gs_timing_start", "gs_timing_read", "gs_set_wait_limit",
-                 "gs_render_bwd_accumulate"):
+                 "gs_render_bwd_accumulate", "gs_render_fwd_zero"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -247,6 +249,19 @@ def gs_render_bwd_views(n, splats, sorted_ids, ranges, cam, n_views, T_final, la
                                      _ptr(dL_drgb), _ptr(dL_dsplat), _ptr(status),
                                      _bg3(background), _ptr(dL_dT), _stream(stream)),
            "gs_render_bwd_views")
+
+
+def gs_render_fwd_zero(n, splats, sorted_ids, ranges, cam, sched, rgb, T_final, last, fwd_state,
+                       stats, pixel_hits, status, zero_out, background=None, stream=None):
+    """gs_render_fwd_bg that also clears zero_out (every element), e.g. the
+    gradient array a gs_render_bwd_accumulate of the frame adds into."""
+    _check(lib().gs_render_fwd_zero(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges),
+                                    C.byref(cam), C.byref(sched) if sched is not None else None,
+                                    _ptr(rgb), _ptr(T_final), _ptr(last), _ptr(fwd_state),
+                                    fwd_state.numel() * fwd_state.element_size(), _ptr(stats),
+                                    _ptr(pixel_hits), _ptr(status), _bg3(background),
+                                    _ptr(zero_out), int(zero_out.numel()), _stream(stream)),
+           "gs_render_fwd_zero")
 
 
 def gs_render_bwd_accumulate(n, splats, sorted_ids, ranges, cam, n_views, T_final, last,
@@ -548,15 +563,24 @@ class Rasterizer:
             self._ensure(n, max(I + I // 8, 1024))
         raise GsError(GS_ERR_CAPACITY, "bin_and_sort")
 
-    def render_fwd(self, n, stats=False, background=None):
+    def render_fwd(self, n, stats=False, background=None, clear_grads=False):
         """Enqueue the forward. stats: also count hits (self.stats, self.pixel_hits,
-        both cleared first). background: 3 floats (host), or None for black."""
+        both cleared first). background: 3 floats (host), or None for black.
+        clear_grads: the forward also clears the gradient rows of the n splats
+        (for render_bwd(..., accumulate=True)); one view only."""
         self._ensure(n, self.capacity)
         st = ph = None
         if stats:
             self.stats.zero_()
             self.pixel_hits.zero_()
             st, ph = self.stats, self.pixel_hits
+        if clear_grads:
+            if self.V > 1:
+                raise ValueError("clear_grads takes one view")
+            gs_render_fwd_zero(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched,
+                               self.rgb, self.T, self.last, self.fwd_state, st, ph, self.status,
+                               self.grads[:n], background)
+            return self.rgb, self.T, self.last
         if self.V > 1:
             gs_render_fwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
                                 self.sched, self.rgb, self.T, self.last, self.fwd_state, st, ph,
@@ -570,9 +594,15 @@ class Rasterizer:
             gs_render_fwd_bg(*args, background)
         return self.rgb, self.T, self.last
 
-    def render_bwd(self, n, dL_drgb, background=None, dL_dT=None):
+    def render_bwd(self, n, dL_drgb, background=None, dL_dT=None, accumulate=False):
         """Enqueue the backward. background as for render_fwd; dL_dT [H][W] on the
-        device, or None."""
+        device, or None. accumulate: add into the gradient rows (cleared by
+        render_fwd(..., clear_grads=True) or holding earlier sums)."""
+        if accumulate:
+            gs_render_bwd_accumulate(n, self.splats, self.sorted_ids, self.ranges, self.cam,
+                                     self.V, self.T, self.last, self.fwd_state, dL_drgb,
+                                     self.grads, self.status, background, dL_dT)
+            return self.grads[:n]
         if self.V > 1:
             gs_render_bwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
                                 self.T, self.last, self.fwd_state, dL_drgb, self.grads,
@@ -596,11 +626,15 @@ class Rasterizer:
         """Bin, sort, forward and (with dL_drgb) backward of the current splats,
         then one read of the frame's status; a pair overflow grows the buffers and
         runs the frame again. Returns I."""
+        # one view: the forward clears the gradient rows in its idle end and
+        # the backward adds into them (no clearing launch of its own)
+        fused = dL_drgb is not None and self.V == 1
         for _ in range(3):
             self.enqueue_bin_sort(n)
-            self.render_fwd(n, stats=stats, background=background)
+            self.render_fwd(n, stats=stats, background=background, clear_grads=fused)
             if dL_drgb is not None:
-                self.render_bwd(n, dL_drgb, background=background, dL_dT=dL_dT)
+                self.render_bwd(n, dL_drgb, background=background, dL_dT=dL_dT,
+                                accumulate=fused)
             st, I = self.frame_status(n)
             if st == GS_OK:
                 return I

@@ -28,8 +28,8 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
                                 int64_t cap_pairs, int64_t *stats, int32_t *pixel_hits,
-                                int32_t *status, int workers_waves, hipEvent_t ev0,
-                                hipEvent_t ev1, hipStream_t st);
+                                int32_t *status, int workers_waves, float *clear,
+                                int64_t nclear, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, const CamK &cam,
                               int chunk_mode, int force_k, int force_h, double lambda_,
                               double beta, double eps, int nblocks, void *fwd_state,
@@ -307,8 +307,10 @@ int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
                  const int32_t *tile_ranges, CamK k, const gs_sched *sched, float *rgb,
                  float *T_final, int32_t *last, void *fwd_state, size_t fwd_state_bytes,
                  int64_t *stats, int32_t *pixel_hits, int32_t *device_status,
-                 const float *background, void *stream) {
+                 const float *background, float *clear, int64_t nclear, void *stream) {
   if (n < 0 || !set_background(background, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (nclear < 0 || (nclear > 0 && (!clear || !aligned(clear, 16))))
+    return GS_ERR_INVALID_ARGUMENT;
   if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT) return GS_ERR_UNSUPPORTED;
   if (!tile_ranges || !rgb || !T_final || !last || !fwd_state || !device_status)
     return GS_ERR_INVALID_ARGUMENT;
@@ -331,7 +333,8 @@ int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
   timing_slot(0, e0, e1);
   return hip_status(gs_launch_render_fwd(n, splats, sorted_ids, tile_ranges, k, sc, rgb, T_final,
                                          last, fwd_state, cap_pairs, stats, pixel_hits,
-                                         device_status, workers, e0, e1, (hipStream_t)stream));
+                                         device_status, workers, nclear > 0 ? clear : nullptr,
+                                         nclear, e0, e1, (hipStream_t)stream));
 }
 
 int32_t plan_impl(const int32_t *tile_counts, const CamK &k, const gs_sched *sched,
@@ -431,7 +434,22 @@ int32_t gs_render_fwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
   CamK k;
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
-                  fwd_state_bytes, stats, pixel_hits, device_status, background, stream);
+                  fwd_state_bytes, stats, pixel_hits, device_status, background, nullptr, 0,
+                  stream);
+}
+
+int32_t gs_render_fwd_zero(int32_t n, const float *splats, const int32_t *sorted_ids,
+                           const int32_t *tile_ranges, const gs_camera *cam,
+                           const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
+                           void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                           int32_t *pixel_hits, int32_t *device_status, const float *background,
+                           float *zero_out, int64_t zero_count, void *stream) {
+  CamK k;
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (zero_count < 0 || (zero_count > 0 && !zero_out)) return GS_ERR_INVALID_ARGUMENT;
+  return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
+                  fwd_state_bytes, stats, pixel_hits, device_status, background, zero_out,
+                  zero_count, stream);
 }
 
 int32_t gs_render_fwd(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -573,7 +591,8 @@ int32_t gs_render_fwd_views(int32_t n, const float *splats, const int32_t *sorte
   CamK k;
   if (!prep_views(cam, n_views, &k)) return GS_ERR_INVALID_ARGUMENT;
   return fwd_impl(n, splats, sorted_ids, tile_ranges, k, sched, rgb, T_final, last, fwd_state,
-                  fwd_state_bytes, stats, pixel_hits, device_status, background, stream);
+                  fwd_state_bytes, stats, pixel_hits, device_status, background, nullptr, 0,
+                  stream);
 }
 
 int32_t gs_render_bwd_views(int32_t n, const float *splats, const int32_t *sorted_ids,

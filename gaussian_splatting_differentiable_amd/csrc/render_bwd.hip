@@ -36,12 +36,10 @@ namespace {
 
 constexpr float NEG_HALF_LOG2E = -0.72134752044448170368f;
 
-// Backward queue order. The forward pass leaves every item's walk length (the
-// quarter's or chunk's last hit), so the backward can serve its items longest
-// first exactly ([LOAD-IMB] section 4.1 orders by N_t, which overstates the work
-// of tiles whose pixels saturate early). One workgroup per group sorts the
-// group's backward items stably by a quarter-octave bucket of that length.
-constexpr int BO_T = 1024, BO_W = BO_T / 64, BO_BITS = 6, BO_BINS = 1 << BO_BITS;
+// The backward's preparation for frames with few tiles: one workgroup per
+// group sorts the group's backward items (quarters, or their pieces between
+// cuts) stably by the bin of their walk length.
+constexpr int BO_T = 1024, BO_W = BO_T / 64;
 constexpr int BO_IPL = 4;  // items per lane per span of the queue build
 
 // Walk length of a backward item: its quarter's last hit, or the longest of
@@ -58,12 +56,6 @@ __device__ __forceinline__ int item_len(const FwdState &fs, int it, int k) {
       return fs.chunk_last[chunk_index(idx, item_chunk(it), q, k)];
   }
 }
-
-// A plain tile whose walk spans more entries than this is walked by quarters:
-// on a long list whose batches hold few contributors each, a batch costs about
-// one memory round trip for its records, and a whole tile visits every batch
-// where any of its quarters has a contributor.
-constexpr int SPLIT_WALK = 2048;
 
 // The backward item a forward item of the group's queue gives, or -1, and its
 // walk length: a chunk's quarter (pass B) gives itself; a plain tile gives one
@@ -85,11 +77,6 @@ __device__ __forceinline__ int bwd_item(const FwdState &fs, int it, bool split, 
   }
   len = whole;
   return q == 0 ? it : -1;
-}
-
-__device__ __forceinline__ uint32_t order_bin(int len) {
-  const int b = (int)(4.0f * __log2f((float)max(len, 0) + 1.0f));
-  return (uint32_t)(BO_BINS - 1 - min(b, BO_BINS - 1));  // ascending bin = longest first
 }
 
 __device__ __forceinline__ int ceil64(int v) { return (max(v, 0) + 63) >> 6; }
@@ -600,7 +587,8 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     const Splat *__restrict__ splats, int n, const int32_t *__restrict__ sorted_ids,
     const int2 *__restrict__ ranges, CamK cam, const float *__restrict__ Tfin,
     const int32_t *__restrict__ last, char *__restrict__ state, int ntiles,
-    const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads) {
+    const float *__restrict__ dL, const float *__restrict__ dT, float *__restrict__ grads,
+    const int32_t *__restrict__ status) {
   __shared__ Staged stage_all[GS_WAVES_PER_BLOCK][SLOTS];
   // per-slot gradient sums and gradient rows, two sets per wave
   __shared__ float gacc_all[GS_WAVES_PER_BLOCK][2 * 9 * SLOTS];
@@ -609,7 +597,13 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
   float *gacc = gacc_all[wave_in_block()];
   int32_t *rows = rows_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
-  if (!fs.hdr->run_b) return;  // the frame failed earlier: nothing to differentiate
+  // the frame failed earlier: nothing to differentiate
+  if (!fs.hdr->run_f || *status != GS_OK) return;
+  // bins: the forward filed the items (frames with few tiles: the preparation
+  // wrote bitems)
+  const bool bins = fs.hdr->bmode != 0;
+  __shared__ int bpre[GS_GROUPS * BPRE];
+  if (bins) load_bin_starts(fs, bpre);
   for (int i = __lane_id(); i < 2 * 9 * SLOTS; i += GS_WAVE) gacc[i] = 0.0f;
   if (__lane_id() == 0) {
     Staged dead;
@@ -625,12 +619,19 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
   // rows 4 (s / 8) to 4 (s / 8) + 3 of the quarter
   const int quad = lane >> 4, col = lane & 7, r4 = 4 * ((lane >> 3) & 1);
   __shared__ uint32_t drained;
+  __shared__ int waves_out;
+  if (threadIdx.x == 0) waves_out = 0;
   Worker wk = make_worker(&drained);
   for (;;) {
-    const int t = next_item(fs, 1, wk);
-    if (t < 0) break;
+    int it;
+    if (bins) {
+      if (!next_bin_item(fs, bpre, wk, gridDim.x, it)) break;
+    } else {
+      const int t = next_item(fs, 1, wk);
+      if (t < 0) break;
+      it = fs.bitems[t];
+    }
     wk.round++;
-    const int it = fs.bitems[t];
     const int kind = item_kind(it), p = item_chunk(it);
     const int idx = item_index(it);
     const bool plain = kind == ITEM_PLAIN || kind == ITEM_QUARTER;
@@ -758,6 +759,22 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     walk_back<WIDE>(splats, n, sorted_ids, cs, contrib_base(fs, 0, tile, rg.x) + ((cs - rg.x) >> 6),
                     fs.nw, nbw, x, stage, gacc, rows, grads);
   }
+  // The last wave out of the launch resets the queue heads, so the backward
+  // may run again on this state (every other wave has made its last pop).
+  if (lane == 0 && atomicAdd(&waves_out, 1) == GS_WAVES_PER_BLOCK - 1 &&
+      atomicAdd(&fs.hdr->bexit, 1) == (int)gridDim.x - 1) {
+    for (int g = 0; g < GS_GROUPS; g++) queue_head(fs, 1, g)[0] = bins ? 0 : fs.hdr->init_b[g];
+    fs.hdr->bexit = 0;
+  }
+}
+
+// The overwritten gradient array's zeroing, for frames whose backward has no
+// preparation.
+__global__ void __launch_bounds__(256) k_zero(float *__restrict__ out, int64_t nout) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n4 = nout / 4;
+  if (i < n4) reinterpret_cast<float4 *>(out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i < nout - 4 * n4) out[4 * n4 + i] = 0.0f;
 }
 
 }  // namespace
@@ -772,10 +789,16 @@ hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorte
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   // accumulating: the caller's gradient array is the starting point, not zeroed
-  const int zero_blocks = accumulate ? 0 : (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
-  hipLaunchKernelGGL(few_tiles(ntiles, nblocks) ? k_bwd_prep<true> : k_bwd_prep<false>,
-                     dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
-                     reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng, status);
+  // A frame with few tiles has its backward items ordered (and its long walks
+  // cut) by the preparation, beside the zeroing; any other frame's forward
+  // filed them, and only the zeroing remains.
+  if (few_tiles(ntiles, nblocks)) {
+    const int zero_blocks = accumulate ? 0 : (int)((ng / 4 + 4 + BO_T - 1) / BO_T);
+    hipLaunchKernelGGL(k_bwd_prep<true>, dim3(GS_GROUPS + zero_blocks), dim3(BO_T), 0, st,
+                       reinterpret_cast<char *>(fwd_state), ntiles, nblocks, grads, ng, status);
+  } else if (!accumulate && ng > 0) {
+    hipLaunchKernelGGL(k_zero, dim3(gs_div_up(ng / 4 + 4, 256)), dim3(256), 0, st, grads, ng);
+  }
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, st);
     if (e != hipSuccess) return e;
@@ -785,7 +808,7 @@ hipError_t gs_launch_render_bwd(int n, const float *splats, const int32_t *sorte
                      dim3(GS_WAVE * GS_WAVES_PER_BLOCK), 0, st,
                      reinterpret_cast<const Splat *>(splats), n, sorted_ids,
                      reinterpret_cast<const int2 *>(ranges), cam, T, last,
-                     reinterpret_cast<char *>(fwd_state), ntiles, dL, dT, grads);
+                     reinterpret_cast<char *>(fwd_state), ntiles, dL, dT, grads, status);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
   return e;

@@ -66,7 +66,12 @@ struct PlanHdr {
   // the rest the knobs and worker count it was built with.
   int32_t planned, plan_pairs;
   int32_t plan_mode, plan_force_k, plan_force_h, plan_nblocks;
-  double plan_lambda, plan_beta, plan_eps;
+  float plan_lambda, plan_beta, plan_eps;
+  // 1: the forward files each backward item into a bin of its walk length as
+  // the item's walk ends (bcnt, blist); 0: the backward's preparation writes
+  // bitems (frames with few tiles, whose walks it may cut into pieces)
+  int32_t bmode;
+  int32_t bexit;  // workgroups of a backward launch that have finished
 };
 static_assert(sizeof(PlanHdr) <= 256, "the plan header fills one 256-byte slot");
 constexpr int32_t PLAN_READY = 0x504C414E;
@@ -117,11 +122,29 @@ __host__ __device__ __forceinline__ bool records_cuts(int ntiles, int nblocks) {
   return few_tiles(ntiles, nblocks) && ntiles <= GS_CUT_TILES_MAX;
 }
 
+// Backward queue order. The forward pass knows every item's walk length (its
+// last hit) when the walk ends, so the backward can serve its items longest
+// first by that length ([LOAD-IMB] section 4.1 orders by N_t, which overstates
+// the work of tiles whose pixels saturate early): items are kept in
+// quarter-octave bins of the length, longest bin first.
+constexpr int BO_BITS = 6, BO_BINS = 1 << BO_BITS;
+
+__device__ __forceinline__ uint32_t order_bin(int len) {
+  const int b = (int)(4.0f * __log2f((float)max(len, 0) + 1.0f));
+  return (uint32_t)(BO_BINS - 1 - min(b, BO_BINS - 1));  // ascending bin = longest first
+}
+
+// A plain tile whose walk spans more entries than this is walked by quarters
+// in the backward: on a long list whose batches hold few contributors each, a
+// batch costs about one memory round trip for its records, and a whole tile
+// visits every batch where any of its quarters has a contributor.
+constexpr int SPLIT_WALK = 2048;
+
 // Byte layout of fwd_state for T tiles and a pair capacity cap (the contributor
 // bitmap comes last, so the capacity a state serves follows from its size).
 struct FwdLayout {
   size_t hdr, heads, sub_last, order, counts, items, sat, doneA, doneB, chunk_last, PA, CB, TB,
-      LB, HB, bitems, qcut, cut, contrib, total;
+      LB, HB, bitems, qcut, cut, tlen, bcnt, blist, contrib, total;
 };
 
 __host__ __device__ inline FwdLayout fwd_layout(int T, int64_t cap) {
@@ -151,6 +174,9 @@ __host__ __device__ inline FwdLayout fwd_layout(int T, int64_t cap) {
   L.bitems = take(4 * (size_t)GS_PIECES * ((size_t)T * 4 + 2 * cq));
   L.qcut = take(4 * (size_t)T * 4);
   L.cut = take(4 * (size_t)(T <= GS_CUT_TILES_MAX ? T : 0) * GS_CUT_FLOATS);
+  L.tlen = take(8 * (size_t)T);
+  L.bcnt = take(4 * (size_t)GS_GROUPS * BO_BINS);
+  L.blist = take(4 * (size_t)BO_BINS * ((size_t)T * 4 + 2 * cq));
   L.contrib = take(8 * 4 * (size_t)contrib_words(T, cap));
   L.total = off;
   return L;
@@ -174,6 +200,9 @@ struct FwdState {
   int32_t *bitems;  // the backward's queue items, longest walk first within each group
   int32_t *qcut;    // per quarter: the cuts its forward walk reached
   float *cut;       // per tile: the cut record (GS_CUT_FLOATS)
+  uint64_t *tlen;   // per tile: its quarters' walk lengths + 1, 16 bits each, as they end
+  int32_t *bcnt;    // [group][bin] backward items filed so far
+  int32_t *blist;   // the backward's items by group and bin (bin_base)
   uint64_t *contrib;  // [4][nw] contributor words
   int64_t nw;         // words per quarter: the schedule sets hdr->nw, kernels copy it here
 };
@@ -202,6 +231,9 @@ __host__ __device__ inline FwdState fwd_state_at(void *base, int T) {
   s.bitems = reinterpret_cast<int32_t *>(b + L.bitems);
   s.qcut = reinterpret_cast<int32_t *>(b + L.qcut);
   s.cut = reinterpret_cast<float *>(b + L.cut);
+  s.tlen = reinterpret_cast<uint64_t *>(b + L.tlen);
+  s.bcnt = reinterpret_cast<int32_t *>(b + L.bcnt);
+  s.blist = reinterpret_cast<int32_t *>(b + L.blist);
   s.contrib = reinterpret_cast<uint64_t *>(b + L.contrib);
   s.nw = 0;
   return s;
@@ -220,6 +252,14 @@ __host__ __device__ __forceinline__ int32_t *queue_head(const FwdState &fs, int 
 // First of group g's backward items in bitems[].
 __host__ __device__ __forceinline__ int bwd_base(const PlanHdr *hd, int g) {
   return GS_PIECES * (hd->qoff[g] + hd->qa[g]);
+}
+
+// First slot of bin b of group g in blist[]: each bin of a group has room for
+// every item of the group's forward queue (a backward item comes from one
+// forward item: a whole tile from its quarter 0, a quarter or a chunk quarter
+// from itself).
+__host__ __device__ __forceinline__ int bin_base(const PlanHdr *hd, int g, int b) {
+  return BO_BINS * hd->qoff[g] + b * (hd->qoff[g + 1] - hd->qoff[g]);
 }
 
 
@@ -415,6 +455,71 @@ __device__ __forceinline__ int next_item(const FwdState &fs, int pass, Worker &w
     if (t >= 0) return t;
   }
   return -1;
+}
+
+// The backward's items filed in bins by the forward (bmode 1). Each workgroup
+// keeps every group's bin starts in LDS: bpre[g][b] = items of group g in
+// bins before b, bpre[g][BO_BINS] the group's total. Call from every thread
+// before make_worker (whose barrier publishes the table).
+constexpr int BPRE = BO_BINS + 1;
+__device__ __forceinline__ void load_bin_starts(const FwdState &fs, int *bpre) {
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  if (g < GS_GROUPS) {
+    int v = fs.bcnt[g * BO_BINS + lane];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(v, d, 64);
+      if (lane >= d) v += u;
+    }
+    bpre[g * BPRE + lane + 1] = v;
+    if (lane == 0) bpre[g * BPRE] = 0;
+  }
+}
+
+// Item at position c of group g's backward order (bins longest first).
+__device__ __forceinline__ int bin_item(const FwdState &fs, const int *bpre, int g, int c) {
+  const int lane = __lane_id();
+  // bins that end at or before c come first (the starts are non-decreasing)
+  const int b = __popcll(wave_ballot(bpre[g * BPRE + lane + 1] <= c));
+  return fs.blist[bin_base(fs.hdr, g, b) + c - bpre[g * BPRE + b]];
+}
+
+// Next backward item from the bins into `it`; false when every group is
+// served (an item's kind sits in its top bits, so no value of `it` is free to
+// mark that). The same hand-out as next_item: the first item by the worker's
+// index in its home group, then pops, home group first, with group g's head
+// counting the pops past its static hand-out.
+__device__ __forceinline__ bool next_bin_item(const FwdState &fs, const int *bpre, Worker &w,
+                                              int nblocks, int &it) {
+  if (w.round == 0) {
+    const int tot = bpre[w.home * BPRE + BO_BINS];
+    if (w.wg < min(tot, group_workers(w.home, nblocks))) {
+      it = bin_item(fs, bpre, w.home, w.wg);
+      return true;
+    }
+  }
+  for (int c = 0; c < GS_GROUPS; c++) {
+    const int g = (w.home + (c + 1) / 2 * ((c & 1) ? 1 : -1) + GS_GROUPS) % GS_GROUPS;
+    if (w.known & (1u << g)) continue;
+    const uint32_t dm = __hip_atomic_load(w.drained, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (wave_first((int)dm) & (1 << g)) {
+      w.known |= 1u << g;
+      continue;
+    }
+    const int tot = bpre[g * BPRE + BO_BINS];
+    const int init = min(tot, group_workers(g, nblocks));
+    if (init < tot) {
+      const int pos = init + queue_pop(queue_head(fs, 1, g));
+      if (pos < tot) {
+        it = bin_item(fs, bpre, g, pos);
+        return true;
+      }
+    }
+    w.known |= 1u << g;
+    if (__lane_id() == 0)
+      __hip_atomic_fetch_or(w.drained, 1u << g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  return false;
 }
 
 __device__ __forceinline__ void st_flag(int32_t *p, int v) {

@@ -275,6 +275,65 @@ __device__ __forceinline__ int ld_i(const int32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The backward's queue, filed as the forward's walks end (frames whose
+// backward has no preparation): quarter `quad` of a plain tile adds its walk
+// length to the tile's length word; the quarter that completes the word files
+// the tile's backward items in the bins of their walks: the whole tile
+// (walked by the longest of its quarters), or, when that walk is long, its
+// four quarters. One returning atomic per quarter, one more per filed item.
+__device__ __forceinline__ void file_plain(const FwdState &fs, int tile, int quad, int wlast,
+                                           int tiles_x) {
+  const int lane = __lane_id();
+  const uint64_t mine = (uint64_t)(min(wlast, 65534) + 1) << (16 * quad);
+  uint64_t old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_or(&fs.tlen[tile], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t o = ((uint64_t)(uint32_t)wave_first((int)(old >> 32)) << 32) |
+                     (uint32_t)wave_first((int)(uint32_t)old);
+  const int seen = ((o & 0xFFFFull) != 0) + (((o >> 16) & 0xFFFFull) != 0) +
+                   (((o >> 32) & 0xFFFFull) != 0) + ((o >> 48) != 0);
+  if (seen != 3) return;  // another quarter of the tile is still walking
+  const uint64_t all = o | mine;
+  const int l0 = (int)(all & 0xFFFFull) - 1, l1 = (int)((all >> 16) & 0xFFFFull) - 1;
+  const int l2 = (int)((all >> 32) & 0xFFFFull) - 1, l3 = (int)(all >> 48) - 1;
+  const int whole = max(max(l0, l1), max(l2, l3));
+  const bool split = whole > SPLIT_WALK;
+  if (split ? lane < 4 : lane == 0) {
+    const int len = !split ? whole : lane == 0 ? l0 : lane == 1 ? l1 : lane == 2 ? l2 : l3;
+    const int item = split ? make_item(ITEM_QUARTER, lane, 0, tile) : make_item(ITEM_PLAIN, 0, 0, tile);
+    const int g = tile_group(tile, tiles_x);
+    const uint32_t b = order_bin(len);
+    const int pos = atomicAdd(&fs.bcnt[g * BO_BINS + b], 1);
+    fs.blist[bin_base(fs.hdr, g, b) + pos] = item;
+  }
+}
+
+// A chunk's quarter is a backward item of its own (pass B's item).
+__device__ __forceinline__ void file_chunk(const FwdState &fs, int item, int tile, int wlast,
+                                           int tiles_x) {
+  if (__lane_id() != 0) return;
+  const int g = tile_group(tile, tiles_x);
+  const uint32_t b = order_bin(wlast);
+  const int pos = atomicAdd(&fs.bcnt[g * BO_BINS + b], 1);
+  fs.blist[bin_base(fs.hdr, g, b) + pos] = item;
+}
+
+// A worker with no tile left clears its own slice of the caller's array (the
+// gradient array a backward of this frame adds into): slices of whole float4s
+// by worker index, so no counter is shared and a late worker adds only its
+// slice's stores to the end of the launch.
+__device__ __forceinline__ void clear_slice(float *__restrict__ out, int64_t nout) {
+  const int lane = __lane_id();
+  const int64_t workers = (int64_t)gridDim.x * GS_WAVES_PER_BLOCK;
+  const int64_t w = (int64_t)blockIdx.x * GS_WAVES_PER_BLOCK + wave_in_block();
+  const int64_t n4 = nout / 4;                      // whole float4s
+  const int64_t per = (n4 + workers - 1) / workers;  // float4s per worker
+  const int64_t a = min(n4, w * per), e = min(n4, a + per);
+  float4 *o4 = reinterpret_cast<float4 *>(out);
+  for (int64_t i = a + lane; i < e; i += 64) o4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (w == workers - 1 && lane < nout - 4 * n4) out[4 * n4 + lane] = 0.0f;  // the ragged end
+}
+
 // STATS: count hits, tested entries and sub-tile hits (only when the caller asks
 // for them: the counters cost a few scalar instructions per entry). CUTS: the
 // frame has few tiles, and its plain walks record their state at the cuts.
@@ -285,11 +344,13 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
     int32_t *__restrict__ last, char *__restrict__ state, int T,
     unsigned long long *__restrict__ stats, int32_t *__restrict__ pixel_hits,
-    int32_t *__restrict__ status, int spin_limit) {
+    int32_t *__restrict__ status, int spin_limit, float *__restrict__ clear, int64_t nclear) {
   __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
   Splat *sbuf = sbuf_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, T);
-  if (!fs.hdr->run_f) return;  // the frame failed earlier: the schedule planned nothing
+  // a frame that failed earlier has an empty plan: its workers only clear
+  const bool run = fs.hdr->run_f != 0;
+  const bool bins = fs.hdr->bmode != 0;
   fs.nw = fs.hdr->nw;
   const int k = fs.hdr->k;
   const int P = cam.width * cam.height * cam.views;
@@ -298,7 +359,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
   __shared__ uint32_t drained;
   Worker wk = make_worker(&drained);
   for (;;) {
-    const int t = next_item(fs, 0, wk);
+    const int t = run ? next_item(fs, 0, wk) : -1;
     if (t < 0) break;
     wk.round++;
     const int it = fs.items[t];
@@ -314,6 +375,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
           fs.sub_last[tile * 4 + quad] = 0;
           fs.qcut[tile * 4 + quad] = 0;
         }
+        if (bins) file_plain(fs, tile, quad, 0, cam.tiles_x);
         continue;
       }
       int ncut = 0;
@@ -339,6 +401,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
         fs.sub_last[tile * 4 + quad] = r.wlast;
         fs.qcut[tile * 4 + quad] = ncut;
       }
+      if (bins) file_plain(fs, tile, quad, r.wlast, cam.tiles_x);
       continue;
     }
     int cs, ce;
@@ -408,6 +471,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     fs.LB[cp] = r.consumed;
     if (STATS) fs.HB[cp] = r.nh;
     if (lane == 0) fs.chunk_last[ci] = r.wlast;
+    if (bins) file_chunk(fs, it, tile, r.wlast, cam.tiles_x);
     wave_release();
     int prev = 0;
     if (lane == 0)
@@ -452,6 +516,7 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
       if (STATS && pixel_hits) pixel_hits[x.p] += nhv;
     }
   }
+  if (clear) clear_slice(clear, nclear);
   if (STATS && stats && lane == 0) {
     atomicAdd(&stats[0], (unsigned long long)nhits);
     atomicAdd(&stats[1], nsteps * (unsigned long long)GS_WAVE);
@@ -473,8 +538,8 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
                                 int64_t cap_pairs, int64_t *stats, int32_t *pixel_hits,
-                                int32_t *status, int workers_waves, hipEvent_t ev0,
-                                hipEvent_t ev1, hipStream_t st) {
+                                int32_t *status, int workers_waves, float *clear,
+                                int64_t nclear, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
   hipError_t e = gs_launch_schedule(ranges, nullptr, cam, sched.chunk_mode, sched.force_k, sched.force_h,
@@ -493,7 +558,7 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,
                      reinterpret_cast<unsigned long long *>(stats), pixel_hits, status,
-                     gs_wait_limit(GS_SPIN_LIMIT));
+                     gs_wait_limit(GS_SPIN_LIMIT), clear, clear ? nclear : (int64_t)0);
   e = hipGetLastError();
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
   return e;

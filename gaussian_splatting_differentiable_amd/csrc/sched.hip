@@ -254,10 +254,13 @@ __device__ void empty_plan(const FwdState &fs) {
     fs.hdr->nb[threadIdx.x] = 0;
     queue_head(fs, 0, threadIdx.x)[0] = queue_head(fs, 1, threadIdx.x)[0] = 0;
   }
+  for (int i = threadIdx.x; i < GS_GROUPS * BO_BINS; i += blockDim.x) fs.bcnt[i] = 0;
   if (threadIdx.x == 0) {
     fs.hdr->h = 0;
     fs.hdr->k = 1;
     fs.hdr->nA = fs.hdr->nplain = 0;
+    fs.hdr->bmode = 1;
+    fs.hdr->bexit = 0;
   }
 }
 
@@ -450,6 +453,7 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     __syncthreads();
   }
   if (h == 0) k = 1;
+  const int bins = few_tiles(T, nblocks) ? 0 : 1;
 
   // 4. queues. The LPT positions e in [0, T) fall into classes (group of the
   //    tile, chunked iff e < h); a stable partition by class keeps the LPT order
@@ -502,10 +506,18 @@ __global__ void __launch_bounds__(NT) k_schedule(const int2 *__restrict__ ranges
     fs.hdr->init_f[g] = init_f;
     fs.hdr->init_b[g] = init_b;
     queue_head(fs, 0, g)[0] = init_f;
-    queue_head(fs, 1, g)[0] = init_b;
+    // the backward's head counts pops past its static hand-out, which a frame
+    // with few tiles learns from its preparation (that sets the head) and any
+    // other from the forward's bins
+    queue_head(fs, 1, g)[0] = bins ? 0 : init_b;
   }
+  // the forward files the backward's items by bin as their walks end
+  for (int i = threadIdx.x; i < GS_GROUPS * BO_BINS; i += NT) fs.bcnt[i] = 0;
+  for (int t = threadIdx.x; t < T; t += NT) fs.tlen[t] = 0ull;
   if (threadIdx.x <= GS_GROUPS) fs.hdr->qoff[threadIdx.x] = qoff[threadIdx.x];
   if (threadIdx.x == 0) {
+    fs.hdr->bmode = bins;
+    fs.hdr->bexit = 0;
     fs.hdr->h = h;
     fs.hdr->k = k;
     fs.hdr->nA = nA;

@@ -320,6 +320,22 @@ int32_t gs_render_bwd_bg(int32_t n, const float *splats, const int32_t *sorted_i
                          const float *dL_drgb, float *dL_dsplat, int32_t *device_status,
                          const float *background, const float *dL_dT, void *stream);
 
+/* gs_render_fwd_bg that also sets zero_out[0 .. zero_count) to zero: each of
+ * the frame's workers clears its own slice once no tile is left for it, so the
+ * clearing fills the idle end of the persistent launch instead of a launch of
+ * its own before the backward. Meant for the gradient array that a
+ * gs_render_bwd_accumulate of the same frame then adds into (together the
+ * results of gs_render_bwd_bg, up to the order of the float additions).
+ *   zero_out: device, 16-byte aligned, zero_count floats (0 and NULL: none);
+ *     cleared whatever the frame's device_status (a failed frame clears only).
+ * Other arguments, outputs and errors as for gs_render_fwd_bg. */
+int32_t gs_render_fwd_zero(int32_t n, const float *splats, const int32_t *sorted_ids,
+                           const int32_t *tile_ranges, const gs_camera *cam,
+                           const gs_sched *sched, float *rgb, float *T_final, int32_t *last,
+                           void *fwd_state, size_t fwd_state_bytes, int64_t *stats,
+                           int32_t *pixel_hits, int32_t *device_status, const float *background,
+                           float *zero_out, int64_t zero_count, void *stream);
+
 /* gs_render_bwd_bg (n_views 1) or gs_render_bwd_views (n_views > 1) adding
  * the gradients into dL_dsplat instead of overwriting it: the caller
  * initialises the array (zeros for one frame's gradients, or the sums of

@@ -448,9 +448,12 @@ def _plan_layout(T):
         off += rnd(b)
     bitems = off
     qcut = bitems + rnd(4 * 4 * (4 * T + 2 * cq))
-    off = qcut + rnd(4 * 4 * T) + rnd(4 * (T if T <= 2048 else 0) * 15 * 256)
+    tlen = qcut + rnd(4 * 4 * T) + rnd(4 * (T if T <= 2048 else 0) * 15 * 256)
+    bcnt = tlen + rnd(8 * T)
+    blist = bcnt + rnd(4 * 8 * 64)
+    off = blist + rnd(4 * 64 * (4 * T + 2 * cq))
     return dict(hdr=hdr, heads=heads, sub_last=sub_last, order=order, counts=counts, items=items,
-                bitems=bitems, qcut=qcut, contrib=off)
+                bitems=bitems, qcut=qcut, bcnt=bcnt, blist=blist, contrib=off)
 
 
 def read_contrib(r, ranges):
@@ -495,37 +498,68 @@ CUT_BATCHES = (2, 4, 8)  # a plain walk's cut points, in 64-entry batches
 
 def read_bwd_queue(r):
     """The backward's items per group, and per quarter the forward's walk
-    length (1 + the last entry any pixel blended) and the cuts it reached."""
+    length (1 + the last entry any pixel blended) and the cuts it reached.
+    A frame with few tiles has them in the preparation's list; any other frame
+    in the bins the forward filed them in (group g, bin b: the b-th of 64
+    quarter-octave bins of the walk length, longest first), read in bin order,
+    and for those the bins are returned as well."""
     T = r.tiles
     L = _plan_layout(T)
     raw = host(r.fwd_state)
-    hdr = raw[:208].view(np.int32)
-    qoff, qa, nb = hdr[6:15], hdr[15:23], hdr[39:47]
-    groups = []
-    for g in range(8):
-        base = L["bitems"] + 4 * 4 * (int(qoff[g]) + int(qa[g]))
-        groups.append(raw[base:base + 4 * int(nb[g])].view(np.int32).copy())
+    hdr = raw[:256].view(np.int32)
+    qoff, qa, nb, bmode = hdr[6:15], hdr[15:23], hdr[39:47], int(hdr[61])
+    groups, bins = [], []
+    if bmode:
+        bcnt = raw[L["bcnt"]:L["bcnt"] + 4 * 8 * 64].view(np.int32).reshape(8, 64)
+        for g in range(8):
+            span = int(qoff[g + 1]) - int(qoff[g])
+            its, bs = [], []
+            for b in range(64):
+                base = L["blist"] + 4 * (64 * int(qoff[g]) + b * span)
+                its.append(raw[base:base + 4 * int(bcnt[g, b])].view(np.int32))
+                bs.append(np.full(int(bcnt[g, b]), b))
+            groups.append(np.concatenate(its).copy())
+            bins.append(np.concatenate(bs))
+    else:
+        for g in range(8):
+            base = L["bitems"] + 4 * 4 * (int(qoff[g]) + int(qa[g]))
+            groups.append(raw[base:base + 4 * int(nb[g])].view(np.int32).copy())
     sub_last = raw[L["sub_last"]:L["sub_last"] + 16 * T].view(np.int32).reshape(T, 4).copy()
     qcut = raw[L["qcut"]:L["qcut"] + 16 * T].view(np.int32).reshape(T, 4).copy()
-    return groups, sub_last, qcut
+    return groups, sub_last, qcut, (bins if bmode else None)
 
 
-def check_bwd_queue(groups, sub_last, qcut, ranges, quarters):
+def check_bwd_queue(groups, sub_last, qcut, bins, ranges, quarters):
     """Every plain tile's walk (or, when quarters, every quarter's) is served
     once: whole, or as all of its pieces between the cuts below its length;
     a quarter reached every cut below its walk's end and none past its list.
-    Only a frame walked by quarters (few tiles) records cuts."""
+    Only a frame walked by quarters (few tiles) records cuts. Items filed in
+    bins by the forward: a plain item's bin is that of its walk length (64
+    quarter-octave bins, longest first; the device's log2 may round a length
+    at a bin edge either way)."""
     items = np.concatenate(groups)
     kind, quad, p, idx = (items >> 30) & 3, (items >> 28) & 3, (items >> 24) & 15, items & 0xFFFFFF
     assert not np.any(kind == 1)
+    if bins is not None:
+        b = np.concatenate(bins)
+        pl = kind != 2
+        walk = np.where(kind[pl] == 3, sub_last[idx[pl], quad[pl]], sub_last[idx[pl]].max(axis=1))
+        l4 = 4.0 * np.log2(np.maximum(walk, 0) + 1.0)
+        want = 63 - np.minimum(np.floor(l4), 63)
+        edge = np.abs(l4 - np.round(l4)) < 1e-3
+        assert np.all((b[pl] == want) | (edge & (np.abs(b[pl] - want) <= 1)))
     plain = kind != 2
     seen = {}
     for kd, q, pp, t in zip(kind[plain], quad[plain], p[plain], idx[plain]):
         key = (int(t), int(q) if kd == 3 else -1)
-        assert (kd == 3) == quarters
+        # by quarters: every tile of a frame with few tiles; in any other frame
+        # the tiles whose whole walk spans more than 2048 entries
+        assert (kd == 3) == (quarters or int(sub_last[t].max()) > 2048)
         seen.setdefault(key, []).append(int(pp))
     T = len(ranges)
-    assert len(seen) == (4 * T if quarters else T)
+    h = len(set(int(s) for s in idx[kind == 2]))  # chunked tiles (their slots)
+    nsplit = sum(1 for (t, q) in seen if q >= 0) // 4
+    assert len(seen) == (4 * (T - h) if quarters else T - h + 3 * nsplit)
     npieces = 0
     for (t, q), ps in seen.items():
         walk = int(sub_last[t, q]) if q >= 0 else int(sub_last[t].max())

@@ -159,3 +159,19 @@ def test_argument_validation_needs_no_gpu(gsr):
     assert L.gs_plan_tiles(p16, C.byref(bad), None, st256, 1 << 30, p16, None) == -1
     assert L.gs_plan_tiles_views(p16, C.byref(cam), 17, None, st256, 1 << 30, p16, None) == -1
     assert L.gs_plan_tiles(p16, C.byref(big), None, st256, 1 << 40, p16, None) == -5
+
+
+def test_forward_clear_argument_validation_needs_no_gpu(gsr):
+    """gs_render_fwd_zero: a negative count, a missing or misaligned array with a
+    positive count are rejected before any HIP call."""
+    L = gsr.lib()
+    cam = gsr.GsCamera()
+    cam.width, cam.height, cam.fx, cam.fy = 64, 64, 64.0, 64.0
+    p16 = C.c_void_p(1 << 20)
+    st256 = gsr.fwd_state_size(64, 64, 1 << 10)
+    common = (1, p16, p16, p16, C.byref(cam), None, p16, p16, p16, p16, st256, None, None, p16,
+              None)
+    assert L.gs_render_fwd_zero(*common, p16, -1, None) == gsr.GS_ERR_INVALID_ARGUMENT
+    assert L.gs_render_fwd_zero(*common, None, 16, None) == gsr.GS_ERR_INVALID_ARGUMENT
+    assert L.gs_render_fwd_zero(*common, C.c_void_p((1 << 20) + 4), 16,
+                                None) == gsr.GS_ERR_INVALID_ARGUMENT
