@@ -231,6 +231,8 @@ def stage_times(gsr, r, n, dL, steps, warmup):
     side = torch.cuda.Stream()
     ev_bin, ev_plan = torch.cuda.Event(), torch.cuda.Event()
 
+    planned = gsr.planned_sched(r.sched)  # the forward checks the plan built ahead itself
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -249,7 +251,7 @@ def stage_times(gsr, r, n, dL, steps, warmup):
         stream.wait_event(ev_plan)
         # the forward clears the gradient rows once its workers run out of
         # tiles; the backward adds into them
-        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
+        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, planned, r.rgb, r.T,
                                r.last, r.fwd_state, None, None, r.status, r.grads[:n])
         if ev is not None:
             ev[3].record(stream)
@@ -459,6 +461,8 @@ def main():
     cap = r.capacity
     stages = ["bin", "sort", "fwd", "bwd"]
 
+    planned = gsr.planned_sched(r.sched)  # the forward checks the plan built ahead itself
+
     def step(ev=None, evp=None):
         if ev is not None:
             ev[0].record(stream)
@@ -481,7 +485,7 @@ def main():
         stream.wait_event(ev_plan)
         # the forward clears the gradient rows once its workers run out of
         # tiles; the backward adds into them
-        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, r.sched, r.rgb, r.T,
+        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, planned, r.rgb, r.T,
                                r.last, r.fwd_state, None, None, r.status, r.grads[:n])
         if ev is not None:
             ev[3].record(stream)

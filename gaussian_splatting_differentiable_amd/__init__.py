@@ -50,7 +50,8 @@ class GsCamera(C.Structure):
 
 class GsSched(C.Structure):
     _fields_ = [("chunk_mode", C.c_int32), ("force_k", C.c_int32), ("force_h", C.c_int32),
-                ("lambda_", C.c_float), ("beta", C.c_float), ("eps", C.c_float)]
+                ("lambda_", C.c_float), ("beta", C.c_float), ("eps", C.c_float),
+                ("planned", C.c_int32)]
 
 
 _lib_handle = None
@@ -136,9 +137,17 @@ HK_MAX = 4096  # cap on h*k, the chunks of chunked tiles per frame
 
 def make_sched(chunk_mode: int = 1, force_k: int = 0, force_h: int = 0,
                lambda_: float = DEFAULT_LAMBDA, beta: float = DEFAULT_BETA,
-               eps: float = DEFAULT_EPS) -> GsSched:
+               eps: float = DEFAULT_EPS, planned: int = 0) -> GsSched:
     return GsSched(int(chunk_mode), int(force_k), int(force_h), float(lambda_), float(beta),
-                   float(eps))
+                   float(eps), int(planned))
+
+
+def planned_sched(sched) -> GsSched:
+    """A copy of sched (None: the defaults) for a forward whose plan was built
+    ahead with gs_plan_tiles on a stream it waits for."""
+    s = make_sched() if sched is None else GsSched.from_buffer_copy(sched)
+    s.planned = 1
+    return s
 
 
 def _ptr(t):
@@ -464,6 +473,7 @@ class Rasterizer:
         self.tile_counts = torch.zeros(self.tiles, dtype=torch.int32, device=dev)
         self.fwd_state = None
         self.plan_ahead = bool(plan_ahead)
+        self._plan_pending = False  # a plan built ahead waits for the next forward
         self._side = None
 
     def _ensure(self, n, capacity):
@@ -544,6 +554,20 @@ class Rasterizer:
             gs_plan_tiles_views(self.tile_counts, self.cam, self.V, self.sched, self.fwd_state,
                                 self.status, stream=self._side)
         self._ev_plan.record(self._side)
+        self._plan_pending = True
+
+    def clear_state(self):
+        """Zero the forward state (a plan built ahead is dropped with it)."""
+        self.fwd_state.zero_()
+        self._plan_pending = False
+
+    def _fwd_sched(self):
+        """The forward's knobs: with a plan built ahead for this frame, the forward
+        checks it inside its own launch (planned)."""
+        if not self._plan_pending:
+            return self.sched
+        self._plan_pending = False
+        return planned_sched(self.sched)
 
     def frame_status(self, n):
         """(device status, pair count I) of the frame, read once (synchronises)."""
@@ -574,19 +598,20 @@ class Rasterizer:
             self.stats.zero_()
             self.pixel_hits.zero_()
             st, ph = self.stats, self.pixel_hits
+        sched = self._fwd_sched()
         if clear_grads:
             if self.V > 1:
                 raise ValueError("clear_grads takes one view")
-            gs_render_fwd_zero(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched,
+            gs_render_fwd_zero(n, self.splats, self.sorted_ids, self.ranges, self.cam, sched,
                                self.rgb, self.T, self.last, self.fwd_state, st, ph, self.status,
                                self.grads[:n], background)
             return self.rgb, self.T, self.last
         if self.V > 1:
             gs_render_fwd_views(n, self.splats, self.sorted_ids, self.ranges, self.cam, self.V,
-                                self.sched, self.rgb, self.T, self.last, self.fwd_state, st, ph,
+                                sched, self.rgb, self.T, self.last, self.fwd_state, st, ph,
                                 self.status, background)
             return self.rgb, self.T, self.last
-        args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, self.sched, self.rgb,
+        args = (n, self.splats, self.sorted_ids, self.ranges, self.cam, sched, self.rgb,
                 self.T, self.last, self.fwd_state, st, ph, self.status)
         if background is None:
             gs_render_fwd(*args)

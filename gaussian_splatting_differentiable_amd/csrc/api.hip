@@ -157,6 +157,7 @@ gs_sched default_sched() {
   s.lambda_ = 131072.0f;  // measured on MI355X (see gs_sched in gs.h)
   s.beta = 0.25f;
   s.eps = 0.10f;
+  s.planned = 0;
   return s;
 }
 
@@ -325,7 +326,7 @@ int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
   if (!aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
   const gs_sched sc = sched ? *sched : default_sched();
   if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
-      !(sc.beta >= 0.0f))
+      !(sc.beta >= 0.0f) || (sc.planned != 0 && sc.planned != 1))
     return GS_ERR_INVALID_ARGUMENT;
   const int workers = worker_waves();
   if (workers <= 0) return GS_ERR_HIP;

@@ -597,13 +597,14 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
   float *gacc = gacc_all[wave_in_block()];
   int32_t *rows = rows_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, ntiles);
+  const int bc = bin_count(fs);
   // the frame failed earlier: nothing to differentiate
   if (!fs.hdr->run_f || *status != GS_OK) return;
   // bins: the forward filed the items (frames with few tiles: the preparation
   // wrote bitems)
   const bool bins = fs.hdr->bmode != 0;
   __shared__ int bpre[GS_GROUPS * BPRE];
-  if (bins) load_bin_starts(fs, bpre);
+  if (bins) bin_starts(bc, bpre);
   for (int i = __lane_id(); i < 2 * 9 * SLOTS; i += GS_WAVE) gacc[i] = 0.0f;
   if (__lane_id() == 0) {
     Staged dead;
@@ -759,11 +760,13 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_bwd(
     walk_back<WIDE>(splats, n, sorted_ids, cs, contrib_base(fs, 0, tile, rg.x) + ((cs - rg.x) >> 6),
                     fs.nw, nbw, x, stage, gacc, rows, grads);
   }
-  // The last wave out of the launch resets the queue heads, so the backward
-  // may run again on this state (every other wave has made its last pop).
-  if (lane == 0 && atomicAdd(&waves_out, 1) == GS_WAVES_PER_BLOCK - 1 &&
+  // The last wave out of the launch resets the bins' queue heads, so the
+  // backward may run again on this state (every other wave has made its last
+  // pop). A frame with few tiles has its heads set by its preparation, which
+  // runs before every backward launch.
+  if (bins && lane == 0 && atomicAdd(&waves_out, 1) == GS_WAVES_PER_BLOCK - 1 &&
       atomicAdd(&fs.hdr->bexit, 1) == (int)gridDim.x - 1) {
-    for (int g = 0; g < GS_GROUPS; g++) queue_head(fs, 1, g)[0] = bins ? 0 : fs.hdr->init_b[g];
+    for (int g = 0; g < GS_GROUPS; g++) queue_head(fs, 1, g)[0] = 0;
     fs.hdr->bexit = 0;
   }
 }

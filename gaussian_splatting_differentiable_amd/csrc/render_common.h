@@ -459,13 +459,18 @@ __device__ __forceinline__ int next_item(const FwdState &fs, int pass, Worker &w
 
 // The backward's items filed in bins by the forward (bmode 1). Each workgroup
 // keeps every group's bin starts in LDS: bpre[g][b] = items of group g in
-// bins before b, bpre[g][BO_BINS] the group's total. Call from every thread
-// before make_worker (whose barrier publishes the table).
+// bins before b, bpre[g][BO_BINS] the group's total. Wave g < GS_GROUPS
+// loads group g's counts (bin_count, issued first, beside the header's loads)
+// and scans them; call bin_starts from every thread before make_worker (whose
+// barrier publishes the table).
 constexpr int BPRE = BO_BINS + 1;
-__device__ __forceinline__ void load_bin_starts(const FwdState &fs, int *bpre) {
+__device__ __forceinline__ int bin_count(const FwdState &fs) {
+  const int g = threadIdx.x >> 6;
+  return g < GS_GROUPS ? fs.bcnt[g * BO_BINS + (threadIdx.x & 63)] : 0;
+}
+__device__ __forceinline__ void bin_starts(int v, int *bpre) {
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   if (g < GS_GROUPS) {
-    int v = fs.bcnt[g * BO_BINS + lane];
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int u = __shfl_up(v, d, 64);

@@ -334,6 +334,48 @@ __device__ __forceinline__ void clear_slice(float *__restrict__ out, int64_t nou
   if (w == workers - 1 && lane < nout - 4 * n4) out[4 * n4 + lane] = 0.0f;  // the ragged end
 }
 
+// A plan built ahead that the forward checks itself (no hand-over launch): the
+// knobs and worker count it must have been built with, and the state's
+// contributor words per quarter.
+struct PlanKey {
+  int planned;  // 1: check the waiting plan in the launch
+  int mode, force_k, force_h, nblocks;
+  float lambda_, beta, eps;
+  long long nw;
+};
+
+// Whether this frame runs. planned: thread 0 of every workgroup checks the
+// plan built ahead against the frame (the same decision everywhere: the tile
+// grid, the knobs, the pair total against the tile ranges, the status), and
+// workgroup 0 records it for the backward; a mismatch is GS_ERR_WORKSPACE.
+// Otherwise the hand-over (or the schedule it built) decided.
+__device__ __forceinline__ bool frame_runs(const FwdState &fs, const PlanKey &key, int T,
+                                           const int2 *__restrict__ ranges,
+                                           unsigned long long *__restrict__ stats,
+                                           int32_t *__restrict__ status) {
+  if (!key.planned) return fs.hdr->run_f != 0;
+  __shared__ int s_run;
+  if (threadIdx.x == 0) {
+    const int st = *status;
+    const int64_t npairs = T > 0 ? (int64_t)ranges[T - 1].y : 0;
+    const PlanHdr *hd = fs.hdr;
+    const bool match = (hd->planned == PLAN_READY) & (hd->ntiles == T) & (hd->nw == key.nw) &
+                       (hd->plan_mode == key.mode) & (hd->plan_force_k == key.force_k) &
+                       (hd->plan_force_h == key.force_h) & (hd->plan_nblocks == key.nblocks) &
+                       (hd->plan_lambda == key.lambda_) & (hd->plan_beta == key.beta) &
+                       (hd->plan_eps == key.eps) & (npairs == (int64_t)hd->plan_pairs);
+    if (st == GS_OK && !match) report_status(status, GS_ERR_WORKSPACE);
+    const bool run = hd->run_f && st == GS_OK && match;
+    if (blockIdx.x == 0) {
+      fs.hdr->run_f = run;
+      if (run && stats) atomicAdd(&stats[3], (unsigned long long)hd->h);
+    }
+    s_run = run;
+  }
+  __syncthreads();
+  return s_run != 0;
+}
+
 // STATS: count hits, tested entries and sub-tile hits (only when the caller asks
 // for them: the counters cost a few scalar instructions per entry). CUTS: the
 // frame has few tiles, and its plain walks record their state at the cuts.
@@ -344,12 +386,13 @@ __attribute__((amdgpu_waves_per_eu(4))) k_render_fwd(
     const int2 *__restrict__ ranges, CamK cam, float *__restrict__ rgb, float *__restrict__ Tout,
     int32_t *__restrict__ last, char *__restrict__ state, int T,
     unsigned long long *__restrict__ stats, int32_t *__restrict__ pixel_hits,
-    int32_t *__restrict__ status, int spin_limit, float *__restrict__ clear, int64_t nclear) {
+    int32_t *__restrict__ status, int spin_limit, float *__restrict__ clear, int64_t nclear,
+    PlanKey key) {
   __shared__ Splat sbuf_all[GS_WAVES_PER_BLOCK][BATCH];
   Splat *sbuf = sbuf_all[wave_in_block()];
   FwdState fs = fwd_state_at(state, T);
   // a frame that failed earlier has an empty plan: its workers only clear
-  const bool run = fs.hdr->run_f != 0;
+  const bool run = frame_runs(fs, key, T, ranges, stats, status);
   const bool bins = fs.hdr->bmode != 0;
   fs.nw = fs.hdr->nw;
   const int k = fs.hdr->k;
@@ -542,9 +585,23 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                                 int64_t nclear, hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
   const int ntiles = cam.tiles_x * cam.tiles_y;
   const int nblocks = workers_waves / GS_WAVES_PER_BLOCK;
-  hipError_t e = gs_launch_schedule(ranges, nullptr, cam, sched.chunk_mode, sched.force_k, sched.force_h,
-                                    sched.lambda_, sched.beta, sched.eps, nblocks, fwd_state,
-                                    stats, status, cap_pairs, st);
+  PlanKey key;
+  key.planned = sched.planned;
+  key.mode = sched.chunk_mode;
+  key.force_k = sched.force_k;
+  key.force_h = sched.force_h;
+  key.nblocks = nblocks;
+  key.lambda_ = sched.lambda_;
+  key.beta = sched.beta;
+  key.eps = sched.eps;
+  key.nw = contrib_words(ntiles, cap_pairs);
+  hipError_t e = hipSuccess;
+  // a plan built ahead is checked inside the launch; otherwise the schedule
+  // hands a waiting plan over, or builds one
+  if (!sched.planned)
+    e = gs_launch_schedule(ranges, nullptr, cam, sched.chunk_mode, sched.force_k, sched.force_h,
+                           sched.lambda_, sched.beta, sched.eps, nblocks, fwd_state, stats, status,
+                           cap_pairs, st);
   if (e != hipSuccess) return e;
   // persistent workers, GS_WAVES_PER_BLOCK per workgroup; workers that find the
   // queues empty exit at once
@@ -558,7 +615,7 @@ hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorte
                      reinterpret_cast<const int2 *>(ranges), cam, rgb, T, last,
                      reinterpret_cast<char *>(fwd_state), ntiles,
                      reinterpret_cast<unsigned long long *>(stats), pixel_hits, status,
-                     gs_wait_limit(GS_SPIN_LIMIT), clear, clear ? nclear : (int64_t)0);
+                     gs_wait_limit(GS_SPIN_LIMIT), clear, clear ? nclear : (int64_t)0, key);
   e = hipGetLastError();
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
   return e;

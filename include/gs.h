@@ -106,6 +106,13 @@ typedef struct {
   float lambda_;
   float beta;
   float eps;
+  /* 1: the caller built this frame's plan ahead with gs_plan_tiles (same
+   * knobs) on a stream this call's stream waits for; gs_render_fwd then checks
+   * it inside its own launch instead of launching the hand-over first, and a
+   * frame without a matching plan fails with GS_ERR_WORKSPACE. 0: gs_render_fwd
+   * takes a plan built ahead if one waits, else builds it. gs_plan_tiles
+   * ignores this field. */
+  int32_t planned;
 } gs_sched;
 
 /* Human-readable name of a status (host). */

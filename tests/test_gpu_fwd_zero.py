@@ -34,7 +34,7 @@ def _frame(gsr, sc, ref):
     r._ensure(n, r.capacity)
     r.splats[:n].copy_(dev(ref["splats"]))
     r.bin_and_sort(n)
-    r.fwd_state.zero_()
+    r.clear_state()
     return r, n, dev(sc.dL_drgb)
 
 

@@ -89,7 +89,7 @@ def run_stages(gsr, sc, ref, capacity=None, sched=None, background=None, dL_dT=N
     # cleared so that contributor words the forward does not write read as zero
     r.sorted_ids[:npairs].copy_(dev(ref["sorted_ids"]))
     r.ranges.copy_(dev(ref["ranges"]))
-    r.fwd_state.zero_()
+    r.clear_state()
     r.render_fwd(n, stats=True, background=background)
     out["contrib"] = read_contrib(r, ref["ranges"])
     grads = r.render_bwd(n, dev(sc.dL_drgb), background=background,

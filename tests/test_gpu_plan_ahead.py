@@ -170,3 +170,66 @@ def test_plan_over_the_state_capacity_is_reported():
     r.render_fwd(sc.n)
     st, _ = r.frame_status(sc.n)
     assert st == gsr.GS_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- planned: checked in the launch
+
+def _planned_forward(gsr, r, n, sched):
+    gsr.gs_render_fwd(n, r.splats, r.sorted_ids, r.ranges, r.cam, gsr.planned_sched(sched), r.rgb,
+                      r.T, r.last, r.fwd_state, None, None, r.status)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_planned_forward_equals_the_handed_over_one(cfg):
+    """With sched.planned the forward checks the plan built ahead inside its own
+    launch (no hand-over launch): the same plan, the same images bit for bit."""
+    gsr = _gsr()
+    sc, ref = reference(cfg)
+    out = {}
+    for planned in (False, True):
+        r = rasterizer(gsr, sc, ref, plan_ahead=False)
+        r.enqueue_bin_sort(sc.n)
+        counts = np.diff(ref["ranges"], axis=1)[:, 0].astype(np.int32)
+        gsr.gs_plan_tiles(dev(counts), r.cam, r.sched, r.fwd_state, r.status)
+        if planned:
+            _planned_forward(gsr, r, sc.n, r.sched)
+        else:
+            r.render_fwd(sc.n)
+        r.check(f"planned={planned}")
+        g = host(r.render_bwd(sc.n, dev(sc.dL_drgb))).copy()
+        r.check(f"planned={planned} backward")
+        out[planned] = (plan_fields(read_plan(r)), host(r.rgb), host(r.T), host(r.last), g)
+    for k in out[True][0]:
+        assert np.array_equal(np.asarray(out[True][0][k]), np.asarray(out[False][0][k])), k
+    for a, b in zip(out[True][1:4], out[False][1:4]):
+        assert np.array_equal(a, b)
+    rel = np.linalg.norm(out[True][4] - out[False][4], axis=0) / np.linalg.norm(out[False][4], axis=0)
+    assert np.all(rel <= 1e-5)
+
+
+def test_planned_forward_without_a_plan_is_reported():
+    """sched.planned on a state that holds no plan built ahead: GS_ERR_WORKSPACE,
+    the forward renders nothing and the backward adds nothing."""
+    gsr = _gsr()
+    sc, ref = reference(1)
+    r = rasterizer(gsr, sc, ref, plan_ahead=False)
+    r.enqueue_bin_sort(sc.n)
+    r.clear_state()
+    r.rgb.fill_(7.0)
+    _planned_forward(gsr, r, sc.n, r.sched)
+    g = r.render_bwd(sc.n, dev(sc.dL_drgb))
+    st, _ = r.frame_status(sc.n)
+    assert st == gsr.GS_ERR_WORKSPACE
+    assert torch.all(r.rgb == 7.0).item() and np.all(host(g) == 0)
+
+
+def test_planned_forward_with_other_knobs_is_reported():
+    gsr = _gsr()
+    sc, ref = reference(2)
+    r = rasterizer(gsr, sc, ref, sched=gsr.make_sched(chunk_mode=0), plan_ahead=False)
+    r.enqueue_bin_sort(sc.n)
+    counts = np.diff(ref["ranges"], axis=1)[:, 0].astype(np.int32)
+    gsr.gs_plan_tiles(dev(counts), r.cam, gsr.make_sched(chunk_mode=0), r.fwd_state, r.status)
+    _planned_forward(gsr, r, sc.n, gsr.make_sched(chunk_mode=2, force_k=8, force_h=3))
+    st, _ = r.frame_status(sc.n)
+    assert st == gsr.GS_ERR_WORKSPACE
