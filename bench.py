@@ -2,10 +2,12 @@
 
 Workload: the garden-shaped scene, 1,535,033 Gaussians, SH degree 3,
 1297x840 image (82 x 53 = 4346 tiles), seeded synthetic data already resident
-in HBM. A step runs gs_bin_tiles, gs_sort_keys, gs_render_fwd and
-gs_render_bwd on one HIP stream over the projected splats, and gs_plan_tiles
-(the tile schedule, from the binning pass's tile counts) on a second stream
-while the sort runs; the forward waits for it. gs_project (the feeder) is
+in HBM. A step runs gs_bin_tiles, gs_sort_keys_plan (the sort, with the tile
+schedule built in a spare workgroup of its last pass; frames whose last pass
+is too short to hide it build it beside the sort on a second stream with
+gs_plan_tiles), gs_render_fwd_zero (the forward, which checks that schedule in
+its own launch and clears the gradient rows in its workers' idle end) and
+gs_render_bwd_accumulate, over the projected splats. gs_project (the feeder) is
 timed in its own loop and reported beside it. The
 headline value is tile-Gaussian pairs per second over the step. The roofline
 object covers the longest raster kernel, with algorithmic work per unit as
@@ -223,34 +225,47 @@ def frame_diagnostics(gsr, sc, r, n, cus):
     }
 
 
-def stage_times(gsr, r, n, dL, steps, warmup):
-    """Median ms of bin, sort (with the schedule built beside it), forward and
-    backward over `steps` frames, HIP events between the calls."""
+def make_step(gsr, r, n, dL, npairs):
+    """One frame's calls on the current stream, as `step(ev=None)`: bin, sort,
+    forward and backward, with HIP events ev[0..4] around them when given. The
+    tile schedule is built inside the sort when the frame's last tile pass runs
+    long enough to hide it (gsr.plan_in_sort), else beside the sort on a second
+    stream that the forward's stream waits for; either way the forward checks
+    it in its own launch. The forward clears the gradient rows in its workers'
+    idle end and the backward adds into them."""
     import torch
     stream = torch.cuda.current_stream()
+    planned = gsr.planned_sched(r.sched)
+    in_sort = gsr.plan_in_sort(r.tiles, npairs)
     side = torch.cuda.Stream()
     ev_bin, ev_plan = torch.cuda.Event(), torch.cuda.Event()
-
-    planned = gsr.planned_sched(r.sched)  # the forward checks the plan built ahead itself
+    cap = r.capacity
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        gsr.gs_bin_tiles(n, r.splats, r.cam, r.capacity, r.offsets, None, None, r.status,
-                         r.workspace, tile_counts=r.tile_counts)
-        ev_bin.record(stream)
-        side.wait_event(ev_bin)
-        gsr.gs_plan_tiles(r.tile_counts, r.cam, r.sched, r.fwd_state, r.status, stream=side)
-        ev_plan.record(side)
+        if in_sort:
+            gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status,
+                             r.workspace)
+        else:
+            gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status,
+                             r.workspace, tile_counts=r.tile_counts)
+            ev_bin.record(stream)
+            side.wait_event(ev_bin)
+            gsr.gs_plan_tiles(r.tile_counts, r.cam, r.sched, r.fwd_state, r.status, stream=side)
+            ev_plan.record(side)
         if ev is not None:
             ev[1].record(stream)
-        gsr.gs_sort_keys(n, r.splats, r.offsets, r.capacity, r.cam, None, r.sorted_ids,
-                         r.ranges, r.status, r.workspace)
+        if in_sort:
+            gsr.gs_sort_keys_plan(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids,
+                                  r.ranges, r.sched, r.fwd_state, r.status, r.workspace)
+        else:
+            gsr.gs_sort_keys(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids, r.ranges,
+                             r.status, r.workspace)
         if ev is not None:
             ev[2].record(stream)
-        stream.wait_event(ev_plan)
-        # the forward clears the gradient rows once its workers run out of
-        # tiles; the backward adds into them
+        if not in_sort:
+            stream.wait_event(ev_plan)
         gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, planned, r.rgb, r.T,
                                r.last, r.fwd_state, None, None, r.status, r.grads[:n])
         if ev is not None:
@@ -259,6 +274,16 @@ def stage_times(gsr, r, n, dL, steps, warmup):
                                      r.fwd_state, dL, r.grads, r.status)
         if ev is not None:
             ev[4].record(stream)
+
+    return step, in_sort
+
+
+def stage_times(gsr, r, n, dL, steps, warmup):
+    """Median ms of bin, sort (with the tile schedule built inside it or beside
+    it), forward and backward over `steps` frames, HIP events between the calls."""
+    import torch
+    npairs = int(r.offsets[n:n + 1].item())
+    step, _ = make_step(gsr, r, n, dL, npairs)
 
     for _ in range(warmup):
         step()
@@ -456,43 +481,8 @@ def main():
           f"{sub_hits}, chunked tiles {chunked} x {chunks}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()  # the schedule, built beside the sort
-    ev_bin, ev_plan = torch.cuda.Event(), torch.cuda.Event()
-    cap = r.capacity
     stages = ["bin", "sort", "fwd", "bwd"]
-
-    planned = gsr.planned_sched(r.sched)  # the forward checks the plan built ahead itself
-
-    def step(ev=None, evp=None):
-        if ev is not None:
-            ev[0].record(stream)
-        gsr.gs_bin_tiles(n, r.splats, r.cam, cap, r.offsets, None, None, r.status, r.workspace,
-                         tile_counts=r.tile_counts)
-        ev_bin.record(stream)
-        side.wait_event(ev_bin)
-        if evp is not None:
-            evp[0].record(side)
-        gsr.gs_plan_tiles(r.tile_counts, r.cam, r.sched, r.fwd_state, r.status, stream=side)
-        if evp is not None:
-            evp[1].record(side)
-        ev_plan.record(side)
-        if ev is not None:
-            ev[1].record(stream)
-        gsr.gs_sort_keys(n, r.splats, r.offsets, cap, r.cam, None, r.sorted_ids, r.ranges,
-                         r.status, r.workspace)
-        if ev is not None:
-            ev[2].record(stream)
-        stream.wait_event(ev_plan)
-        # the forward clears the gradient rows once its workers run out of
-        # tiles; the backward adds into them
-        gsr.gs_render_fwd_zero(n, r.splats, r.sorted_ids, r.ranges, r.cam, planned, r.rgb, r.T,
-                               r.last, r.fwd_state, None, None, r.status, r.grads[:n])
-        if ev is not None:
-            ev[3].record(stream)
-        gsr.gs_render_bwd_accumulate(n, r.splats, r.sorted_ids, r.ranges, r.cam, 1, r.T, r.last,
-                                     r.fwd_state, dL, r.grads, r.status)
-        if ev is not None:
-            ev[4].record(stream)
+    step, plan_in_sort = make_step(gsr, r, n, dL, npairs)
 
     for _ in range(args.warmup):
         step()
@@ -505,10 +495,8 @@ def main():
     # the stage breakdown: the same steps again with HIP events between the calls
     # (kept out of the timed loop above, whose steps they would lengthen)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    pevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-               for _ in range(args.steps)]
     for k in range(args.steps):
-        step(events[k], pevents[k])
+        step(events[k])
     torch.cuda.synchronize()
     # the raster kernels' own durations: the same steps again, with a pair of HIP
     # events recorded on the stream around each raster kernel launch (kept out
@@ -527,8 +515,6 @@ def main():
     for ev in events:
         for i, s in enumerate(stages):
             per[s].append(ev[i].elapsed_time(ev[i + 1]))
-    # the schedule on the side stream (overlapped with the sort, not a stage)
-    per["plan"] = [e[0].elapsed_time(e[1]) for e in pevents]
     ms = {s: float(np.median(v)) for s, v in per.items()}
     ms_min = {s: float(np.min(v)) for s, v in per.items()}
     ms_step = t_wall * 1e3 / args.steps
@@ -677,7 +663,9 @@ def main():
                                f"{cam.width}x{cam.height} image, {cam.num_tiles} tiles",
                    "pairs": npairs, "hits": hits, "lane_evaluations": lane_evals,
                    "subtile_hits": sub_hits, "chunk_mode": args.chunk_mode,
-                   "chunked_tiles": chunked, "chunks_per_tile": chunks},
+                   "chunked_tiles": chunked, "chunks_per_tile": chunks,
+                   "schedule": "built inside the sort" if plan_in_sort
+                   else "built beside the sort on a second stream"},
         "ms": {k: round(v, 4) for k, v in ms.items()},
         "ms_min": {k: round(v, 4) for k, v in ms_min.items()},
         "ms_project": round(ms_project, 4),

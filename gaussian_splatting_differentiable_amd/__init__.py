@@ -32,7 +32,7 @@ EXPORTS = ("gs_strerror", "gs_workspace_size", "gs_fwd_state_size", "gs_project"
            "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd",
            "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views", "gs_timing_start",
            "gs_timing_read", "gs_set_wait_limit", "gs_render_bwd_accumulate",
-           "gs_render_fwd_zero")
+           "gs_render_fwd_zero", "gs_sort_keys_plan")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -83,6 +83,8 @@ def lib():
     L.gs_render_fwd_bg.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P]
     L.gs_render_bwd_bg.argtypes = L.gs_render_bwd.argtypes[:-1] + [P, P, P]
     L.gs_render_fwd_zero.argtypes = L.gs_render_fwd.argtypes[:-1] + [P, P, i64, P]
+    L.gs_sort_keys_plan.argtypes = [i32, P, P, i64, cam_p, P, P, P, C.POINTER(GsSched), P, sz, P,
+                                    P, sz, P]
     L.gs_workspace_size_views.argtypes = [i32, i32, i32, i32, i64]
     L.gs_workspace_size_views.restype = sz
     L.gs_fwd_state_size_views.argtypes = [i32, i32, i32, i64]
@@ -108,7 +110,7 @@ def lib():
                  "gs_render_fwd_views", "gs_render_bwd_views", "gs_sort_keys", "gs_render_fwd",
                  "gs_render_bwd", "gs_sort_keys_noalloc", "gs_plan_tiles", "gs_plan_tiles_views",
                  "gs_timing_start", "gs_timing_read", "gs_set_wait_limit",
-                 "gs_render_bwd_accumulate", "gs_render_fwd_zero"):
+                 "gs_render_bwd_accumulate", "gs_render_fwd_zero", "gs_sort_keys_plan"):
         getattr(L, name).restype = i32
     _lib_handle = L
     return L
@@ -140,6 +142,18 @@ def make_sched(chunk_mode: int = 1, force_k: int = 0, force_h: int = 0,
                eps: float = DEFAULT_EPS, planned: int = 0) -> GsSched:
     return GsSched(int(chunk_mode), int(force_k), int(force_h), float(lambda_), float(beta),
                    float(eps), int(planned))
+
+
+TILE_PASS_PARTITION = 16384  # pairs per partition of the sort's tile passes
+
+
+def plan_in_sort(tiles: int, pairs: int) -> bool:
+    """Whether gs_sort_keys_plan hides the tile schedule (about 30 us in one
+    workgroup) inside the sort: the frame has a 5-bit tile pass (257 to 8192
+    tiles) with at least one round of partitions on every compute unit. Other
+    frames build the schedule beside the sort on a second stream."""
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return 256 < tiles <= 8192 and pairs >= cus * TILE_PASS_PARTITION
 
 
 def planned_sched(sched) -> GsSched:
@@ -358,6 +372,19 @@ def gs_sort_keys(n, splats, offsets, capacity, cam, sorted_keys, sorted_ids, ran
            "gs_sort_keys")
 
 
+def gs_sort_keys_plan(n, splats, offsets, capacity, cam, sorted_keys, sorted_ids, ranges, sched,
+                      fwd_state, status, workspace, stream=None):
+    """gs_sort_keys that also builds the frame's tile schedule into fwd_state, for
+    a forward with planned_sched(sched) on the same stream."""
+    _check(lib().gs_sort_keys_plan(int(n), _ptr(splats), _ptr(offsets), int(capacity),
+                                   C.byref(cam), _ptr(sorted_keys), _ptr(sorted_ids), _ptr(ranges),
+                                   C.byref(sched) if sched is not None else None, _ptr(fwd_state),
+                                   fwd_state.numel() * fwd_state.element_size(), _ptr(status),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)),
+           "gs_sort_keys_plan")
+
+
 def gs_render_fwd(n, splats, sorted_ids, ranges, cam, sched, rgb, T_final, last, fwd_state,
                   stats, pixel_hits, status, stream=None):
     _check(lib().gs_render_fwd(int(n), _ptr(splats), _ptr(sorted_ids), _ptr(ranges), C.byref(cam),
@@ -444,9 +471,11 @@ class Rasterizer:
     Every call only enqueues work on the current stream. The frame's device
     status word is read once, after the frame (``frame_status``); ``run_frame``
     chains a whole frame and, when the pairs overflowed the buffers, grows them
-    and runs the frame again. With plan_ahead the tile schedule is built from
-    the binning pass's tile counts on a second stream while the sort runs
-    (gs_plan_tiles), and the forward uses it.
+    and runs the frame again. With plan_ahead the tile schedule is built
+    before the forward needs it: for one view inside the sort
+    (gs_sort_keys_plan), for a batch of views from the binning pass's tile
+    counts on a second stream while the sort runs (gs_plan_tiles_views); the
+    forward then checks it in its own launch (sched.planned).
     """
 
     def __init__(self, camera, device="cuda", capacity=1 << 20, sched=None, n_views=1,
@@ -474,6 +503,7 @@ class Rasterizer:
         self.fwd_state = None
         self.plan_ahead = bool(plan_ahead)
         self._plan_pending = False  # a plan built ahead waits for the next forward
+        self._pairs_seen = 0  # the last frame's pairs (where its schedule is built)
         self._side = None
 
     def _ensure(self, n, capacity):
@@ -525,6 +555,14 @@ class Rasterizer:
         else:
             gs_bin_tiles_views(n, self.splats, self.cam, self.V, self.capacity, self.offsets,
                                keys, ids, self.status, self.workspace, tile_counts=tc)
+        if self.V == 1 and self.plan_ahead and plan_in_sort(self.tiles, self._pairs_seen):
+            # the sort builds the schedule in a spare workgroup of its last pass
+            gs_sort_keys_plan(n, self.splats, self.offsets, self.capacity, self.cam, skeys,
+                              self.sorted_ids, self.ranges, self.sched, self.fwd_state,
+                              self.status, self.workspace)
+            self._plan_pending = True
+            return
+        # otherwise the schedule beside the sort, on a second stream
         if self.plan_ahead:
             self._enqueue_plan()
         if self.V == 1:
@@ -572,6 +610,7 @@ class Rasterizer:
     def frame_status(self, n):
         """(device status, pair count I) of the frame, read once (synchronises)."""
         both = torch.cat([self.status, self.offsets[n:n + 1]]).cpu()
+        self._pairs_seen = int(both[1])
         return int(both[0]), int(both[1])
 
     def bin_and_sort(self, n, want_keys=False, want_emission=False):

@@ -23,7 +23,8 @@ hipError_t gs_launch_bin(int n, const float *splats, const CamK &cam, int64_t ca
 size_t gs_sort_ws_bytes(int n, int64_t cap, int tiles_x, int tiles_y);
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
-                          int32_t *ranges, int32_t *status, void *ws, hipStream_t st);
+                          int32_t *ranges, int32_t *status, void *ws, const SortPlan *plan,
+                          hipStream_t st);
 hipError_t gs_launch_render_fwd(int n, const float *splats, const int32_t *sorted_ids,
                                 const int32_t *ranges, const CamK &cam, const gs_sched &sched,
                                 float *rgb, float *T, int32_t *last, void *fwd_state,
@@ -288,7 +289,8 @@ int32_t bin_impl(int32_t n, const float *splats, const CamK &k, int64_t pair_cap
 
 int32_t sort_impl(int32_t n, const float *splats, const int32_t *offsets, int64_t pair_capacity,
                   const CamK &k, uint64_t *sorted_keys, int32_t *sorted_ids, int32_t *tile_ranges,
-                  int32_t *device_status, void *workspace, size_t workspace_bytes, void *stream) {
+                  int32_t *device_status, void *workspace, size_t workspace_bytes, void *stream,
+                  const SortPlan *plan = nullptr) {
   if (n < 0 || pair_capacity < 0) return GS_ERR_INVALID_ARGUMENT;
   if (batch_tiles(k) > GS_MAX_TILES || n >= GS_COUNT_LIMIT || pair_capacity >= GS_COUNT_LIMIT)
     return GS_ERR_UNSUPPORTED;
@@ -301,7 +303,8 @@ int32_t sort_impl(int32_t n, const float *splats, const int32_t *offsets, int64_
   if (workspace_bytes < gs_sort_ws_bytes(n, pair_capacity, k.tiles_x, k.tiles_y))
     return GS_ERR_WORKSPACE;
   return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
-                                   tile_ranges, device_status, workspace, (hipStream_t)stream));
+                                   tile_ranges, device_status, workspace, plan,
+                                   (hipStream_t)stream));
 }
 
 int32_t fwd_impl(int32_t n, const float *splats, const int32_t *sorted_ids,
@@ -416,6 +419,36 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
   if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
   return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
                    device_status, workspace, workspace_bytes, stream);
+}
+
+int32_t gs_sort_keys_plan(int32_t n, const float *splats, const int32_t *offsets,
+                          int64_t pair_capacity, const gs_camera *cam, uint64_t *sorted_keys,
+                          int32_t *sorted_ids, int32_t *tile_ranges, const gs_sched *sched,
+                          void *fwd_state, size_t fwd_state_bytes, int32_t *device_status,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  CamK k;
+  if (!prep_camera(cam, &k)) return GS_ERR_INVALID_ARGUMENT;
+  if (!fwd_state || !aligned(fwd_state, 256)) return GS_ERR_INVALID_ARGUMENT;
+  const int64_t cap_pairs = fwd_state_capacity((int)batch_tiles(k), fwd_state_bytes);
+  if (cap_pairs < 0) return GS_ERR_WORKSPACE;
+  const gs_sched sc = sched ? *sched : default_sched();
+  if (sc.chunk_mode < 0 || sc.chunk_mode > 2 || !(sc.eps >= 0.0f) || !(sc.lambda_ >= 0.0f) ||
+      !(sc.beta >= 0.0f))
+    return GS_ERR_INVALID_ARGUMENT;
+  const int workers = worker_waves();
+  if (workers <= 0) return GS_ERR_HIP;
+  SortPlan plan;
+  plan.fwd_state = fwd_state;
+  plan.mode = sc.chunk_mode;
+  plan.force_k = sc.force_k;
+  plan.force_h = sc.force_h;
+  plan.nblocks = workers / GS_WAVES_PER_BLOCK;
+  plan.lambda_ = sc.lambda_;
+  plan.beta = sc.beta;
+  plan.eps = sc.eps;
+  plan.cap = cap_pairs;
+  return sort_impl(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids, tile_ranges,
+                   device_status, workspace, workspace_bytes, stream, &plan);
 }
 
 int32_t gs_plan_tiles(const int32_t *tile_counts, const gs_camera *cam, const gs_sched *sched,
@@ -680,7 +713,7 @@ int32_t gs_sort_keys_noalloc(int32_t n, const float *splats, const gs_camera *ca
                                device_status, ws, st);
   if (e != hipSuccess) return GS_ERR_HIP;
   return hip_status(gs_launch_sort(n, splats, offsets, pair_capacity, k, sorted_keys, sorted_ids,
-                                   tile_ranges, device_status, ws, st));
+                                   tile_ranges, device_status, ws, nullptr, st));
 }
 
 int32_t gs_set_wait_limit(int32_t probes) {

@@ -34,6 +34,15 @@ struct CamK {
   int view;         // the projection's camera index within its batch
 };
 
+// The tile schedule a sort may build beside its last tile pass
+// (gs_sort_keys_plan): where, with which knobs and worker count.
+struct SortPlan {
+  void *fwd_state;
+  int mode, force_k, force_h, nblocks;
+  double lambda_, beta, eps;
+  int64_t cap;  // the pairs the forward state holds
+};
+
 // View index stored in a splat record's pad word.
 __device__ __forceinline__ int record_view(const Splat &s) { return __float_as_int(s.p2.w); }
 

@@ -40,6 +40,7 @@
 #include <stddef.h>
 
 #include "bin_spans.h"
+#include "sched_body.h"
 
 namespace {
 
@@ -495,6 +496,13 @@ struct PassIn {
   int dhist_copies;            // ... as this many copies, B apart, to be summed
   uint32_t *wide_kout, *wide_vout;  // third depth pass: its output when the fourth pass runs
   int spin_limit;              // probes before a look-back wait gives up
+  // the 5-bit tile pass: the frame's tile schedule, built by its first workgroup
+  // from the tile counts (plan_state null: none)
+  char *plan_state;
+  const int32_t *plan_counts;
+  int plan_mode, plan_force_k, plan_force_h, plan_nblocks;
+  double plan_lambda, plan_beta, plan_eps;
+  int64_t plan_cap;
 };
 
 template <int NT, int ITEMS, int BITS, int SRC>
@@ -506,8 +514,10 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   constexpr int B = 1 << BITS;
   constexpr int NWV = NT / 64;
   constexpr int PART = NT * ITEMS;
-  __shared__ uint32_t s_key[PART];
-  __shared__ uint32_t s_val[PART];
+  // keys and values in one array: the schedule's workgroup (below) takes all of
+  // it as its working LDS
+  __shared__ __align__(16) uint32_t s_kv[2 * PART];
+  uint32_t *const s_key = s_kv, *const s_val = s_kv + PART;
   __shared__ int s_wcnt[NWV][B];
   __shared__ int s_lbase[B];
   __shared__ uint32_t s_gbase[B];
@@ -515,6 +525,25 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   __shared__ uint32_t s_mark[SRC == SRC_EMIT ? PART / 32 : 1];
   __shared__ uint32_t s_h2[SRC == SRC_DEPTH0 ? 512 : 1], s_h3[SRC == SRC_DEPTH0 ? 32 : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The 5-bit tile pass (frames of 257 to 8192 tiles) builds the frame's tile
+  // schedule in its first workgroup, beside the partitions, with the key and
+  // value arrays as the schedule's LDS (4 x 8192 words); its partitions are
+  // the later workgroups.
+  constexpr bool PLANS = SRC == SRC_KEYS && BITS == 5 && NT == 1024 && 2 * PART == 4 * 8192;
+  int bid = blockIdx.x;
+  if constexpr (PLANS) {
+    if (in.plan_state) {
+      if (blockIdx.x == 0) {
+        const int T = in.tiles_x * in.tiles_y;
+        sched_impl::schedule_frame<true>(nullptr, in.plan_counts, T, in.tiles_x, in.plan_mode,
+                                         in.plan_force_k, in.plan_force_h, in.plan_lambda,
+                                         in.plan_beta, in.plan_eps, in.plan_nblocks,
+                                         in.plan_state, nullptr, in.status, in.plan_cap, s_kv);
+        return;
+      }
+      bid -= 1;
+    }
+  }
   // a depth pass takes its digit offsets (and the first one the number of
   // visible splats) from its digit histogram itself
   uint32_t dbase0 = 0;
@@ -549,7 +578,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     // blocks beyond the frame's partitions take no ticket (the launch is sized
     // for the capacity); exactly the first parts_of(n) block indices remain
     const int n_pre = SRC == SRC_DEPTH0 ? n_max : clamp_n(*n_dev, n_max);
-    if ((int64_t)blockIdx.x * PART >= (int64_t)n_pre) return;
+    if ((int64_t)bid * PART >= (int64_t)n_pre) return;
   }
   // after the first pass, a frame that has failed (here or in a call beside
   // this one) sorts no further: its earlier passes may have left positions
@@ -922,9 +951,19 @@ hipError_t gs_launch_bin_count(int n, const float *splats, const CamK &cam, int6
 
 int32_t gs_wait_limit(int32_t fallback);
 
+hipError_t gs_launch_schedule(const int32_t *ranges, const int32_t *counts, const CamK &cam,
+                              int chunk_mode, int force_k, int force_h, double lambda_,
+                              double beta, double eps, int nblocks, void *fwd_state,
+                              int64_t *stats, int32_t *status, int64_t cap_pairs,
+                              hipStream_t st);
+
+// plan (or null): build the frame's tile schedule into plan->fwd_state as well,
+// from the sort's tile counts: inside the 5-bit tile pass when the frame has
+// one (257 to 8192 tiles), else in a schedule launch after the sort.
 hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, int64_t cap,
                           const CamK &cam, uint64_t *sorted_keys, int32_t *sorted_ids,
-                          int32_t *ranges, int32_t *status, void *ws, hipStream_t st) {
+                          int32_t *ranges, int32_t *status, void *ws, const SortPlan *plan,
+                          hipStream_t st) {
   const Splat *sp = reinterpret_cast<const Splat *>(splats);
   const int ntiles = cam.tiles_x * cam.tiles_y;
   SortWs w = carve(reinterpret_cast<char *>(ws), n, cap, cam.tiles_x, cam.tiles_y);
@@ -1007,6 +1046,7 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
                      w.doff, w.part_first, status);
   int tbits = 1;
   while ((1 << tbits) < ntiles) tbits++;
+  bool planned = false;  // the schedule was built inside a tile pass
   // tile passes: the first generates its partition's pairs itself
   const int npt = (int)(parts_of(cap, TS_PART) > 1 ? parts_of(cap, TS_PART) : 1);
   uint32_t *status_t0 = w.status + 4 * w.pd, *status_t1 = status_t0 + w.pt;
@@ -1035,11 +1075,27 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
     final_tiles = sorted_keys ? w.tk[1] : nullptr;
     // the high digit has tbits - 8 significant bits: rank on 5 of them when
     // they fit (up to 8192 tiles), which cuts the ballots and the look-back
-    if (tbits - b0 <= 5)
-      hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 5, SRC_KEYS>), dim3(npt),
+    if (tbits - b0 <= 5) {
+      PassIn h = in;
+      if (plan) {
+        h.plan_state = reinterpret_cast<char *>(plan->fwd_state);
+        h.plan_counts = w.tile_counts;
+        h.tiles_x = cam.tiles_x;
+        h.tiles_y = cam.tiles_y;
+        h.plan_mode = plan->mode;
+        h.plan_force_k = plan->force_k;
+        h.plan_force_h = plan->force_h;
+        h.plan_nblocks = plan->nblocks;
+        h.plan_lambda = plan->lambda_;
+        h.plan_beta = plan->beta;
+        h.plan_eps = plan->eps;
+        h.plan_cap = plan->cap;
+        planned = true;
+      }
+      hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 5, SRC_KEYS>), dim3(npt + (plan ? 1 : 0)),
                          dim3(TS_THREADS), 0, st, w.tk[0], w.tv[0], final_tiles, ids_out, i_dev,
-                         capi, b0, tbase(1), status_t1, ticket(5), err, in);
-    else
+                         capi, b0, tbase(1), status_t1, ticket(5), err, h);
+    } else
       hipLaunchKernelGGL((k_onesweep<TS_THREADS, TS_ITEMS, 8, SRC_KEYS>), dim3(npt),
                          dim3(TS_THREADS), 0, st, w.tk[0], w.tv[0], final_tiles, ids_out, i_dev,
                          capi, b0, tbase(1), status_t1, ticket(5), err, in);
@@ -1048,5 +1104,10 @@ hipError_t gs_launch_sort(int n, const float *splats, const int32_t *offsets, in
     hipLaunchKernelGGL(k_sorted_keys, dim3(gs_div_up(cap > 0 ? cap : 1, 256)), dim3(256), 0, st,
                        ctl, capi, final_tiles, reinterpret_cast<const uint32_t *>(sorted_ids), sp,
                        sorted_keys, status);
-  return hipGetLastError();
+  hipError_t err_launch = hipGetLastError();
+  if (err_launch == hipSuccess && plan && !planned)
+    err_launch = gs_launch_schedule(nullptr, w.tile_counts, cam, plan->mode, plan->force_k,
+                                    plan->force_h, plan->lambda_, plan->beta, plan->eps,
+                                    plan->nblocks, plan->fwd_state, nullptr, status, plan->cap, st);
+  return err_launch;
 }

@@ -232,6 +232,21 @@ int32_t gs_sort_keys(int32_t n, const float *splats, const int32_t *offsets, int
                      int32_t *tile_ranges, int32_t *device_status, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* gs_sort_keys that also builds the frame's tile schedule (as gs_plan_tiles
+ * would, from the per-tile counts the sort itself holds) into fwd_state: a
+ * frame of 257 to 8192 tiles builds it in one more workgroup of its last tile
+ * pass, beside that pass's partitions, any other after the sort in a launch of
+ * its own. The plan waits for a gs_render_fwd with sched->planned = 1 on the
+ * same stream, which needs no event between the streams and no hand-over
+ * launch.
+ *   sched (NULL = defaults; `planned` ignored), fwd_state, fwd_state_bytes: as
+ *   for gs_plan_tiles; everything else as for gs_sort_keys. */
+int32_t gs_sort_keys_plan(int32_t n, const float *splats, const int32_t *offsets,
+                          int64_t pair_capacity, const gs_camera *cam, uint64_t *sorted_keys,
+                          int32_t *sorted_ids, int32_t *tile_ranges, const gs_sched *sched,
+                          void *fwd_state, size_t fwd_state_bytes, int32_t *device_status,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* The frame's tile schedule, built ahead of gs_render_fwd from the per-tile
  * counts of gs_bin_tiles (section 4 of the load-imbalance page: the
  * longest-first order of the tiles by pair count, the Eq. 6 chunking policy and

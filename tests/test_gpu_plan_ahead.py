@@ -233,3 +233,30 @@ def test_planned_forward_with_other_knobs_is_reported():
     _planned_forward(gsr, r, sc.n, gsr.make_sched(chunk_mode=2, force_k=8, force_h=3))
     st, _ = r.frame_status(sc.n)
     assert st == gsr.GS_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- the plan built inside the sort
+
+@pytest.mark.parametrize("name", list(SCHEDS))
+@pytest.mark.parametrize("size", [(600, 400), (1601, 1399), (256, 256)])
+def test_plan_built_in_the_sort_equals_the_forward_plan(size, name):
+    """gs_sort_keys_plan builds the schedule in a spare workgroup of its 5-bit
+    tile pass (600x400: 950 tiles), or after the sort when the frame has no such
+    pass (1601x1399: 8888 tiles; 256x256: 256 tiles); a planned forward uses it.
+    The plan equals the one the forward builds itself, field for field, and the
+    images are the same bit for bit."""
+    gsr = _gsr()
+    W, H = size
+    sc = scenegen.random_scene(41, 20000, W, H, 0.9 * W)
+    ref = oracle.frame(sc)
+    out = {}
+    for ahead in (True, False):
+        r = rasterizer(gsr, sc, ref, sched=gsr.make_sched(**SCHEDS[name]), plan_ahead=ahead)
+        r.run_frame(sc.n)
+        out[ahead] = (plan_fields(read_plan(r)), host(r.rgb), host(r.T), host(r.last))
+    pa, pb = out[True][0], out[False][0]
+    for k in pa:
+        assert np.array_equal(pa[k], pb[k]), k
+    check_queues(read_plan(r), (W + 15) // 16)
+    for a, b in zip(out[True][1:], out[False][1:]):
+        assert np.array_equal(a, b)
