@@ -175,3 +175,26 @@ def test_forward_clear_argument_validation_needs_no_gpu(gsr):
     assert L.gs_render_fwd_zero(*common, None, 16, None) == gsr.GS_ERR_INVALID_ARGUMENT
     assert L.gs_render_fwd_zero(*common, C.c_void_p((1 << 20) + 4), 16,
                                 None) == gsr.GS_ERR_INVALID_ARGUMENT
+
+
+def test_sort_with_plan_argument_validation_needs_no_gpu(gsr):
+    """gs_sort_keys_plan: a missing or misaligned forward state, one too small for
+    the tile grid, and bad schedule knobs are rejected before any HIP call."""
+    L = gsr.lib()
+    cam = gsr.GsCamera()
+    cam.width, cam.height, cam.fx, cam.fy = 64, 64, 64.0, 64.0
+    p = C.c_void_p(1 << 20)
+    st = gsr.fwd_state_size(64, 64, 1 << 10)
+    ws = gsr.workspace_size(16, 64, 64, 1 << 10)
+    args = lambda sched, fs, fsb: (16, p, p, 1 << 10, C.byref(cam), None, p, p, sched, fs, fsb, p, p,
+                                   ws, None)
+    assert L.gs_sort_keys_plan(*args(None, None, st)) == gsr.GS_ERR_INVALID_ARGUMENT
+    assert L.gs_sort_keys_plan(*args(None, C.c_void_p((1 << 20) + 64), st)) == \
+        gsr.GS_ERR_INVALID_ARGUMENT
+    assert L.gs_sort_keys_plan(*args(None, p, 64)) == gsr.GS_ERR_WORKSPACE
+    bad = gsr.make_sched(chunk_mode=3)
+    assert L.gs_sort_keys_plan(*args(C.byref(bad), p, st)) == gsr.GS_ERR_INVALID_ARGUMENT
+    # the forward refuses a `planned` value other than 0 and 1
+    odd = gsr.make_sched(planned=2)
+    assert L.gs_render_fwd(1, p, p, p, C.byref(cam), C.byref(odd), p, p, p, p, st, None, None, p,
+                           None) == gsr.GS_ERR_INVALID_ARGUMENT
