@@ -98,3 +98,32 @@ def test_a_failed_frame_only_clears():
                                  r.fwd_state, dL, r.grads, r.status)
     assert np.all(host(r.grads)[:n] == 0)
     assert int(host(r.status)[0]) == gsr.GS_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("cfg", [3, 5, 2])
+def test_the_benchmarked_chain_matches_the_oracle(cfg):
+    """Rasterizer.run_frame with dL/dC, the chain bench.py times: bin, the sort
+    with the schedule built inside it (garden and urban, from the second frame
+    on; small builds it beside the sort), the planned forward that clears the
+    gradient rows, the accumulating backward. Image, transmittance, last entry
+    and gradients against the oracle, on the oracle's splat records, for two
+    frames in a row (the counting forward: the same images bit for bit)."""
+    from test_gpu_parity import check_forward
+    gsr = _gsr()
+    sc, ref = reference(cfg)
+    n = sc.n
+    r = gsr.Rasterizer(sc.camera, capacity=max(len(ref["sorted_ids"]), 1))
+    r._ensure(n, r.capacity)
+    r.splats[:n].copy_(dev(ref["splats"]))
+    dL = dev(sc.dL_drgb)
+    for frame in range(2):
+        r.grads.fill_(float("nan"))
+        I = r.run_frame(n, dL, stats=True)
+        assert I == len(ref["sorted_ids"])
+        in_sort = gsr.plan_in_sort(r.tiles, I) and frame == 1
+        print(f"config {cfg} frame {frame}: schedule built "
+              f"{'inside' if in_sort else 'beside'} the sort", flush=True)
+        out = dict(rgb=host(r.rgb), T=host(r.T), last=host(r.last), grads=host(r.grads)[:n].copy(),
+                   pixel_hits=host(r.pixel_hits), stats=host(r.stats))
+        check_forward(ref, out)
+        check_backward(ref, out)
