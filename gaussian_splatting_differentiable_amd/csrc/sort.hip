@@ -39,6 +39,8 @@
 // This TU includes the canonical binning code: compile with -ffp-contract=off.
 #include <stddef.h>
 
+#include <type_traits>
+
 #include "bin_spans.h"
 #include "sched_body.h"
 
@@ -136,7 +138,8 @@ struct SortWs {
   int32_t *tile_counts;     // T
   int32_t *tile_diff;       // tiles_y x (tiles_x + 1): per-row difference array of pair counts
   uint32_t *dkey;           // n: depth key per splat (NO_DEPTH without pairs)
-  uint32_t *dk[2], *dv[2];  // n each: depth passes
+  uint32_t *dk[2];          // n each: depth passes, keys
+  uint32_t *dv[2];          // n 64-bit values each: splat id, its pair count above it
   uint32_t *dfinal;         // n: splat ids in depth order (the last depth pass's output)
   int32_t *dcnt;            // n: pair counts in depth order
   int32_t *doff;            // n + 1: pair offsets in depth order
@@ -165,7 +168,7 @@ SortWs carve(char *base, int n, int64_t cap, int tiles_x, int tiles_y) {
   w.tile_diff = (int32_t *)take(4 * (int64_t)tiles_y * (tiles_x + 1));
   w.dkey = (uint32_t *)take(4 * n2);
   for (int i = 0; i < 2; i++) w.dk[i] = (uint32_t *)take(4 * n2);
-  for (int i = 0; i < 2; i++) w.dv[i] = (uint32_t *)take(4 * n2);
+  for (int i = 0; i < 2; i++) w.dv[i] = (uint32_t *)take(8 * n2);  // id | pair count << 32
   w.dfinal = (uint32_t *)take(4 * n2);
   w.dcnt = (int32_t *)take(4 * n2);
   w.doff = (int32_t *)take(4 * n2);
@@ -516,8 +519,15 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   constexpr int PART = NT * ITEMS;
   // keys and values in one array: the schedule's workgroup (below) takes all of
   // it as its working LDS
-  __shared__ __align__(16) uint32_t s_kv[2 * PART];
-  uint32_t *const s_key = s_kv, *const s_val = s_kv + PART;
+  // The depth passes carry 64-bit values: the splat id in the low word and its
+  // pair count in the high word (read by the first pass in id order), so that
+  // the last one writes the counts in depth order without gathering them.
+  constexpr bool DEPTH = NT == DS_THREADS && ITEMS == DS_ITEMS && SRC != SRC_EMIT;
+  using VT = typename std::conditional<DEPTH, uint64_t, uint32_t>::type;
+  constexpr int VW = sizeof(VT) / 4;
+  __shared__ __align__(16) uint32_t s_kv[(1 + VW) * PART];
+  uint32_t *const s_key = s_kv;
+  VT *const s_val = reinterpret_cast<VT *>(s_kv + PART);
   __shared__ int s_wcnt[NWV][B];
   __shared__ int s_lbase[B];
   __shared__ uint32_t s_gbase[B];
@@ -661,18 +671,28 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   const bool wide = SRC == SRC_DEPTH0 && in.ctl->emax - emin > 15;
   const int64_t base = p0 + (int64_t)w * (ITEMS * 64);
   const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t key[ITEMS], val[ITEMS];
+  uint32_t key[ITEMS];
+  VT val[ITEMS];
   int rnk[ITEMS];
+  int hi[SRC == SRC_DEPTH0 ? ITEMS : 1], lo[SRC == SRC_DEPTH0 ? ITEMS : 1];
   // all of this thread's keys are loaded before any is ranked
 #pragma unroll
   for (int r = 0; r < ITEMS; r++) {
     const int64_t e = base + r * 64 + lane;
-    uint32_t k = NO_DEPTH, v = 0;
+    uint32_t k = NO_DEPTH;
+    VT v = 0;
+    if constexpr (SRC == SRC_DEPTH0) {
+      // the splat's pair count, loaded outside the branch so that every
+      // load is in flight at once (a slot past the end reads splat 0's)
+      const int64_t ec = e < n ? e : 0;
+      hi[r] = in.offsets[ec + 1];
+      lo[r] = in.offsets[ec];
+    }
     if (e < n) {
       if constexpr (SRC == SRC_DEPTH0) {
         k = in.dkey[e];
         if (k != NO_DEPTH) k -= (uint32_t)emin << 23;  // order kept: positive depths
-        v = (uint32_t)e;
+        v = (VT)e;
       } else if constexpr (SRC == SRC_EMIT) {
         // the nearest row start at or before this pair (position 0 always
         // starts one: the partition's first pair opens a row record)
@@ -685,11 +705,16 @@ __global__ void __launch_bounds__(NT) k_onesweep(
         v = s_val[st];
       } else {
         k = kin[e];
-        v = vin[e];
+        v = reinterpret_cast<const VT *>(vin)[e];
       }
     }
     key[r] = k;
     val[r] = v;
+  }
+  if constexpr (SRC == SRC_DEPTH0) {
+#pragma unroll
+    for (int r = 0; r < ITEMS; r++)
+      if (base + r * 64 + lane < n) val[r] |= (VT)(uint32_t)(hi[r] - lo[r]) << 32;
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; r++) {
@@ -805,6 +830,7 @@ __global__ void __launch_bounds__(NT) k_onesweep(
   // the third depth pass hands its keys to the fourth when that one runs
   const bool handoff = in.wide_vout && in.ctl->wide;
   uint32_t *ko = handoff ? in.wide_kout : kout, *vo = handoff ? in.wide_vout : vout;
+  // the last depth pass splits its values: ids to vout, pair counts to cout
   int32_t *co = handoff ? nullptr : in.cout;
   for (int i = tid; i < nv; i += NT) {
     const uint32_t k = s_key[i];
@@ -812,9 +838,13 @@ __global__ void __launch_bounds__(NT) k_onesweep(
     const uint32_t dst = s_gbase[d] + (uint32_t)(i - s_lbase[d]);
     if (dst >= (uint32_t)bound) continue;  // only after a look-back bound was hit (err is set)
     if (ko) ko[dst] = k;
-    const uint32_t v = s_val[i];
-    vo[dst] = v;
-    if (co) co[dst] = in.offsets[v + 1] - in.offsets[v];
+    const VT v = s_val[i];
+    if (co) {
+      vo[dst] = (uint32_t)v;
+      co[dst] = (int32_t)(v >> 32);
+    } else {
+      reinterpret_cast<VT *>(vo)[dst] = v;
+    }
   }
 }
 
