@@ -19,8 +19,10 @@
 //     less the smallest exponent (key - (emin << 23): the depths are positive,
 //     so the order is kept, and 27 bits hold every key when the exponents span
 //     fewer than 16 values), and a fourth over bits 27-31 that runs only when
-//     they span more (6144-key partitions); the last also writes each splat's
-//     pair count in depth order;
+//     they span more (6144-key partitions). Their values are 64-bit: the splat
+//     id, and above it the splat's pair count, read by the first pass in id
+//     order, so the last pass writes the counts in depth order from its own
+//     values;
 //   - an exclusive scan of those counts: the pair offsets in depth order, and
 //     for every 16384-pair partition the splat its first pair belongs to;
 //   - the first tile pass (low 8 bits of the tile id) with the emission fused
